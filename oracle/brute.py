@@ -1,0 +1,115 @@
+"""Second, independent formulation of the oracle for tiny inputs (test infrastructure).
+
+Pure Python over numpy scalars: binary32 scalar arithmetic for the codec
+(numpy's float32 scalar operations round once per operation, to nearest even)
+and math.fsum-free explicit float64 loops for attention.  It exists to
+cross-check ``kvq_oracle.c`` on inputs small enough for Python loops; it does
+not import that library.
+
+Sources: asymmetric min-max parameters and the clamp-round code
+("Atom: Low-bit Quantization for Efficient and Accurate LLM Serving",
+section 三 "核心公式"); dequantization (q - zero) * scale
+("KV Cache的Int4量化：如何解决Attention Sink导致的量化精度崩塌问题", section 2);
+attention softmax(q K^T / sqrt(d)) V (same post, section 3).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+f32 = np.float32
+
+
+def quant_group(values, bits: int):
+    """Returns (scale, zero, codes) with one binary32 rounding per operation."""
+    xs = [f32(v) for v in values]
+    mn = min(xs)
+    mx = max(xs)
+    qmax = f32((1 << bits) - 1)
+    s = f32(f32(mx - mn) / qmax)
+    if mx == mn or s == f32(0):
+        s = f32(abs(mn)) if mn != f32(0) else f32(1)
+    z = f32(np.rint(f32(f32(-mn) / s)))
+    if z == f32(0):
+        z = f32(0.0)
+    codes = []
+    for x in xs:
+        t = f32(f32(np.rint(f32(x / s))) + z)
+        t = min(max(t, f32(0)), qmax)
+        codes.append(int(t))
+    return s, z, codes
+
+
+def dequant(code: int, s, z):
+    return f32(f32(f32(code) - f32(z)) * f32(s))
+
+
+def attention(q, K, V, scale: float):
+    """Explicit-loop binary64 attention of one query row over the rows of K, V."""
+    T = len(K)
+    D = len(q)
+    scores = []
+    for j in range(T):
+        acc = 0.0
+        for c in range(D):
+            acc += float(q[c]) * float(K[j][c])
+        scores.append(acc * scale)
+    m = max(scores)
+    ws = [math.exp(s - m) for s in scores]
+    den = sum(ws)
+    out = [sum(ws[j] * float(V[j][c]) for j in range(T)) / den for c in range(D)]
+    return np.array(out), m + math.log(den)
+
+
+def build_slice(k_tok, v_tok, *, bits, k_group, v_group, residual, n_sink):
+    """Token-by-token cache construction, written independently of the C oracle.
+
+    Returns dict with lists: sinks, quantized (dequantized K', V' rows in token
+    order), residual rows, codes and metadata, and the flush count.
+    """
+    D = len(k_tok[0])
+    sinks_k, sinks_v, res_k, res_v = [], [], [], []
+    qk_rows, qv_rows = [], []
+    k_codes, v_codes, k_meta, v_meta = [], [], [], []
+    flushes = 0
+    for kt, vt in zip(k_tok, v_tok):
+        if len(sinks_k) < n_sink:
+            sinks_k.append(list(kt))
+            sinks_v.append(list(vt))
+            continue
+        res_k.append(list(kt))
+        res_v.append(list(vt))
+        if len(res_k) < residual:
+            continue
+        flushes += 1
+        # keys: per channel over each run of k_group tokens
+        for j0 in range(0, residual, k_group):
+            block = res_k[j0:j0 + k_group]
+            rows = [[None] * D for _ in block]
+            crow = [[0] * D for _ in block]
+            meta = []
+            for c in range(D):
+                s, z, q = quant_group([row[c] for row in block], bits)
+                meta.append((s, z))
+                for i, code in enumerate(q):
+                    rows[i][c] = dequant(code, s, z)
+                    crow[i][c] = code
+            qk_rows.extend(rows)
+            k_codes.extend(crow)
+            k_meta.append(meta)
+        # values: per token, per run of v_group channels
+        for row in res_v:
+            out, crow, meta = [], [], []
+            for h in range(0, D, v_group):
+                s, z, q = quant_group(row[h:h + v_group], bits)
+                meta.append((s, z))
+                out.extend(dequant(code, s, z) for code in q)
+                crow.extend(q)
+            qv_rows.append(out)
+            v_codes.append(crow)
+            v_meta.append(meta)
+        res_k, res_v = [], []
+    return dict(sinks_k=sinks_k, sinks_v=sinks_v, qk=qk_rows, qv=qv_rows,
+                res_k=res_k, res_v=res_v, k_codes=k_codes, v_codes=v_codes,
+                k_meta=k_meta, v_meta=v_meta, flushes=flushes)

@@ -1,0 +1,289 @@
+/*
+ * kvq_oracle.c -- plain, slow CPU oracle for low-bit KV-cache decode attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test-suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  It shares no code with
+ * the HIP library: no headers, no helpers, no tables.
+ *
+ * What it computes, and where the pages state it:
+ *   - the asymmetric min-max group quantizer and its inverse
+ *       scale = (max - min) / (2^n - 1), zero = round(-min / scale)
+ *         ("KV Cache的Int4量化：如何解决Attention Sink导致的量化精度崩塌问题",
+ *          section 2 "量化基础：线性量化", Min-Max bullet; and
+ *          "Atom: Low-bit Quantization for Efficient and Accurate LLM Serving",
+ *          section 三 "核心公式", asymmetric parameters with clip factor c = 1)
+ *       code = clamp(round(x / scale) + zero, 0, 2^n - 1)
+ *         (Atom review, section 三 "核心公式", quantized-tensor formula)
+ *       x' = (code - zero) * scale
+ *         (Int4 KV-cache post, section 2, dequantization formula)
+ *   - the KIVI cache layout: keys grouped per channel over G tokens, values
+ *     per token, newest tokens in a full-precision residual that is quantized
+ *     and appended once it holds R tokens, then emptied
+ *       ("LLM系列：KVCache量化1 KIVI: A Tuning-Free Asymmetric 2bit Quantiz",
+ *        section 1 "KIVI", key-cache split into grouped part and residual)
+ *   - attention softmax(q K^T / sqrt(d)) V over every cached token
+ *       (Int4 KV-cache post, section 3, attention formula; KIVI notes, section 1,
+ *        logits as the concatenation of the grouped and residual parts;
+ *        "Resumo Técnico: LogQuant", Metodologia item 4: token order does not
+ *        change the result).
+ *
+ * Precision.  The codec is an encoding, so it is followed step by step in
+ * IEEE-754 binary32 with round-to-nearest-even per operation (build with
+ * -ffp-contract=off, no fast-math, denormals kept): exactly one rounding per
+ * written operation, in the written order.  Attention has a plain closed form
+ * and is computed in binary64 from the exact fp32 dequantized values.
+ *
+ * Readings where the pages are silent (each is listed with its reason in the
+ * design notes of the repository):
+ *   round = round-half-to-even; codes unsigned in [0, 2^n - 1];
+ *   code = clamp(rint(x/s) + z) in that order; clip factor c = 1;
+ *   a group whose computed scale is 0 (max == min, or a range so small that
+ *   range/(2^n-1) underflows) uses scale |min| (or 1 when min == 0);
+ *   a zero point of -0 is stored as +0; zero points are integer-valued fp32
+ *   and may fall outside [0, 2^n - 1];
+ *   the whole residual (R tokens, keys and values) is flushed when it reaches R;
+ *   the first S tokens of a sequence stay full precision for good (sinks);
+ *   query head h reads kv head h / (Hq / Hkv).
+ */
+#include <math.h>
+#include <stdint.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+#include <stdlib.h>
+#include <string.h>
+
+#if defined(__FAST_MATH__)
+#error "the oracle must not be built with fast-math"
+#endif
+
+/* ---------------------------------------------------------------------- */
+/* group quantizer                                                         */
+/* ---------------------------------------------------------------------- */
+
+/*
+ * Quantize m values x[0], x[stride], ... to n-bit codes.  Writes the group's
+ * scale and zero point and the codes q[0], q[qstride], ...
+ */
+void orc_quant_group(const float* x, int64_t m, int64_t stride, int bits,
+                     float* s_out, float* z_out, uint8_t* q, int64_t qstride)
+{
+    float mn = x[0], mx = x[0];
+    for (int64_t i = 1; i < m; ++i) {
+        float v = x[i * stride];
+        if (v < mn) mn = v;
+        if (v > mx) mx = v;
+    }
+    const float qmax = (float)((1 << bits) - 1);  /* 2^n - 1, exact */
+    float range = mx - mn;
+    float s = range / qmax;
+    if (mx == mn || s == 0.0f) {
+        /* degenerate group: keep the closed forms with a nonzero scale */
+        s = (mn != 0.0f) ? fabsf(mn) : 1.0f;
+    }
+    float negmn = -mn;
+    float z = rintf(negmn / s);
+    if (z == 0.0f) z = 0.0f; /* canonical +0 */
+    for (int64_t i = 0; i < m; ++i) {
+        float xi = x[i * stride];
+        float r = rintf(xi / s);
+        float t = r + z;
+        if (t < 0.0f) t = 0.0f;
+        if (t > qmax) t = qmax;
+        q[i * qstride] = (uint8_t)t;
+    }
+    *s_out = s;
+    *z_out = z;
+}
+
+/* x' = (code - zero) * scale */
+float orc_dequant(uint8_t q, float s, float z)
+{
+    float d = (float)q - z;
+    return d * s;
+}
+
+/* ---------------------------------------------------------------------- */
+/* cache state of one (sequence, kv-head) slice                            */
+/* ---------------------------------------------------------------------- */
+
+typedef struct {
+    int D, bits, G, GV, R, S;
+    /* buffers owned by the caller */
+    float* sink_k; float* sink_v;               /* [S, D]            */
+    uint8_t* k_codes; float* k_scale; float* k_zero;   /* [Lq,D] [Lq/G,D] */
+    uint8_t* v_codes; float* v_scale; float* v_zero;   /* [Lq,D] [Lq,D/GV] */
+    float* res_k; float* res_v;                 /* [R, D]            */
+    int64_t nS, Lq, r, flushes;
+} orc_slice;
+
+/* Quantize the full residual (R tokens) and append it to the quantized part. */
+static void flush_residual(orc_slice* c)
+{
+    const int D = c->D, G = c->G, GV = c->GV, R = c->R;
+    const int nvg = D / GV;
+    /* keys: one group per channel over each run of G tokens */
+    for (int j = 0; j < R / G; ++j) {
+        int64_t grp = c->Lq / G + j;
+        for (int ch = 0; ch < D; ++ch) {
+            orc_quant_group(c->res_k + (int64_t)j * G * D + ch, G, D, c->bits,
+                            &c->k_scale[grp * D + ch], &c->k_zero[grp * D + ch],
+                            c->k_codes + (c->Lq + (int64_t)j * G) * D + ch, D);
+        }
+    }
+    /* values: one group per run of GV channels of each token */
+    for (int t = 0; t < R; ++t) {
+        int64_t tok = c->Lq + t;
+        for (int h = 0; h < nvg; ++h) {
+            orc_quant_group(c->res_v + (int64_t)t * D + (int64_t)h * GV, GV, 1, c->bits,
+                            &c->v_scale[tok * nvg + h], &c->v_zero[tok * nvg + h],
+                            c->v_codes + tok * D + (int64_t)h * GV, 1);
+        }
+    }
+    c->Lq += R;
+    c->r = 0;
+    c->flushes += 1;
+}
+
+/* Append one token: sink slot while sinks remain, else residual; flush at R. */
+static void append_token(orc_slice* c, const float* k, const float* v)
+{
+    const int D = c->D;
+    if (c->nS < c->S) {
+        memcpy(c->sink_k + c->nS * D, k, sizeof(float) * D);
+        memcpy(c->sink_v + c->nS * D, v, sizeof(float) * D);
+        c->nS += 1;
+        return;
+    }
+    memcpy(c->res_k + c->r * D, k, sizeof(float) * D);
+    memcpy(c->res_v + c->r * D, v, sizeof(float) * D);
+    c->r += 1;
+    if (c->r == c->R) flush_residual(c);
+}
+
+/*
+ * Build the cache of one slice by appending n tokens (fp32 [n, D] each) one
+ * at a time.  counts[0..3] receive nS, Lq, r and the number of flushes.
+ * Output buffers must hold the sizes given above for Lq = R*floor((n-S)/R).
+ * Returns 0, or -1 on an invalid configuration.
+ */
+int orc_build_slice(int D, int bits, int G, int GV, int R, int S,
+                    const float* k_tok, const float* v_tok, int64_t n,
+                    float* sink_k, float* sink_v,
+                    uint8_t* k_codes, float* k_scale, float* k_zero,
+                    uint8_t* v_codes, float* v_scale, float* v_zero,
+                    float* res_k, float* res_v, int64_t* counts)
+{
+    if (D <= 0 || G <= 0 || GV <= 0 || R <= 0 || S < 0 || n < 0) return -1;
+    if (bits != 2 && bits != 4) return -1;
+    if (R % G != 0 || D % GV != 0) return -1;
+    orc_slice c = {D, bits, G, GV, R, S, sink_k, sink_v, k_codes, k_scale, k_zero,
+                   v_codes, v_scale, v_zero, res_k, res_v, 0, 0, 0, 0};
+    for (int64_t t = 0; t < n; ++t)
+        append_token(&c, k_tok + t * D, v_tok + t * D);
+    counts[0] = c.nS; counts[1] = c.Lq; counts[2] = c.r; counts[3] = c.flushes;
+    return 0;
+}
+
+/*
+ * Dequantize one slice into chronological token order: sinks, then the
+ * quantized tokens, then the residual.  k_out, v_out: fp32 [nS+Lq+r, D].
+ */
+void orc_dequant_slice(int D, int G, int GV, int64_t nS, int64_t Lq, int64_t r,
+                       const float* sink_k, const float* sink_v,
+                       const uint8_t* k_codes, const float* k_scale, const float* k_zero,
+                       const uint8_t* v_codes, const float* v_scale, const float* v_zero,
+                       const float* res_k, const float* res_v,
+                       float* k_out, float* v_out)
+{
+    const int nvg = D / GV;
+    memcpy(k_out, sink_k, sizeof(float) * nS * D);
+    memcpy(v_out, sink_v, sizeof(float) * nS * D);
+    for (int64_t t = 0; t < Lq; ++t) {
+        int64_t grp = t / G;
+        for (int ch = 0; ch < D; ++ch) {
+            k_out[(nS + t) * D + ch] = orc_dequant(k_codes[t * D + ch],
+                                                   k_scale[grp * D + ch], k_zero[grp * D + ch]);
+            int h = ch / GV;
+            v_out[(nS + t) * D + ch] = orc_dequant(v_codes[t * D + ch],
+                                                   v_scale[t * nvg + h], v_zero[t * nvg + h]);
+        }
+    }
+    memcpy(k_out + (nS + Lq) * D, res_k, sizeof(float) * r * D);
+    memcpy(v_out + (nS + Lq) * D, res_v, sizeof(float) * r * D);
+}
+
+/* ---------------------------------------------------------------------- */
+/* attention                                                               */
+/* ---------------------------------------------------------------------- */
+
+/*
+ * out = softmax(scale * q K^T) V and lse = log(sum(exp(scale * q K^T))) for one
+ * query row over T tokens, in binary64.  The order of the tokens is immaterial.
+ */
+void orc_attention(const float* q, const float* K, const float* V, int64_t T, int D,
+                   double scale, double* out, double* lse)
+{
+    double* sc = (double*)malloc(sizeof(double) * (T > 0 ? T : 1));
+    double M = -INFINITY;
+    for (int64_t j = 0; j < T; ++j) {
+        double dot = 0.0;
+        for (int c = 0; c < D; ++c) dot += (double)q[c] * (double)K[j * D + c];
+        sc[j] = dot * scale;
+        if (sc[j] > M) M = sc[j];
+    }
+    double den = 0.0;
+    for (int c = 0; c < D; ++c) out[c] = 0.0;
+    for (int64_t j = 0; j < T; ++j) {
+        double w = exp(sc[j] - M);
+        den += w;
+        for (int c = 0; c < D; ++c) out[c] += w * (double)V[j * D + c];
+    }
+    for (int c = 0; c < D; ++c) out[c] /= den;
+    *lse = M + log(den);
+    free(sc);
+}
+
+/*
+ * One decode step over n independent slices that share a cache state
+ * (nS, Lq, r): dequantize each slice, then attend each of its g query heads.
+ * Arrays are the per-slice arrays above stacked along a leading slice axis;
+ * q is fp32 [n, g, D]; out [n, g, D] and lse [n, g] are binary64.
+ * Slices are independent, so they are spread over OpenMP threads.
+ */
+void orc_decode_slices(int64_t n, int g, int D, int G, int GV,
+                       int64_t nS, int64_t Lq, int64_t r, double scale,
+                       const float* sink_k, const float* sink_v,
+                       const uint8_t* k_codes, const float* k_scale, const float* k_zero,
+                       const uint8_t* v_codes, const float* v_scale, const float* v_zero,
+                       const float* res_k, const float* res_v,
+                       const float* q, double* out, double* lse)
+{
+    const int64_t T = nS + Lq + r;
+    const int64_t nvg = D / GV;
+    #pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < n; ++i) {
+        float* kf = (float*)malloc(sizeof(float) * (T > 0 ? T : 1) * D);
+        float* vf = (float*)malloc(sizeof(float) * (T > 0 ? T : 1) * D);
+        orc_dequant_slice(D, G, GV, nS, Lq, r,
+                          sink_k + i * nS * D, sink_v + i * nS * D,
+                          k_codes + i * Lq * D, k_scale + i * (Lq / G) * D,
+                          k_zero + i * (Lq / G) * D,
+                          v_codes + i * Lq * D, v_scale + i * Lq * nvg, v_zero + i * Lq * nvg,
+                          res_k + i * r * D, res_v + i * r * D, kf, vf);
+        for (int h = 0; h < g; ++h)
+            orc_attention(q + (i * g + h) * D, kf, vf, T, D, scale,
+                          out + (i * g + h) * D, lse + i * g + h);
+        free(kf);
+        free(vf);
+    }
+}
+
+int orc_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

@@ -1,0 +1,102 @@
+"""The oracle's pins catch plausible mistakes.
+
+Each case plants one mistake in a copy of the oracle's C source (on the CPU, in a
+temporary directory), builds it, swaps it in, and runs the pin tests: at least one
+pin must fail.  The committed oracle itself is never modified.
+"""
+import os
+
+import pytest
+
+import oracle
+import tests.test_oracle_cache as tc
+import tests.test_oracle_codec as tq
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "kvq_oracle.c")
+
+MUTANTS = {
+    # rounding half away from zero instead of half to even
+    "half_away": ("float r = rintf(xi / s);", "float r = roundf(xi / s);"),
+    # the zero point added before rounding (the other operation order)
+    "add_before_round": ("float r = rintf(xi / s);\n        float t = r + z;",
+                         "float t = rintf(xi / s + z);"),
+    # missing upper clamp
+    "no_upper_clamp": ("if (t > qmax) t = qmax;", ""),
+    # signed code range [-2^(n-1), 2^(n-1)-1]
+    "signed_clamp": ("if (t > qmax) t = qmax;",
+                     "if (t > (float)((1 << (bits - 1)) - 1)) t = (float)((1 << (bits - 1)) - 1);"),
+    # 2^n levels in the scale instead of 2^n - 1
+    "scale_2n": ("float s = range / qmax;", "float s = range / (qmax + 1.0f);"),
+    # no degenerate-group rule (division by a zero scale)
+    "no_degenerate_rule": ("if (mx == mn || s == 0.0f) {", "if (0) {"),
+    # a zero point of -0 kept as is
+    "keep_negative_zero": ("if (z == 0.0f) z = 0.0f;", ""),
+    # dequantization in the expanded order q*s - z*s
+    "dequant_expanded": ("float d = (float)q - z;\n    return d * s;",
+                         "return (float)q * s - z * s;"),
+    # flush before storing the token (residual may hold R tokens between calls)
+    "flush_before_append": (
+        "    memcpy(c->res_k + c->r * D, k, sizeof(float) * D);\n"
+        "    memcpy(c->res_v + c->r * D, v, sizeof(float) * D);\n"
+        "    c->r += 1;\n"
+        "    if (c->r == c->R) flush_residual(c);",
+        "    if (c->r == c->R) flush_residual(c);\n"
+        "    memcpy(c->res_k + c->r * D, k, sizeof(float) * D);\n"
+        "    memcpy(c->res_v + c->r * D, v, sizeof(float) * D);\n"
+        "    c->r += 1;"),
+    # keys grouped along channels of a token instead of along tokens of a channel
+    "key_groups_transposed": ("orc_quant_group(c->res_k + (int64_t)j * G * D + ch, G, D, c->bits,",
+                              "orc_quant_group(c->res_k + (int64_t)j * G * D + ch, G, 1, c->bits,"),
+    # softmax scale dropped
+    "no_softmax_scale": ("sc[j] = dot * scale;", "sc[j] = dot;"),
+    # the last token of the cache is left out of the softmax denominator
+    "drop_last_token": ("    for (int64_t j = 0; j < T; ++j) {\n        double w = exp(sc[j] - M);",
+                        "    for (int64_t j = 0; j < T - 1; ++j) {\n        double w = exp(sc[j] - M);"),
+    # residual tokens left out of the dequantized token sequence
+    "drop_residual": ("memcpy(k_out + (nS + Lq) * D, res_k, sizeof(float) * r * D);",
+                      "memset(k_out + (nS + Lq) * D, 0, sizeof(float) * r * D);"),
+}
+
+
+def _pins():
+    """Every pin test, bound to its parameters."""
+    pins = []
+    for case in tq._cases():
+        pins.append(lambda c=case: tq.test_golden_example(c))
+    for bits in (2, 4):
+        pins.append(lambda b=bits: tq.test_invariants_random_groups(b))
+        pins.append(lambda b=bits: tq.test_exact_grid_reconstruction(b))
+    pins.append(tq.test_signed_zero_inputs)
+    pins.append(tq.test_underflowing_scale_uses_degenerate_rule)
+    for args in [(0, 8, 4, 29), (3, 8, 2, 40), (5, 16, 4, 100)]:
+        pins.append(lambda a=args: tc.test_counts_closed_form(*a))
+    pins += [tc.test_flush_exactly_at_R, tc.test_grouping_axes_by_direct_regrouping,
+             tc.test_workload_schedules_flush_where_expected,
+             tc.test_attention_closed_form_equal_keys_and_zero_query,
+             tc.test_attention_single_token, tc.test_attention_matches_torch_sdpa_float64,
+             tc.test_unquantized_cache_is_plain_attention]
+    return pins
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_reject_mutant(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert old in src, "mutation anchor not found: " + name
+    mutated = src.replace(old, new, 1)
+    assert mutated != src
+    p = tmp_path / ("mut_%s.c" % name)
+    p.write_text(mutated)
+    so = oracle.compile_source(str(p), str(tmp_path / ("mut_%s.so" % name)))
+    saved = oracle._lib
+    oracle._lib = oracle.load(so)
+    failed = 0
+    try:
+        for pin in _pins():
+            try:
+                pin()
+            except Exception:
+                failed += 1
+    finally:
+        oracle._lib = saved
+    assert failed > 0, "no pin caught mutant " + name
