@@ -1,0 +1,244 @@
+"""Benchmark of quantized decode attention over a low-bit KV cache on one MI355X.
+
+One step = one pass of the whole hot path over one batch: append one token per
+sequence (residual copy; a flush when the residual fills) and decode attention
+of one query per (sequence, query head) over sinks + quantized tokens +
+residual.  Inputs are resident in HBM before timing starts.
+
+To measure HBM rather than the 256 MB MALL, the benchmark keeps L independent
+caches of the same workload ("layers") whose combined size is at least three
+times the MALL, and step s works on layer s mod L (as consecutive layers of a
+model would): every step streams its layer's cache from HBM.
+
+Prints one JSON line.  `value` is the effective KV bandwidth of the step:
+algorithmic bytes of decode attention (packed codes, scales and zero points,
+full-precision sinks and residual, q in and fp32 out) per step divided by the
+wall time per step.  `roofline.achieved` uses the decode kernel's own duration,
+timed with HIP events on the stream it is launched on.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import workloads as wl  # noqa: E402
+
+METRIC = "effective KV GB/s (and % HBM peak) of quantized decode attention; tokens/s"
+HBM_PEAK_GBS = 8000.0
+MALL_BYTES = 256 * 2 ** 20
+DEFAULT_WORKLOAD = "llama7b_mha_int4"
+DECODE_SOURCES = ["decode_impl.h", "decode_dispatch.h", "decode.hip", "kvq_internal.h"]
+
+
+def algorithmic_bytes(w: wl.Workload, n_sink: int, n_quant: int, n_resid: int) -> int:
+    """Bytes the method itself must move for one decode-attention call."""
+    D, e = w.head_dim, wl.elem_bytes(w.dtype)
+    per_slice = (n_quant * 2 * D * w.bits // 8                 # K and V codes
+                 + (n_quant // w.k_group) * 2 * D * 4            # K scale + zero
+                 + n_quant * (D // w.v_group) * 2 * 4            # V scale + zero
+                 + (n_sink + n_resid) * 2 * D * e)               # full-precision tokens
+    return w.batch * w.n_kv_heads * per_slice + w.batch * w.n_q_heads * D * (e + 4)
+
+
+def decode_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in DECODE_SOURCES:
+        with open(os.path.join(ROOT, "bit_quantized_kv_kvq_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(w: wl.Workload):
+    """HBM bytes per decode launch from the committed counter summary, if it was
+    taken on the current decode kernel source for this workload; else None."""
+    path = os.path.join(ROOT, "profiles", "decode_traffic_%s.json" % w.name)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("decode_source_hash") != decode_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w: wl.Workload, budget_s: float):
+    """The oracle, as it is, on host cores: the decode step (dequantize + binary64
+    attention) of a bounded sample of (sequence, kv-head) slices of the workload."""
+    import oracle
+    n_slices_total = w.batch * w.n_kv_heads
+    # sample: as many slices as fit about budget_s of CPU work, measured on a probe
+    slices = [(b, h) for b in range(w.batch) for h in range(w.n_kv_heads)]
+    probe = slices[:1]
+    states = [oracle.slice_state(w, b, h, 0) for b, h in probe]
+    g = w.gqa
+    qs = np.stack([np.stack([wl.storage_to_f32(wl.query_slice(w, b, h * g + j)[0], w.dtype)
+                             for j in range(g)]) for b, h in probe])
+    scale = oracle.default_scale(w.head_dim)
+    t0 = time.perf_counter()
+    oracle.decode_slices(states, qs, scale)
+    t_probe = max(time.perf_counter() - t0, 1e-4)
+    threads = oracle.num_threads()
+    n = int(min(n_slices_total, max(threads, budget_s / t_probe * threads)))
+    n = max(1, n)
+    sample = slices[:n]
+    states = [oracle.slice_state(w, b, h, 0) for b, h in sample]
+    qs = np.stack([np.stack([wl.storage_to_f32(wl.query_slice(w, b, h * g + j)[0], w.dtype)
+                             for j in range(g)]) for b, h in sample])
+    t0 = time.perf_counter()
+    oracle.decode_slices(states, qs, scale)
+    dt = time.perf_counter() - t0
+    st = states[0]
+    full = algorithmic_bytes(w, st["n_sink"], st["n_quant"], st["n_resid"])
+    frac = n / n_slices_total
+    gbs = full * frac / dt / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": "decode step (dequantize + binary64 attention) of %d of %d (sequence, "
+                      "kv-head) slices after the %d-token prefill; %.2f s; full-step estimate "
+                      "%.3f s" % (n, n_slices_total, w.prefill, dt, dt / frac),
+            "seconds_per_step_estimate": round(dt / frac, 4)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--layers", type=int, default=0, help="caches rotated per step (0 = auto)")
+    ap.add_argument("--split-tokens", type=int, default=0)
+    ap.add_argument("--cpu-budget", type=float, default=12.0,
+                    help="seconds of oracle work for the CPU baseline (0 = skip)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this path runs on one GPU; a run on %d GPUs is not provided "
+              "(the decode shards with no exchange over (sequence, kv-head) slices)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import bit_quantized_kv_kvq_amd as kvq
+    from workloads.torch_io import TORCH_DTYPES, to_torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    w = wl.get(args.workload)
+    total_steps = args.warmup + args.steps
+
+    # size of one cache's decode traffic; enough layers to overflow the MALL 3x
+    nq0 = w.residual * ((w.prefill - min(w.prefill, w.n_sink)) // w.residual)
+    b0 = algorithmic_bytes(w, min(w.prefill, w.n_sink), nq0, w.prefill - min(w.prefill, w.n_sink) - nq0)
+    L = args.layers or max(2, math.ceil(3 * MALL_BYTES / b0))
+    per_layer_steps = (total_steps + L - 1) // L
+    max_tokens = w.prefill + per_layer_steps
+
+    print("bench: workload %s, %d layers, %d warmup + %d timed steps" %
+          (w.name, L, args.warmup, args.steps), file=sys.stderr, flush=True)
+    Kp, Vp = wl.prefill_batch(w)
+    Kd, Vd = to_torch(Kp, w.dtype, dev), to_torch(Vp, w.dtype, dev)
+    del Kp, Vp
+    caches = []
+    for _ in range(L):
+        c = kvq.Cache(batch=w.batch, n_kv_heads=w.n_kv_heads, n_q_heads=w.n_q_heads,
+                      head_dim=w.head_dim, bits=w.bits, k_group=w.k_group, v_group=w.v_group,
+                      residual=w.residual, n_sink=w.n_sink, dtype=TORCH_DTYPES[w.dtype],
+                      max_tokens=max_tokens, device=dev)
+        if args.split_tokens:
+            c.set_split_tokens(args.split_tokens)
+        c.append(Kd, Vd)
+        caches.append(c)
+    del Kd, Vd
+    Ks, Vs = wl.steps_batch(w)
+    Ks = to_torch(Ks, w.dtype, dev)[:, :, :, None].contiguous()   # [steps, B, Hkv, 1, D]
+    Vs = to_torch(Vs, w.dtype, dev)[:, :, :, None].contiguous()
+    Q = to_torch(wl.queries_batch(w), w.dtype, dev)                 # [nq, B, Hq, D]
+    out = torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=torch.float32, device=dev)
+    lse = torch.empty((w.batch, w.n_q_heads), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    print("bench: caches ready", file=sys.stderr, flush=True)
+
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    step_bytes = []
+
+    def step(s: int, timed_idx: int | None):
+        c = caches[s % L]
+        i = (s // L) % w.steps
+        c.append(Ks[i], Vs[i])
+        if timed_idx is not None:
+            _, nS, Lq, r = c.state()
+            step_bytes.append(algorithmic_bytes(w, nS, Lq, r))
+            ev[timed_idx][0].record(stream)
+        c.decode(Q[i % Q.shape[0]], out=out, lse=lse)
+        if timed_idx is not None:
+            ev[timed_idx][1].record(stream)
+
+    for s in range(args.warmup):
+        step(s, None)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(args.warmup + k, k)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    dec_ms = [a.elapsed_time(b) for a, b in ev]
+    dec_avg_ms = sum(dec_ms) / len(dec_ms)
+    bytes_avg = sum(step_bytes) / len(step_bytes)
+    value = bytes_avg / (ms_per_step * 1e-3) / 1e9
+    achieved = bytes_avg / (dec_avg_ms * 1e-3) / 1e9
+    traffic = traffic_from_profile(w)
+
+    cpu = None
+    if args.cpu_budget > 0:
+        print("bench: CPU baseline (oracle)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(w, args.cpu_budget)
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "n_kv_heads": w.n_kv_heads,
+                   "n_q_heads": w.n_q_heads, "head_dim": w.head_dim, "context": w.prefill,
+                   "bits": w.bits, "k_group": w.k_group, "v_group": w.v_group,
+                   "residual": w.residual, "n_sink": w.n_sink, "storage": w.dtype,
+                   "layers_rotated": L, "parallelism": "single GPU"},
+        "tokens_per_s": round(w.batch / (ms_per_step * 1e-3), 1),
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "decode_kernel_us": round(dec_avg_ms * 1e3, 3),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic,
+                     "algorithmic_bytes_per_launch": int(bytes_avg)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

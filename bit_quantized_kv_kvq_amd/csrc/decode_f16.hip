@@ -1,0 +1,8 @@
+// decode_f16.hip -- decode kernel instantiations for f16 storage.
+#include "decode_dispatch.h"
+
+namespace kvq {
+namespace dec {
+KVQ_DEFINE_LAUNCH(DT_F16)
+}  // namespace dec
+}  // namespace kvq

@@ -1,0 +1,8 @@
+// decode_f32.hip -- decode kernel instantiations for f32 storage.
+#include "decode_dispatch.h"
+
+namespace kvq {
+namespace dec {
+KVQ_DEFINE_LAUNCH(DT_F32)
+}  // namespace dec
+}  // namespace kvq

@@ -1,0 +1,333 @@
+// kvq_host.cpp -- the C-ABI of libkvq: config validation, the cache state
+// machine (sinks / quantized groups / residual), split planning and kernel
+// launches on the caller's stream.  The host never waits on the device.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <new>
+
+#include "../../include/kvq.h"
+#include "kvq_internal.h"
+
+using namespace kvq;
+
+struct kvq_cache {
+    Layout L;
+    DevPtrs P;
+    char* buf;
+    int64_t nS, Lq, r;        // sinks held, quantized tokens, residual tokens
+    int64_t split_tokens;     // 0 = automatic
+    int num_cu;
+    int nsplit_cap;           // max splits per slice the workspace holds
+    float sm_scale;
+};
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+kvq_status fail(kvq_status st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+kvq_status ok() {
+    g_err[0] = '\0';
+    return KVQ_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+kvq_status validate(const kvq_config* c) {
+    if (!c) return fail(KVQ_ERR_INVALID_ARG, "config is NULL");
+    if (c->reserved != 0) return fail(KVQ_ERR_INVALID_ARG, "reserved field must be 0");
+    if (c->batch < 1 || c->n_kv_heads < 1 || c->n_q_heads < 1 || c->head_dim < 1)
+        return fail(KVQ_ERR_INVALID_ARG, "batch, heads and head_dim must be positive");
+    if (c->n_q_heads % c->n_kv_heads != 0)
+        return fail(KVQ_ERR_INVALID_ARG, "n_q_heads (%d) is not a multiple of n_kv_heads (%d)",
+                    c->n_q_heads, c->n_kv_heads);
+    if (c->k_group < 1 || c->v_group < 1 || c->residual < 1)
+        return fail(KVQ_ERR_INVALID_ARG, "k_group, v_group and residual must be positive");
+    if (c->residual % c->k_group != 0)
+        return fail(KVQ_ERR_INVALID_ARG, "residual (%d) is not a multiple of k_group (%d)",
+                    c->residual, c->k_group);
+    if (c->head_dim % c->v_group != 0)
+        return fail(KVQ_ERR_INVALID_ARG, "head_dim (%d) is not a multiple of v_group (%d)",
+                    c->head_dim, c->v_group);
+    if (c->n_sink < 0) return fail(KVQ_ERR_INVALID_ARG, "n_sink must be >= 0");
+    if (c->max_tokens < 1) return fail(KVQ_ERR_INVALID_ARG, "max_tokens must be >= 1");
+    if (c->dtype != KVQ_F32 && c->dtype != KVQ_BF16 && c->dtype != KVQ_F16)
+        return fail(KVQ_ERR_INVALID_ARG, "unknown dtype %d", c->dtype);
+    if (!(c->sm_scale >= 0.0f) || isinf(c->sm_scale))
+        return fail(KVQ_ERR_INVALID_ARG, "sm_scale must be finite and >= 0");
+    if (c->bits != 2 && c->bits != 4) return fail(KVQ_ERR_UNSUPPORTED, "bits must be 2 or 4");
+    if (c->head_dim != 64 && c->head_dim != 128)
+        return fail(KVQ_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+    const int g = c->n_q_heads / c->n_kv_heads;
+    if (g != 1 && g != 2 && g != 4 && g != 8)
+        return fail(KVQ_ERR_UNSUPPORTED, "n_q_heads / n_kv_heads must be 1, 2, 4 or 8");
+    if (c->k_group % 32 != 0 || c->k_group > 256)
+        return fail(KVQ_ERR_UNSUPPORTED, "k_group must be a multiple of 32 and at most 256");
+    if (c->v_group < 16 || c->v_group % 16 != 0)
+        return fail(KVQ_ERR_UNSUPPORTED, "v_group must be a multiple of 16");
+    if ((int64_t)c->batch * c->n_kv_heads > 65535)
+        return fail(KVQ_ERR_UNSUPPORTED, "batch * n_kv_heads must be at most 65535");
+    return KVQ_OK;
+}
+
+Layout make_layout(const kvq_config* c) {
+    Layout L;
+    L.B = c->batch;
+    L.Hkv = c->n_kv_heads;
+    L.Hq = c->n_q_heads;
+    L.D = c->head_dim;
+    L.bits = c->bits;
+    L.G = c->k_group;
+    L.GV = c->v_group;
+    L.R = c->residual;
+    L.S = c->n_sink;
+    L.dtype = c->dtype;
+    L.esize = c->dtype == KVQ_F32 ? 4 : 2;
+    L.gqa = L.Hq / L.Hkv;
+    L.nvg = L.D / L.GV;
+    L.row_bytes = L.D * L.bits / 8;
+    L.BH = (int64_t)L.B * L.Hkv;
+    L.max_tokens = c->max_tokens;
+    const int64_t after_sink = std::max<int64_t>(0, c->max_tokens - L.S);
+    L.Lq_cap = (int64_t)L.R * (after_sink / L.R);
+    L.ng_cap = L.Lq_cap / L.G;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t o = off;
+        off = align256(off + bytes);
+        return o;
+    };
+    const size_t fp_row = (size_t)L.D * L.esize;
+    L.off_ksink = take((size_t)L.BH * L.S * fp_row);
+    L.off_vsink = take((size_t)L.BH * L.S * fp_row);
+    L.off_kres = take((size_t)L.BH * L.R * fp_row);
+    L.off_vres = take((size_t)L.BH * L.R * fp_row);
+    L.off_kcodes = take((size_t)L.BH * L.Lq_cap * L.row_bytes);
+    L.off_vcodes = take((size_t)L.BH * L.Lq_cap * L.row_bytes);
+    L.off_kmeta = take((size_t)L.BH * L.ng_cap * 2 * L.D * sizeof(float));
+    L.off_vmeta = take((size_t)L.BH * L.Lq_cap * L.nvg * 2 * sizeof(float));
+    L.total = off;
+    return L;
+}
+
+kvq_status check_hip(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(KVQ_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+    return KVQ_OK;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+DecodePlan make_plan(const kvq_cache* c) {
+    const Layout& L = c->L;
+    DecodePlan p;
+    p.Lq = c->Lq;
+    p.nS = (int)c->nS;
+    p.r = (int)c->r;
+    p.has_fp = (c->nS + c->r) > 0 ? 1 : 0;
+    const int64_t ng = c->Lq / L.G;
+    const int cap_q = c->nsplit_cap - 1;
+    int64_t gps;
+    if (c->split_tokens > 0) {
+        gps = (c->split_tokens + L.G - 1) / L.G;
+    } else {
+        const int64_t target = 4LL * c->num_cu;  // workgroups for the whole device
+        gps = (L.BH * ng + target - 1) / target;
+        gps = std::max<int64_t>(gps, std::min<int64_t>(kWaves, ng));
+    }
+    gps = std::max<int64_t>(gps, 1);
+    if (ng > 0 && (ng + gps - 1) / gps > cap_q) gps = (ng + cap_q - 1) / cap_q;
+    p.gps = (int)gps;
+    p.nsplit_q = ng > 0 ? (int)((ng + gps - 1) / gps) : 0;
+    p.nsplit = p.nsplit_q + p.has_fp;
+    return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+kvq_status kvq_cache_bytes(const kvq_config* cfg, size_t* bytes) {
+    kvq_status st = validate(cfg);
+    if (st != KVQ_OK) return st;
+    if (!bytes) return fail(KVQ_ERR_INVALID_ARG, "bytes is NULL");
+    *bytes = make_layout(cfg).total;
+    return ok();
+}
+
+kvq_status kvq_cache_create(const kvq_config* cfg, void* dev_buf, size_t bytes, kvq_cache** out) {
+    kvq_status st = validate(cfg);
+    if (st != KVQ_OK) return st;
+    if (!dev_buf || !out) return fail(KVQ_ERR_INVALID_ARG, "dev_buf or out is NULL");
+    if (!aligned(dev_buf, 256)) return fail(KVQ_ERR_INVALID_ARG, "dev_buf must be 256-byte aligned");
+    Layout L = make_layout(cfg);
+    if (bytes < L.total)
+        return fail(KVQ_ERR_BUFFER_TOO_SMALL, "cache buffer holds %zu bytes, needs %zu", bytes, L.total);
+    int dev = 0, ncu = 0;
+    if ((st = check_hip(hipGetDevice(&dev), "hipGetDevice")) != KVQ_OK) return st;
+    if ((st = check_hip(hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev),
+                        "hipDeviceGetAttribute")) != KVQ_OK)
+        return st;
+    kvq_cache* c = new (std::nothrow) kvq_cache;
+    if (!c) return fail(KVQ_ERR_INVALID_ARG, "out of host memory");
+    c->L = L;
+    c->buf = (char*)dev_buf;
+    c->P.ksink = c->buf + L.off_ksink;
+    c->P.vsink = c->buf + L.off_vsink;
+    c->P.kres = c->buf + L.off_kres;
+    c->P.vres = c->buf + L.off_vres;
+    c->P.kcodes = (uint8_t*)(c->buf + L.off_kcodes);
+    c->P.vcodes = (uint8_t*)(c->buf + L.off_vcodes);
+    c->P.kmeta = (float*)(c->buf + L.off_kmeta);
+    c->P.vmeta = (float*)(c->buf + L.off_vmeta);
+    c->nS = c->Lq = c->r = 0;
+    c->split_tokens = 0;
+    c->num_cu = ncu > 0 ? ncu : 256;
+    const int64_t want = std::max<int64_t>(8, (16LL * c->num_cu + L.BH - 1) / L.BH);
+    const int64_t cap_q = std::min<int64_t>(std::min<int64_t>(want, 256), kMaxCombine / L.gqa - 1);
+    c->nsplit_cap = (int)cap_q + 1;
+    c->sm_scale = cfg->sm_scale > 0.0f ? cfg->sm_scale : (float)(1.0 / sqrt((double)L.D));
+    *out = c;
+    return ok();
+}
+
+kvq_status kvq_cache_destroy(kvq_cache* cache) {
+    delete cache;
+    return ok();
+}
+
+kvq_status kvq_append(kvq_cache* c, const void* k, const void* v, int64_t n_new, void* stream) {
+    if (!c) return fail(KVQ_ERR_INVALID_ARG, "cache is NULL");
+    if (n_new < 0) return fail(KVQ_ERR_INVALID_ARG, "n_new must be >= 0");
+    if (n_new == 0) return ok();
+    if (!k || !v) return fail(KVQ_ERR_INVALID_ARG, "k or v is NULL");
+    if (!aligned(k, 16) || !aligned(v, 16)) return fail(KVQ_ERR_INVALID_ARG, "k and v must be 16-byte aligned");
+    const Layout& L = c->L;
+    const int64_t total = c->nS + c->Lq + c->r;
+    if (n_new > L.max_tokens - total)
+        return fail(KVQ_ERR_CAPACITY, "append of %lld tokens exceeds max_tokens %lld (holding %lld)",
+                    (long long)n_new, (long long)L.max_tokens, (long long)total);
+    hipStream_t s = (hipStream_t)stream;
+    kvq_status st;
+    int64_t src = 0, rem = n_new;
+    // 1. sinks
+    if (c->nS < L.S && rem > 0) {
+        const int64_t take = std::min<int64_t>(L.S - c->nS, rem);
+        if ((st = check_hip(launch_copy_tokens(L, k, n_new, src, c->P.ksink, L.S, c->nS, take, s), "append")) ||
+            (st = check_hip(launch_copy_tokens(L, v, n_new, src, c->P.vsink, L.S, c->nS, take, s), "append")))
+            return st;
+        c->nS += take;
+        src += take;
+        rem -= take;
+    }
+    // 2. top up a partly filled residual; flush it when it reaches R
+    if (rem > 0 && c->r > 0) {
+        const int64_t take = std::min<int64_t>(L.R - c->r, rem);
+        if ((st = check_hip(launch_copy_tokens(L, k, n_new, src, c->P.kres, L.R, c->r, take, s), "append")) ||
+            (st = check_hip(launch_copy_tokens(L, v, n_new, src, c->P.vres, L.R, c->r, take, s), "append")))
+            return st;
+        c->r += take;
+        src += take;
+        rem -= take;
+        if (c->r == L.R) {
+            if ((st = check_hip(launch_quantize(L, c->P, c->P.kres, c->P.vres, L.R, 0, L.R / L.G, c->Lq, s),
+                                "flush")))
+                return st;
+            c->Lq += L.R;
+            c->r = 0;
+        }
+    }
+    // 3. complete R-token blocks straight from the input
+    const int64_t nblk = rem / L.R;
+    if (nblk > 0) {
+        if ((st = check_hip(launch_quantize(L, c->P, k, v, n_new, src, nblk * (L.R / L.G), c->Lq, s),
+                            "quantize")))
+            return st;
+        c->Lq += nblk * L.R;
+        src += nblk * L.R;
+        rem -= nblk * L.R;
+    }
+    // 4. the remainder starts a new residual
+    if (rem > 0) {
+        if ((st = check_hip(launch_copy_tokens(L, k, n_new, src, c->P.kres, L.R, 0, rem, s), "append")) ||
+            (st = check_hip(launch_copy_tokens(L, v, n_new, src, c->P.vres, L.R, 0, rem, s), "append")))
+            return st;
+        c->r = rem;
+    }
+    return ok();
+}
+
+kvq_status kvq_decode_workspace_bytes(const kvq_cache* c, size_t* bytes) {
+    if (!c || !bytes) return fail(KVQ_ERR_INVALID_ARG, "NULL argument");
+    *bytes = decode_workspace_bytes(c->L, c->nsplit_cap);
+    return ok();
+}
+
+kvq_status kvq_decode_attention(kvq_cache* c, const void* q, float* out, float* lse, void* ws,
+                                size_t ws_bytes, void* stream) {
+    if (!c || !q || !out || !ws) return fail(KVQ_ERR_INVALID_ARG, "cache, q, out or ws is NULL");
+    if (!aligned(q, 4) || !aligned(out, 4) || (lse && !aligned(lse, 4)) || !aligned(ws, 256))
+        return fail(KVQ_ERR_INVALID_ARG, "misaligned q, out, lse or ws");
+    if (c->nS + c->Lq + c->r == 0) return fail(KVQ_ERR_INVALID_ARG, "attention on an empty cache");
+    const size_t need = decode_workspace_bytes(c->L, c->nsplit_cap);
+    if (ws_bytes < need)
+        return fail(KVQ_ERR_BUFFER_TOO_SMALL, "workspace holds %zu bytes, needs %zu", ws_bytes, need);
+    const DecodePlan p = make_plan(c);
+    kvq_status st = check_hip(launch_decode(c->L, c->P, p, q, out, lse, ws, c->sm_scale, (hipStream_t)stream,
+                                            c->nsplit_cap),
+                              "decode");
+    if (st != KVQ_OK) return st;
+    return ok();
+}
+
+kvq_status kvq_dequantize(const kvq_cache* c, float* k_out, float* v_out, void* stream) {
+    if (!c || !k_out || !v_out) return fail(KVQ_ERR_INVALID_ARG, "NULL argument");
+    kvq_status st = check_hip(launch_dequantize(c->L, c->P, c->nS, c->Lq, c->r, k_out, v_out,
+                                                (hipStream_t)stream),
+                              "dequantize");
+    if (st != KVQ_OK) return st;
+    return ok();
+}
+
+kvq_status kvq_export(const kvq_cache* c, uint8_t* k_codes, float* k_scale, float* k_zero,
+                      uint8_t* v_codes, float* v_scale, float* v_zero, void* stream) {
+    if (!c) return fail(KVQ_ERR_INVALID_ARG, "cache is NULL");
+    kvq_status st = check_hip(launch_export(c->L, c->P, c->Lq, k_codes, k_scale, k_zero, v_codes,
+                                            v_scale, v_zero, (hipStream_t)stream),
+                              "export");
+    if (st != KVQ_OK) return st;
+    return ok();
+}
+
+kvq_status kvq_cache_state(const kvq_cache* c, int64_t* n_tokens, int64_t* n_sink, int64_t* n_quant,
+                           int64_t* n_resid) {
+    if (!c) return fail(KVQ_ERR_INVALID_ARG, "cache is NULL");
+    if (n_tokens) *n_tokens = c->nS + c->Lq + c->r;
+    if (n_sink) *n_sink = c->nS;
+    if (n_quant) *n_quant = c->Lq;
+    if (n_resid) *n_resid = c->r;
+    return ok();
+}
+
+kvq_status kvq_set_split_tokens(kvq_cache* c, int64_t tokens_per_split) {
+    if (!c) return fail(KVQ_ERR_INVALID_ARG, "cache is NULL");
+    if (tokens_per_split < 0) return fail(KVQ_ERR_INVALID_ARG, "tokens_per_split must be >= 0");
+    c->split_tokens = tokens_per_split;
+    return ok();
+}
+
+const char* kvq_last_error(void) { return g_err; }
+
+}  // extern "C"

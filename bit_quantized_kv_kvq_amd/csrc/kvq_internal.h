@@ -1,0 +1,118 @@
+// kvq_internal.h -- cache layout, packing format and kernel launch interfaces
+// shared by the host library and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kvq {
+
+enum DType : int { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2 };
+
+constexpr int kWaves = 4;              // waves per decode / quantize workgroup
+constexpr int kThreads = 64 * kWaves;  // 256 threads
+constexpr int kMaxCombine = 1024;      // max (splits x query heads per kv head)
+
+// ---------------------------------------------------------------------------
+// Device buffer layout of one cache.  Every array is indexed by the flattened
+// (sequence, kv head) slice bh = b * Hkv + kvh first:
+//   k_sink, v_sink : [BH][S][D]        storage dtype
+//   k_res,  v_res  : [BH][R][D]        storage dtype
+//   k_codes,v_codes: [BH][Lq_cap][D*bits/8] packed codes, one row per token
+//   k_meta         : [BH][Lq_cap/G][2][D]  fp32 (scales row, then zeros row)
+//   v_meta         : [BH][Lq_cap][D/G_V][2] fp32 (scale, zero) pairs
+// Lq_cap = R * floor((max_tokens - S) / R): the largest quantized length a
+// sequence of max_tokens tokens can reach.
+// ---------------------------------------------------------------------------
+struct Layout {
+    int B, Hkv, Hq, D, bits, G, GV, R, S, dtype, esize, gqa, nvg, row_bytes;
+    int64_t BH, max_tokens, Lq_cap, ng_cap;
+    size_t off_ksink, off_vsink, off_kres, off_vres, off_kcodes, off_vcodes, off_kmeta,
+        off_vmeta, total;
+};
+
+struct DevPtrs {
+    char* ksink;
+    char* vsink;
+    char* kres;
+    char* vres;
+    uint8_t* kcodes;
+    uint8_t* vcodes;
+    float* kmeta;
+    float* vmeta;
+};
+
+// ---------------------------------------------------------------------------
+// Packing.  A token row of D codes is stored as D*bits/32 dwords.  Dword i of
+// the row holds the 32/bits channels c = (32/bits)*i + j, j = 0..32/bits-1, with
+// channel j in byte (j & 3) at bit offset bits * (j >> 2) inside that byte.
+// Hence (dword >> (bits * k)) & (0x0F0F0F0F or 0x03030303) yields the four
+// channels 4k..4k+3 of the dword as the four bytes of a word, ready for the
+// byte-to-float conversions, and the unpacked order is the channel order.
+// ---------------------------------------------------------------------------
+__host__ __device__ inline int pack_shift(int bits, int j) { return 8 * (j & 3) + bits * (j >> 2); }
+
+// ---------------------------------------------------------------------------
+// storage dtype helpers
+// ---------------------------------------------------------------------------
+__device__ inline float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+__device__ inline float f16_to_f32(uint16_t h) {
+    _Float16 x;
+    __builtin_memcpy(&x, &h, 2);
+    return (float)x;
+}
+
+template <int DT>
+__device__ inline float load_as_f32(const void* base, int64_t idx) {
+    if constexpr (DT == DT_F32) {
+        return reinterpret_cast<const float*>(base)[idx];
+    } else if constexpr (DT == DT_BF16) {
+        return bf16_to_f32(reinterpret_cast<const uint16_t*>(base)[idx]);
+    } else {
+        return f16_to_f32(reinterpret_cast<const uint16_t*>(base)[idx]);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// launch interfaces (defined in the .hip sources)
+// ---------------------------------------------------------------------------
+
+// Copy n tokens of every slice from src[bh][src_tok0 + i][D] (src holds
+// src_tokens tokens per slice) to dst[bh][dst_tok0 + i][D] (dst holds
+// dst_tokens per slice).  Storage dtype preserved.
+hipError_t launch_copy_tokens(const Layout& L, const void* src, int64_t src_tokens, int64_t src_tok0,
+                              char* dst, int64_t dst_tokens, int64_t dst_tok0, int64_t n,
+                              hipStream_t stream);
+
+// Quantize n_groups consecutive key groups (n_groups * G tokens) of every slice,
+// read from src_k/src_v[bh][src_tok0 + t][D] (src_tokens tokens per slice), into
+// quantized token positions dst_tok0 + t.
+hipError_t launch_quantize(const Layout& L, const DevPtrs& P, const void* src_k, const void* src_v,
+                           int64_t src_tokens, int64_t src_tok0, int64_t n_groups, int64_t dst_tok0,
+                           hipStream_t stream);
+
+struct DecodePlan {
+    int64_t Lq;          // quantized tokens per slice
+    int nS, r;           // sinks held, residual tokens held
+    int gps;             // key groups per quantized split
+    int nsplit_q;        // quantized splits per slice
+    int nsplit;          // total splits per slice (quantized + optional full-precision)
+    int has_fp;          // 1 if a full-precision split covers sinks and residual
+};
+
+hipError_t launch_decode(const Layout& L, const DevPtrs& P, const DecodePlan& plan, const void* q,
+                         float* out, float* lse, void* ws, float sm_scale, hipStream_t stream,
+                         int nsplit_cap);
+
+size_t decode_workspace_bytes(const Layout& L, int max_splits);
+
+hipError_t launch_dequantize(const Layout& L, const DevPtrs& P, int64_t nS, int64_t Lq, int64_t r,
+                             float* k_out, float* v_out, hipStream_t stream);
+
+hipError_t launch_export(const Layout& L, const DevPtrs& P, int64_t Lq, uint8_t* k_codes,
+                         float* k_scale, float* k_zero, uint8_t* v_codes, float* v_scale,
+                         float* v_zero, hipStream_t stream);
+
+}  // namespace kvq

@@ -1,0 +1,344 @@
+// quant.hip -- append, flush (group quantize + pack), dequantize and export kernels.
+//
+// Group quantizer (asymmetric min-max, "Atom: Low-bit Quantization for Efficient
+// and Accurate LLM Serving", section 三 "核心公式"; dequantization from "KV Cache的
+// Int4量化：如何解决Attention Sink导致的量化精度崩塌问题", section 2):
+//   s = (max - min) / (2^n - 1); z = rint(-min / s); q = clamp(rint(x / s) + z, 0, 2^n - 1)
+//   x' = (q - z) * s
+// binary32 with one rounding per operation in this order (IEEE division, rint =
+// round half to even); a zero scale (constant group or underflowing range) is
+// replaced by |min| (1 when min == 0); a zero point of -0 is stored as +0.
+// Grouping (KIVI notes, "LLM系列：KVCache量化1 KIVI…", section 1): keys per channel
+// over each run of G tokens, values per token over each run of G_V channels.
+#include "kvq_internal.h"
+
+namespace kvq {
+namespace {
+
+#pragma clang fp contract(off)
+
+struct QParams {
+    float s, z;
+};
+
+__device__ inline QParams group_params(float mn, float mx, float qmax) {
+    float range = mx - mn;
+    float s = range / qmax;
+    if (mx == mn || s == 0.0f) s = (mn != 0.0f) ? fabsf(mn) : 1.0f;
+    float z = rintf((-mn) / s);
+    if (z == 0.0f) z = 0.0f;  // +0
+    return {s, z};
+}
+
+__device__ inline uint32_t group_code(float x, QParams p, float qmax) {
+    float t = rintf(x / p.s) + p.z;
+    t = t < 0.0f ? 0.0f : t;
+    t = t > qmax ? qmax : t;
+    return (uint32_t)t;
+}
+
+// ---------------------------------------------------------------------------
+// token copy (sink / residual slots), 16-byte vectors
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void copy_tokens_kernel(const uint4* __restrict__ src,
+                                                          int64_t src_tokens, int64_t src_tok0,
+                                                          uint4* __restrict__ dst, int64_t dst_tokens,
+                                                          int64_t dst_tok0, int64_t n, int row_vec,
+                                                          int64_t total) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        int64_t v = i % row_vec;
+        int64_t t = (i / row_vec) % n;
+        int64_t bh = i / ((int64_t)row_vec * n);
+        dst[(bh * dst_tokens + dst_tok0 + t) * row_vec + v] =
+            src[(bh * src_tokens + src_tok0 + t) * row_vec + v];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// quantize + pack one key group (G tokens x D channels) and the values of the
+// same G tokens.  grid = (n_groups, BH), block = 256.
+// ---------------------------------------------------------------------------
+struct QuantArgs {
+    const void* src_k;
+    const void* src_v;
+    int64_t src_tokens, src_tok0, dst_tok0;
+    int D, G, GV, nvg, row_bytes;
+    int64_t Lq_cap, ng_cap;
+    uint8_t* kcodes;
+    uint8_t* vcodes;
+    float* kmeta;
+    float* vmeta;
+};
+
+template <int BITS>
+__device__ inline void pack_rows(const uint8_t* s_codes, int rows, int D, int row_bytes,
+                                 uint8_t* dst_row0) {
+    constexpr int CPD = 32 / BITS;  // channels per dword
+    const int dpr = D / CPD;
+    for (int i = threadIdx.x; i < rows * dpr; i += blockDim.x) {
+        int t = i / dpr, w = i % dpr;
+        const uint8_t* c = s_codes + t * D + w * CPD;
+        uint32_t word = 0;
+#pragma unroll
+        for (int j = 0; j < CPD; ++j) word |= (uint32_t)c[j] << pack_shift(BITS, j);
+        reinterpret_cast<uint32_t*>(dst_row0 + (int64_t)t * row_bytes)[w] = word;
+    }
+}
+
+template <int DT, int BITS>
+__global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
+    extern __shared__ uint8_t s_codes[];  // [G][D]
+    constexpr float qmax = (float)((1 << BITS) - 1);
+    const int grp = blockIdx.x;
+    const int64_t bh = blockIdx.y;
+    const int D = a.D, G = a.G;
+    const int64_t src_row0 = bh * a.src_tokens + a.src_tok0 + (int64_t)grp * G;
+    const int64_t dst_tok = a.dst_tok0 + (int64_t)grp * G;  // first quantized token
+    const int64_t dst_grp = dst_tok / G;
+
+    // keys: one group per channel over the G tokens
+    for (int c = threadIdx.x; c < D; c += blockDim.x) {
+        const int64_t base = src_row0 * D + c;
+        float mn = load_as_f32<DT>(a.src_k, base), mx = mn;
+        for (int t = 1; t < G; ++t) {
+            float v = load_as_f32<DT>(a.src_k, base + (int64_t)t * D);
+            if (v < mn) mn = v;
+            if (v > mx) mx = v;
+        }
+        QParams p = group_params(mn, mx, qmax);
+        for (int t = 0; t < G; ++t)
+            s_codes[t * D + c] =
+                (uint8_t)group_code(load_as_f32<DT>(a.src_k, base + (int64_t)t * D), p, qmax);
+        float* km = a.kmeta + (bh * a.ng_cap + dst_grp) * 2 * D;
+        km[c] = p.s;
+        km[D + c] = p.z;
+    }
+    __syncthreads();
+    pack_rows<BITS>(s_codes, G, D, a.row_bytes, a.kcodes + (bh * a.Lq_cap + dst_tok) * a.row_bytes);
+    __syncthreads();
+
+    // values: one group per run of G_V channels of each token
+    const int GV = a.GV, nvg = a.nvg;
+    for (int i = threadIdx.x; i < G * nvg; i += blockDim.x) {
+        const int t = i / nvg, h = i % nvg;
+        const int64_t base = (src_row0 + t) * D + (int64_t)h * GV;
+        float mn = load_as_f32<DT>(a.src_v, base), mx = mn;
+        for (int j = 1; j < GV; ++j) {
+            float v = load_as_f32<DT>(a.src_v, base + j);
+            if (v < mn) mn = v;
+            if (v > mx) mx = v;
+        }
+        QParams p = group_params(mn, mx, qmax);
+        for (int j = 0; j < GV; ++j)
+            s_codes[t * D + h * GV + j] =
+                (uint8_t)group_code(load_as_f32<DT>(a.src_v, base + j), p, qmax);
+        float* vm = a.vmeta + ((bh * a.Lq_cap + dst_tok + t) * nvg + h) * 2;
+        vm[0] = p.s;
+        vm[1] = p.z;
+    }
+    __syncthreads();
+    pack_rows<BITS>(s_codes, G, D, a.row_bytes, a.vcodes + (bh * a.Lq_cap + dst_tok) * a.row_bytes);
+}
+
+// ---------------------------------------------------------------------------
+// dequantize to fp32 in token order (sinks, quantized, residual)
+// ---------------------------------------------------------------------------
+struct DeqArgs {
+    const char* ksink;
+    const char* vsink;
+    const char* kres;
+    const char* vres;
+    const uint8_t* kcodes;
+    const uint8_t* vcodes;
+    const float* kmeta;
+    const float* vmeta;
+    float* kout;
+    float* vout;
+    int64_t nS, Lq, r, T, Lq_cap, ng_cap;
+    int S, R, D, G, GV, nvg, bits, row_bytes;
+};
+
+__device__ inline uint32_t unpack_code(const uint8_t* row, int c, int bits) {
+    const int cpd = 32 / bits;
+    uint32_t w = reinterpret_cast<const uint32_t*>(row)[c / cpd];
+    return (w >> pack_shift(bits, c % cpd)) & ((1u << bits) - 1u);
+}
+
+template <int DT>
+__global__ __launch_bounds__(256) void dequantize_kernel(DeqArgs a) {
+    const int64_t bh = blockIdx.y;
+    const int64_t n = a.T * a.D;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t t = i / a.D;
+        const int c = (int)(i % a.D);
+        float kx, vx;
+        if (t < a.nS) {
+            const int64_t idx = (bh * a.S + t) * a.D + c;
+            kx = load_as_f32<DT>(a.ksink, idx);
+            vx = load_as_f32<DT>(a.vsink, idx);
+        } else if (t < a.nS + a.Lq) {
+            const int64_t tq = t - a.nS;
+            const int64_t row = bh * a.Lq_cap + tq;
+            const float* km = a.kmeta + (bh * a.ng_cap + tq / a.G) * 2 * a.D;
+            const float* vm = a.vmeta + (row * a.nvg + c / a.GV) * 2;
+            const float kq = (float)unpack_code(a.kcodes + row * a.row_bytes, c, a.bits);
+            const float vq = (float)unpack_code(a.vcodes + row * a.row_bytes, c, a.bits);
+            kx = (kq - km[a.D + c]) * km[c];
+            vx = (vq - vm[1]) * vm[0];
+        } else {
+            const int64_t idx = (bh * a.R + (t - a.nS - a.Lq)) * a.D + c;
+            kx = load_as_f32<DT>(a.kres, idx);
+            vx = load_as_f32<DT>(a.vres, idx);
+        }
+        a.kout[(bh * a.T + t) * a.D + c] = kx;
+        a.vout[(bh * a.T + t) * a.D + c] = vx;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// canonical export of codes and metadata
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void export_kernel(DeqArgs a, uint8_t* k_codes, float* k_scale,
+                                                     float* k_zero, uint8_t* v_codes,
+                                                     float* v_scale, float* v_zero) {
+    const int64_t bh = blockIdx.y;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t ncode = a.Lq * a.D;
+    for (int64_t i = i0; i < ncode; i += stride) {
+        const int64_t t = i / a.D;
+        const int c = (int)(i % a.D);
+        const int64_t row = bh * a.Lq_cap + t;
+        if (k_codes) k_codes[bh * ncode + i] = (uint8_t)unpack_code(a.kcodes + row * a.row_bytes, c, a.bits);
+        if (v_codes) v_codes[bh * ncode + i] = (uint8_t)unpack_code(a.vcodes + row * a.row_bytes, c, a.bits);
+    }
+    const int64_t nk = (a.Lq / a.G) * a.D;
+    for (int64_t i = i0; i < nk; i += stride) {
+        const int64_t g = i / a.D;
+        const int c = (int)(i % a.D);
+        const float* km = a.kmeta + (bh * a.ng_cap + g) * 2 * a.D;
+        if (k_scale) k_scale[bh * nk + i] = km[c];
+        if (k_zero) k_zero[bh * nk + i] = km[a.D + c];
+    }
+    const int64_t nv = a.Lq * a.nvg;
+    for (int64_t i = i0; i < nv; i += stride) {
+        const float* vm = a.vmeta + (bh * a.Lq_cap * a.nvg + i) * 2;
+        if (v_scale) v_scale[bh * nv + i] = vm[0];
+        if (v_zero) v_zero[bh * nv + i] = vm[1];
+    }
+}
+
+DeqArgs make_deq_args(const Layout& L, const DevPtrs& P, int64_t nS, int64_t Lq, int64_t r) {
+    DeqArgs a;
+    a.ksink = P.ksink;
+    a.vsink = P.vsink;
+    a.kres = P.kres;
+    a.vres = P.vres;
+    a.kcodes = P.kcodes;
+    a.vcodes = P.vcodes;
+    a.kmeta = P.kmeta;
+    a.vmeta = P.vmeta;
+    a.kout = nullptr;
+    a.vout = nullptr;
+    a.nS = nS;
+    a.Lq = Lq;
+    a.r = r;
+    a.T = nS + Lq + r;
+    a.Lq_cap = L.Lq_cap;
+    a.ng_cap = L.ng_cap;
+    a.S = L.S;
+    a.R = L.R;
+    a.D = L.D;
+    a.G = L.G;
+    a.GV = L.GV;
+    a.nvg = L.nvg;
+    a.bits = L.bits;
+    a.row_bytes = L.row_bytes;
+    return a;
+}
+
+int grid_for(int64_t work, int64_t per_block, int cap) {
+    int64_t g = (work + per_block - 1) / per_block;
+    if (g < 1) g = 1;
+    if (g > cap) g = cap;
+    return (int)g;
+}
+
+}  // namespace
+
+hipError_t launch_copy_tokens(const Layout& L, const void* src, int64_t src_tokens, int64_t src_tok0,
+                              char* dst, int64_t dst_tokens, int64_t dst_tok0, int64_t n,
+                              hipStream_t stream) {
+    if (n <= 0) return hipSuccess;
+    const int row_vec = L.D * L.esize / 16;
+    const int64_t total = L.BH * n * row_vec;
+    const int grid = grid_for(total, 256, 65535);
+    copy_tokens_kernel<<<grid, 256, 0, stream>>>(reinterpret_cast<const uint4*>(src), src_tokens,
+                                                 src_tok0, reinterpret_cast<uint4*>(dst), dst_tokens,
+                                                 dst_tok0, n, row_vec, total);
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize(const Layout& L, const DevPtrs& P, const void* src_k, const void* src_v,
+                           int64_t src_tokens, int64_t src_tok0, int64_t n_groups, int64_t dst_tok0,
+                           hipStream_t stream) {
+    if (n_groups <= 0) return hipSuccess;
+    QuantArgs a;
+    a.src_k = src_k;
+    a.src_v = src_v;
+    a.src_tokens = src_tokens;
+    a.src_tok0 = src_tok0;
+    a.dst_tok0 = dst_tok0;
+    a.D = L.D;
+    a.G = L.G;
+    a.GV = L.GV;
+    a.nvg = L.nvg;
+    a.row_bytes = L.row_bytes;
+    a.Lq_cap = L.Lq_cap;
+    a.ng_cap = L.ng_cap;
+    a.kcodes = P.kcodes;
+    a.vcodes = P.vcodes;
+    a.kmeta = P.kmeta;
+    a.vmeta = P.vmeta;
+    const size_t lds = (size_t)L.G * L.D;
+    dim3 grid((unsigned)n_groups, (unsigned)L.BH);
+#define KVQ_QLAUNCH(DT, BITS) quantize_kernel<DT, BITS><<<grid, 256, lds, stream>>>(a)
+    if (L.bits == 4) {
+        if (L.dtype == DT_F32) KVQ_QLAUNCH(DT_F32, 4);
+        else if (L.dtype == DT_BF16) KVQ_QLAUNCH(DT_BF16, 4);
+        else KVQ_QLAUNCH(DT_F16, 4);
+    } else {
+        if (L.dtype == DT_F32) KVQ_QLAUNCH(DT_F32, 2);
+        else if (L.dtype == DT_BF16) KVQ_QLAUNCH(DT_BF16, 2);
+        else KVQ_QLAUNCH(DT_F16, 2);
+    }
+#undef KVQ_QLAUNCH
+    return hipGetLastError();
+}
+
+hipError_t launch_dequantize(const Layout& L, const DevPtrs& P, int64_t nS, int64_t Lq, int64_t r,
+                             float* k_out, float* v_out, hipStream_t stream) {
+    DeqArgs a = make_deq_args(L, P, nS, Lq, r);
+    a.kout = k_out;
+    a.vout = v_out;
+    if (a.T == 0) return hipSuccess;
+    dim3 grid(grid_for(a.T * L.D, 256, 4096), (unsigned)L.BH);
+    if (L.dtype == DT_F32) dequantize_kernel<DT_F32><<<grid, 256, 0, stream>>>(a);
+    else if (L.dtype == DT_BF16) dequantize_kernel<DT_BF16><<<grid, 256, 0, stream>>>(a);
+    else dequantize_kernel<DT_F16><<<grid, 256, 0, stream>>>(a);
+    return hipGetLastError();
+}
+
+hipError_t launch_export(const Layout& L, const DevPtrs& P, int64_t Lq, uint8_t* k_codes,
+                         float* k_scale, float* k_zero, uint8_t* v_codes, float* v_scale,
+                         float* v_zero, hipStream_t stream) {
+    if (Lq == 0) return hipSuccess;
+    DeqArgs a = make_deq_args(L, P, 0, Lq, 0);
+    dim3 grid(grid_for(Lq * L.D, 256, 4096), (unsigned)L.BH);
+    export_kernel<<<grid, 256, 0, stream>>>(a, k_codes, k_scale, k_zero, v_codes, v_scale, v_zero);
+    return hipGetLastError();
+}
+
+}  // namespace kvq

@@ -1,0 +1,196 @@
+/*
+ * kvq.h -- decode attention over a low-bit (INT4 / INT2) KV cache on MI355X.
+ *
+ * The cache follows the KIVI scheme ("LLM系列：KVCache量化1 KIVI: A Tuning-Free
+ * Asymmetric 2bit Quantiz", section 1 "KIVI"):
+ *   - keys are quantized per channel, one group per G consecutive tokens;
+ *   - values are quantized per token, one group per G_V consecutive channels;
+ *   - the newest tokens sit in a full-precision residual of capacity R; when it
+ *     holds R tokens they are quantized, appended to the quantized part, and the
+ *     residual is emptied;
+ *   - optionally the first S tokens of every sequence stay full precision for
+ *     good ("attention sinks", "KV Cache的Int4量化：如何解决Attention Sink导致的量化精度
+ *     崩塌问题", section 3).
+ * Each group is quantized with asymmetric min-max parameters ("Atom: Low-bit
+ * Quantization for Efficient and Accurate LLM Serving", section 三 "核心公式"):
+ *   scale s = (max - min) / (2^n - 1)       zero z = round(-min / s)
+ *   code  q = clamp(round(x / s) + z, 0, 2^n - 1)
+ *   x'      = (q - z) * s                   (Int4 KV-cache post, section 2)
+ * all in IEEE binary32, round half to even, in exactly that operation order.
+ * A group whose scale comes out 0 (all values equal, or a range so small that
+ * range / (2^n - 1) underflows) uses s = |min| (s = 1 when min == 0), so that it
+ * reproduces exactly; a zero point of -0 is stored as +0.
+ *
+ * Decode attention computes, for every query head h of every sequence b,
+ *   out = softmax(q K'^T * sm_scale) V'      (Int4 KV-cache post, section 3)
+ * over all cached tokens of kv head h / (n_q_heads / n_kv_heads): the sinks, the
+ * dequantized tokens and the residual (KIVI notes, section 1: logits of the
+ * grouped and residual parts are concatenated before the softmax; the order of
+ * tokens does not change the result, "Resumo Técnico: LogQuant", Metodologia 4).
+ *
+ * Conventions shared by every call:
+ *   - All device memory (cache buffer, inputs, outputs, workspace) is owned by
+ *     the caller and must stay alive until the enqueued work has finished.  The
+ *     library owns only the host-side handle.  It never allocates device memory.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Every call validates its arguments on the host before anything is
+ *     enqueued; on error nothing is enqueued and the cache state is unchanged.
+ *     Work is asynchronous on `stream`; the host never waits for the device.
+ *   - Non-finite inputs, and inputs whose per-group range overflows binary32,
+ *     give undefined (but memory-safe) results.
+ *   - A handle is not thread-safe; calls on one handle must be serialized, and
+ *     all of its work must be enqueued on streams ordered with each other.
+ *   - kvq_last_error() returns a thread-local, library-owned message describing
+ *     the last failed call on the calling thread.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum kvq_status {
+    KVQ_OK = 0,
+    KVQ_ERR_INVALID_ARG = -1,      /* bad pointer, shape or config value          */
+    KVQ_ERR_UNSUPPORTED = -2,      /* valid but not supported by these kernels    */
+    KVQ_ERR_CAPACITY = -3,         /* append would exceed max_tokens              */
+    KVQ_ERR_BUFFER_TOO_SMALL = -4, /* cache buffer or workspace below the minimum */
+    KVQ_ERR_DEVICE = -5            /* a HIP runtime or launch error               */
+} kvq_status;
+
+typedef enum kvq_dtype {
+    KVQ_F32 = 0,
+    KVQ_BF16 = 1,
+    KVQ_F16 = 2
+} kvq_dtype;
+
+typedef struct kvq_config {
+    int32_t batch;        /* B  >= 1                                              */
+    int32_t n_kv_heads;   /* Hkv >= 1                                             */
+    int32_t n_q_heads;    /* Hq, a multiple of Hkv; Hq / Hkv in {1, 2, 4, 8}      */
+    int32_t head_dim;     /* D in {64, 128}                                       */
+    int32_t bits;         /* n in {2, 4}                                          */
+    int32_t k_group;      /* G: tokens per key group; a multiple of 16            */
+    int32_t v_group;      /* G_V: channels per value group; divides D, >= 16      */
+    int32_t residual;     /* R: residual capacity; a multiple of G                */
+    int32_t n_sink;       /* S >= 0: leading tokens kept at full precision        */
+    int32_t dtype;        /* kvq_dtype of K, V, q and of the sink/residual store  */
+    int64_t max_tokens;   /* capacity per sequence, >= 1                          */
+    float sm_scale;       /* softmax scale; 0 selects 1/sqrt(D)                   */
+    int32_t reserved;     /* must be 0                                            */
+} kvq_config;
+
+typedef struct kvq_cache kvq_cache; /* opaque host-side handle */
+
+/*
+ * Minimum size in bytes of the device buffer that holds a cache of `cfg`:
+ * sinks, residual, packed codes and scales/zero points for max_tokens tokens
+ * per sequence.  Errors: INVALID_ARG / UNSUPPORTED as for kvq_cache_create.
+ */
+kvq_status kvq_cache_bytes(const kvq_config* cfg, size_t* bytes);
+
+/*
+ * Create an empty cache in the caller's device buffer `dev_buf` (>= the size
+ * from kvq_cache_bytes, 256-byte aligned).  The buffer's contents need no
+ * initialisation.  *out receives the handle, to be freed with
+ * kvq_cache_destroy.  Errors: INVALID_ARG (null pointer, non-positive sizes,
+ * Hq % Hkv != 0, R % G != 0, D % G_V != 0, reserved != 0, misaligned buffer),
+ * UNSUPPORTED (bits not 2/4, D not 64/128, Hq/Hkv not 1/2/4/8, G % 16 != 0,
+ * G_V < 16), BUFFER_TOO_SMALL, DEVICE (no current HIP device).
+ */
+kvq_status kvq_cache_create(const kvq_config* cfg, void* dev_buf, size_t bytes,
+                            kvq_cache** out);
+
+/* Free a handle (NULL is accepted).  The device buffer stays the caller's. */
+kvq_status kvq_cache_destroy(kvq_cache* cache);
+
+/*
+ * Append n_new tokens to every sequence (KIVI notes, section 1: the new key
+ * and value go to the residual; the residual is quantized and appended to the
+ * grouped part when it reaches R tokens).  Equivalent, bit for bit, to n_new
+ * one-token appends: the first S tokens ever appended become sinks, each later
+ * token goes to residual slot r, and whenever r reaches R the R residual
+ * tokens are quantized (keys per channel over each run of G tokens, values per
+ * token over each run of G_V channels) and the residual is emptied, so that
+ * 0 <= r < R after every call.  Complete R-token blocks of a bulk append are
+ * quantized straight from the input.
+ *   k, v : device, [B, Hkv, n_new, D] contiguous, in cfg.dtype.
+ * n_new == 0 is a no-op.  Errors: INVALID_ARG (null, n_new < 0),
+ * CAPACITY (tokens + n_new > max_tokens), DEVICE.
+ */
+kvq_status kvq_append(kvq_cache* cache, const void* k, const void* v, int64_t n_new,
+                      void* stream);
+
+/*
+ * Size in bytes of the decode workspace for this cache (split partials and
+ * completion counters; constant over the cache's lifetime).
+ */
+kvq_status kvq_decode_workspace_bytes(const kvq_cache* cache, size_t* bytes);
+
+/*
+ * Decode attention for one query per (sequence, query head):
+ *   out[b, h, :] = softmax(q[b, h] . K'^T * sm_scale) V'
+ *   lse[b, h]    = log(sum(exp(q[b, h] . K'^T * sm_scale)))   (natural log)
+ * over every cached token of kv head h / (Hq / Hkv).  The keys and values of
+ * the quantized part are dequantized on the fly; the token range is split
+ * across workgroups and the partial softmax states are merged with a
+ * log-sum-exp combine.
+ *   q   : device, [B, Hq, D] in cfg.dtype.
+ *   out : device, [B, Hq, D] fp32.       lse : device, [B, Hq] fp32, or NULL.
+ *   ws  : device workspace of >= kvq_decode_workspace_bytes bytes, 256-byte
+ *         aligned, ZERO-FILLED before its first use; every call leaves its
+ *         counters zero again.  Calls that share a workspace must not overlap.
+ * The result matches the binary64 definition to within about 1e-4 absolute for
+ * the documented workloads.  Errors: INVALID_ARG (null q/out/ws, empty cache),
+ * BUFFER_TOO_SMALL (ws), DEVICE.
+ */
+kvq_status kvq_decode_attention(kvq_cache* cache, const void* q, float* out, float* lse,
+                                void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Dequantize the whole cache to fp32 in chronological token order (sinks, then
+ * the quantized tokens as x' = (q - z) * s, then the residual); the round trip
+ * of the Int4 KV-cache post's section 5.1 `quantize` helper.
+ *   k_out, v_out : device, [B, Hkv, n_tokens, D] fp32.
+ * Errors: INVALID_ARG (null), DEVICE.
+ */
+kvq_status kvq_dequantize(const kvq_cache* cache, float* k_out, float* v_out, void* stream);
+
+/*
+ * Export the quantized part in a canonical, unpacked layout (for bit-exact
+ * comparison; independent of the internal packing):
+ *   k_codes, v_codes : device uint8 [B, Hkv, n_quant, D]
+ *   k_scale, k_zero  : device fp32  [B, Hkv, n_quant / G, D]
+ *   v_scale, v_zero  : device fp32  [B, Hkv, n_quant, D / G_V]
+ * Any pointer may be NULL to skip that array.  Errors: DEVICE.
+ */
+kvq_status kvq_export(const kvq_cache* cache, uint8_t* k_codes, float* k_scale, float* k_zero,
+                      uint8_t* v_codes, float* v_scale, float* v_zero, void* stream);
+
+/*
+ * Host-side counters (no device access): total tokens per sequence, sinks
+ * held, quantized tokens and residual tokens.  Any pointer may be NULL.
+ */
+kvq_status kvq_cache_state(const kvq_cache* cache, int64_t* n_tokens, int64_t* n_sink,
+                           int64_t* n_quant, int64_t* n_resid);
+
+/*
+ * Tuning and testing knob: tokens per decode split of the quantized part
+ * (rounded up to whole key groups).  0 restores the automatic choice.  The
+ * result does not depend on the split, up to floating-point reassociation.
+ * Errors: INVALID_ARG (negative).
+ */
+kvq_status kvq_set_split_tokens(kvq_cache* cache, int64_t tokens_per_split);
+
+/* Message of the last failed call on this thread ("" if none).  Library-owned. */
+const char* kvq_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

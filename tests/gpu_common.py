@@ -1,0 +1,107 @@
+"""Shared helpers of the GPU tests: drive a workload through the C-ABI on cuda:0 and
+compare with the CPU oracle.
+
+Bars (the target of this path): codes, scales and zero points bit-exact; attention
+outputs within ATOL = 1e-3 absolute of the binary64 oracle, for every output of
+every attention call checked.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+from workloads.torch_io import TORCH_DTYPES, to_torch
+
+ATOL = 1e-3
+
+gpu = pytest.mark.gpu
+
+
+def require_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def log(msg: str):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def make_cache(w: wl.Workload, max_tokens: int | None = None, **over):
+    from bit_quantized_kv_kvq_amd import Cache
+    kw = dict(batch=w.batch, n_kv_heads=w.n_kv_heads, n_q_heads=w.n_q_heads,
+              head_dim=w.head_dim, bits=w.bits, k_group=w.k_group, v_group=w.v_group,
+              residual=w.residual, n_sink=w.n_sink, dtype=TORCH_DTYPES[w.dtype],
+              max_tokens=max_tokens or w.max_tokens, device=torch.device("cuda:0"))
+    kw.update(over)
+    return Cache(**kw)
+
+
+class WorkloadRun:
+    """Uploads a workload and steps through its schedule on the GPU."""
+
+    def __init__(self, w: wl.Workload, cache=None):
+        self.w = w
+        self.dev = torch.device("cuda:0")
+        self.cache = cache or make_cache(w)
+        Kp, Vp = wl.prefill_batch(w)
+        self.cache.append(to_torch(Kp, w.dtype, self.dev), to_torch(Vp, w.dtype, self.dev))
+        del Kp, Vp
+        Ks, Vs = wl.steps_batch(w)
+        self.Ks = to_torch(Ks, w.dtype, self.dev)
+        self.Vs = to_torch(Vs, w.dtype, self.dev)
+        self.Q = to_torch(wl.queries_batch(w), w.dtype, self.dev)
+        self.n_steps = 0
+
+    def append_step(self, s: int):
+        self.cache.append(self.Ks[s][:, :, None].contiguous(), self.Vs[s][:, :, None].contiguous())
+        self.n_steps = s + 1
+
+    def attend(self, qi: int):
+        out, lse = self.cache.decode(self.Q[qi].contiguous())
+        return out, lse
+
+    def run(self, on_attend):
+        """on_attend(n_steps, qi, out, lse) after every attention call of the schedule."""
+        for op, idx in wl.schedule(self.w):
+            if op == "append":
+                self.append_step(idx)
+            else:
+                out, lse = self.attend(idx)
+                on_attend(self.n_steps, idx, out, lse)
+
+
+def export_cpu(cache):
+    torch.cuda.synchronize()
+    ex = cache.export()
+    torch.cuda.synchronize()
+    return {k: v.cpu().numpy() for k, v in ex.items()}
+
+
+def assert_export_slice_matches(ex, st, b: int, kvh: int):
+    """Bit-exact codes, scales and zero points of slice (b, kvh) vs an oracle state."""
+    Lq = st["n_quant"]
+    assert ex["k_codes"].shape[2] == Lq
+    np.testing.assert_array_equal(ex["k_codes"][b, kvh], st["k_codes"])
+    np.testing.assert_array_equal(ex["v_codes"][b, kvh], st["v_codes"])
+    for name in ("k_scale", "k_zero", "v_scale", "v_zero"):
+        got = np.ascontiguousarray(ex[name][b, kvh]).view(np.uint32)
+        want = np.ascontiguousarray(st[name]).view(np.uint32)
+        np.testing.assert_array_equal(got, want, err_msg=name)
+
+
+def check_outputs(w, out_cpu, lse_cpu, b: int, kvh: int, n_steps: int, qi: int):
+    """Max abs error of out/lse of every query head of (b, kvh) vs the oracle."""
+    eo, el = oracle.expected_outputs(w, b, kvh, n_steps, qi)
+    g = w.gqa
+    got = out_cpu[b, kvh * g:(kvh + 1) * g].astype(np.float64)
+    err = float(np.abs(got - eo).max())
+    lerr = float(np.abs(lse_cpu[b, kvh * g:(kvh + 1) * g].astype(np.float64) - el).max())
+    assert err <= ATOL, (w.name, b, kvh, n_steps, qi, err)
+    assert lerr <= ATOL, (w.name, b, kvh, n_steps, qi, lerr)
+    return err

@@ -1,0 +1,230 @@
+"""GPU tests of the boundary's semantics and edge cases, through the C-ABI."""
+import numpy as np
+import pytest
+import torch
+
+import bit_quantized_kv_kvq_amd as kvq
+import oracle
+import workloads as wl
+from tests.gpu_common import (ATOL, assert_export_slice_matches, export_cpu, gpu, log,
+                              make_cache, require_gpu)
+from workloads.torch_io import TORCH_DTYPES, to_torch
+
+pytestmark = gpu
+
+DEV = torch.device("cuda:0")
+
+
+def _w(**kw):
+    base = wl.get("C2").replace(name="edge", batch=2, n_kv_heads=2, n_q_heads=2, prefill=0,
+                                steps=0, k_group=32, v_group=32, residual=64)
+    return base.replace(**kw)
+
+
+def _tokens(w, n, seed, scale=1.0, offset=0.0):
+    x = wl.random_tokens(seed, (w.batch, w.n_kv_heads, n, w.head_dim), w.dtype, scale, offset)
+    return x
+
+
+def _oracle_states(w, K, V):
+    """Oracle states of every slice for host storage arrays K, V [B, Hkv, n, D]."""
+    kf = wl.storage_to_f32(K, w.dtype)
+    vf = wl.storage_to_f32(V, w.dtype)
+    return {(b, h): oracle.build_slice(kf[b, h], vf[b, h], head_dim=w.head_dim, bits=w.bits,
+                                       k_group=w.k_group, v_group=w.v_group,
+                                       residual=w.residual, n_sink=w.n_sink)
+            for b in range(w.batch) for h in range(w.n_kv_heads)}
+
+
+def _attend_and_check(w, cache, K, V, seed=5):
+    q = wl.random_tokens(seed, (w.batch, w.n_q_heads, w.head_dim), w.dtype)
+    out, lse = cache.decode(to_torch(q, w.dtype, DEV))
+    torch.cuda.synchronize()
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    sts = _oracle_states(w, K, V)
+    qf = wl.storage_to_f32(q, w.dtype)
+    scale = oracle.default_scale(w.head_dim)
+    err = 0.0
+    for (b, h), st in sts.items():
+        Kd, Vd = oracle.dequant_slice(st)
+        for j in range(w.gqa):
+            hq = h * w.gqa + j
+            eo, el = oracle.attention(qf[b, hq], Kd, Vd, scale)
+            err = max(err, float(np.abs(out[b, hq] - eo).max()), abs(float(lse[b, hq]) - el))
+    assert err <= ATOL, err
+    return sts, err
+
+
+@pytest.mark.parametrize("kw", [
+    dict(),                                             # bf16 MHA INT4
+    dict(bits=2),
+    dict(dtype="f16"),
+    dict(dtype="f32", head_dim=64, v_group=16),
+    dict(n_q_heads=4),                                  # GQA 2
+    dict(n_q_heads=16, bits=2),                         # GQA 8
+    dict(n_q_heads=16, bits=4, head_dim=64),            # GQA 8, D64
+    dict(n_sink=3),
+    dict(k_group=64, residual=128, v_group=128),
+    dict(k_group=96, residual=192, v_group=64),         # group not a power of two
+])
+@pytest.mark.parametrize("n", [1, 63, 64, 65, 200])
+def test_variants_against_oracle(kw, n):
+    require_gpu()
+    w = _w(**kw)
+    log("case %s n=%d" % (kw, n))
+    cache = make_cache(w, max_tokens=256)
+    K, V = _tokens(w, n, 11, 2.0), _tokens(w, n, 12)
+    cache.append(to_torch(K, w.dtype, DEV), to_torch(V, w.dtype, DEV))
+    sts, err = _attend_and_check(w, cache, K, V)
+    ex = export_cpu(cache)
+    for (b, h), st in sts.items():
+        assert_export_slice_matches(ex, st, b, h)
+
+
+def test_bulk_append_equals_one_token_appends():
+    require_gpu()
+    w = _w(n_sink=2, bits=2)
+    n = 3 * 64 + 17
+    K, V = _tokens(w, n, 21, 3.0), _tokens(w, n, 22)
+    a = make_cache(w, max_tokens=n)
+    a.append(to_torch(K, w.dtype, DEV), to_torch(V, w.dtype, DEV))
+    b = make_cache(w, max_tokens=n)
+    # irregular chunking: 1, 5, 1, 70, ...
+    i, sizes = 0, [1, 5, 1, 70, 2, 64, 1]
+    j = 0
+    while i < n:
+        m = min(sizes[j % len(sizes)], n - i)
+        b.append(to_torch(np.ascontiguousarray(K[:, :, i:i + m]), w.dtype, DEV),
+                 to_torch(np.ascontiguousarray(V[:, :, i:i + m]), w.dtype, DEV))
+        i += m
+        j += 1
+    assert a.state() == b.state()
+    ea, eb = export_cpu(a), export_cpu(b)
+    for k in ea:
+        np.testing.assert_array_equal(ea[k], eb[k])
+    ka, va = a.dequantize()
+    kb, vb = b.dequantize()
+    assert torch.equal(ka, kb) and torch.equal(va, vb)
+
+
+def test_adversarial_groups_bit_exact():
+    require_gpu()
+    w = _w(dtype="f32", head_dim=64, v_group=16, k_group=32, residual=32, bits=4)
+    n = 32 * 6
+    rng = np.random.default_rng(3)
+    K = rng.standard_normal((w.batch, w.n_kv_heads, n, 64)).astype(np.float32)
+    V = rng.standard_normal((w.batch, w.n_kv_heads, n, 64)).astype(np.float32)
+    K[0, 0, 0:32, :] = 0.7              # constant key groups
+    K[0, 0, 32:64, 5] = -0.0            # signed zeros
+    K[0, 0, 32:64, 6] = np.where(np.arange(32) % 2, 0.0, -0.0)
+    K[0, 1, 64:96, :] = (rng.standard_normal((32, 64)) * 1e-40).astype(np.float32)  # subnormals
+    K[1, 0, 96:128, :] = 5.0 + rng.uniform(0, 1, (32, 64)).astype(np.float32)       # one-signed
+    K[1, 1, 128:160, :] = (rng.integers(-3, 4, (32, 64)) * 0.25).astype(np.float32)  # ties
+    K[1, 1, 160:192, 3] = np.float32(1.4e-45) * np.arange(32)  # tiny range, scale underflow
+    V[0, 0, :, 0:16] = -2.5             # constant value groups
+    V[0, 1, :, 16:32] = 0.0
+    V[1, 0, :, 32:48] = (rng.standard_normal((n, 16)) * 1e-42).astype(np.float32)
+    V[1, 1, 5, :] = np.float32(1e30)
+    V[1, 1, 6, :] = np.float32(-1e30)
+    cache = make_cache(w, max_tokens=n)
+    cache.append(to_torch(K, "f32", DEV), to_torch(V, "f32", DEV))
+    ex = export_cpu(cache)
+    for (b, h), st in _oracle_states(w, K, V).items():
+        assert_export_slice_matches(ex, st, b, h)
+    kd, vd = cache.dequantize()
+    kd, vd = kd.cpu().numpy(), vd.cpu().numpy()
+    for (b, h), st in _oracle_states(w, K, V).items():
+        Ko, Vo = oracle.dequant_slice(st)
+        np.testing.assert_array_equal(kd[b, h].view(np.uint32), Ko.view(np.uint32))
+        np.testing.assert_array_equal(vd[b, h].view(np.uint32), Vo.view(np.uint32))
+
+
+def test_state_machine_and_empty_cases():
+    require_gpu()
+    w = _w(n_sink=4, residual=64, k_group=32)
+    cache = make_cache(w, max_tokens=200)
+    q = to_torch(wl.random_tokens(1, (w.batch, w.n_q_heads, w.head_dim), w.dtype), w.dtype, DEV)
+    # empty cache: attention is an argument error and enqueues nothing
+    with pytest.raises(kvq.KVQError) as ei:
+        cache.decode(q)
+    assert ei.value.status == kvq.KVQ_ERR_INVALID_ARG
+    # n_new == 0 is a no-op
+    z = torch.empty((w.batch, w.n_kv_heads, 0, w.head_dim), dtype=TORCH_DTYPES[w.dtype], device=DEV)
+    cache.append(z, z)
+    assert cache.state() == (0, 0, 0, 0)
+    K, V = _tokens(w, 200, 31), _tokens(w, 200, 32)
+    done = 0
+    for m in [2, 2, 3, 60, 1, 64, 68]:   # sinks only, sinks + residual, flushes, ...
+        cache.append(to_torch(np.ascontiguousarray(K[:, :, done:done + m]), w.dtype, DEV),
+                     to_torch(np.ascontiguousarray(V[:, :, done:done + m]), w.dtype, DEV))
+        done += m
+        N = done
+        nS = min(N, 4)
+        assert cache.state() == (N, nS, 64 * ((N - nS) // 64), (N - nS) % 64)
+        _attend_and_check(w, cache, K[:, :, :done], V[:, :, :done], seed=done)
+    # capacity: one more token is rejected and changes nothing
+    one = to_torch(np.ascontiguousarray(K[:, :, :1]), w.dtype, DEV)
+    with pytest.raises(kvq.KVQError) as ei:
+        cache.append(one, one)
+    assert ei.value.status == kvq.KVQ_ERR_CAPACITY
+    assert cache.state() == (200, 4, 192, 4)
+    _attend_and_check(w, cache, K, V, seed=99)
+
+
+def test_workspace_and_argument_errors():
+    require_gpu()
+    w = _w()
+    cache = make_cache(w, max_tokens=128)
+    K, V = _tokens(w, 70, 41), _tokens(w, 70, 42)
+    cache.append(to_torch(K, w.dtype, DEV), to_torch(V, w.dtype, DEV))
+    q = to_torch(wl.random_tokens(2, (w.batch, w.n_q_heads, w.head_dim), w.dtype), w.dtype, DEV)
+    out = torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=torch.float32, device=DEV)
+    with pytest.raises(kvq.KVQError) as ei:
+        kvq.kvq_decode_attention(cache.handle, q.data_ptr(), out.data_ptr(), 0, cache._ws_ptr,
+                                 cache.ws_bytes - 1, torch.cuda.current_stream().cuda_stream)
+    assert ei.value.status == kvq.KVQ_ERR_BUFFER_TOO_SMALL
+    with pytest.raises(kvq.KVQError) as ei:
+        kvq.kvq_decode_attention(cache.handle, q.data_ptr(), out.data_ptr(), 0, cache._ws_ptr + 16,
+                                 cache.ws_bytes, torch.cuda.current_stream().cuda_stream)
+    assert ei.value.status == kvq.KVQ_ERR_INVALID_ARG
+    with pytest.raises(kvq.KVQError) as ei:
+        kvq.kvq_append(cache.handle, K.ctypes.data * 0, 0, 1, 0)
+    assert ei.value.status == kvq.KVQ_ERR_INVALID_ARG
+    with pytest.raises(kvq.KVQError) as ei:
+        kvq.kvq_append(cache.handle, 16, 16, -1, 0)
+    assert ei.value.status == kvq.KVQ_ERR_INVALID_ARG
+    assert cache.state() == (70, 0, 64, 6)
+    # lse is optional
+    o2, l2 = cache.decode(q, with_lse=False)
+    assert l2 is None
+    o1, _ = cache.decode(q)
+    assert torch.equal(o1, o2)
+    _attend_and_check(w, cache, K, V, seed=2)
+
+
+def test_sm_scale_override():
+    require_gpu()
+    w = _w()
+    K, V = _tokens(w, 100, 51), _tokens(w, 100, 52)
+    a = make_cache(w, max_tokens=100, sm_scale=0.3)
+    a.append(to_torch(K, w.dtype, DEV), to_torch(V, w.dtype, DEV))
+    q = wl.random_tokens(7, (w.batch, w.n_q_heads, w.head_dim), w.dtype)
+    out, lse = a.decode(to_torch(q, w.dtype, DEV))
+    out = out.cpu().numpy()
+    qf = wl.storage_to_f32(q, w.dtype)
+    for (b, h), st in _oracle_states(w, K, V).items():
+        Kd, Vd = oracle.dequant_slice(st)
+        eo, _ = oracle.attention(qf[b, h], Kd, Vd, float(np.float32(0.3)))
+        assert np.abs(out[b, h] - eo).max() <= ATOL
+
+
+def test_two_caches_share_one_stream():
+    require_gpu()
+    w = _w(bits=2)
+    K, V = _tokens(w, 150, 61), _tokens(w, 150, 62)
+    a = make_cache(w, max_tokens=150)
+    b = make_cache(w.replace(bits=4), max_tokens=150)
+    a.append(to_torch(K, w.dtype, DEV), to_torch(V, w.dtype, DEV))
+    b.append(to_torch(K, w.dtype, DEV), to_torch(V, w.dtype, DEV))
+    _attend_and_check(w, a, K, V)
+    _attend_and_check(w.replace(bits=4), b, K, V)

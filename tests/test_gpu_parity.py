@@ -1,0 +1,163 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C-ABI.
+
+Small versions of every workload (all slices, every attention call, sizes that
+span several tiles and splits with a ragged residual tail and at least one flush)
+and the full-size workloads in the launch configuration the benchmark times
+(sampled slices checked one by one).  Codes, scales and zero points must be
+bit-exact; attention outputs and log-sum-exp within 1e-3 absolute.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+from tests.gpu_common import (ATOL, WorkloadRun, assert_export_slice_matches, check_outputs,
+                              export_cpu, gpu, log, make_cache, require_gpu)
+
+pytestmark = gpu
+
+SMALL = {
+    "tiny": wl.get("tiny"),
+    "llama7b_small": wl.get("C2").replace(name="llama7b_small", batch=2, n_kv_heads=3,
+                                          n_q_heads=3, prefill=1000, steps=30),
+    "kivi2_small": wl.get("C3").replace(name="kivi2_small", batch=2, n_kv_heads=3, n_q_heads=3,
+                                        prefill=700, steps=40),
+    "gqa_small": wl.get("C4").replace(name="gqa_small", batch=2, n_kv_heads=2, n_q_heads=8,
+                                      prefill=1200, steps=20),
+    "sink_small": wl.get("C5").replace(name="sink_small", batch=1, n_kv_heads=2, n_q_heads=8,
+                                       prefill=1000, steps=40),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_workload_all_slices_every_step(name):
+    require_gpu()
+    w = SMALL[name]
+    log("case %s: %s" % (name, w))
+    run = WorkloadRun(w)
+    # after the bulk prefill: every slice bit-exact
+    ex = export_cpu(run.cache)
+    for b in range(w.batch):
+        for h in range(w.n_kv_heads):
+            assert_export_slice_matches(ex, oracle.slice_state(w, b, h, 0), b, h)
+    worst = [0.0]
+    flush_checked = []
+
+    def on_attend(n_steps, qi, out, lse):
+        torch.cuda.synchronize()
+        o, l = out.cpu().numpy(), lse.cpu().numpy()
+        n_tok, nS, Lq, r = run.cache.state()
+        N = w.prefill + n_steps
+        assert nS == min(N, w.n_sink)
+        assert Lq == w.residual * ((N - nS) // w.residual) and r == (N - nS) % w.residual
+        for b in range(w.batch):
+            for h in range(w.n_kv_heads):
+                worst[0] = max(worst[0], check_outputs(w, o, l, b, h, n_steps, qi))
+        if n_steps > 0 and r == 0 and n_steps not in flush_checked:
+            flush_checked.append(n_steps)
+            exf = export_cpu(run.cache)
+            for b in range(w.batch):
+                for h in range(w.n_kv_heads):
+                    assert_export_slice_matches(exf, oracle.slice_state(w, b, h, n_steps), b, h)
+
+    run.run(on_attend)
+    ex = export_cpu(run.cache)
+    for b in range(w.batch):
+        for h in range(w.n_kv_heads):
+            assert_export_slice_matches(ex, oracle.slice_state(w, b, h, w.steps), b, h)
+    log("case %s: max |out - oracle| = %.3g, flushes checked at steps %s" % (name, worst[0], flush_checked))
+
+
+@pytest.mark.parametrize("name", ["llama7b_small", "sink_small", "tiny"])
+def test_dequantize_bit_exact(name):
+    require_gpu()
+    w = SMALL[name]
+    run = WorkloadRun(w)
+    for s in range(min(w.steps, 7)):
+        run.append_step(s)
+    K, V = run.cache.dequantize()
+    torch.cuda.synchronize()
+    K, V = K.cpu().numpy(), V.cpu().numpy()
+    for b in range(w.batch):
+        for h in range(w.n_kv_heads):
+            Ko, Vo = oracle.dequant_slice(oracle.slice_state(w, b, h, run.n_steps))
+            np.testing.assert_array_equal(K[b, h].view(np.uint32), Ko.view(np.uint32))
+            np.testing.assert_array_equal(V[b, h].view(np.uint32), Vo.view(np.uint32))
+
+
+@pytest.mark.parametrize("name", ["llama7b_small", "gqa_small", "sink_small", "kivi2_small"])
+def test_split_count_invariance(name):
+    require_gpu()
+    w = SMALL[name]
+    run = WorkloadRun(w)
+    run.append_step(0)
+    q = run.Q[0].contiguous()
+    ref, ref_lse = run.cache.decode(q)
+    ref, ref_lse = ref.clone(), ref_lse.clone()
+    for tokens in [w.k_group, 2 * w.k_group, 3 * w.k_group, 5 * w.k_group, 1 << 30]:
+        run.cache.set_split_tokens(tokens)
+        out, lse = run.cache.decode(q)
+        torch.cuda.synchronize()
+        d = (out - ref).abs().max().item()
+        dl = (lse - ref_lse).abs().max().item()
+        assert d <= 1e-5 and dl <= 1e-5, (tokens, d, dl)
+    run.cache.set_split_tokens(0)
+    out, _ = run.cache.decode(q)
+    assert torch.equal(out, ref)
+
+
+def test_repeat_calls_are_bitwise_deterministic():
+    require_gpu()
+    w = SMALL["gqa_small"]
+    run = WorkloadRun(w)
+    run.append_step(0)
+    q = run.Q[0].contiguous()
+    a, la = run.cache.decode(q)
+    a, la = a.clone(), la.clone()
+    for _ in range(5):
+        b, lb = run.cache.decode(q)
+        assert torch.equal(a, b) and torch.equal(la, lb)
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads, sampled slices
+# ---------------------------------------------------------------------------
+
+FULL = {
+    "llama7b_mha_int4": ([(0, 0), (3, 17), (7, 31)], None),
+    "kivi2_long_batch": ([(0, 0), (31, 31)], None),
+    "gqa_32k_int4": ([(0, 0), (15, 7)], None),
+    "long_128k_sink_int2": ([(0, 0), (0, 7)], {0, 3, 4, 7}),
+}
+
+
+@pytest.mark.parametrize("name", list(FULL))
+def test_full_size_sampled(name):
+    require_gpu()
+    w = wl.get(name)
+    samples, steps_to_check = FULL[name]
+    log("full-size case %s: %s" % (name, w.description))
+    run = WorkloadRun(w)
+    log("  prefill uploaded and quantized")
+    ex = export_cpu(run.cache)
+    for b, h in samples:
+        assert_export_slice_matches(ex, oracle.slice_state(w, b, h, 0), b, h)
+    del ex
+    last_q = wl.n_queries(w) - 1
+    checked = []
+
+    def on_attend(n_steps, qi, out, lse):
+        want = qi in (0, last_q) or (steps_to_check is not None and qi in steps_to_check)
+        if not want:
+            return
+        torch.cuda.synchronize()
+        o, l = out.cpu().numpy(), lse.cpu().numpy()
+        for b, h in samples:
+            checked.append(check_outputs(w, o, l, b, h, n_steps, qi))
+
+    run.run(on_attend)
+    ex = export_cpu(run.cache)
+    for b, h in samples:
+        assert_export_slice_matches(ex, oracle.slice_state(w, b, h, w.steps), b, h)
+    log("  %s: %d sampled outputs, max err %.3g" % (name, len(checked), max(checked)))

@@ -128,8 +128,9 @@ def get(name: str) -> Workload:
 def round_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """fp32 -> bf16 bit pattern (uint16), round to nearest even.  Finite input."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    u = x.view(np.uint32)
+    # no uint32 overflow for finite inputs: the largest finite pattern is 0xff7fffff
+    u = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
     return u.astype(np.uint16)
 
 
