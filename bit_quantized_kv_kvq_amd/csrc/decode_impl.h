@@ -78,6 +78,14 @@ __device__ __forceinline__ float group_sum(float v) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// device-scope store / load of split partials exchanged between workgroups
+__device__ __forceinline__ void publish(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float fetch(const float* p) {
+    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 template <int LW>
 struct Vec;
 template <>
@@ -109,7 +117,9 @@ __device__ __forceinline__ void unpack(const uint32_t (&w)[LW], float (&f)[LW * 
     for (int d = 0; d < LW; ++d) {
 #pragma unroll
         for (int sub = 0; sub < CPD / 4; ++sub) {
-            const uint32_t x = (w[d] >> (BITS * sub)) & MASK;
+            // opaque mask so that each byte converts with one v_cvt_f32_ubyteN
+            uint32_t x;
+            asm("v_and_b32 %0, %1, %2" : "=v"(x) : "i"(MASK), "v"(w[d] >> (BITS * sub)));
             f[d * CPD + 4 * sub + 0] = (float)(x & 0xFFu);
             f[d * CPD + 4 * sub + 1] = (float)((x >> 8) & 0xFFu);
             f[d * CPD + 4 * sub + 2] = (float)((x >> 16) & 0xFFu);
@@ -457,25 +467,32 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
             if (c == 0 && a.lse) a.lse[qrow0 + h] = (M + __log2f(L)) * 0.69314718055994530942f;
         } else {
             const int64_t pidx = (bh * a.nsplit_cap + split) * GQ + h;
-            a.part_acc[pidx * D + c] = A;
+            publish(&a.part_acc[pidx * D + c], A);
             if (c == 0) {
-                a.part_ml[pidx * 2] = M;
-                a.part_ml[pidx * 2 + 1] = L;
+                publish(&a.part_ml[pidx * 2], M);
+                publish(&a.part_ml[pidx * 2 + 1], L);
             }
         }
     }
     if (single) return;
 
-    // last workgroup of this slice merges all splits (log-sum-exp combine)
-    __threadfence();
+    // Last workgroup of this slice merges all splits (log-sum-exp combine).
+    // The partials were written with device-scope stores, which write through the
+    // XCD's L2; every wave waits until its stores are acknowledged, then one
+    // thread counts the arrival.  The last arrival reads the partials back with
+    // device-scope loads.  No L2 write-back or invalidate is needed because all
+    // data exchanged between workgroups moves through device-scope accesses.
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __syncthreads();
     if (tid == 0) {
-        const unsigned prev = atomicAdd(&a.counters[bh], 1u);
-        sm.last = (prev == (unsigned)(a.nsplit - 1));
+        const unsigned prev =
+            __hip_atomic_fetch_add(&a.counters[bh], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        sm.last = prev == (unsigned)(a.nsplit - 1);
     }
     __syncthreads();
     if (!sm.last) return;
-    __threadfence();
 
     const int ns = a.nsplit;
     const float* pml = a.part_ml + bh * a.nsplit_cap * GQ * 2;
@@ -483,13 +500,13 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
     // per-head max and sum over splits: head h handled by wave h % kWaves
     for (int h = wave; h < GQ; h += kWaves) {
         float M = -INFINITY;
-        for (int i = lane; i < ns; i += 64) M = fmaxf(M, __builtin_nontemporal_load(&pml[(i * GQ + h) * 2]));
+        for (int i = lane; i < ns; i += 64) M = fmaxf(M, fetch(&pml[(i * GQ + h) * 2]));
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) M = fmaxf(M, __shfl_xor(M, off));
         float L = 0.0f;
         for (int i = lane; i < ns; i += 64) {
-            const float mi = __builtin_nontemporal_load(&pml[(i * GQ + h) * 2]);
-            const float li = __builtin_nontemporal_load(&pml[(i * GQ + h) * 2 + 1]);
+            const float mi = fetch(&pml[(i * GQ + h) * 2]);
+            const float li = fetch(&pml[(i * GQ + h) * 2 + 1]);
             const float w = (mi == -INFINITY) ? 0.0f : fast_exp2(mi - M);
             sm.cw[i * GQ + h] = w;
             L = fmaf(li, w, L);
@@ -506,17 +523,17 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
         float A0 = 0.0f, A1 = 0.0f, A2 = 0.0f, A3 = 0.0f;
         int i = 0;
         for (; i + 4 <= ns; i += 4) {
-            A0 = fmaf(__builtin_nontemporal_load(&pacc[((i + 0) * GQ + h) * D + c]), sm.cw[(i + 0) * GQ + h], A0);
-            A1 = fmaf(__builtin_nontemporal_load(&pacc[((i + 1) * GQ + h) * D + c]), sm.cw[(i + 1) * GQ + h], A1);
-            A2 = fmaf(__builtin_nontemporal_load(&pacc[((i + 2) * GQ + h) * D + c]), sm.cw[(i + 2) * GQ + h], A2);
-            A3 = fmaf(__builtin_nontemporal_load(&pacc[((i + 3) * GQ + h) * D + c]), sm.cw[(i + 3) * GQ + h], A3);
+            A0 = fmaf(fetch(&pacc[((i + 0) * GQ + h) * D + c]), sm.cw[(i + 0) * GQ + h], A0);
+            A1 = fmaf(fetch(&pacc[((i + 1) * GQ + h) * D + c]), sm.cw[(i + 1) * GQ + h], A1);
+            A2 = fmaf(fetch(&pacc[((i + 2) * GQ + h) * D + c]), sm.cw[(i + 2) * GQ + h], A2);
+            A3 = fmaf(fetch(&pacc[((i + 3) * GQ + h) * D + c]), sm.cw[(i + 3) * GQ + h], A3);
         }
-        for (; i < ns; ++i) A0 = fmaf(__builtin_nontemporal_load(&pacc[(i * GQ + h) * D + c]), sm.cw[i * GQ + h], A0);
+        for (; i < ns; ++i) A0 = fmaf(fetch(&pacc[(i * GQ + h) * D + c]), sm.cw[i * GQ + h], A0);
         const float L = sm.cL[h];
         a.out[(qrow0 + h) * D + c] = ((A0 + A1) + (A2 + A3)) / L;
         if (c == 0 && a.lse) a.lse[qrow0 + h] = (sm.cM[h] + __log2f(L)) * 0.69314718055994530942f;
     }
-    if (tid == 0) atomicExch(&a.counters[bh], 0u);
+    if (tid == 0) __hip_atomic_store(&a.counters[bh], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace dec

@@ -225,8 +225,9 @@ kvq_status kvq_append(kvq_cache* c, const void* k, const void* v, int64_t n_new,
     // 1. sinks
     if (c->nS < L.S && rem > 0) {
         const int64_t take = std::min<int64_t>(L.S - c->nS, rem);
-        if ((st = check_hip(launch_copy_tokens(L, k, n_new, src, c->P.ksink, L.S, c->nS, take, s), "append")) ||
-            (st = check_hip(launch_copy_tokens(L, v, n_new, src, c->P.vsink, L.S, c->nS, take, s), "append")))
+        if ((st = check_hip(launch_copy_tokens(L, k, v, n_new, src, c->P.ksink, c->P.vsink, L.S, c->nS,
+                                               take, s),
+                            "append")))
             return st;
         c->nS += take;
         src += take;
@@ -235,8 +236,9 @@ kvq_status kvq_append(kvq_cache* c, const void* k, const void* v, int64_t n_new,
     // 2. top up a partly filled residual; flush it when it reaches R
     if (rem > 0 && c->r > 0) {
         const int64_t take = std::min<int64_t>(L.R - c->r, rem);
-        if ((st = check_hip(launch_copy_tokens(L, k, n_new, src, c->P.kres, L.R, c->r, take, s), "append")) ||
-            (st = check_hip(launch_copy_tokens(L, v, n_new, src, c->P.vres, L.R, c->r, take, s), "append")))
+        if ((st = check_hip(launch_copy_tokens(L, k, v, n_new, src, c->P.kres, c->P.vres, L.R, c->r, take,
+                                               s),
+                            "append")))
             return st;
         c->r += take;
         src += take;
@@ -261,8 +263,8 @@ kvq_status kvq_append(kvq_cache* c, const void* k, const void* v, int64_t n_new,
     }
     // 4. the remainder starts a new residual
     if (rem > 0) {
-        if ((st = check_hip(launch_copy_tokens(L, k, n_new, src, c->P.kres, L.R, 0, rem, s), "append")) ||
-            (st = check_hip(launch_copy_tokens(L, v, n_new, src, c->P.vres, L.R, 0, rem, s), "append")))
+        if ((st = check_hip(launch_copy_tokens(L, k, v, n_new, src, c->P.kres, c->P.vres, L.R, 0, rem, s),
+                            "append")))
             return st;
         c->r = rem;
     }

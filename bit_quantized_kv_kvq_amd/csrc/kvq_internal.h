@@ -79,12 +79,12 @@ __device__ inline float load_as_f32(const void* base, int64_t idx) {
 // launch interfaces (defined in the .hip sources)
 // ---------------------------------------------------------------------------
 
-// Copy n tokens of every slice from src[bh][src_tok0 + i][D] (src holds
-// src_tokens tokens per slice) to dst[bh][dst_tok0 + i][D] (dst holds
-// dst_tokens per slice).  Storage dtype preserved.
-hipError_t launch_copy_tokens(const Layout& L, const void* src, int64_t src_tokens, int64_t src_tok0,
-                              char* dst, int64_t dst_tokens, int64_t dst_tok0, int64_t n,
-                              hipStream_t stream);
+// Copy n tokens of every slice of K and V from src_*[bh][src_tok0 + i][D] (src
+// holds src_tokens tokens per slice) to dst_*[bh][dst_tok0 + i][D] (dst holds
+// dst_tokens per slice), in one launch.  Storage dtype preserved.
+hipError_t launch_copy_tokens(const Layout& L, const void* src_k, const void* src_v,
+                              int64_t src_tokens, int64_t src_tok0, char* dst_k, char* dst_v,
+                              int64_t dst_tokens, int64_t dst_tok0, int64_t n, hipStream_t stream);
 
 // Quantize n_groups consecutive key groups (n_groups * G tokens) of every slice,
 // read from src_k/src_v[bh][src_tok0 + t][D] (src_tokens tokens per slice), into

@@ -40,18 +40,27 @@ __device__ inline uint32_t group_code(float x, QParams p, float qmax) {
 // ---------------------------------------------------------------------------
 // token copy (sink / residual slots), 16-byte vectors
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void copy_tokens_kernel(const uint4* __restrict__ src,
+__global__ __launch_bounds__(256) void copy_tokens_kernel(const uint4* __restrict__ src_k,
+                                                          const uint4* __restrict__ src_v,
                                                           int64_t src_tokens, int64_t src_tok0,
-                                                          uint4* __restrict__ dst, int64_t dst_tokens,
+                                                          uint4* __restrict__ dst_k,
+                                                          uint4* __restrict__ dst_v, int64_t dst_tokens,
                                                           int64_t dst_tok0, int64_t n, int row_vec,
                                                           int64_t total) {
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+    // total = BH * n * row_vec vectors of K, then as many of V
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < 2 * total;
          i += (int64_t)gridDim.x * blockDim.x) {
-        int64_t v = i % row_vec;
-        int64_t t = (i / row_vec) % n;
-        int64_t bh = i / ((int64_t)row_vec * n);
-        dst[(bh * dst_tokens + dst_tok0 + t) * row_vec + v] =
-            src[(bh * src_tokens + src_tok0 + t) * row_vec + v];
+        const bool is_v = i >= total;
+        const int64_t j = is_v ? i - total : i;
+        const int64_t v = j % row_vec;
+        const int64_t t = (j / row_vec) % n;
+        const int64_t bh = j / ((int64_t)row_vec * n);
+        const int64_t si = (bh * src_tokens + src_tok0 + t) * row_vec + v;
+        const int64_t di = (bh * dst_tokens + dst_tok0 + t) * row_vec + v;
+        if (is_v)
+            dst_v[di] = src_v[si];
+        else
+            dst_k[di] = src_k[si];
     }
 }
 
@@ -268,16 +277,17 @@ int grid_for(int64_t work, int64_t per_block, int cap) {
 
 }  // namespace
 
-hipError_t launch_copy_tokens(const Layout& L, const void* src, int64_t src_tokens, int64_t src_tok0,
-                              char* dst, int64_t dst_tokens, int64_t dst_tok0, int64_t n,
-                              hipStream_t stream) {
+hipError_t launch_copy_tokens(const Layout& L, const void* src_k, const void* src_v,
+                              int64_t src_tokens, int64_t src_tok0, char* dst_k, char* dst_v,
+                              int64_t dst_tokens, int64_t dst_tok0, int64_t n, hipStream_t stream) {
     if (n <= 0) return hipSuccess;
     const int row_vec = L.D * L.esize / 16;
     const int64_t total = L.BH * n * row_vec;
-    const int grid = grid_for(total, 256, 65535);
-    copy_tokens_kernel<<<grid, 256, 0, stream>>>(reinterpret_cast<const uint4*>(src), src_tokens,
-                                                 src_tok0, reinterpret_cast<uint4*>(dst), dst_tokens,
-                                                 dst_tok0, n, row_vec, total);
+    const int grid = grid_for(2 * total, 256, 65535);
+    copy_tokens_kernel<<<grid, 256, 0, stream>>>(
+        reinterpret_cast<const uint4*>(src_k), reinterpret_cast<const uint4*>(src_v), src_tokens,
+        src_tok0, reinterpret_cast<uint4*>(dst_k), reinterpret_cast<uint4*>(dst_v), dst_tokens,
+        dst_tok0, n, row_vec, total);
     return hipGetLastError();
 }
 
