@@ -1,31 +1,30 @@
 // decode_dispatch.h -- instantiation table of the decode kernel for one storage
-// dtype (included by decode_<dtype>.hip with KVQ_DT defined).
+// dtype (included by decode_<dtype>.hip).
 #pragma once
 #include "decode_impl.h"
 
 namespace kvq {
 namespace dec {
 
+// Kernel entry of the instantiation for (bits, head_dim, query heads per kv head,
+// key channels per lane, tile), or nullptr if there is none.
 template <int DT>
-hipError_t launch_decode_dt(const DecArgs& a, int bits, int D, int gqa, int cpl, int tile, dim3 grid,
-                            hipStream_t s);
+const void* decode_kernel_ptr(int bits, int D, int gqa, int cpl, int tile);
 
 template <>
-hipError_t launch_decode_dt<DT_F32>(const DecArgs&, int, int, int, int, int, dim3, hipStream_t);
+const void* decode_kernel_ptr<DT_F32>(int, int, int, int, int);
 template <>
-hipError_t launch_decode_dt<DT_BF16>(const DecArgs&, int, int, int, int, int, dim3, hipStream_t);
+const void* decode_kernel_ptr<DT_BF16>(int, int, int, int, int);
 template <>
-hipError_t launch_decode_dt<DT_F16>(const DecArgs&, int, int, int, int, int, dim3, hipStream_t);
+const void* decode_kernel_ptr<DT_F16>(int, int, int, int, int);
 
-// Channels per lane (CPL) by (head_dim, query heads per kv head, bits): wide lanes
-// for MHA, narrower lanes when several query heads multiply the register state.
-// The host picks the widest listed CPL that divides the value group size, so a
-// lane's channels never straddle two value groups.
-#define KVQ_DECODE_CASE(DT, BITS, D_, GQ_, CPL_, TILE_)                                           \
-    if (bits == BITS && D == D_ && gqa == GQ_ && cpl == CPL_ && tile == TILE_) {                  \
-        decode_kernel<DT, BITS, D_, GQ_, CPL_, TILE_><<<grid, kThreads, 0, s>>>(a);               \
-        return hipGetLastError();                                                                 \
-    }
+// Key channels per lane (CPL): 32 for MHA with head_dim 128 (4 lanes per token),
+// 16 when several query heads multiply the register state, 8 for 8 query heads
+// with 4-bit codes.  The host picks CPL so that D / CPL lanes cover at least the
+// value groups of a token (D / CPL >= D / G_V).
+#define KVQ_DECODE_CASE(DT, BITS, D_, GQ_, CPL_, TILE_)                                     \
+    if (bits == BITS && D == D_ && gqa == GQ_ && cpl == CPL_ && tile == TILE_)              \
+        return reinterpret_cast<const void*>(&decode_kernel<DT, BITS, D_, GQ_, CPL_, TILE_>);
 
 #define KVQ_DECODE_TILES(DT, BITS, D_, GQ_, CPL_) \
     KVQ_DECODE_CASE(DT, BITS, D_, GQ_, CPL_, 32)  \
@@ -51,12 +50,11 @@ hipError_t launch_decode_dt<DT_F16>(const DecArgs&, int, int, int, int, int, dim
     KVQ_DECODE_TILES(DT, 4, 64, 8, 8)        \
     KVQ_DECODE_TILES(DT, 2, 64, 8, 16)
 
-#define KVQ_DEFINE_LAUNCH(DT)                                                                       \
-    template <>                                                                                     \
-    hipError_t launch_decode_dt<DT>(const DecArgs& a, int bits, int D, int gqa, int cpl, int tile,   \
-                                    dim3 grid, hipStream_t s) {                                     \
-        KVQ_DECODE_TABLE(DT)                                                                        \
-        return hipErrorInvalidValue;                                                                \
+#define KVQ_DEFINE_KERNEL_PTR(DT)                                                        \
+    template <>                                                                          \
+    const void* decode_kernel_ptr<DT>(int bits, int D, int gqa, int cpl, int tile) {    \
+        KVQ_DECODE_TABLE(DT)                                                             \
+        return nullptr;                                                                  \
     }
 
 }  // namespace dec

@@ -3,6 +3,6 @@
 
 namespace kvq {
 namespace dec {
-KVQ_DEFINE_LAUNCH(DT_F32)
+KVQ_DEFINE_KERNEL_PTR(DT_F32)
 }  // namespace dec
 }  // namespace kvq

@@ -104,6 +104,10 @@ Layout make_layout(const kvq_config* c) {
     const int64_t after_sink = std::max<int64_t>(0, c->max_tokens - L.S);
     L.Lq_cap = (int64_t)L.R * (after_sink / L.R);
     L.ng_cap = L.Lq_cap / L.G;
+    L.rec_kcodes = 8 * L.D;
+    L.rec_vcodes = L.rec_kcodes + L.G * L.row_bytes;
+    L.rec_vmeta = L.rec_vcodes + L.G * L.row_bytes;
+    L.rec_bytes = (int)align256((size_t)L.rec_vmeta + (size_t)L.G * L.nvg * 8);
     size_t off = 0;
     auto take = [&](size_t bytes) {
         size_t o = off;
@@ -115,10 +119,7 @@ Layout make_layout(const kvq_config* c) {
     L.off_vsink = take((size_t)L.BH * L.S * fp_row);
     L.off_kres = take((size_t)L.BH * L.R * fp_row);
     L.off_vres = take((size_t)L.BH * L.R * fp_row);
-    L.off_kcodes = take((size_t)L.BH * L.Lq_cap * L.row_bytes);
-    L.off_vcodes = take((size_t)L.BH * L.Lq_cap * L.row_bytes);
-    L.off_kmeta = take((size_t)L.BH * L.ng_cap * 2 * L.D * sizeof(float));
-    L.off_vmeta = take((size_t)L.BH * L.Lq_cap * L.nvg * 2 * sizeof(float));
+    L.off_rec = take((size_t)L.BH * L.ng_cap * L.rec_bytes);
     L.total = off;
     return L;
 }
@@ -130,31 +131,6 @@ kvq_status check_hip(hipError_t e, const char* what) {
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
-DecodePlan make_plan(const kvq_cache* c) {
-    const Layout& L = c->L;
-    DecodePlan p;
-    p.Lq = c->Lq;
-    p.nS = (int)c->nS;
-    p.r = (int)c->r;
-    p.has_fp = (c->nS + c->r) > 0 ? 1 : 0;
-    const int64_t ng = c->Lq / L.G;
-    const int cap_q = c->nsplit_cap - 1;
-    int64_t gps;
-    if (c->split_tokens > 0) {
-        gps = (c->split_tokens + L.G - 1) / L.G;
-    } else {
-        const int64_t target = 4LL * c->num_cu;  // workgroups for the whole device
-        gps = (L.BH * ng + target - 1) / target;
-        gps = std::max<int64_t>(gps, std::min<int64_t>(kWaves, ng));
-    }
-    gps = std::max<int64_t>(gps, 1);
-    if (ng > 0 && (ng + gps - 1) / gps > cap_q) gps = (ng + cap_q - 1) / cap_q;
-    p.gps = (int)gps;
-    p.nsplit_q = ng > 0 ? (int)((ng + gps - 1) / gps) : 0;
-    p.nsplit = p.nsplit_q + p.has_fp;
-    return p;
-}
-
 }  // namespace
 
 extern "C" {
@@ -163,7 +139,9 @@ kvq_status kvq_cache_bytes(const kvq_config* cfg, size_t* bytes) {
     kvq_status st = validate(cfg);
     if (st != KVQ_OK) return st;
     if (!bytes) return fail(KVQ_ERR_INVALID_ARG, "bytes is NULL");
-    *bytes = make_layout(cfg).total;
+    const Layout L = make_layout(cfg);
+    if (!decode_supported(L)) return fail(KVQ_ERR_UNSUPPORTED, "no decode kernel for this configuration");
+    *bytes = L.total;
     return ok();
 }
 
@@ -173,6 +151,7 @@ kvq_status kvq_cache_create(const kvq_config* cfg, void* dev_buf, size_t bytes, 
     if (!dev_buf || !out) return fail(KVQ_ERR_INVALID_ARG, "dev_buf or out is NULL");
     if (!aligned(dev_buf, 256)) return fail(KVQ_ERR_INVALID_ARG, "dev_buf must be 256-byte aligned");
     Layout L = make_layout(cfg);
+    if (!decode_supported(L)) return fail(KVQ_ERR_UNSUPPORTED, "no decode kernel for this configuration");
     if (bytes < L.total)
         return fail(KVQ_ERR_BUFFER_TOO_SMALL, "cache buffer holds %zu bytes, needs %zu", bytes, L.total);
     int dev = 0, ncu = 0;
@@ -188,10 +167,7 @@ kvq_status kvq_cache_create(const kvq_config* cfg, void* dev_buf, size_t bytes, 
     c->P.vsink = c->buf + L.off_vsink;
     c->P.kres = c->buf + L.off_kres;
     c->P.vres = c->buf + L.off_vres;
-    c->P.kcodes = (uint8_t*)(c->buf + L.off_kcodes);
-    c->P.vcodes = (uint8_t*)(c->buf + L.off_vcodes);
-    c->P.kmeta = (float*)(c->buf + L.off_kmeta);
-    c->P.vmeta = (float*)(c->buf + L.off_vmeta);
+    c->P.rec = (uint8_t*)(c->buf + L.off_rec);
     c->nS = c->Lq = c->r = 0;
     c->split_tokens = 0;
     c->num_cu = ncu > 0 ? ncu : 256;
@@ -286,9 +262,14 @@ kvq_status kvq_decode_attention(kvq_cache* c, const void* q, float* out, float* 
     const size_t need = decode_workspace_bytes(c->L, c->nsplit_cap);
     if (ws_bytes < need)
         return fail(KVQ_ERR_BUFFER_TOO_SMALL, "workspace holds %zu bytes, needs %zu", ws_bytes, need);
-    const DecodePlan p = make_plan(c);
-    kvq_status st = check_hip(launch_decode(c->L, c->P, p, q, out, lse, ws, c->sm_scale, (hipStream_t)stream,
-                                            c->nsplit_cap),
+    DecodeRequest rq;
+    rq.Lq = c->Lq;
+    rq.nS = c->nS;
+    rq.r = c->r;
+    rq.split_tokens = c->split_tokens;
+    rq.num_cu = c->num_cu;
+    rq.nsplit_cap = c->nsplit_cap;
+    kvq_status st = check_hip(launch_decode(c->L, c->P, rq, q, out, lse, ws, c->sm_scale, (hipStream_t)stream),
                               "decode");
     if (st != KVQ_OK) return st;
     return ok();

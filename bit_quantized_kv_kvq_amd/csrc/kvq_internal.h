@@ -15,21 +15,26 @@ constexpr int kThreads = 64 * kWaves;  // 256 threads
 constexpr int kMaxCombine = 1024;      // max (splits x query heads per kv head)
 
 // ---------------------------------------------------------------------------
-// Device buffer layout of one cache.  Every array is indexed by the flattened
-// (sequence, kv head) slice bh = b * Hkv + kvh first:
+// Device buffer layout of one cache.  Slices bh = b * Hkv + kvh come first:
 //   k_sink, v_sink : [BH][S][D]        storage dtype
 //   k_res,  v_res  : [BH][R][D]        storage dtype
-//   k_codes,v_codes: [BH][Lq_cap][D*bits/8] packed codes, one row per token
-//   k_meta         : [BH][Lq_cap/G][2][D]  fp32 (scales row, then zeros row)
-//   v_meta         : [BH][Lq_cap][D/G_V][2] fp32 (scale, zero) pairs
+//   records        : [BH][Lq_cap / G]  one record of rec_bytes per key group
 // Lq_cap = R * floor((max_tokens - S) / R): the largest quantized length a
-// sequence of max_tokens tokens can reach.
+// sequence of max_tokens tokens can reach.  A key group's record holds, in the
+// order decode attention streams them:
+//   kmeta  : fp32 [2][D]              key scales, then key zero points
+//   kcodes : [G][D*bits/8]            key codes, one packed row per token
+//   vcodes : [G/TB][D] uint32         value codes: for each block of TB = 32/bits
+//                                     tokens, one dword per channel holding the
+//                                     block's tokens (token j at pack_shift(bits, j))
+//   vmeta  : fp32 [G][D/G_V][2]       value (scale, zero) per token and group
+// so a slice's quantized tokens are one contiguous stream of records.
 // ---------------------------------------------------------------------------
 struct Layout {
     int B, Hkv, Hq, D, bits, G, GV, R, S, dtype, esize, gqa, nvg, row_bytes;
     int64_t BH, max_tokens, Lq_cap, ng_cap;
-    size_t off_ksink, off_vsink, off_kres, off_vres, off_kcodes, off_vcodes, off_kmeta,
-        off_vmeta, total;
+    int rec_bytes, rec_kcodes, rec_vcodes, rec_vmeta;
+    size_t off_ksink, off_vsink, off_kres, off_vres, off_rec, total;
 };
 
 struct DevPtrs {
@@ -37,10 +42,7 @@ struct DevPtrs {
     char* vsink;
     char* kres;
     char* vres;
-    uint8_t* kcodes;
-    uint8_t* vcodes;
-    float* kmeta;
-    float* vmeta;
+    uint8_t* rec;
 };
 
 // ---------------------------------------------------------------------------
@@ -52,6 +54,11 @@ struct DevPtrs {
 // byte-to-float conversions, and the unpacked order is the channel order.
 // ---------------------------------------------------------------------------
 __host__ __device__ inline int pack_shift(int bits, int j) { return 8 * (j & 3) + bits * (j >> 2); }
+
+// Record addressing.
+__host__ __device__ inline size_t rec_offset(int64_t bh, int64_t grp, int64_t ng_cap, int rec_bytes) {
+    return (size_t)(bh * ng_cap + grp) * (size_t)rec_bytes;
+}
 
 // ---------------------------------------------------------------------------
 // storage dtype helpers
@@ -93,18 +100,19 @@ hipError_t launch_quantize(const Layout& L, const DevPtrs& P, const void* src_k,
                            int64_t src_tokens, int64_t src_tok0, int64_t n_groups, int64_t dst_tok0,
                            hipStream_t stream);
 
-struct DecodePlan {
-    int64_t Lq;          // quantized tokens per slice
-    int nS, r;           // sinks held, residual tokens held
-    int gps;             // key groups per quantized split
-    int nsplit_q;        // quantized splits per slice
-    int nsplit;          // total splits per slice (quantized + optional full-precision)
-    int has_fp;          // 1 if a full-precision split covers sinks and residual
+struct DecodeRequest {
+    int64_t Lq;            // quantized tokens per slice
+    int64_t nS, r;         // sinks held, residual tokens held
+    int64_t split_tokens;  // tokens per split override (0 = automatic)
+    int num_cu;            // compute units of the device
+    int nsplit_cap;        // splits per slice the workspace holds
 };
 
-hipError_t launch_decode(const Layout& L, const DevPtrs& P, const DecodePlan& plan, const void* q,
-                         float* out, float* lse, void* ws, float sm_scale, hipStream_t stream,
-                         int nsplit_cap);
+hipError_t launch_decode(const Layout& L, const DevPtrs& P, const DecodeRequest& rq, const void* q,
+                         float* out, float* lse, void* ws, float sm_scale, hipStream_t stream);
+
+// true if an instantiation of the decode kernel serves this layout
+bool decode_supported(const Layout& L);
 
 size_t decode_workspace_bytes(const Layout& L, int max_splits);
 

@@ -66,20 +66,19 @@ __global__ __launch_bounds__(256) void copy_tokens_kernel(const uint4* __restric
 
 // ---------------------------------------------------------------------------
 // quantize + pack one key group (G tokens x D channels) and the values of the
-// same G tokens.  grid = (n_groups, BH), block = 256.
+// same G tokens into the group's record.  grid = (n_groups, BH), block = 256.
 // ---------------------------------------------------------------------------
 struct QuantArgs {
     const void* src_k;
     const void* src_v;
     int64_t src_tokens, src_tok0, dst_tok0;
     int D, G, GV, nvg, row_bytes;
-    int64_t Lq_cap, ng_cap;
-    uint8_t* kcodes;
-    uint8_t* vcodes;
-    float* kmeta;
-    float* vmeta;
+    int64_t ng_cap;
+    int rec_bytes, rec_kcodes, rec_vcodes, rec_vmeta;
+    uint8_t* rec;
 };
 
+// key rows: dword w of token row t holds channels CPD*w + j at pack_shift(j)
 template <int BITS>
 __device__ inline void pack_rows(const uint8_t* s_codes, int rows, int D, int row_bytes,
                                  uint8_t* dst_row0) {
@@ -95,6 +94,20 @@ __device__ inline void pack_rows(const uint8_t* s_codes, int rows, int D, int ro
     }
 }
 
+// value blocks: dword (b, c) holds tokens TB*b + j of channel c at pack_shift(j)
+template <int BITS>
+__device__ inline void pack_blocks(const uint8_t* s_codes, int rows, int D, uint32_t* dst) {
+    constexpr int TB = 32 / BITS;  // tokens per dword
+    const int nblk = rows / TB;
+    for (int i = threadIdx.x; i < nblk * D; i += blockDim.x) {
+        const int b = i / D, c = i % D;
+        uint32_t word = 0;
+#pragma unroll
+        for (int j = 0; j < TB; ++j) word |= (uint32_t)s_codes[(b * TB + j) * D + c] << pack_shift(BITS, j);
+        dst[i] = word;
+    }
+}
+
 template <int DT, int BITS>
 __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
     extern __shared__ uint8_t s_codes[];  // [G][D]
@@ -103,8 +116,9 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
     const int64_t bh = blockIdx.y;
     const int D = a.D, G = a.G;
     const int64_t src_row0 = bh * a.src_tokens + a.src_tok0 + (int64_t)grp * G;
-    const int64_t dst_tok = a.dst_tok0 + (int64_t)grp * G;  // first quantized token
-    const int64_t dst_grp = dst_tok / G;
+    const int64_t dst_grp = a.dst_tok0 / G + grp;
+    uint8_t* rec = a.rec + rec_offset(bh, dst_grp, a.ng_cap, a.rec_bytes);
+    float* kmeta = reinterpret_cast<float*>(rec);
 
     // keys: one group per channel over the G tokens
     for (int c = threadIdx.x; c < D; c += blockDim.x) {
@@ -119,16 +133,16 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
         for (int t = 0; t < G; ++t)
             s_codes[t * D + c] =
                 (uint8_t)group_code(load_as_f32<DT>(a.src_k, base + (int64_t)t * D), p, qmax);
-        float* km = a.kmeta + (bh * a.ng_cap + dst_grp) * 2 * D;
-        km[c] = p.s;
-        km[D + c] = p.z;
+        kmeta[c] = p.s;
+        kmeta[D + c] = p.z;
     }
     __syncthreads();
-    pack_rows<BITS>(s_codes, G, D, a.row_bytes, a.kcodes + (bh * a.Lq_cap + dst_tok) * a.row_bytes);
+    pack_rows<BITS>(s_codes, G, D, a.row_bytes, rec + a.rec_kcodes);
     __syncthreads();
 
     // values: one group per run of G_V channels of each token
     const int GV = a.GV, nvg = a.nvg;
+    float* vmeta = reinterpret_cast<float*>(rec + a.rec_vmeta);
     for (int i = threadIdx.x; i < G * nvg; i += blockDim.x) {
         const int t = i / nvg, h = i % nvg;
         const int64_t base = (src_row0 + t) * D + (int64_t)h * GV;
@@ -142,12 +156,11 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
         for (int j = 0; j < GV; ++j)
             s_codes[t * D + h * GV + j] =
                 (uint8_t)group_code(load_as_f32<DT>(a.src_v, base + j), p, qmax);
-        float* vm = a.vmeta + ((bh * a.Lq_cap + dst_tok + t) * nvg + h) * 2;
-        vm[0] = p.s;
-        vm[1] = p.z;
+        vmeta[i * 2] = p.s;
+        vmeta[i * 2 + 1] = p.z;
     }
     __syncthreads();
-    pack_rows<BITS>(s_codes, G, D, a.row_bytes, a.vcodes + (bh * a.Lq_cap + dst_tok) * a.row_bytes);
+    pack_blocks<BITS>(s_codes, G, D, reinterpret_cast<uint32_t*>(rec + a.rec_vcodes));
 }
 
 // ---------------------------------------------------------------------------
@@ -158,20 +171,24 @@ struct DeqArgs {
     const char* vsink;
     const char* kres;
     const char* vres;
-    const uint8_t* kcodes;
-    const uint8_t* vcodes;
-    const float* kmeta;
-    const float* vmeta;
+    const uint8_t* rec;
     float* kout;
     float* vout;
-    int64_t nS, Lq, r, T, Lq_cap, ng_cap;
+    int64_t nS, Lq, r, T, ng_cap;
     int S, R, D, G, GV, nvg, bits, row_bytes;
+    int rec_bytes, rec_kcodes, rec_vcodes, rec_vmeta;
 };
 
-__device__ inline uint32_t unpack_code(const uint8_t* row, int c, int bits) {
-    const int cpd = 32 / bits;
-    uint32_t w = reinterpret_cast<const uint32_t*>(row)[c / cpd];
-    return (w >> pack_shift(bits, c % cpd)) & ((1u << bits) - 1u);
+__device__ inline uint32_t key_code(const DeqArgs& a, const uint8_t* rec, int t, int c) {
+    const int cpd = 32 / a.bits;
+    const uint32_t w = reinterpret_cast<const uint32_t*>(rec + a.rec_kcodes + (int64_t)t * a.row_bytes)[c / cpd];
+    return (w >> pack_shift(a.bits, c % cpd)) & ((1u << a.bits) - 1u);
+}
+
+__device__ inline uint32_t value_code(const DeqArgs& a, const uint8_t* rec, int t, int c) {
+    const int tb = 32 / a.bits;
+    const uint32_t w = reinterpret_cast<const uint32_t*>(rec + a.rec_vcodes)[(t / tb) * a.D + c];
+    return (w >> pack_shift(a.bits, t % tb)) & ((1u << a.bits) - 1u);
 }
 
 template <int DT>
@@ -189,11 +206,12 @@ __global__ __launch_bounds__(256) void dequantize_kernel(DeqArgs a) {
             vx = load_as_f32<DT>(a.vsink, idx);
         } else if (t < a.nS + a.Lq) {
             const int64_t tq = t - a.nS;
-            const int64_t row = bh * a.Lq_cap + tq;
-            const float* km = a.kmeta + (bh * a.ng_cap + tq / a.G) * 2 * a.D;
-            const float* vm = a.vmeta + (row * a.nvg + c / a.GV) * 2;
-            const float kq = (float)unpack_code(a.kcodes + row * a.row_bytes, c, a.bits);
-            const float vq = (float)unpack_code(a.vcodes + row * a.row_bytes, c, a.bits);
+            const int tg = (int)(tq % a.G);
+            const uint8_t* rec = a.rec + rec_offset(bh, tq / a.G, a.ng_cap, a.rec_bytes);
+            const float* km = reinterpret_cast<const float*>(rec);
+            const float* vm = reinterpret_cast<const float*>(rec + a.rec_vmeta) + ((int64_t)tg * a.nvg + c / a.GV) * 2;
+            const float kq = (float)key_code(a, rec, tg, c);
+            const float vq = (float)value_code(a, rec, tg, c);
             kx = (kq - km[a.D + c]) * km[c];
             vx = (vq - vm[1]) * vm[0];
         } else {
@@ -219,21 +237,25 @@ __global__ __launch_bounds__(256) void export_kernel(DeqArgs a, uint8_t* k_codes
     for (int64_t i = i0; i < ncode; i += stride) {
         const int64_t t = i / a.D;
         const int c = (int)(i % a.D);
-        const int64_t row = bh * a.Lq_cap + t;
-        if (k_codes) k_codes[bh * ncode + i] = (uint8_t)unpack_code(a.kcodes + row * a.row_bytes, c, a.bits);
-        if (v_codes) v_codes[bh * ncode + i] = (uint8_t)unpack_code(a.vcodes + row * a.row_bytes, c, a.bits);
+        const uint8_t* rec = a.rec + rec_offset(bh, t / a.G, a.ng_cap, a.rec_bytes);
+        const int tg = (int)(t % a.G);
+        if (k_codes) k_codes[bh * ncode + i] = (uint8_t)key_code(a, rec, tg, c);
+        if (v_codes) v_codes[bh * ncode + i] = (uint8_t)value_code(a, rec, tg, c);
     }
     const int64_t nk = (a.Lq / a.G) * a.D;
     for (int64_t i = i0; i < nk; i += stride) {
         const int64_t g = i / a.D;
         const int c = (int)(i % a.D);
-        const float* km = a.kmeta + (bh * a.ng_cap + g) * 2 * a.D;
+        const float* km = reinterpret_cast<const float*>(a.rec + rec_offset(bh, g, a.ng_cap, a.rec_bytes));
         if (k_scale) k_scale[bh * nk + i] = km[c];
         if (k_zero) k_zero[bh * nk + i] = km[a.D + c];
     }
     const int64_t nv = a.Lq * a.nvg;
     for (int64_t i = i0; i < nv; i += stride) {
-        const float* vm = a.vmeta + (bh * a.Lq_cap * a.nvg + i) * 2;
+        const int64_t t = i / a.nvg;
+        const int h = (int)(i % a.nvg);
+        const uint8_t* rec = a.rec + rec_offset(bh, t / a.G, a.ng_cap, a.rec_bytes);
+        const float* vm = reinterpret_cast<const float*>(rec + a.rec_vmeta) + ((t % a.G) * a.nvg + h) * 2;
         if (v_scale) v_scale[bh * nv + i] = vm[0];
         if (v_zero) v_zero[bh * nv + i] = vm[1];
     }
@@ -245,17 +267,13 @@ DeqArgs make_deq_args(const Layout& L, const DevPtrs& P, int64_t nS, int64_t Lq,
     a.vsink = P.vsink;
     a.kres = P.kres;
     a.vres = P.vres;
-    a.kcodes = P.kcodes;
-    a.vcodes = P.vcodes;
-    a.kmeta = P.kmeta;
-    a.vmeta = P.vmeta;
+    a.rec = P.rec;
     a.kout = nullptr;
     a.vout = nullptr;
     a.nS = nS;
     a.Lq = Lq;
     a.r = r;
     a.T = nS + Lq + r;
-    a.Lq_cap = L.Lq_cap;
     a.ng_cap = L.ng_cap;
     a.S = L.S;
     a.R = L.R;
@@ -265,6 +283,10 @@ DeqArgs make_deq_args(const Layout& L, const DevPtrs& P, int64_t nS, int64_t Lq,
     a.nvg = L.nvg;
     a.bits = L.bits;
     a.row_bytes = L.row_bytes;
+    a.rec_bytes = L.rec_bytes;
+    a.rec_kcodes = L.rec_kcodes;
+    a.rec_vcodes = L.rec_vcodes;
+    a.rec_vmeta = L.rec_vmeta;
     return a;
 }
 
@@ -306,12 +328,12 @@ hipError_t launch_quantize(const Layout& L, const DevPtrs& P, const void* src_k,
     a.GV = L.GV;
     a.nvg = L.nvg;
     a.row_bytes = L.row_bytes;
-    a.Lq_cap = L.Lq_cap;
     a.ng_cap = L.ng_cap;
-    a.kcodes = P.kcodes;
-    a.vcodes = P.vcodes;
-    a.kmeta = P.kmeta;
-    a.vmeta = P.vmeta;
+    a.rec_bytes = L.rec_bytes;
+    a.rec_kcodes = L.rec_kcodes;
+    a.rec_vcodes = L.rec_vcodes;
+    a.rec_vmeta = L.rec_vmeta;
+    a.rec = P.rec;
     const size_t lds = (size_t)L.G * L.D;
     dim3 grid((unsigned)n_groups, (unsigned)L.BH);
 #define KVQ_QLAUNCH(DT, BITS) quantize_kernel<DT, BITS><<<grid, 256, lds, stream>>>(a)

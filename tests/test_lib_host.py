@@ -36,14 +36,15 @@ def _cfg(**kw):
 
 
 def _expected_bytes(c):
+    """Sinks and residual (K and V), then one record per key group of capacity."""
     al = lambda x: (x + 255) & ~255
     e = 4 if c.dtype == kvq.KVQ_F32 else 2
     BH = c.batch * c.n_kv_heads
-    D = c.head_dim
+    D, G = c.head_dim, c.k_group
     Lq_cap = c.residual * (max(0, c.max_tokens - c.n_sink) // c.residual)
-    parts = [BH * c.n_sink * D * e] * 2 + [BH * c.residual * D * e] * 2 + \
-            [BH * Lq_cap * D * c.bits // 8] * 2 + \
-            [BH * (Lq_cap // c.k_group) * 2 * D * 4, BH * Lq_cap * (D // c.v_group) * 2 * 4]
+    row = D * c.bits // 8
+    rec = al(8 * D + 2 * G * row + G * (D // c.v_group) * 8)
+    parts = [BH * c.n_sink * D * e] * 2 + [BH * c.residual * D * e] * 2 + [BH * (Lq_cap // G) * rec]
     return sum(al(p) for p in parts)
 
 
