@@ -19,6 +19,7 @@ timed with HIP events on the stream it is launched on.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import math
@@ -72,6 +73,43 @@ def traffic_from_profile(w: wl.Workload):
     return t.get("hbm_bytes_per_launch")
 
 
+class HipEvents:
+    """Timing events of the HIP runtime this process already uses (the one torch
+    loaded), created without the system-scope fence that default events add
+    (its cache write-back and invalidate would lengthen the timed kernels)."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        path = next(l.split()[-1] for l in open("/proc/self/maps") if "libamdhip64.so" in l)
+        self.lib = ctypes.CDLL(path)
+        self.lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self):
+        e = ctypes.c_void_p()
+        if self.lib.hipEventCreateWithFlags(ctypes.byref(e), self.DISABLE_SYSTEM_FENCE) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
+        return e
+
+    def record(self, e, stream):
+        if self.lib.hipEventRecord(e, stream) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = ctypes.c_float()
+        if self.lib.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def destroy(self, events):
+        for e in events:
+            self.lib.hipEventDestroy(e)
+
+
 def cpu_baseline(w: wl.Workload, budget_s: float):
     """The oracle, as it is, on host cores: the decode step (dequantize + binary64
     attention) of a bounded sample of (sequence, kv-head) slices of the workload."""
@@ -116,8 +154,10 @@ def cpu_baseline(w: wl.Workload, budget_s: float):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default: layers x residual, one flush per layer)")
+    # enough warm-up steps for the GPU clocks to settle (short bursts run slower)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--layers", type=int, default=0, help="caches rotated per step (0 = auto)")
     ap.add_argument("--split-tokens", type=int, default=0)
@@ -141,12 +181,16 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     w = wl.get(args.workload)
-    total_steps = args.warmup + args.steps
 
     # size of one cache's decode traffic; enough layers to overflow the MALL 3x
     nq0 = w.residual * ((w.prefill - min(w.prefill, w.n_sink)) // w.residual)
     b0 = algorithmic_bytes(w, min(w.prefill, w.n_sink), nq0, w.prefill - min(w.prefill, w.n_sink) - nq0)
     L = args.layers or min(64, max(2, math.ceil(3 * MALL_BYTES / b0)))
+    # by default every layer appends R tokens in the timed region, so the region
+    # holds each layer's residual flush once (its amortised share of the steps)
+    if args.steps is None:
+        args.steps = L * w.residual
+    total_steps = args.warmup + args.steps
     per_layer_steps = (total_steps + L - 1) // L
     max_tokens = w.prefill + per_layer_steps
 
@@ -176,33 +220,63 @@ def main():
     print("bench: caches ready", file=sys.stderr, flush=True)
 
     stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
-    step_bytes = []
+    hip = HipEvents()
+    ev = [(hip.create(), hip.create()) for _ in range(args.steps)]
 
-    def step(s: int, timed_idx: int | None):
+    # The timed loop calls the C-ABI directly with arguments prepared here, so that
+    # the host enqueues a step faster than the GPU runs it: the GPU never waits
+    # for the host inside the timed region, and the events around each decode
+    # time the kernel alone.
+    lib = kvq.lib()
+    append_fn, decode_fn = lib.kvq_append, lib.kvq_decode_attention
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    out_p, lse_p = ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(lse.data_ptr())
+    plan, step_bytes = [], []
+    for s in range(total_steps):
         c = caches[s % L]
         i = (s // L) % w.steps
-        c.append(Ks[i], Vs[i])
+        plan.append((ctypes.c_void_p(c.handle), ctypes.c_void_p(Ks[i].data_ptr()),
+                     ctypes.c_void_p(Vs[i].data_ptr()), ctypes.c_void_p(Q[i % Q.shape[0]].data_ptr()),
+                     ctypes.c_void_p(c._ws_ptr), c.ws_bytes))
+        # cache state after this step's append: the schedule fixes it
+        n = w.prefill + s // L + 1
+        nS = min(n, w.n_sink)
+        Lq = w.residual * ((n - nS) // w.residual)
+        step_bytes.append(algorithmic_bytes(w, nS, Lq, n - nS - Lq))
+
+    def step(s: int, timed_idx):
+        h, kp, vp, qp, wsp, wsb = plan[s]
+        st = append_fn(h, kp, vp, 1, sp)
+        if st:
+            raise kvq.KVQError(st, kvq.kvq_last_error())
         if timed_idx is not None:
-            _, nS, Lq, r = c.state()
-            step_bytes.append(algorithmic_bytes(w, nS, Lq, r))
-            ev[timed_idx][0].record(stream)
-        c.decode(Q[i % Q.shape[0]], out=out, lse=lse)
+            hip.record(ev[timed_idx][0], sp)
+        st = decode_fn(h, qp, out_p, lse_p, wsp, wsb, sp)
+        if st:
+            raise kvq.KVQError(st, kvq.kvq_last_error())
         if timed_idx is not None:
-            ev[timed_idx][1].record(stream)
+            hip.record(ev[timed_idx][1], sp)
 
     for s in range(args.warmup):
         step(s, None)
     torch.cuda.synchronize()
+    # the cache state the schedule predicts is the one the library reports
+    for li, c in enumerate(caches):
+        n_done = len(range(li, args.warmup, L))
+        n = w.prefill + n_done
+        nS = min(n, w.n_sink)
+        Lq = w.residual * ((n - nS) // w.residual)
+        assert tuple(c.state()) == (n, nS, Lq, n - nS - Lq), (li, c.state())
     t0 = time.perf_counter()
     for k in range(args.steps):
         step(args.warmup + k, k)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    step_bytes = step_bytes[args.warmup:]
 
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    dec_ms = [a.elapsed_time(b) for a, b in ev]
+    dec_ms = [hip.elapsed_ms(a, b) for a, b in ev]
+    hip.destroy([e for pair in ev for e in pair])
     dec_avg_ms = sum(dec_ms) / len(dec_ms)
     bytes_avg = sum(step_bytes) / len(step_bytes)
     value = bytes_avg / (ms_per_step * 1e-3) / 1e9

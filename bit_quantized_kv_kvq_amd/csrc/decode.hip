@@ -1,10 +1,6 @@
 // decode.hip -- decode attention launch: instantiation choice, split planning
-// (one round of workgroups at the kernel's occupancy) and workspace layout
+// (about one workgroup per CU) and workspace layout
 // (counters, then split maxima/sums, then split accumulators).
-#include <stdlib.h>
-
-#include <mutex>
-
 #include "decode_dispatch.h"
 
 namespace kvq {
@@ -26,51 +22,33 @@ WsLayout ws_layout(const Layout& L, int cap) {
 
 struct Choice {
     const void* fn;
-    int cpl, tile, lds;
+    int cpl, tile, tpg, lds;
 };
 
 Choice choose(const Layout& L) {
     Choice c;
-    c.tile = (L.G % 64 == 0 && L.gqa == 1) ? 64 : 32;
-    // tuning override: KVQ_DECODE_TILE=32|64 (ignored when the key group is not a multiple)
-    static const int tile_env = getenv("KVQ_DECODE_TILE") ? atoi(getenv("KVQ_DECODE_TILE")) : 0;
-    if ((tile_env == 32 || tile_env == 64) && L.G % tile_env == 0) c.tile = tile_env;
+    c.tile = (L.gqa == 1 && L.G >= 64) ? 64 : 32;
+    c.tpg = L.G / c.tile;
     if (L.D == 128 && L.gqa == 1)
         c.cpl = (L.nvg <= 4) ? 32 : 16;
     else if (L.gqa == 8 && L.bits == 4)
         c.cpl = 8;
     else
         c.cpl = 16;
-    switch (L.dtype) {
-        case DT_F32: c.fn = dec::decode_kernel_ptr<DT_F32>(L.bits, L.D, L.gqa, c.cpl, c.tile); break;
-        case DT_BF16: c.fn = dec::decode_kernel_ptr<DT_BF16>(L.bits, L.D, L.gqa, c.cpl, c.tile); break;
-        default: c.fn = dec::decode_kernel_ptr<DT_F16>(L.bits, L.D, L.gqa, c.cpl, c.tile); break;
+    c.fn = nullptr;
+    if (c.tile * c.tpg == L.G) {
+        if (L.bits == 4 && L.D == 128) c.fn = dec::decode_kernel_ptr<4, 128>(L.gqa, c.cpl, c.tile, c.tpg);
+        if (L.bits == 2 && L.D == 128) c.fn = dec::decode_kernel_ptr<2, 128>(L.gqa, c.cpl, c.tile, c.tpg);
+        if (L.bits == 4 && L.D == 64) c.fn = dec::decode_kernel_ptr<4, 64>(L.gqa, c.cpl, c.tile, c.tpg);
+        if (L.bits == 2 && L.D == 64) c.fn = dec::decode_kernel_ptr<2, 64>(L.gqa, c.cpl, c.tile, c.tpg);
     }
     // dynamic LDS of the chosen instantiation (see LdsPlan)
-    const int wave = (L.gqa * dec::kLimbs * L.D + L.gqa * L.nvg * dec::kLimbs * c.tile + 4 * L.gqa * L.nvg + 15) & ~15;
+    const int wave = (L.gqa * dec::kLimbs * L.D + 2 * L.gqa * L.nvg * dec::kLimbs * c.tile + 15) & ~15;
     const int wg = kWaves * L.gqa * L.D + kWaves * L.gqa * 2 + kMaxCombine + 16 + 4;
     c.lds = kWaves * wave + 4 * wg;
     return c;
 }
 
-// workgroups of one instantiation that fit on a CU at once (cached)
-int blocks_per_cu(const void* fn, int lds) {
-    static std::mutex mu;
-    static const void* fns[64];
-    static int ldss[64], vals[64], n = 0;
-    std::lock_guard<std::mutex> g(mu);
-    for (int i = 0; i < n; ++i)
-        if (fns[i] == fn && ldss[i] == lds) return vals[i];
-    int v = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, fn, kThreads, lds) != hipSuccess || v < 1) v = 1;
-    if (n < 64) {
-        fns[n] = fn;
-        ldss[n] = lds;
-        vals[n] = v;
-        ++n;
-    }
-    return v;
-}
 }  // namespace
 
 size_t decode_workspace_bytes(const Layout& L, int max_splits) { return ws_layout(L, max_splits).total; }
@@ -83,15 +61,18 @@ hipError_t launch_decode(const Layout& L, const DevPtrs& P, const DecodeRequest&
     if (!ch.fn) return hipErrorInvalidValue;
     const WsLayout w = ws_layout(L, rq.nsplit_cap);
 
-    // split plan: about one round of workgroups over the whole device, whole key
-    // groups per split, a multiple of the wave count when splits are long
+    // Split plan: about one workgroup per CU, whole key groups per split, a
+    // multiple of the wave count when splits are long.  Long per-wave streams
+    // beat more workgroups per CU: every stream pays a start-up latency and the
+    // split combine, while the prefetch ring already covers the memory latency
+    // at one workgroup per CU.
     const int64_t ng = rq.Lq / L.G;
     const int cap_q = rq.nsplit_cap;
     int64_t gps = 1;
     if (rq.split_tokens > 0) {
         gps = (rq.split_tokens + L.G - 1) / L.G;
     } else if (ng > 0) {
-        const int64_t slots = (int64_t)blocks_per_cu(ch.fn, ch.lds) * rq.num_cu;
+        const int64_t slots = rq.num_cu;
         gps = (L.BH * ng + slots - 1) / slots;
         if (gps > kWaves) gps = (gps + kWaves - 1) / kWaves * kWaves;
     }
@@ -123,11 +104,9 @@ hipError_t launch_decode(const Layout& L, const DevPtrs& P, const DecodeRequest&
     a.nS = (int)rq.nS;
     a.nfp = (int)(rq.nS + rq.r);
     a.G = L.G;
+    a.dtype = L.dtype;
     a.GV = L.GV;
     a.nvg = L.nvg;
-    int lg = 0;
-    while ((1 << lg) < L.nvg) ++lg;
-    a.log2nvg = lg;
     a.gps = (int)gps;
     a.ngroups = (int)ng;
     a.nsplit = nsplit;

@@ -1,60 +1,66 @@
-// decode_dispatch.h -- instantiation table of the decode kernel for one storage
-// dtype (included by decode_<dtype>.hip).
+// decode_dispatch.h -- instantiation table of the decode kernel (included by
+// decode_b<bits>_d<head_dim>.hip).
 #pragma once
 #include "decode_impl.h"
 
 namespace kvq {
 namespace dec {
 
-// Kernel entry of the instantiation for (bits, head_dim, query heads per kv head,
-// key channels per lane, tile), or nullptr if there is none.
-template <int DT>
-const void* decode_kernel_ptr(int bits, int D, int gqa, int cpl, int tile);
+// Kernel entry of the instantiation for (query heads per kv head, key channels
+// per lane, tile, tiles per key group) at a code width and head_dim, or nullptr
+// if there is none.  Defined in decode_b<bits>_d<head_dim>.hip.
+template <int BITS, int D>
+const void* decode_kernel_ptr(int gqa, int cpl, int tile, int tpg);
 
 template <>
-const void* decode_kernel_ptr<DT_F32>(int, int, int, int, int);
+const void* decode_kernel_ptr<4, 128>(int, int, int, int);
 template <>
-const void* decode_kernel_ptr<DT_BF16>(int, int, int, int, int);
+const void* decode_kernel_ptr<2, 128>(int, int, int, int);
 template <>
-const void* decode_kernel_ptr<DT_F16>(int, int, int, int, int);
+const void* decode_kernel_ptr<4, 64>(int, int, int, int);
+template <>
+const void* decode_kernel_ptr<2, 64>(int, int, int, int);
 
 // Key channels per lane (CPL): 32 for MHA with head_dim 128 (4 lanes per token),
 // 16 when several query heads multiply the register state, 8 for 8 query heads
 // with 4-bit codes.  The host picks CPL so that D / CPL lanes cover at least the
-// value groups of a token (D / CPL >= D / G_V).
-#define KVQ_DECODE_CASE(DT, BITS, D_, GQ_, CPL_, TILE_)                                     \
-    if (bits == BITS && D == D_ && gqa == GQ_ && cpl == CPL_ && tile == TILE_)              \
-        return reinterpret_cast<const void*>(&decode_kernel<DT, BITS, D_, GQ_, CPL_, TILE_>);
+// value groups of a token (D / CPL >= D / G_V).  Tiles are 64 tokens for one
+// query head per kv head and 32 otherwise; key groups of 32 to 256 tokens.
+#define KVQ_DECODE_CASE(BITS, D_, GQ_, CPL_, TILE_, TPG_)                     \
+    if (gqa == GQ_ && cpl == CPL_ && tile == TILE_ && tpg == TPG_)           \
+        return reinterpret_cast<const void*>(&decode_kernel<BITS, D_, GQ_, CPL_, TILE_, TPG_>);
 
-#define KVQ_DECODE_TILES(DT, BITS, D_, GQ_, CPL_) \
-    KVQ_DECODE_CASE(DT, BITS, D_, GQ_, CPL_, 32)  \
-    KVQ_DECODE_CASE(DT, BITS, D_, GQ_, CPL_, 64)
+#define KVQ_DECODE_GROUPS_MHA(BITS, D_, CPL_)     \
+    KVQ_DECODE_CASE(BITS, D_, 1, CPL_, 32, 1)     \
+    KVQ_DECODE_CASE(BITS, D_, 1, CPL_, 64, 1)     \
+    KVQ_DECODE_CASE(BITS, D_, 1, CPL_, 64, 2)     \
+    KVQ_DECODE_CASE(BITS, D_, 1, CPL_, 64, 4)
 
-#define KVQ_DECODE_TABLE(DT)                 \
-    KVQ_DECODE_TILES(DT, 4, 128, 1, 32)      \
-    KVQ_DECODE_TILES(DT, 2, 128, 1, 32)      \
-    KVQ_DECODE_TILES(DT, 4, 128, 1, 16)      \
-    KVQ_DECODE_TILES(DT, 2, 128, 1, 16)      \
-    KVQ_DECODE_TILES(DT, 4, 128, 2, 16)      \
-    KVQ_DECODE_TILES(DT, 2, 128, 2, 16)      \
-    KVQ_DECODE_TILES(DT, 4, 128, 4, 16)      \
-    KVQ_DECODE_TILES(DT, 2, 128, 4, 16)      \
-    KVQ_DECODE_TILES(DT, 4, 128, 8, 8)       \
-    KVQ_DECODE_TILES(DT, 2, 128, 8, 16)      \
-    KVQ_DECODE_TILES(DT, 4, 64, 1, 16)       \
-    KVQ_DECODE_TILES(DT, 2, 64, 1, 16)       \
-    KVQ_DECODE_TILES(DT, 4, 64, 2, 16)       \
-    KVQ_DECODE_TILES(DT, 2, 64, 2, 16)       \
-    KVQ_DECODE_TILES(DT, 4, 64, 4, 16)       \
-    KVQ_DECODE_TILES(DT, 2, 64, 4, 16)       \
-    KVQ_DECODE_TILES(DT, 4, 64, 8, 8)        \
-    KVQ_DECODE_TILES(DT, 2, 64, 8, 16)
+#define KVQ_DECODE_GROUPS_GQA(BITS, D_, GQ_, CPL_) \
+    KVQ_DECODE_CASE(BITS, D_, GQ_, CPL_, 32, 1)    \
+    KVQ_DECODE_CASE(BITS, D_, GQ_, CPL_, 32, 2)    \
+    KVQ_DECODE_CASE(BITS, D_, GQ_, CPL_, 32, 4)    \
+    KVQ_DECODE_CASE(BITS, D_, GQ_, CPL_, 32, 8)
 
-#define KVQ_DEFINE_KERNEL_PTR(DT)                                                        \
-    template <>                                                                          \
-    const void* decode_kernel_ptr<DT>(int bits, int D, int gqa, int cpl, int tile) {    \
-        KVQ_DECODE_TABLE(DT)                                                             \
-        return nullptr;                                                                  \
+// CPL for 8 query heads: 8 with 4-bit codes (fewer key digit registers), else 16
+#define KVQ_DECODE_TABLE_D128(BITS)                      \
+    KVQ_DECODE_GROUPS_MHA(BITS, 128, 32)                 \
+    KVQ_DECODE_GROUPS_MHA(BITS, 128, 16)                 \
+    KVQ_DECODE_GROUPS_GQA(BITS, 128, 2, 16)              \
+    KVQ_DECODE_GROUPS_GQA(BITS, 128, 4, 16)              \
+    KVQ_DECODE_GROUPS_GQA(BITS, 128, 8, (BITS == 4 ? 8 : 16))
+
+#define KVQ_DECODE_TABLE_D64(BITS)                       \
+    KVQ_DECODE_GROUPS_MHA(BITS, 64, 16)                  \
+    KVQ_DECODE_GROUPS_GQA(BITS, 64, 2, 16)               \
+    KVQ_DECODE_GROUPS_GQA(BITS, 64, 4, 16)               \
+    KVQ_DECODE_GROUPS_GQA(BITS, 64, 8, (BITS == 4 ? 8 : 16))
+
+#define KVQ_DEFINE_KERNEL_PTR(BITS, D_)                                               \
+    template <>                                                                       \
+    const void* decode_kernel_ptr<BITS, D_>(int gqa, int cpl, int tile, int tpg) {   \
+        KVQ_DECODE_TABLE_D##D_(BITS)                                                  \
+        return nullptr;                                                               \
     }
 
 }  // namespace dec

@@ -44,6 +44,8 @@
 //     KV byte is read from HBM once.
 #pragma once
 
+#include <type_traits>
+
 #include "kvq_internal.h"
 
 namespace kvq {
@@ -63,20 +65,21 @@ struct DecArgs {
     unsigned* counters;  // [BH]
     int64_t ng_cap;
     int rec_bytes, rec_kcodes, rec_vcodes, rec_vmeta;
-    int Hkv, S, R, nS, nfp, G, GV, nvg, log2nvg, gps, ngroups, nsplit, nsplit_cap;
+    int dtype;  // storage dtype of q, sinks and residual (DT_*)
+    int Hkv, S, R, nS, nfp, G, GV, nvg, gps, ngroups, nsplit, nsplit_cap;
     float qscale;  // sm_scale * log2(e)
 };
 
 constexpr int kLimbs = 5;
-constexpr float kLazy = 8.0f;  // running-max slack (log2 units) before a rescale
 
 // ---------------------------------------------------------------------------
 // cross-lane helpers
 // ---------------------------------------------------------------------------
+// Every control used here (quad permutes, row mirrors) reads a valid lane for
+// every lane, so bound_ctrl only lets the move fold into the consuming operation.
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
-                                                                 0xF, 0xF, false));
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
 }
 
 // Sum over aligned groups of N consecutive lanes; every lane of a group gets the
@@ -129,6 +132,56 @@ __device__ __forceinline__ float xor_sum(float v, int from) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// True when the predicate holds on any active lane; the result is a scalar, so a
+// branch on it is a scalar branch.  Used for predicates that are wave-uniform by
+// construction but that the compiler cannot prove uniform.
+__device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
+
+// Buffer loads: a buffer resource (base address and size in scalar registers), a
+// per-lane byte offset, and a wave-uniform byte offset in a scalar register.  The
+// per-lane offsets of a tile stream stay fixed and only the scalar offset moves,
+// so a tile load costs no vector address arithmetic.  Third descriptor dword for
+// gfx9-family raw buffers (32-bit data format, no swizzle, no stride).
+constexpr int kBufferWord3 = 0x00020000;
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferWord3);
+}
+template <int N>
+struct UVec {
+    typedef uint32_t T __attribute__((ext_vector_type(N)));
+};
+template <>
+struct UVec<1> {
+    typedef uint32_t T;
+};
+template <int N>
+__device__ __forceinline__ typename UVec<N>::T bload(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    if constexpr (N == 1) return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+    else if constexpr (N == 2) return __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+    else {
+        static_assert(N == 4, "1, 2 or 4 dwords");
+        return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+    }
+}
+// Element i of a dword vector (or the dword itself).
+template <typename T>
+__device__ __forceinline__ uint32_t elem(const T& v, int i) {
+    if constexpr (sizeof(T) == 4) return v;
+    else return v[i];
+}
+// Hands a whole register tuple to the code that follows.  Without it, the
+// vectors a tile buffer holds are split into single dwords, and such buffers
+// carried around a loop are not kept in the registers their loads write (the
+// back edge then copies them, waiting for the loads in flight).
+template <typename T>
+__device__ __forceinline__ T whole(T v) {
+    asm("" : "+v"(v));
+    return v;
+}
+
 // Orders this wave's LDS writes before its following LDS reads (one wave only).
 __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -171,6 +224,24 @@ __device__ __forceinline__ void store_digits(uint8_t* dst, int stride, int n) {
     }
 }
 
+// Digit `li` (a two's-complement nibble, in the low half of a byte) of the
+// balanced base-16 expansion of each of U integers, stored as U consecutive bytes.
+// Adding C_li = 8 (16^li - 1) / 15 turns the digits below li into their offset
+// (non-negative) form, so the shifted sum holds digit li in its low nibble.
+template <int U>
+__device__ __forceinline__ void store_digit_run(uint8_t* dst, const int (&n)[U], int li) {
+    const int C = (int)((8u * ((1u << (4 * li)) - 1u)) / 15u);
+    uint32_t w[(U + 3) / 4];
+#pragma unroll
+    for (int k = 0; k < (U + 3) / 4; ++k) w[k] = 0;
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+        w[u / 4] |= (((uint32_t)(n[u] + C) >> (4 * li)) & 15u) << (8 * (u % 4));
+    if constexpr (U == 2) *reinterpret_cast<uint16_t*>(dst) = (uint16_t)w[0];
+    else if constexpr (U == 4) *reinterpret_cast<uint32_t*>(dst) = w[0];
+    else *reinterpret_cast<u32x2*>(dst) = u32x2{w[0], w[1]};
+}
+
 __device__ __forceinline__ uint32_t lds32(const uint8_t* p) { return *reinterpret_cast<const uint32_t*>(p); }
 
 // A nibble dword of codes pairs a "lo" run of 4 items (byte k, low nibble) with a
@@ -180,12 +251,11 @@ __device__ __forceinline__ uint32_t digit_dword(const uint8_t* lo, const uint8_t
     return lds32(lo) | (lds32(hi) << 4);
 }
 
-template <int N>
-__device__ __forceinline__ float pick(const float (&a)[N], int i) {
-    float r = a[0];
-#pragma unroll
-    for (int k = 1; k < N; ++k) r = (i == k) ? a[k] : r;
-    return r;
+// One element of the query (storage dtype chosen at run time; wave-uniform).
+__device__ __forceinline__ float load_q(const void* base, int64_t idx, int dtype) {
+    if (dtype == DT_F32) return load_as_f32<DT_F32>(base, idx);
+    if (dtype == DT_BF16) return load_as_f32<DT_BF16>(base, idx);
+    return load_as_f32<DT_F16>(base, idx);
 }
 
 template <int DT, int N>
@@ -194,37 +264,15 @@ __device__ __forceinline__ void load_row(const char* base, int64_t elem0, float 
     for (int c = 0; c < N; ++c) f[c] = load_as_f32<DT>(base, elem0 + c);
 }
 
-template <int LW>
-struct Vec;
-template <>
-struct Vec<1> {
-    using T = uint32_t;
-};
-template <>
-struct Vec<2> {
-    using T = uint2;
-};
-template <>
-struct Vec<4> {
-    using T = uint4;
-};
-
-template <int LW>
-__device__ __forceinline__ void load_words(const uint8_t* p, uint32_t (&w)[LW]) {
-    using T = typename Vec<LW>::T;
-    T v = *reinterpret_cast<const T*>(p);
-    __builtin_memcpy(w, &v, sizeof(T));
-}
-
 // ---------------------------------------------------------------------------
 // LDS carve-up (dynamic shared memory)
 // ---------------------------------------------------------------------------
 template <int D, int GQ, int TILE>
 struct LdsPlan {
-    // per wave: key digits [GQ][limb][D] bytes, weight digits [GQ][nvg][limb][TILE]
-    // bytes, weight scales [GQ][nvg] fp32
+    // per wave: key digits [GQ][limb][D] bytes, then two buffers of weight digits
+    // [GQ][nvg][limb][TILE] bytes (alternating by tile)
     __host__ __device__ static int wave_bytes(int nvg) {
-        const int b = GQ * kLimbs * D + GQ * nvg * kLimbs * TILE + 4 * GQ * nvg;
+        const int b = GQ * kLimbs * D + 2 * GQ * nvg * kLimbs * TILE;
         return (b + 15) & ~15;
     }
     // per workgroup: wave states and combine scratch
@@ -235,7 +283,7 @@ struct LdsPlan {
 // ---------------------------------------------------------------------------
 // the kernel: grid = (nsplit, BH)
 // ---------------------------------------------------------------------------
-template <int DT, int BITS, int D, int GQ, int CPL, int TILE>
+template <int BITS, int D, int GQ, int CPL, int TILE, int TPG>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
     constexpr int LPT = D / CPL;           // key lanes per token
     constexpr int TPW = 64 / LPT;          // tokens per key wave-load
@@ -252,6 +300,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
     static_assert(LW >= 1 && LW * 32 == CPL * BITS, "key lane chunk must be whole dwords");
     static_assert(U >= 1 && U * TPW == TILE, "tile must be whole key wave-loads");
     static_assert(NVL >= 1 && NVL * 2 * TB == TILE, "tile must be whole value wave-loads");
+    static_assert(TPG == 1 || TPG == 2 || TPG == 4 || TPG == 8, "tiles per key group");
+    static_assert(TILE % 32 == 0 && (U == 2 || U == 4 || U == 8), "digit runs of 2, 4 or 8 bytes");
 
     extern __shared__ __align__(16) unsigned char dsm[];
     using LP = LdsPlan<D, GQ, TILE>;
@@ -259,12 +309,14 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
     const int split = blockIdx.x;
     const int64_t bh = blockIdx.y;
     const int b = (int)(bh / a.Hkv), kvh = (int)(bh % a.Hkv);
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    // wave index as a scalar, so that loop bounds and branches derived from it are
+    // wave-uniform (scalar branches, no exec-mask loops)
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int nvg = a.nvg;
 
     uint8_t* kd = dsm + wave * LP::wave_bytes(nvg);            // key digits
-    uint8_t* pd = kd + GQ * kLimbs * D;                         // weight digits
-    float* psc = reinterpret_cast<float*>(pd + GQ * nvg * kLimbs * TILE);
+    uint8_t* pd = kd + GQ * kLimbs * D;                         // weight digits (x2)
     float* wg = reinterpret_cast<float*>(dsm + kWaves * LP::wave_bytes(nvg));
     float* s_acc = wg;                                          // [kWaves][GQ][D]
     float* s_ml = s_acc + kWaves * GQ * D;                      // [kWaves][GQ][2]
@@ -277,7 +329,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
     const int hb = lane >> 5;                  // value half: block parity
     const int c0v = (lane & 31) * VCPL;        // value channels of this lane
     const int gv = c0v / a.GV;                 // their value group
-    const int gz = chunk & (nvg - 1);          // value group of this lane's (token, group) pairs
+    // value scales: lane chunk < nvg of a key slot owns value group `chunk` of the
+    // slot's tokens (nvg <= LPT); the other lanes load a valid duplicate
+    const int gz = chunk & (nvg - 1);
+    const bool owner = chunk < nvg;
     const int64_t qrow0 = (int64_t)b * a.Hkv * GQ + (int64_t)kvh * GQ;
 
     float m[GQ], lpart[GQ], zpart[GQ], accv[GQ][VCPL];
@@ -291,7 +346,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
     }
 
     // Rescales the state when the wave-uniform running max grows.
-    auto update_max = [&](const float (&mt)[GQ]) {
+    auto update_max = [&](const float (&mt)[GQ]) __attribute__((always_inline)) {
         bool grow = false;
         float mnew[GQ];
 #pragma unroll
@@ -299,7 +354,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
             mnew[h] = fmaxf(m[h], mt[h]);
             grow |= mnew[h] > m[h];
         }
-        if (grow) {  // wave-uniform
+        if (wave_any(grow)) {
 #pragma unroll
             for (int h = 0; h < GQ; ++h) {
                 const float f = fast_exp2(m[h] - mnew[h]);
@@ -313,157 +368,128 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
     };
 
     // ---------------- quantized key groups of this split ----------------
-    const int G = a.G;
-    const int tpg = G / TILE;
+    // The loop over the wave's key groups (TILE * TPG tokens each) is unrolled over
+    // BODY tiles (whole groups) and is free of branches: the query fold of a group sits at a
+    // fixed position in the body, and every tile rescales the softmax state and
+    // turns its value dot products into fp32.  (A branch in the loop body makes the
+    // compiler copy the tile buffers at the back edge, which waits for the loads in
+    // flight and serialises the memory stream.)
+    constexpr int BODY = TPG > 4 ? TPG : 4;   // tiles per loop iteration (4 or 8)
+    constexpr int GB = BODY / TPG;            // key groups per loop iteration
     const int g_begin = split * a.gps;
     const int g_end = min(g_begin + a.gps, a.ngroups);
     const int n_my_groups = g_begin + wave < g_end ? (g_end - g_begin - wave + kWaves - 1) / kWaves : 0;
-    const int n_tiles = n_my_groups * tpg;
 
-    if (n_tiles > 0) {
+    {
         float qv[GQ][KM];
 #pragma unroll
         for (int h = 0; h < GQ; ++h)
 #pragma unroll
             for (int j = 0; j < KM; ++j)
-                qv[h][j] = load_as_f32<DT>(a.q, (qrow0 + h) * D + KM * lane + j) * a.qscale;
+                qv[h][j] = load_q(a.q, (qrow0 + h) * D + KM * lane + j, a.dtype) * a.qscale;
 
-        // One tile of this wave's stream; ks/kz are the key scales/zeros of the
-        // tile's group, loaded when the tile is the first of its group.
+        // One tile of the wave's stream.  Key token slot * U + u of the tile is
+        // scored by the LPT lanes of `slot`; value block hb * NVL + vl (TB tokens)
+        // of channels c0v.. is handled by this lane.  ks/kz (key scales and zero
+        // points of this lane's KM fold channels) are loaded with a group's first tile.
         struct Tile {
-            uint32_t k[U][LW];
-            uint32_t v[NVL][VCPL];
-            float2 vm[U];
-            float ks[KM], kz[KM];
+            typename UVec<LW>::T k[U];
+            typename UVec<VCPL>::T v[NVL];
+            u32x2 vm[U];  // value scale, zero point (fp32 bits) of (token, group gz)
+            typename UVec<KM>::T ks, kz;
         };
-        // Loader position: record of the current group and tile within it.  Once the
-        // last tile has been issued, further loads repeat it (never out of range).
-        const uint8_t* lrec = a.rec + rec_offset(bh, g_begin + wave, a.ng_cap, a.rec_bytes);
-        const size_t group_step = (size_t)kWaves * a.rec_bytes;
-        int ltig = 0, issued = 0;
-        const int upairs = U * nvg;
-        auto load_next = [&](Tile& t) {
-            const uint8_t* r = lrec;
-            const int t0 = ltig * TILE;  // first token of the tile in its group
+        const __amdgpu_buffer_rsrc_t rs =
+            make_rsrc(a.rec + rec_offset(bh, 0, a.ng_cap, a.rec_bytes), (uint32_t)(a.ng_cap * a.rec_bytes));
+        const uint32_t grp0 = (uint32_t)(g_begin + wave) * (uint32_t)a.rec_bytes;
+        const uint32_t group_step = (uint32_t)(kWaves * a.rec_bytes);
+        const int last_group = n_my_groups - 1;
+        // per-lane byte offsets, the same for every tile
+        const uint32_t k_off = (uint32_t)a.rec_kcodes + slot * U * RB + chunk * (LW * 4);
+        const uint32_t v_off = (uint32_t)a.rec_vcodes + (hb * NVL * D + c0v) * 4;
+        const uint32_t km_off = KM * lane * 4;
+        uint32_t vm_off[U];
 #pragma unroll
-            for (int u = 0; u < U; ++u)
-                load_words<LW>(r + a.rec_kcodes + (t0 + u * TPW + slot) * RB + chunk * (LW * 4), t.k[u]);
+        for (int u = 0; u < U; ++u) vm_off[u] = (uint32_t)a.rec_vmeta + ((slot * U + u) * nvg + gz) * 8;
+
+        // Loads tile `tig` of the wave's key group j; groups past the last one
+        // reload the last (the loop prefetches one tile beyond its end).
+        auto load = [&](Tile& t, int j, int tig, bool kmeta) __attribute__((always_inline)) {
+            const uint32_t grp = grp0 + (uint32_t)min(j, last_group) * group_step;
+            const int t0 = tig * TILE;
 #pragma unroll
-            for (int vl = 0; vl < NVL; ++vl)
-                load_words<VCPL>(r + a.rec_vcodes + ((size_t)(t0 / TB + 2 * vl + hb) * D + c0v) * 4, t.v[vl]);
-            const float* vmeta = reinterpret_cast<const float*>(r + a.rec_vmeta);
+            for (int u = 0; u < U; ++u) t.k[u] = bload<LW>(rs, k_off + u * RB, grp + t0 * RB);
 #pragma unroll
-            for (int k = 0; k < U; ++k) {
-                int p = chunk + k * LPT;
-                p = p < upairs ? p : chunk;  // unused pairs reload a valid one
-                t.vm[k] = *reinterpret_cast<const float2*>(
-                    vmeta + ((t0 + (p >> a.log2nvg) * TPW + slot) * nvg + gz) * 2);
-            }
-            if (ltig == 0) {  // wave-uniform
-                const float* km = reinterpret_cast<const float*>(r);
+            for (int vl = 0; vl < NVL; ++vl) t.v[vl] = bload<VCPL>(rs, v_off + vl * D * 4, grp + (t0 / TB) * D * 4);
 #pragma unroll
-                for (int j = 0; j < KM; ++j) t.ks[j] = km[KM * lane + j], t.kz[j] = km[D + KM * lane + j];
-            }
-            if (issued + 1 < n_tiles) {
-                ++issued;
-                if (++ltig == tpg) {
-                    ltig = 0;
-                    lrec += group_step;
-                }
+            for (int u = 0; u < U; ++u) t.vm[u] = bload<2>(rs, vm_off[u], grp + t0 * nvg * 8);
+            if (kmeta) {  // constant at every call site
+                t.ks = bload<KM>(rs, km_off, grp);
+                t.kz = bload<KM>(rs, km_off + D * 4, grp);
             }
         };
 
         uint32_t kl[GQ][kLimbs][KND];  // key digit dwords of this lane's channels
         float kinv[GQ], kbias[GQ];
-        int ctig = 0;  // consumer: tile within group
 
-        // Value accumulators in fixed point: per channel and digit, sums of
-        // dot8(weight digits, codes - 8) over all tiles since the last flush; they
-        // represent accv += vinv * sum_i 16^i va[i].  Each dot8 is at most 512 in
-        // magnitude, so they cannot overflow within a split.
-        int va[GQ][VCPL][kLimbs];
-        float vmul[GQ], vinv[GQ];
+        // Folds the key scales of a group into the query, in fixed point: digit
+        // dwords of rint(q_c s_c 2^k) for this lane's key channels, and the
+        // zero-point term sum_c q_c s_c (z_c - bias).
+        auto fold = [&](const Tile& cur) __attribute__((always_inline)) {
+            float qt[GQ][KM], mx[GQ], bp[GQ];
+            const auto ks = whole(cur.ks), kz = whole(cur.kz);
 #pragma unroll
-        for (int h = 0; h < GQ; ++h) {
-            vmul[h] = 0.0f;
-            vinv[h] = 0.0f;
+            for (int h = 0; h < GQ; ++h) {
+                mx[h] = 0.0f;
+                bp[h] = 0.0f;
 #pragma unroll
-            for (int c = 0; c < VCPL; ++c)
-#pragma unroll
-                for (int li = 0; li < kLimbs; ++li) va[h][c][li] = 0;
-        }
-        auto flush_head = [&](int h) {
-            const float w1 = vinv[h] * 16.0f, w2 = vinv[h] * 256.0f, w3 = vinv[h] * 4096.0f,
-                        w4 = vinv[h] * 65536.0f;
-#pragma unroll
-            for (int c = 0; c < VCPL; ++c) {
-                float t = accv[h][c];
-                t = fmaf((float)va[h][c][0], vinv[h], t);
-                t = fmaf((float)va[h][c][1], w1, t);
-                t = fmaf((float)va[h][c][2], w2, t);
-                t = fmaf((float)va[h][c][3], w3, t);
-                t = fmaf((float)va[h][c][4], w4, t);
-                accv[h][c] = t;
-#pragma unroll
-                for (int li = 0; li < kLimbs; ++li) va[h][c][li] = 0;
+                for (int j = 0; j < KM; ++j) {
+                    qt[h][j] = qv[h][j] * __uint_as_float(elem(ks, j));
+                    mx[h] = fmaxf(mx[h], fabsf(qt[h][j]));
+                    bp[h] = fmaf(qt[h][j], __uint_as_float(elem(kz, j)) - (float)ZB, bp[h]);
+                }
             }
+#pragma unroll
+            for (int h = 0; h < GQ; ++h) {
+                const FixScale fs = fix_scale(group_max<64>(mx[h]));
+                kinv[h] = fs.inv;
+                kbias[h] = group_sum<64>(bp[h]);
+#pragma unroll
+                for (int j = 0; j < KM; ++j)
+                    store_digits(kd + (h * kLimbs) * D + KM * lane + j, D, (int)rintf(qt[h][j] * fs.mul));
+            }
+            wave_lds_sync();
+#pragma unroll
+            for (int h = 0; h < GQ; ++h)
+#pragma unroll
+                for (int li = 0; li < kLimbs; ++li) {
+                    const uint8_t* base = kd + (h * kLimbs + li) * D + chunk * CPL;
+#pragma unroll
+                    for (int nd = 0; nd < KND; ++nd) {
+                        if constexpr (BITS == 4)
+                            kl[h][li][nd] = digit_dword(base + 8 * nd, base + 8 * nd + 4);
+                        else
+                            kl[h][li][nd] = digit_dword(base + 16 * (nd >> 1) + 4 * (nd & 1),
+                                                        base + 16 * (nd >> 1) + 8 + 4 * (nd & 1));
+                    }
+                }
         };
 
-        auto process = [&](const Tile& cur) {
-            if (ctig == 0) {
-                // fold the group's key scales into the query, in fixed point
-                float qt[GQ][KM], mx[GQ], bp[GQ];
-#pragma unroll
-                for (int h = 0; h < GQ; ++h) {
-                    mx[h] = 0.0f;
-                    bp[h] = 0.0f;
-#pragma unroll
-                    for (int j = 0; j < KM; ++j) {
-                        qt[h][j] = qv[h][j] * cur.ks[j];
-                        mx[h] = fmaxf(mx[h], fabsf(qt[h][j]));
-                        bp[h] = fmaf(qt[h][j], cur.kz[j] - (float)ZB, bp[h]);
-                    }
-                }
-#pragma unroll
-                for (int h = 0; h < GQ; ++h) {
-                    const FixScale fs = fix_scale(group_max<64>(mx[h]));
-                    kinv[h] = fs.inv;
-                    kbias[h] = group_sum<64>(bp[h]);
-#pragma unroll
-                    for (int j = 0; j < KM; ++j)
-                        store_digits(kd + (h * kLimbs) * D + KM * lane + j, D, (int)rintf(qt[h][j] * fs.mul));
-                }
-                wave_lds_sync();
-#pragma unroll
-                for (int h = 0; h < GQ; ++h)
-#pragma unroll
-                    for (int li = 0; li < kLimbs; ++li) {
-                        const uint8_t* base = kd + (h * kLimbs + li) * D + chunk * CPL;
-#pragma unroll
-                        for (int nd = 0; nd < KND; ++nd) {
-                            if constexpr (BITS == 4)
-                                kl[h][li][nd] = digit_dword(base + 8 * nd, base + 8 * nd + 4);
-                            else
-                                kl[h][li][nd] = digit_dword(base + 16 * (nd >> 1) + 4 * (nd & 1),
-                                                            base + 16 * (nd >> 1) + 8 + 4 * (nd & 1));
-                        }
-                    }
-                wave_lds_sync();
-            }
-            if (++ctig == tpg) ctig = 0;
-
+        // One tile: scores, softmax update, weight digits through LDS (buffer pb of
+        // two, alternating by tile), value dot products folded into fp32.
+        auto process = [&](const Tile& cur, uint8_t* pb) __attribute__((always_inline)) {
             // ---- key scores of this slot's U tokens ----
             float sc[GQ][U];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 uint32_t cw[KND];
+                const auto kw = whole(cur.k[u]);
 #pragma unroll
                 for (int d = 0; d < LW; ++d) {
                     if constexpr (BITS == 4) {
-                        cw[d] = cur.k[u][d] ^ 0x88888888u;
+                        cw[d] = elem(kw, d);  // fields are already code - 8
                     } else {
-                        cw[2 * d] = cur.k[u][d] & 0x33333333u;
-                        cw[2 * d + 1] = (cur.k[u][d] >> 2) & 0x33333333u;
+                        cw[2 * d] = elem(kw, d) & 0x33333333u;
+                        cw[2 * d + 1] = (elem(kw, d) >> 2) & 0x33333333u;
                     }
                 }
 #pragma unroll
@@ -478,192 +504,237 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
                     sc[h][u] = (float)acc;
                 }
             }
-            // ---- online softmax, lazily rescaled: the running max only moves when
-            //      a tile's max exceeds it by more than kLazy (weights stay <= 2^kLazy)
-            float mt[GQ];
-            bool grow = false;
+            // ---- online softmax: wave-uniform running max, rescaled every tile ----
+            float vinv[GQ];
 #pragma unroll
             for (int h = 0; h < GQ; ++h) {
-                mt[h] = -INFINITY;
+                float mt = -INFINITY;
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
                     sc[h][u] = group_sum<LPT>(sc[h][u]) * kinv[h] - kbias[h];
-                    mt[h] = fmaxf(mt[h], sc[h][u]);
+                    mt = fmaxf(mt, sc[h][u]);
                 }
-                mt[h] = slots_max<LPT>(mt[h]);
-                grow |= mt[h] > m[h] + kLazy;
-            }
-            bool rescaled[GQ];
+                mt = slots_max<LPT>(mt);
+                const float mn = fmaxf(m[h], mt);
+                const float f = fast_exp2(m[h] - mn);  // 0 while m is -inf
+                m[h] = mn;
+                lpart[h] *= f;
+                zpart[h] *= f;
 #pragma unroll
-            for (int h = 0; h < GQ; ++h) rescaled[h] = false;
-            if (grow) {  // wave-uniform
-#pragma unroll
-                for (int h = 0; h < GQ; ++h) {
-                    if (mt[h] > m[h] + kLazy) {
-                        flush_head(h);
-                        const float f = fast_exp2(m[h] - mt[h]);
-                        m[h] = mt[h];
-                        lpart[h] *= f;
-                        zpart[h] *= f;
-#pragma unroll
-                        for (int c = 0; c < VCPL; ++c) accv[h][c] *= f;
-                        rescaled[h] = true;
-                    }
-                }
-            }
+                for (int c = 0; c < VCPL; ++c) accv[h][c] *= f;
 
-            // ---- weights p_t s_t -> fixed-point digits in LDS ----
-#pragma unroll
-            for (int h = 0; h < GQ; ++h) {
-                float p[U];
-#pragma unroll
-                for (int u = 0; u < U; ++u) p[u] = fast_exp2(sc[h][u] - m[h]);
+                // ---- weights p_t s_t -> fixed-point digits in LDS ----
                 float pt[U], mx = 0.0f;
 #pragma unroll
-                for (int k = 0; k < U; ++k) {
-                    const int pi = chunk + k * LPT;
-                    const bool valid = pi < upairs;
-                    const float pu = pick(p, pi >> a.log2nvg);
-                    pt[k] = valid ? pu * cur.vm[k].x : 0.0f;
-                    zpart[h] = fmaf(pt[k], cur.vm[k].y - (float)ZB, zpart[h]);
-                    if (valid && gz == 0) lpart[h] += pu;
-                    mx = fmaxf(mx, pt[k]);
+                for (int u = 0; u < U; ++u) {
+                    const float p = fast_exp2(sc[h][u] - mn);
+                    const u32x2 vm = whole(cur.vm[u]);
+                    pt[u] = p * __uint_as_float(vm.x);
+                    // each (token, value group) counted by one lane, each token once
+                    zpart[h] = fmaf(owner ? pt[u] : 0.0f, __uint_as_float(vm.y) - (float)ZB, zpart[h]);
+                    lpart[h] += chunk == 0 ? p : 0.0f;
+                    mx = fmaxf(mx, pt[u]);
                 }
-                mx = group_max<64>(mx);
-                // keep the fixed-point scale unless this tile would overflow it
-                if (rescaled[h] || mx * vmul[h] >= 262144.0f) {  // wave-uniform
-                    if (!rescaled[h]) flush_head(h);
-                    const FixScale fs = fix_scale(mx);
-                    vmul[h] = fs.mul;
-                    vinv[h] = fs.inv;
-                }
-                uint8_t* dst = pd + ((h * nvg + gz) * kLimbs) * TILE;
+                const FixScale fs = fix_scale(group_max<64>(mx));
+                vinv[h] = fs.inv;
+                int n[U];
 #pragma unroll
-                for (int k = 0; k < U; ++k) {
-                    const int pi = chunk + k * LPT;
-                    if (pi < upairs)
-                        store_digits(dst + (pi >> a.log2nvg) * TPW + slot, TILE, (int)rintf(pt[k] * vmul[h]));
-                }
+                for (int u = 0; u < U; ++u) n[u] = (int)rintf(pt[u] * fs.mul);
+                // every lane of a (slot, value group) writes the same bytes
+                uint8_t* dst = pb + ((h * nvg + gz) * kLimbs) * TILE + slot * U;
+#pragma unroll
+                for (int li = 0; li < kLimbs; ++li) store_digit_run<U>(dst + li * TILE, n, li);
             }
             wave_lds_sync();
 
-            // ---- values: dot products along tokens into the fixed-point accumulators ----
+            // ---- values: integer dot products along tokens, digits by Horner ----
+            uint32_t vw[NVL][VCPL][VNE];
+#pragma unroll
+            for (int vl = 0; vl < NVL; ++vl) {
+                const auto vv = whole(cur.v[vl]);
+#pragma unroll
+                for (int c = 0; c < VCPL; ++c) {
+                    if constexpr (BITS == 4) {
+                        vw[vl][c][0] = elem(vv, c);  // fields are already code - 8
+                    } else {
+                        vw[vl][c][0] = elem(vv, c) & 0x33333333u;
+                        vw[vl][c][VNE - 1] = (elem(vv, c) >> 2) & 0x33333333u;
+                    }
+                }
+            }
 #pragma unroll
             for (int h = 0; h < GQ; ++h) {
-                const uint8_t* pbase = pd + ((h * nvg + gv) * kLimbs) * TILE;
+                const uint8_t* pbase = pb + ((h * nvg + gv) * kLimbs) * TILE + hb * (TILE / 2);
+                int acc[VCPL];
 #pragma unroll
-                for (int vl = 0; vl < NVL; ++vl) {
-                    const int blk = 2 * vl + hb;  // block within the tile
-                    uint32_t vw[VCPL][VNE];
+                for (int c = 0; c < VCPL; ++c) acc[c] = 0;
 #pragma unroll
-                    for (int c = 0; c < VCPL; ++c) {
-                        if constexpr (BITS == 4) {
-                            vw[c][0] = cur.v[vl][c] ^ 0x88888888u;
-                        } else {
-                            vw[c][0] = cur.v[vl][c] & 0x33333333u;
-                            vw[c][VNE - 1] = (cur.v[vl][c] >> 2) & 0x33333333u;
-                        }
+                for (int li = kLimbs - 1; li >= 0; --li) {
+                    // digit bytes of this half's TILE / 2 tokens
+                    uint32_t w[TILE / 8];
+#pragma unroll
+                    for (int q4 = 0; q4 < TILE / 32; ++q4) {
+                        const u32x4 x = *reinterpret_cast<const u32x4*>(pbase + li * TILE + 16 * q4);
+                        w[4 * q4] = x.x, w[4 * q4 + 1] = x.y, w[4 * q4 + 2] = x.z, w[4 * q4 + 3] = x.w;
                     }
 #pragma unroll
-                    for (int li = 0; li < kLimbs; ++li) {
-                        const uint8_t* tb = pbase + li * TILE + blk * TB;
+                    for (int c = 0; c < VCPL; ++c) acc[c] <<= 4;
+#pragma unroll
+                    for (int vl = 0; vl < NVL; ++vl) {
                         uint32_t dl[VNE];
                         if constexpr (BITS == 4) {
-                            dl[0] = digit_dword(tb, tb + 4);
+                            dl[0] = w[2 * vl] | (w[2 * vl + 1] << 4);
                         } else {
-                            dl[0] = digit_dword(tb, tb + 8);
-                            dl[VNE - 1] = digit_dword(tb + 4, tb + 12);
+                            dl[0] = w[4 * vl] | (w[4 * vl + 2] << 4);
+                            dl[VNE - 1] = w[4 * vl + 1] | (w[4 * vl + 3] << 4);
                         }
 #pragma unroll
                         for (int c = 0; c < VCPL; ++c)
 #pragma unroll
-                            for (int e = 0; e < VNE; ++e) va[h][c][li] = dot8(dl[e], vw[c][e], va[h][c][li]);
+                            for (int e = 0; e < VNE; ++e) acc[c] = dot8(dl[e], vw[vl][c][e], acc[c]);
                     }
                 }
+#pragma unroll
+                for (int c = 0; c < VCPL; ++c) accv[h][c] = fmaf((float)acc[c], vinv[h], accv[h][c]);
             }
-            wave_lds_sync();
         };
 
-        // three tile buffers: two tiles in flight while one is processed
-        Tile t0, t1, t2;
-        load_next(t0);
-        load_next(t1);
-        for (int i = 0; i < n_tiles; i += 3) {
-            load_next(t2);
-            process(t0);
-            if (i + 1 >= n_tiles) break;
-            load_next(t0);
-            process(t1);
-            if (i + 2 >= n_tiles) break;
-            load_next(t1);
-            process(t2);
+        // A ring of four tile buffers: three tiles are in flight while one is
+        // processed.  Step B of the body processes body tile B (group B / TPG of
+        // the iteration, tile B % TPG) from buffer B % 4 and prefetches body tile
+        // B + 3 into buffer (B + 3) % 4.  The scheduling barriers keep each
+        // buffer's new loads below the last use of its old contents and issue
+        // the prefetch before the wait for the current tile.
+        uint8_t* pd0 = pd;
+        uint8_t* pd1 = pd + GQ * nvg * kLimbs * TILE;
+        Tile t0, t1, t2, t3;
+        if (n_my_groups > 0) {
+            load(t0, 0, 0, true);
+            load(t1, 1 / TPG, 1 % TPG, 1 % TPG == 0);
+            load(t2, 2 / TPG, 2 % TPG, 2 % TPG == 0);
         }
-#pragma unroll
-        for (int h = 0; h < GQ; ++h) flush_head(h);
-    }
 
-    // ---------------- full-precision tokens (sinks, residual) ----------------
-    const int f0 = (int)((int64_t)split * a.nfp / a.nsplit);
-    const int f1 = (int)((int64_t)(split + 1) * a.nfp / a.nsplit);
-    if (f1 > f0) {
-        float qf[GQ][CPL];
+        // ---------------- full-precision tokens (sinks, residual) ----------------
+        // Scored while the first quantized tiles are in flight, with a lane map of
+        // their own (CPLF channels per lane, few registers).  Each step loads all
+        // its key and value rows before any arithmetic; rows past the split's end
+        // reload its first row and get weight 0.
+        const int f0 = (int)((int64_t)split * a.nfp / a.nsplit);
+        const int f1 = (int)((int64_t)(split + 1) * a.nfp / a.nsplit);
+        if (f1 > f0) {
+            constexpr int CPLF = 16;          // key channels per lane
+            constexpr int LPTF = D / CPLF;    // lanes per token
+            constexpr int TPWF = 64 / LPTF;   // tokens per wave step
+            const int slotf = lane / LPTF, chunkf = lane % LPTF;
+            float qf[GQ][CPLF];
 #pragma unroll
-        for (int h = 0; h < GQ; ++h)
+            for (int h = 0; h < GQ; ++h)
 #pragma unroll
-            for (int c = 0; c < CPL; ++c)
-                qf[h][c] = load_as_f32<DT>(a.q, (qrow0 + h) * D + chunk * CPL + c) * a.qscale;
-        auto row_of = [&](int j, const char*& kp, const char*& vp) -> int64_t {
-            if (j < a.nS) {
-                kp = a.ksink, vp = a.vsink;
-                return bh * a.S + j;
-            }
-            kp = a.kres, vp = a.vres;
-            return bh * a.R + (j - a.nS);
-        };
-        for (int j0 = f0 + wave * TPW; j0 < f1; j0 += kWaves * TPW) {
-            const int j = j0 + slot;
-            const bool valid = j < f1;
-            float s[GQ];
-            {
-                float kf[CPL];
-                const char *kp, *vp;
-                const int64_t row = row_of(valid ? j : f0, kp, vp);
-                load_row<DT, CPL>(kp, row * D + chunk * CPL, kf);
+                for (int c = 0; c < CPLF; ++c)
+                    qf[h][c] = load_q(a.q, (qrow0 + h) * D + chunkf * CPLF + c, a.dtype) * a.qscale;
+            auto row_of = [&](int j, const char*& kp, const char*& vp) -> int64_t {
+                if (j < a.nS) {
+                    kp = a.ksink, vp = a.vsink;
+                    return bh * a.S + j;
+                }
+                kp = a.kres, vp = a.vres;
+                return bh * a.R + (j - a.nS);
+            };
+            // the token loop, for the storage dtype of this cache
+            auto fp_tokens = [&](auto dtc) __attribute__((always_inline)) {
+                constexpr int DT = decltype(dtc)::value;
+                for (int j0 = f0 + wave * TPWF; j0 < f1; j0 += kWaves * TPWF) {
+                    const int j = j0 + slotf;
+                    const bool valid = j < f1;
+                    float kf[CPLF];
+                    float vf[TPWF / 2][VCPL];  // value rows: half hb takes slots hb, hb + 2, ...
+                    {
+                        const char *kp, *vp;
+                        const int64_t row = row_of(valid ? j : f0, kp, vp);
+                        load_row<DT, CPLF>(kp, row * D + chunkf * CPLF, kf);
+                    }
 #pragma unroll
-                for (int h = 0; h < GQ; ++h) {
-                    float t = 0.0f;
+                    for (int k = 0; k < TPWF / 2; ++k) {
+                        const int jt = j0 + 2 * k + hb;
+                        const char *kp, *vp;
+                        const int64_t row = row_of(jt < f1 ? jt : f0, kp, vp);
+                        load_row<DT, VCPL>(vp, row * D + c0v, vf[k]);
+                    }
+                    float s[GQ];
 #pragma unroll
-                    for (int c = 0; c < CPL; ++c) t = fmaf(qf[h][c], kf[c], t);
-                    t = group_sum<LPT>(t);
-                    s[h] = valid ? t : -INFINITY;
+                    for (int h = 0; h < GQ; ++h) {
+                        float t = 0.0f;
+#pragma unroll
+                        for (int c = 0; c < CPLF; ++c) t = fmaf(qf[h][c], kf[c], t);
+                        t = group_sum<LPTF>(t);
+                        s[h] = valid ? t : -INFINITY;
+                    }
+                    float mt[GQ];
+#pragma unroll
+                    for (int h = 0; h < GQ; ++h) mt[h] = xor_max(s[h], LPTF);
+                    update_max(mt);
+                    float pv[GQ];
+#pragma unroll
+                    for (int h = 0; h < GQ; ++h) {
+                        pv[h] = valid ? fast_exp2(s[h] - m[h]) : 0.0f;
+                        if (chunkf == 0) lpart[h] += pv[h];
+                    }
+#pragma unroll
+                    for (int k = 0; k < TPWF / 2; ++k) {
+                        const int sl = 2 * k + hb;
+#pragma unroll
+                        for (int h = 0; h < GQ; ++h) {
+                            const float psl = __shfl(pv[h], sl * LPTF);  // 0 past the end
+#pragma unroll
+                            for (int c = 0; c < VCPL; ++c) accv[h][c] = fmaf(psl, vf[k][c], accv[h][c]);
+                        }
+                    }
+                }
+            };
+            if (a.dtype == DT_BF16) fp_tokens(std::integral_constant<int, DT_BF16>());
+            else if (a.dtype == DT_F16) fp_tokens(std::integral_constant<int, DT_F16>());
+            else fp_tokens(std::integral_constant<int, DT_F32>());
+        }
+
+        // ---------------- the quantized stream ----------------
+        if (n_my_groups > 0) {
+            const int n_iter = n_my_groups / GB;
+            auto step = [&](auto bc, int it, Tile& cur, Tile& nxt) __attribute__((always_inline)) {
+                constexpr int B = decltype(bc)::value;
+                constexpr int NB = B + 3;  // body tile to prefetch (may be in the next iteration)
+                load(nxt, it * GB + NB / TPG, NB % TPG, NB % TPG == 0);
+                __builtin_amdgcn_sched_barrier(0);
+                if constexpr (B % TPG == 0) fold(cur);
+                process(cur, (B & 1) ? pd1 : pd0);
+                __builtin_amdgcn_sched_barrier(0);
+            };
+            for (int it = 0; it < n_iter; ++it) {
+                step(std::integral_constant<int, 0>(), it, t0, t3);
+                step(std::integral_constant<int, 1>(), it, t1, t0);
+                step(std::integral_constant<int, 2>(), it, t2, t1);
+                step(std::integral_constant<int, 3>(), it, t3, t2);
+                if constexpr (BODY == 8) {
+                    step(std::integral_constant<int, 4>(), it, t0, t3);
+                    step(std::integral_constant<int, 5>(), it, t1, t0);
+                    step(std::integral_constant<int, 6>(), it, t2, t1);
+                    step(std::integral_constant<int, 7>(), it, t3, t2);
                 }
             }
-            float mt[GQ];
-#pragma unroll
-            for (int h = 0; h < GQ; ++h) mt[h] = xor_max(s[h], LPT);
-            update_max(mt);
-            float pv[GQ];
-#pragma unroll
-            for (int h = 0; h < GQ; ++h) {
-                pv[h] = valid ? fast_exp2(s[h] - m[h]) : 0.0f;
-                if (chunk == 0) lpart[h] += pv[h];
-            }
-            // value rows: half hb takes slots hb, hb + 2, ...
-            for (int k = 0; k < TPW / 2; ++k) {
-                const int sl = 2 * k + hb;
-                float psl[GQ];
-#pragma unroll
-                for (int h = 0; h < GQ; ++h) psl[h] = __shfl(pv[h], sl * LPT);
-                const int jt = j0 + sl;
-                if (jt < f1) {
-                    const char *kp, *vp;
-                    const int64_t row = row_of(jt, kp, vp);
-                    float vf[VCPL];
-                    load_row<DT, VCPL>(vp, row * D + c0v, vf);
-#pragma unroll
-                    for (int h = 0; h < GQ; ++h)
-#pragma unroll
-                        for (int c = 0; c < VCPL; ++c) accv[h][c] = fmaf(psl[h], vf[c], accv[h][c]);
+            // Groups after the last whole iteration: fewer than GB, at most three
+            // tiles, already in t0, t1, t2.
+            if constexpr (GB > 1) {
+                const int tail = (n_my_groups - n_iter * GB) * TPG;
+                if (tail >= 1) {
+                    fold(t0);
+                    process(t0, pd0);
+                }
+                if (tail >= 2) {
+                    if constexpr (TPG == 1) fold(t1);
+                    process(t1, pd1);
+                }
+                if (tail >= 3) {
+                    fold(t2);  // TPG == 1
+                    process(t2, pd0);
                 }
             }
         }

@@ -46,6 +46,8 @@ kvq_status ok() {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+Layout make_layout(const kvq_config* c);
+
 kvq_status validate(const kvq_config* c) {
     if (!c) return fail(KVQ_ERR_INVALID_ARG, "config is NULL");
     if (c->reserved != 0) return fail(KVQ_ERR_INVALID_ARG, "reserved field must be 0");
@@ -74,12 +76,18 @@ kvq_status validate(const kvq_config* c) {
     const int g = c->n_q_heads / c->n_kv_heads;
     if (g != 1 && g != 2 && g != 4 && g != 8)
         return fail(KVQ_ERR_UNSUPPORTED, "n_q_heads / n_kv_heads must be 1, 2, 4 or 8");
-    if (c->k_group % 32 != 0 || c->k_group > 256)
-        return fail(KVQ_ERR_UNSUPPORTED, "k_group must be a multiple of 32 and at most 256");
+    if (c->k_group != 32 && c->k_group != 64 && c->k_group != 128 && c->k_group != 256)
+        return fail(KVQ_ERR_UNSUPPORTED, "k_group must be 32, 64, 128 or 256");
     if (c->v_group < 16 || c->v_group % 16 != 0)
         return fail(KVQ_ERR_UNSUPPORTED, "v_group must be a multiple of 16");
     if ((int64_t)c->batch * c->n_kv_heads > 65535)
         return fail(KVQ_ERR_UNSUPPORTED, "batch * n_kv_heads must be at most 65535");
+    {   // the decode kernel addresses one slice's records with 32-bit offsets
+        const Layout L = make_layout(c);
+        if (L.ng_cap * (int64_t)L.rec_bytes > (int64_t)INT32_MAX)
+            return fail(KVQ_ERR_UNSUPPORTED, "max_tokens %lld gives more than 2 GiB of quantized "
+                        "records per (sequence, kv head)", (long long)c->max_tokens);
+    }
     return KVQ_OK;
 }
 

@@ -79,6 +79,7 @@ struct QuantArgs {
 };
 
 // key rows: dword w of token row t holds channels CPD*w + j at pack_shift(j)
+// (each field biased by code_bias)
 template <int BITS>
 __device__ inline void pack_rows(const uint8_t* s_codes, int rows, int D, int row_bytes,
                                  uint8_t* dst_row0) {
@@ -89,12 +90,13 @@ __device__ inline void pack_rows(const uint8_t* s_codes, int rows, int D, int ro
         const uint8_t* c = s_codes + t * D + w * CPD;
         uint32_t word = 0;
 #pragma unroll
-        for (int j = 0; j < CPD; ++j) word |= (uint32_t)c[j] << pack_shift(BITS, j);
+        for (int j = 0; j < CPD; ++j) word |= ((uint32_t)c[j] ^ code_bias(BITS)) << pack_shift(BITS, j);
         reinterpret_cast<uint32_t*>(dst_row0 + (int64_t)t * row_bytes)[w] = word;
     }
 }
 
 // value blocks: dword (b, c) holds tokens TB*b + j of channel c at pack_shift(j)
+// (each field biased by code_bias)
 template <int BITS>
 __device__ inline void pack_blocks(const uint8_t* s_codes, int rows, int D, uint32_t* dst) {
     constexpr int TB = 32 / BITS;  // tokens per dword
@@ -103,7 +105,8 @@ __device__ inline void pack_blocks(const uint8_t* s_codes, int rows, int D, uint
         const int b = i / D, c = i % D;
         uint32_t word = 0;
 #pragma unroll
-        for (int j = 0; j < TB; ++j) word |= (uint32_t)s_codes[(b * TB + j) * D + c] << pack_shift(BITS, j);
+        for (int j = 0; j < TB; ++j)
+            word |= ((uint32_t)s_codes[(b * TB + j) * D + c] ^ code_bias(BITS)) << pack_shift(BITS, j);
         dst[i] = word;
     }
 }
@@ -182,13 +185,13 @@ struct DeqArgs {
 __device__ inline uint32_t key_code(const DeqArgs& a, const uint8_t* rec, int t, int c) {
     const int cpd = 32 / a.bits;
     const uint32_t w = reinterpret_cast<const uint32_t*>(rec + a.rec_kcodes + (int64_t)t * a.row_bytes)[c / cpd];
-    return (w >> pack_shift(a.bits, c % cpd)) & ((1u << a.bits) - 1u);
+    return ((w >> pack_shift(a.bits, c % cpd)) & ((1u << a.bits) - 1u)) ^ code_bias(a.bits);
 }
 
 __device__ inline uint32_t value_code(const DeqArgs& a, const uint8_t* rec, int t, int c) {
     const int tb = 32 / a.bits;
     const uint32_t w = reinterpret_cast<const uint32_t*>(rec + a.rec_vcodes)[(t / tb) * a.D + c];
-    return (w >> pack_shift(a.bits, t % tb)) & ((1u << a.bits) - 1u);
+    return ((w >> pack_shift(a.bits, t % tb)) & ((1u << a.bits) - 1u)) ^ code_bias(a.bits);
 }
 
 template <int DT>

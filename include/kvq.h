@@ -74,8 +74,9 @@ typedef struct kvq_config {
     int32_t n_q_heads;    /* Hq, a multiple of Hkv; Hq / Hkv in {1, 2, 4, 8}      */
     int32_t head_dim;     /* D in {64, 128}                                       */
     int32_t bits;         /* n in {2, 4}                                          */
-    int32_t k_group;      /* G: tokens per key group; a multiple of 16            */
-    int32_t v_group;      /* G_V: channels per value group; divides D, >= 16      */
+    int32_t k_group;      /* G: tokens per key group; 32, 64, 128 or 256          */
+    int32_t v_group;      /* G_V: channels per value group; divides D, a multiple */
+                          /* of 16                                                */
     int32_t residual;     /* R: residual capacity; a multiple of G                */
     int32_t n_sink;       /* S >= 0: leading tokens kept at full precision        */
     int32_t dtype;        /* kvq_dtype of K, V, q and of the sink/residual store  */
@@ -99,8 +100,10 @@ kvq_status kvq_cache_bytes(const kvq_config* cfg, size_t* bytes);
  * initialisation.  *out receives the handle, to be freed with
  * kvq_cache_destroy.  Errors: INVALID_ARG (null pointer, non-positive sizes,
  * Hq % Hkv != 0, R % G != 0, D % G_V != 0, reserved != 0, misaligned buffer),
- * UNSUPPORTED (bits not 2/4, D not 64/128, Hq/Hkv not 1/2/4/8, G % 16 != 0,
- * G_V < 16), BUFFER_TOO_SMALL, DEVICE (no current HIP device).
+ * UNSUPPORTED (bits not 2/4, D not 64/128, Hq/Hkv not 1/2/4/8, G not in
+ * {32, 64, 128, 256}, G_V not a multiple of 16, B * Hkv > 65535, more than
+ * 2 GiB of quantized records per (sequence, kv head)), BUFFER_TOO_SMALL,
+ * DEVICE (no current HIP device).
  */
 kvq_status kvq_cache_create(const kvq_config* cfg, void* dev_buf, size_t bytes,
                             kvq_cache** out);

@@ -64,8 +64,10 @@ def _attend_and_check(w, cache, K, V, seed=5):
     dict(n_q_heads=16, bits=2),                         # GQA 8
     dict(n_q_heads=16, bits=4, head_dim=64),            # GQA 8, D64
     dict(n_sink=3),
-    dict(k_group=64, residual=128, v_group=128),
-    dict(k_group=96, residual=192, v_group=64),         # group not a power of two
+    dict(k_group=64, residual=128, v_group=128),        # 64-token tiles, one per group
+    dict(k_group=128, residual=128, v_group=64),        # two tiles per group
+    dict(n_q_heads=8, k_group=128, residual=128),       # GQA 4, four tiles per group
+    dict(n_q_heads=8, bits=2, k_group=64, residual=128, v_group=64),  # GQA 4, two per group
 ])
 @pytest.mark.parametrize("n", [1, 63, 64, 65, 200])
 def test_variants_against_oracle(kw, n):
@@ -74,6 +76,24 @@ def test_variants_against_oracle(kw, n):
     log("case %s n=%d" % (kw, n))
     cache = make_cache(w, max_tokens=256)
     K, V = _tokens(w, n, 11, 2.0), _tokens(w, n, 12)
+    cache.append(to_torch(K, w.dtype, DEV), to_torch(V, w.dtype, DEV))
+    sts, err = _attend_and_check(w, cache, K, V)
+    ex = export_cpu(cache)
+    for (b, h), st in sts.items():
+        assert_export_slice_matches(ex, st, b, h)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(k_group=256, residual=256, v_group=128),                # 64-token tiles, four per group
+    dict(k_group=256, residual=256, n_q_heads=4, bits=2),        # GQA 2, eight 32-token tiles
+])
+@pytest.mark.parametrize("n", [600, 1100])
+def test_long_groups_against_oracle(kw, n):
+    require_gpu()
+    w = _w(**kw)
+    log("case %s n=%d" % (kw, n))
+    cache = make_cache(w, max_tokens=1200)
+    K, V = _tokens(w, n, 21, 2.0), _tokens(w, n, 22)
     cache.append(to_torch(K, w.dtype, DEV), to_torch(V, w.dtype, DEV))
     sts, err = _attend_and_check(w, cache, K, V)
     ex = export_cpu(cache)

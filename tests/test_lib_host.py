@@ -65,6 +65,8 @@ def test_cache_bytes_matches_layout(kw):
     (dict(residual=100), kvq.KVQ_ERR_INVALID_ARG),
     (dict(v_group=48), kvq.KVQ_ERR_INVALID_ARG),
     (dict(k_group=48, residual=96), kvq.KVQ_ERR_UNSUPPORTED),
+    (dict(k_group=96, residual=192), kvq.KVQ_ERR_UNSUPPORTED),
+    (dict(k_group=16, residual=64), kvq.KVQ_ERR_UNSUPPORTED),
     (dict(k_group=512, residual=512), kvq.KVQ_ERR_UNSUPPORTED),
     (dict(v_group=8), kvq.KVQ_ERR_UNSUPPORTED),
     (dict(batch=0), kvq.KVQ_ERR_INVALID_ARG),
