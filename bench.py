@@ -39,7 +39,8 @@ METRIC = "effective KV GB/s (and % HBM peak) of quantized decode attention; toke
 HBM_PEAK_GBS = 8000.0
 MALL_BYTES = 256 * 2 ** 20
 DEFAULT_WORKLOAD = "llama7b_mha_int4"
-DECODE_SOURCES = ["decode_impl.h", "decode_dispatch.h", "decode.hip", "kvq_internal.h"]
+DECODE_SOURCES = ["decode_impl.h", "decode_dispatch.h", "decode.hip", "kvq_internal.h",
+                  "decode_b4_d128.hip", "decode_b2_d128.hip", "decode_b4_d64.hip", "decode_b2_d64.hip"]
 
 
 def algorithmic_bytes(w: wl.Workload, n_sink: int, n_quant: int, n_resid: int) -> int:
@@ -71,6 +72,55 @@ def traffic_from_profile(w: wl.Workload):
     if t.get("decode_source_hash") != decode_source_hash():
         return None
     return t.get("hbm_bytes_per_launch")
+
+
+COPY_PROBE_BYTES = 1 << 30
+
+
+def copy_probe(torch, dev):
+    """A plain device copy of known size (1 GiB read, 1 GiB written), ten times, so
+    that rocprofv3's FETCH_SIZE / WRITE_SIZE per dispatch can be scaled to bytes."""
+    src = torch.ones(COPY_PROBE_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(10):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": COPY_PROBE_BYTES, "copy_probe_bytes_written": COPY_PROBE_BYTES,
+                      "dispatches": 10}))
+
+
+def _counter_means(path: str, name_part: str) -> dict:
+    """Mean value per dispatch of each counter of the kernels whose name contains name_part."""
+    import csv
+    sums, counts = {}, {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if name_part in r["Kernel_Name"]:
+                k = r["Counter_Name"]
+                sums[k] = sums.get(k, 0.0) + float(r["Counter_Value"])
+                counts[k] = counts.get(k, 0) + 1
+    return {k: sums[k] / counts[k] for k in sums}
+
+
+def write_traffic(w: wl.Workload, dec_fetch: str, dec_write: str, copy_fetch: str, copy_write: str):
+    """HBM bytes per decode launch: the decode kernel's FETCH_SIZE and WRITE_SIZE (KiB per
+    dispatch) scaled by what the same counters read for the 1 GiB copy probe."""
+    f_dec = _counter_means(dec_fetch, "decode_kernel")["FETCH_SIZE"]
+    w_dec = _counter_means(dec_write, "decode_kernel")["WRITE_SIZE"]
+    f_cp = _counter_means(copy_fetch, "elementwise")["FETCH_SIZE"]
+    w_cp = _counter_means(copy_write, "elementwise")["WRITE_SIZE"]
+    k_fetch = COPY_PROBE_BYTES / (f_cp * 1024.0)
+    k_write = COPY_PROBE_BYTES / (w_cp * 1024.0)
+    out = {"workload": w.name, "decode_source_hash": decode_source_hash(),
+           "fetch_kib_per_dispatch": f_dec, "write_kib_per_dispatch": w_dec,
+           "copy_probe_fetch_kib": f_cp, "copy_probe_write_kib": w_cp,
+           "fetch_scale": k_fetch, "write_scale": k_write,
+           "hbm_bytes_per_launch": int(f_dec * 1024.0 * k_fetch + w_dec * 1024.0 * k_write)}
+    path = os.path.join(ROOT, "profiles", "decode_traffic_%s.json" % w.name)
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
 
 
 class HipEvents:
@@ -163,7 +213,17 @@ def main():
     ap.add_argument("--split-tokens", type=int, default=0)
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="run only a plain 1 GiB device copy (calibrates the HBM byte counters)")
+    ap.add_argument("--write-traffic", nargs=4, metavar=("DECODE_FETCH", "DECODE_WRITE", "COPY_FETCH",
+                                                         "COPY_WRITE"),
+                    help="write profiles/decode_traffic_<workload>.json from rocprofv3 --pmc "
+                         "counter_collection.csv files of the bench and of --copy-probe (no GPU)")
     args = ap.parse_args()
+
+    if args.write_traffic:
+        write_traffic(wl.get(args.workload), *args.write_traffic)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: this path runs on one GPU; a run on %d GPUs is not provided "
@@ -180,6 +240,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
+    if args.copy_probe:
+        copy_probe(torch, dev)
+        return
     w = wl.get(args.workload)
 
     # size of one cache's decode traffic; enough layers to overflow the MALL 3x
