@@ -251,17 +251,27 @@ __device__ __forceinline__ uint32_t digit_dword(const uint8_t* lo, const uint8_t
     return lds32(lo) | (lds32(hi) << 4);
 }
 
-// One element of the query (storage dtype chosen at run time; wave-uniform).
-__device__ __forceinline__ float load_q(const void* base, int64_t idx, int dtype) {
-    if (dtype == DT_F32) return load_as_f32<DT_F32>(base, idx);
-    if (dtype == DT_BF16) return load_as_f32<DT_BF16>(base, idx);
-    return load_as_f32<DT_F16>(base, idx);
+// nw dwords from p (aligned to the largest load used): 16-byte loads where they
+// fit, then 8 and 4.
+__device__ __forceinline__ void load_dwords(const char* p, uint32_t* w, int nw) {
+    int i = 0;
+    for (; i + 4 <= nw; i += 4) {
+        const uint4 x = *reinterpret_cast<const uint4*>(p + 4 * i);
+        w[i] = x.x, w[i + 1] = x.y, w[i + 2] = x.z, w[i + 3] = x.w;
+    }
+    for (; i + 2 <= nw; i += 2) {
+        const uint2 x = *reinterpret_cast<const uint2*>(p + 4 * i);
+        w[i] = x.x, w[i + 1] = x.y;
+    }
+    for (; i < nw; ++i) w[i] = *reinterpret_cast<const uint32_t*>(p + 4 * i);
 }
 
-template <int DT, int N>
-__device__ __forceinline__ void load_row(const char* base, int64_t elem0, float (&f)[N]) {
-#pragma unroll
-    for (int c = 0; c < N; ++c) f[c] = load_as_f32<DT>(base, elem0 + c);
+// Element i of packed storage words as fp32.
+template <int DT>
+__device__ __forceinline__ float packed_f32(const uint32_t* w, int i) {
+    if constexpr (DT == DT_F32) return __uint_as_float(w[i]);
+    else if constexpr (DT == DT_BF16) return __uint_as_float((w[i >> 1] >> (16 * (i & 1))) << 16);
+    else return f16_to_f32((uint16_t)(w[i >> 1] >> (16 * (i & 1))));
 }
 
 // ---------------------------------------------------------------------------
@@ -381,12 +391,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
     const int n_my_groups = g_begin + wave < g_end ? (g_end - g_begin - wave + kWaves - 1) / kWaves : 0;
 
     {
-        float qv[GQ][KM];
-#pragma unroll
-        for (int h = 0; h < GQ; ++h)
-#pragma unroll
-            for (int j = 0; j < KM; ++j)
-                qv[h][j] = load_q(a.q, (qrow0 + h) * D + KM * lane + j, a.dtype) * a.qscale;
+        float qv[GQ][KM];  // folded query of this lane's KM channels (set in the prologue)
 
         // One tile of the wave's stream.  Key token slot * U + u of the tile is
         // scored by the LPT lanes of `slot`; value block hb * NVL + vl (TB tokens)
@@ -412,9 +417,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
         for (int u = 0; u < U; ++u) vm_off[u] = (uint32_t)a.rec_vmeta + ((slot * U + u) * nvg + gz) * 8;
 
         // Loads tile `tig` of the wave's key group j; groups past the last one
-        // reload the last (the loop prefetches one tile beyond its end).
+        // reload the last (the loop prefetches beyond its end).  A wave with no
+        // group reads group 0 of its split's range, or past the records' end,
+        // where buffer loads return zeros; those words are never used.
         auto load = [&](Tile& t, int j, int tig, bool kmeta) __attribute__((always_inline)) {
-            const uint32_t grp = grp0 + (uint32_t)min(j, last_group) * group_step;
+            const uint32_t grp = grp0 + (uint32_t)min(j, max(last_group, 0)) * group_step;
             const int t0 = tig * TILE;
 #pragma unroll
             for (int u = 0; u < U; ++u) t.k[u] = bload<LW>(rs, k_off + u * RB, grp + t0 * RB);
@@ -608,75 +615,98 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
         uint8_t* pd0 = pd;
         uint8_t* pd1 = pd + GQ * nvg * kLimbs * TILE;
         Tile t0, t1, t2, t3;
-        if (n_my_groups > 0) {
-            load(t0, 0, 0, true);
-            load(t1, 1 / TPG, 1 % TPG, 1 % TPG == 0);
-            load(t2, 2 / TPG, 2 % TPG, 2 % TPG == 0);
-        }
 
-        // ---------------- full-precision tokens (sinks, residual) ----------------
-        // Scored while the first quantized tiles are in flight, with a lane map of
-        // their own (CPLF channels per lane, few registers).  Each step loads all
-        // its key and value rows before any arithmetic; rows past the split's end
-        // reload its first row and get weight 0.
+        // ---------------- prologue: full-precision tokens (sinks, residual) ---------
+        // The sinks and residual tokens of the split are scored while the first
+        // quantized tiles are in flight, with a lane map of their own (CPLF channels
+        // per lane, few registers).  Load order: query words, the first iteration's
+        // key and value rows, then the tile prefetch; everything up to the first
+        // iteration's arithmetic is straight-line code for one storage dtype, so
+        // each wait is for its own loads only, not for the prefetch behind them.
+        // Rows past the split's end reload its first row and get weight 0.
         const int f0 = (int)((int64_t)split * a.nfp / a.nsplit);
         const int f1 = (int)((int64_t)(split + 1) * a.nfp / a.nsplit);
-        if (f1 > f0) {
-            constexpr int CPLF = 16;          // key channels per lane
-            constexpr int LPTF = D / CPLF;    // lanes per token
-            constexpr int TPWF = 64 / LPTF;   // tokens per wave step
-            const int slotf = lane / LPTF, chunkf = lane % LPTF;
-            float qf[GQ][CPLF];
+        constexpr int CPLF = 16;          // key channels per lane
+        constexpr int LPTF = D / CPLF;    // lanes per token
+        constexpr int TPWF = 64 / LPTF;   // tokens per wave step
+        const int slotf = lane / LPTF, chunkf = lane % LPTF;
+        // storage row of full-precision token j (sinks first, then the residual);
+        // selects, not branches, so the loads stay in one basic block
+        auto row_of = [&](int j, const char*& kp, const char*& vp) -> int64_t {
+            const bool sink = j < a.nS;
+            kp = sink ? a.ksink : a.kres;
+            vp = sink ? a.vsink : a.vres;
+            return sink ? bh * a.S + j : bh * a.R + (j - a.nS);
+        };
+        auto prologue = [&](auto dtc) __attribute__((always_inline)) {
+            constexpr int DT = decltype(dtc)::value;
+            constexpr int ES = DT == DT_F32 ? 4 : 2;  // bytes per element
+            constexpr int KW = CPLF * ES / 4;         // key dwords per lane and token
+            constexpr int VW = VCPL * ES / 4;         // value dwords per lane and token
+            uint32_t qv_w[GQ][KM], qf_w[GQ][CPLF];
 #pragma unroll
-            for (int h = 0; h < GQ; ++h)
+            for (int h = 0; h < GQ; ++h) {
+                const char* qv_p = reinterpret_cast<const char*>(a.q) + ((qrow0 + h) * D + KM * lane) * ES;
+                if constexpr (KM * ES >= 4) load_dwords(qv_p, qv_w[h], KM * ES / 4);
+                else qv_w[h][0] = *reinterpret_cast<const uint16_t*>(qv_p);  // one 16-bit element
+                load_dwords(reinterpret_cast<const char*>(a.q) + ((qrow0 + h) * D + chunkf * CPLF) * ES, qf_w[h], KW);
+            }
+            // Two wave steps (2 x TPWF tokens) per iteration: the rows of both are
+            // loaded, still packed, before either is scored.
+            uint32_t kw[2][KW];
+            uint32_t vw[2][TPWF / 2][VW];  // value rows: half hb takes slots hb, hb + 2, ...
+            auto load_iter = [&](int j00) __attribute__((always_inline)) {
 #pragma unroll
-                for (int c = 0; c < CPLF; ++c)
-                    qf[h][c] = load_q(a.q, (qrow0 + h) * D + chunkf * CPLF + c, a.dtype) * a.qscale;
-            auto row_of = [&](int j, const char*& kp, const char*& vp) -> int64_t {
-                if (j < a.nS) {
-                    kp = a.ksink, vp = a.vsink;
-                    return bh * a.S + j;
-                }
-                kp = a.kres, vp = a.vres;
-                return bh * a.R + (j - a.nS);
-            };
-            // the token loop, for the storage dtype of this cache
-            auto fp_tokens = [&](auto dtc) __attribute__((always_inline)) {
-                constexpr int DT = decltype(dtc)::value;
-                for (int j0 = f0 + wave * TPWF; j0 < f1; j0 += kWaves * TPWF) {
+                for (int st = 0; st < 2; ++st) {
+                    const int j0 = j00 + st * kWaves * TPWF;
                     const int j = j0 + slotf;
-                    const bool valid = j < f1;
-                    float kf[CPLF];
-                    float vf[TPWF / 2][VCPL];  // value rows: half hb takes slots hb, hb + 2, ...
-                    {
-                        const char *kp, *vp;
-                        const int64_t row = row_of(valid ? j : f0, kp, vp);
-                        load_row<DT, CPLF>(kp, row * D + chunkf * CPLF, kf);
-                    }
+                    const char *kp, *vp;
+                    const int64_t row = row_of(j < f1 ? j : f0, kp, vp);
+                    load_dwords(kp + (row * D + chunkf * CPLF) * ES, kw[st], KW);
 #pragma unroll
                     for (int k = 0; k < TPWF / 2; ++k) {
                         const int jt = j0 + 2 * k + hb;
-                        const char *kp, *vp;
-                        const int64_t row = row_of(jt < f1 ? jt : f0, kp, vp);
-                        load_row<DT, VCPL>(vp, row * D + c0v, vf[k]);
+                        const int64_t vrow = row_of(jt < f1 ? jt : f0, kp, vp);
+                        load_dwords(vp + (vrow * D + c0v) * ES, vw[st][k], VW);
                     }
-                    float s[GQ];
+                }
+            };
+            const int jfirst = f0 + wave * TPWF;
+            load_iter(jfirst);
+            load(t0, 0, 0, true);
+            load(t1, 1 / TPG, 1 % TPG, 1 % TPG == 0);
+            load(t2, 2 / TPG, 2 % TPG, 2 % TPG == 0);
+            __builtin_amdgcn_sched_barrier(0);  // every load above issues before any wait below
+            float qf[GQ][CPLF];
+#pragma unroll
+            for (int h = 0; h < GQ; ++h) {
+#pragma unroll
+                for (int j = 0; j < KM; ++j) qv[h][j] = packed_f32<DT>(qv_w[h], j) * a.qscale;
+#pragma unroll
+                for (int c = 0; c < CPLF; ++c) qf[h][c] = packed_f32<DT>(qf_w[h], c) * a.qscale;
+            }
+            auto score_iter = [&](int j00) __attribute__((always_inline)) {
+#pragma unroll
+                for (int st = 0; st < 2; ++st) {
+                    const int j0 = j00 + st * kWaves * TPWF;
+                    const bool valid = j0 + slotf < f1;
+                    float sc[GQ];
 #pragma unroll
                     for (int h = 0; h < GQ; ++h) {
                         float t = 0.0f;
 #pragma unroll
-                        for (int c = 0; c < CPLF; ++c) t = fmaf(qf[h][c], kf[c], t);
+                        for (int c = 0; c < CPLF; ++c) t = fmaf(qf[h][c], packed_f32<DT>(kw[st], c), t);
                         t = group_sum<LPTF>(t);
-                        s[h] = valid ? t : -INFINITY;
+                        sc[h] = valid ? t : -INFINITY;
                     }
                     float mt[GQ];
 #pragma unroll
-                    for (int h = 0; h < GQ; ++h) mt[h] = xor_max(s[h], LPTF);
+                    for (int h = 0; h < GQ; ++h) mt[h] = xor_max(sc[h], LPTF);
                     update_max(mt);
                     float pv[GQ];
 #pragma unroll
                     for (int h = 0; h < GQ; ++h) {
-                        pv[h] = valid ? fast_exp2(s[h] - m[h]) : 0.0f;
+                        pv[h] = valid ? fast_exp2(sc[h] - m[h]) : 0.0f;
                         if (chunkf == 0) lpart[h] += pv[h];
                     }
 #pragma unroll
@@ -686,15 +716,21 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
                         for (int h = 0; h < GQ; ++h) {
                             const float psl = __shfl(pv[h], sl * LPTF);  // 0 past the end
 #pragma unroll
-                            for (int c = 0; c < VCPL; ++c) accv[h][c] = fmaf(psl, vf[k][c], accv[h][c]);
+                            for (int c = 0; c < VCPL; ++c)
+                                accv[h][c] = fmaf(psl, packed_f32<DT>(vw[st][k], c), accv[h][c]);
                         }
                     }
                 }
             };
-            if (a.dtype == DT_BF16) fp_tokens(std::integral_constant<int, DT_BF16>());
-            else if (a.dtype == DT_F16) fp_tokens(std::integral_constant<int, DT_F16>());
-            else fp_tokens(std::integral_constant<int, DT_F32>());
-        }
+            score_iter(jfirst);  // a no-op when the split has no full-precision token here
+            for (int j00 = jfirst + 2 * kWaves * TPWF; j00 < f1; j00 += 2 * kWaves * TPWF) {
+                load_iter(j00);
+                score_iter(j00);
+            }
+        };
+        if (a.dtype == DT_BF16) prologue(std::integral_constant<int, DT_BF16>());
+        else if (a.dtype == DT_F16) prologue(std::integral_constant<int, DT_F16>());
+        else prologue(std::integral_constant<int, DT_F32>());
 
         // ---------------- the quantized stream ----------------
         if (n_my_groups > 0) {
