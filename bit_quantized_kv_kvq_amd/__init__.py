@@ -30,7 +30,8 @@ STATUS_NAMES = {0: "KVQ_OK", -1: "KVQ_ERR_INVALID_ARG", -2: "KVQ_ERR_UNSUPPORTED
 KVQ_F32, KVQ_BF16, KVQ_F16 = 0, 1, 2
 
 EXPORTED = ["kvq_cache_bytes", "kvq_cache_create", "kvq_cache_destroy", "kvq_append",
-            "kvq_decode_workspace_bytes", "kvq_decode_attention", "kvq_dequantize", "kvq_export",
+            "kvq_decode_workspace_bytes", "kvq_decode_attention", "kvq_append_decode",
+            "kvq_dequantize", "kvq_export",
             "kvq_cache_state", "kvq_set_split_tokens", "kvq_last_error"]
 
 
@@ -71,6 +72,7 @@ def lib() -> ctypes.CDLL:
             "kvq_append": [P, P, P, i64, P],
             "kvq_decode_workspace_bytes": [P, ctypes.POINTER(ctypes.c_size_t)],
             "kvq_decode_attention": [P, P, P, P, P, ctypes.c_size_t, P],
+            "kvq_append_decode": [P, P, P, P, P, P, P, ctypes.c_size_t, P],
             "kvq_dequantize": [P, P, P, P],
             "kvq_export": [P, P, P, P, P, P, P, P],
             "kvq_cache_state": [P] + [ctypes.POINTER(i64)] * 4,
@@ -134,6 +136,14 @@ def kvq_decode_attention(handle: int, q_ptr: int, out_ptr: int, lse_ptr: int, ws
     _check(lib().kvq_decode_attention(ctypes.c_void_p(handle), ctypes.c_void_p(q_ptr),
                                       ctypes.c_void_p(out_ptr), ctypes.c_void_p(lse_ptr or None),
                                       ctypes.c_void_p(ws_ptr), ws_bytes, ctypes.c_void_p(stream)))
+
+
+def kvq_append_decode(handle: int, k_ptr: int, v_ptr: int, q_ptr: int, out_ptr: int, lse_ptr: int,
+                      ws_ptr: int, ws_bytes: int, stream: int):
+    _check(lib().kvq_append_decode(ctypes.c_void_p(handle), ctypes.c_void_p(k_ptr),
+                                   ctypes.c_void_p(v_ptr), ctypes.c_void_p(q_ptr),
+                                   ctypes.c_void_p(out_ptr), ctypes.c_void_p(lse_ptr or None),
+                                   ctypes.c_void_p(ws_ptr), ws_bytes, ctypes.c_void_p(stream)))
 
 
 def kvq_dequantize(handle: int, k_ptr: int, v_ptr: int, stream: int):

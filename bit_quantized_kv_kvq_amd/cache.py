@@ -109,6 +109,29 @@ class Cache:
                                 self.ws_bytes, _stream())
         return out, lse
 
+    def append_decode(self, k: torch.Tensor, v: torch.Tensor, q: torch.Tensor,
+                      out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                      with_lse: bool = True):
+        """One decode step: append one token per sequence (k, v [B, Hkv, 1, D]), then
+        attention of q [B, Hq, D] over the cache, in one library call."""
+        c = self.cfg
+        self._check_tokens(k, "k")
+        self._check_tokens(v, "v")
+        if k.shape[2] != 1 or v.shape[2] != 1:
+            raise ValueError("append_decode appends exactly one token per sequence")
+        if q.dtype != self.dtype or q.device != self.device or not q.is_contiguous() or \
+                tuple(q.shape) != (c.batch, c.n_q_heads, c.head_dim):
+            raise ValueError("q must be a contiguous [B, Hq, D] %s tensor" % self.dtype)
+        if out is None:
+            out = torch.empty((c.batch, c.n_q_heads, c.head_dim), dtype=torch.float32,
+                              device=self.device)
+        if lse is None and with_lse:
+            lse = torch.empty((c.batch, c.n_q_heads), dtype=torch.float32, device=self.device)
+        _k.kvq_append_decode(self.handle, k.data_ptr(), v.data_ptr(), q.data_ptr(), out.data_ptr(),
+                             lse.data_ptr() if lse is not None else 0, self._ws_ptr, self.ws_bytes,
+                             _stream())
+        return out, lse
+
     def dequantize(self) -> Tuple[torch.Tensor, torch.Tensor]:
         """fp32 K', V' [B, Hkv, n_tokens, D] in token order (sinks, quantized, residual)."""
         c = self.cfg

@@ -87,6 +87,8 @@ hipError_t launch_decode(const Layout& L, const DevPtrs& P, const DecodeRequest&
     a.vsink = P.vsink;
     a.kres = P.kres;
     a.vres = P.vres;
+    a.knew = static_cast<const char*>(rq.knew);
+    a.vnew = static_cast<const char*>(rq.vnew);
     a.q = q;
     a.out = out;
     a.lse = lse;

@@ -57,6 +57,8 @@ struct DecArgs {
     const char* vsink;
     const char* kres;
     const char* vres;
+    const char* knew;    // fused append: newest token's K, V rows [BH][D], or null
+    const char* vnew;
     const void* q;
     float* out;
     float* lse;
@@ -136,6 +138,18 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // branch on it is a scalar branch.  Used for predicates that are wave-uniform by
 // construction but that the compiler cannot prove uniform.
 __device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
+
+// A kernel-argument pointer as an opaque wave-uniform value.  Selects between
+// such values stay selects; selects between the argument fields themselves may
+// be rewritten into a per-lane load of the chosen field.
+__device__ __forceinline__ const char* arg_ptr(const char* p) {
+    typedef __attribute__((address_space(1))) const char gchar;
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    // a global-memory pointer, so that accesses through it stay global accesses
+    return (const char*)reinterpret_cast<gchar*>(((uint64_t)hi << 32) | lo);
+}
 
 // Buffer loads: a buffer resource (base address and size in scalar registers), a
 // per-lane byte offset, and a wave-uniform byte offset in a scalar register.  The
@@ -344,6 +358,32 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
     const int gz = chunk & (nvg - 1);
     const bool owner = chunk < nvg;
     const int64_t qrow0 = (int64_t)b * a.Hkv * GQ + (int64_t)kvh * GQ;
+    const char* const ksink = arg_ptr(a.ksink);
+    const char* const vsink = arg_ptr(a.vsink);
+    const char* const kres = arg_ptr(a.kres);
+    const char* const vres = arg_ptr(a.vres);
+    const char* const knew = arg_ptr(a.knew);
+    const char* const vnew = arg_ptr(a.vnew);
+
+    // Fused append: split 0 stores the newest token into its residual row (the
+    // attention below reads it from the input, so no workgroup waits for this
+    // store).  The row is loaded here, first of all loads, and stored after the
+    // prologue, when it has long arrived.  esize * D bytes per row, a multiple
+    // of 16; lanes [0, chunks) carry K, [chunks, 2 chunks) carry V.
+    const bool copy_fresh = knew != nullptr && split == 0 && wave == kWaves - 1;
+    uint4 fresh_word = make_uint4(0u, 0u, 0u, 0u);
+    uint4* fresh_dst = nullptr;
+    if (copy_fresh) {
+        const int es = a.dtype == DT_F32 ? 4 : 2;
+        const int chunks = D * es / 16;
+        const int64_t dst_row = bh * a.R + (a.nfp - 1 - a.nS);
+        if (lane < 2 * chunks) {
+            const bool is_v = lane >= chunks;
+            const int c = is_v ? lane - chunks : lane;
+            fresh_word = reinterpret_cast<const uint4*>((is_v ? vnew : knew) + bh * D * es)[c];
+            fresh_dst = reinterpret_cast<uint4*>(const_cast<char*>(is_v ? vres : kres) + dst_row * D * es) + c;
+        }
+    }
 
     float m[GQ], lpart[GQ], zpart[GQ], accv[GQ][VCPL];
 #pragma unroll
@@ -630,13 +670,20 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
         constexpr int LPTF = D / CPLF;    // lanes per token
         constexpr int TPWF = 64 / LPTF;   // tokens per wave step
         const int slotf = lane / LPTF, chunkf = lane % LPTF;
-        // storage row of full-precision token j (sinks first, then the residual);
-        // selects, not branches, so the loads stay in one basic block
-        auto row_of = [&](int j, const char*& kp, const char*& vp) -> int64_t {
-            const bool sink = j < a.nS;
-            kp = sink ? a.ksink : a.kres;
-            vp = sink ? a.vsink : a.vres;
-            return sink ? bh * a.S + j : bh * a.R + (j - a.nS);
+        // Byte address of element e0 of full-precision token j's key (or value) row:
+        // sinks first, then the residual; with a fused append the newest token
+        // comes from the caller's input.  Chosen by integer selects on finished
+        // addresses (selects between the argument pointers would make the compiler
+        // copy the kernel arguments to scratch memory).
+        auto row_addr = [&](int j, int64_t e0, int es, bool key) -> const char* {
+            typedef __attribute__((address_space(1))) const char gchar;
+            const int64_t erow = (int64_t)D * es;
+            const uint64_t a_sink = reinterpret_cast<uint64_t>(key ? ksink : vsink) + (bh * a.S + j) * erow;
+            const uint64_t a_res = reinterpret_cast<uint64_t>(key ? kres : vres) + (bh * a.R + (j - a.nS)) * erow;
+            const uint64_t a_new = reinterpret_cast<uint64_t>(key ? knew : vnew) + bh * erow;
+            const bool fresh = knew != nullptr && j == a.nfp - 1;
+            const uint64_t x = (fresh ? a_new : j < a.nS ? a_sink : a_res) + e0 * es;
+            return (const char*)reinterpret_cast<gchar*>(x);
         };
         auto prologue = [&](auto dtc) __attribute__((always_inline)) {
             constexpr int DT = decltype(dtc)::value;
@@ -660,14 +707,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
                 for (int st = 0; st < 2; ++st) {
                     const int j0 = j00 + st * kWaves * TPWF;
                     const int j = j0 + slotf;
-                    const char *kp, *vp;
-                    const int64_t row = row_of(j < f1 ? j : f0, kp, vp);
-                    load_dwords(kp + (row * D + chunkf * CPLF) * ES, kw[st], KW);
+                    load_dwords(row_addr(j < f1 ? j : f0, chunkf * CPLF, ES, true), kw[st], KW);
 #pragma unroll
                     for (int k = 0; k < TPWF / 2; ++k) {
                         const int jt = j0 + 2 * k + hb;
-                        const int64_t vrow = row_of(jt < f1 ? jt : f0, kp, vp);
-                        load_dwords(vp + (vrow * D + c0v) * ES, vw[st][k], VW);
+                        load_dwords(row_addr(jt < f1 ? jt : f0, c0v, ES, false), vw[st][k], VW);
                     }
                 }
             };
@@ -731,6 +775,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
         if (a.dtype == DT_BF16) prologue(std::integral_constant<int, DT_BF16>());
         else if (a.dtype == DT_F16) prologue(std::integral_constant<int, DT_F16>());
         else prologue(std::integral_constant<int, DT_F32>());
+        if (fresh_dst != nullptr) *fresh_dst = fresh_word;
 
         // ---------------- the quantized stream ----------------
         if (n_my_groups > 0) {

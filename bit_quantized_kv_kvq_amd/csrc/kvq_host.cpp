@@ -283,6 +283,43 @@ kvq_status kvq_decode_attention(kvq_cache* c, const void* q, float* out, float* 
     return ok();
 }
 
+kvq_status kvq_append_decode(kvq_cache* c, const void* k, const void* v, const void* q, float* out,
+                             float* lse, void* ws, size_t ws_bytes, void* stream) {
+    if (!c || !k || !v || !q || !out || !ws)
+        return fail(KVQ_ERR_INVALID_ARG, "cache, k, v, q, out or ws is NULL");
+    const Layout& L = c->L;
+    // A token that lands in a sink slot or fills the residual (flush) takes the
+    // two-call path; every other token is appended inside the decode launch.
+    if (c->nS < L.S || c->r + 1 >= L.R) {
+        kvq_status st = kvq_append(c, k, v, 1, stream);
+        if (st != KVQ_OK) return st;
+        return kvq_decode_attention(c, q, out, lse, ws, ws_bytes, stream);
+    }
+    if (!aligned(k, 16) || !aligned(v, 16)) return fail(KVQ_ERR_INVALID_ARG, "k and v must be 16-byte aligned");
+    if (!aligned(q, 4) || !aligned(out, 4) || (lse && !aligned(lse, 4)) || !aligned(ws, 256))
+        return fail(KVQ_ERR_INVALID_ARG, "misaligned q, out, lse or ws");
+    const int64_t total = c->nS + c->Lq + c->r;
+    if (1 > L.max_tokens - total)
+        return fail(KVQ_ERR_CAPACITY, "append of 1 token exceeds max_tokens %lld", (long long)L.max_tokens);
+    const size_t need = decode_workspace_bytes(L, c->nsplit_cap);
+    if (ws_bytes < need)
+        return fail(KVQ_ERR_BUFFER_TOO_SMALL, "workspace holds %zu bytes, needs %zu", ws_bytes, need);
+    DecodeRequest rq;
+    rq.Lq = c->Lq;
+    rq.nS = c->nS;
+    rq.r = c->r + 1;
+    rq.split_tokens = c->split_tokens;
+    rq.num_cu = c->num_cu;
+    rq.nsplit_cap = c->nsplit_cap;
+    rq.knew = k;
+    rq.vnew = v;
+    kvq_status st = check_hip(launch_decode(L, c->P, rq, q, out, lse, ws, c->sm_scale, (hipStream_t)stream),
+                              "append_decode");
+    if (st != KVQ_OK) return st;
+    c->r += 1;
+    return ok();
+}
+
 kvq_status kvq_dequantize(const kvq_cache* c, float* k_out, float* v_out, void* stream) {
     if (!c || !k_out || !v_out) return fail(KVQ_ERR_INVALID_ARG, "NULL argument");
     kvq_status st = check_hip(launch_dequantize(c->L, c->P, c->nS, c->Lq, c->r, k_out, v_out,

@@ -110,6 +110,11 @@ struct DecodeRequest {
     int64_t split_tokens;  // tokens per split override (0 = automatic)
     int num_cu;            // compute units of the device
     int nsplit_cap;        // splits per slice the workspace holds
+    // Fused one-token append: the newest residual token (index r - 1) is read from
+    // these [B*Hkv][D] inputs instead of the residual, and split 0 of each slice
+    // writes it to residual row r - 1.  Null for a plain decode.
+    const void* knew = nullptr;
+    const void* vnew = nullptr;
 };
 
 hipError_t launch_decode(const Layout& L, const DevPtrs& P, const DecodeRequest& rq, const void* q,

@@ -155,6 +155,26 @@ kvq_status kvq_decode_attention(kvq_cache* cache, const void* q, float* out, flo
                                 void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * One decode step in one call: append one token per sequence, then decode
+ * attention with the given query; the result and the cache state are exactly
+ * those of kvq_append(cache, k, v, 1, stream) followed by
+ * kvq_decode_attention(cache, q, out, lse, ws, ws_bytes, stream) (KIVI notes,
+ * section 1: the step's key and value join the residual before the logits of
+ * the grouped part and the residual are concatenated).  When the token goes to
+ * the residual without filling it, the append happens inside the decode launch
+ * (the kernel reads the new token from k and v and stores it into the
+ * residual); a token that becomes a sink or fills the residual (a flush) takes
+ * the two-call path.
+ *   k, v : device, [B, Hkv, 1, D] contiguous, in cfg.dtype, 16-byte aligned;
+ *          they must stay unmodified until the enqueued work completes.
+ *   q, out, lse, ws : as for kvq_decode_attention.
+ * Errors: those of kvq_append and kvq_decode_attention; nothing is enqueued and
+ * the state is unchanged when validation fails.
+ */
+kvq_status kvq_append_decode(kvq_cache* cache, const void* k, const void* v, const void* q,
+                             float* out, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Dequantize the whole cache to fp32 in chronological token order (sinks, then
  * the quantized tokens as x' = (q - z) * s, then the residual); the round trip
  * of the Int4 KV-cache post's section 5.1 `quantize` helper.
