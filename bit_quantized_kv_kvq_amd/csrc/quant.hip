@@ -111,56 +111,144 @@ __device__ inline void pack_blocks(const uint8_t* s_codes, int rows, int D, uint
     }
 }
 
+// Storage words of 8 consecutive elements (16 bytes of a 16-bit dtype, 32 bytes
+// of fp32) as fp32.
+template <int DT>
+__device__ inline void load8_f32(const void* base, int64_t elem0, float (&f)[8]) {
+    if constexpr (DT == DT_F32) {
+        const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + elem0);
+        const float4 x = p[0], y = p[1];
+        f[0] = x.x, f[1] = x.y, f[2] = x.z, f[3] = x.w, f[4] = y.x, f[5] = y.y, f[6] = y.z, f[7] = y.w;
+    } else {
+        const uint4 w = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(base) + elem0);
+        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint16_t lo = (uint16_t)(ws[i] & 0xFFFFu), hi = (uint16_t)(ws[i] >> 16);
+            f[2 * i] = DT == DT_BF16 ? bf16_to_f32(lo) : f16_to_f32(lo);
+            f[2 * i + 1] = DT == DT_BF16 ? bf16_to_f32(hi) : f16_to_f32(hi);
+        }
+    }
+}
+
+// Two consecutive elements as fp32.
+template <int DT>
+__device__ inline void load2_f32(const void* base, int64_t elem0, float& x0, float& x1) {
+    if constexpr (DT == DT_F32) {
+        const float2 x = *reinterpret_cast<const float2*>(reinterpret_cast<const float*>(base) + elem0);
+        x0 = x.x, x1 = x.y;
+    } else {
+        const uint32_t w = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint16_t*>(base) + elem0);
+        const uint16_t lo = (uint16_t)(w & 0xFFFFu), hi = (uint16_t)(w >> 16);
+        x0 = DT == DT_BF16 ? bf16_to_f32(lo) : f16_to_f32(lo);
+        x1 = DT == DT_BF16 ? bf16_to_f32(hi) : f16_to_f32(hi);
+    }
+}
+
+// One workgroup per key group.  Keys: thread (channel pair cp, part p) covers
+// tokens [p G/P, (p+1) G/P) of channels 2cp, 2cp+1 (coalesced across the
+// workgroup); the P partial minima/maxima of a channel meet in LDS.  Values: TPI
+// consecutive lanes share one (token, value group), each with GV/TPI channels in
+// runs of 8 (16-byte loads), and meet by lane shuffles.  Every element is read
+// twice (min/max, then codes); the second read hits the caches.  Codes go to LDS
+// and are packed from there.
 template <int DT, int BITS>
 __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
-    extern __shared__ uint8_t s_codes[];  // [G][D]
+    extern __shared__ __align__(16) uint8_t smem[];
     constexpr float qmax = (float)((1 << BITS) - 1);
     const int grp = blockIdx.x;
     const int64_t bh = blockIdx.y;
-    const int D = a.D, G = a.G;
+    const int D = a.D, G = a.G, tid = threadIdx.x;
+    uint8_t* s_codes = smem;                                               // [G][D]
+    float* s_mm = reinterpret_cast<float*>(smem + (((size_t)G * D + 15) & ~(size_t)15));  // [P][D][2]
     const int64_t src_row0 = bh * a.src_tokens + a.src_tok0 + (int64_t)grp * G;
     const int64_t dst_grp = a.dst_tok0 / G + grp;
     uint8_t* rec = a.rec + rec_offset(bh, dst_grp, a.ng_cap, a.rec_bytes);
     float* kmeta = reinterpret_cast<float*>(rec);
 
-    // keys: one group per channel over the G tokens
-    for (int c = threadIdx.x; c < D; c += blockDim.x) {
-        const int64_t base = src_row0 * D + c;
-        float mn = load_as_f32<DT>(a.src_k, base), mx = mn;
-        for (int t = 1; t < G; ++t) {
-            float v = load_as_f32<DT>(a.src_k, base + (int64_t)t * D);
-            if (v < mn) mn = v;
-            if (v > mx) mx = v;
+    // ---- keys ----
+    {
+        const int CH = D / 2;            // channel pairs
+        const int P = 256 / CH;          // token parts (4 for D = 128, 8 for D = 64)
+        const int GP = G / P;            // tokens per thread
+        const int cp = tid % CH, part = tid / CH, c = 2 * cp;
+        const int64_t e0 = (src_row0 + (int64_t)part * GP) * D + c;
+        float mn0 = INFINITY, mn1 = INFINITY, mx0 = -INFINITY, mx1 = -INFINITY;
+#pragma unroll 8
+        for (int t = 0; t < GP; ++t) {
+            float x0, x1;
+            load2_f32<DT>(a.src_k, e0 + (int64_t)t * D, x0, x1);
+            mn0 = fminf(mn0, x0), mx0 = fmaxf(mx0, x0);
+            mn1 = fminf(mn1, x1), mx1 = fmaxf(mx1, x1);
         }
-        QParams p = group_params(mn, mx, qmax);
-        for (int t = 0; t < G; ++t)
-            s_codes[t * D + c] =
-                (uint8_t)group_code(load_as_f32<DT>(a.src_k, base + (int64_t)t * D), p, qmax);
-        kmeta[c] = p.s;
-        kmeta[D + c] = p.z;
+        s_mm[(part * D + c) * 2] = mn0, s_mm[(part * D + c) * 2 + 1] = mx0;
+        s_mm[(part * D + c + 1) * 2] = mn1, s_mm[(part * D + c + 1) * 2 + 1] = mx1;
+        __syncthreads();
+        mn0 = s_mm[c * 2], mx0 = s_mm[c * 2 + 1], mn1 = s_mm[(c + 1) * 2], mx1 = s_mm[(c + 1) * 2 + 1];
+        for (int q = 1; q < P; ++q) {
+            mn0 = fminf(mn0, s_mm[(q * D + c) * 2]), mx0 = fmaxf(mx0, s_mm[(q * D + c) * 2 + 1]);
+            mn1 = fminf(mn1, s_mm[(q * D + c + 1) * 2]), mx1 = fmaxf(mx1, s_mm[(q * D + c + 1) * 2 + 1]);
+        }
+        const QParams p0 = group_params(mn0, mx0, qmax), p1 = group_params(mn1, mx1, qmax);
+#pragma unroll 8
+        for (int t = 0; t < GP; ++t) {
+            float x0, x1;
+            load2_f32<DT>(a.src_k, e0 + (int64_t)t * D, x0, x1);
+            const uint32_t q0 = group_code(x0, p0, qmax), q1 = group_code(x1, p1, qmax);
+            *reinterpret_cast<uint16_t*>(s_codes + (part * GP + t) * D + c) = (uint16_t)(q0 | (q1 << 8));
+        }
+        if (part == 0) {
+            kmeta[c] = p0.s, kmeta[c + 1] = p1.s;
+            kmeta[D + c] = p0.z, kmeta[D + c + 1] = p1.z;
+        }
     }
     __syncthreads();
     pack_rows<BITS>(s_codes, G, D, a.row_bytes, rec + a.rec_kcodes);
     __syncthreads();
 
-    // values: one group per run of G_V channels of each token
-    const int GV = a.GV, nvg = a.nvg;
-    float* vmeta = reinterpret_cast<float*>(rec + a.rec_vmeta);
-    for (int i = threadIdx.x; i < G * nvg; i += blockDim.x) {
-        const int t = i / nvg, h = i % nvg;
-        const int64_t base = (src_row0 + t) * D + (int64_t)h * GV;
-        float mn = load_as_f32<DT>(a.src_v, base), mx = mn;
-        for (int j = 1; j < GV; ++j) {
-            float v = load_as_f32<DT>(a.src_v, base + j);
-            if (v < mn) mn = v;
-            if (v > mx) mx = v;
+    // ---- values ----
+    {
+        const int GV = a.GV, nvg = a.nvg;
+        float* vmeta = reinterpret_cast<float*>(rec + a.rec_vmeta);
+        const int items = G * nvg;
+        int tpi = 256 / items;                    // lanes per (token, group)
+        tpi = tpi < 1 ? 1 : tpi > GV / 8 ? GV / 8 : tpi;
+        const int cpt = GV / tpi;                 // channels per lane, a multiple of 8
+        for (int i0 = 0; i0 < items * tpi; i0 += 256) {
+            const int i = (i0 + tid) / tpi, sub = (i0 + tid) % tpi;
+            const bool live = i < items;
+            const int t = live ? i / nvg : 0, h = live ? i % nvg : 0;
+            const int64_t e0 = (src_row0 + t) * D + (int64_t)h * GV + sub * cpt;
+            float mn = INFINITY, mx = -INFINITY;
+            for (int j = 0; j < cpt; j += 8) {
+                float f[8];
+                load8_f32<DT>(a.src_v, e0 + j, f);
+#pragma unroll
+                for (int k = 0; k < 8; ++k) mn = fminf(mn, f[k]), mx = fmaxf(mx, f[k]);
+            }
+            for (int o = 1; o < tpi; o <<= 1) {   // lanes of one item are consecutive
+                mn = fminf(mn, __shfl_xor(mn, o));
+                mx = fmaxf(mx, __shfl_xor(mx, o));
+            }
+            const QParams p = group_params(mn, mx, qmax);
+            if (live) {
+                for (int j = 0; j < cpt; j += 8) {
+                    float f[8];
+                    load8_f32<DT>(a.src_v, e0 + j, f);
+                    uint32_t lo = 0, hi = 0;
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        lo |= group_code(f[k], p, qmax) << (8 * k);
+                        hi |= group_code(f[k + 4], p, qmax) << (8 * k);
+                    }
+                    *reinterpret_cast<uint2*>(s_codes + t * D + h * GV + sub * cpt + j) = make_uint2(lo, hi);
+                }
+                if (sub == 0) {
+                    vmeta[i * 2] = p.s;
+                    vmeta[i * 2 + 1] = p.z;
+                }
+            }
         }
-        QParams p = group_params(mn, mx, qmax);
-        for (int j = 0; j < GV; ++j)
-            s_codes[t * D + h * GV + j] =
-                (uint8_t)group_code(load_as_f32<DT>(a.src_v, base + j), p, qmax);
-        vmeta[i * 2] = p.s;
-        vmeta[i * 2 + 1] = p.z;
     }
     __syncthreads();
     pack_blocks<BITS>(s_codes, G, D, reinterpret_cast<uint32_t*>(rec + a.rec_vcodes));
@@ -337,7 +425,8 @@ hipError_t launch_quantize(const Layout& L, const DevPtrs& P, const void* src_k,
     a.rec_vcodes = L.rec_vcodes;
     a.rec_vmeta = L.rec_vmeta;
     a.rec = P.rec;
-    const size_t lds = (size_t)L.G * L.D;
+    // codes [G][D] bytes, then the keys' partial minima/maxima [P][D][2] fp32
+    const size_t lds = (((size_t)L.G * L.D + 15) & ~(size_t)15) + (size_t)(256 / (L.D / 2)) * L.D * 2 * sizeof(float);
     dim3 grid((unsigned)n_groups, (unsigned)L.BH);
 #define KVQ_QLAUNCH(DT, BITS) quantize_kernel<DT, BITS><<<grid, 256, lds, stream>>>(a)
     if (L.bits == 4) {
