@@ -15,8 +15,13 @@ model would): every step streams its layer's cache from HBM.
 Prints one JSON line.  `value` is the effective KV bandwidth of the step:
 algorithmic bytes of decode attention (packed codes, scales and zero points,
 full-precision sinks and residual, q in and fp32 out) per step divided by the
-wall time per step.  `roofline.achieved` uses the decode kernel's own duration,
-timed with HIP events on the stream it is launched on.
+wall time per step.  `roofline.achieved` uses the decode kernel's own duration:
+on every EVENT_STRIDE-th timed step the launch records two HIP events at the
+kernel's start and end (kvq_set_timing_events, hipExtLaunchKernel on the stream
+the kernel runs on).  `decode_call_us` is the duration between events recorded
+on the stream around the call, dispatch gaps included.  `stream_read_ceiling`
+is the bandwidth of a plain streaming read (a max-reduction over 1 GiB) on the
+same device: an achievable ceiling beside the 8 TB/s peak, not the denominator.
 """
 from __future__ import annotations
 
@@ -90,6 +95,26 @@ def copy_probe(torch, dev):
     torch.cuda.synchronize()
     print(json.dumps({"copy_probe_bytes_read": COPY_PROBE_BYTES, "copy_probe_bytes_written": COPY_PROBE_BYTES,
                       "dispatches": 10}))
+
+
+def stream_read_ceiling(torch, dev) -> dict:
+    """Bandwidth of a plain streaming read: torch.amax over 1 GiB of int32 (median of 10)."""
+    x = torch.ones(2 ** 28, dtype=torch.int32, device=dev)
+    for _ in range(3):
+        torch.amax(x)
+    times = []
+    for _ in range(10):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        torch.amax(x)
+        b.record()
+        b.synchronize()
+        times.append(a.elapsed_time(b))
+    times.sort()
+    ms = times[len(times) // 2]
+    del x
+    return {"gbs": round(2 ** 30 / (ms * 1e-3) / 1e9, 1), "kernel": "torch.amax over 1 GiB int32",
+            "ms": round(ms, 4)}
 
 
 def _counter_means(path: str, name_part: str) -> dict:
@@ -287,11 +312,16 @@ def main():
 
     stream = torch.cuda.current_stream()
     hip = HipEvents()
-    # Events bracket the decode launch of every EVENT_STRIDE-th timed step: each
-    # event record is a packet on the stream, so timing every step would lengthen
-    # the steps being measured.
+    # Every EVENT_STRIDE-th timed step, the library records two events at the
+    # start and end of the decode kernel itself (kvq_set_timing_events); these
+    # give the kernel duration of the roofline.  Half a stride later, two events
+    # recorded on the stream around the call give the call's duration, dispatch
+    # gaps included (reported beside it).  Timing every step would lengthen the
+    # steps being measured.
     timed_steps = [k for k in range(args.steps) if k % EVENT_STRIDE == 0]
+    call_steps = [k for k in range(args.steps) if k % EVENT_STRIDE == EVENT_STRIDE // 2]
     ev = {k: (hip.create(), hip.create()) for k in timed_steps}
+    ev_call = {k: (hip.create(), hip.create()) for k in call_steps}
 
     # The timed loop calls the C-ABI directly with arguments prepared here, so that
     # the host enqueues a step faster than the GPU runs it: the GPU never waits
@@ -300,6 +330,7 @@ def main():
     lib = kvq.lib()
     append_fn, decode_fn = lib.kvq_append, lib.kvq_decode_attention
     fused_fn = lib.kvq_append_decode
+    set_events = lib.kvq_set_timing_events
     sp = ctypes.c_void_p(stream.cuda_stream)
     out_p, lse_p = ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(lse.data_ptr())
     plan, step_bytes = [], []
@@ -321,22 +352,26 @@ def main():
                      ctypes.c_void_p(c._ws_ptr), c.ws_bytes))
         step_bytes.append(algorithmic_bytes(w, nS, Lq, r))
 
-    def step(s: int, timed_idx):
+    def step(s: int, k):
         fused, h, kp, vp, qp, wsp, wsb = plan[s]
         if not fused:
             st = append_fn(h, kp, vp, 1, sp)
             if st:
                 raise kvq.KVQError(st, kvq.kvq_last_error())
-        if timed_idx is not None:
-            hip.record(ev[timed_idx][0], sp)
+        if k in ev:
+            set_events(h, ev[k][0], ev[k][1])
+        if k in ev_call:
+            hip.record(ev_call[k][0], sp)
         if fused:
             st = fused_fn(h, kp, vp, qp, out_p, lse_p, wsp, wsb, sp)
         else:
             st = decode_fn(h, qp, out_p, lse_p, wsp, wsb, sp)
         if st:
             raise kvq.KVQError(st, kvq.kvq_last_error())
-        if timed_idx is not None:
-            hip.record(ev[timed_idx][1], sp)
+        if k in ev:
+            set_events(h, None, None)
+        if k in ev_call:
+            hip.record(ev_call[k][1], sp)
 
     for s in range(args.warmup):
         step(s, None)
@@ -350,14 +385,15 @@ def main():
         assert tuple(c.state()) == (n, nS, Lq, n - nS - Lq), (li, c.state())
     t0 = time.perf_counter()
     for k in range(args.steps):
-        step(args.warmup + k, k if k in ev else None)
+        step(args.warmup + k, k)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     step_bytes = step_bytes[args.warmup:]
 
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     dec_ms = [hip.elapsed_ms(*ev[k]) for k in timed_steps]
-    hip.destroy([e for pair in ev.values() for e in pair])
+    call_ms = [hip.elapsed_ms(*ev_call[k]) for k in call_steps]
+    hip.destroy([e for d in (ev, ev_call) for pair in d.values() for e in pair])
     dec_avg_ms = sum(dec_ms) / len(dec_ms)
     bytes_avg = sum(step_bytes) / len(step_bytes)
     value = bytes_avg / (ms_per_step * 1e-3) / 1e9
@@ -365,6 +401,8 @@ def main():
     launch_bytes = sum(timed_bytes) / len(timed_bytes)
     achieved = sum(timed_bytes) / (sum(dec_ms) * 1e-3) / 1e9
     traffic = traffic_from_profile(w)
+
+    ceiling = stream_read_ceiling(torch, dev)
 
     cpu = None
     if args.cpu_budget > 0:
@@ -392,6 +430,9 @@ def main():
         "tokens_per_s": round(w.batch / (ms_per_step * 1e-3), 1),
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "decode_kernel_us": round(dec_avg_ms * 1e3, 3),
+        "decode_call_us": round(sum(call_ms) / max(1, len(call_ms)) * 1e3, 3),
+        "stream_read_ceiling": ceiling,
+        "frac_of_stream_ceiling": round(achieved / ceiling["gbs"], 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,

@@ -8,7 +8,7 @@ CPU fallback: if libkvq.so is missing or fails to load, every call raises.
 Low-level functions mirror the C entry points one to one (kvq_cache_bytes,
 kvq_cache_create, kvq_append, kvq_decode_workspace_bytes, kvq_decode_attention,
 kvq_dequantize, kvq_export, kvq_cache_state, kvq_set_split_tokens,
-kvq_last_error); ``Cache`` bundles them with torch-allocated buffers.
+kvq_set_timing_events, kvq_last_error); ``Cache`` bundles them with torch-allocated buffers.
 """
 from __future__ import annotations
 
@@ -32,7 +32,7 @@ KVQ_F32, KVQ_BF16, KVQ_F16 = 0, 1, 2
 EXPORTED = ["kvq_cache_bytes", "kvq_cache_create", "kvq_cache_destroy", "kvq_append",
             "kvq_decode_workspace_bytes", "kvq_decode_attention", "kvq_append_decode",
             "kvq_dequantize", "kvq_export",
-            "kvq_cache_state", "kvq_set_split_tokens", "kvq_last_error"]
+            "kvq_cache_state", "kvq_set_split_tokens", "kvq_set_timing_events", "kvq_last_error"]
 
 
 class KVQError(RuntimeError):
@@ -77,6 +77,7 @@ def lib() -> ctypes.CDLL:
             "kvq_export": [P, P, P, P, P, P, P, P],
             "kvq_cache_state": [P] + [ctypes.POINTER(i64)] * 4,
             "kvq_set_split_tokens": [P, i64],
+            "kvq_set_timing_events": [P, P, P],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -165,6 +166,11 @@ def kvq_cache_state(handle: int) -> Tuple[int, int, int, int]:
 
 def kvq_set_split_tokens(handle: int, tokens: int):
     _check(lib().kvq_set_split_tokens(ctypes.c_void_p(handle), tokens))
+
+
+def kvq_set_timing_events(handle: int, start_event, stop_event):
+    """start_event, stop_event: hipEvent_t handles (int or ctypes.c_void_p), or None, None."""
+    _check(lib().kvq_set_timing_events(ctypes.c_void_p(handle), start_event, stop_event))
 
 
 from .cache import Cache, torch_dtype_code  # noqa: E402  (needs the names above)

@@ -164,6 +164,11 @@ class Cache:
     def set_split_tokens(self, n: int):
         _k.kvq_set_split_tokens(self.handle, n)
 
+    def set_timing_events(self, start_event, stop_event):
+        """Record hipEvent_t handles at the start and end of every later decode kernel
+        of this cache (None, None stops)."""
+        _k.kvq_set_timing_events(self.handle, start_event, stop_event)
+
     def close(self):
         if self.handle is not None:
             _k.kvq_cache_destroy(self.handle)

@@ -1,6 +1,8 @@
 // decode.hip -- decode attention launch: instantiation choice, split planning
 // (about one workgroup per CU) and workspace layout
 // (counters, then split maxima/sums, then split accumulators).
+#include <hip/hip_ext.h>
+
 #include "decode_dispatch.h"
 
 namespace kvq {
@@ -115,8 +117,11 @@ hipError_t launch_decode(const Layout& L, const DevPtrs& P, const DecodeRequest&
     a.nsplit_cap = rq.nsplit_cap;
     a.qscale = sm_scale * 1.4426950408889634f;
     void* args[] = {&a};
-    return hipLaunchKernel(ch.fn, dim3((unsigned)nsplit, (unsigned)L.BH), dim3(kThreads), args,
-                           (size_t)ch.lds, stream);
+    const dim3 grid((unsigned)nsplit, (unsigned)L.BH);
+    if (rq.ev_start != nullptr)
+        return hipExtLaunchKernel(ch.fn, grid, dim3(kThreads), args, (size_t)ch.lds, stream, rq.ev_start,
+                                  rq.ev_stop, 0);
+    return hipLaunchKernel(ch.fn, grid, dim3(kThreads), args, (size_t)ch.lds, stream);
 }
 
 }  // namespace kvq

@@ -139,6 +139,18 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // construction but that the compiler cannot prove uniform.
 __device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
 
+// f(std::integral_constant<int, I>()) for I = 0 .. N - 1, unrolled at compile time.
+template <int I, int N>
+struct StaticFor {
+    template <typename F>
+    __device__ __forceinline__ static void run(F& f) {
+        if constexpr (I < N) {
+            f(std::integral_constant<int, I>());
+            StaticFor<I + 1, N>::run(f);
+        }
+    }
+};
+
 // A kernel-argument pointer as an opaque wave-uniform value.  Selects between
 // such values stay selects; selects between the argument fields themselves may
 // be rewritten into a per-lane load of the chosen field.
@@ -424,8 +436,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
     // turns its value dot products into fp32.  (A branch in the loop body makes the
     // compiler copy the tile buffers at the back edge, which waits for the loads in
     // flight and serialises the memory stream.)
-    constexpr int BODY = TPG > 4 ? TPG : 4;   // tiles per loop iteration (4 or 8)
-    constexpr int GB = BODY / TPG;            // key groups per loop iteration
+    // Ring of NR tile buffers: NR - 1 tiles in flight while one is processed.
+    constexpr int NR = 4;
+    constexpr int BODY = TPG > NR ? TPG : NR;  // tiles per loop iteration (4 or 8)
+    constexpr int GB = BODY / TPG;             // key groups per loop iteration
     const int g_begin = split * a.gps;
     const int g_end = min(g_begin + a.gps, a.ngroups);
     const int n_my_groups = g_begin + wave < g_end ? (g_end - g_begin - wave + kWaves - 1) / kWaves : 0;
@@ -646,15 +660,15 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
             }
         };
 
-        // A ring of four tile buffers: three tiles are in flight while one is
-        // processed.  Step B of the body processes body tile B (group B / TPG of
-        // the iteration, tile B % TPG) from buffer B % 4 and prefetches body tile
-        // B + 3 into buffer (B + 3) % 4.  The scheduling barriers keep each
-        // buffer's new loads below the last use of its old contents and issue
-        // the prefetch before the wait for the current tile.
+        // The tile ring.  Step B of the body processes body tile B (group
+        // B / TPG of the iteration, tile B % TPG) from buffer B % NR and
+        // prefetches body tile B + NR - 1 into buffer (B + NR - 1) % NR.  The
+        // scheduling barriers keep each buffer's new loads below the last use of
+        // its old contents and issue the prefetch before the wait for the
+        // current tile.
         uint8_t* pd0 = pd;
         uint8_t* pd1 = pd + GQ * nvg * kLimbs * TILE;
-        Tile t0, t1, t2, t3;
+        Tile tr[NR];
 
         // ---------------- prologue: full-precision tokens (sinks, residual) ---------
         // The sinks and residual tokens of the split are scored while the first
@@ -717,9 +731,13 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
             };
             const int jfirst = f0 + wave * TPWF;
             load_iter(jfirst);
-            load(t0, 0, 0, true);
-            load(t1, 1 / TPG, 1 % TPG, 1 % TPG == 0);
-            load(t2, 2 / TPG, 2 % TPG, 2 % TPG == 0);
+            auto load_first = [&](auto ic) __attribute__((always_inline)) {
+                constexpr int I = decltype(ic)::value;
+                load(tr[I], I / TPG, I % TPG, I % TPG == 0);
+                // tiles issue in ring order: the loop's waits count on it
+                __builtin_amdgcn_sched_barrier(0);
+            };
+            StaticFor<0, NR - 1>::run(load_first);
             __builtin_amdgcn_sched_barrier(0);  // every load above issues before any wait below
             float qf[GQ][CPLF];
 #pragma unroll
@@ -780,43 +798,29 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
         // ---------------- the quantized stream ----------------
         if (n_my_groups > 0) {
             const int n_iter = n_my_groups / GB;
-            auto step = [&](auto bc, int it, Tile& cur, Tile& nxt) __attribute__((always_inline)) {
+            int it = 0;
+            auto step = [&](auto bc) __attribute__((always_inline)) {
                 constexpr int B = decltype(bc)::value;
-                constexpr int NB = B + 3;  // body tile to prefetch (may be in the next iteration)
-                load(nxt, it * GB + NB / TPG, NB % TPG, NB % TPG == 0);
+                constexpr int NB = B + NR - 1;  // body tile to prefetch (may be in the next iteration)
+                load(tr[NB % NR], it * GB + NB / TPG, NB % TPG, NB % TPG == 0);
                 __builtin_amdgcn_sched_barrier(0);
-                if constexpr (B % TPG == 0) fold(cur);
-                process(cur, (B & 1) ? pd1 : pd0);
+                if constexpr (B % TPG == 0) fold(tr[B % NR]);
+                process(tr[B % NR], (B & 1) ? pd1 : pd0);
                 __builtin_amdgcn_sched_barrier(0);
             };
-            for (int it = 0; it < n_iter; ++it) {
-                step(std::integral_constant<int, 0>(), it, t0, t3);
-                step(std::integral_constant<int, 1>(), it, t1, t0);
-                step(std::integral_constant<int, 2>(), it, t2, t1);
-                step(std::integral_constant<int, 3>(), it, t3, t2);
-                if constexpr (BODY == 8) {
-                    step(std::integral_constant<int, 4>(), it, t0, t3);
-                    step(std::integral_constant<int, 5>(), it, t1, t0);
-                    step(std::integral_constant<int, 6>(), it, t2, t1);
-                    step(std::integral_constant<int, 7>(), it, t3, t2);
-                }
-            }
-            // Groups after the last whole iteration: fewer than GB, at most three
-            // tiles, already in t0, t1, t2.
+            for (; it < n_iter; ++it) StaticFor<0, BODY>::run(step);
+            // Groups after the last whole iteration: fewer than GB, so at most
+            // NR - TPG tiles, already in the first NR - 1 buffers.
             if constexpr (GB > 1) {
                 const int tail = (n_my_groups - n_iter * GB) * TPG;
-                if (tail >= 1) {
-                    fold(t0);
-                    process(t0, pd0);
-                }
-                if (tail >= 2) {
-                    if constexpr (TPG == 1) fold(t1);
-                    process(t1, pd1);
-                }
-                if (tail >= 3) {
-                    fold(t2);  // TPG == 1
-                    process(t2, pd0);
-                }
+                auto tail_step = [&](auto ic) __attribute__((always_inline)) {
+                    constexpr int I = decltype(ic)::value;
+                    if (tail > I) {
+                        if constexpr (I % TPG == 0) fold(tr[I]);
+                        process(tr[I], (I & 1) ? pd1 : pd0);
+                    }
+                };
+                StaticFor<0, NR - TPG>::run(tail_step);
             }
         }
     }

@@ -25,6 +25,7 @@ struct kvq_cache {
     int num_cu;
     int nsplit_cap;           // max splits per slice the workspace holds
     float sm_scale;
+    hipEvent_t ev_start = nullptr, ev_stop = nullptr;  // decode kernel timing (caller's events)
 };
 
 namespace {
@@ -277,6 +278,8 @@ kvq_status kvq_decode_attention(kvq_cache* c, const void* q, float* out, float* 
     rq.split_tokens = c->split_tokens;
     rq.num_cu = c->num_cu;
     rq.nsplit_cap = c->nsplit_cap;
+    rq.ev_start = c->ev_start;
+    rq.ev_stop = c->ev_stop;
     kvq_status st = check_hip(launch_decode(c->L, c->P, rq, q, out, lse, ws, c->sm_scale, (hipStream_t)stream),
                               "decode");
     if (st != KVQ_OK) return st;
@@ -313,6 +316,8 @@ kvq_status kvq_append_decode(kvq_cache* c, const void* k, const void* v, const v
     rq.nsplit_cap = c->nsplit_cap;
     rq.knew = k;
     rq.vnew = v;
+    rq.ev_start = c->ev_start;
+    rq.ev_stop = c->ev_stop;
     kvq_status st = check_hip(launch_decode(L, c->P, rq, q, out, lse, ws, c->sm_scale, (hipStream_t)stream),
                               "append_decode");
     if (st != KVQ_OK) return st;
@@ -353,6 +358,15 @@ kvq_status kvq_set_split_tokens(kvq_cache* c, int64_t tokens_per_split) {
     if (!c) return fail(KVQ_ERR_INVALID_ARG, "cache is NULL");
     if (tokens_per_split < 0) return fail(KVQ_ERR_INVALID_ARG, "tokens_per_split must be >= 0");
     c->split_tokens = tokens_per_split;
+    return ok();
+}
+
+kvq_status kvq_set_timing_events(kvq_cache* c, void* start_event, void* stop_event) {
+    if (!c) return fail(KVQ_ERR_INVALID_ARG, "cache is NULL");
+    if ((start_event == nullptr) != (stop_event == nullptr))
+        return fail(KVQ_ERR_INVALID_ARG, "start_event and stop_event must both be set or both be NULL");
+    c->ev_start = static_cast<hipEvent_t>(start_event);
+    c->ev_stop = static_cast<hipEvent_t>(stop_event);
     return ok();
 }
 

@@ -115,6 +115,9 @@ struct DecodeRequest {
     // writes it to residual row r - 1.  Null for a plain decode.
     const void* knew = nullptr;
     const void* vnew = nullptr;
+    // If set, HIP events that take the decode kernel's own start and end times.
+    hipEvent_t ev_start = nullptr;
+    hipEvent_t ev_stop = nullptr;
 };
 
 hipError_t launch_decode(const Layout& L, const DevPtrs& P, const DecodeRequest& rq, const void* q,

@@ -209,6 +209,19 @@ kvq_status kvq_cache_state(const kvq_cache* cache, int64_t* n_tokens, int64_t* n
  */
 kvq_status kvq_set_split_tokens(kvq_cache* cache, int64_t tokens_per_split);
 
+/*
+ * Measurement hook: every later decode launch of this cache (kvq_decode_attention,
+ * kvq_append_decode) records start_event at the start of its decode kernel and
+ * stop_event at its end, so hipEventElapsedTime(start, stop) is the kernel's own
+ * duration, without the dispatch gaps that events recorded around the call
+ * include.  Both are hipEvent_t handles created by the caller with timing
+ * enabled; the caller keeps them alive while a launch that records them is
+ * pending.  NULL, NULL stops the recording.  A launch that takes two kernels
+ * (an append that flushes, then the decode) records the decode kernel only.
+ * Errors: INVALID_ARG (NULL cache, or exactly one event NULL).
+ */
+kvq_status kvq_set_timing_events(kvq_cache* cache, void* start_event, void* stop_event);
+
 /* Message of the last failed call on this thread ("" if none).  Library-owned. */
 const char* kvq_last_error(void);
 

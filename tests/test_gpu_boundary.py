@@ -248,3 +248,55 @@ def test_two_caches_share_one_stream():
     b.append(to_torch(K, w.dtype, DEV), to_torch(V, w.dtype, DEV))
     _attend_and_check(w, a, K, V)
     _attend_and_check(w.replace(bits=4), b, K, V)
+
+
+def _hip_runtime():
+    """The HIP runtime library torch loaded (for event calls in the tests)."""
+    import ctypes
+    path = next(l.split()[-1] for l in open("/proc/self/maps") if "libamdhip64.so" in l)
+    rt = ctypes.CDLL(path)
+    rt.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    rt.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+    rt.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    return rt
+
+
+def test_timing_events_record_the_decode_kernel():
+    import ctypes
+    require_gpu()
+    w = _w()
+    cache = make_cache(w, max_tokens=256)
+    K, V = _tokens(w, 151, 81), _tokens(w, 151, 82)
+    cache.append(to_torch(K[:, :, :150], w.dtype, DEV), to_torch(V[:, :, :150], w.dtype, DEV))
+    q = to_torch(wl.random_tokens(9, (w.batch, w.n_q_heads, w.head_dim), w.dtype), w.dtype, DEV)
+    ref, ref_lse = cache.decode(q)
+    ref, ref_lse = ref.clone(), ref_lse.clone()
+    rt = _hip_runtime()
+    ev = [ctypes.c_void_p() for _ in range(2)]
+    for e in ev:
+        assert rt.hipEventCreate(ctypes.byref(e)) == 0
+    try:
+        with pytest.raises(kvq.KVQError) as ei:
+            cache.set_timing_events(ev[0], None)
+        assert ei.value.status == kvq.KVQ_ERR_INVALID_ARG
+        cache.set_timing_events(ev[0], ev[1])
+        out, lse = cache.decode(q)
+        torch.cuda.synchronize()
+        ms = ctypes.c_float()
+        assert rt.hipEventElapsedTime(ctypes.byref(ms), ev[0], ev[1]) == 0
+        assert 0.0 < ms.value < 1000.0, ms.value
+        assert torch.equal(out, ref) and torch.equal(lse, ref_lse)
+        # the fused one-token step records the same way
+        kn, vn = (to_torch(x[:, :, 150:151], w.dtype, DEV) for x in (K, V))
+        out, lse = cache.append_decode(kn, vn, q)
+        torch.cuda.synchronize()
+        ms2 = ctypes.c_float()
+        assert rt.hipEventElapsedTime(ctypes.byref(ms2), ev[0], ev[1]) == 0
+        assert 0.0 < ms2.value < 1000.0, ms2.value
+        log("decode kernel %.1f us, fused step kernel %.1f us" % (ms.value * 1e3, ms2.value * 1e3))
+        cache.set_timing_events(None, None)
+        _attend_and_check(w, cache, K, V, seed=9)
+    finally:
+        torch.cuda.synchronize()
+        for e in ev:
+            rt.hipEventDestroy(e)

@@ -94,6 +94,7 @@ def test_reserved_field_and_null_pointers():
     assert lib.kvq_cache_state(None, None, None, None, None) == kvq.KVQ_ERR_INVALID_ARG
     assert lib.kvq_append(None, None, None, 1, None) == kvq.KVQ_ERR_INVALID_ARG
     assert lib.kvq_decode_attention(None, None, None, None, None, 0, None) == kvq.KVQ_ERR_INVALID_ARG
+    assert lib.kvq_set_timing_events(None, None, None) == kvq.KVQ_ERR_INVALID_ARG
     assert lib.kvq_cache_destroy(None) == kvq.KVQ_OK
     assert kvq.kvq_last_error() == ""
 
