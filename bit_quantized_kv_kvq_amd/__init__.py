@@ -8,7 +8,7 @@ CPU fallback: if libkvq.so is missing or fails to load, every call raises.
 Low-level functions mirror the C entry points one to one (kvq_cache_bytes,
 kvq_cache_create, kvq_append, kvq_decode_workspace_bytes, kvq_decode_attention,
 kvq_dequantize, kvq_export, kvq_cache_state, kvq_set_split_tokens,
-kvq_set_timing_events, kvq_last_error); ``Cache`` bundles them with torch-allocated buffers.
+kvq_set_timing_events, kvq_stream_read_probe, kvq_last_error); ``Cache`` bundles them with torch-allocated buffers.
 """
 from __future__ import annotations
 
@@ -32,7 +32,8 @@ KVQ_F32, KVQ_BF16, KVQ_F16 = 0, 1, 2
 EXPORTED = ["kvq_cache_bytes", "kvq_cache_create", "kvq_cache_destroy", "kvq_append",
             "kvq_decode_workspace_bytes", "kvq_decode_attention", "kvq_append_decode",
             "kvq_dequantize", "kvq_export",
-            "kvq_cache_state", "kvq_set_split_tokens", "kvq_set_timing_events", "kvq_last_error"]
+            "kvq_cache_state", "kvq_set_split_tokens", "kvq_set_timing_events", "kvq_stream_read_probe",
+            "kvq_last_error"]
 
 
 class KVQError(RuntimeError):
@@ -78,6 +79,7 @@ def lib() -> ctypes.CDLL:
             "kvq_cache_state": [P] + [ctypes.POINTER(i64)] * 4,
             "kvq_set_split_tokens": [P, i64],
             "kvq_set_timing_events": [P, P, P],
+            "kvq_stream_read_probe": [P, ctypes.c_size_t, ctypes.c_int32, P, P],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -166,6 +168,11 @@ def kvq_cache_state(handle: int) -> Tuple[int, int, int, int]:
 
 def kvq_set_split_tokens(handle: int, tokens: int):
     _check(lib().kvq_set_split_tokens(ctypes.c_void_p(handle), tokens))
+
+
+def kvq_stream_read_probe(buf: int, nbytes: int, blocks_per_cu: int, sink: int, stream: int):
+    _check(lib().kvq_stream_read_probe(ctypes.c_void_p(buf), nbytes, blocks_per_cu,
+                                       ctypes.c_void_p(sink), ctypes.c_void_p(stream)))
 
 
 def kvq_set_timing_events(handle: int, start_event, stop_event):

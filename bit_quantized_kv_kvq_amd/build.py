@@ -19,7 +19,7 @@ ARCH = "gfx950"
 
 # the decode instantiations first: they take longest
 SOURCES = ["decode_b4_d128.hip", "decode_b2_d128.hip", "decode_b4_d64.hip", "decode_b2_d64.hip",
-           "kvq_host.cpp", "quant.hip", "decode.hip"]
+           "kvq_host.cpp", "quant.hip", "decode.hip", "probe.hip"]
 
 # -packed-fp32-ops: no packed fp32 VALU instructions anywhere.
 # correctly rounded fp32 division: the codec divides exactly as IEEE binary32.

@@ -16,6 +16,11 @@
 
 using namespace kvq;
 
+namespace kvq {
+// probe.hip: one streaming read of n16 16-byte words at buf with `blocks` workgroups of 256
+hipError_t launch_stream_read(const void* buf, int64_t n16, int blocks, unsigned* sink, hipStream_t stream);
+}  // namespace kvq
+
 struct kvq_cache {
     Layout L;
     DevPtrs P;
@@ -367,6 +372,26 @@ kvq_status kvq_set_timing_events(kvq_cache* c, void* start_event, void* stop_eve
         return fail(KVQ_ERR_INVALID_ARG, "start_event and stop_event must both be set or both be NULL");
     c->ev_start = static_cast<hipEvent_t>(start_event);
     c->ev_stop = static_cast<hipEvent_t>(stop_event);
+    return ok();
+}
+
+kvq_status kvq_stream_read_probe(const void* buf, size_t bytes, int32_t blocks_per_cu, uint32_t* sink,
+                                 void* stream) {
+    if (!buf || !sink) return fail(KVQ_ERR_INVALID_ARG, "buf or sink is NULL");
+    if (!aligned(buf, 16) || !aligned(sink, 4) || bytes % 16 != 0)
+        return fail(KVQ_ERR_INVALID_ARG, "buf must be 16-byte aligned and bytes a multiple of 16");
+    if (blocks_per_cu < 1 || blocks_per_cu > 64) return fail(KVQ_ERR_INVALID_ARG, "blocks_per_cu must be in [1, 64]");
+    if (bytes == 0) return ok();
+    int dev = 0, ncu = 0;
+    kvq_status st;
+    if ((st = check_hip(hipGetDevice(&dev), "hipGetDevice")) != KVQ_OK) return st;
+    if ((st = check_hip(hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev),
+                        "hipDeviceGetAttribute")) != KVQ_OK)
+        return st;
+    const int blocks = std::max(ncu, 1) * blocks_per_cu;
+    st = check_hip(launch_stream_read(buf, (int64_t)(bytes / 16), blocks, sink, (hipStream_t)stream),
+                   "stream_read_probe");
+    if (st != KVQ_OK) return st;
     return ok();
 }
 

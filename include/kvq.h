@@ -222,6 +222,21 @@ kvq_status kvq_set_split_tokens(kvq_cache* cache, int64_t tokens_per_split);
  */
 kvq_status kvq_set_timing_events(kvq_cache* cache, void* start_event, void* stop_event);
 
+/*
+ * Measurement hook, independent of any cache: one plain streaming read of
+ * `bytes` of device memory at `buf` (16-byte loads, eight in flight per
+ * thread, blocks_per_cu workgroups of 256 threads per compute unit of the
+ * current device), enqueued on `stream`.  Timed by the caller, it gives the
+ * read bandwidth that a kernel streaming its input once can reach on this
+ * device.  The data is folded with XOR; `sink` (4 device bytes) is written
+ * only when the fold equals one fixed word, so its contents are meaningless.
+ * buf: 16-byte aligned, bytes a multiple of 16.  Nothing is allocated.
+ * Errors: INVALID_ARG (NULL or misaligned pointers, blocks_per_cu outside
+ * [1, 64]); DEVICE (launch failure).
+ */
+kvq_status kvq_stream_read_probe(const void* buf, size_t bytes, int32_t blocks_per_cu, uint32_t* sink,
+                                 void* stream);
+
 /* Message of the last failed call on this thread ("" if none).  Library-owned. */
 const char* kvq_last_error(void);
 

@@ -300,3 +300,20 @@ def test_timing_events_record_the_decode_kernel():
         torch.cuda.synchronize()
         for e in ev:
             rt.hipEventDestroy(e)
+
+
+def test_stream_read_probe():
+    require_gpu()
+    x = torch.arange(1 << 20, dtype=torch.int32, device=DEV)
+    sink = torch.zeros(1, dtype=torch.int32, device=DEV)
+    sp = torch.cuda.current_stream().cuda_stream
+    for bpc in (1, 4):
+        kvq.kvq_stream_read_probe(x.data_ptr(), x.numel() * 4, bpc, sink.data_ptr(), sp)
+    kvq.kvq_stream_read_probe(x.data_ptr(), 48, 1, sink.data_ptr(), sp)  # less than one word per thread
+    torch.cuda.synchronize()
+    for args, why in [((x.data_ptr() + 4, 64, 1), "misaligned"), ((x.data_ptr(), 60, 1), "ragged size"),
+                      ((x.data_ptr(), 64, 0), "no workgroups"), ((0, 64, 1), "null")]:
+        with pytest.raises(kvq.KVQError) as ei:
+            kvq.kvq_stream_read_probe(*args, sink.data_ptr(), sp)
+        assert ei.value.status == kvq.KVQ_ERR_INVALID_ARG, why
+    assert torch.equal(x, torch.arange(1 << 20, dtype=torch.int32, device=DEV))  # read only
