@@ -18,7 +18,8 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 # the decode instantiations first: they take longest
-SOURCES = ["decode_b4_d128.hip", "decode_b2_d128.hip", "decode_b4_d64.hip", "decode_b2_d64.hip",
+SOURCES = ["decode_mf_b4_d128.hip", "decode_mf_b2_d128.hip", "decode_mf_b4_d64.hip", "decode_mf_b2_d64.hip",
+           "decode_b4_d128.hip", "decode_b2_d128.hip", "decode_b4_d64.hip", "decode_b2_d64.hip",
            "kvq_host.cpp", "quant.hip", "decode.hip", "probe.hip"]
 
 # -packed-fp32-ops: no packed fp32 VALU instructions anywhere.

@@ -45,7 +45,24 @@ Choice choose(const Layout& L) {
         if (L.bits == 2 && L.D == 64) c.fn = dec::decode_kernel_ptr<2, 64>(L.gqa, c.cpl, c.tile, c.tpg);
     }
     // dynamic LDS of the chosen instantiation (see LdsPlan)
-    const int wave = (L.gqa * dec::kLimbs * L.D + 2 * L.gqa * L.nvg * dec::kLimbs * c.tile + 15) & ~15;
+    int wave = (L.gqa * dec::kLimbs * L.D + 2 * L.gqa * L.nvg * dec::kLimbs * c.tile + 15) & ~15;
+    // Several query heads per kv head, key groups of 64 to 256 tokens and value
+    // groups of 64 channels or more: the quantized stream runs on the matrix cores.
+    if (L.gqa >= 2 && L.G >= 64 && L.G <= 256 && L.GV >= 64 && (L.D == 128 || L.nvg == 1)) {
+        const void* mf = nullptr;
+        const int tpg = L.G / 64;
+        if (L.bits == 4 && L.D == 128) mf = dec::decode_mf_kernel_ptr<4, 128>(L.gqa, tpg, L.nvg);
+        if (L.bits == 2 && L.D == 128) mf = dec::decode_mf_kernel_ptr<2, 128>(L.gqa, tpg, L.nvg);
+        if (L.bits == 4 && L.D == 64) mf = dec::decode_mf_kernel_ptr<4, 64>(L.gqa, tpg, L.nvg);
+        if (L.bits == 2 && L.D == 64) mf = dec::decode_mf_kernel_ptr<2, 64>(L.gqa, tpg, L.nvg);
+        if (mf != nullptr) {
+            c.fn = mf;
+            c.tile = 64;
+            c.tpg = tpg;
+            const int rbk = (L.gqa + 3) / 4;
+            wave = rbk * (L.D / 64) * 1024 + 2 * L.nvg * rbk * 1024;  // MStream::lds_bytes
+        }
+    }
     const int wg = kWaves * L.gqa * L.D + kWaves * L.gqa * 2 + kMaxCombine + 16 + 4;
     c.lds = kWaves * wave + 4 * wg;
     return c;

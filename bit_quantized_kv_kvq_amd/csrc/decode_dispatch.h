@@ -12,6 +12,12 @@ namespace dec {
 template <int BITS, int D>
 const void* decode_kernel_ptr(int gqa, int cpl, int tile, int tpg);
 
+// Matrix-core stream (several query heads per kv head): kernel entry for (query
+// heads per kv head, 64-token tiles per key group, value groups per token), or
+// nullptr.  Defined in decode_mf_b<bits>_d<head_dim>.hip.
+template <int BITS, int D>
+const void* decode_mf_kernel_ptr(int gqa, int tpg, int nvg);
+
 template <>
 const void* decode_kernel_ptr<4, 128>(int, int, int, int);
 template <>
@@ -20,6 +26,14 @@ template <>
 const void* decode_kernel_ptr<4, 64>(int, int, int, int);
 template <>
 const void* decode_kernel_ptr<2, 64>(int, int, int, int);
+template <>
+const void* decode_mf_kernel_ptr<4, 128>(int, int, int);
+template <>
+const void* decode_mf_kernel_ptr<2, 128>(int, int, int);
+template <>
+const void* decode_mf_kernel_ptr<4, 64>(int, int, int);
+template <>
+const void* decode_mf_kernel_ptr<2, 64>(int, int, int);
 
 // Key channels per lane (CPL): 32 for MHA with head_dim 128 (4 lanes per token),
 // 16 when several query heads multiply the register state, 8 for 8 query heads
@@ -55,6 +69,31 @@ const void* decode_kernel_ptr<2, 64>(int, int, int, int);
     KVQ_DECODE_GROUPS_GQA(BITS, 64, 2, 16)               \
     KVQ_DECODE_GROUPS_GQA(BITS, 64, 4, 16)               \
     KVQ_DECODE_GROUPS_GQA(BITS, 64, 8, (BITS == 4 ? 8 : 16))
+
+#define KVQ_DECODE_MF_CASE(BITS, D_, GQ_, TPG_, NVG_)                    \
+    if (gqa == GQ_ && tpg == TPG_ && nvg == NVG_)                        \
+        return reinterpret_cast<const void*>(&decode_kernel<BITS, D_, GQ_, 16, 64, TPG_, true, NVG_>);
+
+#define KVQ_DECODE_MF_TPG(BITS, D_, GQ_, NVG_)   \
+    KVQ_DECODE_MF_CASE(BITS, D_, GQ_, 1, NVG_)   \
+    KVQ_DECODE_MF_CASE(BITS, D_, GQ_, 2, NVG_)   \
+    KVQ_DECODE_MF_CASE(BITS, D_, GQ_, 4, NVG_)
+
+#define KVQ_DECODE_MF_GQ(BITS, D_, NVG_)   \
+    KVQ_DECODE_MF_TPG(BITS, D_, 2, NVG_)   \
+    KVQ_DECODE_MF_TPG(BITS, D_, 4, NVG_)   \
+    KVQ_DECODE_MF_TPG(BITS, D_, 8, NVG_)
+
+// value groups of 64 channels or more: one or two per token at head_dim 128, one at 64
+#define KVQ_DECODE_MF_TABLE_D128(BITS) KVQ_DECODE_MF_GQ(BITS, 128, 1) KVQ_DECODE_MF_GQ(BITS, 128, 2)
+#define KVQ_DECODE_MF_TABLE_D64(BITS) KVQ_DECODE_MF_GQ(BITS, 64, 1)
+
+#define KVQ_DEFINE_MF_KERNEL_PTR(BITS, D_)                                           \
+    template <>                                                                      \
+    const void* decode_mf_kernel_ptr<BITS, D_>(int gqa, int tpg, int nvg) {          \
+        KVQ_DECODE_MF_TABLE_D##D_(BITS)                                              \
+        return nullptr;                                                              \
+    }
 
 #define KVQ_DEFINE_KERNEL_PTR(BITS, D_)                                               \
     template <>                                                                       \

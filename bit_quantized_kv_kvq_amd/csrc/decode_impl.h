@@ -301,13 +301,367 @@ __device__ __forceinline__ float packed_f32(const uint32_t* w, int i) {
 }
 
 // ---------------------------------------------------------------------------
+// Quantized stream on the matrix cores, for several query heads per kv head.
+//
+// With GQ query heads sharing a kv head, the key and value dot products of a
+// tile are small dense matrix products: scores [heads x tokens] = Q' [heads x
+// channels] . K^T, and outputs [heads x channels] += W [heads x tokens] . V.  They
+// run on v_mfma_i32_16x16x64_i8 in exact integer arithmetic.  The fixed-point
+// operand (the folded query q_c s_c of a key group, or the weights p_t s_t of a
+// tile; |n| <= 2^18 as in the VALU path) is split into three balanced base-256
+// digits, and each (query head, digit) pair is one row of the 16-row A operand
+// (rows 4 h + digit; row 4 h + 3 and absent heads are zero).  The codes, unpacked
+// to unsigned bytes, are the B operand.  The digits are recombined by shifts
+// (Horner) in int32: |sum_c n_c u_c| <= 2^18 * 15 * 128 < 2^31.  Zero points enter
+// through sum_c (q_c s_c) z_c and sum_t (p_t s_t) z_t in fp32, as in the VALU path.
+//
+// Operand layout of the instruction (lane l, byte e of its 16 bytes): A row l % 16,
+// k = 16 (l / 16) + e; B column l % 16, same k; result column l % 16, rows
+// 4 (l / 16) .. + 3, so lane l holds all digit rows of head l / 16 of its block.
+//   keys:   16 tokens per product (column j = token), k = channel: lane l reads
+//           the D/4 channels (D/4) (l / 16) .. of token l % 16 with one load;
+//   values: 64 tokens per product (k = token 16 (l / 16) + e), 16 channels per
+//           product: product n holds channels 64 (n / 4) + 4 j + n % 4 (j = column),
+//           so the 16 columns of a product share one value group (G_V >= 64) and a
+//           lane loads four adjacent channels with one 16-byte load.
+// A tile is 64 tokens of one key group; a ring of four tiles streams the wave's
+// groups as in the VALU path.
+// ---------------------------------------------------------------------------
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ i32x4 mfma_i8(const i32x4& a, const i32x4& b, const i32x4& c) {
+    return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+}
+
+// the three balanced base-256 digits of n (|n| <= 2^18) as int8 bytes 0, 1, 2
+__device__ __forceinline__ uint32_t digits256(int n) { return ((uint32_t)(n + 32896) ^ 0x8080u); }
+
+// exact recombination of digit rows 0..2 of a product (row 3 is zero)
+__device__ __forceinline__ int horner256(const i32x4& r) { return (r[2] * 256 + r[1]) * 256 + r[0]; }
+
+template <int BITS, int D, int GQ, int TPG, int NVG>
+struct MStream {
+    static constexpr int TM = 64;               // tokens per tile
+    static constexpr int NSB = TM / 16;         // key products per tile and row block
+    static constexpr int RBK = (GQ + 3) / 4;    // 16-row blocks (four heads each)
+    static constexpr int NKK = D / 64;          // key products per 16 tokens (64 channels each)
+    static constexpr int NVB = D / 64;          // 64-channel blocks of the values
+    static constexpr int NVM = D / 16;          // value products per row block
+    static constexpr int TB = 32 / BITS;        // tokens per value dword
+    static constexpr int VBB = 16 / TB;         // value dwords per lane, channel and tile
+    static constexpr int RB = D * BITS / 8;     // key row bytes
+    static constexpr int KLW = RB / 16;         // key dwords per lane and token
+    static constexpr int KM = D / 64;           // fold channels per lane
+    static constexpr int VCPL = D / 32;
+    static constexpr int AK_BYTES = RBK * NKK * 1024;
+    static constexpr int AV_BYTES = NVG * RBK * 1024;
+    static constexpr int BODY = TPG > 4 ? TPG : 4;
+    static constexpr int GB = BODY / TPG;
+    static __host__ __device__ constexpr int lds_bytes() { return AK_BYTES + 2 * AV_BYTES; }
+
+    struct Tile {
+        typename UVec<KLW>::T k[NSB];
+        u32x4 v[NVB][VBB];
+        typename UVec<2 * NVG>::T vm[NSB];  // (scale, zero) of each value group of token 16 sb + l % 16
+        typename UVec<KM>::T ks, kz;
+    };
+
+    __amdgpu_buffer_rsrc_t rs;
+    uint32_t grp0, group_step;
+    int last_group, lane;
+    uint32_t k_off, v_off, vm_off, km_off;
+    uint8_t* ak_lds;  // [RBK][NKK][16 rows][64 bytes]
+    uint8_t* av_lds;  // [2][NVG][RBK][16 rows][64 bytes]
+    Tile t[4];
+    i32x4 ak[RBK][NKK];
+    float kinv_l[RBK], kbias_l[RBK];
+    float m_l[RBK], l2[RBK], z2[RBK][NVG], acc2[RBK][NVM];
+
+    __device__ __forceinline__ void init(const DecArgs& a, int64_t bh, int g_first, int n_my_groups, int ln,
+                                         uint8_t* lds) {
+        lane = ln;
+        rs = make_rsrc(a.rec + rec_offset(bh, 0, a.ng_cap, a.rec_bytes), (uint32_t)(a.ng_cap * a.rec_bytes));
+        grp0 = (uint32_t)g_first * (uint32_t)a.rec_bytes;
+        group_step = (uint32_t)(kWaves * a.rec_bytes);
+        last_group = n_my_groups - 1;
+        const int j = lane & 15, kb = lane >> 4;
+        k_off = (uint32_t)a.rec_kcodes + j * RB + kb * (KLW * 4);
+        v_off = (uint32_t)a.rec_vcodes + (kb * VBB * D + 4 * j) * 4;
+        vm_off = (uint32_t)a.rec_vmeta + j * NVG * 8;
+        km_off = KM * lane * 4;
+        ak_lds = lds;
+        av_lds = lds + AK_BYTES;
+        // padding rows (digit row 3 of every head, absent heads) stay zero
+        for (int i = lane * 16; i < lds_bytes(); i += 64 * 16) *reinterpret_cast<u32x4*>(lds + i) = u32x4{0u, 0u, 0u, 0u};
+        wave_lds_sync();
+#pragma unroll
+        for (int rb = 0; rb < RBK; ++rb) {
+            m_l[rb] = -INFINITY;
+            l2[rb] = 0.0f;
+#pragma unroll
+            for (int g = 0; g < NVG; ++g) z2[rb][g] = 0.0f;
+#pragma unroll
+            for (int n = 0; n < NVM; ++n) acc2[rb][n] = 0.0f;
+        }
+    }
+
+    // Tile `tig` of the wave's key group j (groups past the last reload the last).
+    __device__ __forceinline__ void load(Tile& tt, int j, int tig, bool kmeta) {
+        const uint32_t grp = grp0 + (uint32_t)min(j, max(last_group, 0)) * group_step;
+        const int t0 = tig * TM;
+#pragma unroll
+        for (int sb = 0; sb < NSB; ++sb) tt.k[sb] = bload<KLW>(rs, k_off, grp + (t0 + 16 * sb) * RB);
+#pragma unroll
+        for (int m = 0; m < NVB; ++m)
+#pragma unroll
+            for (int bb = 0; bb < VBB; ++bb)
+                tt.v[m][bb] = bload<4>(rs, v_off, grp + ((t0 / TB + bb) * D + 64 * m) * 4);
+#pragma unroll
+        for (int sb = 0; sb < NSB; ++sb) tt.vm[sb] = bload<2 * NVG>(rs, vm_off, grp + (t0 + 16 * sb) * NVG * 8);
+        if (kmeta) {  // constant at every call site
+            tt.ks = bload<KM>(rs, km_off, grp);
+            tt.kz = bload<KM>(rs, km_off + D * 4, grp);
+        }
+    }
+
+    // the first three tiles, in ring order
+    __device__ __forceinline__ void start() {
+        auto first = [&](auto ic) __attribute__((always_inline)) {
+            constexpr int I = decltype(ic)::value;
+            load(t[I], I / TPG, I % TPG, I % TPG == 0);
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        StaticFor<0, 3>::run(first);
+    }
+
+    // Key group fold: digit rows of rint(q_c s_c 2^k) into LDS in product order,
+    // then this lane's A operands; per-lane 2^-k and zero-point term of its head.
+    __device__ __forceinline__ void fold(const Tile& cur, const float (&qv)[GQ][KM]) {
+        const auto ks = whole(cur.ks), kz = whole(cur.kz);
+        float qt[GQ][KM], mx[GQ], bp[GQ], kinv[GQ], kbias[GQ];
+#pragma unroll
+        for (int h = 0; h < GQ; ++h) {
+            mx[h] = 0.0f;
+            bp[h] = 0.0f;
+#pragma unroll
+            for (int j = 0; j < KM; ++j) {
+                qt[h][j] = qv[h][j] * __uint_as_float(elem(ks, j));
+                mx[h] = fmaxf(mx[h], fabsf(qt[h][j]));
+                bp[h] = fmaf(qt[h][j], __uint_as_float(elem(kz, j)), bp[h]);
+            }
+        }
+#pragma unroll
+        for (int h = 0; h < GQ; ++h) {
+            const FixScale fs = fix_scale(group_max<64>(mx[h]));
+            kinv[h] = fs.inv;
+            kbias[h] = group_sum<64>(bp[h]);
+#pragma unroll
+            for (int j = 0; j < KM; ++j) {
+                const int c = KM * lane + j;
+                const int kb = c / (D / 4), kk = (c % (D / 4)) / 16, e = c % 16;
+                uint8_t* dst = ak_lds + ((h / 4 * NKK + kk) * 16 + 4 * (h % 4)) * 64 + kb * 16 + e;
+                const uint32_t d = digits256((int)rintf(qt[h][j] * fs.mul));
+                dst[0] = (uint8_t)d;
+                dst[64] = (uint8_t)(d >> 8);
+                dst[128] = (uint8_t)(d >> 16);
+            }
+        }
+        wave_lds_sync();
+        const int hs = lane >> 4;
+#pragma unroll
+        for (int rb = 0; rb < RBK; ++rb) {
+#pragma unroll
+            for (int kk = 0; kk < NKK; ++kk)
+                ak[rb][kk] = *reinterpret_cast<const i32x4*>(ak_lds + ((rb * NKK + kk) * 16 + (lane & 15)) * 64 + hs * 16);
+            float ki = 0.0f, kbi = 0.0f;
+#pragma unroll
+            for (int hh = 0; hh < 4; ++hh)
+                if (4 * rb + hh < GQ) {
+                    ki = hs == hh ? kinv[4 * rb + hh] : ki;
+                    kbi = hs == hh ? kbias[4 * rb + hh] : kbi;
+                }
+            kinv_l[rb] = ki;
+            kbias_l[rb] = kbi;
+        }
+    }
+
+    // unsigned code bytes of four 4-bit codes (two dwords of 8) or of sixteen
+    // 2-bit codes (one dword), in item order
+    __device__ __forceinline__ static i32x4 unpack(uint32_t w0, uint32_t w1) {
+        if constexpr (BITS == 4) {
+            w0 ^= 0x88888888u;
+            w1 ^= 0x88888888u;
+            return i32x4{(int)(w0 & 0x0F0F0F0Fu), (int)((w0 >> 4) & 0x0F0F0F0Fu), (int)(w1 & 0x0F0F0F0Fu),
+                         (int)((w1 >> 4) & 0x0F0F0F0Fu)};
+        } else {
+            return i32x4{(int)(w0 & 0x03030303u), (int)((w0 >> 2) & 0x03030303u), (int)((w0 >> 4) & 0x03030303u),
+                         (int)((w0 >> 6) & 0x03030303u)};
+        }
+    }
+
+    // One tile: scores on the matrix cores, softmax update, weight digits through
+    // LDS (buffer `buf` of two), value products folded into fp32.
+    __device__ __forceinline__ void process(const Tile& cur, int buf) {
+        const i32x4 zero = {0, 0, 0, 0};
+        float sc[RBK][NSB];
+#pragma unroll
+        for (int sb = 0; sb < NSB; ++sb) {
+            const auto kw = whole(cur.k[sb]);
+            i32x4 bk[NKK];
+#pragma unroll
+            for (int kk = 0; kk < NKK; ++kk) {
+                if constexpr (BITS == 4) bk[kk] = unpack(elem(kw, 2 * kk), elem(kw, 2 * kk + 1));
+                else bk[kk] = unpack(elem(kw, kk), 0u);
+            }
+#pragma unroll
+            for (int rb = 0; rb < RBK; ++rb) {
+                i32x4 r = mfma_i8(ak[rb][0], bk[0], zero);
+#pragma unroll
+                for (int kk = 1; kk < NKK; ++kk) r = mfma_i8(ak[rb][kk], bk[kk], r);
+                sc[rb][sb] = (float)horner256(r) * kinv_l[rb] - kbias_l[rb];
+            }
+        }
+        uint8_t* avb = av_lds + buf * AV_BYTES;
+        float vinv[RBK][NVG];
+        const int tok = lane & 15, row = 4 * (lane >> 4);
+#pragma unroll
+        for (int rb = 0; rb < RBK; ++rb) {
+            float mt = sc[rb][0];
+#pragma unroll
+            for (int sb = 1; sb < NSB; ++sb) mt = fmaxf(mt, sc[rb][sb]);
+            mt = group_max<16>(mt);
+            const float mn = fmaxf(m_l[rb], mt);
+            const float f = fast_exp2(m_l[rb] - mn);  // 0 while m is -inf
+            m_l[rb] = mn;
+            l2[rb] *= f;
+#pragma unroll
+            for (int g = 0; g < NVG; ++g) z2[rb][g] *= f;
+#pragma unroll
+            for (int n = 0; n < NVM; ++n) acc2[rb][n] *= f;
+            float p[NSB];
+#pragma unroll
+            for (int sb = 0; sb < NSB; ++sb) {
+                p[sb] = fast_exp2(sc[rb][sb] - mn);
+                l2[rb] += p[sb];
+            }
+#pragma unroll
+            for (int g = 0; g < NVG; ++g) {
+                float w[NSB], wmax = 0.0f;
+#pragma unroll
+                for (int sb = 0; sb < NSB; ++sb) {
+                    const auto vmw = whole(cur.vm[sb]);
+                    w[sb] = p[sb] * __uint_as_float(elem(vmw, 2 * g));
+                    z2[rb][g] = fmaf(w[sb], __uint_as_float(elem(vmw, 2 * g + 1)), z2[rb][g]);
+                    wmax = fmaxf(wmax, w[sb]);
+                }
+                const FixScale fs = fix_scale(group_max<16>(wmax));
+                vinv[rb][g] = fs.inv;
+#pragma unroll
+                for (int sb = 0; sb < NSB; ++sb) {
+                    const uint32_t d = digits256((int)rintf(w[sb] * fs.mul));
+                    uint8_t* dst = avb + ((g * RBK + rb) * 16 + row) * 64 + 16 * sb + tok;
+                    dst[0] = (uint8_t)d;
+                    dst[64] = (uint8_t)(d >> 8);
+                    dst[128] = (uint8_t)(d >> 16);
+                }
+            }
+        }
+        wave_lds_sync();
+        i32x4 av[NVG][RBK];
+#pragma unroll
+        for (int g = 0; g < NVG; ++g)
+#pragma unroll
+            for (int rb = 0; rb < RBK; ++rb)
+                av[g][rb] = *reinterpret_cast<const i32x4*>(avb + ((g * RBK + rb) * 16 + (lane & 15)) * 64 + (lane >> 4) * 16);
+#pragma unroll
+        for (int m = 0; m < NVB; ++m) {
+            const u32x4 w0 = whole(cur.v[m][0]);
+            const u32x4 w1 = whole(cur.v[m][VBB - 1]);
+            const int g = NVG == 1 ? 0 : m;  // two value groups: one per 64-channel block
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const i32x4 bv = unpack(w0[i], w1[i]);
+#pragma unroll
+                for (int rb = 0; rb < RBK; ++rb) {
+                    const i32x4 r = mfma_i8(av[g][rb], bv, zero);
+                    acc2[rb][4 * m + i] = fmaf((float)horner256(r), vinv[rb][g], acc2[rb][4 * m + i]);
+                }
+            }
+        }
+    }
+
+    // The wave's key groups, in the ring of four tiles (see the VALU stream).
+    __device__ __forceinline__ void run(int n_my_groups, const float (&qv)[GQ][KM]) {
+        const int n_iter = n_my_groups / GB;
+        int it = 0;
+        auto step = [&](auto bc) __attribute__((always_inline)) {
+            constexpr int B = decltype(bc)::value;
+            constexpr int NB = B + 3;
+            load(t[NB % 4], it * GB + NB / TPG, NB % TPG, NB % TPG == 0);
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (B % TPG == 0) fold(t[B % 4], qv);
+            process(t[B % 4], B & 1);
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        for (; it < n_iter; ++it) StaticFor<0, BODY>::run(step);
+        if constexpr (GB > 1) {
+            const int tail = (n_my_groups - n_iter * GB) * TPG;
+            auto tail_step = [&](auto ic) __attribute__((always_inline)) {
+                constexpr int I = decltype(ic)::value;
+                if (tail > I) {
+                    if constexpr (I % TPG == 0) fold(t[I], qv);
+                    process(t[I], I & 1);
+                }
+            };
+            StaticFor<0, 4 - TPG>::run(tail_step);
+        }
+    }
+
+    // Merges the stream's state into the wave state of the VALU layout (running
+    // max m, per-lane sums lpart and zpart, accumulators accv of channels
+    // 32-lane-strided), and leaves the stream's accumulators, rescaled, in s_acc
+    // ([GQ][D] floats of this wave) for the wave-state step to add.
+    __device__ __forceinline__ void merge(float (&m)[GQ], float (&lpart)[GQ], float (&zpart)[GQ],
+                                          float (&accv)[GQ][VCPL], float* s_acc) {
+        const int hs = lane >> 4, j = lane & 15;
+#pragma unroll
+        for (int h = 0; h < GQ; ++h) {
+            const int rb = h / 4, hh = h % 4;
+            const float m2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, m_l[rb]), 16 * hh));
+            const float M = fmaxf(m[h], m2);
+            const float f1 = m[h] == -INFINITY ? 0.0f : fast_exp2(m[h] - M);
+            const float f2 = m2 == -INFINITY ? 0.0f : fast_exp2(m2 - M);
+            m[h] = M;
+            lpart[h] *= f1;
+            zpart[h] *= f1;
+#pragma unroll
+            for (int c = 0; c < VCPL; ++c) accv[h][c] *= f1;
+            const bool mine = hs == hh;
+            lpart[h] += mine ? l2[rb] * f2 : 0.0f;
+#pragma unroll
+            for (int g = 0; g < NVG; ++g) {
+                const float zs = group_sum<16>(z2[rb][g]);
+                zpart[h] += (mine && j == g) ? zs * f2 : 0.0f;
+            }
+            if (mine) {
+#pragma unroll
+                for (int n = 0; n < NVM; ++n) s_acc[h * D + 64 * (n / 4) + 4 * j + (n % 4)] = acc2[rb][n] * f2;
+            }
+        }
+        wave_lds_sync();
+    }
+};
+
+// ---------------------------------------------------------------------------
 // LDS carve-up (dynamic shared memory)
 // ---------------------------------------------------------------------------
-template <int D, int GQ, int TILE>
+template <int D, int GQ, int TILE, int MFB = 0>
 struct LdsPlan {
     // per wave: key digits [GQ][limb][D] bytes, then two buffers of weight digits
-    // [GQ][nvg][limb][TILE] bytes (alternating by tile)
+    // [GQ][nvg][limb][TILE] bytes (alternating by tile); with the matrix-core
+    // stream, its operand rows (MFB bytes)
     __host__ __device__ static int wave_bytes(int nvg) {
+        if (MFB > 0) return MFB;
         const int b = GQ * kLimbs * D + 2 * GQ * nvg * kLimbs * TILE;
         return (b + 15) & ~15;
     }
@@ -319,7 +673,9 @@ struct LdsPlan {
 // ---------------------------------------------------------------------------
 // the kernel: grid = (nsplit, BH)
 // ---------------------------------------------------------------------------
-template <int BITS, int D, int GQ, int CPL, int TILE, int TPG>
+// MF: the quantized stream runs on the matrix cores (MStream; TILE 64, TPG = G / 64,
+// NVGT value groups per token); otherwise on the VALU with the CPL / TILE / TPG map.
+template <int BITS, int D, int GQ, int CPL, int TILE, int TPG, bool MF = false, int NVGT = 1>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
     constexpr int LPT = D / CPL;           // key lanes per token
     constexpr int TPW = 64 / LPT;          // tokens per key wave-load
@@ -340,7 +696,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
     static_assert(TILE % 32 == 0 && (U == 2 || U == 4 || U == 8), "digit runs of 2, 4 or 8 bytes");
 
     extern __shared__ __align__(16) unsigned char dsm[];
-    using LP = LdsPlan<D, GQ, TILE>;
+    using MS = MStream<BITS, D, GQ, TPG, NVGT>;
+    using LP = LdsPlan<D, GQ, TILE, MF ? MS::lds_bytes() : 0>;
 
     const int split = blockIdx.x;
     const int64_t bh = blockIdx.y;
@@ -446,6 +803,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
 
     {
         float qv[GQ][KM];  // folded query of this lane's KM channels (set in the prologue)
+        MS ms;             // the matrix-core stream (MF only)
+        if constexpr (MF) ms.init(a, bh, g_begin + wave, n_my_groups, lane, kd);
 
         // One tile of the wave's stream.  Key token slot * U + u of the tile is
         // scored by the LPT lanes of `slot`; value block hb * NVL + vl (TB tokens)
@@ -737,7 +1096,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
                 // tiles issue in ring order: the loop's waits count on it
                 __builtin_amdgcn_sched_barrier(0);
             };
-            StaticFor<0, NR - 1>::run(load_first);
+            if constexpr (MF) ms.start();
+            else StaticFor<0, NR - 1>::run(load_first);
             __builtin_amdgcn_sched_barrier(0);  // every load above issues before any wait below
             float qf[GQ][CPLF];
 #pragma unroll
@@ -796,7 +1156,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
         if (fresh_dst != nullptr) *fresh_dst = fresh_word;
 
         // ---------------- the quantized stream ----------------
-        if (n_my_groups > 0) {
+        if constexpr (MF) {
+            if (n_my_groups > 0) ms.run(n_my_groups, qv);
+            ms.merge(m, lpart, zpart, accv, s_acc + wave * GQ * D);
+        } else if (n_my_groups > 0) {
             const int n_iter = n_my_groups / GB;
             int it = 0;
             auto step = [&](auto bc) __attribute__((always_inline)) {
@@ -834,7 +1197,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
 #pragma unroll
         for (int c = 0; c < VCPL; ++c) {
             const float tot = accv[h][c] + __shfl_xor(accv[h][c], 32) - Zv;
-            if (lane < 32) s_acc[(wave * GQ + h) * D + c0v + c] = tot;
+            float* dst = &s_acc[(wave * GQ + h) * D + c0v + c];
+            if (lane < 32) *dst = MF ? *dst + tot : tot;  // MF: the stream's part is already there
         }
         if (lane == 0) {
             s_ml[(wave * GQ + h) * 2] = m[h];
