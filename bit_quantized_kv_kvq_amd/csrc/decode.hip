@@ -63,7 +63,7 @@ Choice choose(const Layout& L) {
             wave = rbk * (L.D / 64) * 1024 + 2 * L.nvg * rbk * 1024;  // MStream::lds_bytes
         }
     }
-    const int wg = kWaves * L.gqa * L.D + kWaves * L.gqa * 2 + kMaxCombine + 16 + 4;
+    const int wg = kWaves * L.gqa * L.D + kWaves * L.gqa * 2 + 4;  // LdsPlan::wg_floats
     c.lds = kWaves * wave + 4 * wg;
     return c;
 }

@@ -84,16 +84,30 @@ __device__ __forceinline__ float dpp(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
 }
 
+// Lane l's value (l wave-uniform), read into a scalar register.
+__device__ __forceinline__ float lane_value(float v, int l) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+// Whole-wave sum and max when every lane of each 16-lane row holds its row's
+// result: the four row results are read as scalars (no cross-row shuffle through
+// LDS), and every lane gets the same bits.  Full exec mask required.
+__device__ __forceinline__ float rows_sum(float v) {
+    return (lane_value(v, 0) + lane_value(v, 16)) + (lane_value(v, 32) + lane_value(v, 48));
+}
+__device__ __forceinline__ float rows_max(float v) {
+    return fmaxf(fmaxf(lane_value(v, 0), lane_value(v, 16)), fmaxf(lane_value(v, 32), lane_value(v, 48)));
+}
+
 // Sum over aligned groups of N consecutive lanes; every lane of a group gets the
-// same (bitwise identical) sum.
+// same (bitwise identical) sum.  N = 64 needs the full exec mask.
 template <int N>
 __device__ __forceinline__ float group_sum(float v) {
     if constexpr (N >= 2) v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
     if constexpr (N >= 4) v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
     if constexpr (N >= 8) v += dpp<0x141>(v);  // row_half_mirror
     if constexpr (N >= 16) v += dpp<0x140>(v); // row_mirror
-    if constexpr (N >= 32) v += __shfl_xor(v, 16);
-    if constexpr (N >= 64) v += __shfl_xor(v, 32);
+    if constexpr (N == 32) v += __shfl_xor(v, 16);
+    if constexpr (N == 64) v = rows_sum(v);
     return v;
 }
 
@@ -104,32 +118,20 @@ __device__ __forceinline__ float group_max(float v) {
     if constexpr (N >= 4) v = fmaxf(v, dpp<0x4E>(v));
     if constexpr (N >= 8) v = fmaxf(v, dpp<0x141>(v));
     if constexpr (N >= 16) v = fmaxf(v, dpp<0x140>(v));
-    if constexpr (N >= 32) v = fmaxf(v, __shfl_xor(v, 16));
-    if constexpr (N >= 64) v = fmaxf(v, __shfl_xor(v, 32));
+    if constexpr (N == 32) v = fmaxf(v, __shfl_xor(v, 16));
+    if constexpr (N == 64) v = rows_max(v);
     return v;
 }
 
 // Max over the slots of a wave when every group of LPT lanes holds one value:
-// reduces lanes LPT apart (values are equal inside a group).
+// reduces lanes LPT apart (values are equal inside a group).  Full exec mask.
 template <int LPT>
 __device__ __forceinline__ float slots_max(float v) {
     if constexpr (LPT == 1) return group_max<64>(v);
     else if constexpr (LPT == 2) { v = fmaxf(v, dpp<0x4E>(v)); }
     if constexpr (LPT <= 4) v = fmaxf(v, dpp<0x141>(v));
     if constexpr (LPT <= 8) v = fmaxf(v, dpp<0x140>(v));
-    v = fmaxf(v, __shfl_xor(v, 16));
-    v = fmaxf(v, __shfl_xor(v, 32));
-    return v;
-}
-
-// max / sum over all lanes whose index agrees modulo `from` (a power of two)
-__device__ __forceinline__ float xor_max(float v, int from) {
-    for (int off = from; off < 64; off <<= 1) v = fmaxf(v, __shfl_xor(v, off));
-    return v;
-}
-__device__ __forceinline__ float xor_sum(float v, int from) {
-    for (int off = from; off < 64; off <<= 1) v += __shfl_xor(v, off);
-    return v;
+    return rows_max(v);
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -324,8 +326,8 @@ __device__ __forceinline__ float packed_f32(const uint32_t* w, int i) {
 //           product: product n holds channels 64 (n / 4) + 4 j + n % 4 (j = column),
 //           so the 16 columns of a product share one value group (G_V >= 64) and a
 //           lane loads four adjacent channels with one 16-byte load.
-// A tile is 64 tokens of one key group; a ring of four tiles streams the wave's
-// groups as in the VALU path.
+// A tile is 64 tokens of one key group; a ring of tiles streams the wave's groups
+// as in the VALU path.
 // ---------------------------------------------------------------------------
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
@@ -355,8 +357,11 @@ struct MStream {
     static constexpr int VCPL = D / 32;
     static constexpr int AK_BYTES = RBK * NKK * 1024;
     static constexpr int AV_BYTES = NVG * RBK * 1024;
-    static constexpr int BODY = TPG > 4 ? TPG : 4;
-    static constexpr int GB = BODY / TPG;
+    // Ring of NRM tile buffers, NRM - 1 in flight while one is processed.  (Six
+    // buffers measured slower: more register traffic per tile.)
+    static constexpr int NRM = 4;
+    static constexpr int BODY = TPG > NRM ? TPG : NRM;  // tiles per loop iteration
+    static constexpr int GB = BODY / TPG;               // key groups per loop iteration
     static __host__ __device__ constexpr int lds_bytes() { return AK_BYTES + 2 * AV_BYTES; }
 
     struct Tile {
@@ -372,7 +377,7 @@ struct MStream {
     uint32_t k_off, v_off, vm_off, km_off;
     uint8_t* ak_lds;  // [RBK][NKK][16 rows][64 bytes]
     uint8_t* av_lds;  // [2][NVG][RBK][16 rows][64 bytes]
-    Tile t[4];
+    Tile t[NRM];
     i32x4 ak[RBK][NKK];
     float kinv_l[RBK], kbias_l[RBK];
     float m_l[RBK], l2[RBK], z2[RBK][NVG], acc2[RBK][NVM];
@@ -424,14 +429,14 @@ struct MStream {
         }
     }
 
-    // the first three tiles, in ring order
+    // the first NRM - 1 tiles, in ring order
     __device__ __forceinline__ void start() {
         auto first = [&](auto ic) __attribute__((always_inline)) {
             constexpr int I = decltype(ic)::value;
             load(t[I], I / TPG, I % TPG, I % TPG == 0);
             __builtin_amdgcn_sched_barrier(0);
         };
-        StaticFor<0, 3>::run(first);
+        StaticFor<0, NRM - 1>::run(first);
     }
 
     // Key group fold: digit rows of rint(q_c s_c 2^k) into LDS in product order,
@@ -590,17 +595,17 @@ struct MStream {
         }
     }
 
-    // The wave's key groups, in the ring of four tiles (see the VALU stream).
+    // The wave's key groups, through the tile ring (as in the VALU stream).
     __device__ __forceinline__ void run(int n_my_groups, const float (&qv)[GQ][KM]) {
         const int n_iter = n_my_groups / GB;
         int it = 0;
         auto step = [&](auto bc) __attribute__((always_inline)) {
             constexpr int B = decltype(bc)::value;
-            constexpr int NB = B + 3;
-            load(t[NB % 4], it * GB + NB / TPG, NB % TPG, NB % TPG == 0);
+            constexpr int NB = B + NRM - 1;
+            load(t[NB % NRM], it * GB + NB / TPG, NB % TPG, NB % TPG == 0);
             __builtin_amdgcn_sched_barrier(0);
-            if constexpr (B % TPG == 0) fold(t[B % 4], qv);
-            process(t[B % 4], B & 1);
+            if constexpr (B % TPG == 0) fold(t[B % NRM], qv);
+            process(t[B % NRM], B & 1);
             __builtin_amdgcn_sched_barrier(0);
         };
         for (; it < n_iter; ++it) StaticFor<0, BODY>::run(step);
@@ -613,7 +618,7 @@ struct MStream {
                     process(t[I], I & 1);
                 }
             };
-            StaticFor<0, 4 - TPG>::run(tail_step);
+            StaticFor<0, NRM - TPG>::run(tail_step);
         }
     }
 
@@ -665,8 +670,8 @@ struct LdsPlan {
         const int b = GQ * kLimbs * D + 2 * GQ * nvg * kLimbs * TILE;
         return (b + 15) & ~15;
     }
-    // per workgroup: wave states and combine scratch
-    __host__ __device__ static int wg_floats() { return kWaves * GQ * D + kWaves * GQ * 2 + kMaxCombine + 16 + 4; }
+    // per workgroup: wave states and the last-arrival flag
+    __host__ __device__ static int wg_floats() { return kWaves * GQ * D + kWaves * GQ * 2 + 4; }
     __host__ __device__ static int bytes(int nvg) { return kWaves * wave_bytes(nvg) + 4 * wg_floats(); }
 };
 
@@ -713,10 +718,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
     float* wg = reinterpret_cast<float*>(dsm + kWaves * LP::wave_bytes(nvg));
     float* s_acc = wg;                                          // [kWaves][GQ][D]
     float* s_ml = s_acc + kWaves * GQ * D;                      // [kWaves][GQ][2]
-    float* s_cw = s_ml + kWaves * GQ * 2;                       // [kMaxCombine]
-    float* s_cM = s_cw + kMaxCombine;                           // [8]
-    float* s_cL = s_cM + 8;                                     // [8]
-    int* s_last = reinterpret_cast<int*>(s_cL + 8);
+    int* s_last = reinterpret_cast<int*>(s_ml + kWaves * GQ * 2);
 
     const int slot = lane / LPT, chunk = lane % LPT;
     const int hb = lane >> 5;                  // value half: block parity
@@ -1123,7 +1125,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
                     }
                     float mt[GQ];
 #pragma unroll
-                    for (int h = 0; h < GQ; ++h) mt[h] = xor_max(sc[h], LPTF);
+                    for (int h = 0; h < GQ; ++h) mt[h] = slots_max<LPTF>(sc[h]);
                     update_max(mt);
                     float pv[GQ];
 #pragma unroll
@@ -1191,9 +1193,14 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
     // ---------------- wave state -> LDS ----------------
 #pragma unroll
     for (int h = 0; h < GQ; ++h) {
-        const float L = xor_sum(lpart[h], 1);
-        const float Zg = xor_sum(zpart[h], nvg);  // total for value group lane % nvg
-        const float Zv = __shfl(Zg, gv);
+        const float L = group_sum<64>(lpart[h]);
+        // zpart of lane l belongs to value group l % nvg; Zv is the total of this
+        // lane's channel group gv (nvg is a power of two, wave-uniform)
+        float Zv = 0.0f;
+        for (int g = 0; g < nvg; ++g) {
+            const float Zg = group_sum<64>((lane & (nvg - 1)) == g ? zpart[h] : 0.0f);
+            Zv = gv == g ? Zg : Zv;
+        }
 #pragma unroll
         for (int c = 0; c < VCPL; ++c) {
             const float tot = accv[h][c] + __shfl_xor(accv[h][c], 32) - Zv;
@@ -1254,43 +1261,42 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
     __syncthreads();
     if (!*s_last) return;
 
+    // Each thread merges the splits of its (head, channel) elements on its own:
+    // the maxima, sums and accumulators of a batch of kBatch splits are all
+    // loaded before the first is used (one L2 round trip per batch), and merged
+    // in split order with an online rescale between batches.
     const int ns = a.nsplit;
     const float* pml = a.part_ml + bh * a.nsplit_cap * GQ * 2;
     const float* pacc = a.part_acc + bh * a.nsplit_cap * GQ * D;
-    // per-head max and weights over splits: head h handled by wave h % kWaves
-    for (int h = wave; h < GQ; h += kWaves) {
-        float M = -INFINITY;
-        for (int i = lane; i < ns; i += 64) M = fmaxf(M, fetch(&pml[(i * GQ + h) * 2]));
-        M = xor_max(M, 1);
-        float L = 0.0f;
-        for (int i = lane; i < ns; i += 64) {
-            const float mi = fetch(&pml[(i * GQ + h) * 2]);
-            const float li = fetch(&pml[(i * GQ + h) * 2 + 1]);
-            const float w = (mi == -INFINITY) ? 0.0f : fast_exp2(mi - M);
-            s_cw[i * GQ + h] = w;
-            L = fmaf(li, w, L);
-        }
-        L = group_sum<64>(L);
-        if (lane == 0) {
-            s_cM[h] = M;
-            s_cL[h] = L;
-        }
-    }
-    __syncthreads();
+    constexpr int kBatch = 16;
     for (int e = tid; e < GQ * D; e += kThreads) {
         const int h = e / D, c = e % D;
-        float A0 = 0.0f, A1 = 0.0f, A2 = 0.0f, A3 = 0.0f;
-        int i = 0;
-        for (; i + 4 <= ns; i += 4) {
-            A0 = fmaf(fetch(&pacc[((i + 0) * GQ + h) * D + c]), s_cw[(i + 0) * GQ + h], A0);
-            A1 = fmaf(fetch(&pacc[((i + 1) * GQ + h) * D + c]), s_cw[(i + 1) * GQ + h], A1);
-            A2 = fmaf(fetch(&pacc[((i + 2) * GQ + h) * D + c]), s_cw[(i + 2) * GQ + h], A2);
-            A3 = fmaf(fetch(&pacc[((i + 3) * GQ + h) * D + c]), s_cw[(i + 3) * GQ + h], A3);
+        float M = -INFINITY, L = 0.0f, A = 0.0f;
+        for (int i0 = 0; i0 < ns; i0 += kBatch) {
+            float mi[kBatch], li[kBatch], ai[kBatch];
+#pragma unroll
+            for (int k = 0; k < kBatch; ++k) {
+                const int i = min(i0 + k, ns - 1);
+                mi[k] = fetch(&pml[(i * GQ + h) * 2]);
+                li[k] = fetch(&pml[(i * GQ + h) * 2 + 1]);
+                ai[k] = fetch(&pacc[(i * GQ + h) * D + c]);
+            }
+            float Mb = M;
+#pragma unroll
+            for (int k = 0; k < kBatch; ++k) Mb = i0 + k < ns ? fmaxf(Mb, mi[k]) : Mb;
+            const float f = M == -INFINITY ? 0.0f : fast_exp2(M - Mb);
+            L *= f;
+            A *= f;
+#pragma unroll
+            for (int k = 0; k < kBatch; ++k) {
+                const float w = (i0 + k < ns && mi[k] != -INFINITY) ? fast_exp2(mi[k] - Mb) : 0.0f;
+                L = fmaf(li[k], w, L);
+                A = fmaf(ai[k], w, A);
+            }
+            M = Mb;
         }
-        for (; i < ns; ++i) A0 = fmaf(fetch(&pacc[(i * GQ + h) * D + c]), s_cw[i * GQ + h], A0);
-        const float L = s_cL[h];
-        a.out[(qrow0 + h) * D + c] = ((A0 + A1) + (A2 + A3)) / L;
-        if (c == 0 && a.lse) a.lse[qrow0 + h] = (s_cM[h] + __log2f(L)) * 0.69314718055994530942f;
+        a.out[(qrow0 + h) * D + c] = A / L;
+        if (c == 0 && a.lse) a.lse[qrow0 + h] = (M + __log2f(L)) * 0.69314718055994530942f;
     }
     if (tid == 0) __hip_atomic_store(&a.counters[bh], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
