@@ -44,11 +44,11 @@ def load(path: str):
     L = ctypes.CDLL(path)
     P = ctypes.c_void_p
     i64, i32, dbl = ctypes.c_int64, ctypes.c_int, ctypes.c_double
-    L.orc_quant_group.argtypes = [P, i64, i64, i32, P, P, P, i64]
+    L.orc_quant_group.argtypes = [P, i64, i64, i32, i32, P, P, P, i64]
     L.orc_quant_group.restype = None
     L.orc_dequant.argtypes = [ctypes.c_uint8, ctypes.c_float, ctypes.c_float]
     L.orc_dequant.restype = ctypes.c_float
-    L.orc_build_slice.argtypes = [i32, i32, i32, i32, i32, i32, P, P, i64] + [P] * 10 + [P]
+    L.orc_build_slice.argtypes = [i32, i32, i32, i32, i32, i32, i32, P, P, i64] + [P] * 10 + [P]
     L.orc_build_slice.restype = i32
     L.orc_dequant_slice.argtypes = [i32, i32, i32, i64, i64, i64] + [P] * 12
     L.orc_dequant_slice.restype = None
@@ -86,14 +86,15 @@ def _f32(a) -> np.ndarray:
 # codec
 # ---------------------------------------------------------------------------
 
-def quant_group(x, bits: int):
-    """Quantize one group.  Returns (scale: np.float32, zero: np.float32, codes: uint8[m])."""
+def quant_group(x, bits: int, codec: int = 0):
+    """Quantize one group (codec 0 asymmetric min-max, 1 symmetric).
+    Returns (scale: np.float32, zero: np.float32, codes: uint8[m])."""
     x = _f32(x).ravel()
     m = x.size
     s = np.zeros(1, np.float32)
     z = np.zeros(1, np.float32)
     q = np.zeros(m, np.uint8)
-    lib().orc_quant_group(_p(x), m, 1, bits, _p(s), _p(z), _p(q), 1)
+    lib().orc_quant_group(_p(x), m, 1, bits, codec, _p(s), _p(z), _p(q), 1)
     return s[0], z[0], q
 
 
@@ -114,10 +115,11 @@ def dequant(q, s, z) -> np.ndarray:
 # ---------------------------------------------------------------------------
 
 def build_slice(k_tok, v_tok, *, head_dim: int, bits: int, k_group: int, v_group: int,
-                residual: int, n_sink: int) -> Dict[str, np.ndarray]:
+                residual: int, n_sink: int, codec: int = 0) -> Dict[str, np.ndarray]:
     """Append the tokens of one (sequence, kv-head) one at a time; return the state.
 
-    k_tok, v_tok: fp32 [n, D] (already rounded to the storage dtype).
+    k_tok, v_tok: fp32 [n, D] (already rounded to the storage dtype).  codec: 0
+    asymmetric min-max groups, 1 symmetric groups.
     """
     k_tok = _f32(k_tok)
     v_tok = _f32(v_tok)
@@ -135,7 +137,7 @@ def build_slice(k_tok, v_tok, *, head_dim: int, bits: int, k_group: int, v_group
         v_zero=np.zeros((Lq, nvg), np.float32),
         res_k=np.zeros((R, D), np.float32), res_v=np.zeros((R, D), np.float32))
     counts = np.zeros(4, np.int64)
-    rc = lib().orc_build_slice(D, bits, G, GV, R, S, _p(k_tok), _p(v_tok), n,
+    rc = lib().orc_build_slice(D, bits, codec, G, GV, R, S, _p(k_tok), _p(v_tok), n,
                                _p(st["sink_k"]), _p(st["sink_v"]),
                                _p(st["k_codes"]), _p(st["k_scale"]), _p(st["k_zero"]),
                                _p(st["v_codes"]), _p(st["v_scale"]), _p(st["v_zero"]),
@@ -149,7 +151,7 @@ def build_slice(k_tok, v_tok, *, head_dim: int, bits: int, k_group: int, v_group
     st["res_k"] = st["res_k"][:r_]
     st["res_v"] = st["res_v"][:r_]
     st.update(n_sink=nS_, n_quant=Lq_, n_resid=r_, flushes=fl, head_dim=D, bits=bits,
-              k_group=G, v_group=GV, residual=R, S=S)
+              k_group=G, v_group=GV, residual=R, S=S, codec=codec)
     return st
 
 
@@ -233,7 +235,7 @@ def slice_state(w, b: int, kvh: int, n_steps: int):
     """Oracle cache state of slice (b, kvh) after the prefill and n_steps appends."""
     k, v = slice_tokens_f32(w, b, kvh, n_steps)
     return build_slice(k, v, head_dim=w.head_dim, bits=w.bits, k_group=w.k_group,
-                       v_group=w.v_group, residual=w.residual, n_sink=w.n_sink)
+                       v_group=w.v_group, residual=w.residual, n_sink=w.n_sink, codec=w.codec)
 
 
 def expected_outputs(w, b: int, kvh: int, n_steps: int, qi: int, scale: float | None = None):

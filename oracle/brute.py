@@ -21,12 +21,28 @@ import numpy as np
 f32 = np.float32
 
 
-def quant_group(values, bits: int):
-    """Returns (scale, zero, codes) with one binary32 rounding per operation."""
+def quant_group(values, bits: int, codec: int = 0):
+    """Returns (scale, zero, codes) with one binary32 rounding per operation.
+
+    codec 0: asymmetric min-max; codec 1: symmetric, scale 2 max|x| / (2^n - 1),
+    signed code clamp(rint(x / scale), -2^(n-1), 2^(n-1) - 1) stored plus 2^(n-1)
+    (Atom review, section 三 "核心公式", symmetric simplification, c = 1).
+    """
     xs = [f32(v) for v in values]
     mn = min(xs)
     mx = max(xs)
     qmax = f32((1 << bits) - 1)
+    if codec == 1:
+        amax = max(abs(mn), abs(mx))
+        s = f32(f32(f32(2) * amax) / qmax)
+        if s == f32(0):
+            s = amax if amax != f32(0) else f32(1)
+        half = 1 << (bits - 1)
+        codes = []
+        for x in xs:
+            r = int(np.rint(f32(x / s)))
+            codes.append(min(max(r, -half), half - 1) + half)
+        return s, f32(half), codes
     s = f32(f32(mx - mn) / qmax)
     if mx == mn or s == f32(0):
         s = f32(abs(mn)) if mn != f32(0) else f32(1)
@@ -62,7 +78,7 @@ def attention(q, K, V, scale: float):
     return np.array(out), m + math.log(den)
 
 
-def build_slice(k_tok, v_tok, *, bits, k_group, v_group, residual, n_sink):
+def build_slice(k_tok, v_tok, *, bits, k_group, v_group, residual, n_sink, codec=0):
     """Token-by-token cache construction, written independently of the C oracle.
 
     Returns dict with lists: sinks, quantized (dequantized K', V' rows in token
@@ -90,7 +106,7 @@ def build_slice(k_tok, v_tok, *, bits, k_group, v_group, residual, n_sink):
             crow = [[0] * D for _ in block]
             meta = []
             for c in range(D):
-                s, z, q = quant_group([row[c] for row in block], bits)
+                s, z, q = quant_group([row[c] for row in block], bits, codec)
                 meta.append((s, z))
                 for i, code in enumerate(q):
                     rows[i][c] = dequant(code, s, z)
@@ -102,7 +118,7 @@ def build_slice(k_tok, v_tok, *, bits, k_group, v_group, residual, n_sink):
         for row in res_v:
             out, crow, meta = [], [], []
             for h in range(0, D, v_group):
-                s, z, q = quant_group(row[h:h + v_group], bits)
+                s, z, q = quant_group(row[h:h + v_group], bits, codec)
                 meta.append((s, z))
                 out.extend(dequant(code, s, z) for code in q)
                 crow.extend(q)

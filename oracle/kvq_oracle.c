@@ -16,6 +16,12 @@
  *         (Atom review, section 三 "核心公式", quantized-tensor formula)
  *       x' = (code - zero) * scale
  *         (Int4 KV-cache post, section 2, dequantization formula)
+ *   - the symmetric variant of the same quantizer (codec 1)
+ *       scale = 2 max|x| / (2^n - 1), signed code clamp(round(x / scale),
+ *       -2^(n-1), 2^(n-1) - 1)
+ *         (Atom review, section 三 "核心公式", symmetric simplification, c = 1),
+ *       stored as the unsigned code signed + 2^(n-1), i.e. zero = 2^(n-1), so
+ *       the same dequantization applies
  *   - the KIVI cache layout: keys grouped per channel over G tokens, values
  *     per token, newest tokens in a full-precision residual that is quantized
  *     and appended once it holds R tokens, then emptied
@@ -41,6 +47,9 @@
  *   range/(2^n-1) underflows) uses scale |min| (or 1 when min == 0);
  *   a zero point of -0 is stored as +0; zero points are integer-valued fp32
  *   and may fall outside [0, 2^n - 1];
+ *   symmetric codec: max|x| from the group's min and max; a group whose scale
+ *   computes to 0 uses max|x| (or 1 when the group is all zeros); the signed
+ *   code range [-2^(n-1), 2^(n-1) - 1] is stored offset by 2^(n-1);
  *   the whole residual (R tokens, keys and values) is flushed when it reaches R;
  *   the first S tokens of a sequence stay full precision for good (sinks);
  *   query head h reads kv head h / (Hq / Hkv).
@@ -61,11 +70,15 @@
 /* group quantizer                                                         */
 /* ---------------------------------------------------------------------- */
 
+#define ORC_CODEC_ASYMMETRIC 0
+#define ORC_CODEC_SYMMETRIC 1
+
 /*
- * Quantize m values x[0], x[stride], ... to n-bit codes.  Writes the group's
- * scale and zero point and the codes q[0], q[qstride], ...
+ * Quantize m values x[0], x[stride], ... to n-bit codes with the asymmetric
+ * (codec 0) or symmetric (codec 1) quantizer.  Writes the group's scale and
+ * zero point and the codes q[0], q[qstride], ...
  */
-void orc_quant_group(const float* x, int64_t m, int64_t stride, int bits,
+void orc_quant_group(const float* x, int64_t m, int64_t stride, int bits, int codec,
                      float* s_out, float* z_out, uint8_t* q, int64_t qstride)
 {
     float mn = x[0], mx = x[0];
@@ -75,6 +88,22 @@ void orc_quant_group(const float* x, int64_t m, int64_t stride, int bits,
         if (v > mx) mx = v;
     }
     const float qmax = (float)((1 << bits) - 1);  /* 2^n - 1, exact */
+    if (codec == ORC_CODEC_SYMMETRIC) {
+        const float amax = fabsf(mn) > fabsf(mx) ? fabsf(mn) : fabsf(mx);
+        const float twice = 2.0f * amax;        /* exact */
+        float ss = twice / qmax;
+        if (ss == 0.0f) ss = (amax != 0.0f) ? amax : 1.0f;
+        const float zz = (float)(1 << (bits - 1));  /* 2^(n-1): signed code + zz */
+        for (int64_t i = 0; i < m; ++i) {
+            float r = rintf(x[i * stride] / ss);
+            if (r < -zz) r = -zz;
+            if (r > zz - 1.0f) r = zz - 1.0f;
+            q[i * qstride] = (uint8_t)(r + zz);
+        }
+        *s_out = ss;
+        *z_out = zz;
+        return;
+    }
     float range = mx - mn;
     float s = range / qmax;
     if (mx == mn || s == 0.0f) {
@@ -108,7 +137,7 @@ float orc_dequant(uint8_t q, float s, float z)
 /* ---------------------------------------------------------------------- */
 
 typedef struct {
-    int D, bits, G, GV, R, S;
+    int D, bits, codec, G, GV, R, S;
     /* buffers owned by the caller */
     float* sink_k; float* sink_v;               /* [S, D]            */
     uint8_t* k_codes; float* k_scale; float* k_zero;   /* [Lq,D] [Lq/G,D] */
@@ -126,7 +155,7 @@ static void flush_residual(orc_slice* c)
     for (int j = 0; j < R / G; ++j) {
         int64_t grp = c->Lq / G + j;
         for (int ch = 0; ch < D; ++ch) {
-            orc_quant_group(c->res_k + (int64_t)j * G * D + ch, G, D, c->bits,
+            orc_quant_group(c->res_k + (int64_t)j * G * D + ch, G, D, c->bits, c->codec,
                             &c->k_scale[grp * D + ch], &c->k_zero[grp * D + ch],
                             c->k_codes + (c->Lq + (int64_t)j * G) * D + ch, D);
         }
@@ -135,7 +164,7 @@ static void flush_residual(orc_slice* c)
     for (int t = 0; t < R; ++t) {
         int64_t tok = c->Lq + t;
         for (int h = 0; h < nvg; ++h) {
-            orc_quant_group(c->res_v + (int64_t)t * D + (int64_t)h * GV, GV, 1, c->bits,
+            orc_quant_group(c->res_v + (int64_t)t * D + (int64_t)h * GV, GV, 1, c->bits, c->codec,
                             &c->v_scale[tok * nvg + h], &c->v_zero[tok * nvg + h],
                             c->v_codes + tok * D + (int64_t)h * GV, 1);
         }
@@ -167,7 +196,7 @@ static void append_token(orc_slice* c, const float* k, const float* v)
  * Output buffers must hold the sizes given above for Lq = R*floor((n-S)/R).
  * Returns 0, or -1 on an invalid configuration.
  */
-int orc_build_slice(int D, int bits, int G, int GV, int R, int S,
+int orc_build_slice(int D, int bits, int codec, int G, int GV, int R, int S,
                     const float* k_tok, const float* v_tok, int64_t n,
                     float* sink_k, float* sink_v,
                     uint8_t* k_codes, float* k_scale, float* k_zero,
@@ -176,8 +205,9 @@ int orc_build_slice(int D, int bits, int G, int GV, int R, int S,
 {
     if (D <= 0 || G <= 0 || GV <= 0 || R <= 0 || S < 0 || n < 0) return -1;
     if (bits != 2 && bits != 4) return -1;
+    if (codec != ORC_CODEC_ASYMMETRIC && codec != ORC_CODEC_SYMMETRIC) return -1;
     if (R % G != 0 || D % GV != 0) return -1;
-    orc_slice c = {D, bits, G, GV, R, S, sink_k, sink_v, k_codes, k_scale, k_zero,
+    orc_slice c = {D, bits, codec, G, GV, R, S, sink_k, sink_v, k_codes, k_scale, k_zero,
                    v_codes, v_scale, v_zero, res_k, res_v, 0, 0, 0, 0};
     for (int64_t t = 0; t < n; ++t)
         append_token(&c, k_tok + t * D, v_tok + t * D);

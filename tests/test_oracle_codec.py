@@ -8,6 +8,9 @@
   exact constant groups, min maps to code 0, exact grid reconstruction, dequant as
   one rounded product.
 - Agreement with the independent pure-Python formulation (oracle.brute).
+- The symmetric quantizer (codec 1) of the same Atom section: worked examples,
+  and invariants (fixed zero point 2^(n-1), s/2 bound inside the signed range,
+  clipping only above it, odd symmetry of the codes, exact zero).
 """
 import json
 import os
@@ -37,7 +40,7 @@ def _bits(x):
 @pytest.mark.parametrize("case", _cases(), ids=lambda c: c["id"])
 def test_golden_example(case):
     x = np.array([_f32(v) for v in case["x"]], np.float32)
-    s, z, q = oracle.quant_group(x, case["bits"])
+    s, z, q = oracle.quant_group(x, case["bits"], case.get("codec", 0))
     assert _bits(s) == int(case["scale_bits"], 16), (float(s), case["scale"])
     assert s == _f32(case["scale"])
     assert _bits(z) == _bits(_f32(case["zero"]))  # +0, never -0
@@ -139,5 +142,52 @@ def test_matches_pure_python_formulation(bits):
     for x in _random_groups(99 + bits, 300, bits):
         s, z, q = oracle.quant_group(x, bits)
         s2, z2, q2 = brute.quant_group(list(x), bits)
+        assert _bits(s) == _bits(s2) and _bits(z) == _bits(z2)
+        assert list(q) == q2
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_symmetric_invariants_random_groups(bits):
+    qmax = (1 << bits) - 1
+    half = 1 << (bits - 1)
+    for x in _random_groups(4321 + bits, 600, bits):
+        s, z, q = oracle.quant_group(x, bits, 1)
+        amax = float(np.abs(x).max())
+        assert s > 0 and np.isfinite(s)
+        # the zero point is 2^(n-1): stored codes are the signed codes plus 2^(n-1)
+        assert z == half
+        assert q.min() >= 0 and q.max() <= qmax
+        xd = oracle.dequant(q, s, z)
+        # dequant is a single rounded product of (code - z) and s
+        d = (q.astype(np.float32) - z).astype(np.float32)
+        assert np.array_equal(xd, (d * s).astype(np.float32))
+        if amax == 0.0:
+            assert np.all(q == half) and np.all(xd == 0)
+            continue
+        # the scale is 2 max|x| / (2^n - 1) within one rounding (or the degenerate rule)
+        if float(s) != amax:
+            assert abs(float(s) - 2 * amax / qmax) <= 2.0 ** -23 * float(s) + 1e-45
+        # |x' - x| <= s/2 inside the signed range; above it the code is clipped to the top
+        xs = x.astype(np.float64)
+        inside = xs <= (half - 0.5) * float(s) * (1 - 2.0 ** -20)
+        slack = 2.0 ** -20 * amax + 1e-44
+        err = np.abs(xd.astype(np.float64) - xs)
+        assert np.all(err[inside] <= float(s) / 2 + slack), (x, s, q)
+        assert np.all(q[xs > (half - 0.5) * float(s) * (1 + 2.0 ** -20)] == qmax)
+        # a zero input is reproduced exactly
+        assert np.all(xd[x == 0] == 0)
+        # odd symmetry: x and -x get codes that mirror around z (both inside the range)
+        sym = np.concatenate([x, -x])
+        s2, z2, q2 = oracle.quant_group(sym, bits, 1)
+        m = x.size
+        ok = (np.abs(sym[:m].astype(np.float64)) <= (half - 0.5) * float(s2) * (1 - 2.0 ** -20))
+        assert np.all((q2[:m].astype(int) + q2[m:].astype(int))[ok] == 2 * half)
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_symmetric_matches_pure_python_formulation(bits):
+    for x in _random_groups(77 + bits, 300, bits):
+        s, z, q = oracle.quant_group(x, bits, 1)
+        s2, z2, q2 = brute.quant_group(list(x), bits, 1)
         assert _bits(s) == _bits(s2) and _bits(z) == _bits(z2)
         assert list(q) == q2

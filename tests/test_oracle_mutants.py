@@ -52,6 +52,15 @@ MUTANTS = {
     # the last token of the cache is left out of the softmax denominator
     "drop_last_token": ("    for (int64_t j = 0; j < T; ++j) {\n        double w = exp(sc[j] - M);",
                         "    for (int64_t j = 0; j < T - 1; ++j) {\n        double w = exp(sc[j] - M);"),
+    # symmetric scale without the factor 2 (max|x| / (2^n - 1))
+    "sym_no_factor_2": ("const float twice = 2.0f * amax;", "const float twice = amax;"),
+    # symmetric zero point one level low
+    "sym_zero_off_by_one": ("const float zz = (float)(1 << (bits - 1));",
+                            "const float zz = (float)((1 << (bits - 1)) - 1);"),
+    # symmetric upper clamp at 2^(n-1) (one code too many)
+    "sym_upper_clamp": ("if (r > zz - 1.0f) r = zz - 1.0f;", "if (r > zz) r = zz;"),
+    # symmetric rounding half away from zero
+    "sym_half_away": ("float r = rintf(x[i * stride] / ss);", "float r = roundf(x[i * stride] / ss);"),
     # residual tokens left out of the dequantized token sequence
     "drop_residual": ("memcpy(k_out + (nS + Lq) * D, res_k, sizeof(float) * r * D);",
                       "memset(k_out + (nS + Lq) * D, 0, sizeof(float) * r * D);"),
@@ -65,6 +74,7 @@ def _pins():
         pins.append(lambda c=case: tq.test_golden_example(c))
     for bits in (2, 4):
         pins.append(lambda b=bits: tq.test_invariants_random_groups(b))
+        pins.append(lambda b=bits: tq.test_symmetric_invariants_random_groups(b))
         pins.append(lambda b=bits: tq.test_exact_grid_reconstruction(b))
     pins.append(tq.test_signed_zero_inputs)
     pins.append(tq.test_underflowing_scale_uses_degenerate_rule)

@@ -55,6 +55,7 @@ class Workload:
     k_outlier_scale: float = 1.0
     k_offset_range: float = 0.0     # per-(kv-head, channel) key mean ~ U(-a, a)
     sink_scale: float = 1.0         # K and V scale of the first n_sink tokens
+    codec: int = 0                  # 0 asymmetric min-max groups, 1 symmetric groups
 
     @property
     def gqa(self) -> int:
@@ -110,6 +111,14 @@ WORKLOADS: Dict[str, Workload] = {
         bits=2, k_group=64, v_group=64, residual=256, n_sink=4,
         prefill=131072, steps=8, attend_after_prefill=False, seed=1005,
         sink_scale=20.0),
+    "llama7b_mha_int4_sym": Workload(
+        name="llama7b_mha_int4_sym",
+        description="the Llama-7B-shaped MHA decode with symmetric INT4 groups: B8 H32 D128, "
+                    "context 4096, bf16, G128 / G_V128, R128, 64 decode steps",
+        batch=8, n_kv_heads=32, n_q_heads=32, head_dim=128, dtype="bf16",
+        bits=4, k_group=128, v_group=128, residual=128, n_sink=0,
+        prefill=4096, steps=64, attend_after_prefill=False, seed=1002,
+        k_outlier_channels=4, k_outlier_scale=8.0, codec=1),
 }
 
 # short aliases in the order the workloads are listed
