@@ -304,7 +304,7 @@ def main():
         c = kvq.Cache(batch=w.batch, n_kv_heads=w.n_kv_heads, n_q_heads=w.n_q_heads,
                       head_dim=w.head_dim, bits=w.bits, k_group=w.k_group, v_group=w.v_group,
                       residual=w.residual, n_sink=w.n_sink, dtype=TORCH_DTYPES[w.dtype],
-                      max_tokens=max_tokens, device=dev)
+                      max_tokens=max_tokens, device=dev, codec=w.codec)
         if args.split_tokens:
             c.set_split_tokens(args.split_tokens)
         c.append(Kd, Vd)
@@ -435,6 +435,7 @@ def main():
                    "n_q_heads": w.n_q_heads, "head_dim": w.head_dim, "context": w.prefill,
                    "bits": w.bits, "k_group": w.k_group, "v_group": w.v_group,
                    "residual": w.residual, "n_sink": w.n_sink, "storage": w.dtype,
+                   "codec": "symmetric" if w.codec else "asymmetric",
                    "layers_rotated": L, "parallelism": "single GPU"},
         "tokens_per_s": round(w.batch / (ms_per_step * 1e-3), 1),
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),

@@ -28,6 +28,7 @@ STATUS_NAMES = {0: "KVQ_OK", -1: "KVQ_ERR_INVALID_ARG", -2: "KVQ_ERR_UNSUPPORTED
                 -3: "KVQ_ERR_CAPACITY", -4: "KVQ_ERR_BUFFER_TOO_SMALL", -5: "KVQ_ERR_DEVICE"}
 
 KVQ_F32, KVQ_BF16, KVQ_F16 = 0, 1, 2
+KVQ_CODEC_ASYMMETRIC, KVQ_CODEC_SYMMETRIC = 0, 1
 
 EXPORTED = ["kvq_cache_bytes", "kvq_cache_create", "kvq_cache_destroy", "kvq_append",
             "kvq_decode_workspace_bytes", "kvq_decode_attention", "kvq_append_decode",
@@ -50,7 +51,7 @@ class Config(ctypes.Structure):
                 ("v_group", ctypes.c_int32), ("residual", ctypes.c_int32),
                 ("n_sink", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("max_tokens", ctypes.c_int64), ("sm_scale", ctypes.c_float),
-                ("reserved", ctypes.c_int32)]
+                ("codec", ctypes.c_int32)]
 
 
 _lib = None
@@ -101,9 +102,9 @@ def _check(status: int):
 
 
 def make_config(*, batch, n_kv_heads, n_q_heads, head_dim, bits, k_group, v_group, residual,
-                n_sink=0, dtype=KVQ_BF16, max_tokens, sm_scale=0.0) -> Config:
+                n_sink=0, dtype=KVQ_BF16, max_tokens, sm_scale=0.0, codec=KVQ_CODEC_ASYMMETRIC) -> Config:
     return Config(batch, n_kv_heads, n_q_heads, head_dim, bits, k_group, v_group, residual,
-                  n_sink, dtype, max_tokens, sm_scale, 0)
+                  n_sink, dtype, max_tokens, sm_scale, codec)
 
 
 def kvq_cache_bytes(cfg: Config) -> int:

@@ -56,7 +56,8 @@ Layout make_layout(const kvq_config* c);
 
 kvq_status validate(const kvq_config* c) {
     if (!c) return fail(KVQ_ERR_INVALID_ARG, "config is NULL");
-    if (c->reserved != 0) return fail(KVQ_ERR_INVALID_ARG, "reserved field must be 0");
+    if (c->codec != KVQ_CODEC_ASYMMETRIC && c->codec != KVQ_CODEC_SYMMETRIC)
+        return fail(KVQ_ERR_INVALID_ARG, "codec must be KVQ_CODEC_ASYMMETRIC or KVQ_CODEC_SYMMETRIC");
     if (c->batch < 1 || c->n_kv_heads < 1 || c->n_q_heads < 1 || c->head_dim < 1)
         return fail(KVQ_ERR_INVALID_ARG, "batch, heads and head_dim must be positive");
     if (c->n_q_heads % c->n_kv_heads != 0)
@@ -104,6 +105,7 @@ Layout make_layout(const kvq_config* c) {
     L.Hq = c->n_q_heads;
     L.D = c->head_dim;
     L.bits = c->bits;
+    L.codec = c->codec;
     L.G = c->k_group;
     L.GV = c->v_group;
     L.R = c->residual;

@@ -34,7 +34,7 @@ constexpr int kMaxCombine = 1024;      // max (splits x query heads per kv head)
 // dot products take as is.
 // ---------------------------------------------------------------------------
 struct Layout {
-    int B, Hkv, Hq, D, bits, G, GV, R, S, dtype, esize, gqa, nvg, row_bytes;
+    int B, Hkv, Hq, D, bits, codec, G, GV, R, S, dtype, esize, gqa, nvg, row_bytes;
     int64_t BH, max_tokens, Lq_cap, ng_cap;
     int rec_bytes, rec_kcodes, rec_vcodes, rec_vmeta;
     size_t off_ksink, off_vsink, off_kres, off_vres, off_rec, total;

@@ -30,6 +30,16 @@ __device__ inline QParams group_params(float mn, float mx, float qmax) {
     return {s, z};
 }
 
+// Symmetric variant: s = 2 max|x| / (2^n - 1), z = 2^(n-1) (the signed code
+// clamp(round(x / s), -2^(n-1), 2^(n-1) - 1) plus 2^(n-1) is group_code's
+// clamp(round(x / s) + z, 0, 2^n - 1): both sides are exact small integers).
+__device__ inline QParams group_params_sym(float mn, float mx, float qmax) {
+    const float amax = fmaxf(fabsf(mn), fabsf(mx));
+    float s = (2.0f * amax) / qmax;
+    if (s == 0.0f) s = (amax != 0.0f) ? amax : 1.0f;
+    return {s, 0.5f * (qmax + 1.0f)};
+}
+
 __device__ inline uint32_t group_code(float x, QParams p, float qmax) {
     float t = rintf(x / p.s) + p.z;
     t = t < 0.0f ? 0.0f : t;
@@ -75,6 +85,7 @@ struct QuantArgs {
     int D, G, GV, nvg, row_bytes;
     int64_t ng_cap;
     int rec_bytes, rec_kcodes, rec_vcodes, rec_vmeta;
+    int codec;  // kvq_codec
     uint8_t* rec;
 };
 
@@ -189,7 +200,8 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
             mn0 = fminf(mn0, s_mm[(q * D + c) * 2]), mx0 = fmaxf(mx0, s_mm[(q * D + c) * 2 + 1]);
             mn1 = fminf(mn1, s_mm[(q * D + c + 1) * 2]), mx1 = fmaxf(mx1, s_mm[(q * D + c + 1) * 2 + 1]);
         }
-        const QParams p0 = group_params(mn0, mx0, qmax), p1 = group_params(mn1, mx1, qmax);
+        const QParams p0 = a.codec ? group_params_sym(mn0, mx0, qmax) : group_params(mn0, mx0, qmax);
+        const QParams p1 = a.codec ? group_params_sym(mn1, mx1, qmax) : group_params(mn1, mx1, qmax);
 #pragma unroll 8
         for (int t = 0; t < GP; ++t) {
             float x0, x1;
@@ -230,7 +242,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
                 mn = fminf(mn, __shfl_xor(mn, o));
                 mx = fmaxf(mx, __shfl_xor(mx, o));
             }
-            const QParams p = group_params(mn, mx, qmax);
+            const QParams p = a.codec ? group_params_sym(mn, mx, qmax) : group_params(mn, mx, qmax);
             if (live) {
                 for (int j = 0; j < cpt; j += 8) {
                     float f[8];
@@ -424,6 +436,7 @@ hipError_t launch_quantize(const Layout& L, const DevPtrs& P, const void* src_k,
     a.rec_kcodes = L.rec_kcodes;
     a.rec_vcodes = L.rec_vcodes;
     a.rec_vmeta = L.rec_vmeta;
+    a.codec = L.codec;
     a.rec = P.rec;
     // codes [G][D] bytes, then the keys' partial minima/maxima [P][D][2] fp32
     const size_t lds = (((size_t)L.G * L.D + 15) & ~(size_t)15) + (size_t)(256 / (L.D / 2)) * L.D * 2 * sizeof(float);

@@ -68,6 +68,22 @@ typedef enum kvq_dtype {
     KVQ_F16 = 2
 } kvq_dtype;
 
+/*
+ * Group quantizer of the cache ("Atom: Low-bit Quantization for Efficient and
+ * Accurate LLM Serving", section 三 "核心公式"; clip factor 1):
+ *   ASYMMETRIC: s = (max - min) / (2^n - 1), z = round(-min / s),
+ *               code = clamp(round(x / s) + z, 0, 2^n - 1)
+ *   SYMMETRIC:  s = 2 max|x| / (2^n - 1), signed code
+ *               clamp(round(x / s), -2^(n-1), 2^(n-1) - 1), stored as that code
+ *               + 2^(n-1), i.e. with z = 2^(n-1)
+ * Both dequantize as x' = (code - z) s.  A group whose scale computes to 0 uses
+ * |min| (asymmetric) or max|x| (symmetric), or 1 when that is 0.
+ */
+typedef enum kvq_codec {
+    KVQ_CODEC_ASYMMETRIC = 0,
+    KVQ_CODEC_SYMMETRIC = 1
+} kvq_codec;
+
 typedef struct kvq_config {
     int32_t batch;        /* B  >= 1                                              */
     int32_t n_kv_heads;   /* Hkv >= 1                                             */
@@ -82,7 +98,7 @@ typedef struct kvq_config {
     int32_t dtype;        /* kvq_dtype of K, V, q and of the sink/residual store  */
     int64_t max_tokens;   /* capacity per sequence, >= 1                          */
     float sm_scale;       /* softmax scale; 0 selects 1/sqrt(D)                   */
-    int32_t reserved;     /* must be 0                                            */
+    int32_t codec;        /* kvq_codec of the key and value groups (0: asymmetric) */
 } kvq_config;
 
 typedef struct kvq_cache kvq_cache; /* opaque host-side handle */
@@ -99,7 +115,7 @@ kvq_status kvq_cache_bytes(const kvq_config* cfg, size_t* bytes);
  * from kvq_cache_bytes, 256-byte aligned).  The buffer's contents need no
  * initialisation.  *out receives the handle, to be freed with
  * kvq_cache_destroy.  Errors: INVALID_ARG (null pointer, non-positive sizes,
- * Hq % Hkv != 0, R % G != 0, D % G_V != 0, reserved != 0, misaligned buffer),
+ * Hq % Hkv != 0, R % G != 0, D % G_V != 0, codec not a kvq_codec, misaligned buffer),
  * UNSUPPORTED (bits not 2/4, D not 64/128, Hq/Hkv not 1/2/4/8, G not in
  * {32, 64, 128, 256}, G_V not a multiple of 16, B * Hkv > 65535, more than
  * 2 GiB of quantized records per (sequence, kv head)), BUFFER_TOO_SMALL,

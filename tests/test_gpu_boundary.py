@@ -32,7 +32,7 @@ def _oracle_states(w, K, V):
     vf = wl.storage_to_f32(V, w.dtype)
     return {(b, h): oracle.build_slice(kf[b, h], vf[b, h], head_dim=w.head_dim, bits=w.bits,
                                        k_group=w.k_group, v_group=w.v_group,
-                                       residual=w.residual, n_sink=w.n_sink)
+                                       residual=w.residual, n_sink=w.n_sink, codec=w.codec)
             for b in range(w.batch) for h in range(w.n_kv_heads)}
 
 
@@ -68,6 +68,9 @@ def _attend_and_check(w, cache, K, V, seed=5):
     dict(k_group=128, residual=128, v_group=64),        # two tiles per group
     dict(n_q_heads=8, k_group=128, residual=128),       # GQA 4, four tiles per group
     dict(n_q_heads=8, bits=2, k_group=64, residual=128, v_group=64),  # GQA 4, two per group
+    dict(codec=1),                                      # symmetric groups
+    dict(codec=1, bits=2, n_sink=3, dtype="f32", head_dim=64, v_group=16),
+    dict(codec=1, n_q_heads=8, k_group=64, residual=128, v_group=64),  # symmetric, matrix cores
 ])
 @pytest.mark.parametrize("n", [1, 63, 64, 65, 200])
 def test_variants_against_oracle(kw, n):

@@ -27,6 +27,8 @@ SMALL = {
                                       prefill=1200, steps=20),
     "sink_small": wl.get("C5").replace(name="sink_small", batch=1, n_kv_heads=2, n_q_heads=8,
                                        prefill=1000, steps=40),
+    "sym_small": wl.get("llama7b_mha_int4_sym").replace(name="sym_small", batch=2, n_kv_heads=3,
+                                                        n_q_heads=3, prefill=1000, steps=30),
 }
 
 
@@ -134,6 +136,7 @@ FULL = {
     "kivi2_long_batch": ([(0, 0), (31, 31)], None),
     "gqa_32k_int4": ([(0, 0), (15, 7)], None),
     "long_128k_sink_int2": ([(0, 0), (0, 7)], {0, 3, 4, 7}),
+    "llama7b_mha_int4_sym": ([(0, 0), (5, 9)], None),
 }
 
 

@@ -83,12 +83,15 @@ def test_invalid_configs_are_rejected(kw, status):
     assert ei.value.message  # thread-local message is set
 
 
-def test_reserved_field_and_null_pointers():
+def test_codec_field_and_null_pointers():
     c = _cfg()
-    c.reserved = 1
-    with pytest.raises(kvq.KVQError) as ei:
-        kvq.kvq_cache_bytes(c)
-    assert ei.value.status == kvq.KVQ_ERR_INVALID_ARG
+    for bad in (2, -1, 7):
+        c.codec = bad
+        with pytest.raises(kvq.KVQError) as ei:
+            kvq.kvq_cache_bytes(c)
+        assert ei.value.status == kvq.KVQ_ERR_INVALID_ARG
+    c.codec = kvq.KVQ_CODEC_SYMMETRIC
+    assert kvq.kvq_cache_bytes(c) > 0
     lib = kvq.lib()
     assert lib.kvq_cache_bytes(None, None) == kvq.KVQ_ERR_INVALID_ARG
     assert lib.kvq_cache_state(None, None, None, None, None) == kvq.KVQ_ERR_INVALID_ARG

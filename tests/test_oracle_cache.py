@@ -97,14 +97,14 @@ def test_grouping_axes_by_direct_regrouping():
     assert np.array_equal(st["res_v"], v[S + 24:])
 
 
-@pytest.mark.parametrize("bits,S", [(2, 0), (4, 3)])
-def test_matches_pure_python_cache(bits, S):
+@pytest.mark.parametrize("bits,S,codec", [(2, 0, 0), (4, 3, 0), (2, 1, 1), (4, 0, 1)])
+def test_matches_pure_python_cache(bits, S, codec):
     D, G, GV, R = 8, 4, 4, 8
     k, v = _tokens(40 + bits, S + 3 * R + 5, D, scale=2.0)
     st = oracle.build_slice(k, v, head_dim=D, bits=bits, k_group=G, v_group=GV,
-                            residual=R, n_sink=S)
+                            residual=R, n_sink=S, codec=codec)
     br = brute.build_slice(k.tolist(), v.tolist(), bits=bits, k_group=G, v_group=GV,
-                           residual=R, n_sink=S)
+                           residual=R, n_sink=S, codec=codec)
     K, V = oracle.dequant_slice(st)
     Kb = np.array(br["sinks_k"] + br["qk"] + br["res_k"], np.float32).reshape(-1, D)
     Vb = np.array(br["sinks_v"] + br["qv"] + br["res_v"], np.float32).reshape(-1, D)
