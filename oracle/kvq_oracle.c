@@ -16,6 +16,8 @@
  *         (Atom review, section 三 "核心公式", quantized-tensor formula)
  *       x' = (code - zero) * scale
  *         (Int4 KV-cache post, section 2, dequantization formula)
+ *   - code widths n = 2, 4 and 8 (8-bit codes: the per-layer INT8 / INT4 mixed
+ *     precision of the Int4 KV-cache post, section 5.1)
  *   - the symmetric variant of the same quantizer (codec 1)
  *       scale = 2 max|x| / (2^n - 1), signed code clamp(round(x / scale),
  *       -2^(n-1), 2^(n-1) - 1)
@@ -204,7 +206,7 @@ int orc_build_slice(int D, int bits, int codec, int G, int GV, int R, int S,
                     float* res_k, float* res_v, int64_t* counts)
 {
     if (D <= 0 || G <= 0 || GV <= 0 || R <= 0 || S < 0 || n < 0) return -1;
-    if (bits != 2 && bits != 4) return -1;
+    if (bits != 2 && bits != 4 && bits != 8) return -1;
     if (codec != ORC_CODEC_ASYMMETRIC && codec != ORC_CODEC_SYMMETRIC) return -1;
     if (R % G != 0 || D % GV != 0) return -1;
     orc_slice c = {D, bits, codec, G, GV, R, S, sink_k, sink_v, k_codes, k_scale, k_zero,

@@ -97,7 +97,7 @@ def test_grouping_axes_by_direct_regrouping():
     assert np.array_equal(st["res_v"], v[S + 24:])
 
 
-@pytest.mark.parametrize("bits,S,codec", [(2, 0, 0), (4, 3, 0), (2, 1, 1), (4, 0, 1)])
+@pytest.mark.parametrize("bits,S,codec", [(2, 0, 0), (4, 3, 0), (2, 1, 1), (4, 0, 1), (8, 2, 0), (8, 0, 1)])
 def test_matches_pure_python_cache(bits, S, codec):
     D, G, GV, R = 8, 4, 4, 8
     k, v = _tokens(40 + bits, S + 3 * R + 5, D, scale=2.0)

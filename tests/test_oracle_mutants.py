@@ -72,7 +72,7 @@ def _pins():
     pins = []
     for case in tq._cases():
         pins.append(lambda c=case: tq.test_golden_example(c))
-    for bits in (2, 4):
+    for bits in (2, 4, 8):
         pins.append(lambda b=bits: tq.test_invariants_random_groups(b))
         pins.append(lambda b=bits: tq.test_symmetric_invariants_random_groups(b))
         pins.append(lambda b=bits: tq.test_exact_grid_reconstruction(b))
