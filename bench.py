@@ -49,7 +49,8 @@ EVENT_STRIDE = 8
 DEFAULT_WORKLOAD = "llama7b_mha_int4"
 DECODE_SOURCES = ["decode_impl.h", "decode_dispatch.h", "decode.hip", "kvq_internal.h",
                   "decode_b4_d128.hip", "decode_b2_d128.hip", "decode_b4_d64.hip", "decode_b2_d64.hip",
-                  "decode_mf_b4_d128.hip", "decode_mf_b2_d128.hip", "decode_mf_b4_d64.hip", "decode_mf_b2_d64.hip"]
+                  "decode_mf_b4_d128.hip", "decode_mf_b2_d128.hip", "decode_mf_b4_d64.hip", "decode_mf_b2_d64.hip",
+                  "decode_mf_b8_d128.hip", "decode_mf_b8_d64.hip"]
 
 
 def algorithmic_bytes(w: wl.Workload, n_sink: int, n_quant: int, n_resid: int) -> int:

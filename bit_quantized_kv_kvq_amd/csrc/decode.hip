@@ -46,15 +46,18 @@ Choice choose(const Layout& L) {
     }
     // dynamic LDS of the chosen instantiation (see LdsPlan)
     int wave = (L.gqa * dec::kLimbs * L.D + 2 * L.gqa * L.nvg * dec::kLimbs * c.tile + 15) & ~15;
-    // Several query heads per kv head, key groups of 64 to 256 tokens and value
-    // groups of 64 channels or more: the quantized stream runs on the matrix cores.
-    if (L.gqa >= 2 && L.G >= 64 && L.G <= 256 && L.GV >= 64 && (L.D == 128 || L.nvg == 1)) {
+    // Several query heads per kv head (or 8-bit codes), key groups of 64 to 256
+    // tokens and value groups of 64 channels or more: the quantized stream runs on
+    // the matrix cores.
+    if ((L.gqa >= 2 || L.bits == 8) && L.G >= 64 && L.G <= 256 && L.GV >= 64 && (L.D == 128 || L.nvg == 1)) {
         const void* mf = nullptr;
         const int tpg = L.G / 64;
         if (L.bits == 4 && L.D == 128) mf = dec::decode_mf_kernel_ptr<4, 128>(L.gqa, tpg, L.nvg);
         if (L.bits == 2 && L.D == 128) mf = dec::decode_mf_kernel_ptr<2, 128>(L.gqa, tpg, L.nvg);
         if (L.bits == 4 && L.D == 64) mf = dec::decode_mf_kernel_ptr<4, 64>(L.gqa, tpg, L.nvg);
         if (L.bits == 2 && L.D == 64) mf = dec::decode_mf_kernel_ptr<2, 64>(L.gqa, tpg, L.nvg);
+        if (L.bits == 8 && L.D == 128) mf = dec::decode_mf_kernel_ptr<8, 128>(L.gqa, tpg, L.nvg);
+        if (L.bits == 8 && L.D == 64) mf = dec::decode_mf_kernel_ptr<8, 64>(L.gqa, tpg, L.nvg);
         if (mf != nullptr) {
             c.fn = mf;
             c.tile = 64;

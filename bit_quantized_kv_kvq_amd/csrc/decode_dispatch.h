@@ -34,6 +34,10 @@ template <>
 const void* decode_mf_kernel_ptr<4, 64>(int, int, int);
 template <>
 const void* decode_mf_kernel_ptr<2, 64>(int, int, int);
+template <>
+const void* decode_mf_kernel_ptr<8, 128>(int, int, int);
+template <>
+const void* decode_mf_kernel_ptr<8, 64>(int, int, int);
 
 // Key channels per lane (CPL): 32 for MHA with head_dim 128 (4 lanes per token),
 // 16 when several query heads multiply the register state, 8 for 8 query heads
@@ -87,6 +91,17 @@ const void* decode_mf_kernel_ptr<2, 64>(int, int, int);
 // value groups of 64 channels or more: one or two per token at head_dim 128, one at 64
 #define KVQ_DECODE_MF_TABLE_D128(BITS) KVQ_DECODE_MF_GQ(BITS, 128, 1) KVQ_DECODE_MF_GQ(BITS, 128, 2)
 #define KVQ_DECODE_MF_TABLE_D64(BITS) KVQ_DECODE_MF_GQ(BITS, 64, 1)
+// 8-bit codes run on the matrix cores only: one query head per kv head as well
+#define KVQ_DECODE_MF8_TABLE_D128                                          \
+    KVQ_DECODE_MF_TPG(8, 128, 1, 1) KVQ_DECODE_MF_TPG(8, 128, 1, 2) KVQ_DECODE_MF_TABLE_D128(8)
+#define KVQ_DECODE_MF8_TABLE_D64 KVQ_DECODE_MF_TPG(8, 64, 1, 1) KVQ_DECODE_MF_TABLE_D64(8)
+
+#define KVQ_DEFINE_MF8_KERNEL_PTR(D_)                                           \
+    template <>                                                                 \
+    const void* decode_mf_kernel_ptr<8, D_>(int gqa, int tpg, int nvg) {        \
+        KVQ_DECODE_MF8_TABLE_D##D_                                              \
+        return nullptr;                                                         \
+    }
 
 #define KVQ_DEFINE_MF_KERNEL_PTR(BITS, D_)                                           \
     template <>                                                                      \

@@ -312,10 +312,13 @@ __device__ __forceinline__ float packed_f32(const uint32_t* w, int i) {
 // operand (the folded query q_c s_c of a key group, or the weights p_t s_t of a
 // tile; |n| <= 2^18 as in the VALU path) is split into three balanced base-256
 // digits, and each (query head, digit) pair is one row of the 16-row A operand
-// (rows 4 h + digit; row 4 h + 3 and absent heads are zero).  The codes, unpacked
-// to unsigned bytes, are the B operand.  The digits are recombined by shifts
-// (Horner) in int32: |sum_c n_c u_c| <= 2^18 * 15 * 128 < 2^31.  Zero points enter
-// through sum_c (q_c s_c) z_c and sum_t (p_t s_t) z_t in fp32, as in the VALU path.
+// (rows 4 h + digit; row 4 h + 3 and absent heads are zero).  The codes are the B
+// operand: 4- and 2-bit codes unpacked to unsigned bytes, 8-bit fields (int8
+// code - 128) as loaded.  The digits are recombined by shifts (Horner) in int32
+// for 4- and 2-bit codes (|sum_c n_c u_c| <= 2^18 * 15 * 128 < 2^31), in fp32 for
+// 8-bit codes.  Zero points enter through sum_c (q_c s_c) (z_c - o) and
+// sum_t (p_t s_t) (z_t - o) in fp32 (o = 128 for 8-bit fields, else 0), as in
+// the VALU path.  One query head per kv head is the case GQ = 1 (8-bit codes).
 //
 // Operand layout of the instruction (lane l, byte e of its 16 bytes): A row l % 16,
 // k = 16 (l / 16) + e; B column l % 16, same k; result column l % 16, rows
@@ -353,6 +356,11 @@ struct MStream {
     static constexpr int VBB = 16 / TB;         // value dwords per lane, channel and tile
     static constexpr int RB = D * BITS / 8;     // key row bytes
     static constexpr int KLW = RB / 16;         // key dwords per lane and token
+    static constexpr int KLD = KLW > 4 ? 4 : KLW;  // dwords per key load
+    static constexpr int KLN = KLW / KLD;          // key loads per lane and token
+    // 8-bit fields are int8 code - 128 (used as stored); 4- and 2-bit codes are
+    // unpacked to unsigned bytes
+    static constexpr float ZOFF = BITS == 8 ? 128.0f : 0.0f;
     static constexpr int KM = D / 64;           // fold channels per lane
     static constexpr int VCPL = D / 32;
     static constexpr int AK_BYTES = RBK * NKK * 1024;
@@ -365,7 +373,7 @@ struct MStream {
     static __host__ __device__ constexpr int lds_bytes() { return AK_BYTES + 2 * AV_BYTES; }
 
     struct Tile {
-        typename UVec<KLW>::T k[NSB];
+        typename UVec<KLD>::T k[NSB][KLN];
         u32x4 v[NVB][VBB];
         typename UVec<2 * NVG>::T vm[NSB];  // (scale, zero) of each value group of token 16 sb + l % 16
         typename UVec<KM>::T ks, kz;
@@ -415,7 +423,9 @@ struct MStream {
         const uint32_t grp = grp0 + (uint32_t)min(j, max(last_group, 0)) * group_step;
         const int t0 = tig * TM;
 #pragma unroll
-        for (int sb = 0; sb < NSB; ++sb) tt.k[sb] = bload<KLW>(rs, k_off, grp + (t0 + 16 * sb) * RB);
+        for (int sb = 0; sb < NSB; ++sb)
+#pragma unroll
+            for (int ln = 0; ln < KLN; ++ln) tt.k[sb][ln] = bload<KLD>(rs, k_off + 16 * ln, grp + (t0 + 16 * sb) * RB);
 #pragma unroll
         for (int m = 0; m < NVB; ++m)
 #pragma unroll
@@ -452,7 +462,7 @@ struct MStream {
             for (int j = 0; j < KM; ++j) {
                 qt[h][j] = qv[h][j] * __uint_as_float(elem(ks, j));
                 mx[h] = fmaxf(mx[h], fabsf(qt[h][j]));
-                bp[h] = fmaf(qt[h][j], __uint_as_float(elem(kz, j)), bp[h]);
+                bp[h] = fmaf(qt[h][j], __uint_as_float(elem(kz, j)) - ZOFF, bp[h]);
             }
         }
 #pragma unroll
@@ -490,6 +500,14 @@ struct MStream {
         }
     }
 
+    // Digit rows of one product back to the integer sum: in int32 (Horner) for
+    // 4- and 2-bit codes, whose totals stay below 2^31; in fp32 for 8-bit codes
+    // (each row sum is exact in fp32, the total may exceed 2^31).
+    __device__ __forceinline__ static float combine(const i32x4& r) {
+        if constexpr (BITS == 8) return fmaf((float)r[2], 65536.0f, fmaf((float)r[1], 256.0f, (float)r[0]));
+        else return (float)horner256(r);
+    }
+
     // unsigned code bytes of four 4-bit codes (two dwords of 8) or of sixteen
     // 2-bit codes (one dword), in item order
     __device__ __forceinline__ static i32x4 unpack(uint32_t w0, uint32_t w1) {
@@ -511,19 +529,24 @@ struct MStream {
         float sc[RBK][NSB];
 #pragma unroll
         for (int sb = 0; sb < NSB; ++sb) {
-            const auto kw = whole(cur.k[sb]);
             i32x4 bk[NKK];
+            if constexpr (BITS == 8) {
 #pragma unroll
-            for (int kk = 0; kk < NKK; ++kk) {
-                if constexpr (BITS == 4) bk[kk] = unpack(elem(kw, 2 * kk), elem(kw, 2 * kk + 1));
-                else bk[kk] = unpack(elem(kw, kk), 0u);
+                for (int kk = 0; kk < NKK; ++kk) bk[kk] = __builtin_bit_cast(i32x4, whole(cur.k[sb][kk]));
+            } else {
+                const auto kw = whole(cur.k[sb][0]);
+#pragma unroll
+                for (int kk = 0; kk < NKK; ++kk) {
+                    if constexpr (BITS == 4) bk[kk] = unpack(elem(kw, 2 * kk), elem(kw, 2 * kk + 1));
+                    else bk[kk] = unpack(elem(kw, kk), 0u);
+                }
             }
 #pragma unroll
             for (int rb = 0; rb < RBK; ++rb) {
                 i32x4 r = mfma_i8(ak[rb][0], bk[0], zero);
 #pragma unroll
                 for (int kk = 1; kk < NKK; ++kk) r = mfma_i8(ak[rb][kk], bk[kk], r);
-                sc[rb][sb] = (float)horner256(r) * kinv_l[rb] - kbias_l[rb];
+                sc[rb][sb] = combine(r) * kinv_l[rb] - kbias_l[rb];
             }
         }
         uint8_t* avb = av_lds + buf * AV_BYTES;
@@ -556,7 +579,7 @@ struct MStream {
                 for (int sb = 0; sb < NSB; ++sb) {
                     const auto vmw = whole(cur.vm[sb]);
                     w[sb] = p[sb] * __uint_as_float(elem(vmw, 2 * g));
-                    z2[rb][g] = fmaf(w[sb], __uint_as_float(elem(vmw, 2 * g + 1)), z2[rb][g]);
+                    z2[rb][g] = fmaf(w[sb], __uint_as_float(elem(vmw, 2 * g + 1)) - ZOFF, z2[rb][g]);
                     wmax = fmaxf(wmax, w[sb]);
                 }
                 const FixScale fs = fix_scale(group_max<16>(wmax));
@@ -580,16 +603,19 @@ struct MStream {
                 av[g][rb] = *reinterpret_cast<const i32x4*>(avb + ((g * RBK + rb) * 16 + (lane & 15)) * 64 + (lane >> 4) * 16);
 #pragma unroll
         for (int m = 0; m < NVB; ++m) {
-            const u32x4 w0 = whole(cur.v[m][0]);
-            const u32x4 w1 = whole(cur.v[m][VBB - 1]);
+            u32x4 w[VBB];
+#pragma unroll
+            for (int bb = 0; bb < VBB; ++bb) w[bb] = whole(cur.v[m][bb]);
             const int g = NVG == 1 ? 0 : m;  // two value groups: one per 64-channel block
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const i32x4 bv = unpack(w0[i], w1[i]);
+                i32x4 bv;
+                if constexpr (BITS == 8) bv = i32x4{(int)w[0][i], (int)w[1][i], (int)w[2][i], (int)w[3][i]};
+                else bv = unpack(w[0][i], w[VBB - 1][i]);
 #pragma unroll
                 for (int rb = 0; rb < RBK; ++rb) {
                     const i32x4 r = mfma_i8(av[g][rb], bv, zero);
-                    acc2[rb][4 * m + i] = fmaf((float)horner256(r), vinv[rb][g], acc2[rb][4 * m + i]);
+                    acc2[rb][4 * m + i] = fmaf(combine(r), vinv[rb][g], acc2[rb][4 * m + i]);
                 }
             }
         }
@@ -685,16 +711,21 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
     constexpr int LPT = D / CPL;           // key lanes per token
     constexpr int TPW = 64 / LPT;          // tokens per key wave-load
     constexpr int U = TILE / TPW;          // tokens per slot per tile
-    constexpr int LW = CPL * BITS / 32;    // packed key dwords per lane per token
+    // Code width of the VALU stream.  8-bit codes always take the matrix-core
+    // stream (MF); their instantiations compile the VALU stream as 4-bit code
+    // that never runs.
+    constexpr int VB = BITS == 8 ? 4 : BITS;
+    static_assert(BITS != 8 || MF, "8-bit codes run on the matrix-core stream only");
+    constexpr int LW = CPL * VB / 32;      // packed key dwords per lane per token
     constexpr int KND = CPL / 8;           // key nibble dwords per lane per token
-    constexpr int RB = D * BITS / 8;       // key row bytes
-    constexpr int TB = 32 / BITS;          // tokens per value dword
+    constexpr int RB = D * VB / 8;         // key row bytes
+    constexpr int TB = 32 / VB;            // tokens per value dword
     constexpr int VCPL = D / 32;           // value channels per lane
     constexpr int NVL = TILE / (2 * TB);   // value wave-loads per tile
     constexpr int VNE = TB / 8;            // nibble dwords per value code dword
     constexpr int KM = D / 64;             // channels per lane in the query fold
-    constexpr int ZB = BITS == 4 ? 8 : 0;  // code bias
-    static_assert(LW >= 1 && LW * 32 == CPL * BITS, "key lane chunk must be whole dwords");
+    constexpr int ZB = VB == 4 ? 8 : 0;    // code bias
+    static_assert(LW >= 1 && LW * 32 == CPL * VB, "key lane chunk must be whole dwords");
     static_assert(U >= 1 && U * TPW == TILE, "tile must be whole key wave-loads");
     static_assert(NVL >= 1 && NVL * 2 * TB == TILE, "tile must be whole value wave-loads");
     static_assert(TPG == 1 || TPG == 2 || TPG == 4 || TPG == 8, "tiles per key group");
@@ -887,7 +918,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
                     const uint8_t* base = kd + (h * kLimbs + li) * D + chunk * CPL;
 #pragma unroll
                     for (int nd = 0; nd < KND; ++nd) {
-                        if constexpr (BITS == 4)
+                        if constexpr (VB == 4)
                             kl[h][li][nd] = digit_dword(base + 8 * nd, base + 8 * nd + 4);
                         else
                             kl[h][li][nd] = digit_dword(base + 16 * (nd >> 1) + 4 * (nd & 1),
@@ -907,7 +938,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
                 const auto kw = whole(cur.k[u]);
 #pragma unroll
                 for (int d = 0; d < LW; ++d) {
-                    if constexpr (BITS == 4) {
+                    if constexpr (VB == 4) {
                         cw[d] = elem(kw, d);  // fields are already code - 8
                     } else {
                         cw[2 * d] = elem(kw, d) & 0x33333333u;
@@ -976,7 +1007,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
                 const auto vv = whole(cur.v[vl]);
 #pragma unroll
                 for (int c = 0; c < VCPL; ++c) {
-                    if constexpr (BITS == 4) {
+                    if constexpr (VB == 4) {
                         vw[vl][c][0] = elem(vv, c);  // fields are already code - 8
                     } else {
                         vw[vl][c][0] = elem(vv, c) & 0x33333333u;
@@ -1004,7 +1035,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
 #pragma unroll
                     for (int vl = 0; vl < NVL; ++vl) {
                         uint32_t dl[VNE];
-                        if constexpr (BITS == 4) {
+                        if constexpr (VB == 4) {
                             dl[0] = w[2 * vl] | (w[2 * vl + 1] << 4);
                         } else {
                             dl[0] = w[4 * vl] | (w[4 * vl + 2] << 4);

@@ -77,7 +77,7 @@ kvq_status validate(const kvq_config* c) {
         return fail(KVQ_ERR_INVALID_ARG, "unknown dtype %d", c->dtype);
     if (!(c->sm_scale >= 0.0f) || isinf(c->sm_scale))
         return fail(KVQ_ERR_INVALID_ARG, "sm_scale must be finite and >= 0");
-    if (c->bits != 2 && c->bits != 4) return fail(KVQ_ERR_UNSUPPORTED, "bits must be 2 or 4");
+    if (c->bits != 2 && c->bits != 4 && c->bits != 8) return fail(KVQ_ERR_UNSUPPORTED, "bits must be 2, 4 or 8");
     if (c->head_dim != 64 && c->head_dim != 128)
         return fail(KVQ_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
     const int g = c->n_q_heads / c->n_kv_heads;

@@ -31,7 +31,8 @@ constexpr int kMaxCombine = 1024;      // max (splits x query heads per kv head)
 // so a slice's quantized tokens are one contiguous stream of records.  A packed
 // field holds the code XOR code_bias(bits): for 4-bit codes the field is the
 // two's-complement nibble of code - 8, which the decode kernel's signed 4-bit
-// dot products take as is.
+// dot products take as is; for 8-bit codes it is the int8 code - 128, which the
+// matrix cores' int8 products take as is.
 // ---------------------------------------------------------------------------
 struct Layout {
     int B, Hkv, Hq, D, bits, codec, G, GV, R, S, dtype, esize, gqa, nvg, row_bytes;
@@ -57,7 +58,7 @@ struct DevPtrs {
 // byte-to-float conversions, and the unpacked order is the channel order.
 // ---------------------------------------------------------------------------
 __host__ __device__ inline int pack_shift(int bits, int j) { return 8 * (j & 3) + bits * (j >> 2); }
-__host__ __device__ inline uint32_t code_bias(int bits) { return bits == 4 ? 8u : 0u; }
+__host__ __device__ inline uint32_t code_bias(int bits) { return bits == 4 ? 8u : bits == 8 ? 128u : 0u; }
 
 // Record addressing.
 __host__ __device__ inline size_t rec_offset(int64_t bh, int64_t grp, int64_t ng_cap, int rec_bytes) {

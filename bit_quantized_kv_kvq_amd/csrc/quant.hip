@@ -446,10 +446,14 @@ hipError_t launch_quantize(const Layout& L, const DevPtrs& P, const void* src_k,
         if (L.dtype == DT_F32) KVQ_QLAUNCH(DT_F32, 4);
         else if (L.dtype == DT_BF16) KVQ_QLAUNCH(DT_BF16, 4);
         else KVQ_QLAUNCH(DT_F16, 4);
-    } else {
+    } else if (L.bits == 2) {
         if (L.dtype == DT_F32) KVQ_QLAUNCH(DT_F32, 2);
         else if (L.dtype == DT_BF16) KVQ_QLAUNCH(DT_BF16, 2);
         else KVQ_QLAUNCH(DT_F16, 2);
+    } else {
+        if (L.dtype == DT_F32) KVQ_QLAUNCH(DT_F32, 8);
+        else if (L.dtype == DT_BF16) KVQ_QLAUNCH(DT_BF16, 8);
+        else KVQ_QLAUNCH(DT_F16, 8);
     }
 #undef KVQ_QLAUNCH
     return hipGetLastError();

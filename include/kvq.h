@@ -89,7 +89,9 @@ typedef struct kvq_config {
     int32_t n_kv_heads;   /* Hkv >= 1                                             */
     int32_t n_q_heads;    /* Hq, a multiple of Hkv; Hq / Hkv in {1, 2, 4, 8}      */
     int32_t head_dim;     /* D in {64, 128}                                       */
-    int32_t bits;         /* n in {2, 4}                                          */
+    int32_t bits;         /* n in {2, 4, 8}; 8-bit codes need G >= 64 and G_V   */
+                          /* >= 64.  Mixed precision per layer: one cache per    */
+                          /* layer, each with its own bits                       */
     int32_t k_group;      /* G: tokens per key group; 32, 64, 128 or 256          */
     int32_t v_group;      /* G_V: channels per value group; divides D, a multiple */
                           /* of 16                                                */
@@ -116,8 +118,9 @@ kvq_status kvq_cache_bytes(const kvq_config* cfg, size_t* bytes);
  * initialisation.  *out receives the handle, to be freed with
  * kvq_cache_destroy.  Errors: INVALID_ARG (null pointer, non-positive sizes,
  * Hq % Hkv != 0, R % G != 0, D % G_V != 0, codec not a kvq_codec, misaligned buffer),
- * UNSUPPORTED (bits not 2/4, D not 64/128, Hq/Hkv not 1/2/4/8, G not in
- * {32, 64, 128, 256}, G_V not a multiple of 16, B * Hkv > 65535, more than
+ * UNSUPPORTED (bits not 2/4/8, D not 64/128, Hq/Hkv not 1/2/4/8, G not in
+ * {32, 64, 128, 256}, G_V not a multiple of 16, 8-bit codes with G or G_V
+ * below 64, B * Hkv > 65535, more than
  * 2 GiB of quantized records per (sequence, kv head)), BUFFER_TOO_SMALL,
  * DEVICE (no current HIP device).
  */

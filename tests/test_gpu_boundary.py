@@ -71,6 +71,9 @@ def _attend_and_check(w, cache, K, V, seed=5):
     dict(codec=1),                                      # symmetric groups
     dict(codec=1, bits=2, n_sink=3, dtype="f32", head_dim=64, v_group=16),
     dict(codec=1, n_q_heads=8, k_group=64, residual=128, v_group=64),  # symmetric, matrix cores
+    dict(bits=8, k_group=64, residual=128, v_group=64),                # 8-bit, one head per kv head
+    dict(bits=8, n_q_heads=8, k_group=128, residual=128, v_group=128, n_sink=3),  # 8-bit GQA 4
+    dict(bits=8, codec=1, head_dim=64, dtype="f32", k_group=64, residual=64, v_group=64),
 ])
 @pytest.mark.parametrize("n", [1, 63, 64, 65, 200])
 def test_variants_against_oracle(kw, n):

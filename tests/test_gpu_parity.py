@@ -29,6 +29,8 @@ SMALL = {
                                        prefill=1000, steps=40),
     "sym_small": wl.get("llama7b_mha_int4_sym").replace(name="sym_small", batch=2, n_kv_heads=3,
                                                         n_q_heads=3, prefill=1000, steps=30),
+    "int8_small": wl.get("llama7b_mha_int8").replace(name="int8_small", batch=2, n_kv_heads=3,
+                                                     n_q_heads=6, prefill=1000, steps=30),
 }
 
 
@@ -137,6 +139,7 @@ FULL = {
     "gqa_32k_int4": ([(0, 0), (15, 7)], None),
     "long_128k_sink_int2": ([(0, 0), (0, 7)], {0, 3, 4, 7}),
     "llama7b_mha_int4_sym": ([(0, 0), (5, 9)], None),
+    "llama7b_mha_int8": ([(0, 0), (7, 30)], None),
 }
 
 

@@ -50,7 +50,8 @@ def _expected_bytes(c):
 
 @pytest.mark.parametrize("kw", [{}, dict(bits=2), dict(dtype=kvq.KVQ_F32, head_dim=64, v_group=64),
                                 dict(n_sink=0, max_tokens=129), dict(max_tokens=3),
-                                dict(n_q_heads=32, n_kv_heads=4)])
+                                dict(n_q_heads=32, n_kv_heads=4), dict(bits=8, v_group=64),
+                                dict(bits=8, n_q_heads=4, k_group=128, v_group=128)])
 def test_cache_bytes_matches_layout(kw):
     c = _cfg(**kw)
     assert kvq.kvq_cache_bytes(c) == _expected_bytes(c)
@@ -58,7 +59,9 @@ def test_cache_bytes_matches_layout(kw):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(bits=3), kvq.KVQ_ERR_UNSUPPORTED),
-    (dict(bits=8), kvq.KVQ_ERR_UNSUPPORTED),
+    (dict(bits=8), kvq.KVQ_ERR_UNSUPPORTED),                 # 8-bit codes need G_V >= 64
+    (dict(bits=8, k_group=32, v_group=64), kvq.KVQ_ERR_UNSUPPORTED),  # and G >= 64
+    (dict(bits=16), kvq.KVQ_ERR_UNSUPPORTED),
     (dict(head_dim=96, v_group=32), kvq.KVQ_ERR_UNSUPPORTED),
     (dict(n_q_heads=12, n_kv_heads=4), kvq.KVQ_ERR_UNSUPPORTED),
     (dict(n_q_heads=6, n_kv_heads=4), kvq.KVQ_ERR_INVALID_ARG),

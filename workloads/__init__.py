@@ -119,6 +119,15 @@ WORKLOADS: Dict[str, Workload] = {
         bits=4, k_group=128, v_group=128, residual=128, n_sink=0,
         prefill=4096, steps=64, attend_after_prefill=False, seed=1002,
         k_outlier_channels=4, k_outlier_scale=8.0, codec=1),
+    "llama7b_mha_int8": Workload(
+        name="llama7b_mha_int8",
+        description="the Llama-7B-shaped MHA decode with INT8 groups (a layer kept at 8 bits "
+                    "in per-layer mixed precision): B8 H32 D128, context 4096, bf16, "
+                    "G128 / G_V128, R128, 64 decode steps",
+        batch=8, n_kv_heads=32, n_q_heads=32, head_dim=128, dtype="bf16",
+        bits=8, k_group=128, v_group=128, residual=128, n_sink=0,
+        prefill=4096, steps=64, attend_after_prefill=False, seed=1002,
+        k_outlier_channels=4, k_outlier_scale=8.0),
 }
 
 # short aliases in the order the workloads are listed
