@@ -8,7 +8,8 @@ CPU fallback: if libkvq.so is missing or fails to load, every call raises.
 Low-level functions mirror the C entry points one to one (kvq_cache_bytes,
 kvq_cache_create, kvq_append, kvq_decode_workspace_bytes, kvq_decode_attention,
 kvq_dequantize, kvq_export, kvq_cache_state, kvq_set_split_tokens,
-kvq_set_timing_events, kvq_stream_read_probe, kvq_last_error); ``Cache`` bundles them with torch-allocated buffers.
+kvq_set_timing_events, kvq_stream_read_probe, kvq_append_ragged, kvq_seq_lengths,
+kvq_last_error); ``Cache`` bundles them with torch-allocated buffers.
 """
 from __future__ import annotations
 
@@ -34,7 +35,7 @@ EXPORTED = ["kvq_cache_bytes", "kvq_cache_create", "kvq_cache_destroy", "kvq_app
             "kvq_decode_workspace_bytes", "kvq_decode_attention", "kvq_append_decode",
             "kvq_dequantize", "kvq_export",
             "kvq_cache_state", "kvq_set_split_tokens", "kvq_set_timing_events", "kvq_stream_read_probe",
-            "kvq_last_error"]
+            "kvq_append_ragged", "kvq_seq_lengths", "kvq_last_error"]
 
 
 class KVQError(RuntimeError):
@@ -81,6 +82,8 @@ def lib() -> ctypes.CDLL:
             "kvq_set_split_tokens": [P, i64],
             "kvq_set_timing_events": [P, P, P],
             "kvq_stream_read_probe": [P, ctypes.c_size_t, ctypes.c_int32, P, P],
+            "kvq_append_ragged": [P, P, P, ctypes.POINTER(ctypes.c_int32), i64, P],
+            "kvq_seq_lengths": [P, ctypes.POINTER(i64)],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -169,6 +172,19 @@ def kvq_cache_state(handle: int) -> Tuple[int, int, int, int]:
 
 def kvq_set_split_tokens(handle: int, tokens: int):
     _check(lib().kvq_set_split_tokens(ctypes.c_void_p(handle), tokens))
+
+
+def kvq_append_ragged(handle: int, k: int, v: int, n_new, n_max: int, stream: int):
+    """n_new: sequence of B ints (host)."""
+    arr = (ctypes.c_int32 * len(n_new))(*[int(x) for x in n_new])
+    _check(lib().kvq_append_ragged(ctypes.c_void_p(handle), ctypes.c_void_p(k), ctypes.c_void_p(v), arr,
+                                   n_max, ctypes.c_void_p(stream)))
+
+
+def kvq_seq_lengths(handle: int, batch: int):
+    arr = (ctypes.c_int64 * batch)()
+    _check(lib().kvq_seq_lengths(ctypes.c_void_p(handle), arr))
+    return [int(x) for x in arr]
 
 
 def kvq_stream_read_probe(buf: int, nbytes: int, blocks_per_cu: int, sink: int, stream: int):

@@ -92,6 +92,21 @@ class Cache:
             raise ValueError("k and v shapes differ")
         _k.kvq_append(self.handle, k.data_ptr(), v.data_ptr(), k.shape[2], _stream())
 
+    def append_ragged(self, k: torch.Tensor, v: torch.Tensor, n_new):
+        """Append n_new[b] tokens to sequence b: k, v [B, Hkv, n_max, D] in the cache
+        dtype (rows past n_new[b] are not read); n_new: B ints in [0, n_max]."""
+        self._check_tokens(k, "k")
+        self._check_tokens(v, "v")
+        if k.shape != v.shape:
+            raise ValueError("k and v shapes differ")
+        if len(n_new) != self.cfg.batch:
+            raise ValueError("n_new needs one count per sequence")
+        _k.kvq_append_ragged(self.handle, k.data_ptr(), v.data_ptr(), list(n_new), k.shape[2], _stream())
+
+    def seq_lengths(self):
+        """Tokens held by each sequence (host-side)."""
+        return _k.kvq_seq_lengths(self.handle, self.cfg.batch)
+
     def decode(self, q: torch.Tensor, out: Optional[torch.Tensor] = None,
                lse: Optional[torch.Tensor] = None, with_lse: bool = True):
         """Attention of q [B, Hq, D] over the cache -> (out fp32 [B, Hq, D], lse fp32 [B, Hq])."""
@@ -136,9 +151,10 @@ class Cache:
         """fp32 K', V' [B, Hkv, n_tokens, D] in token order (sinks, quantized, residual)."""
         c = self.cfg
         T = self.state()[0]
-        k = torch.empty((c.batch, c.n_kv_heads, T, c.head_dim), dtype=torch.float32,
+        # zero-filled: rows past a shorter sequence's own length are not written
+        k = torch.zeros((c.batch, c.n_kv_heads, T, c.head_dim), dtype=torch.float32,
                         device=self.device)
-        v = torch.empty_like(k)
+        v = torch.zeros_like(k)
         _k.kvq_dequantize(self.handle, k.data_ptr(), v.data_ptr(), _stream())
         return k, v
 
@@ -148,14 +164,14 @@ class Cache:
         Lq = self.state()[2]
         dev = self.device
         out = dict(
-            k_codes=torch.empty((c.batch, c.n_kv_heads, Lq, c.head_dim), dtype=torch.uint8, device=dev),
-            k_scale=torch.empty((c.batch, c.n_kv_heads, Lq // c.k_group, c.head_dim),
+            k_codes=torch.zeros((c.batch, c.n_kv_heads, Lq, c.head_dim), dtype=torch.uint8, device=dev),
+            k_scale=torch.zeros((c.batch, c.n_kv_heads, Lq // c.k_group, c.head_dim),
                                 dtype=torch.float32, device=dev),
-            v_codes=torch.empty((c.batch, c.n_kv_heads, Lq, c.head_dim), dtype=torch.uint8, device=dev),
-            v_scale=torch.empty((c.batch, c.n_kv_heads, Lq, c.head_dim // c.v_group),
+            v_codes=torch.zeros((c.batch, c.n_kv_heads, Lq, c.head_dim), dtype=torch.uint8, device=dev),
+            v_scale=torch.zeros((c.batch, c.n_kv_heads, Lq, c.head_dim // c.v_group),
                                 dtype=torch.float32, device=dev))
-        out["k_zero"] = torch.empty_like(out["k_scale"])
-        out["v_zero"] = torch.empty_like(out["v_scale"])
+        out["k_zero"] = torch.zeros_like(out["k_scale"])
+        out["v_zero"] = torch.zeros_like(out["v_scale"])
         ptrs = [out[n].data_ptr() if out[n].numel() else 0
                 for n in ("k_codes", "k_scale", "k_zero", "v_codes", "v_scale", "v_zero")]
         _k.kvq_export(self.handle, ptrs, _stream())

@@ -136,6 +136,8 @@ hipError_t launch_decode(const Layout& L, const DevPtrs& P, const DecodeRequest&
     a.nsplit = nsplit;
     a.nsplit_cap = rq.nsplit_cap;
     a.qscale = sm_scale * 1.4426950408889634f;
+    a.base_len = rq.rg.base_len;
+    a.len_delta = rq.rg.delta;
     void* args[] = {&a};
     const dim3 grid((unsigned)nsplit, (unsigned)L.BH);
     if (rq.ev_start != nullptr)

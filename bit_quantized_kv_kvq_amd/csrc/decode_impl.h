@@ -70,6 +70,10 @@ struct DecArgs {
     int dtype;  // storage dtype of q, sinks and residual (DT_*)
     int Hkv, S, R, nS, nfp, G, GV, nvg, gps, ngroups, nsplit, nsplit_cap;
     float qscale;  // sm_scale * log2(e)
+    // Sequences of different lengths: sequence b holds base_len[b] + len_delta
+    // tokens, and nS, nfp, ngroups above are replaced by its own; null otherwise.
+    const int* base_len;
+    int len_delta;
 };
 
 constexpr int kLimbs = 5;
@@ -738,6 +742,14 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
     const int split = blockIdx.x;
     const int64_t bh = blockIdx.y;
     const int b = (int)(bh / a.Hkv), kvh = (int)(bh % a.Hkv);
+    // this slice's sinks, full-precision tokens and key groups
+    int nS_s = a.nS, nfp_s = a.nfp, ng_s = a.ngroups;
+    if (a.base_len != nullptr) {
+        const SliceState st = slice_state((int64_t)a.base_len[b] + a.len_delta, a.S, a.R);
+        nS_s = st.nS;
+        nfp_s = st.nS + st.r;
+        ng_s = st.Lq / a.G;
+    }
     const int tid = threadIdx.x, lane = tid & 63;
     // wave index as a scalar, so that loop bounds and branches derived from it are
     // wave-uniform (scalar branches, no exec-mask loops)
@@ -778,7 +790,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
     if (copy_fresh) {
         const int es = a.dtype == DT_F32 ? 4 : 2;
         const int chunks = D * es / 16;
-        const int64_t dst_row = bh * a.R + (a.nfp - 1 - a.nS);
+        const int64_t dst_row = bh * a.R + (nfp_s - 1 - nS_s);
         if (lane < 2 * chunks) {
             const bool is_v = lane >= chunks;
             const int c = is_v ? lane - chunks : lane;
@@ -831,7 +843,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
     constexpr int BODY = TPG > NR ? TPG : NR;  // tiles per loop iteration (4 or 8)
     constexpr int GB = BODY / TPG;             // key groups per loop iteration
     const int g_begin = split * a.gps;
-    const int g_end = min(g_begin + a.gps, a.ngroups);
+    const int g_end = min(g_begin + a.gps, ng_s);
     const int n_my_groups = g_begin + wave < g_end ? (g_end - g_begin - wave + kWaves - 1) / kWaves : 0;
 
     {
@@ -1070,8 +1082,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
         // iteration's arithmetic is straight-line code for one storage dtype, so
         // each wait is for its own loads only, not for the prefetch behind them.
         // Rows past the split's end reload its first row and get weight 0.
-        const int f0 = (int)((int64_t)split * a.nfp / a.nsplit);
-        const int f1 = (int)((int64_t)(split + 1) * a.nfp / a.nsplit);
+        const int f0 = (int)((int64_t)split * nfp_s / a.nsplit);
+        const int f1 = (int)((int64_t)(split + 1) * nfp_s / a.nsplit);
         constexpr int CPLF = 16;          // key channels per lane
         constexpr int LPTF = D / CPLF;    // lanes per token
         constexpr int TPWF = 64 / LPTF;   // tokens per wave step
@@ -1085,10 +1097,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
             typedef __attribute__((address_space(1))) const char gchar;
             const int64_t erow = (int64_t)D * es;
             const uint64_t a_sink = reinterpret_cast<uint64_t>(key ? ksink : vsink) + (bh * a.S + j) * erow;
-            const uint64_t a_res = reinterpret_cast<uint64_t>(key ? kres : vres) + (bh * a.R + (j - a.nS)) * erow;
+            const uint64_t a_res = reinterpret_cast<uint64_t>(key ? kres : vres) + (bh * a.R + (j - nS_s)) * erow;
             const uint64_t a_new = reinterpret_cast<uint64_t>(key ? knew : vnew) + bh * erow;
-            const bool fresh = knew != nullptr && j == a.nfp - 1;
-            const uint64_t x = (fresh ? a_new : j < a.nS ? a_sink : a_res) + e0 * es;
+            const bool fresh = knew != nullptr && j == nfp_s - 1;
+            const uint64_t x = (fresh ? a_new : j < nS_s ? a_sink : a_res) + e0 * es;
             return (const char*)reinterpret_cast<gchar*>(x);
         };
         auto prologue = [&](auto dtc) __attribute__((always_inline)) {

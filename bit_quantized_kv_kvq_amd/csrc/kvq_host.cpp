@@ -10,6 +10,7 @@
 
 #include <algorithm>
 #include <new>
+#include <vector>
 
 #include "../../include/kvq.h"
 #include "kvq_internal.h"
@@ -25,7 +26,12 @@ struct kvq_cache {
     Layout L;
     DevPtrs P;
     char* buf;
-    int64_t nS, Lq, r;        // sinks held, quantized tokens, residual tokens
+    int64_t nS, Lq, r;        // sinks held, quantized tokens, residual tokens (all sequences
+                              // alike; with `ragged`, those of the longest sequence)
+    bool ragged = false;      // the sequences differ in length
+    std::vector<int64_t> len; // tokens per sequence
+    int len_delta = 0;        // one-token appends to every sequence since base_len was set
+    int* base_len = nullptr;  // device int32 [B] in the cache buffer (ragged caches)
     int64_t split_tokens;     // 0 = automatic
     int num_cu;
     int nsplit_cap;           // max splits per slice the workspace holds
@@ -136,6 +142,7 @@ Layout make_layout(const kvq_config* c) {
     L.off_kres = take((size_t)L.BH * L.R * fp_row);
     L.off_vres = take((size_t)L.BH * L.R * fp_row);
     L.off_rec = take((size_t)L.BH * L.ng_cap * L.rec_bytes);
+    L.off_lens = take((size_t)L.B * sizeof(int));
     L.total = off;
     return L;
 }
@@ -185,6 +192,10 @@ kvq_status kvq_cache_create(const kvq_config* cfg, void* dev_buf, size_t bytes, 
     c->P.vres = c->buf + L.off_vres;
     c->P.rec = (uint8_t*)(c->buf + L.off_rec);
     c->nS = c->Lq = c->r = 0;
+    c->ragged = false;
+    c->len.assign((size_t)L.B, 0);
+    c->len_delta = 0;
+    c->base_len = reinterpret_cast<int*>(c->buf + L.off_lens);
     c->split_tokens = 0;
     c->num_cu = ncu > 0 ? ncu : 256;
     const int64_t want = std::max<int64_t>(8, (16LL * c->num_cu + L.BH - 1) / L.BH);
@@ -200,6 +211,96 @@ kvq_status kvq_cache_destroy(kvq_cache* cache) {
     return ok();
 }
 
+}  // extern "C"
+
+namespace {
+
+// Appends n_new tokens (src_*[bh][src_tokens][D], tokens 0 .. n_new - 1) to slices
+// [bh0, bh0 + nbh), which all hold the state st (updated).  Sinks first, then a
+// partly filled residual (flushed when it reaches R), then whole R-token blocks
+// quantized straight from the input, then the remainder as a new residual.
+kvq_status append_slices(kvq_cache* c, const void* k, const void* v, int64_t n_new, int64_t src_tokens,
+                         int64_t bh0, int64_t nbh, SliceState& st, hipStream_t s) {
+    const Layout& L = c->L;
+    kvq_status e;
+    int64_t src = 0, rem = n_new;
+    // 1. sinks
+    if (st.nS < L.S && rem > 0) {
+        const int64_t take = std::min<int64_t>(L.S - st.nS, rem);
+        if ((e = check_hip(launch_copy_tokens(L, k, v, src_tokens, src, c->P.ksink, c->P.vsink, L.S, st.nS,
+                                              take, bh0, nbh, s),
+                           "append")))
+            return e;
+        st.nS += (int)take;
+        src += take;
+        rem -= take;
+    }
+    // 2. top up a partly filled residual; flush it when it reaches R
+    if (rem > 0 && st.r > 0) {
+        const int64_t take = std::min<int64_t>(L.R - st.r, rem);
+        if ((e = check_hip(launch_copy_tokens(L, k, v, src_tokens, src, c->P.kres, c->P.vres, L.R, st.r, take,
+                                              bh0, nbh, s),
+                           "append")))
+            return e;
+        st.r += (int)take;
+        src += take;
+        rem -= take;
+        if (st.r == L.R) {
+            if ((e = check_hip(launch_quantize(L, c->P, c->P.kres, c->P.vres, L.R, 0, L.R / L.G, st.Lq, bh0, nbh, s),
+                               "flush")))
+                return e;
+            st.Lq += L.R;
+            st.r = 0;
+        }
+    }
+    // 3. complete R-token blocks straight from the input
+    const int64_t nblk = rem / L.R;
+    if (nblk > 0) {
+        if ((e = check_hip(launch_quantize(L, c->P, k, v, src_tokens, src, nblk * (L.R / L.G), st.Lq, bh0, nbh, s),
+                           "quantize")))
+            return e;
+        st.Lq += (int)(nblk * L.R);
+        src += nblk * L.R;
+        rem -= nblk * L.R;
+    }
+    // 4. the remainder starts a new residual
+    if (rem > 0) {
+        if ((e = check_hip(launch_copy_tokens(L, k, v, src_tokens, src, c->P.kres, c->P.vres, L.R, 0, rem,
+                                              bh0, nbh, s),
+                           "append")))
+            return e;
+        st.r = (int)rem;
+    }
+    return KVQ_OK;
+}
+
+int64_t max_len(const kvq_cache* c) { return *std::max_element(c->len.begin(), c->len.end()); }
+
+// After an append: back to the uniform state when every sequence has the same
+// length; otherwise the state of the longest sequence, with the device lengths
+// rewritten (write_lengths) or advanced by the caller.
+kvq_status settle(kvq_cache* c, bool write_lengths, hipStream_t s) {
+    const int64_t mx = max_len(c);
+    const bool equal = *std::min_element(c->len.begin(), c->len.end()) == mx;
+    const SliceState st = slice_state(mx, c->L.S, c->L.R);
+    c->nS = st.nS, c->Lq = st.Lq, c->r = st.r;
+    if (equal) {
+        c->ragged = false;
+        return KVQ_OK;
+    }
+    c->ragged = true;
+    if (write_lengths) {
+        kvq_status e = check_hip(launch_set_lengths(c->L, c->base_len, c->len.data(), s), "append");
+        if (e != KVQ_OK) return e;
+        c->len_delta = 0;
+    }
+    return KVQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 kvq_status kvq_append(kvq_cache* c, const void* k, const void* v, int64_t n_new, void* stream) {
     if (!c) return fail(KVQ_ERR_INVALID_ARG, "cache is NULL");
     if (n_new < 0) return fail(KVQ_ERR_INVALID_ARG, "n_new must be >= 0");
@@ -207,59 +308,79 @@ kvq_status kvq_append(kvq_cache* c, const void* k, const void* v, int64_t n_new,
     if (!k || !v) return fail(KVQ_ERR_INVALID_ARG, "k or v is NULL");
     if (!aligned(k, 16) || !aligned(v, 16)) return fail(KVQ_ERR_INVALID_ARG, "k and v must be 16-byte aligned");
     const Layout& L = c->L;
-    const int64_t total = c->nS + c->Lq + c->r;
+    const int64_t total = max_len(c);
     if (n_new > L.max_tokens - total)
         return fail(KVQ_ERR_CAPACITY, "append of %lld tokens exceeds max_tokens %lld (holding %lld)",
                     (long long)n_new, (long long)L.max_tokens, (long long)total);
     hipStream_t s = (hipStream_t)stream;
     kvq_status st;
-    int64_t src = 0, rem = n_new;
-    // 1. sinks
-    if (c->nS < L.S && rem > 0) {
-        const int64_t take = std::min<int64_t>(L.S - c->nS, rem);
-        if ((st = check_hip(launch_copy_tokens(L, k, v, n_new, src, c->P.ksink, c->P.vsink, L.S, c->nS,
-                                               take, s),
-                            "append")))
-            return st;
-        c->nS += take;
-        src += take;
-        rem -= take;
+    if (!c->ragged) {
+        SliceState ss{(int)c->nS, (int)c->Lq, (int)c->r};
+        if ((st = append_slices(c, k, v, n_new, n_new, 0, L.BH, ss, s)) != KVQ_OK) return st;
+        c->nS = ss.nS, c->Lq = ss.Lq, c->r = ss.r;
+        for (auto& n : c->len) n += n_new;
+        return ok();
     }
-    // 2. top up a partly filled residual; flush it when it reaches R
-    if (rem > 0 && c->r > 0) {
-        const int64_t take = std::min<int64_t>(L.R - c->r, rem);
-        if ((st = check_hip(launch_copy_tokens(L, k, v, n_new, src, c->P.kres, c->P.vres, L.R, c->r, take,
-                                               s),
+    if (n_new == 1) {
+        // every sequence's token to its own sink slot or residual row, then the
+        // flush of each sequence whose residual is now full
+        if ((st = check_hip(launch_copy_one_ragged(L, c->P, k, v, Ragged{c->base_len, c->len_delta}, s),
                             "append")))
             return st;
-        c->r += take;
-        src += take;
-        rem -= take;
-        if (c->r == L.R) {
-            if ((st = check_hip(launch_quantize(L, c->P, c->P.kres, c->P.vres, L.R, 0, L.R / L.G, c->Lq, s),
-                                "flush")))
-                return st;
-            c->Lq += L.R;
-            c->r = 0;
+        for (int b = 0; b < L.B; ++b) {
+            const SliceState ss = slice_state(c->len[b], L.S, L.R);
+            if (c->len[b] >= L.S && ss.r + 1 == L.R) {
+                if ((st = check_hip(launch_quantize(L, c->P, c->P.kres, c->P.vres, L.R, 0, L.R / L.G, ss.Lq,
+                                                    (int64_t)b * L.Hkv, L.Hkv, s),
+                                    "flush")))
+                    return st;
+            }
+            c->len[b] += 1;
         }
+        c->len_delta += 1;
+        return (st = settle(c, false, s)) != KVQ_OK ? st : ok();
     }
-    // 3. complete R-token blocks straight from the input
-    const int64_t nblk = rem / L.R;
-    if (nblk > 0) {
-        if ((st = check_hip(launch_quantize(L, c->P, k, v, n_new, src, nblk * (L.R / L.G), c->Lq, s),
-                            "quantize")))
-            return st;
-        c->Lq += nblk * L.R;
-        src += nblk * L.R;
-        rem -= nblk * L.R;
+    // several tokens: sequence by sequence
+    for (int b = 0; b < L.B; ++b) {
+        SliceState ss = slice_state(c->len[b], L.S, L.R);
+        if ((st = append_slices(c, k, v, n_new, n_new, (int64_t)b * L.Hkv, L.Hkv, ss, s)) != KVQ_OK) return st;
+        c->len[b] += n_new;
     }
-    // 4. the remainder starts a new residual
-    if (rem > 0) {
-        if ((st = check_hip(launch_copy_tokens(L, k, v, n_new, src, c->P.kres, c->P.vres, L.R, 0, rem, s),
-                            "append")))
-            return st;
-        c->r = rem;
+    return (st = settle(c, true, s)) != KVQ_OK ? st : ok();
+}
+
+kvq_status kvq_append_ragged(kvq_cache* c, const void* k, const void* v, const int32_t* n_new, int64_t n_max,
+                             void* stream) {
+    if (!c || !n_new) return fail(KVQ_ERR_INVALID_ARG, "cache or n_new is NULL");
+    if (n_max < 0) return fail(KVQ_ERR_INVALID_ARG, "n_max must be >= 0");
+    const Layout& L = c->L;
+    bool any = false;
+    for (int b = 0; b < L.B; ++b) {
+        if (n_new[b] < 0 || n_new[b] > n_max)
+            return fail(KVQ_ERR_INVALID_ARG, "n_new[%d] = %d is outside [0, n_max = %lld]", b, n_new[b],
+                        (long long)n_max);
+        if (n_new[b] > L.max_tokens - c->len[b])
+            return fail(KVQ_ERR_CAPACITY, "append of %d tokens to sequence %d exceeds max_tokens %lld (holding %lld)",
+                        n_new[b], b, (long long)L.max_tokens, (long long)c->len[b]);
+        any |= n_new[b] > 0;
     }
+    if (!any) return ok();
+    if (!k || !v) return fail(KVQ_ERR_INVALID_ARG, "k or v is NULL");
+    if (!aligned(k, 16) || !aligned(v, 16)) return fail(KVQ_ERR_INVALID_ARG, "k and v must be 16-byte aligned");
+    hipStream_t s = (hipStream_t)stream;
+    kvq_status st;
+    for (int b = 0; b < L.B; ++b) {
+        if (n_new[b] == 0) continue;
+        SliceState ss = slice_state(c->len[b], L.S, L.R);
+        if ((st = append_slices(c, k, v, n_new[b], n_max, (int64_t)b * L.Hkv, L.Hkv, ss, s)) != KVQ_OK) return st;
+        c->len[b] += n_new[b];
+    }
+    return (st = settle(c, true, s)) != KVQ_OK ? st : ok();
+}
+
+kvq_status kvq_seq_lengths(const kvq_cache* c, int64_t* lens) {
+    if (!c || !lens) return fail(KVQ_ERR_INVALID_ARG, "cache or lens is NULL");
+    for (int b = 0; b < c->L.B; ++b) lens[b] = c->len[b];
     return ok();
 }
 
@@ -274,11 +395,13 @@ kvq_status kvq_decode_attention(kvq_cache* c, const void* q, float* out, float* 
     if (!c || !q || !out || !ws) return fail(KVQ_ERR_INVALID_ARG, "cache, q, out or ws is NULL");
     if (!aligned(q, 4) || !aligned(out, 4) || (lse && !aligned(lse, 4)) || !aligned(ws, 256))
         return fail(KVQ_ERR_INVALID_ARG, "misaligned q, out, lse or ws");
-    if (c->nS + c->Lq + c->r == 0) return fail(KVQ_ERR_INVALID_ARG, "attention on an empty cache");
+    if (*std::min_element(c->len.begin(), c->len.end()) == 0)
+        return fail(KVQ_ERR_INVALID_ARG, c->ragged ? "attention on an empty sequence" : "attention on an empty cache");
     const size_t need = decode_workspace_bytes(c->L, c->nsplit_cap);
     if (ws_bytes < need)
         return fail(KVQ_ERR_BUFFER_TOO_SMALL, "workspace holds %zu bytes, needs %zu", ws_bytes, need);
     DecodeRequest rq;
+    if (c->ragged) rq.rg = Ragged{c->base_len, c->len_delta};
     rq.Lq = c->Lq;
     rq.nS = c->nS;
     rq.r = c->r;
@@ -298,9 +421,10 @@ kvq_status kvq_append_decode(kvq_cache* c, const void* k, const void* v, const v
     if (!c || !k || !v || !q || !out || !ws)
         return fail(KVQ_ERR_INVALID_ARG, "cache, k, v, q, out or ws is NULL");
     const Layout& L = c->L;
-    // A token that lands in a sink slot or fills the residual (flush) takes the
-    // two-call path; every other token is appended inside the decode launch.
-    if (c->nS < L.S || c->r + 1 >= L.R) {
+    // A token that lands in a sink slot or fills the residual (flush), or a cache
+    // whose sequences differ in length, takes the two-call path; every other token
+    // is appended inside the decode launch.
+    if (c->ragged || c->nS < L.S || c->r + 1 >= L.R) {
         kvq_status st = kvq_append(c, k, v, 1, stream);
         if (st != KVQ_OK) return st;
         return kvq_decode_attention(c, q, out, lse, ws, ws_bytes, stream);
@@ -329,12 +453,14 @@ kvq_status kvq_append_decode(kvq_cache* c, const void* k, const void* v, const v
                               "append_decode");
     if (st != KVQ_OK) return st;
     c->r += 1;
+    for (auto& n : c->len) n += 1;
     return ok();
 }
 
 kvq_status kvq_dequantize(const kvq_cache* c, float* k_out, float* v_out, void* stream) {
     if (!c || !k_out || !v_out) return fail(KVQ_ERR_INVALID_ARG, "NULL argument");
     kvq_status st = check_hip(launch_dequantize(c->L, c->P, c->nS, c->Lq, c->r, k_out, v_out,
+                                                c->ragged ? Ragged{c->base_len, c->len_delta} : Ragged{},
                                                 (hipStream_t)stream),
                               "dequantize");
     if (st != KVQ_OK) return st;
@@ -345,7 +471,9 @@ kvq_status kvq_export(const kvq_cache* c, uint8_t* k_codes, float* k_scale, floa
                       uint8_t* v_codes, float* v_scale, float* v_zero, void* stream) {
     if (!c) return fail(KVQ_ERR_INVALID_ARG, "cache is NULL");
     kvq_status st = check_hip(launch_export(c->L, c->P, c->Lq, k_codes, k_scale, k_zero, v_codes,
-                                            v_scale, v_zero, (hipStream_t)stream),
+                                            v_scale, v_zero,
+                                            c->ragged ? Ragged{c->base_len, c->len_delta} : Ragged{},
+                                            (hipStream_t)stream),
                               "export");
     if (st != KVQ_OK) return st;
     return ok();

@@ -38,8 +38,30 @@ struct Layout {
     int B, Hkv, Hq, D, bits, codec, G, GV, R, S, dtype, esize, gqa, nvg, row_bytes;
     int64_t BH, max_tokens, Lq_cap, ng_cap;
     int rec_bytes, rec_kcodes, rec_vcodes, rec_vmeta;
-    size_t off_ksink, off_vsink, off_kres, off_vres, off_rec, total;
+    size_t off_ksink, off_vsink, off_kres, off_vres, off_rec, off_lens, total;
 };
+
+// Sequences of different lengths.  Sequence b holds base_len[b] + delta tokens;
+// base_len (int32 [B]) lives in the cache buffer, written by launch_set_lengths,
+// and delta counts the one-token appends to every sequence since then.  A null
+// base_len means every sequence has the length the launch is given.
+struct Ragged {
+    const int* base_len = nullptr;
+    int delta = 0;
+};
+
+// Sinks held, quantized tokens and residual tokens of a sequence of n tokens:
+// the first S tokens are sinks, then whole runs of R tokens are quantized and
+// fewer than R stay in the residual.
+struct SliceState {
+    int nS, Lq, r;
+};
+__host__ __device__ inline SliceState slice_state(int64_t n, int S, int R) {
+    const int64_t nS = n < S ? n : S;
+    const int64_t q = n - nS;
+    const int64_t Lq = (q / R) * R;
+    return {(int)nS, (int)Lq, (int)(q - Lq)};
+}
 
 struct DevPtrs {
     char* ksink;
@@ -91,19 +113,28 @@ __device__ inline float load_as_f32(const void* base, int64_t idx) {
 // launch interfaces (defined in the .hip sources)
 // ---------------------------------------------------------------------------
 
-// Copy n tokens of every slice of K and V from src_*[bh][src_tok0 + i][D] (src
-// holds src_tokens tokens per slice) to dst_*[bh][dst_tok0 + i][D] (dst holds
+// Copy n tokens of slices [bh0, bh0 + nbh) of K and V from src_*[bh][src_tok0 + i][D]
+// (src holds src_tokens tokens per slice) to dst_*[bh][dst_tok0 + i][D] (dst holds
 // dst_tokens per slice), in one launch.  Storage dtype preserved.
 hipError_t launch_copy_tokens(const Layout& L, const void* src_k, const void* src_v,
                               int64_t src_tokens, int64_t src_tok0, char* dst_k, char* dst_v,
-                              int64_t dst_tokens, int64_t dst_tok0, int64_t n, hipStream_t stream);
+                              int64_t dst_tokens, int64_t dst_tok0, int64_t n, int64_t bh0, int64_t nbh,
+                              hipStream_t stream);
 
-// Quantize n_groups consecutive key groups (n_groups * G tokens) of every slice,
-// read from src_k/src_v[bh][src_tok0 + t][D] (src_tokens tokens per slice), into
-// quantized token positions dst_tok0 + t.
+// Quantize n_groups consecutive key groups (n_groups * G tokens) of slices
+// [bh0, bh0 + nbh), read from src_k/src_v[bh][src_tok0 + t][D] (src_tokens tokens
+// per slice), into quantized token positions dst_tok0 + t.
 hipError_t launch_quantize(const Layout& L, const DevPtrs& P, const void* src_k, const void* src_v,
                            int64_t src_tokens, int64_t src_tok0, int64_t n_groups, int64_t dst_tok0,
-                           hipStream_t stream);
+                           int64_t bh0, int64_t nbh, hipStream_t stream);
+
+// One token per sequence (src_*[bh][D]) into each slice's own sink slot or residual
+// row, from the sequence's length before the append (rg).
+hipError_t launch_copy_one_ragged(const Layout& L, const DevPtrs& P, const void* src_k, const void* src_v,
+                                  Ragged rg, hipStream_t stream);
+
+// base_len[b] = lens[b] for b < L.B (lens: host array).
+hipError_t launch_set_lengths(const Layout& L, int* base_len, const int64_t* lens, hipStream_t stream);
 
 struct DecodeRequest {
     int64_t Lq;            // quantized tokens per slice
@@ -119,6 +150,9 @@ struct DecodeRequest {
     // If set, HIP events that take the decode kernel's own start and end times.
     hipEvent_t ev_start = nullptr;
     hipEvent_t ev_stop = nullptr;
+    // Sequences of different lengths: each slice's state comes from its length;
+    // Lq, nS, r above are then those of the longest sequence (split plan, grid).
+    Ragged rg;
 };
 
 hipError_t launch_decode(const Layout& L, const DevPtrs& P, const DecodeRequest& rq, const void* q,
@@ -129,11 +163,15 @@ bool decode_supported(const Layout& L);
 
 size_t decode_workspace_bytes(const Layout& L, int max_splits);
 
+// Dequantize to [BH][T_out][D] fp32 (T_out = nS + Lq + r, the longest sequence's
+// length with rg); with rg, rows past a slice's own length are not written.
 hipError_t launch_dequantize(const Layout& L, const DevPtrs& P, int64_t nS, int64_t Lq, int64_t r,
-                             float* k_out, float* v_out, hipStream_t stream);
+                             float* k_out, float* v_out, Ragged rg, hipStream_t stream);
 
+// Export codes [BH][Lq][D] and metadata (Lq of the longest sequence with rg; rows past
+// a slice's own quantized length are not written).
 hipError_t launch_export(const Layout& L, const DevPtrs& P, int64_t Lq, uint8_t* k_codes,
                          float* k_scale, float* k_zero, uint8_t* v_codes, float* v_scale,
-                         float* v_zero, hipStream_t stream);
+                         float* v_zero, Ragged rg, hipStream_t stream);
 
 }  // namespace kvq

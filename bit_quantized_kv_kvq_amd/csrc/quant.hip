@@ -10,6 +10,8 @@
 // replaced by |min| (1 when min == 0); a zero point of -0 is stored as +0.
 // Grouping (KIVI notes, "LLM系列：KVCache量化1 KIVI…", section 1): keys per channel
 // over each run of G tokens, values per token over each run of G_V channels.
+#include <algorithm>
+
 #include "kvq_internal.h"
 
 namespace kvq {
@@ -56,15 +58,15 @@ __global__ __launch_bounds__(256) void copy_tokens_kernel(const uint4* __restric
                                                           uint4* __restrict__ dst_k,
                                                           uint4* __restrict__ dst_v, int64_t dst_tokens,
                                                           int64_t dst_tok0, int64_t n, int row_vec,
-                                                          int64_t total) {
-    // total = BH * n * row_vec vectors of K, then as many of V
+                                                          int64_t bh0, int64_t total) {
+    // total = nbh * n * row_vec vectors of K, then as many of V
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < 2 * total;
          i += (int64_t)gridDim.x * blockDim.x) {
         const bool is_v = i >= total;
         const int64_t j = is_v ? i - total : i;
         const int64_t v = j % row_vec;
         const int64_t t = (j / row_vec) % n;
-        const int64_t bh = j / ((int64_t)row_vec * n);
+        const int64_t bh = bh0 + j / ((int64_t)row_vec * n);
         const int64_t si = (bh * src_tokens + src_tok0 + t) * row_vec + v;
         const int64_t di = (bh * dst_tokens + dst_tok0 + t) * row_vec + v;
         if (is_v)
@@ -72,6 +74,42 @@ __global__ __launch_bounds__(256) void copy_tokens_kernel(const uint4* __restric
         else
             dst_k[di] = src_k[si];
     }
+}
+
+// One token per sequence (src [BH][D]) into each slice's own sink slot or residual
+// row, for caches whose sequences differ in length: the slice's length before the
+// append is base_len[b] + delta.  A slice with n < S tokens takes sink slot n;
+// otherwise residual row n - S - Lq (fewer than R tokens wait there).
+__global__ __launch_bounds__(256) void copy_one_ragged_kernel(const uint4* __restrict__ src_k,
+                                                              const uint4* __restrict__ src_v,
+                                                              uint4* __restrict__ ksink, uint4* __restrict__ vsink,
+                                                              uint4* __restrict__ kres, uint4* __restrict__ vres,
+                                                              const int* __restrict__ base_len, int delta,
+                                                              int Hkv, int S, int R, int row_vec, int64_t total) {
+    // total = BH * row_vec vectors of K, then as many of V
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < 2 * total;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const bool is_v = i >= total;
+        const int64_t j = is_v ? i - total : i;
+        const int64_t v = j % row_vec;
+        const int64_t bh = j / row_vec;
+        const int64_t n = (int64_t)base_len[bh / Hkv] + delta;
+        const SliceState st = slice_state(n, S, R);
+        uint4* dst;
+        if (n < S) dst = (is_v ? vsink : ksink) + (bh * S + n) * row_vec + v;
+        else dst = (is_v ? vres : kres) + (bh * R + st.r) * row_vec + v;
+        *dst = (is_v ? src_v : src_k)[bh * row_vec + v];
+    }
+}
+
+// base_len[i] = v[i] for i < n (values passed in the kernel arguments)
+constexpr int kLenChunk = 256;
+struct LenChunk {
+    int n;
+    int v[kLenChunk];
+};
+__global__ __launch_bounds__(kLenChunk) void set_lengths_kernel(int* __restrict__ dst, LenChunk c) {
+    if ((int)threadIdx.x < c.n) dst[threadIdx.x] = c.v[threadIdx.x];
 }
 
 // ---------------------------------------------------------------------------
@@ -86,6 +124,7 @@ struct QuantArgs {
     int64_t ng_cap;
     int rec_bytes, rec_kcodes, rec_vcodes, rec_vmeta;
     int codec;  // kvq_codec
+    int64_t bh0;  // first slice of the launch
     uint8_t* rec;
 };
 
@@ -168,7 +207,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
     extern __shared__ __align__(16) uint8_t smem[];
     constexpr float qmax = (float)((1 << BITS) - 1);
     const int grp = blockIdx.x;
-    const int64_t bh = blockIdx.y;
+    const int64_t bh = a.bh0 + blockIdx.y;
     const int D = a.D, G = a.G, tid = threadIdx.x;
     uint8_t* s_codes = smem;                                               // [G][D]
     float* s_mm = reinterpret_cast<float*>(smem + (((size_t)G * D + 15) & ~(size_t)15));  // [P][D][2]
@@ -277,10 +316,22 @@ struct DeqArgs {
     const uint8_t* rec;
     float* kout;
     float* vout;
-    int64_t nS, Lq, r, T, ng_cap;
+    int64_t nS, Lq, r, T, ng_cap;  // the slices' state; with base_len, the longest sequence's
     int S, R, D, G, GV, nvg, bits, row_bytes;
     int rec_bytes, rec_kcodes, rec_vcodes, rec_vmeta;
+    const int* base_len;  // sequences of different lengths (see Ragged), or null
+    int delta;
+    int Hkv;
 };
+
+// State of slice bh: the launch's (uniform) one, or the one of its sequence's length.
+__device__ inline void deq_slice(const DeqArgs& a, int64_t bh, int64_t& nS, int64_t& Lq, int64_t& r) {
+    nS = a.nS, Lq = a.Lq, r = a.r;
+    if (a.base_len != nullptr) {
+        const SliceState st = slice_state((int64_t)a.base_len[bh / a.Hkv] + a.delta, a.S, a.R);
+        nS = st.nS, Lq = st.Lq, r = st.r;
+    }
+}
 
 __device__ inline uint32_t key_code(const DeqArgs& a, const uint8_t* rec, int t, int c) {
     const int cpd = 32 / a.bits;
@@ -297,18 +348,20 @@ __device__ inline uint32_t value_code(const DeqArgs& a, const uint8_t* rec, int 
 template <int DT>
 __global__ __launch_bounds__(256) void dequantize_kernel(DeqArgs a) {
     const int64_t bh = blockIdx.y;
-    const int64_t n = a.T * a.D;
+    int64_t nS, Lq, r;
+    deq_slice(a, bh, nS, Lq, r);
+    const int64_t n = (nS + Lq + r) * a.D;  // this slice's tokens; rows up to a.T in the output
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
          i += (int64_t)gridDim.x * blockDim.x) {
         const int64_t t = i / a.D;
         const int c = (int)(i % a.D);
         float kx, vx;
-        if (t < a.nS) {
+        if (t < nS) {
             const int64_t idx = (bh * a.S + t) * a.D + c;
             kx = load_as_f32<DT>(a.ksink, idx);
             vx = load_as_f32<DT>(a.vsink, idx);
-        } else if (t < a.nS + a.Lq) {
-            const int64_t tq = t - a.nS;
+        } else if (t < nS + Lq) {
+            const int64_t tq = t - nS;
             const int tg = (int)(tq % a.G);
             const uint8_t* rec = a.rec + rec_offset(bh, tq / a.G, a.ng_cap, a.rec_bytes);
             const float* km = reinterpret_cast<const float*>(rec);
@@ -318,7 +371,7 @@ __global__ __launch_bounds__(256) void dequantize_kernel(DeqArgs a) {
             kx = (kq - km[a.D + c]) * km[c];
             vx = (vq - vm[1]) * vm[0];
         } else {
-            const int64_t idx = (bh * a.R + (t - a.nS - a.Lq)) * a.D + c;
+            const int64_t idx = (bh * a.R + (t - nS - Lq)) * a.D + c;
             kx = load_as_f32<DT>(a.kres, idx);
             vx = load_as_f32<DT>(a.vres, idx);
         }
@@ -336,8 +389,10 @@ __global__ __launch_bounds__(256) void export_kernel(DeqArgs a, uint8_t* k_codes
     const int64_t bh = blockIdx.y;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t ncode = a.Lq * a.D;
-    for (int64_t i = i0; i < ncode; i += stride) {
+    int64_t nS_b, Lq_b, r_b;
+    deq_slice(a, bh, nS_b, Lq_b, r_b);
+    const int64_t ncode = a.Lq * a.D;  // output rows per slice (the longest sequence's)
+    for (int64_t i = i0; i < Lq_b * a.D; i += stride) {
         const int64_t t = i / a.D;
         const int c = (int)(i % a.D);
         const uint8_t* rec = a.rec + rec_offset(bh, t / a.G, a.ng_cap, a.rec_bytes);
@@ -346,7 +401,7 @@ __global__ __launch_bounds__(256) void export_kernel(DeqArgs a, uint8_t* k_codes
         if (v_codes) v_codes[bh * ncode + i] = (uint8_t)value_code(a, rec, tg, c);
     }
     const int64_t nk = (a.Lq / a.G) * a.D;
-    for (int64_t i = i0; i < nk; i += stride) {
+    for (int64_t i = i0; i < (Lq_b / a.G) * a.D; i += stride) {
         const int64_t g = i / a.D;
         const int c = (int)(i % a.D);
         const float* km = reinterpret_cast<const float*>(a.rec + rec_offset(bh, g, a.ng_cap, a.rec_bytes));
@@ -354,7 +409,7 @@ __global__ __launch_bounds__(256) void export_kernel(DeqArgs a, uint8_t* k_codes
         if (k_zero) k_zero[bh * nk + i] = km[a.D + c];
     }
     const int64_t nv = a.Lq * a.nvg;
-    for (int64_t i = i0; i < nv; i += stride) {
+    for (int64_t i = i0; i < Lq_b * a.nvg; i += stride) {
         const int64_t t = i / a.nvg;
         const int h = (int)(i % a.nvg);
         const uint8_t* rec = a.rec + rec_offset(bh, t / a.G, a.ng_cap, a.rec_bytes);
@@ -364,8 +419,11 @@ __global__ __launch_bounds__(256) void export_kernel(DeqArgs a, uint8_t* k_codes
     }
 }
 
-DeqArgs make_deq_args(const Layout& L, const DevPtrs& P, int64_t nS, int64_t Lq, int64_t r) {
+DeqArgs make_deq_args(const Layout& L, const DevPtrs& P, int64_t nS, int64_t Lq, int64_t r, Ragged rg) {
     DeqArgs a;
+    a.base_len = rg.base_len;
+    a.delta = rg.delta;
+    a.Hkv = L.Hkv;
     a.ksink = P.ksink;
     a.vsink = P.vsink;
     a.kres = P.kres;
@@ -404,22 +462,47 @@ int grid_for(int64_t work, int64_t per_block, int cap) {
 
 hipError_t launch_copy_tokens(const Layout& L, const void* src_k, const void* src_v,
                               int64_t src_tokens, int64_t src_tok0, char* dst_k, char* dst_v,
-                              int64_t dst_tokens, int64_t dst_tok0, int64_t n, hipStream_t stream) {
-    if (n <= 0) return hipSuccess;
+                              int64_t dst_tokens, int64_t dst_tok0, int64_t n, int64_t bh0, int64_t nbh,
+                              hipStream_t stream) {
+    if (n <= 0 || nbh <= 0) return hipSuccess;
     const int row_vec = L.D * L.esize / 16;
-    const int64_t total = L.BH * n * row_vec;
+    const int64_t total = nbh * n * row_vec;
     const int grid = grid_for(2 * total, 256, 65535);
     copy_tokens_kernel<<<grid, 256, 0, stream>>>(
         reinterpret_cast<const uint4*>(src_k), reinterpret_cast<const uint4*>(src_v), src_tokens,
         src_tok0, reinterpret_cast<uint4*>(dst_k), reinterpret_cast<uint4*>(dst_v), dst_tokens,
-        dst_tok0, n, row_vec, total);
+        dst_tok0, n, row_vec, bh0, total);
     return hipGetLastError();
+}
+
+hipError_t launch_copy_one_ragged(const Layout& L, const DevPtrs& P, const void* src_k, const void* src_v,
+                                  Ragged rg, hipStream_t stream) {
+    const int row_vec = L.D * L.esize / 16;
+    const int64_t total = L.BH * row_vec;
+    const int grid = grid_for(2 * total, 256, 65535);
+    copy_one_ragged_kernel<<<grid, 256, 0, stream>>>(
+        reinterpret_cast<const uint4*>(src_k), reinterpret_cast<const uint4*>(src_v),
+        reinterpret_cast<uint4*>(P.ksink), reinterpret_cast<uint4*>(P.vsink), reinterpret_cast<uint4*>(P.kres),
+        reinterpret_cast<uint4*>(P.vres), rg.base_len, rg.delta, L.Hkv, L.S, L.R, row_vec, total);
+    return hipGetLastError();
+}
+
+hipError_t launch_set_lengths(const Layout& L, int* base_len, const int64_t* lens, hipStream_t stream) {
+    for (int b0 = 0; b0 < L.B; b0 += kLenChunk) {
+        LenChunk c;
+        c.n = std::min(kLenChunk, L.B - b0);
+        for (int i = 0; i < c.n; ++i) c.v[i] = (int)lens[b0 + i];
+        set_lengths_kernel<<<1, kLenChunk, 0, stream>>>(base_len + b0, c);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 hipError_t launch_quantize(const Layout& L, const DevPtrs& P, const void* src_k, const void* src_v,
                            int64_t src_tokens, int64_t src_tok0, int64_t n_groups, int64_t dst_tok0,
-                           hipStream_t stream) {
-    if (n_groups <= 0) return hipSuccess;
+                           int64_t bh0, int64_t nbh, hipStream_t stream) {
+    if (n_groups <= 0 || nbh <= 0) return hipSuccess;
     QuantArgs a;
     a.src_k = src_k;
     a.src_v = src_v;
@@ -437,10 +520,11 @@ hipError_t launch_quantize(const Layout& L, const DevPtrs& P, const void* src_k,
     a.rec_vcodes = L.rec_vcodes;
     a.rec_vmeta = L.rec_vmeta;
     a.codec = L.codec;
+    a.bh0 = bh0;
     a.rec = P.rec;
     // codes [G][D] bytes, then the keys' partial minima/maxima [P][D][2] fp32
     const size_t lds = (((size_t)L.G * L.D + 15) & ~(size_t)15) + (size_t)(256 / (L.D / 2)) * L.D * 2 * sizeof(float);
-    dim3 grid((unsigned)n_groups, (unsigned)L.BH);
+    dim3 grid((unsigned)n_groups, (unsigned)nbh);
 #define KVQ_QLAUNCH(DT, BITS) quantize_kernel<DT, BITS><<<grid, 256, lds, stream>>>(a)
     if (L.bits == 4) {
         if (L.dtype == DT_F32) KVQ_QLAUNCH(DT_F32, 4);
@@ -460,8 +544,8 @@ hipError_t launch_quantize(const Layout& L, const DevPtrs& P, const void* src_k,
 }
 
 hipError_t launch_dequantize(const Layout& L, const DevPtrs& P, int64_t nS, int64_t Lq, int64_t r,
-                             float* k_out, float* v_out, hipStream_t stream) {
-    DeqArgs a = make_deq_args(L, P, nS, Lq, r);
+                             float* k_out, float* v_out, Ragged rg, hipStream_t stream) {
+    DeqArgs a = make_deq_args(L, P, nS, Lq, r, rg);
     a.kout = k_out;
     a.vout = v_out;
     if (a.T == 0) return hipSuccess;
@@ -474,9 +558,9 @@ hipError_t launch_dequantize(const Layout& L, const DevPtrs& P, int64_t nS, int6
 
 hipError_t launch_export(const Layout& L, const DevPtrs& P, int64_t Lq, uint8_t* k_codes,
                          float* k_scale, float* k_zero, uint8_t* v_codes, float* v_scale,
-                         float* v_zero, hipStream_t stream) {
+                         float* v_zero, Ragged rg, hipStream_t stream) {
     if (Lq == 0) return hipSuccess;
-    DeqArgs a = make_deq_args(L, P, 0, Lq, 0);
+    DeqArgs a = make_deq_args(L, P, 0, Lq, 0, rg);
     dim3 grid(grid_for(Lq * L.D, 256, 4096), (unsigned)L.BH);
     export_kernel<<<grid, 256, 0, stream>>>(a, k_codes, k_scale, k_zero, v_codes, v_scale, v_zero);
     return hipGetLastError();

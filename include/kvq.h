@@ -139,10 +139,11 @@ kvq_status kvq_cache_destroy(kvq_cache* cache);
  * tokens are quantized (keys per channel over each run of G tokens, values per
  * token over each run of G_V channels) and the residual is emptied, so that
  * 0 <= r < R after every call.  Complete R-token blocks of a bulk append are
- * quantized straight from the input.
+ * quantized straight from the input.  Each sequence follows this from its own
+ * length when the sequences differ in length (see kvq_append_ragged).
  *   k, v : device, [B, Hkv, n_new, D] contiguous, in cfg.dtype.
  * n_new == 0 is a no-op.  Errors: INVALID_ARG (null, n_new < 0),
- * CAPACITY (tokens + n_new > max_tokens), DEVICE.
+ * CAPACITY (the longest sequence's tokens + n_new > max_tokens), DEVICE.
  */
 kvq_status kvq_append(kvq_cache* cache, const void* k, const void* v, int64_t n_new,
                       void* stream);
@@ -157,7 +158,8 @@ kvq_status kvq_decode_workspace_bytes(const kvq_cache* cache, size_t* bytes);
  * Decode attention for one query per (sequence, query head):
  *   out[b, h, :] = softmax(q[b, h] . K'^T * sm_scale) V'
  *   lse[b, h]    = log(sum(exp(q[b, h] . K'^T * sm_scale)))   (natural log)
- * over every cached token of kv head h / (Hq / Hkv).  The keys and values of
+ * over every cached token of kv head h / (Hq / Hkv) (of sequence b's own
+ * length when the sequences differ in length).  The keys and values of
  * the quantized part are dequantized on the fly; the token range is split
  * across workgroups and the partial softmax states are merged with a
  * log-sum-exp combine.
@@ -167,8 +169,8 @@ kvq_status kvq_decode_workspace_bytes(const kvq_cache* cache, size_t* bytes);
  *         aligned, ZERO-FILLED before its first use; every call leaves its
  *         counters zero again.  Calls that share a workspace must not overlap.
  * The result matches the binary64 definition to within about 1e-4 absolute for
- * the documented workloads.  Errors: INVALID_ARG (null q/out/ws, empty cache),
- * BUFFER_TOO_SMALL (ws), DEVICE.
+ * the documented workloads.  Errors: INVALID_ARG (null q/out/ws, an empty
+ * sequence), BUFFER_TOO_SMALL (ws), DEVICE.
  */
 kvq_status kvq_decode_attention(kvq_cache* cache, const void* q, float* out, float* lse,
                                 void* ws, size_t ws_bytes, void* stream);
@@ -197,7 +199,9 @@ kvq_status kvq_append_decode(kvq_cache* cache, const void* k, const void* v, con
  * Dequantize the whole cache to fp32 in chronological token order (sinks, then
  * the quantized tokens as x' = (q - z) * s, then the residual); the round trip
  * of the Int4 KV-cache post's section 5.1 `quantize` helper.
- *   k_out, v_out : device, [B, Hkv, n_tokens, D] fp32.
+ *   k_out, v_out : device, [B, Hkv, n_tokens, D] fp32 (n_tokens of
+ *                  kvq_cache_state; rows past a shorter sequence's own length
+ *                  are not written).
  * Errors: INVALID_ARG (null), DEVICE.
  */
 kvq_status kvq_dequantize(const kvq_cache* cache, float* k_out, float* v_out, void* stream);
@@ -208,17 +212,46 @@ kvq_status kvq_dequantize(const kvq_cache* cache, float* k_out, float* v_out, vo
  *   k_codes, v_codes : device uint8 [B, Hkv, n_quant, D]
  *   k_scale, k_zero  : device fp32  [B, Hkv, n_quant / G, D]
  *   v_scale, v_zero  : device fp32  [B, Hkv, n_quant, D / G_V]
- * Any pointer may be NULL to skip that array.  Errors: DEVICE.
+ * (n_quant of kvq_cache_state; rows past a shorter sequence's own quantized
+ * tokens are not written).  Any pointer may be NULL to skip that array.
+ * Errors: DEVICE.
  */
 kvq_status kvq_export(const kvq_cache* cache, uint8_t* k_codes, float* k_scale, float* k_zero,
                       uint8_t* v_codes, float* v_scale, float* v_zero, void* stream);
 
 /*
  * Host-side counters (no device access): total tokens per sequence, sinks
- * held, quantized tokens and residual tokens.  Any pointer may be NULL.
+ * held, quantized tokens and residual tokens.  When the sequences differ in
+ * length: those of the longest sequence.  Any pointer may be NULL.
  */
 kvq_status kvq_cache_state(const kvq_cache* cache, int64_t* n_tokens, int64_t* n_sink,
                            int64_t* n_quant, int64_t* n_resid);
+
+/*
+ * Append a different number of tokens to each sequence: sequence b takes the
+ * first n_new[b] of its rows, as n_new[b] one-token appends from its own state
+ * (sinks, residual and flushes exactly as for kvq_append; KIVI notes,
+ * section 1).  The sequences then differ in length: every later call follows
+ * each sequence's own length (kvq_append of one token per sequence writes each
+ * token to its own slot and flushes only the sequences whose residual fills;
+ * decode attention, dequantize and export use each slice's own tokens).  The
+ * cache returns to the uniform layout's fast paths when the lengths agree again.
+ *   k, v  : device, [B, Hkv, n_max, D] contiguous, in cfg.dtype (rows past
+ *           n_new[b] are not read).
+ *   n_new : host, int32 [B], each in [0, n_max].
+ * All zero is a no-op.  Validation is complete before anything is enqueued.
+ * The sequence lengths live in the cache buffer, written on `stream`.
+ * Errors: INVALID_ARG (null, n_max < 0, n_new[b] outside [0, n_max]),
+ * CAPACITY (a sequence would exceed max_tokens), DEVICE.
+ */
+kvq_status kvq_append_ragged(kvq_cache* cache, const void* k, const void* v, const int32_t* n_new,
+                             int64_t n_max, void* stream);
+
+/*
+ * Host-side: tokens held by each sequence, lens[b] for b < B (host array).
+ * Errors: INVALID_ARG (null).
+ */
+kvq_status kvq_seq_lengths(const kvq_cache* cache, int64_t* lens);
 
 /*
  * Tuning and testing knob: tokens per decode split of the quantized part

@@ -36,7 +36,8 @@ def _cfg(**kw):
 
 
 def _expected_bytes(c):
-    """Sinks and residual (K and V), then one record per key group of capacity."""
+    """Sinks and residual (K and V), one record per key group of capacity, then the
+    int32 length of every sequence."""
     al = lambda x: (x + 255) & ~255
     e = 4 if c.dtype == kvq.KVQ_F32 else 2
     BH = c.batch * c.n_kv_heads
@@ -44,7 +45,7 @@ def _expected_bytes(c):
     Lq_cap = c.residual * (max(0, c.max_tokens - c.n_sink) // c.residual)
     row = D * c.bits // 8
     rec = al(8 * D + 2 * G * row + G * (D // c.v_group) * 8)
-    parts = [BH * c.n_sink * D * e] * 2 + [BH * c.residual * D * e] * 2 + [BH * (Lq_cap // G) * rec]
+    parts = [BH * c.n_sink * D * e] * 2 + [BH * c.residual * D * e] * 2 + [BH * (Lq_cap // G) * rec, 4 * c.batch]
     return sum(al(p) for p in parts)
 
 
