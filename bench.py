@@ -63,6 +63,19 @@ def algorithmic_bytes(w: wl.Workload, n_sink: int, n_quant: int, n_resid: int) -
     return w.batch * w.n_kv_heads * per_slice + w.batch * w.n_q_heads * D * (e + 4)
 
 
+def slice_counts(w: wl.Workload, n: int):
+    """(sinks, quantized, residual) tokens of a sequence of n tokens."""
+    nS = min(n, w.n_sink)
+    Lq = w.residual * ((n - nS) // w.residual)
+    return nS, Lq, n - nS - Lq
+
+
+def algorithmic_bytes_seqs(w: wl.Workload, lens) -> int:
+    """algorithmic_bytes for sequences of the given lengths (one per sequence)."""
+    per_seq = [algorithmic_bytes(w.replace(batch=1), *slice_counts(w, n)) for n in lens]
+    return sum(per_seq)
+
+
 def decode_source_hash() -> str:
     h = hashlib.sha256()
     for name in DECODE_SOURCES:
@@ -218,20 +231,27 @@ def cpu_baseline(w: wl.Workload, budget_s: float):
     n = int(min(n_slices_total, max(threads, budget_s / t_probe * threads)))
     n = max(1, n)
     sample = slices[:n]
-    states = [oracle.slice_state(w, b, h, 0) for b, h in sample]
-    qs = np.stack([np.stack([wl.storage_to_f32(wl.query_slice(w, b, h * g + j)[0], w.dtype)
-                             for j in range(g)]) for b, h in sample])
+    # one batched oracle call per sequence (its slices share one length)
+    groups = []
+    for b in sorted({b for b, _ in sample}):
+        hs = [h for bb, h in sample if bb == b]
+        groups.append(([oracle.slice_state(w, b, h, 0) for h in hs],
+                       np.stack([np.stack([wl.storage_to_f32(wl.query_slice(w, b, h * g + j)[0], w.dtype)
+                                           for j in range(g)]) for h in hs])))
     reps, t0 = 0, time.perf_counter()
     while True:   # repeat the sampled step until the budget is spent
-        oracle.decode_slices(states, qs, scale)
+        for states, qs in groups:
+            oracle.decode_slices(states, qs, scale)
         reps += 1
         if time.perf_counter() - t0 >= budget_s:
             break
     dt = (time.perf_counter() - t0) / reps
-    st = states[0]
-    full = algorithmic_bytes(w, st["n_sink"], st["n_quant"], st["n_resid"])
-    frac = n / n_slices_total
-    gbs = full * frac / dt / 1e9
+    # algorithmic bytes of the sampled slices (a sequence's bytes split evenly over its kv heads)
+    lens = wl.prefill_lengths(w)
+    full = algorithmic_bytes_seqs(w, lens)
+    sampled = sum(algorithmic_bytes_seqs(w, [lens[b]]) / w.n_kv_heads for b, _ in sample)
+    frac = sampled / full
+    gbs = sampled / dt / 1e9
     return {"value": round(gbs, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": "decode step (dequantize + binary64 attention) of %d of %d (sequence, "
                       "kv-head) slices after the %d-token prefill, repeated %d times in %.1f s; "
@@ -284,8 +304,9 @@ def main():
     w = wl.get(args.workload)
 
     # size of one cache's decode traffic; enough layers to overflow the MALL 3x
-    nq0 = w.residual * ((w.prefill - min(w.prefill, w.n_sink)) // w.residual)
-    b0 = algorithmic_bytes(w, min(w.prefill, w.n_sink), nq0, w.prefill - min(w.prefill, w.n_sink) - nq0)
+    lens0 = wl.prefill_lengths(w)
+    ragged = len(set(lens0)) > 1
+    b0 = algorithmic_bytes_seqs(w, lens0)
     L = args.layers or min(64, max(2, math.ceil(3 * MALL_BYTES / b0)))
     # by default every layer appends R tokens in the timed region, so the region
     # holds each layer's residual flush once (its amortised share of the steps)
@@ -308,7 +329,10 @@ def main():
                       max_tokens=max_tokens, device=dev, codec=w.codec)
         if args.split_tokens:
             c.set_split_tokens(args.split_tokens)
-        c.append(Kd, Vd)
+        if ragged:
+            c.append_ragged(Kd, Vd, lens0)
+        else:
+            c.append(Kd, Vd)
         caches.append(c)
     del Kd, Vd
     Ks, Vs = wl.steps_batch(w)
@@ -349,18 +373,16 @@ def main():
         i = (s // L) % w.steps
         # cache state before and after this step's append: the schedule fixes it
         n = w.prefill + s // L + 1
-        nS = min(n, w.n_sink)
-        Lq = w.residual * ((n - nS) // w.residual)
-        r = n - nS - Lq
+        nS, Lq, r = slice_counts(w, n)
         # The step is one kvq_append_decode call when the token joins the residual
-        # without filling it; otherwise (a sink, or a flush) the library appends and
-        # decodes in two launches, and the bench makes the same two calls itself so
-        # that the events bracket the decode alone.
-        fused = n > w.n_sink and r != 0
+        # without filling it; otherwise (a sink, a flush, or sequences of different
+        # lengths) the library appends and decodes in two launches, and the bench
+        # makes the same two calls itself so that the events bracket the decode alone.
+        fused = n > w.n_sink and r != 0 and not ragged
         plan.append((fused, ctypes.c_void_p(c.handle), ctypes.c_void_p(Ks[i].data_ptr()),
                      ctypes.c_void_p(Vs[i].data_ptr()), ctypes.c_void_p(Q[i % Q.shape[0]].data_ptr()),
                      ctypes.c_void_p(c._ws_ptr), c.ws_bytes))
-        step_bytes.append(algorithmic_bytes(w, nS, Lq, r))
+        step_bytes.append(algorithmic_bytes_seqs(w, [n0 + s // L + 1 for n0 in lens0]))
 
     def step(s: int, k):
         fused, h, kp, vp, qp, wsp, wsb = plan[s]
@@ -389,10 +411,9 @@ def main():
     # the cache state the schedule predicts is the one the library reports
     for li, c in enumerate(caches):
         n_done = len(range(li, args.warmup, L))
+        assert c.seq_lengths() == [n0 + n_done for n0 in lens0], (li, c.seq_lengths())
         n = w.prefill + n_done
-        nS = min(n, w.n_sink)
-        Lq = w.residual * ((n - nS) // w.residual)
-        assert tuple(c.state()) == (n, nS, Lq, n - nS - Lq), (li, c.state())
+        assert tuple(c.state()) == (n,) + slice_counts(w, n), (li, c.state())
     t0 = time.perf_counter()
     for k in range(args.steps):
         step(args.warmup + k, k)
@@ -434,6 +455,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "n_kv_heads": w.n_kv_heads,
                    "n_q_heads": w.n_q_heads, "head_dim": w.head_dim, "context": w.prefill,
+                   **({"contexts": lens0} if ragged else {}),
                    "bits": w.bits, "k_group": w.k_group, "v_group": w.v_group,
                    "residual": w.residual, "n_sink": w.n_sink, "storage": w.dtype,
                    "codec": "symmetric" if w.codec else "asymmetric",

@@ -94,6 +94,8 @@ hipError_t launch_decode(const Layout& L, const DevPtrs& P, const DecodeRequest&
     if (rq.split_tokens > 0) {
         gps = (rq.split_tokens + L.G - 1) / L.G;
     } else if (ng > 0) {
+        // Sequences of different lengths: planned for the longest (splitting by
+        // the total over all slices measured slower: more workgroups and combines).
         const int64_t slots = rq.num_cu;
         gps = (L.BH * ng + slots - 1) / slots;
         if (gps > kWaves) gps = (gps + kWaves - 1) / kWaves * kWaves;

@@ -222,6 +222,8 @@ def slice_tokens_f32(w, b: int, kvh: int, n_steps: int):
     """fp32 (storage-rounded) tokens of a slice: prefill followed by n_steps step tokens."""
     import workloads as wl
     kp, vp = wl.prefill_slice(w, b, kvh)
+    n0 = wl.prefill_lengths(w)[b]
+    kp, vp = kp[:n0], vp[:n0]
     k = wl.storage_to_f32(kp, w.dtype)
     v = wl.storage_to_f32(vp, w.dtype)
     if n_steps:

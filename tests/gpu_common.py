@@ -50,7 +50,11 @@ class WorkloadRun:
         self.dev = torch.device("cuda:0")
         self.cache = cache or make_cache(w)
         Kp, Vp = wl.prefill_batch(w)
-        self.cache.append(to_torch(Kp, w.dtype, self.dev), to_torch(Vp, w.dtype, self.dev))
+        lens = wl.prefill_lengths(w)
+        if len(set(lens)) > 1:
+            self.cache.append_ragged(to_torch(Kp, w.dtype, self.dev), to_torch(Vp, w.dtype, self.dev), lens)
+        else:
+            self.cache.append(to_torch(Kp, w.dtype, self.dev), to_torch(Vp, w.dtype, self.dev))
         del Kp, Vp
         Ks, Vs = wl.steps_batch(w)
         self.Ks = to_torch(Ks, w.dtype, self.dev)
@@ -84,13 +88,15 @@ def export_cpu(cache):
 
 
 def assert_export_slice_matches(ex, st, b: int, kvh: int):
-    """Bit-exact codes, scales and zero points of slice (b, kvh) vs an oracle state."""
+    """Bit-exact codes, scales and zero points of slice (b, kvh) vs an oracle state
+    (the export holds the longest sequence's rows; a shorter slice uses the first)."""
     Lq = st["n_quant"]
-    assert ex["k_codes"].shape[2] == Lq
-    np.testing.assert_array_equal(ex["k_codes"][b, kvh], st["k_codes"])
-    np.testing.assert_array_equal(ex["v_codes"][b, kvh], st["v_codes"])
-    for name in ("k_scale", "k_zero", "v_scale", "v_zero"):
-        got = np.ascontiguousarray(ex[name][b, kvh]).view(np.uint32)
+    G = st["k_group"]
+    assert ex["k_codes"].shape[2] >= Lq
+    np.testing.assert_array_equal(ex["k_codes"][b, kvh, :Lq], st["k_codes"])
+    np.testing.assert_array_equal(ex["v_codes"][b, kvh, :Lq], st["v_codes"])
+    for name, rows in (("k_scale", Lq // G), ("k_zero", Lq // G), ("v_scale", Lq), ("v_zero", Lq)):
+        got = np.ascontiguousarray(ex[name][b, kvh, :rows]).view(np.uint32)
         want = np.ascontiguousarray(st[name]).view(np.uint32)
         np.testing.assert_array_equal(got, want, err_msg=name)
 

@@ -140,6 +140,7 @@ FULL = {
     "long_128k_sink_int2": ([(0, 0), (0, 7)], {0, 3, 4, 7}),
     "llama7b_mha_int4_sym": ([(0, 0), (5, 9)], None),
     "llama7b_mha_int8": ([(0, 0), (7, 30)], None),
+    "llama7b_mha_int4_ragged": ([(0, 0), (4, 9), (7, 31)], None),
 }
 
 

@@ -56,6 +56,7 @@ class Workload:
     k_offset_range: float = 0.0     # per-(kv-head, channel) key mean ~ U(-a, a)
     sink_scale: float = 1.0         # K and V scale of the first n_sink tokens
     codec: int = 0                  # 0 asymmetric min-max groups, 1 symmetric groups
+    prefill_min_frac: float = 1.0   # sequence b prefills prefill * (1 - (1 - f) b / (B - 1)) tokens
 
     @property
     def gqa(self) -> int:
@@ -119,6 +120,15 @@ WORKLOADS: Dict[str, Workload] = {
         bits=4, k_group=128, v_group=128, residual=128, n_sink=0,
         prefill=4096, steps=64, attend_after_prefill=False, seed=1002,
         k_outlier_channels=4, k_outlier_scale=8.0, codec=1),
+    "llama7b_mha_int4_ragged": Workload(
+        name="llama7b_mha_int4_ragged",
+        description="the Llama-7B-shaped MHA decode on sequences of different lengths: B8 H32 "
+                    "D128, contexts 4096 down to 2048 (evenly spaced), bf16, INT4 G128 / G_V128, "
+                    "R128, 64 decode steps",
+        batch=8, n_kv_heads=32, n_q_heads=32, head_dim=128, dtype="bf16",
+        bits=4, k_group=128, v_group=128, residual=128, n_sink=0,
+        prefill=4096, steps=64, attend_after_prefill=False, seed=1002,
+        k_outlier_channels=4, k_outlier_scale=8.0, prefill_min_frac=0.5),
     "llama7b_mha_int8": Workload(
         name="llama7b_mha_int8",
         description="the Llama-7B-shaped MHA decode with INT8 groups (a layer kept at 8 bits "
@@ -137,6 +147,16 @@ ALIASES = {"C1": "tiny", "C2": "llama7b_mha_int4", "C3": "kivi2_long_batch",
 
 def get(name: str) -> Workload:
     return WORKLOADS[ALIASES.get(name, name)]
+
+
+def prefill_lengths(w: Workload) -> list:
+    """Prefill tokens of each sequence: w.prefill for all, or evenly spaced from
+    w.prefill down to w.prefill * w.prefill_min_frac.  Sequence b's prefill is the
+    first prefill_lengths(w)[b] rows of its prefill draw."""
+    if w.prefill_min_frac == 1.0 or w.batch == 1:
+        return [w.prefill] * w.batch
+    return [int(round(w.prefill * (1.0 - (1.0 - w.prefill_min_frac) * b / (w.batch - 1))))
+            for b in range(w.batch)]
 
 
 # --------------------------------------------------------------------------
