@@ -48,7 +48,7 @@ def load(path: str):
     L.orc_quant_group.restype = None
     L.orc_dequant.argtypes = [ctypes.c_uint8, ctypes.c_float, ctypes.c_float]
     L.orc_dequant.restype = ctypes.c_float
-    L.orc_build_slice.argtypes = [i32, i32, i32, i32, i32, i32, i32, P, P, i64] + [P] * 10 + [P]
+    L.orc_build_slice.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, P, P, i64] + [P] * 10 + [P]
     L.orc_build_slice.restype = i32
     L.orc_dequant_slice.argtypes = [i32, i32, i32, i64, i64, i64] + [P] * 12
     L.orc_dequant_slice.restype = None
@@ -114,12 +114,27 @@ def dequant(q, s, z) -> np.ndarray:
 # one slice of the cache
 # ---------------------------------------------------------------------------
 
+def quantized_count(m: int, residual: int, log_window: int = 0) -> int:
+    """Quantized tokens of a slice holding m tokens past its sinks.
+
+    Whole-residual flushes quantize residual tokens each time the residual fills;
+    the log-sparse retention quantizes W of them once 3W are held, then W more
+    after every further W tokens.
+    """
+    if log_window == 0:
+        return residual * (m // residual)
+    return 0 if m < residual else log_window * ((m - residual) // log_window + 1)
+
+
 def build_slice(k_tok, v_tok, *, head_dim: int, bits: int, k_group: int, v_group: int,
-                residual: int, n_sink: int, codec: int = 0) -> Dict[str, np.ndarray]:
+                residual: int, n_sink: int, codec: int = 0, log_window: int = 0) -> Dict[str, np.ndarray]:
     """Append the tokens of one (sequence, kv-head) one at a time; return the state.
 
     k_tok, v_tok: fp32 [n, D] (already rounded to the storage dtype).  codec: 0
-    asymmetric min-max groups, 1 symmetric groups.
+    asymmetric min-max groups, 1 symmetric groups.  log_window W > 0: LogQuant's
+    log-sparse retention with a full-precision part of residual = 3W tokens
+    ("Resumo Técnico: LogQuant", Metodologia item 2); 0: the whole residual is
+    quantized when it reaches residual tokens.
     """
     k_tok = _f32(k_tok)
     v_tok = _f32(v_tok)
@@ -127,7 +142,7 @@ def build_slice(k_tok, v_tok, *, head_dim: int, bits: int, k_group: int, v_group
     assert D == head_dim and v_tok.shape == k_tok.shape
     S, R, G, GV = n_sink, residual, k_group, v_group
     nS = min(n, S)
-    Lq = R * ((n - nS) // R)
+    Lq = quantized_count(n - nS, R, log_window)
     nvg = D // GV
     st = dict(
         sink_k=np.zeros((S, D), np.float32), sink_v=np.zeros((S, D), np.float32),
@@ -137,7 +152,7 @@ def build_slice(k_tok, v_tok, *, head_dim: int, bits: int, k_group: int, v_group
         v_zero=np.zeros((Lq, nvg), np.float32),
         res_k=np.zeros((R, D), np.float32), res_v=np.zeros((R, D), np.float32))
     counts = np.zeros(4, np.int64)
-    rc = lib().orc_build_slice(D, bits, codec, G, GV, R, S, _p(k_tok), _p(v_tok), n,
+    rc = lib().orc_build_slice(D, bits, codec, G, GV, R, S, log_window, _p(k_tok), _p(v_tok), n,
                                _p(st["sink_k"]), _p(st["sink_v"]),
                                _p(st["k_codes"]), _p(st["k_scale"]), _p(st["k_zero"]),
                                _p(st["v_codes"]), _p(st["v_scale"]), _p(st["v_zero"]),
@@ -151,12 +166,12 @@ def build_slice(k_tok, v_tok, *, head_dim: int, bits: int, k_group: int, v_group
     st["res_k"] = st["res_k"][:r_]
     st["res_v"] = st["res_v"][:r_]
     st.update(n_sink=nS_, n_quant=Lq_, n_resid=r_, flushes=fl, head_dim=D, bits=bits,
-              k_group=G, v_group=GV, residual=R, S=S, codec=codec)
+              k_group=G, v_group=GV, residual=R, S=S, codec=codec, log_window=log_window)
     return st
 
 
 def dequant_slice(st) -> tuple:
-    """fp32 K', V' [nS+Lq+r, D] of a slice state in chronological token order."""
+    """fp32 K', V' [nS+Lq+r, D] of a slice state in storage order (sinks, quantized, residual)."""
     D, G, GV = st["head_dim"], st["k_group"], st["v_group"]
     nS, Lq, r = st["n_sink"], st["n_quant"], st["n_resid"]
     T = nS + Lq + r
@@ -237,7 +252,8 @@ def slice_state(w, b: int, kvh: int, n_steps: int):
     """Oracle cache state of slice (b, kvh) after the prefill and n_steps appends."""
     k, v = slice_tokens_f32(w, b, kvh, n_steps)
     return build_slice(k, v, head_dim=w.head_dim, bits=w.bits, k_group=w.k_group,
-                       v_group=w.v_group, residual=w.residual, n_sink=w.n_sink, codec=w.codec)
+                       v_group=w.v_group, residual=w.residual, n_sink=w.n_sink, codec=w.codec,
+                       log_window=w.log_window)
 
 
 def expected_outputs(w, b: int, kvh: int, n_steps: int, qi: int, scale: float | None = None):

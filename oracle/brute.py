@@ -78,11 +78,17 @@ def attention(q, K, V, scale: float):
     return np.array(out), m + math.log(den)
 
 
-def build_slice(k_tok, v_tok, *, bits, k_group, v_group, residual, n_sink, codec=0):
+def build_slice(k_tok, v_tok, *, bits, k_group, v_group, residual, n_sink, codec=0, log_window=0):
     """Token-by-token cache construction, written independently of the C oracle.
 
-    Returns dict with lists: sinks, quantized (dequantized K', V' rows in token
-    order), residual rows, codes and metadata, and the flush count.
+    log_window W > 0: LogQuant's log-sparse retention ("Resumo Técnico: LogQuant",
+    Metodologia item 2).  The full-precision list holds up to residual = 3W
+    tokens; when full, its first 2W entries are split into pairs, the first of
+    each pair is quantized and the second kept, and the last W entries follow.
+
+    Returns dict with lists: sinks, quantized (dequantized K', V' rows in the
+    order they were quantized), residual rows, codes and metadata, and the
+    flush count.
     """
     D = len(k_tok[0])
     sinks_k, sinks_v, res_k, res_v = [], [], [], []
@@ -99,9 +105,17 @@ def build_slice(k_tok, v_tok, *, bits, k_group, v_group, residual, n_sink, codec
         if len(res_k) < residual:
             continue
         flushes += 1
+        if log_window:
+            W = log_window
+            out_k, out_v = res_k[0:2 * W:2], res_v[0:2 * W:2]
+            res_k = res_k[1:2 * W:2] + res_k[2 * W:]
+            res_v = res_v[1:2 * W:2] + res_v[2 * W:]
+        else:
+            out_k, out_v = res_k, res_v
+            res_k, res_v = [], []
         # keys: per channel over each run of k_group tokens
-        for j0 in range(0, residual, k_group):
-            block = res_k[j0:j0 + k_group]
+        for j0 in range(0, len(out_k), k_group):
+            block = out_k[j0:j0 + k_group]
             rows = [[None] * D for _ in block]
             crow = [[0] * D for _ in block]
             meta = []
@@ -115,7 +129,7 @@ def build_slice(k_tok, v_tok, *, bits, k_group, v_group, residual, n_sink, codec
             k_codes.extend(crow)
             k_meta.append(meta)
         # values: per token, per run of v_group channels
-        for row in res_v:
+        for row in out_v:
             out, crow, meta = [], [], []
             for h in range(0, D, v_group):
                 s, z, q = quant_group(row[h:h + v_group], bits, codec)
@@ -125,7 +139,6 @@ def build_slice(k_tok, v_tok, *, bits, k_group, v_group, residual, n_sink, codec
             qv_rows.append(out)
             v_codes.append(crow)
             v_meta.append(meta)
-        res_k, res_v = [], []
     return dict(sinks_k=sinks_k, sinks_v=sinks_v, qk=qk_rows, qv=qv_rows,
                 res_k=res_k, res_v=res_v, k_codes=k_codes, v_codes=v_codes,
                 k_meta=k_meta, v_meta=v_meta, flushes=flushes)

@@ -29,6 +29,12 @@
  *     and appended once it holds R tokens, then emptied
  *       ("LLM系列：KVCache量化1 KIVI: A Tuning-Free Asymmetric 2bit Quantiz",
  *        section 1 "KIVI", key-cache split into grouped part and residual)
+ *   - LogQuant's log-sparse retention (W > 0): the full-precision part holds
+ *     at most 3W tokens; when full, its oldest 2W tokens are thinned to every
+ *     other one, the thinned-out W are quantized, and the newest W stay
+ *       ("Resumo Técnico: LogQuant", Metodologia item 2, window configuration,
+ *        selection scheme, full-precision reserve and dynamic adjustment; item 4:
+ *        quantized and full-precision tokens may be concatenated in any order)
  *   - attention softmax(q K^T / sqrt(d)) V over every cached token
  *       (Int4 KV-cache post, section 3, attention formula; KIVI notes, section 1,
  *        logits as the concatenation of the grouped and residual parts;
@@ -53,6 +59,10 @@
  *   computes to 0 uses max|x| (or 1 when the group is all zeros); the signed
  *   code range [-2^(n-1), 2^(n-1) - 1] is stored offset by 2^(n-1);
  *   the whole residual (R tokens, keys and values) is flushed when it reaches R;
+ *   log-sparse retention: R = 3W; of each pair of the oldest 2W tokens the
+ *   earlier one is quantized and the later one kept, so that the kept tokens
+ *   thin out with their distance from the newest token; the W quantized tokens
+ *   join the quantized part as W/G key groups in their order;
  *   the first S tokens of a sequence stay full precision for good (sinks);
  *   query head h reads kv head h / (Hq / Hkv).
  */
@@ -140,6 +150,7 @@ float orc_dequant(uint8_t q, float s, float z)
 
 typedef struct {
     int D, bits, codec, G, GV, R, S;
+    int W;                                      /* log window; 0: whole-residual flush */
     /* buffers owned by the caller */
     float* sink_k; float* sink_v;               /* [S, D]            */
     uint8_t* k_codes; float* k_scale; float* k_zero;   /* [Lq,D] [Lq/G,D] */
@@ -148,32 +159,70 @@ typedef struct {
     int64_t nS, Lq, r, flushes;
 } orc_slice;
 
-/* Quantize the full residual (R tokens) and append it to the quantized part. */
-static void flush_residual(orc_slice* c)
+/*
+ * Quantize m tokens (bk, bv: [m, D], m a multiple of G) and append them to the
+ * quantized part.
+ */
+static void quantize_block(orc_slice* c, const float* bk, const float* bv, int m)
 {
-    const int D = c->D, G = c->G, GV = c->GV, R = c->R;
+    const int D = c->D, G = c->G, GV = c->GV;
     const int nvg = D / GV;
     /* keys: one group per channel over each run of G tokens */
-    for (int j = 0; j < R / G; ++j) {
+    for (int j = 0; j < m / G; ++j) {
         int64_t grp = c->Lq / G + j;
         for (int ch = 0; ch < D; ++ch) {
-            orc_quant_group(c->res_k + (int64_t)j * G * D + ch, G, D, c->bits, c->codec,
+            orc_quant_group(bk + (int64_t)j * G * D + ch, G, D, c->bits, c->codec,
                             &c->k_scale[grp * D + ch], &c->k_zero[grp * D + ch],
                             c->k_codes + (c->Lq + (int64_t)j * G) * D + ch, D);
         }
     }
     /* values: one group per run of GV channels of each token */
-    for (int t = 0; t < R; ++t) {
+    for (int t = 0; t < m; ++t) {
         int64_t tok = c->Lq + t;
         for (int h = 0; h < nvg; ++h) {
-            orc_quant_group(c->res_v + (int64_t)t * D + (int64_t)h * GV, GV, 1, c->bits, c->codec,
+            orc_quant_group(bv + (int64_t)t * D + (int64_t)h * GV, GV, 1, c->bits, c->codec,
                             &c->v_scale[tok * nvg + h], &c->v_zero[tok * nvg + h],
                             c->v_codes + tok * D + (int64_t)h * GV, 1);
         }
     }
-    c->Lq += R;
+    c->Lq += m;
+}
+
+/* Quantize the full residual (R tokens) and append it to the quantized part. */
+static void flush_residual(orc_slice* c)
+{
+    quantize_block(c, c->res_k, c->res_v, c->R);
     c->r = 0;
     c->flushes += 1;
+}
+
+/*
+ * Log-sparse retention, the full-precision part holding 3W tokens: of the
+ * oldest 2W (slots 0 .. 2W-1) the earlier token of each pair (slots 0, 2, ...)
+ * is quantized and the later one (slots 1, 3, ...) kept; the kept W and then
+ * the newest W (slots 2W .. 3W-1) form the new full-precision part.
+ */
+static void flush_log(orc_slice* c)
+{
+    const int D = c->D, W = c->W;
+    float* bk = (float*)malloc(sizeof(float) * (size_t)W * D);
+    float* bv = (float*)malloc(sizeof(float) * (size_t)W * D);
+    float* keep_k = (float*)malloc(sizeof(float) * (size_t)2 * W * D);
+    float* keep_v = (float*)malloc(sizeof(float) * (size_t)2 * W * D);
+    for (int i = 0; i < W; ++i) {
+        memcpy(bk + (size_t)i * D, c->res_k + (size_t)(2 * i) * D, sizeof(float) * D);
+        memcpy(bv + (size_t)i * D, c->res_v + (size_t)(2 * i) * D, sizeof(float) * D);
+        memcpy(keep_k + (size_t)i * D, c->res_k + (size_t)(2 * i + 1) * D, sizeof(float) * D);
+        memcpy(keep_v + (size_t)i * D, c->res_v + (size_t)(2 * i + 1) * D, sizeof(float) * D);
+    }
+    memcpy(keep_k + (size_t)W * D, c->res_k + (size_t)2 * W * D, sizeof(float) * (size_t)W * D);
+    memcpy(keep_v + (size_t)W * D, c->res_v + (size_t)2 * W * D, sizeof(float) * (size_t)W * D);
+    quantize_block(c, bk, bv, W);
+    memcpy(c->res_k, keep_k, sizeof(float) * (size_t)2 * W * D);
+    memcpy(c->res_v, keep_v, sizeof(float) * (size_t)2 * W * D);
+    c->r = 2 * W;
+    c->flushes += 1;
+    free(bk); free(bv); free(keep_k); free(keep_v);
 }
 
 /* Append one token: sink slot while sinks remain, else residual; flush at R. */
@@ -189,16 +238,22 @@ static void append_token(orc_slice* c, const float* k, const float* v)
     memcpy(c->res_k + c->r * D, k, sizeof(float) * D);
     memcpy(c->res_v + c->r * D, v, sizeof(float) * D);
     c->r += 1;
-    if (c->r == c->R) flush_residual(c);
+    if (c->r == c->R) {
+        if (c->W > 0) flush_log(c);
+        else flush_residual(c);
+    }
 }
 
 /*
  * Build the cache of one slice by appending n tokens (fp32 [n, D] each) one
- * at a time.  counts[0..3] receive nS, Lq, r and the number of flushes.
- * Output buffers must hold the sizes given above for Lq = R*floor((n-S)/R).
+ * at a time.  W = 0 flushes the whole residual at R tokens; W > 0 selects the
+ * log-sparse retention, with R = 3W and W a multiple of G.  counts[0..3]
+ * receive nS, Lq, r and the number of flushes.  Output buffers must hold the
+ * sizes given above for the final Lq: with m = n - S tokens past the sinks,
+ * R*floor(m/R), or with W > 0, 0 for m < R and W*(floor((m-R)/W) + 1) after.
  * Returns 0, or -1 on an invalid configuration.
  */
-int orc_build_slice(int D, int bits, int codec, int G, int GV, int R, int S,
+int orc_build_slice(int D, int bits, int codec, int G, int GV, int R, int S, int W,
                     const float* k_tok, const float* v_tok, int64_t n,
                     float* sink_k, float* sink_v,
                     uint8_t* k_codes, float* k_scale, float* k_zero,
@@ -209,7 +264,8 @@ int orc_build_slice(int D, int bits, int codec, int G, int GV, int R, int S,
     if (bits != 2 && bits != 4 && bits != 8) return -1;
     if (codec != ORC_CODEC_ASYMMETRIC && codec != ORC_CODEC_SYMMETRIC) return -1;
     if (R % G != 0 || D % GV != 0) return -1;
-    orc_slice c = {D, bits, codec, G, GV, R, S, sink_k, sink_v, k_codes, k_scale, k_zero,
+    if (W < 0 || (W > 0 && (R != 3 * W || W % G != 0))) return -1;
+    orc_slice c = {D, bits, codec, G, GV, R, S, W, sink_k, sink_v, k_codes, k_scale, k_zero,
                    v_codes, v_scale, v_zero, res_k, res_v, 0, 0, 0, 0};
     for (int64_t t = 0; t < n; ++t)
         append_token(&c, k_tok + t * D, v_tok + t * D);
@@ -218,8 +274,9 @@ int orc_build_slice(int D, int bits, int codec, int G, int GV, int R, int S,
 }
 
 /*
- * Dequantize one slice into chronological token order: sinks, then the
- * quantized tokens, then the residual.  k_out, v_out: fp32 [nS+Lq+r, D].
+ * Dequantize one slice in storage order: sinks, then the quantized tokens in
+ * the order they were quantized, then the full-precision part (chronological
+ * order when whole residuals are flushed).  k_out, v_out: fp32 [nS+Lq+r, D].
  */
 void orc_dequant_slice(int D, int G, int GV, int64_t nS, int64_t Lq, int64_t r,
                        const float* sink_k, const float* sink_v,

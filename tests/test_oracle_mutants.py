@@ -11,6 +11,7 @@ import pytest
 import oracle
 import tests.test_oracle_cache as tc
 import tests.test_oracle_codec as tq
+import tests.test_oracle_logquant as tl
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "kvq_oracle.c")
 
@@ -39,14 +40,20 @@ MUTANTS = {
         "    memcpy(c->res_k + c->r * D, k, sizeof(float) * D);\n"
         "    memcpy(c->res_v + c->r * D, v, sizeof(float) * D);\n"
         "    c->r += 1;\n"
-        "    if (c->r == c->R) flush_residual(c);",
-        "    if (c->r == c->R) flush_residual(c);\n"
+        "    if (c->r == c->R) {\n"
+        "        if (c->W > 0) flush_log(c);\n"
+        "        else flush_residual(c);\n"
+        "    }",
+        "    if (c->r == c->R) {\n"
+        "        if (c->W > 0) flush_log(c);\n"
+        "        else flush_residual(c);\n"
+        "    }\n"
         "    memcpy(c->res_k + c->r * D, k, sizeof(float) * D);\n"
         "    memcpy(c->res_v + c->r * D, v, sizeof(float) * D);\n"
         "    c->r += 1;"),
     # keys grouped along channels of a token instead of along tokens of a channel
-    "key_groups_transposed": ("orc_quant_group(c->res_k + (int64_t)j * G * D + ch, G, D, c->bits,",
-                              "orc_quant_group(c->res_k + (int64_t)j * G * D + ch, G, 1, c->bits,"),
+    "key_groups_transposed": ("orc_quant_group(bk + (int64_t)j * G * D + ch, G, D, c->bits,",
+                              "orc_quant_group(bk + (int64_t)j * G * D + ch, G, 1, c->bits,"),
     # softmax scale dropped
     "no_softmax_scale": ("sc[j] = dot * scale;", "sc[j] = dot;"),
     # the last token of the cache is left out of the softmax denominator
@@ -61,6 +68,32 @@ MUTANTS = {
     "sym_upper_clamp": ("if (r > zz - 1.0f) r = zz - 1.0f;", "if (r > zz) r = zz;"),
     # symmetric rounding half away from zero
     "sym_half_away": ("float r = rintf(x[i * stride] / ss);", "float r = roundf(x[i * stride] / ss);"),
+    # log-sparse retention: the later token of each pair quantized, the earlier kept
+    "log_keep_earlier": (
+        "        memcpy(bk + (size_t)i * D, c->res_k + (size_t)(2 * i) * D, sizeof(float) * D);\n"
+        "        memcpy(bv + (size_t)i * D, c->res_v + (size_t)(2 * i) * D, sizeof(float) * D);\n"
+        "        memcpy(keep_k + (size_t)i * D, c->res_k + (size_t)(2 * i + 1) * D, sizeof(float) * D);\n"
+        "        memcpy(keep_v + (size_t)i * D, c->res_v + (size_t)(2 * i + 1) * D, sizeof(float) * D);",
+        "        memcpy(bk + (size_t)i * D, c->res_k + (size_t)(2 * i + 1) * D, sizeof(float) * D);\n"
+        "        memcpy(bv + (size_t)i * D, c->res_v + (size_t)(2 * i + 1) * D, sizeof(float) * D);\n"
+        "        memcpy(keep_k + (size_t)i * D, c->res_k + (size_t)(2 * i) * D, sizeof(float) * D);\n"
+        "        memcpy(keep_v + (size_t)i * D, c->res_v + (size_t)(2 * i) * D, sizeof(float) * D);"),
+    # log-sparse retention: the newest keys taken from the wrong window
+    "log_newest_from_middle": (
+        "memcpy(keep_k + (size_t)W * D, c->res_k + (size_t)2 * W * D, sizeof(float) * (size_t)W * D);",
+        "memcpy(keep_k + (size_t)W * D, c->res_k + (size_t)W * D, sizeof(float) * (size_t)W * D);"),
+    # log-sparse retention: only W tokens kept after a flush
+    "log_keep_w": ("    c->r = 2 * W;", "    c->r = W;"),
+    # log-sparse retention: the oldest W quantized as one run (a sliding window, no thinning)
+    "log_no_thinning": (
+        "        memcpy(bk + (size_t)i * D, c->res_k + (size_t)(2 * i) * D, sizeof(float) * D);\n"
+        "        memcpy(bv + (size_t)i * D, c->res_v + (size_t)(2 * i) * D, sizeof(float) * D);\n"
+        "        memcpy(keep_k + (size_t)i * D, c->res_k + (size_t)(2 * i + 1) * D, sizeof(float) * D);\n"
+        "        memcpy(keep_v + (size_t)i * D, c->res_v + (size_t)(2 * i + 1) * D, sizeof(float) * D);",
+        "        memcpy(bk + (size_t)i * D, c->res_k + (size_t)i * D, sizeof(float) * D);\n"
+        "        memcpy(bv + (size_t)i * D, c->res_v + (size_t)i * D, sizeof(float) * D);\n"
+        "        memcpy(keep_k + (size_t)i * D, c->res_k + (size_t)(W + i) * D, sizeof(float) * D);\n"
+        "        memcpy(keep_v + (size_t)i * D, c->res_v + (size_t)(W + i) * D, sizeof(float) * D);"),
     # residual tokens left out of the dequantized token sequence
     "drop_residual": ("memcpy(k_out + (nS + Lq) * D, res_k, sizeof(float) * r * D);",
                       "memset(k_out + (nS + Lq) * D, 0, sizeof(float) * r * D);"),
@@ -85,6 +118,14 @@ def _pins():
              tc.test_attention_closed_form_equal_keys_and_zero_query,
              tc.test_attention_single_token, tc.test_attention_matches_torch_sdpa_float64,
              tc.test_unquantized_cache_is_plain_attention]
+    for case in tl._cases():
+        pins.append(lambda c=case: tl.test_golden_worked_example(c))
+    for args in [(2, 4, 2, 13), (3, 8, 4, 100)]:
+        pins.append(lambda a=args: tl.test_counts_closed_form(*a))
+    for W in (2, 3):
+        pins.append(lambda w=W: tl.test_every_token_once_newest_kept_and_log_sparse_gaps(w))
+    pins.append(lambda: tl.test_matches_brute(2, 0, 0, 4, 2, 8, 37))
+    pins.append(tl.test_before_first_flush_is_plain_attention)
     return pins
 
 

@@ -57,6 +57,7 @@ class Workload:
     sink_scale: float = 1.0         # K and V scale of the first n_sink tokens
     codec: int = 0                  # 0 asymmetric min-max groups, 1 symmetric groups
     prefill_min_frac: float = 1.0   # sequence b prefills prefill * (1 - (1 - f) b / (B - 1)) tokens
+    log_window: int = 0             # W > 0: log-sparse full-precision retention, residual = 3W
 
     @property
     def gqa(self) -> int:
