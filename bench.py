@@ -64,10 +64,13 @@ def algorithmic_bytes(w: wl.Workload, n_sink: int, n_quant: int, n_resid: int) -
 
 
 def slice_counts(w: wl.Workload, n: int):
-    """(sinks, quantized, residual) tokens of a sequence of n tokens."""
+    """(sinks, quantized, residual) tokens of a sequence of n tokens: a flush when
+    the residual holds R tokens quantizes all R, or W = R / 3 under log-sparse
+    retention."""
     nS = min(n, w.n_sink)
-    Lq = w.residual * ((n - nS) // w.residual)
-    return nS, Lq, n - nS - Lq
+    m, R, Q = n - nS, w.residual, w.log_window or w.residual
+    Lq = 0 if m < R else ((m - R) // Q + 1) * Q
+    return nS, Lq, m - Lq
 
 
 def algorithmic_bytes_seqs(w: wl.Workload, lens) -> int:
@@ -308,10 +311,11 @@ def main():
     ragged = len(set(lens0)) > 1
     b0 = algorithmic_bytes_seqs(w, lens0)
     L = args.layers or min(64, max(2, math.ceil(3 * MALL_BYTES / b0)))
-    # by default every layer appends R tokens in the timed region, so the region
-    # holds each layer's residual flush once (its amortised share of the steps)
+    # by default every layer appends as many tokens as separate two flushes (R, or
+    # W under log-sparse retention) in the timed region, so the region holds each
+    # layer's residual flush once (its amortised share of the steps)
     if args.steps is None:
-        args.steps = L * w.residual
+        args.steps = L * (w.log_window or w.residual)
     total_steps = args.warmup + args.steps
     per_layer_steps = (total_steps + L - 1) // L
     max_tokens = w.prefill + per_layer_steps
@@ -326,7 +330,8 @@ def main():
         c = kvq.Cache(batch=w.batch, n_kv_heads=w.n_kv_heads, n_q_heads=w.n_q_heads,
                       head_dim=w.head_dim, bits=w.bits, k_group=w.k_group, v_group=w.v_group,
                       residual=w.residual, n_sink=w.n_sink, dtype=TORCH_DTYPES[w.dtype],
-                      max_tokens=max_tokens, device=dev, codec=w.codec)
+                      max_tokens=max_tokens, device=dev, codec=w.codec,
+                      retention=kvq.KVQ_RETAIN_LOG if w.log_window else kvq.KVQ_RETAIN_WINDOW)
         if args.split_tokens:
             c.set_split_tokens(args.split_tokens)
         if ragged:
@@ -373,12 +378,12 @@ def main():
         i = (s // L) % w.steps
         # cache state before and after this step's append: the schedule fixes it
         n = w.prefill + s // L + 1
-        nS, Lq, r = slice_counts(w, n)
+        _, _, r0 = slice_counts(w, n - 1)
         # The step is one kvq_append_decode call when the token joins the residual
         # without filling it; otherwise (a sink, a flush, or sequences of different
         # lengths) the library appends and decodes in two launches, and the bench
         # makes the same two calls itself so that the events bracket the decode alone.
-        fused = n > w.n_sink and r != 0 and not ragged
+        fused = n > w.n_sink and r0 + 1 < w.residual and not ragged
         plan.append((fused, ctypes.c_void_p(c.handle), ctypes.c_void_p(Ks[i].data_ptr()),
                      ctypes.c_void_p(Vs[i].data_ptr()), ctypes.c_void_p(Q[i % Q.shape[0]].data_ptr()),
                      ctypes.c_void_p(c._ws_ptr), c.ws_bytes))
@@ -459,6 +464,7 @@ def main():
                    "bits": w.bits, "k_group": w.k_group, "v_group": w.v_group,
                    "residual": w.residual, "n_sink": w.n_sink, "storage": w.dtype,
                    "codec": "symmetric" if w.codec else "asymmetric",
+                   **({"retention": "log-sparse", "log_window": w.log_window} if w.log_window else {}),
                    "layers_rotated": L, "parallelism": "single GPU"},
         "tokens_per_s": round(w.batch / (ms_per_step * 1e-3), 1),
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),

@@ -30,6 +30,7 @@ STATUS_NAMES = {0: "KVQ_OK", -1: "KVQ_ERR_INVALID_ARG", -2: "KVQ_ERR_UNSUPPORTED
 
 KVQ_F32, KVQ_BF16, KVQ_F16 = 0, 1, 2
 KVQ_CODEC_ASYMMETRIC, KVQ_CODEC_SYMMETRIC = 0, 1
+KVQ_RETAIN_WINDOW, KVQ_RETAIN_LOG = 0, 1
 
 EXPORTED = ["kvq_cache_bytes", "kvq_cache_create", "kvq_cache_destroy", "kvq_append",
             "kvq_decode_workspace_bytes", "kvq_decode_attention", "kvq_append_decode",
@@ -52,7 +53,7 @@ class Config(ctypes.Structure):
                 ("v_group", ctypes.c_int32), ("residual", ctypes.c_int32),
                 ("n_sink", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("max_tokens", ctypes.c_int64), ("sm_scale", ctypes.c_float),
-                ("codec", ctypes.c_int32)]
+                ("codec", ctypes.c_int32), ("retention", ctypes.c_int32)]
 
 
 _lib = None
@@ -105,9 +106,10 @@ def _check(status: int):
 
 
 def make_config(*, batch, n_kv_heads, n_q_heads, head_dim, bits, k_group, v_group, residual,
-                n_sink=0, dtype=KVQ_BF16, max_tokens, sm_scale=0.0, codec=KVQ_CODEC_ASYMMETRIC) -> Config:
+                n_sink=0, dtype=KVQ_BF16, max_tokens, sm_scale=0.0, codec=KVQ_CODEC_ASYMMETRIC,
+                retention=KVQ_RETAIN_WINDOW) -> Config:
     return Config(batch, n_kv_heads, n_q_heads, head_dim, bits, k_group, v_group, residual,
-                  n_sink, dtype, max_tokens, sm_scale, codec)
+                  n_sink, dtype, max_tokens, sm_scale, codec, retention)
 
 
 def kvq_cache_bytes(cfg: Config) -> int:

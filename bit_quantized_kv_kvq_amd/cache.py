@@ -28,19 +28,22 @@ class Cache:
     token over groups of `v_group` channels, with `bits`-bit asymmetric min-max
     codes; the newest tokens stay in a full-precision residual of `residual`
     tokens and the first `n_sink` tokens stay full precision for good.
+    `retention` = KVQ_RETAIN_LOG selects LogQuant's log-sparse retention
+    (residual = 3W): a flush quantizes every other token of the oldest 2W.
     """
 
     def __init__(self, *, batch: int, n_kv_heads: int, n_q_heads: int, head_dim: int, bits: int,
                  k_group: int, v_group: int, residual: int, max_tokens: int, n_sink: int = 0,
                  dtype: torch.dtype = torch.bfloat16, sm_scale: float = 0.0,
-                 device: Optional[torch.device] = None, codec: int = 0):
+                 device: Optional[torch.device] = None, codec: int = 0, retention: int = 0):
         _k.lib()
         self.device = torch.device(device or "cuda")
         self.dtype = dtype
         self.cfg = _k.make_config(batch=batch, n_kv_heads=n_kv_heads, n_q_heads=n_q_heads,
                                   head_dim=head_dim, bits=bits, k_group=k_group, v_group=v_group,
                                   residual=residual, n_sink=n_sink, dtype=torch_dtype_code(dtype),
-                                  max_tokens=max_tokens, sm_scale=sm_scale, codec=codec)
+                                  max_tokens=max_tokens, sm_scale=sm_scale, codec=codec,
+                                  retention=retention)
         self.nbytes = _k.kvq_cache_bytes(self.cfg)
         # over-allocate by 256 bytes so the handle's buffer is 256-byte aligned
         self._buf = torch.empty(self.nbytes + 256, dtype=torch.uint8, device=self.device)
@@ -148,7 +151,7 @@ class Cache:
         return out, lse
 
     def dequantize(self) -> Tuple[torch.Tensor, torch.Tensor]:
-        """fp32 K', V' [B, Hkv, n_tokens, D] in token order (sinks, quantized, residual)."""
+        """fp32 K', V' [B, Hkv, n_tokens, D] in storage order (sinks, quantized, residual)."""
         c = self.cfg
         T = self.state()[0]
         # zero-filled: rows past a shorter sequence's own length are not written

@@ -127,6 +127,7 @@ hipError_t launch_decode(const Layout& L, const DevPtrs& P, const DecodeRequest&
     a.Hkv = L.Hkv;
     a.S = L.S;
     a.R = L.R;
+    a.Qf = L.Qf;
     a.nS = (int)rq.nS;
     a.nfp = (int)(rq.nS + rq.r);
     a.G = L.G;

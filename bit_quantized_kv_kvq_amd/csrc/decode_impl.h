@@ -68,7 +68,7 @@ struct DecArgs {
     int64_t ng_cap;
     int rec_bytes, rec_kcodes, rec_vcodes, rec_vmeta;
     int dtype;  // storage dtype of q, sinks and residual (DT_*)
-    int Hkv, S, R, nS, nfp, G, GV, nvg, gps, ngroups, nsplit, nsplit_cap;
+    int Hkv, S, R, Qf, nS, nfp, G, GV, nvg, gps, ngroups, nsplit, nsplit_cap;
     float qscale;  // sm_scale * log2(e)
     // Sequences of different lengths: sequence b holds base_len[b] + len_delta
     // tokens, and nS, nfp, ngroups above are replaced by its own; null otherwise.
@@ -745,7 +745,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
     // this slice's sinks, full-precision tokens and key groups
     int nS_s = a.nS, nfp_s = a.nfp, ng_s = a.ngroups;
     if (a.base_len != nullptr) {
-        const SliceState st = slice_state((int64_t)a.base_len[b] + a.len_delta, a.S, a.R);
+        const SliceState st = slice_state((int64_t)a.base_len[b] + a.len_delta, a.S, a.R, a.Qf);
         nS_s = st.nS;
         nfp_s = st.nS + st.r;
         ng_s = st.Lq / a.G;

@@ -64,6 +64,8 @@ kvq_status validate(const kvq_config* c) {
     if (!c) return fail(KVQ_ERR_INVALID_ARG, "config is NULL");
     if (c->codec != KVQ_CODEC_ASYMMETRIC && c->codec != KVQ_CODEC_SYMMETRIC)
         return fail(KVQ_ERR_INVALID_ARG, "codec must be KVQ_CODEC_ASYMMETRIC or KVQ_CODEC_SYMMETRIC");
+    if (c->retention != KVQ_RETAIN_WINDOW && c->retention != KVQ_RETAIN_LOG)
+        return fail(KVQ_ERR_INVALID_ARG, "retention must be KVQ_RETAIN_WINDOW or KVQ_RETAIN_LOG");
     if (c->batch < 1 || c->n_kv_heads < 1 || c->n_q_heads < 1 || c->head_dim < 1)
         return fail(KVQ_ERR_INVALID_ARG, "batch, heads and head_dim must be positive");
     if (c->n_q_heads % c->n_kv_heads != 0)
@@ -77,6 +79,9 @@ kvq_status validate(const kvq_config* c) {
     if (c->head_dim % c->v_group != 0)
         return fail(KVQ_ERR_INVALID_ARG, "head_dim (%d) is not a multiple of v_group (%d)",
                     c->head_dim, c->v_group);
+    if (c->retention == KVQ_RETAIN_LOG && c->residual % (3 * c->k_group) != 0)
+        return fail(KVQ_ERR_INVALID_ARG, "log-sparse retention needs residual = 3W with W a multiple of "
+                    "k_group (residual %d, k_group %d)", c->residual, c->k_group);
     if (c->n_sink < 0) return fail(KVQ_ERR_INVALID_ARG, "n_sink must be >= 0");
     if (c->max_tokens < 1) return fail(KVQ_ERR_INVALID_ARG, "max_tokens must be >= 1");
     if (c->dtype != KVQ_F32 && c->dtype != KVQ_BF16 && c->dtype != KVQ_F16)
@@ -112,9 +117,11 @@ Layout make_layout(const kvq_config* c) {
     L.D = c->head_dim;
     L.bits = c->bits;
     L.codec = c->codec;
+    L.retention = c->retention;
     L.G = c->k_group;
     L.GV = c->v_group;
     L.R = c->residual;
+    L.Qf = c->retention == KVQ_RETAIN_LOG ? c->residual / 3 : c->residual;
     L.S = c->n_sink;
     L.dtype = c->dtype;
     L.esize = c->dtype == KVQ_F32 ? 4 : 2;
@@ -123,8 +130,10 @@ Layout make_layout(const kvq_config* c) {
     L.row_bytes = L.D * L.bits / 8;
     L.BH = (int64_t)L.B * L.Hkv;
     L.max_tokens = c->max_tokens;
-    const int64_t after_sink = std::max<int64_t>(0, c->max_tokens - L.S);
-    L.Lq_cap = (int64_t)L.R * (after_sink / L.R);
+    {   // the quantized tokens of a full sequence (slice_state, in 64-bit)
+        const int64_t m = std::max<int64_t>(0, c->max_tokens - L.S);
+        L.Lq_cap = m < L.R ? 0 : ((m - L.R) / L.Qf + 1) * L.Qf;
+    }
     L.ng_cap = L.Lq_cap / L.G;
     L.rec_kcodes = 8 * L.D;
     L.rec_vcodes = L.rec_kcodes + L.G * L.row_bytes;
@@ -219,6 +228,8 @@ namespace {
 // [bh0, bh0 + nbh), which all hold the state st (updated).  Sinks first, then a
 // partly filled residual (flushed when it reaches R), then whole R-token blocks
 // quantized straight from the input, then the remainder as a new residual.
+// Under log-sparse retention each flush keeps 2W residual tokens, so the input
+// goes through the residual W tokens at a time.
 kvq_status append_slices(kvq_cache* c, const void* k, const void* v, int64_t n_new, int64_t src_tokens,
                          int64_t bh0, int64_t nbh, SliceState& st, hipStream_t s) {
     const Layout& L = c->L;
@@ -235,6 +246,24 @@ kvq_status append_slices(kvq_cache* c, const void* k, const void* v, int64_t n_n
         src += take;
         rem -= take;
     }
+    if (L.Qf != L.R) {
+        while (rem > 0) {
+            const int64_t take = std::min<int64_t>(L.R - st.r, rem);
+            if ((e = check_hip(launch_copy_tokens(L, k, v, src_tokens, src, c->P.kres, c->P.vres, L.R, st.r,
+                                                  take, bh0, nbh, s),
+                               "append")))
+                return e;
+            st.r += (int)take;
+            src += take;
+            rem -= take;
+            if (st.r == L.R) {
+                if ((e = check_hip(launch_flush(L, c->P, st.Lq, bh0, nbh, s), "flush"))) return e;
+                st.Lq += L.Qf;
+                st.r = L.R - L.Qf;
+            }
+        }
+        return KVQ_OK;
+    }
     // 2. top up a partly filled residual; flush it when it reaches R
     if (rem > 0 && st.r > 0) {
         const int64_t take = std::min<int64_t>(L.R - st.r, rem);
@@ -246,9 +275,7 @@ kvq_status append_slices(kvq_cache* c, const void* k, const void* v, int64_t n_n
         src += take;
         rem -= take;
         if (st.r == L.R) {
-            if ((e = check_hip(launch_quantize(L, c->P, c->P.kres, c->P.vres, L.R, 0, L.R / L.G, st.Lq, bh0, nbh, s),
-                               "flush")))
-                return e;
+            if ((e = check_hip(launch_flush(L, c->P, st.Lq, bh0, nbh, s), "flush"))) return e;
             st.Lq += L.R;
             st.r = 0;
         }
@@ -282,7 +309,7 @@ int64_t max_len(const kvq_cache* c) { return *std::max_element(c->len.begin(), c
 kvq_status settle(kvq_cache* c, bool write_lengths, hipStream_t s) {
     const int64_t mx = max_len(c);
     const bool equal = *std::min_element(c->len.begin(), c->len.end()) == mx;
-    const SliceState st = slice_state(mx, c->L.S, c->L.R);
+    const SliceState st = slice_state(mx, c->L.S, c->L.R, c->L.Qf);
     c->nS = st.nS, c->Lq = st.Lq, c->r = st.r;
     if (equal) {
         c->ragged = false;
@@ -328,11 +355,9 @@ kvq_status kvq_append(kvq_cache* c, const void* k, const void* v, int64_t n_new,
                             "append")))
             return st;
         for (int b = 0; b < L.B; ++b) {
-            const SliceState ss = slice_state(c->len[b], L.S, L.R);
+            const SliceState ss = slice_state(c->len[b], L.S, L.R, L.Qf);
             if (c->len[b] >= L.S && ss.r + 1 == L.R) {
-                if ((st = check_hip(launch_quantize(L, c->P, c->P.kres, c->P.vres, L.R, 0, L.R / L.G, ss.Lq,
-                                                    (int64_t)b * L.Hkv, L.Hkv, s),
-                                    "flush")))
+                if ((st = check_hip(launch_flush(L, c->P, ss.Lq, (int64_t)b * L.Hkv, L.Hkv, s), "flush")))
                     return st;
             }
             c->len[b] += 1;
@@ -342,7 +367,7 @@ kvq_status kvq_append(kvq_cache* c, const void* k, const void* v, int64_t n_new,
     }
     // several tokens: sequence by sequence
     for (int b = 0; b < L.B; ++b) {
-        SliceState ss = slice_state(c->len[b], L.S, L.R);
+        SliceState ss = slice_state(c->len[b], L.S, L.R, L.Qf);
         if ((st = append_slices(c, k, v, n_new, n_new, (int64_t)b * L.Hkv, L.Hkv, ss, s)) != KVQ_OK) return st;
         c->len[b] += n_new;
     }
@@ -371,7 +396,7 @@ kvq_status kvq_append_ragged(kvq_cache* c, const void* k, const void* v, const i
     kvq_status st;
     for (int b = 0; b < L.B; ++b) {
         if (n_new[b] == 0) continue;
-        SliceState ss = slice_state(c->len[b], L.S, L.R);
+        SliceState ss = slice_state(c->len[b], L.S, L.R, L.Qf);
         if ((st = append_slices(c, k, v, n_new[b], n_max, (int64_t)b * L.Hkv, L.Hkv, ss, s)) != KVQ_OK) return st;
         c->len[b] += n_new[b];
     }

@@ -36,6 +36,8 @@ constexpr int kMaxCombine = 1024;      // max (splits x query heads per kv head)
 // ---------------------------------------------------------------------------
 struct Layout {
     int B, Hkv, Hq, D, bits, codec, G, GV, R, S, dtype, esize, gqa, nvg, row_bytes;
+    int retention;  // kvq_retention
+    int Qf;         // tokens quantized per flush: R, or W = R / 3 under log-sparse retention
     int64_t BH, max_tokens, Lq_cap, ng_cap;
     int rec_bytes, rec_kcodes, rec_vcodes, rec_vmeta;
     size_t off_ksink, off_vsink, off_kres, off_vres, off_rec, off_lens, total;
@@ -51,16 +53,18 @@ struct Ragged {
 };
 
 // Sinks held, quantized tokens and residual tokens of a sequence of n tokens:
-// the first S tokens are sinks, then whole runs of R tokens are quantized and
-// fewer than R stay in the residual.
+// the first S tokens are sinks; the residual flushes when it holds R tokens,
+// quantizing Q of them and keeping R - Q.  Whole-residual flushes (Q = R)
+// quantize every run of R tokens; log-sparse retention (Q = R / 3) quantizes Q
+// tokens once R are held and Q more after every further Q tokens.
 struct SliceState {
     int nS, Lq, r;
 };
-__host__ __device__ inline SliceState slice_state(int64_t n, int S, int R) {
+__host__ __device__ inline SliceState slice_state(int64_t n, int S, int R, int Q) {
     const int64_t nS = n < S ? n : S;
-    const int64_t q = n - nS;
-    const int64_t Lq = (q / R) * R;
-    return {(int)nS, (int)Lq, (int)(q - Lq)};
+    const int64_t m = n - nS;
+    const int64_t Lq = m < R ? 0 : ((m - R) / Q + 1) * Q;
+    return {(int)nS, (int)Lq, (int)(m - Lq)};
 }
 
 struct DevPtrs {
@@ -121,12 +125,19 @@ hipError_t launch_copy_tokens(const Layout& L, const void* src_k, const void* sr
                               int64_t dst_tokens, int64_t dst_tok0, int64_t n, int64_t bh0, int64_t nbh,
                               hipStream_t stream);
 
-// Quantize n_groups consecutive key groups (n_groups * G tokens) of slices
-// [bh0, bh0 + nbh), read from src_k/src_v[bh][src_tok0 + t][D] (src_tokens tokens
-// per slice), into quantized token positions dst_tok0 + t.
+// Quantize n_groups key groups (n_groups * G tokens) of slices [bh0, bh0 + nbh),
+// token t read from src_k/src_v[bh][src_tok0 + t * tok_stride][D] (src_tokens
+// rows per slice), into quantized token positions dst_tok0 + t.
 hipError_t launch_quantize(const Layout& L, const DevPtrs& P, const void* src_k, const void* src_v,
                            int64_t src_tokens, int64_t src_tok0, int64_t n_groups, int64_t dst_tok0,
-                           int64_t bh0, int64_t nbh, hipStream_t stream);
+                           int64_t bh0, int64_t nbh, hipStream_t stream, int tok_stride = 1);
+
+// Flush the full residual (R tokens) of slices [bh0, bh0 + nbh) whose quantized
+// part holds Lq tokens: quantize all R (Qf == R), or, under log-sparse retention,
+// quantize rows 0, 2, ..., 2W - 2 (W = Qf) and compact the rest to rows
+// 0 .. 2W - 1.  Leaves Lq + Qf quantized tokens and R - Qf residual tokens.
+hipError_t launch_flush(const Layout& L, const DevPtrs& P, int64_t Lq, int64_t bh0, int64_t nbh,
+                        hipStream_t stream);
 
 // One token per sequence (src_*[bh][D]) into each slice's own sink slot or residual
 // row, from the sequence's length before the append (rg).

@@ -10,6 +10,10 @@
 // replaced by |min| (1 when min == 0); a zero point of -0 is stored as +0.
 // Grouping (KIVI notes, "LLM系列：KVCache量化1 KIVI…", section 1): keys per channel
 // over each run of G tokens, values per token over each run of G_V channels.
+// Flushes: the whole residual when it reaches R tokens (KIVI notes, section 1),
+// or, under log-sparse retention ("Resumo Técnico: LogQuant", Metodologia
+// item 2), the earlier token of each pair among the oldest 2W of a residual of
+// R = 3W tokens, the later ones and the newest W staying at full precision.
 #include <algorithm>
 
 #include "kvq_internal.h"
@@ -85,7 +89,8 @@ __global__ __launch_bounds__(256) void copy_one_ragged_kernel(const uint4* __res
                                                               uint4* __restrict__ ksink, uint4* __restrict__ vsink,
                                                               uint4* __restrict__ kres, uint4* __restrict__ vres,
                                                               const int* __restrict__ base_len, int delta,
-                                                              int Hkv, int S, int R, int row_vec, int64_t total) {
+                                                              int Hkv, int S, int R, int Qf, int row_vec,
+                                                              int64_t total) {
     // total = BH * row_vec vectors of K, then as many of V
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < 2 * total;
          i += (int64_t)gridDim.x * blockDim.x) {
@@ -94,11 +99,41 @@ __global__ __launch_bounds__(256) void copy_one_ragged_kernel(const uint4* __res
         const int64_t v = j % row_vec;
         const int64_t bh = j / row_vec;
         const int64_t n = (int64_t)base_len[bh / Hkv] + delta;
-        const SliceState st = slice_state(n, S, R);
+        const SliceState st = slice_state(n, S, R, Qf);
         uint4* dst;
         if (n < S) dst = (is_v ? vsink : ksink) + (bh * S + n) * row_vec + v;
         else dst = (is_v ? vres : kres) + (bh * R + st.r) * row_vec + v;
         *dst = (is_v ? src_v : src_k)[bh * row_vec + v];
+    }
+}
+
+// Log-sparse retention, after the flush has quantized residual rows 0, 2, ...,
+// 2W - 2: rows 1, 3, ..., 2W - 1 move to rows 0 .. W - 1 and rows 2W .. 3W - 1
+// to rows W .. 2W - 1, in place.  Row i takes row 2i + 1 (i < W) or i + W
+// (i >= W), always a row above i, so a thread that moves one 16-byte column of
+// a slice in increasing i never reads a row it has already overwritten; loading
+// a run of kRun source rows before storing them is safe for the same reason
+// (rows written by earlier runs lie below the run).
+constexpr int kRun = 8;
+__global__ __launch_bounds__(256) void log_compact_kernel(uint4* kres, uint4* vres, int R, int W, int row_vec,
+                                                          int64_t bh0, int64_t total) {
+    // total = nbh * row_vec columns of K, then as many of V
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < 2 * total;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const bool is_v = i >= total;
+        const int64_t j = is_v ? i - total : i;
+        const int64_t bh = bh0 + j / row_vec;
+        uint4* col = (is_v ? vres : kres) + bh * R * row_vec + j % row_vec;
+        for (int i0 = 0; i0 < 2 * W; i0 += kRun) {
+            uint4 x[kRun];
+#pragma unroll
+            for (int u = 0; u < kRun; ++u) {
+                const int r = i0 + u;
+                x[u] = col[(int64_t)(r < W ? 2 * r + 1 : r + W) * row_vec];
+            }
+#pragma unroll
+            for (int u = 0; u < kRun; ++u) col[(int64_t)(i0 + u) * row_vec] = x[u];
+        }
     }
 }
 
@@ -120,6 +155,7 @@ struct QuantArgs {
     const void* src_k;
     const void* src_v;
     int64_t src_tokens, src_tok0, dst_tok0;
+    int tok_stride;  // source rows between consecutive tokens (2: every other row)
     int D, G, GV, nvg, row_bytes;
     int64_t ng_cap;
     int rec_bytes, rec_kcodes, rec_vcodes, rec_vmeta;
@@ -211,7 +247,8 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
     const int D = a.D, G = a.G, tid = threadIdx.x;
     uint8_t* s_codes = smem;                                               // [G][D]
     float* s_mm = reinterpret_cast<float*>(smem + (((size_t)G * D + 15) & ~(size_t)15));  // [P][D][2]
-    const int64_t src_row0 = bh * a.src_tokens + a.src_tok0 + (int64_t)grp * G;
+    const int ts = a.tok_stride;
+    const int64_t src_row0 = bh * a.src_tokens + a.src_tok0 + (int64_t)grp * G * ts;
     const int64_t dst_grp = a.dst_tok0 / G + grp;
     uint8_t* rec = a.rec + rec_offset(bh, dst_grp, a.ng_cap, a.rec_bytes);
     float* kmeta = reinterpret_cast<float*>(rec);
@@ -222,12 +259,13 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
         const int P = 256 / CH;          // token parts (4 for D = 128, 8 for D = 64)
         const int GP = G / P;            // tokens per thread
         const int cp = tid % CH, part = tid / CH, c = 2 * cp;
-        const int64_t e0 = (src_row0 + (int64_t)part * GP) * D + c;
+        const int64_t e0 = (src_row0 + (int64_t)part * GP * ts) * D + c;
+        const int64_t sD = (int64_t)ts * D;
         float mn0 = INFINITY, mn1 = INFINITY, mx0 = -INFINITY, mx1 = -INFINITY;
 #pragma unroll 8
         for (int t = 0; t < GP; ++t) {
             float x0, x1;
-            load2_f32<DT>(a.src_k, e0 + (int64_t)t * D, x0, x1);
+            load2_f32<DT>(a.src_k, e0 + t * sD, x0, x1);
             mn0 = fminf(mn0, x0), mx0 = fmaxf(mx0, x0);
             mn1 = fminf(mn1, x1), mx1 = fmaxf(mx1, x1);
         }
@@ -244,7 +282,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
 #pragma unroll 8
         for (int t = 0; t < GP; ++t) {
             float x0, x1;
-            load2_f32<DT>(a.src_k, e0 + (int64_t)t * D, x0, x1);
+            load2_f32<DT>(a.src_k, e0 + t * sD, x0, x1);
             const uint32_t q0 = group_code(x0, p0, qmax), q1 = group_code(x1, p1, qmax);
             *reinterpret_cast<uint16_t*>(s_codes + (part * GP + t) * D + c) = (uint16_t)(q0 | (q1 << 8));
         }
@@ -269,7 +307,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
             const int i = (i0 + tid) / tpi, sub = (i0 + tid) % tpi;
             const bool live = i < items;
             const int t = live ? i / nvg : 0, h = live ? i % nvg : 0;
-            const int64_t e0 = (src_row0 + t) * D + (int64_t)h * GV + sub * cpt;
+            const int64_t e0 = (src_row0 + (int64_t)t * ts) * D + (int64_t)h * GV + sub * cpt;
             float mn = INFINITY, mx = -INFINITY;
             for (int j = 0; j < cpt; j += 8) {
                 float f[8];
@@ -317,7 +355,7 @@ struct DeqArgs {
     float* kout;
     float* vout;
     int64_t nS, Lq, r, T, ng_cap;  // the slices' state; with base_len, the longest sequence's
-    int S, R, D, G, GV, nvg, bits, row_bytes;
+    int S, R, Qf, D, G, GV, nvg, bits, row_bytes;
     int rec_bytes, rec_kcodes, rec_vcodes, rec_vmeta;
     const int* base_len;  // sequences of different lengths (see Ragged), or null
     int delta;
@@ -328,7 +366,7 @@ struct DeqArgs {
 __device__ inline void deq_slice(const DeqArgs& a, int64_t bh, int64_t& nS, int64_t& Lq, int64_t& r) {
     nS = a.nS, Lq = a.Lq, r = a.r;
     if (a.base_len != nullptr) {
-        const SliceState st = slice_state((int64_t)a.base_len[bh / a.Hkv] + a.delta, a.S, a.R);
+        const SliceState st = slice_state((int64_t)a.base_len[bh / a.Hkv] + a.delta, a.S, a.R, a.Qf);
         nS = st.nS, Lq = st.Lq, r = st.r;
     }
 }
@@ -438,6 +476,7 @@ DeqArgs make_deq_args(const Layout& L, const DevPtrs& P, int64_t nS, int64_t Lq,
     a.ng_cap = L.ng_cap;
     a.S = L.S;
     a.R = L.R;
+    a.Qf = L.Qf;
     a.D = L.D;
     a.G = L.G;
     a.GV = L.GV;
@@ -483,7 +522,7 @@ hipError_t launch_copy_one_ragged(const Layout& L, const DevPtrs& P, const void*
     copy_one_ragged_kernel<<<grid, 256, 0, stream>>>(
         reinterpret_cast<const uint4*>(src_k), reinterpret_cast<const uint4*>(src_v),
         reinterpret_cast<uint4*>(P.ksink), reinterpret_cast<uint4*>(P.vsink), reinterpret_cast<uint4*>(P.kres),
-        reinterpret_cast<uint4*>(P.vres), rg.base_len, rg.delta, L.Hkv, L.S, L.R, row_vec, total);
+        reinterpret_cast<uint4*>(P.vres), rg.base_len, rg.delta, L.Hkv, L.S, L.R, L.Qf, row_vec, total);
     return hipGetLastError();
 }
 
@@ -501,7 +540,7 @@ hipError_t launch_set_lengths(const Layout& L, int* base_len, const int64_t* len
 
 hipError_t launch_quantize(const Layout& L, const DevPtrs& P, const void* src_k, const void* src_v,
                            int64_t src_tokens, int64_t src_tok0, int64_t n_groups, int64_t dst_tok0,
-                           int64_t bh0, int64_t nbh, hipStream_t stream) {
+                           int64_t bh0, int64_t nbh, hipStream_t stream, int tok_stride) {
     if (n_groups <= 0 || nbh <= 0) return hipSuccess;
     QuantArgs a;
     a.src_k = src_k;
@@ -509,6 +548,7 @@ hipError_t launch_quantize(const Layout& L, const DevPtrs& P, const void* src_k,
     a.src_tokens = src_tokens;
     a.src_tok0 = src_tok0;
     a.dst_tok0 = dst_tok0;
+    a.tok_stride = tok_stride;
     a.D = L.D;
     a.G = L.G;
     a.GV = L.GV;
@@ -540,6 +580,20 @@ hipError_t launch_quantize(const Layout& L, const DevPtrs& P, const void* src_k,
         else KVQ_QLAUNCH(DT_F16, 8);
     }
 #undef KVQ_QLAUNCH
+    return hipGetLastError();
+}
+
+hipError_t launch_flush(const Layout& L, const DevPtrs& P, int64_t Lq, int64_t bh0, int64_t nbh, hipStream_t stream) {
+    if (L.Qf == L.R)
+        return launch_quantize(L, P, P.kres, P.vres, L.R, 0, L.R / L.G, Lq, bh0, nbh, stream, 1);
+    const int W = L.Qf;
+    hipError_t e = launch_quantize(L, P, P.kres, P.vres, L.R, 0, W / L.G, Lq, bh0, nbh, stream, 2);
+    if (e != hipSuccess || nbh <= 0) return e;
+    const int row_vec = L.D * L.esize / 16;
+    const int64_t total = nbh * row_vec;
+    const int grid = grid_for(2 * total, 256, 65535);
+    log_compact_kernel<<<grid, 256, 0, stream>>>(reinterpret_cast<uint4*>(P.kres), reinterpret_cast<uint4*>(P.vres),
+                                                 L.R, W, row_vec, bh0, total);
     return hipGetLastError();
 }
 

@@ -7,7 +7,8 @@
  *   - values are quantized per token, one group per G_V consecutive channels;
  *   - the newest tokens sit in a full-precision residual of capacity R; when it
  *     holds R tokens they are quantized, appended to the quantized part, and the
- *     residual is emptied;
+ *     residual is emptied (or, under LogQuant's log-sparse retention, a thinned
+ *     half of its oldest two thirds is quantized: see kvq_retention);
  *   - optionally the first S tokens of every sequence stay full precision for
  *     good ("attention sinks", "KV Cache的Int4量化：如何解决Attention Sink导致的量化精度
  *     崩塌问题", section 3).
@@ -84,6 +85,26 @@ typedef enum kvq_codec {
     KVQ_CODEC_SYMMETRIC = 1
 } kvq_codec;
 
+/*
+ * Which tokens a flush quantizes when the full-precision residual reaches R
+ * tokens:
+ *   WINDOW: all R, leaving the residual empty (KIVI notes, "LLM系列：KVCache量化1
+ *           KIVI…", section 1).
+ *   LOG:    log-sparse retention ("Resumo Técnico: LogQuant", Metodologia
+ *           item 2) with R = 3W, W a multiple of k_group: of the oldest 2W
+ *           residual tokens, taken in pairs, the earlier of each pair is
+ *           quantized (W tokens, W / G key groups, in their order) and the later
+ *           kept; the kept W and the newest W remain, so 2W <= r < 3W after the
+ *           first flush.  The kept tokens thin out with their distance from the
+ *           newest token.  Attention does not depend on where a token is stored
+ *           (same page, item 4), so quantized and kept tokens are stored in the
+ *           order they were quantized or kept, not by position.
+ */
+typedef enum kvq_retention {
+    KVQ_RETAIN_WINDOW = 0,
+    KVQ_RETAIN_LOG = 1
+} kvq_retention;
+
 typedef struct kvq_config {
     int32_t batch;        /* B  >= 1                                              */
     int32_t n_kv_heads;   /* Hkv >= 1                                             */
@@ -101,6 +122,7 @@ typedef struct kvq_config {
     int64_t max_tokens;   /* capacity per sequence, >= 1                          */
     float sm_scale;       /* softmax scale; 0 selects 1/sqrt(D)                   */
     int32_t codec;        /* kvq_codec of the key and value groups (0: asymmetric) */
+    int32_t retention;    /* kvq_retention of the residual flush (0: window)      */
 } kvq_config;
 
 typedef struct kvq_cache kvq_cache; /* opaque host-side handle */
@@ -117,7 +139,8 @@ kvq_status kvq_cache_bytes(const kvq_config* cfg, size_t* bytes);
  * from kvq_cache_bytes, 256-byte aligned).  The buffer's contents need no
  * initialisation.  *out receives the handle, to be freed with
  * kvq_cache_destroy.  Errors: INVALID_ARG (null pointer, non-positive sizes,
- * Hq % Hkv != 0, R % G != 0, D % G_V != 0, codec not a kvq_codec, misaligned buffer),
+ * Hq % Hkv != 0, R % G != 0, D % G_V != 0, codec not a kvq_codec, retention not a
+ * kvq_retention, log-sparse retention with R not a multiple of 3G, misaligned buffer),
  * UNSUPPORTED (bits not 2/4/8, D not 64/128, Hq/Hkv not 1/2/4/8, G not in
  * {32, 64, 128, 256}, G_V not a multiple of 16, 8-bit codes with G or G_V
  * below 64, B * Hkv > 65535, more than
@@ -139,7 +162,9 @@ kvq_status kvq_cache_destroy(kvq_cache* cache);
  * tokens are quantized (keys per channel over each run of G tokens, values per
  * token over each run of G_V channels) and the residual is emptied, so that
  * 0 <= r < R after every call.  Complete R-token blocks of a bulk append are
- * quantized straight from the input.  Each sequence follows this from its own
+ * quantized straight from the input.  Under log-sparse retention a flush
+ * quantizes W of the R tokens instead and keeps 2W (kvq_retention), and a bulk
+ * append passes through the residual.  Each sequence follows this from its own
  * length when the sequences differ in length (see kvq_append_ragged).
  *   k, v : device, [B, Hkv, n_new, D] contiguous, in cfg.dtype.
  * n_new == 0 is a no-op.  Errors: INVALID_ARG (null, n_new < 0),
@@ -196,8 +221,9 @@ kvq_status kvq_append_decode(kvq_cache* cache, const void* k, const void* v, con
                              float* out, float* lse, void* ws, size_t ws_bytes, void* stream);
 
 /*
- * Dequantize the whole cache to fp32 in chronological token order (sinks, then
- * the quantized tokens as x' = (q - z) * s, then the residual); the round trip
+ * Dequantize the whole cache to fp32 in storage order (sinks, then the quantized
+ * tokens as x' = (q - z) * s in the order they were quantized, then the
+ * residual; chronological order under window retention); the round trip
  * of the Int4 KV-cache post's section 5.1 `quantize` helper.
  *   k_out, v_out : device, [B, Hkv, n_tokens, D] fp32 (n_tokens of
  *                  kvq_cache_state; rows past a shorter sequence's own length

@@ -37,7 +37,8 @@ def make_cache(w: wl.Workload, max_tokens: int | None = None, **over):
     kw = dict(batch=w.batch, n_kv_heads=w.n_kv_heads, n_q_heads=w.n_q_heads,
               head_dim=w.head_dim, bits=w.bits, k_group=w.k_group, v_group=w.v_group,
               residual=w.residual, n_sink=w.n_sink, dtype=TORCH_DTYPES[w.dtype],
-              max_tokens=max_tokens or w.max_tokens, device=torch.device("cuda:0"), codec=w.codec)
+              max_tokens=max_tokens or w.max_tokens, device=torch.device("cuda:0"), codec=w.codec,
+              retention=1 if w.log_window else 0)
     kw.update(over)
     return Cache(**kw)
 

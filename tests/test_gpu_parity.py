@@ -31,6 +31,8 @@ SMALL = {
                                                         n_q_heads=3, prefill=1000, steps=30),
     "int8_small": wl.get("llama7b_mha_int8").replace(name="int8_small", batch=2, n_kv_heads=3,
                                                      n_q_heads=6, prefill=1000, steps=30),
+    "logquant_small": wl.get("logquant_gqa_int2").replace(name="logquant_small", batch=2, n_kv_heads=2,
+                                                          n_q_heads=8, prefill=1000, steps=100),
 }
 
 
@@ -47,6 +49,7 @@ def test_small_workload_all_slices_every_step(name):
             assert_export_slice_matches(ex, oracle.slice_state(w, b, h, 0), b, h)
     worst = [0.0]
     flush_checked = []
+    last_Lq = [run.cache.state()[2]]
 
     def on_attend(n_steps, qi, out, lse):
         torch.cuda.synchronize()
@@ -54,11 +57,12 @@ def test_small_workload_all_slices_every_step(name):
         n_tok, nS, Lq, r = run.cache.state()
         N = w.prefill + n_steps
         assert nS == min(N, w.n_sink)
-        assert Lq == w.residual * ((N - nS) // w.residual) and r == (N - nS) % w.residual
+        assert Lq == oracle.quantized_count(N - nS, w.residual, w.log_window) and r == N - nS - Lq
         for b in range(w.batch):
             for h in range(w.n_kv_heads):
                 worst[0] = max(worst[0], check_outputs(w, o, l, b, h, n_steps, qi))
-        if n_steps > 0 and r == 0 and n_steps not in flush_checked:
+        flushed, last_Lq[0] = Lq != last_Lq[0], Lq
+        if n_steps > 0 and flushed and n_steps not in flush_checked:
             flush_checked.append(n_steps)
             exf = export_cpu(run.cache)
             for b in range(w.batch):
@@ -141,6 +145,7 @@ FULL = {
     "llama7b_mha_int4_sym": ([(0, 0), (5, 9)], None),
     "llama7b_mha_int8": ([(0, 0), (7, 30)], None),
     "llama7b_mha_int4_ragged": ([(0, 0), (4, 9), (7, 31)], None),
+    "logquant_gqa_int2": ([(0, 0), (6, 5)], None),
 }
 
 

@@ -42,7 +42,12 @@ def _expected_bytes(c):
     e = 4 if c.dtype == kvq.KVQ_F32 else 2
     BH = c.batch * c.n_kv_heads
     D, G = c.head_dim, c.k_group
-    Lq_cap = c.residual * (max(0, c.max_tokens - c.n_sink) // c.residual)
+    m = max(0, c.max_tokens - c.n_sink)
+    if c.retention == kvq.KVQ_RETAIN_LOG:  # W quantized per flush, the first once 3W are held
+        W = c.residual // 3
+        Lq_cap = 0 if m < c.residual else W * ((m - c.residual) // W + 1)
+    else:
+        Lq_cap = c.residual * (m // c.residual)
     row = D * c.bits // 8
     rec = al(8 * D + 2 * G * row + G * (D // c.v_group) * 8)
     parts = [BH * c.n_sink * D * e] * 2 + [BH * c.residual * D * e] * 2 + [BH * (Lq_cap // G) * rec, 4 * c.batch]
@@ -52,7 +57,11 @@ def _expected_bytes(c):
 @pytest.mark.parametrize("kw", [{}, dict(bits=2), dict(dtype=kvq.KVQ_F32, head_dim=64, v_group=64),
                                 dict(n_sink=0, max_tokens=129), dict(max_tokens=3),
                                 dict(n_q_heads=32, n_kv_heads=4), dict(bits=8, v_group=64),
-                                dict(bits=8, n_q_heads=4, k_group=128, v_group=128)])
+                                dict(bits=8, n_q_heads=4, k_group=128, v_group=128),
+                                dict(retention=kvq.KVQ_RETAIN_LOG, residual=192),
+                                dict(retention=kvq.KVQ_RETAIN_LOG, residual=192, max_tokens=195),
+                                dict(retention=kvq.KVQ_RETAIN_LOG, residual=192, max_tokens=196),
+                                dict(retention=kvq.KVQ_RETAIN_LOG, k_group=32, residual=96, n_sink=0)])
 def test_cache_bytes_matches_layout(kw):
     c = _cfg(**kw)
     assert kvq.kvq_cache_bytes(c) == _expected_bytes(c)
@@ -79,6 +88,10 @@ def test_cache_bytes_matches_layout(kw):
     (dict(dtype=7), kvq.KVQ_ERR_INVALID_ARG),
     (dict(sm_scale=-1.0), kvq.KVQ_ERR_INVALID_ARG),
     (dict(sm_scale=float("nan")), kvq.KVQ_ERR_INVALID_ARG),
+    (dict(retention=2), kvq.KVQ_ERR_INVALID_ARG),
+    (dict(retention=-1), kvq.KVQ_ERR_INVALID_ARG),
+    (dict(retention=kvq.KVQ_RETAIN_LOG), kvq.KVQ_ERR_INVALID_ARG),               # R = 128 is not 3W
+    (dict(retention=kvq.KVQ_RETAIN_LOG, residual=256, k_group=128), kvq.KVQ_ERR_INVALID_ARG),  # 3G does not divide R
 ])
 def test_invalid_configs_are_rejected(kw, status):
     with pytest.raises(kvq.KVQError) as ei:
@@ -126,5 +139,6 @@ def test_workload_configs_are_supported():
                             head_dim=w.head_dim, bits=w.bits, k_group=w.k_group,
                             v_group=w.v_group, residual=w.residual, n_sink=w.n_sink,
                             dtype={"f32": 0, "bf16": 1, "f16": 2}[w.dtype],
-                            max_tokens=w.max_tokens)
+                            max_tokens=w.max_tokens, codec=w.codec,
+                            retention=kvq.KVQ_RETAIN_LOG if w.log_window else kvq.KVQ_RETAIN_WINDOW)
         assert kvq.kvq_cache_bytes(c) > 0

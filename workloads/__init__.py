@@ -139,6 +139,15 @@ WORKLOADS: Dict[str, Workload] = {
         bits=8, k_group=128, v_group=128, residual=128, n_sink=0,
         prefill=4096, steps=64, attend_after_prefill=False, seed=1002,
         k_outlier_channels=4, k_outlier_scale=8.0),
+    "logquant_gqa_int2": Workload(
+        name="logquant_gqa_int2",
+        description="Llama-3.1-8B-shaped GQA decode with LogQuant's log-sparse retention: B8, "
+                    "32 query / 8 KV heads, D128, context 32768, bf16, INT2 G64 / G_V64, "
+                    "full-precision reserve 3W = 192 tokens (W = 64), 64 decode steps",
+        batch=8, n_kv_heads=8, n_q_heads=32, head_dim=128, dtype="bf16",
+        bits=2, k_group=64, v_group=64, residual=192, n_sink=0,
+        prefill=32768, steps=64, attend_after_prefill=False, seed=1006,
+        k_outlier_channels=4, k_outlier_scale=8.0, log_window=64),
 }
 
 # short aliases in the order the workloads are listed
