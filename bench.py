@@ -325,19 +325,28 @@ def main():
     Kp, Vp = wl.prefill_batch(w)
     Kd, Vd = to_torch(Kp, w.dtype, dev), to_torch(Vp, w.dtype, dev)
     del Kp, Vp
+    # paged records: a pool of exactly the pages the sequences reach in the run
+    pool_pages = 0
+    if w.page_groups:
+        pool_pages = sum(-(-(slice_counts(w, n0 + per_layer_steps)[1] // w.k_group) // w.page_groups)
+                         for n0 in lens0)
+    rounds = wl.prefill_rounds(w)
     caches = []
     for _ in range(L):
         c = kvq.Cache(batch=w.batch, n_kv_heads=w.n_kv_heads, n_q_heads=w.n_q_heads,
                       head_dim=w.head_dim, bits=w.bits, k_group=w.k_group, v_group=w.v_group,
                       residual=w.residual, n_sink=w.n_sink, dtype=TORCH_DTYPES[w.dtype],
                       max_tokens=max_tokens, device=dev, codec=w.codec,
-                      retention=kvq.KVQ_RETAIN_LOG if w.log_window else kvq.KVQ_RETAIN_WINDOW)
+                      retention=kvq.KVQ_RETAIN_LOG if w.log_window else kvq.KVQ_RETAIN_WINDOW,
+                      page_groups=w.page_groups, pool_pages=pool_pages)
         if args.split_tokens:
             c.set_split_tokens(args.split_tokens)
-        if ragged:
-            c.append_ragged(Kd, Vd, lens0)
-        else:
+        if len(rounds) == 1 and not ragged:
             c.append(Kd, Vd)
+        else:  # in the workload's prefill rounds
+            for t0, n_new in rounds:
+                n = max(n_new)
+                c.append_ragged(Kd[:, :, t0:t0 + n].contiguous(), Vd[:, :, t0:t0 + n].contiguous(), n_new)
         caches.append(c)
     del Kd, Vd
     Ks, Vs = wl.steps_batch(w)
@@ -465,6 +474,8 @@ def main():
                    "residual": w.residual, "n_sink": w.n_sink, "storage": w.dtype,
                    "codec": "symmetric" if w.codec else "asymmetric",
                    **({"retention": "log-sparse", "log_window": w.log_window} if w.log_window else {}),
+                   **({"page_groups": w.page_groups, "pool_pages": pool_pages,
+                       "prefill_chunk": w.prefill_chunk} if w.page_groups else {}),
                    "layers_rotated": L, "parallelism": "single GPU"},
         "tokens_per_s": round(w.batch / (ms_per_step * 1e-3), 1),
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),

@@ -36,7 +36,8 @@ EXPORTED = ["kvq_cache_bytes", "kvq_cache_create", "kvq_cache_destroy", "kvq_app
             "kvq_decode_workspace_bytes", "kvq_decode_attention", "kvq_append_decode",
             "kvq_dequantize", "kvq_export",
             "kvq_cache_state", "kvq_set_split_tokens", "kvq_set_timing_events", "kvq_stream_read_probe",
-            "kvq_append_ragged", "kvq_seq_lengths", "kvq_last_error"]
+            "kvq_append_ragged", "kvq_seq_lengths", "kvq_release_sequence", "kvq_pool_free_pages",
+            "kvq_last_error"]
 
 
 class KVQError(RuntimeError):
@@ -53,7 +54,8 @@ class Config(ctypes.Structure):
                 ("v_group", ctypes.c_int32), ("residual", ctypes.c_int32),
                 ("n_sink", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("max_tokens", ctypes.c_int64), ("sm_scale", ctypes.c_float),
-                ("codec", ctypes.c_int32), ("retention", ctypes.c_int32)]
+                ("codec", ctypes.c_int32), ("retention", ctypes.c_int32),
+                ("page_groups", ctypes.c_int32), ("pool_pages", ctypes.c_int64)]
 
 
 _lib = None
@@ -85,6 +87,8 @@ def lib() -> ctypes.CDLL:
             "kvq_stream_read_probe": [P, ctypes.c_size_t, ctypes.c_int32, P, P],
             "kvq_append_ragged": [P, P, P, ctypes.POINTER(ctypes.c_int32), i64, P],
             "kvq_seq_lengths": [P, ctypes.POINTER(i64)],
+            "kvq_release_sequence": [P, ctypes.c_int32, P],
+            "kvq_pool_free_pages": [P, ctypes.POINTER(i64)],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -107,9 +111,9 @@ def _check(status: int):
 
 def make_config(*, batch, n_kv_heads, n_q_heads, head_dim, bits, k_group, v_group, residual,
                 n_sink=0, dtype=KVQ_BF16, max_tokens, sm_scale=0.0, codec=KVQ_CODEC_ASYMMETRIC,
-                retention=KVQ_RETAIN_WINDOW) -> Config:
+                retention=KVQ_RETAIN_WINDOW, page_groups=0, pool_pages=0) -> Config:
     return Config(batch, n_kv_heads, n_q_heads, head_dim, bits, k_group, v_group, residual,
-                  n_sink, dtype, max_tokens, sm_scale, codec, retention)
+                  n_sink, dtype, max_tokens, sm_scale, codec, retention, page_groups, pool_pages)
 
 
 def kvq_cache_bytes(cfg: Config) -> int:
@@ -187,6 +191,16 @@ def kvq_seq_lengths(handle: int, batch: int):
     arr = (ctypes.c_int64 * batch)()
     _check(lib().kvq_seq_lengths(ctypes.c_void_p(handle), arr))
     return [int(x) for x in arr]
+
+
+def kvq_release_sequence(handle: int, b: int, stream: int):
+    _check(lib().kvq_release_sequence(ctypes.c_void_p(handle), b, ctypes.c_void_p(stream)))
+
+
+def kvq_pool_free_pages(handle: int) -> int:
+    n = ctypes.c_int64(0)
+    _check(lib().kvq_pool_free_pages(ctypes.c_void_p(handle), ctypes.byref(n)))
+    return n.value
 
 
 def kvq_stream_read_probe(buf: int, nbytes: int, blocks_per_cu: int, sink: int, stream: int):

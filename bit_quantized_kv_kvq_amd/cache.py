@@ -30,12 +30,15 @@ class Cache:
     tokens and the first `n_sink` tokens stay full precision for good.
     `retention` = KVQ_RETAIN_LOG selects LogQuant's log-sparse retention
     (residual = 3W): a flush quantizes every other token of the oldest 2W.
+    `page_groups` > 0 keeps the quantized records in pages of that many key
+    groups from a pool of `pool_pages` pages (0: one per sequence at capacity).
     """
 
     def __init__(self, *, batch: int, n_kv_heads: int, n_q_heads: int, head_dim: int, bits: int,
                  k_group: int, v_group: int, residual: int, max_tokens: int, n_sink: int = 0,
                  dtype: torch.dtype = torch.bfloat16, sm_scale: float = 0.0,
-                 device: Optional[torch.device] = None, codec: int = 0, retention: int = 0):
+                 device: Optional[torch.device] = None, codec: int = 0, retention: int = 0,
+                 page_groups: int = 0, pool_pages: int = 0):
         _k.lib()
         self.device = torch.device(device or "cuda")
         self.dtype = dtype
@@ -43,7 +46,7 @@ class Cache:
                                   head_dim=head_dim, bits=bits, k_group=k_group, v_group=v_group,
                                   residual=residual, n_sink=n_sink, dtype=torch_dtype_code(dtype),
                                   max_tokens=max_tokens, sm_scale=sm_scale, codec=codec,
-                                  retention=retention)
+                                  retention=retention, page_groups=page_groups, pool_pages=pool_pages)
         self.nbytes = _k.kvq_cache_bytes(self.cfg)
         # over-allocate by 256 bytes so the handle's buffer is 256-byte aligned
         self._buf = torch.empty(self.nbytes + 256, dtype=torch.uint8, device=self.device)
@@ -109,6 +112,14 @@ class Cache:
     def seq_lengths(self):
         """Tokens held by each sequence (host-side)."""
         return _k.kvq_seq_lengths(self.handle, self.cfg.batch)
+
+    def release_sequence(self, b: int):
+        """Empty sequence b and return its pages to the pool."""
+        _k.kvq_release_sequence(self.handle, b, _stream())
+
+    def free_pages(self) -> int:
+        """Free pages of the pool (paged records)."""
+        return _k.kvq_pool_free_pages(self.handle)
 
     def decode(self, q: torch.Tensor, out: Optional[torch.Tensor] = None,
                lse: Optional[torch.Tensor] = None, with_lse: bool = True):

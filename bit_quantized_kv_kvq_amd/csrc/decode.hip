@@ -102,6 +102,9 @@ hipError_t launch_decode(const Layout& L, const DevPtrs& P, const DecodeRequest&
     }
     if (gps < 1) gps = 1;
     if (ng > 0 && (ng + gps - 1) / gps > cap_q) gps = (ng + cap_q - 1) / cap_q;
+    // Paged records: a split spans at most 64 pages (one lane each), which
+    // gps <= 63 P guarantees; the cache's split capacity admits it.
+    if (L.lp >= 0 && gps > 63 * ((int64_t)1 << L.lp)) gps = 63 * ((int64_t)1 << L.lp);
     const int nsplit_q = ng > 0 ? (int)((ng + gps - 1) / gps) : 0;
     const int nsplit = nsplit_q > 0 ? nsplit_q : 1;
 
@@ -141,6 +144,12 @@ hipError_t launch_decode(const Layout& L, const DevPtrs& P, const DecodeRequest&
     a.qscale = sm_scale * 1.4426950408889634f;
     a.base_len = rq.rg.base_len;
     a.len_delta = rq.rg.delta;
+    a.table = P.table;
+    a.lp = L.lp;
+    a.max_pages = (int)L.max_pages;
+    a.pool_pages = (int)L.pool_pages;
+    a.page_bytes = (uint32_t)L.page_bytes;
+    a.pool_bytes = (uint32_t)(L.pool_pages * L.page_bytes);
     void* args[] = {&a};
     const dim3 grid((unsigned)nsplit, (unsigned)L.BH);
     if (rq.ev_start != nullptr)

@@ -69,6 +69,11 @@ struct DecArgs {
     int rec_bytes, rec_kcodes, rec_vcodes, rec_vmeta;
     int dtype;  // storage dtype of q, sinks and residual (DT_*)
     int Hkv, S, R, Qf, nS, nfp, G, GV, nvg, gps, ngroups, nsplit, nsplit_cap;
+    // Paged records (table non-null): rec is the page pool (pool_bytes < 4 GiB),
+    // page table int32 [B][max_pages], 2^lp key groups per page, page_bytes each.
+    const int* table;
+    int lp, max_pages, pool_pages;
+    uint32_t page_bytes, pool_bytes;
     float qscale;  // sm_scale * log2(e)
     // Sequences of different lengths: sequence b holds base_len[b] + len_delta
     // tokens, and nS, nfp, ngroups above are replaced by its own; null otherwise.
@@ -181,6 +186,23 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferWord3);
 }
+// Byte offset, inside the records' buffer resource, of key group g0 + kWaves j
+// (a wave's j-th group, at most gmax): page_off of lane (g >> lp) - p_first plus
+// the group's place in its page.  Paged records: lane i of page_off holds the
+// offset of page p_first + i of this slice's split (at most 64 pages), always a
+// page of the pool.  Contiguous records are one page over the slice's own
+// resource (lp = 31, page_off = 0, gmax = its last record).  Every offset so
+// lies inside the resource, for the groups a wave loads beyond its own too.
+struct GroupAddr {
+    int g0, gmax, lp, p_first;
+    uint32_t mask, rec_bytes, page_off;
+    __device__ __forceinline__ uint32_t at(int j) const {
+        const int g = min(g0 + kWaves * j, gmax);
+        const uint32_t po = (uint32_t)__builtin_amdgcn_readlane((int)page_off, (g >> lp) - p_first);
+        return po + ((uint32_t)g & mask) * rec_bytes;
+    }
+};
+
 template <int N>
 struct UVec {
     typedef uint32_t T __attribute__((ext_vector_type(N)));
@@ -384,7 +406,7 @@ struct MStream {
     };
 
     __amdgpu_buffer_rsrc_t rs;
-    uint32_t grp0, group_step;
+    GroupAddr ga;
     int last_group, lane;
     uint32_t k_off, v_off, vm_off, km_off;
     uint8_t* ak_lds;  // [RBK][NKK][16 rows][64 bytes]
@@ -394,12 +416,11 @@ struct MStream {
     float kinv_l[RBK], kbias_l[RBK];
     float m_l[RBK], l2[RBK], z2[RBK][NVG], acc2[RBK][NVM];
 
-    __device__ __forceinline__ void init(const DecArgs& a, int64_t bh, int g_first, int n_my_groups, int ln,
-                                         uint8_t* lds) {
+    __device__ __forceinline__ void init(const DecArgs& a, __amdgpu_buffer_rsrc_t rsrc, const GroupAddr& addr,
+                                         int n_my_groups, int ln, uint8_t* lds) {
         lane = ln;
-        rs = make_rsrc(a.rec + rec_offset(bh, 0, a.ng_cap, a.rec_bytes), (uint32_t)(a.ng_cap * a.rec_bytes));
-        grp0 = (uint32_t)g_first * (uint32_t)a.rec_bytes;
-        group_step = (uint32_t)(kWaves * a.rec_bytes);
+        rs = rsrc;
+        ga = addr;
         last_group = n_my_groups - 1;
         const int j = lane & 15, kb = lane >> 4;
         k_off = (uint32_t)a.rec_kcodes + j * RB + kb * (KLW * 4);
@@ -424,7 +445,7 @@ struct MStream {
 
     // Tile `tig` of the wave's key group j (groups past the last reload the last).
     __device__ __forceinline__ void load(Tile& tt, int j, int tig, bool kmeta) {
-        const uint32_t grp = grp0 + (uint32_t)min(j, max(last_group, 0)) * group_step;
+        const uint32_t grp = ga.at(min(j, max(last_group, 0)));
         const int t0 = tig * TM;
 #pragma unroll
         for (int sb = 0; sb < NSB; ++sb)
@@ -847,9 +868,34 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
     const int n_my_groups = g_begin + wave < g_end ? (g_end - g_begin - wave + kWaves - 1) / kWaves : 0;
 
     {
+        // the records of this slice: its own contiguous stream, or pages of the pool
+        __amdgpu_buffer_rsrc_t rs;
+        GroupAddr ga;
+        ga.g0 = g_begin + wave;
+        ga.rec_bytes = (uint32_t)a.rec_bytes;
+        ga.gmax = a.table == nullptr ? max((int)a.ng_cap - 1, 0) : 0x7FFFFFFF;
+        if (a.table == nullptr) {
+            rs = make_rsrc(a.rec + (size_t)bh * (size_t)a.ng_cap * (size_t)a.rec_bytes,
+                           (uint32_t)(a.ng_cap * a.rec_bytes));
+            ga.lp = 31;
+            ga.mask = 0x7FFFFFFFu;
+            ga.p_first = 0;
+            ga.page_off = 0u;
+        } else {
+            rs = make_rsrc(a.rec, a.pool_bytes);
+            ga.lp = a.lp;
+            ga.mask = (1u << a.lp) - 1u;
+            ga.p_first = g_begin >> a.lp;
+            const int n_pages = ((max(g_end, g_begin + 1) - 1) >> a.lp) - ga.p_first + 1;  // <= 64
+            // entries past a sequence's own pages may be stale: any page of the pool serves,
+            // since those groups' words are never used
+            int page = lane < n_pages ? a.table[(int64_t)b * a.max_pages + ga.p_first + lane] : 0;
+            page = (uint32_t)page < (uint32_t)a.pool_pages ? page : 0;
+            ga.page_off = (uint32_t)page * a.page_bytes + (uint32_t)kvh * ((uint32_t)a.rec_bytes << a.lp);
+        }
         float qv[GQ][KM];  // folded query of this lane's KM channels (set in the prologue)
         MS ms;             // the matrix-core stream (MF only)
-        if constexpr (MF) ms.init(a, bh, g_begin + wave, n_my_groups, lane, kd);
+        if constexpr (MF) ms.init(a, rs, ga, n_my_groups, lane, kd);
 
         // One tile of the wave's stream.  Key token slot * U + u of the tile is
         // scored by the LPT lanes of `slot`; value block hb * NVL + vl (TB tokens)
@@ -861,10 +907,6 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
             u32x2 vm[U];  // value scale, zero point (fp32 bits) of (token, group gz)
             typename UVec<KM>::T ks, kz;
         };
-        const __amdgpu_buffer_rsrc_t rs =
-            make_rsrc(a.rec + rec_offset(bh, 0, a.ng_cap, a.rec_bytes), (uint32_t)(a.ng_cap * a.rec_bytes));
-        const uint32_t grp0 = (uint32_t)(g_begin + wave) * (uint32_t)a.rec_bytes;
-        const uint32_t group_step = (uint32_t)(kWaves * a.rec_bytes);
         const int last_group = n_my_groups - 1;
         // per-lane byte offsets, the same for every tile
         const uint32_t k_off = (uint32_t)a.rec_kcodes + slot * U * RB + chunk * (LW * 4);
@@ -879,7 +921,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
         // group reads group 0 of its split's range, or past the records' end,
         // where buffer loads return zeros; those words are never used.
         auto load = [&](Tile& t, int j, int tig, bool kmeta) __attribute__((always_inline)) {
-            const uint32_t grp = grp0 + (uint32_t)min(j, max(last_group, 0)) * group_step;
+            const uint32_t grp = ga.at(min(j, max(last_group, 0)));
             const int t0 = tig * TILE;
 #pragma unroll
             for (int u = 0; u < U; ++u) t.k[u] = bload<LW>(rs, k_off + u * RB, grp + t0 * RB);

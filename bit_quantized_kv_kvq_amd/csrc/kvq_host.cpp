@@ -37,6 +37,11 @@ struct kvq_cache {
     int nsplit_cap;           // max splits per slice the workspace holds
     float sm_scale;
     hipEvent_t ev_start = nullptr, ev_stop = nullptr;  // decode kernel timing (caller's events)
+    // paged records: host copy of the page table ([B][max_pages], -1 = none), the
+    // free pages (a stack) and the pages each sequence holds
+    std::vector<int> table;
+    std::vector<int> free_pages;
+    std::vector<int> n_pages;
 };
 
 namespace {
@@ -79,6 +84,9 @@ kvq_status validate(const kvq_config* c) {
     if (c->head_dim % c->v_group != 0)
         return fail(KVQ_ERR_INVALID_ARG, "head_dim (%d) is not a multiple of v_group (%d)",
                     c->head_dim, c->v_group);
+    if (c->page_groups < 0 || (c->page_groups & (c->page_groups - 1)) != 0)
+        return fail(KVQ_ERR_INVALID_ARG, "page_groups (%d) must be 0 or a power of two", c->page_groups);
+    if (c->pool_pages < 0) return fail(KVQ_ERR_INVALID_ARG, "pool_pages must be >= 0");
     if (c->retention == KVQ_RETAIN_LOG && c->residual % (3 * c->k_group) != 0)
         return fail(KVQ_ERR_INVALID_ARG, "log-sparse retention needs residual = 3W with W a multiple of "
                     "k_group (residual %d, k_group %d)", c->residual, c->k_group);
@@ -100,11 +108,15 @@ kvq_status validate(const kvq_config* c) {
         return fail(KVQ_ERR_UNSUPPORTED, "v_group must be a multiple of 16");
     if ((int64_t)c->batch * c->n_kv_heads > 65535)
         return fail(KVQ_ERR_UNSUPPORTED, "batch * n_kv_heads must be at most 65535");
-    {   // the decode kernel addresses one slice's records with 32-bit offsets
+    {   // the decode kernel addresses one slice's records, or the page pool, with
+        // 32-bit offsets
         const Layout L = make_layout(c);
-        if (L.ng_cap * (int64_t)L.rec_bytes > (int64_t)INT32_MAX)
+        if (L.lp < 0 && L.ng_cap * (int64_t)L.rec_bytes > (int64_t)INT32_MAX)
             return fail(KVQ_ERR_UNSUPPORTED, "max_tokens %lld gives more than 2 GiB of quantized "
                         "records per (sequence, kv head)", (long long)c->max_tokens);
+        if (L.lp >= 0 && L.pool_pages * L.page_bytes > (int64_t)UINT32_MAX)
+            return fail(KVQ_ERR_UNSUPPORTED, "the page pool (%lld pages of %lld bytes) exceeds 4 GiB",
+                        (long long)L.pool_pages, (long long)L.page_bytes);
     }
     return KVQ_OK;
 }
@@ -150,8 +162,23 @@ Layout make_layout(const kvq_config* c) {
     L.off_vsink = take((size_t)L.BH * L.S * fp_row);
     L.off_kres = take((size_t)L.BH * L.R * fp_row);
     L.off_vres = take((size_t)L.BH * L.R * fp_row);
-    L.off_rec = take((size_t)L.BH * L.ng_cap * L.rec_bytes);
+    if (c->page_groups > 0) {
+        int lp = 0;
+        while ((1 << lp) < c->page_groups) ++lp;
+        L.lp = lp;
+        L.max_pages = (L.ng_cap + c->page_groups - 1) / c->page_groups;
+        L.page_bytes = (int64_t)L.Hkv * c->page_groups * L.rec_bytes;
+        L.pool_pages = c->pool_pages > 0 ? c->pool_pages : (int64_t)L.B * L.max_pages;
+        L.off_rec = take((size_t)(L.pool_pages * L.page_bytes));
+    } else {
+        L.lp = -1;
+        L.max_pages = 0;
+        L.page_bytes = 0;
+        L.pool_pages = 0;
+        L.off_rec = take((size_t)L.BH * L.ng_cap * L.rec_bytes);
+    }
     L.off_lens = take((size_t)L.B * sizeof(int));
+    L.off_table = take((size_t)L.B * L.max_pages * sizeof(int));
     L.total = off;
     return L;
 }
@@ -200,6 +227,7 @@ kvq_status kvq_cache_create(const kvq_config* cfg, void* dev_buf, size_t bytes, 
     c->P.kres = c->buf + L.off_kres;
     c->P.vres = c->buf + L.off_vres;
     c->P.rec = (uint8_t*)(c->buf + L.off_rec);
+    c->P.table = L.lp >= 0 ? reinterpret_cast<int*>(c->buf + L.off_table) : nullptr;
     c->nS = c->Lq = c->r = 0;
     c->ragged = false;
     c->len.assign((size_t)L.B, 0);
@@ -210,6 +238,19 @@ kvq_status kvq_cache_create(const kvq_config* cfg, void* dev_buf, size_t bytes, 
     const int64_t want = std::max<int64_t>(8, (16LL * c->num_cu + L.BH - 1) / L.BH);
     const int64_t cap_q = std::min<int64_t>(std::min<int64_t>(want, 256), kMaxCombine / L.gqa - 1);
     c->nsplit_cap = (int)cap_q + 1;
+    if (L.lp >= 0) {
+        // a decode split spans at most 63 pages' worth of key groups
+        const int64_t per_split = 63 * ((int64_t)1 << L.lp);
+        if ((L.ng_cap + per_split - 1) / per_split > cap_q) {
+            delete c;
+            return fail(KVQ_ERR_UNSUPPORTED, "page_groups %d is too small for max_tokens %lld: decode "
+                        "splits would span more than 63 pages", 1 << L.lp, (long long)L.max_tokens);
+        }
+        c->table.assign((size_t)(L.B * L.max_pages), -1);
+        c->free_pages.resize((size_t)L.pool_pages);
+        for (int64_t i = 0; i < L.pool_pages; ++i) c->free_pages[(size_t)i] = (int)(L.pool_pages - 1 - i);
+        c->n_pages.assign((size_t)L.B, 0);
+    }
     c->sm_scale = cfg->sm_scale > 0.0f ? cfg->sm_scale : (float)(1.0 / sqrt((double)L.D));
     *out = c;
     return ok();
@@ -303,6 +344,39 @@ kvq_status append_slices(kvq_cache* c, const void* k, const void* v, int64_t n_n
 
 int64_t max_len(const kvq_cache* c) { return *std::max_element(c->len.begin(), c->len.end()); }
 
+// Paged records: gives every sequence the pages its key groups need once it holds
+// new_len[b] tokens, from the pool's free pages, and writes the new table entries
+// to the device (stream-ordered before the flushes that use them).  Fails, with
+// nothing changed, when the pool has too few free pages.
+kvq_status reserve_pages(kvq_cache* c, const std::vector<int64_t>& new_len, hipStream_t s) {
+    const Layout& L = c->L;
+    if (L.lp < 0) return KVQ_OK;
+    std::vector<int> need((size_t)L.B);
+    int64_t total = 0;
+    for (int b = 0; b < L.B; ++b) {
+        const int64_t groups = slice_state(new_len[b], L.S, L.R, L.Qf).Lq / L.G;
+        need[b] = (int)((groups + (1 << L.lp) - 1) >> L.lp);
+        total += std::max(0, need[b] - c->n_pages[b]);
+    }
+    if (total > (int64_t)c->free_pages.size())
+        return fail(KVQ_ERR_CAPACITY, "the append needs %lld more pages, the pool has %zu free", (long long)total,
+                    c->free_pages.size());
+    std::vector<int> idx, val;
+    for (int b = 0; b < L.B; ++b) {
+        while (c->n_pages[b] < need[b]) {
+            const int page = c->free_pages.back();
+            c->free_pages.pop_back();
+            const int i = (int)(b * L.max_pages + c->n_pages[b]);
+            c->table[(size_t)i] = page;
+            idx.push_back(i);
+            val.push_back(page);
+            c->n_pages[b] += 1;
+        }
+    }
+    if (idx.empty()) return KVQ_OK;
+    return check_hip(launch_set_entries(c->P.table, idx.data(), val.data(), (int)idx.size(), s), "append");
+}
+
 // After an append: back to the uniform state when every sequence has the same
 // length; otherwise the state of the longest sequence, with the device lengths
 // rewritten (write_lengths) or advanced by the caller.
@@ -341,6 +415,11 @@ kvq_status kvq_append(kvq_cache* c, const void* k, const void* v, int64_t n_new,
                     (long long)n_new, (long long)L.max_tokens, (long long)total);
     hipStream_t s = (hipStream_t)stream;
     kvq_status st;
+    {
+        std::vector<int64_t> to(c->len);
+        for (auto& n : to) n += n_new;
+        if ((st = reserve_pages(c, to, s)) != KVQ_OK) return st;
+    }
     if (!c->ragged) {
         SliceState ss{(int)c->nS, (int)c->Lq, (int)c->r};
         if ((st = append_slices(c, k, v, n_new, n_new, 0, L.BH, ss, s)) != KVQ_OK) return st;
@@ -394,6 +473,11 @@ kvq_status kvq_append_ragged(kvq_cache* c, const void* k, const void* v, const i
     if (!aligned(k, 16) || !aligned(v, 16)) return fail(KVQ_ERR_INVALID_ARG, "k and v must be 16-byte aligned");
     hipStream_t s = (hipStream_t)stream;
     kvq_status st;
+    {
+        std::vector<int64_t> to(c->len);
+        for (int b = 0; b < L.B; ++b) to[(size_t)b] += n_new[b];
+        if ((st = reserve_pages(c, to, s)) != KVQ_OK) return st;
+    }
     for (int b = 0; b < L.B; ++b) {
         if (n_new[b] == 0) continue;
         SliceState ss = slice_state(c->len[b], L.S, L.R, L.Qf);
@@ -401,6 +485,29 @@ kvq_status kvq_append_ragged(kvq_cache* c, const void* k, const void* v, const i
         c->len[b] += n_new[b];
     }
     return (st = settle(c, true, s)) != KVQ_OK ? st : ok();
+}
+
+kvq_status kvq_release_sequence(kvq_cache* c, int32_t b, void* stream) {
+    if (!c) return fail(KVQ_ERR_INVALID_ARG, "cache is NULL");
+    const Layout& L = c->L;
+    if (b < 0 || b >= L.B) return fail(KVQ_ERR_INVALID_ARG, "sequence %d is outside [0, %d)", b, L.B);
+    if (L.lp >= 0) {
+        for (int i = c->n_pages[b] - 1; i >= 0; --i) {
+            int& e = c->table[(size_t)(b * L.max_pages + i)];
+            c->free_pages.push_back(e);
+            e = -1;
+        }
+        c->n_pages[b] = 0;
+    }
+    c->len[b] = 0;
+    kvq_status st = settle(c, true, (hipStream_t)stream);
+    return st != KVQ_OK ? st : ok();
+}
+
+kvq_status kvq_pool_free_pages(const kvq_cache* c, int64_t* free_pages) {
+    if (!c || !free_pages) return fail(KVQ_ERR_INVALID_ARG, "cache or free_pages is NULL");
+    *free_pages = (int64_t)c->free_pages.size();
+    return ok();
 }
 
 kvq_status kvq_seq_lengths(const kvq_cache* c, int64_t* lens) {

@@ -40,8 +40,33 @@ struct Layout {
     int Qf;         // tokens quantized per flush: R, or W = R / 3 under log-sparse retention
     int64_t BH, max_tokens, Lq_cap, ng_cap;
     int rec_bytes, rec_kcodes, rec_vcodes, rec_vmeta;
-    size_t off_ksink, off_vsink, off_kres, off_vres, off_rec, off_lens, total;
+    // Paged records: P = 2^lp key groups of one sequence per page, all kv heads
+    // ([Hkv][P] records, page_bytes), pages from a pool of pool_pages, located
+    // through the table int32 [B][max_pages].  lp = -1: one contiguous stream of
+    // ng_cap records per slice.
+    int lp;
+    int64_t pool_pages, max_pages, page_bytes;
+    size_t off_ksink, off_vsink, off_kres, off_vres, off_rec, off_lens, off_table, total;
 };
+
+// Where the records of a cache are, for kernels: rec is the contiguous records
+// ([BH][ng_cap] of rec_bytes) or the page pool; table (null when contiguous)
+// maps (sequence, page) to a pool page.
+struct RecMap {
+    uint8_t* rec;
+    const int* table;
+    int64_t ng_cap, page_bytes;
+    int rec_bytes, lp, max_pages, Hkv;
+};
+
+// Address of the record of key group grp of slice bh.
+__host__ __device__ inline uint8_t* rec_ptr(const RecMap& m, int64_t bh, int64_t grp) {
+    if (m.table == nullptr) return m.rec + (size_t)(bh * m.ng_cap + grp) * (size_t)m.rec_bytes;
+    const int64_t b = bh / m.Hkv, kvh = bh % m.Hkv;
+    const int64_t page = m.table[b * m.max_pages + (grp >> m.lp)];
+    const int64_t in_page = kvh * ((int64_t)1 << m.lp) + (grp & (((int64_t)1 << m.lp) - 1));
+    return m.rec + (size_t)(page * m.page_bytes) + (size_t)(in_page * m.rec_bytes);
+}
 
 // Sequences of different lengths.  Sequence b holds base_len[b] + delta tokens;
 // base_len (int32 [B]) lives in the cache buffer, written by launch_set_lengths,
@@ -73,7 +98,12 @@ struct DevPtrs {
     char* kres;
     char* vres;
     uint8_t* rec;
+    int* table;  // page table (paged records), else null
 };
+
+inline RecMap rec_map(const Layout& L, const DevPtrs& P) {
+    return RecMap{P.rec, P.table, L.ng_cap, L.page_bytes, L.rec_bytes, L.lp, (int)L.max_pages, L.Hkv};
+}
 
 // ---------------------------------------------------------------------------
 // Packing.  A token row of D codes is stored as D*bits/32 dwords.  Dword i of
@@ -143,6 +173,9 @@ hipError_t launch_flush(const Layout& L, const DevPtrs& P, int64_t Lq, int64_t b
 // row, from the sequence's length before the append (rg).
 hipError_t launch_copy_one_ragged(const Layout& L, const DevPtrs& P, const void* src_k, const void* src_v,
                                   Ragged rg, hipStream_t stream);
+
+// dst[idx[i]] = val[i] for i < n (host arrays), in launches of up to 256 entries.
+hipError_t launch_set_entries(int* dst, const int* idx, const int* val, int n, hipStream_t stream);
 
 // base_len[b] = lens[b] for b < L.B (lens: host array).
 hipError_t launch_set_lengths(const Layout& L, int* base_len, const int64_t* lens, hipStream_t stream);

@@ -137,6 +137,17 @@ __global__ __launch_bounds__(256) void log_compact_kernel(uint4* kres, uint4* vr
     }
 }
 
+// dst[idx[i]] = val[i] for i < n (entries passed in the kernel arguments)
+constexpr int kEntryChunk = 256;
+struct EntryChunk {
+    int n;
+    int idx[kEntryChunk];
+    int val[kEntryChunk];
+};
+__global__ __launch_bounds__(kEntryChunk) void set_entries_kernel(int* __restrict__ dst, EntryChunk c) {
+    if ((int)threadIdx.x < c.n) dst[c.idx[threadIdx.x]] = c.val[threadIdx.x];
+}
+
 // base_len[i] = v[i] for i < n (values passed in the kernel arguments)
 constexpr int kLenChunk = 256;
 struct LenChunk {
@@ -161,7 +172,7 @@ struct QuantArgs {
     int rec_bytes, rec_kcodes, rec_vcodes, rec_vmeta;
     int codec;  // kvq_codec
     int64_t bh0;  // first slice of the launch
-    uint8_t* rec;
+    RecMap rm;
 };
 
 // key rows: dword w of token row t holds channels CPD*w + j at pack_shift(j)
@@ -250,7 +261,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
     const int ts = a.tok_stride;
     const int64_t src_row0 = bh * a.src_tokens + a.src_tok0 + (int64_t)grp * G * ts;
     const int64_t dst_grp = a.dst_tok0 / G + grp;
-    uint8_t* rec = a.rec + rec_offset(bh, dst_grp, a.ng_cap, a.rec_bytes);
+    uint8_t* rec = rec_ptr(a.rm, bh, dst_grp);
     float* kmeta = reinterpret_cast<float*>(rec);
 
     // ---- keys ----
@@ -351,7 +362,7 @@ struct DeqArgs {
     const char* vsink;
     const char* kres;
     const char* vres;
-    const uint8_t* rec;
+    RecMap rm;
     float* kout;
     float* vout;
     int64_t nS, Lq, r, T, ng_cap;  // the slices' state; with base_len, the longest sequence's
@@ -401,7 +412,7 @@ __global__ __launch_bounds__(256) void dequantize_kernel(DeqArgs a) {
         } else if (t < nS + Lq) {
             const int64_t tq = t - nS;
             const int tg = (int)(tq % a.G);
-            const uint8_t* rec = a.rec + rec_offset(bh, tq / a.G, a.ng_cap, a.rec_bytes);
+            const uint8_t* rec = rec_ptr(a.rm, bh, tq / a.G);
             const float* km = reinterpret_cast<const float*>(rec);
             const float* vm = reinterpret_cast<const float*>(rec + a.rec_vmeta) + ((int64_t)tg * a.nvg + c / a.GV) * 2;
             const float kq = (float)key_code(a, rec, tg, c);
@@ -433,7 +444,7 @@ __global__ __launch_bounds__(256) void export_kernel(DeqArgs a, uint8_t* k_codes
     for (int64_t i = i0; i < Lq_b * a.D; i += stride) {
         const int64_t t = i / a.D;
         const int c = (int)(i % a.D);
-        const uint8_t* rec = a.rec + rec_offset(bh, t / a.G, a.ng_cap, a.rec_bytes);
+        const uint8_t* rec = rec_ptr(a.rm, bh, t / a.G);
         const int tg = (int)(t % a.G);
         if (k_codes) k_codes[bh * ncode + i] = (uint8_t)key_code(a, rec, tg, c);
         if (v_codes) v_codes[bh * ncode + i] = (uint8_t)value_code(a, rec, tg, c);
@@ -442,7 +453,7 @@ __global__ __launch_bounds__(256) void export_kernel(DeqArgs a, uint8_t* k_codes
     for (int64_t i = i0; i < (Lq_b / a.G) * a.D; i += stride) {
         const int64_t g = i / a.D;
         const int c = (int)(i % a.D);
-        const float* km = reinterpret_cast<const float*>(a.rec + rec_offset(bh, g, a.ng_cap, a.rec_bytes));
+        const float* km = reinterpret_cast<const float*>(rec_ptr(a.rm, bh, g));
         if (k_scale) k_scale[bh * nk + i] = km[c];
         if (k_zero) k_zero[bh * nk + i] = km[a.D + c];
     }
@@ -450,7 +461,7 @@ __global__ __launch_bounds__(256) void export_kernel(DeqArgs a, uint8_t* k_codes
     for (int64_t i = i0; i < Lq_b * a.nvg; i += stride) {
         const int64_t t = i / a.nvg;
         const int h = (int)(i % a.nvg);
-        const uint8_t* rec = a.rec + rec_offset(bh, t / a.G, a.ng_cap, a.rec_bytes);
+        const uint8_t* rec = rec_ptr(a.rm, bh, t / a.G);
         const float* vm = reinterpret_cast<const float*>(rec + a.rec_vmeta) + ((t % a.G) * a.nvg + h) * 2;
         if (v_scale) v_scale[bh * nv + i] = vm[0];
         if (v_zero) v_zero[bh * nv + i] = vm[1];
@@ -466,7 +477,7 @@ DeqArgs make_deq_args(const Layout& L, const DevPtrs& P, int64_t nS, int64_t Lq,
     a.vsink = P.vsink;
     a.kres = P.kres;
     a.vres = P.vres;
-    a.rec = P.rec;
+    a.rm = rec_map(L, P);
     a.kout = nullptr;
     a.vout = nullptr;
     a.nS = nS;
@@ -538,6 +549,18 @@ hipError_t launch_set_lengths(const Layout& L, int* base_len, const int64_t* len
     return hipSuccess;
 }
 
+hipError_t launch_set_entries(int* dst, const int* idx, const int* val, int n, hipStream_t stream) {
+    for (int i0 = 0; i0 < n; i0 += kEntryChunk) {
+        EntryChunk c;
+        c.n = std::min(kEntryChunk, n - i0);
+        for (int i = 0; i < c.n; ++i) c.idx[i] = idx[i0 + i], c.val[i] = val[i0 + i];
+        set_entries_kernel<<<1, kEntryChunk, 0, stream>>>(dst, c);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
 hipError_t launch_quantize(const Layout& L, const DevPtrs& P, const void* src_k, const void* src_v,
                            int64_t src_tokens, int64_t src_tok0, int64_t n_groups, int64_t dst_tok0,
                            int64_t bh0, int64_t nbh, hipStream_t stream, int tok_stride) {
@@ -561,7 +584,7 @@ hipError_t launch_quantize(const Layout& L, const DevPtrs& P, const void* src_k,
     a.rec_vmeta = L.rec_vmeta;
     a.codec = L.codec;
     a.bh0 = bh0;
-    a.rec = P.rec;
+    a.rm = rec_map(L, P);
     // codes [G][D] bytes, then the keys' partial minima/maxima [P][D][2] fp32
     const size_t lds = (((size_t)L.G * L.D + 15) & ~(size_t)15) + (size_t)(256 / (L.D / 2)) * L.D * 2 * sizeof(float);
     dim3 grid((unsigned)n_groups, (unsigned)nbh);

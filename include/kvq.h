@@ -123,6 +123,10 @@ typedef struct kvq_config {
     float sm_scale;       /* softmax scale; 0 selects 1/sqrt(D)                   */
     int32_t codec;        /* kvq_codec of the key and value groups (0: asymmetric) */
     int32_t retention;    /* kvq_retention of the residual flush (0: window)      */
+    int32_t page_groups;  /* P: key groups per page of paged records, a power of  */
+                          /* two; 0 stores each sequence's records contiguously  */
+    int64_t pool_pages;   /* pages in the pool (paged records); 0 = enough for    */
+                          /* every sequence at max_tokens                         */
 } kvq_config;
 
 typedef struct kvq_cache kvq_cache; /* opaque host-side handle */
@@ -140,11 +144,13 @@ kvq_status kvq_cache_bytes(const kvq_config* cfg, size_t* bytes);
  * initialisation.  *out receives the handle, to be freed with
  * kvq_cache_destroy.  Errors: INVALID_ARG (null pointer, non-positive sizes,
  * Hq % Hkv != 0, R % G != 0, D % G_V != 0, codec not a kvq_codec, retention not a
- * kvq_retention, log-sparse retention with R not a multiple of 3G, misaligned buffer),
+ * kvq_retention, log-sparse retention with R not a multiple of 3G, page_groups not 0
+ * or a power of two, pool_pages < 0, misaligned buffer),
  * UNSUPPORTED (bits not 2/4/8, D not 64/128, Hq/Hkv not 1/2/4/8, G not in
  * {32, 64, 128, 256}, G_V not a multiple of 16, 8-bit codes with G or G_V
  * below 64, B * Hkv > 65535, more than
- * 2 GiB of quantized records per (sequence, kv head)), BUFFER_TOO_SMALL,
+ * 2 GiB of quantized records per (sequence, kv head), a page pool above 4 GiB,
+ * pages so small that a decode split would span more than 63 of them), BUFFER_TOO_SMALL,
  * DEVICE (no current HIP device).
  */
 kvq_status kvq_cache_create(const kvq_config* cfg, void* dev_buf, size_t bytes,
@@ -268,7 +274,8 @@ kvq_status kvq_cache_state(const kvq_cache* cache, int64_t* n_tokens, int64_t* n
  * All zero is a no-op.  Validation is complete before anything is enqueued.
  * The sequence lengths live in the cache buffer, written on `stream`.
  * Errors: INVALID_ARG (null, n_max < 0, n_new[b] outside [0, n_max]),
- * CAPACITY (a sequence would exceed max_tokens), DEVICE.
+ * CAPACITY (a sequence would exceed max_tokens, or the page pool has too few
+ * free pages), DEVICE.
  */
 kvq_status kvq_append_ragged(kvq_cache* cache, const void* k, const void* v, const int32_t* n_new,
                              int64_t n_max, void* stream);
@@ -278,6 +285,31 @@ kvq_status kvq_append_ragged(kvq_cache* cache, const void* k, const void* v, con
  * Errors: INVALID_ARG (null).
  */
 kvq_status kvq_seq_lengths(const kvq_cache* cache, int64_t* lens);
+
+/*
+ * Paged records (cfg.page_groups = P > 0), as a page table manages a serving
+ * KV cache ("Atom: Low-bit Quantization for Efficient and Accurate LLM
+ * Serving", runtime-breakdown figure: self-attention through PageAttention, and
+ * the baselines' list: vLLM keeps the KV cache under a page table to use GPU
+ * memory fully).  The quantized records of a sequence live in pages of P key
+ * groups (all kv heads of those groups), taken from a pool of cfg.pool_pages
+ * pages in the cache buffer as the sequence's quantized part grows and located
+ * through a page table [B][ceil(Lq_cap / (G P))] in the cache buffer.  Sinks and
+ * the residual stay per sequence.  Results are bitwise those of contiguous
+ * records.  An append that needs more pages than the pool has free fails with
+ * CAPACITY and changes nothing.  The pool is at most 4 GiB.
+ *
+ * Release sequence b: its pages return to the pool and it becomes empty (length
+ * 0), ready to take a new sequence; the other sequences are unchanged.  Work
+ * already enqueued on `stream` that reads the released pages completes before
+ * later appends on the same stream reuse them.  Also valid for contiguous records
+ * (the sequence is emptied).  Decode attention needs every sequence non-empty.
+ * Errors: INVALID_ARG (null, b outside [0, B)), DEVICE.
+ */
+kvq_status kvq_release_sequence(kvq_cache* cache, int32_t b, void* stream);
+
+/* Host-side: free pages of the pool (0 for contiguous records).  Errors: INVALID_ARG. */
+kvq_status kvq_pool_free_pages(const kvq_cache* cache, int64_t* free_pages);
 
 /*
  * Tuning and testing knob: tokens per decode split of the quantized part

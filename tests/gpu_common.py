@@ -38,9 +38,21 @@ def make_cache(w: wl.Workload, max_tokens: int | None = None, **over):
               head_dim=w.head_dim, bits=w.bits, k_group=w.k_group, v_group=w.v_group,
               residual=w.residual, n_sink=w.n_sink, dtype=TORCH_DTYPES[w.dtype],
               max_tokens=max_tokens or w.max_tokens, device=torch.device("cuda:0"), codec=w.codec,
-              retention=1 if w.log_window else 0)
+              retention=1 if w.log_window else 0, page_groups=w.page_groups)
     kw.update(over)
     return Cache(**kw)
+
+
+def prefill(cache, w: wl.Workload, Kd, Vd):
+    """The workload's prefill (device K, V [B, Hkv, prefill, D]) in its rounds."""
+    rounds = wl.prefill_rounds(w)
+    t0, n_new = rounds[0]
+    if len(rounds) == 1 and len(set(n_new)) == 1:
+        cache.append(Kd, Vd)
+        return
+    for t0, n_new in rounds:
+        n = max(n_new)
+        cache.append_ragged(Kd[:, :, t0:t0 + n].contiguous(), Vd[:, :, t0:t0 + n].contiguous(), n_new)
 
 
 class WorkloadRun:
@@ -51,11 +63,7 @@ class WorkloadRun:
         self.dev = torch.device("cuda:0")
         self.cache = cache or make_cache(w)
         Kp, Vp = wl.prefill_batch(w)
-        lens = wl.prefill_lengths(w)
-        if len(set(lens)) > 1:
-            self.cache.append_ragged(to_torch(Kp, w.dtype, self.dev), to_torch(Vp, w.dtype, self.dev), lens)
-        else:
-            self.cache.append(to_torch(Kp, w.dtype, self.dev), to_torch(Vp, w.dtype, self.dev))
+        prefill(self.cache, w, to_torch(Kp, w.dtype, self.dev), to_torch(Vp, w.dtype, self.dev))
         del Kp, Vp
         Ks, Vs = wl.steps_batch(w)
         self.Ks = to_torch(Ks, w.dtype, self.dev)

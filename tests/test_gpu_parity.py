@@ -146,6 +146,7 @@ FULL = {
     "llama7b_mha_int8": ([(0, 0), (7, 30)], None),
     "llama7b_mha_int4_ragged": ([(0, 0), (4, 9), (7, 31)], None),
     "logquant_gqa_int2": ([(0, 0), (6, 5)], None),
+    "llama7b_mha_int4_paged": ([(0, 0), (4, 9), (7, 31)], None),
 }
 
 

@@ -50,7 +50,13 @@ def _expected_bytes(c):
         Lq_cap = c.residual * (m // c.residual)
     row = D * c.bits // 8
     rec = al(8 * D + 2 * G * row + G * (D // c.v_group) * 8)
-    parts = [BH * c.n_sink * D * e] * 2 + [BH * c.residual * D * e] * 2 + [BH * (Lq_cap // G) * rec, 4 * c.batch]
+    if c.page_groups:  # a pool of pages of page_groups key groups of every kv head, and a page table
+        max_pages = -(-(Lq_cap // G) // c.page_groups)
+        pool = c.pool_pages or c.batch * max_pages
+        records, table = pool * c.n_kv_heads * c.page_groups * rec, 4 * c.batch * max_pages
+    else:
+        records, table = BH * (Lq_cap // G) * rec, 0
+    parts = [BH * c.n_sink * D * e] * 2 + [BH * c.residual * D * e] * 2 + [records, 4 * c.batch, table]
     return sum(al(p) for p in parts)
 
 
@@ -61,7 +67,10 @@ def _expected_bytes(c):
                                 dict(retention=kvq.KVQ_RETAIN_LOG, residual=192),
                                 dict(retention=kvq.KVQ_RETAIN_LOG, residual=192, max_tokens=195),
                                 dict(retention=kvq.KVQ_RETAIN_LOG, residual=192, max_tokens=196),
-                                dict(retention=kvq.KVQ_RETAIN_LOG, k_group=32, residual=96, n_sink=0)])
+                                dict(retention=kvq.KVQ_RETAIN_LOG, k_group=32, residual=96, n_sink=0),
+                                dict(page_groups=4), dict(page_groups=1, max_tokens=5000),
+                                dict(page_groups=2, pool_pages=7), dict(page_groups=8, max_tokens=100),
+                                dict(page_groups=4, retention=kvq.KVQ_RETAIN_LOG, residual=192)])
 def test_cache_bytes_matches_layout(kw):
     c = _cfg(**kw)
     assert kvq.kvq_cache_bytes(c) == _expected_bytes(c)
@@ -88,6 +97,10 @@ def test_cache_bytes_matches_layout(kw):
     (dict(dtype=7), kvq.KVQ_ERR_INVALID_ARG),
     (dict(sm_scale=-1.0), kvq.KVQ_ERR_INVALID_ARG),
     (dict(sm_scale=float("nan")), kvq.KVQ_ERR_INVALID_ARG),
+    (dict(page_groups=3), kvq.KVQ_ERR_INVALID_ARG),
+    (dict(page_groups=-2), kvq.KVQ_ERR_INVALID_ARG),
+    (dict(page_groups=4, pool_pages=-1), kvq.KVQ_ERR_INVALID_ARG),
+    (dict(page_groups=4, pool_pages=1 << 22), kvq.KVQ_ERR_UNSUPPORTED),       # pool above 4 GiB
     (dict(retention=2), kvq.KVQ_ERR_INVALID_ARG),
     (dict(retention=-1), kvq.KVQ_ERR_INVALID_ARG),
     (dict(retention=kvq.KVQ_RETAIN_LOG), kvq.KVQ_ERR_INVALID_ARG),               # R = 128 is not 3W
@@ -115,6 +128,8 @@ def test_codec_field_and_null_pointers():
     assert lib.kvq_append(None, None, None, 1, None) == kvq.KVQ_ERR_INVALID_ARG
     assert lib.kvq_decode_attention(None, None, None, None, None, 0, None) == kvq.KVQ_ERR_INVALID_ARG
     assert lib.kvq_set_timing_events(None, None, None) == kvq.KVQ_ERR_INVALID_ARG
+    assert lib.kvq_release_sequence(None, 0, None) == kvq.KVQ_ERR_INVALID_ARG
+    assert lib.kvq_pool_free_pages(None, None) == kvq.KVQ_ERR_INVALID_ARG
     assert lib.kvq_cache_destroy(None) == kvq.KVQ_OK
     assert kvq.kvq_last_error() == ""
 

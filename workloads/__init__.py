@@ -58,6 +58,8 @@ class Workload:
     codec: int = 0                  # 0 asymmetric min-max groups, 1 symmetric groups
     prefill_min_frac: float = 1.0   # sequence b prefills prefill * (1 - (1 - f) b / (B - 1)) tokens
     log_window: int = 0             # W > 0: log-sparse full-precision retention, residual = 3W
+    page_groups: int = 0            # P > 0: quantized records in pages of P key groups
+    prefill_chunk: int = 0          # prefill in rounds of this many tokens per sequence (0: at once)
 
     @property
     def gqa(self) -> int:
@@ -139,6 +141,17 @@ WORKLOADS: Dict[str, Workload] = {
         bits=8, k_group=128, v_group=128, residual=128, n_sink=0,
         prefill=4096, steps=64, attend_after_prefill=False, seed=1002,
         k_outlier_channels=4, k_outlier_scale=8.0),
+    "llama7b_mha_int4_paged": Workload(
+        name="llama7b_mha_int4_paged",
+        description="the ragged Llama-7B-shaped MHA decode on paged records: B8 H32 D128, contexts "
+                    "4096 down to 2048, bf16, INT4 G128 / G_V128, R128, pages of 4 key groups (512 "
+                    "tokens) from a pool sized to the sequences, prefilled in 512-token rounds so "
+                    "that the sequences' pages interleave, 64 decode steps",
+        batch=8, n_kv_heads=32, n_q_heads=32, head_dim=128, dtype="bf16",
+        bits=4, k_group=128, v_group=128, residual=128, n_sink=0,
+        prefill=4096, steps=64, attend_after_prefill=False, seed=1002,
+        k_outlier_channels=4, k_outlier_scale=8.0, prefill_min_frac=0.5,
+        page_groups=4, prefill_chunk=512),
     "logquant_gqa_int2": Workload(
         name="logquant_gqa_int2",
         description="Llama-3.1-8B-shaped GQA decode with LogQuant's log-sparse retention: B8, "
@@ -167,6 +180,17 @@ def prefill_lengths(w: Workload) -> list:
         return [w.prefill] * w.batch
     return [int(round(w.prefill * (1.0 - (1.0 - w.prefill_min_frac) * b / (w.batch - 1))))
             for b in range(w.batch)]
+
+
+def prefill_rounds(w: Workload) -> list:
+    """The prefill as rounds of (first token, tokens of each sequence): one round of
+    prefill_lengths(w), or, with prefill_chunk, rounds of up to prefill_chunk
+    tokens per sequence (a serving engine taking prompts a chunk at a time)."""
+    lens = prefill_lengths(w)
+    if not w.prefill_chunk:
+        return [(0, lens)]
+    return [(t0, [max(0, min(w.prefill_chunk, n - t0)) for n in lens])
+            for t0 in range(0, max(lens), w.prefill_chunk)]
 
 
 # --------------------------------------------------------------------------
