@@ -46,15 +46,19 @@ def load(path: str):
     i64, i32, dbl = ctypes.c_int64, ctypes.c_int, ctypes.c_double
     L.orc_quant_group.argtypes = [P, i64, i64, i32, i32, P, P, P, i64]
     L.orc_quant_group.restype = None
+    L.orc_quant_group_skip.argtypes = [P, i64, i64, i32, i32, i64, P, P, P, i64]
+    L.orc_quant_group_skip.restype = None
+    L.orc_outlier_index.argtypes = [P, i64, i64]
+    L.orc_outlier_index.restype = i64
     L.orc_dequant.argtypes = [ctypes.c_uint8, ctypes.c_float, ctypes.c_float]
     L.orc_dequant.restype = ctypes.c_float
-    L.orc_build_slice.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, P, P, i64] + [P] * 10 + [P]
+    L.orc_build_slice.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, i32, P, P, i64] + [P] * 14 + [P]
     L.orc_build_slice.restype = i32
-    L.orc_dequant_slice.argtypes = [i32, i32, i32, i64, i64, i64] + [P] * 12
+    L.orc_dequant_slice.argtypes = [i32, i32, i32, i64, i64, i64] + [P] * 10 + [i32] + [P] * 6
     L.orc_dequant_slice.restype = None
     L.orc_attention.argtypes = [P, P, P, i64, i32, dbl, P, P]
     L.orc_attention.restype = None
-    L.orc_decode_slices.argtypes = [i64, i32, i32, i32, i32, i64, i64, i64, dbl] + [P] * 13
+    L.orc_decode_slices.argtypes = [i64, i32, i32, i32, i32, i64, i64, i64, dbl] + [P] * 10 + [i32] + [P] * 7
     L.orc_decode_slices.restype = None
     L.orc_num_threads.argtypes = []
     L.orc_num_threads.restype = i32
@@ -98,6 +102,19 @@ def quant_group(x, bits: int, codec: int = 0):
     return s[0], z[0], q
 
 
+def quant_group_sparse(x, bits: int, codec: int = 0):
+    """Dense-and-sparse group: (scale, zero, codes, outlier index); the outlier
+    (largest magnitude, first among equals) is left out of the scale and zero."""
+    x = _f32(x).ravel()
+    m = x.size
+    o = int(lib().orc_outlier_index(_p(x), m, 1))
+    s = np.zeros(1, np.float32)
+    z = np.zeros(1, np.float32)
+    q = np.zeros(m, np.uint8)
+    lib().orc_quant_group_skip(_p(x), m, 1, bits, codec, o, _p(s), _p(z), _p(q), 1)
+    return s[0], z[0], q, o
+
+
 def dequant(q, s, z) -> np.ndarray:
     """x' = (q - z) * s elementwise, one fp32 subtraction then one fp32 product."""
     q = np.asarray(q, dtype=np.uint8)
@@ -127,14 +144,17 @@ def quantized_count(m: int, residual: int, log_window: int = 0) -> int:
 
 
 def build_slice(k_tok, v_tok, *, head_dim: int, bits: int, k_group: int, v_group: int,
-                residual: int, n_sink: int, codec: int = 0, log_window: int = 0) -> Dict[str, np.ndarray]:
+                residual: int, n_sink: int, codec: int = 0, log_window: int = 0,
+                outliers: int = 0) -> Dict[str, np.ndarray]:
     """Append the tokens of one (sequence, kv-head) one at a time; return the state.
 
     k_tok, v_tok: fp32 [n, D] (already rounded to the storage dtype).  codec: 0
     asymmetric min-max groups, 1 symmetric groups.  log_window W > 0: LogQuant's
     log-sparse retention with a full-precision part of residual = 3W tokens
     ("Resumo Técnico: LogQuant", Metodologia item 2); 0: the whole residual is
-    quantized when it reaches residual tokens.
+    quantized when it reaches residual tokens.  outliers = 1: KVQuant's per-vector
+    dense-and-sparse quantization, one full-precision outlier per key channel
+    group and per value group (ko_idx/ko_val [Lq/G, D], vo_idx/vo_val [Lq, D/GV]).
     """
     k_tok = _f32(k_tok)
     v_tok = _f32(v_tok)
@@ -150,13 +170,17 @@ def build_slice(k_tok, v_tok, *, head_dim: int, bits: int, k_group: int, v_group
         k_zero=np.zeros((Lq // G, D), np.float32),
         v_codes=np.zeros((Lq, D), np.uint8), v_scale=np.zeros((Lq, nvg), np.float32),
         v_zero=np.zeros((Lq, nvg), np.float32),
-        res_k=np.zeros((R, D), np.float32), res_v=np.zeros((R, D), np.float32))
+        res_k=np.zeros((R, D), np.float32), res_v=np.zeros((R, D), np.float32),
+        ko_idx=np.full((Lq // G, D), -1, np.int32), ko_val=np.zeros((Lq // G, D), np.float32),
+        vo_idx=np.full((Lq, nvg), -1, np.int32), vo_val=np.zeros((Lq, nvg), np.float32))
     counts = np.zeros(4, np.int64)
-    rc = lib().orc_build_slice(D, bits, codec, G, GV, R, S, log_window, _p(k_tok), _p(v_tok), n,
+    rc = lib().orc_build_slice(D, bits, codec, G, GV, R, S, log_window, outliers, _p(k_tok), _p(v_tok), n,
                                _p(st["sink_k"]), _p(st["sink_v"]),
                                _p(st["k_codes"]), _p(st["k_scale"]), _p(st["k_zero"]),
                                _p(st["v_codes"]), _p(st["v_scale"]), _p(st["v_zero"]),
-                               _p(st["res_k"]), _p(st["res_v"]), _p(counts))
+                               _p(st["res_k"]), _p(st["res_v"]),
+                               _p(st["ko_idx"]), _p(st["ko_val"]), _p(st["vo_idx"]), _p(st["vo_val"]),
+                               _p(counts))
     if rc != 0:
         raise ValueError("invalid oracle configuration")
     nS_, Lq_, r_, fl = (int(c) for c in counts)
@@ -166,7 +190,8 @@ def build_slice(k_tok, v_tok, *, head_dim: int, bits: int, k_group: int, v_group
     st["res_k"] = st["res_k"][:r_]
     st["res_v"] = st["res_v"][:r_]
     st.update(n_sink=nS_, n_quant=Lq_, n_resid=r_, flushes=fl, head_dim=D, bits=bits,
-              k_group=G, v_group=GV, residual=R, S=S, codec=codec, log_window=log_window)
+              k_group=G, v_group=GV, residual=R, S=S, codec=codec, log_window=log_window,
+              outliers=outliers)
     return st
 
 
@@ -180,7 +205,9 @@ def dequant_slice(st) -> tuple:
     arrs = [np.ascontiguousarray(st[k]) for k in
             ("sink_k", "sink_v", "k_codes", "k_scale", "k_zero", "v_codes", "v_scale",
              "v_zero", "res_k", "res_v")]
-    lib().orc_dequant_slice(D, G, GV, nS, Lq, r, *[_p(a) for a in arrs], _p(ko), _p(vo))
+    sparse = [np.ascontiguousarray(st[k]) for k in ("ko_idx", "ko_val", "vo_idx", "vo_val")]
+    lib().orc_dequant_slice(D, G, GV, nS, Lq, r, *[_p(a) for a in arrs], int(st.get("outliers", 0)),
+                            *[_p(a) for a in sparse], _p(ko), _p(vo))
     return ko, vo
 
 
@@ -218,9 +245,11 @@ def decode_slices(states, q, scale: float):
 
     arrs = [stack(k) for k in ("sink_k", "sink_v", "k_codes", "k_scale", "k_zero",
                                 "v_codes", "v_scale", "v_zero", "res_k", "res_v")]
+    sparse = [stack(k) for k in ("ko_idx", "ko_val", "vo_idx", "vo_val")]
     out = np.zeros((n, g, D), np.float64)
     lse = np.zeros((n, g), np.float64)
     lib().orc_decode_slices(n, g, D, G, GV, nS, Lq, r, float(scale), *[_p(a) for a in arrs],
+                            int(st0.get("outliers", 0)), *[_p(a) for a in sparse],
                             _p(q), _p(out), _p(lse))
     return out, lse
 
@@ -253,7 +282,7 @@ def slice_state(w, b: int, kvh: int, n_steps: int):
     k, v = slice_tokens_f32(w, b, kvh, n_steps)
     return build_slice(k, v, head_dim=w.head_dim, bits=w.bits, k_group=w.k_group,
                        v_group=w.v_group, residual=w.residual, n_sink=w.n_sink, codec=w.codec,
-                       log_window=w.log_window)
+                       log_window=w.log_window, outliers=w.outliers)
 
 
 def expected_outputs(w, b: int, kvh: int, n_steps: int, qi: int, scale: float | None = None):

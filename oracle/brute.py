@@ -21,16 +21,18 @@ import numpy as np
 f32 = np.float32
 
 
-def quant_group(values, bits: int, codec: int = 0):
+def quant_group(values, bits: int, codec: int = 0, range_of=None):
     """Returns (scale, zero, codes) with one binary32 rounding per operation.
 
     codec 0: asymmetric min-max; codec 1: symmetric, scale 2 max|x| / (2^n - 1),
     signed code clamp(rint(x / scale), -2^(n-1), 2^(n-1) - 1) stored plus 2^(n-1)
     (Atom review, section 三 "核心公式", symmetric simplification, c = 1).
+    range_of: the values whose min and max set the scale (default: values).
     """
     xs = [f32(v) for v in values]
-    mn = min(xs)
-    mx = max(xs)
+    rs = xs if range_of is None else [f32(v) for v in range_of]
+    mn = min(rs)
+    mx = max(rs)
     qmax = f32((1 << bits) - 1)
     if codec == 1:
         amax = max(abs(mn), abs(mx))
@@ -57,6 +59,17 @@ def quant_group(values, bits: int, codec: int = 0):
     return s, z, codes
 
 
+def quant_group_sparse(values, bits: int, codec: int = 0):
+    """KVQuant's per-vector dense-and-sparse split ("LLM系列：KVCache量化1 KIVI…"
+    page, section 3, item (4)): the element of largest magnitude (first among
+    equals) is the outlier; the others set the scale; every element gets a code.
+    Returns (scale, zero, codes, outlier index)."""
+    mags = [abs(float(v)) for v in values]
+    o = mags.index(max(mags))
+    s, z, codes = quant_group(values, bits, codec, range_of=[v for i, v in enumerate(values) if i != o])
+    return s, z, codes, o
+
+
 def dequant(code: int, s, z):
     return f32(f32(f32(code) - f32(z)) * f32(s))
 
@@ -78,7 +91,8 @@ def attention(q, K, V, scale: float):
     return np.array(out), m + math.log(den)
 
 
-def build_slice(k_tok, v_tok, *, bits, k_group, v_group, residual, n_sink, codec=0, log_window=0):
+def build_slice(k_tok, v_tok, *, bits, k_group, v_group, residual, n_sink, codec=0, log_window=0,
+                outliers=0):
     """Token-by-token cache construction, written independently of the C oracle.
 
     log_window W > 0: LogQuant's log-sparse retention ("Resumo Técnico: LogQuant",
@@ -86,14 +100,19 @@ def build_slice(k_tok, v_tok, *, bits, k_group, v_group, residual, n_sink, codec
     tokens; when full, its first 2W entries are split into pairs, the first of
     each pair is quantized and the second kept, and the last W entries follow.
 
+    outliers = 1: dense-and-sparse groups (quant_group_sparse); an outlier
+    dequantizes to its own value.
+
     Returns dict with lists: sinks, quantized (dequantized K', V' rows in the
-    order they were quantized), residual rows, codes and metadata, and the
-    flush count.
+    order they were quantized), residual rows, codes and metadata, outliers
+    (k_out per key block: [(token, value)] per channel; v_out per token:
+    [(channel, value)] per value group), and the flush count.
     """
     D = len(k_tok[0])
     sinks_k, sinks_v, res_k, res_v = [], [], [], []
     qk_rows, qv_rows = [], []
     k_codes, v_codes, k_meta, v_meta = [], [], [], []
+    k_out, v_out = [], []
     flushes = 0
     for kt, vt in zip(k_tok, v_tok):
         if len(sinks_k) < n_sink:
@@ -118,27 +137,39 @@ def build_slice(k_tok, v_tok, *, bits, k_group, v_group, residual, n_sink, codec
             block = out_k[j0:j0 + k_group]
             rows = [[None] * D for _ in block]
             crow = [[0] * D for _ in block]
-            meta = []
+            meta, outs = [], []
             for c in range(D):
-                s, z, q = quant_group([row[c] for row in block], bits, codec)
+                col = [row[c] for row in block]
+                if outliers:
+                    s, z, q, o = quant_group_sparse(col, bits, codec)
+                    outs.append((o, f32(col[o])))
+                else:
+                    (s, z, q), o = quant_group(col, bits, codec), None
                 meta.append((s, z))
                 for i, code in enumerate(q):
-                    rows[i][c] = dequant(code, s, z)
+                    rows[i][c] = f32(col[i]) if i == o else dequant(code, s, z)
                     crow[i][c] = code
             qk_rows.extend(rows)
             k_codes.extend(crow)
             k_meta.append(meta)
+            k_out.append(outs)
         # values: per token, per run of v_group channels
         for row in out_v:
-            out, crow, meta = [], [], []
+            out, crow, meta, outs = [], [], [], []
             for h in range(0, D, v_group):
-                s, z, q = quant_group(row[h:h + v_group], bits, codec)
+                vec = row[h:h + v_group]
+                if outliers:
+                    s, z, q, o = quant_group_sparse(vec, bits, codec)
+                    outs.append((o, f32(vec[o])))
+                else:
+                    (s, z, q), o = quant_group(vec, bits, codec), None
                 meta.append((s, z))
-                out.extend(dequant(code, s, z) for code in q)
+                out.extend(f32(vec[i]) if i == o else dequant(code, s, z) for i, code in enumerate(q))
                 crow.extend(q)
             qv_rows.append(out)
             v_codes.append(crow)
             v_meta.append(meta)
+            v_out.append(outs)
     return dict(sinks_k=sinks_k, sinks_v=sinks_v, qk=qk_rows, qv=qv_rows,
                 res_k=res_k, res_v=res_v, k_codes=k_codes, v_codes=v_codes,
-                k_meta=k_meta, v_meta=v_meta, flushes=flushes)
+                k_meta=k_meta, v_meta=v_meta, k_out=k_out, v_out=v_out, flushes=flushes)

@@ -35,6 +35,12 @@
  *       ("Resumo Técnico: LogQuant", Metodologia item 2, window configuration,
  *        selection scheme, full-precision reserve and dynamic adjustment; item 4:
  *        quantized and full-precision tokens may be concatenated in any order)
+ *   - KVQuant's per-vector dense-and-sparse quantization (outliers = 1): in every
+ *     quantization vector the element of largest magnitude is an outlier, kept
+ *     at full precision beside the codes; the vector's scale and zero point come
+ *     from the other elements ("LLM系列：KVCache量化1 KIVI…" page, section 3
+ *     "KVQuant", item (4): a small share of numeric outliers, e.g. 1%, stays
+ *     unquantized in a separate sparse matrix)
  *   - attention softmax(q K^T / sqrt(d)) V over every cached token
  *       (Int4 KV-cache post, section 3, attention formula; KIVI notes, section 1,
  *        logits as the concatenation of the grouped and residual parts;
@@ -64,6 +70,10 @@
  *   thin out with their distance from the newest token; the W quantized tokens
  *   join the quantized part as W/G key groups in their order;
  *   the first S tokens of a sequence stay full precision for good (sinks);
+ *   dense-and-sparse: one outlier per quantization vector (a key channel over G
+ *   tokens, a token's G_V value channels), the element of largest |x|, the
+ *   lowest index among equal magnitudes; it still receives a code, clamped like
+ *   any other, but dequantizes to its exact value;
  *   query head h reads kv head h / (Hq / Hkv).
  */
 #include <math.h>
@@ -87,14 +97,18 @@
 
 /*
  * Quantize m values x[0], x[stride], ... to n-bit codes with the asymmetric
- * (codec 0) or symmetric (codec 1) quantizer.  Writes the group's scale and
- * zero point and the codes q[0], q[qstride], ...
+ * (codec 0) or symmetric (codec 1) quantizer, the scale and zero point taken
+ * from every element but x[skip * stride] (skip = -1: from all; m >= 2 when
+ * skipping).  Writes the group's scale and zero point and the codes q[0],
+ * q[qstride], ... of all m elements.
  */
-void orc_quant_group(const float* x, int64_t m, int64_t stride, int bits, int codec,
-                     float* s_out, float* z_out, uint8_t* q, int64_t qstride)
+void orc_quant_group_skip(const float* x, int64_t m, int64_t stride, int bits, int codec, int64_t skip,
+                          float* s_out, float* z_out, uint8_t* q, int64_t qstride)
 {
-    float mn = x[0], mx = x[0];
-    for (int64_t i = 1; i < m; ++i) {
+    const int64_t first = skip == 0 ? 1 : 0;
+    float mn = x[first * stride], mx = x[first * stride];
+    for (int64_t i = first + 1; i < m; ++i) {
+        if (i == skip) continue;
         float v = x[i * stride];
         if (v < mn) mn = v;
         if (v > mx) mx = v;
@@ -137,6 +151,21 @@ void orc_quant_group(const float* x, int64_t m, int64_t stride, int bits, int co
     *z_out = z;
 }
 
+void orc_quant_group(const float* x, int64_t m, int64_t stride, int bits, int codec,
+                     float* s_out, float* z_out, uint8_t* q, int64_t qstride)
+{
+    orc_quant_group_skip(x, m, stride, bits, codec, -1, s_out, z_out, q, qstride);
+}
+
+/* The index of the element of largest magnitude (the lowest among equal ones). */
+int64_t orc_outlier_index(const float* x, int64_t m, int64_t stride)
+{
+    int64_t best = 0;
+    for (int64_t i = 1; i < m; ++i)
+        if (fabsf(x[i * stride]) > fabsf(x[best * stride])) best = i;
+    return best;
+}
+
 /* x' = (code - zero) * scale */
 float orc_dequant(uint8_t q, float s, float z)
 {
@@ -156,6 +185,9 @@ typedef struct {
     uint8_t* k_codes; float* k_scale; float* k_zero;   /* [Lq,D] [Lq/G,D] */
     uint8_t* v_codes; float* v_scale; float* v_zero;   /* [Lq,D] [Lq,D/GV] */
     float* res_k; float* res_v;                 /* [R, D]            */
+    int outliers;                               /* one per vector, or none */
+    int32_t* ko_idx; float* ko_val;             /* [Lq/G, D]: token in group, value */
+    int32_t* vo_idx; float* vo_val;             /* [Lq, D/GV]: channel in group, value */
     int64_t nS, Lq, r, flushes;
 } orc_slice;
 
@@ -171,18 +203,30 @@ static void quantize_block(orc_slice* c, const float* bk, const float* bv, int m
     for (int j = 0; j < m / G; ++j) {
         int64_t grp = c->Lq / G + j;
         for (int ch = 0; ch < D; ++ch) {
-            orc_quant_group(bk + (int64_t)j * G * D + ch, G, D, c->bits, c->codec,
-                            &c->k_scale[grp * D + ch], &c->k_zero[grp * D + ch],
-                            c->k_codes + (c->Lq + (int64_t)j * G) * D + ch, D);
+            const float* col = bk + (int64_t)j * G * D + ch;
+            const int64_t o = c->outliers ? orc_outlier_index(col, G, D) : -1;
+            orc_quant_group_skip(col, G, D, c->bits, c->codec, o,
+                                 &c->k_scale[grp * D + ch], &c->k_zero[grp * D + ch],
+                                 c->k_codes + (c->Lq + (int64_t)j * G) * D + ch, D);
+            if (c->outliers) {
+                c->ko_idx[grp * D + ch] = (int32_t)o;
+                c->ko_val[grp * D + ch] = col[o * D];
+            }
         }
     }
     /* values: one group per run of GV channels of each token */
     for (int t = 0; t < m; ++t) {
         int64_t tok = c->Lq + t;
         for (int h = 0; h < nvg; ++h) {
-            orc_quant_group(bv + (int64_t)t * D + (int64_t)h * GV, GV, 1, c->bits, c->codec,
-                            &c->v_scale[tok * nvg + h], &c->v_zero[tok * nvg + h],
-                            c->v_codes + tok * D + (int64_t)h * GV, 1);
+            const float* vec = bv + (int64_t)t * D + (int64_t)h * GV;
+            const int64_t o = c->outliers ? orc_outlier_index(vec, GV, 1) : -1;
+            orc_quant_group_skip(vec, GV, 1, c->bits, c->codec, o,
+                                 &c->v_scale[tok * nvg + h], &c->v_zero[tok * nvg + h],
+                                 c->v_codes + tok * D + (int64_t)h * GV, 1);
+            if (c->outliers) {
+                c->vo_idx[tok * nvg + h] = (int32_t)o;
+                c->vo_val[tok * nvg + h] = vec[o];
+            }
         }
     }
     c->Lq += m;
@@ -251,22 +295,28 @@ static void append_token(orc_slice* c, const float* k, const float* v)
  * receive nS, Lq, r and the number of flushes.  Output buffers must hold the
  * sizes given above for the final Lq: with m = n - S tokens past the sinks,
  * R*floor(m/R), or with W > 0, 0 for m < R and W*(floor((m-R)/W) + 1) after.
+ * outliers = 1 keeps one outlier per quantization vector: ko_idx, ko_val
+ * [Lq/G, D] (token within the group, exact value), vo_idx, vo_val [Lq, D/GV]
+ * (channel within the group, exact value); with outliers = 0 they are unused.
  * Returns 0, or -1 on an invalid configuration.
  */
-int orc_build_slice(int D, int bits, int codec, int G, int GV, int R, int S, int W,
+int orc_build_slice(int D, int bits, int codec, int G, int GV, int R, int S, int W, int outliers,
                     const float* k_tok, const float* v_tok, int64_t n,
                     float* sink_k, float* sink_v,
                     uint8_t* k_codes, float* k_scale, float* k_zero,
                     uint8_t* v_codes, float* v_scale, float* v_zero,
-                    float* res_k, float* res_v, int64_t* counts)
+                    float* res_k, float* res_v,
+                    int32_t* ko_idx, float* ko_val, int32_t* vo_idx, float* vo_val, int64_t* counts)
 {
     if (D <= 0 || G <= 0 || GV <= 0 || R <= 0 || S < 0 || n < 0) return -1;
     if (bits != 2 && bits != 4 && bits != 8) return -1;
     if (codec != ORC_CODEC_ASYMMETRIC && codec != ORC_CODEC_SYMMETRIC) return -1;
     if (R % G != 0 || D % GV != 0) return -1;
     if (W < 0 || (W > 0 && (R != 3 * W || W % G != 0))) return -1;
+    if (outliers != 0 && (outliers != 1 || G < 2 || GV < 2)) return -1;
     orc_slice c = {D, bits, codec, G, GV, R, S, W, sink_k, sink_v, k_codes, k_scale, k_zero,
-                   v_codes, v_scale, v_zero, res_k, res_v, 0, 0, 0, 0};
+                   v_codes, v_scale, v_zero, res_k, res_v, outliers, ko_idx, ko_val, vo_idx, vo_val,
+                   0, 0, 0, 0};
     for (int64_t t = 0; t < n; ++t)
         append_token(&c, k_tok + t * D, v_tok + t * D);
     counts[0] = c.nS; counts[1] = c.Lq; counts[2] = c.r; counts[3] = c.flushes;
@@ -283,6 +333,8 @@ void orc_dequant_slice(int D, int G, int GV, int64_t nS, int64_t Lq, int64_t r,
                        const uint8_t* k_codes, const float* k_scale, const float* k_zero,
                        const uint8_t* v_codes, const float* v_scale, const float* v_zero,
                        const float* res_k, const float* res_v,
+                       int outliers, const int32_t* ko_idx, const float* ko_val,
+                       const int32_t* vo_idx, const float* vo_val,
                        float* k_out, float* v_out)
 {
     const int nvg = D / GV;
@@ -296,6 +348,9 @@ void orc_dequant_slice(int D, int G, int GV, int64_t nS, int64_t Lq, int64_t r,
             int h = ch / GV;
             v_out[(nS + t) * D + ch] = orc_dequant(v_codes[t * D + ch],
                                                    v_scale[t * nvg + h], v_zero[t * nvg + h]);
+            /* outliers: their exact values */
+            if (outliers && ko_idx[grp * D + ch] == t % G) k_out[(nS + t) * D + ch] = ko_val[grp * D + ch];
+            if (outliers && vo_idx[t * nvg + h] == ch - h * GV) v_out[(nS + t) * D + ch] = vo_val[t * nvg + h];
         }
     }
     memcpy(k_out + (nS + Lq) * D, res_k, sizeof(float) * r * D);
@@ -346,6 +401,8 @@ void orc_decode_slices(int64_t n, int g, int D, int G, int GV,
                        const uint8_t* k_codes, const float* k_scale, const float* k_zero,
                        const uint8_t* v_codes, const float* v_scale, const float* v_zero,
                        const float* res_k, const float* res_v,
+                       int outliers, const int32_t* ko_idx, const float* ko_val,
+                       const int32_t* vo_idx, const float* vo_val,
                        const float* q, double* out, double* lse)
 {
     const int64_t T = nS + Lq + r;
@@ -359,7 +416,9 @@ void orc_decode_slices(int64_t n, int g, int D, int G, int GV,
                           k_codes + i * Lq * D, k_scale + i * (Lq / G) * D,
                           k_zero + i * (Lq / G) * D,
                           v_codes + i * Lq * D, v_scale + i * Lq * nvg, v_zero + i * Lq * nvg,
-                          res_k + i * r * D, res_v + i * r * D, kf, vf);
+                          res_k + i * r * D, res_v + i * r * D, outliers,
+                          ko_idx + (outliers ? i * (Lq / G) * D : 0), ko_val + (outliers ? i * (Lq / G) * D : 0),
+                          vo_idx + (outliers ? i * Lq * nvg : 0), vo_val + (outliers ? i * Lq * nvg : 0), kf, vf);
         for (int h = 0; h < g; ++h)
             orc_attention(q + (i * g + h) * D, kf, vf, T, D, scale,
                           out + (i * g + h) * D, lse + i * g + h);

@@ -12,6 +12,7 @@ import oracle
 import tests.test_oracle_cache as tc
 import tests.test_oracle_codec as tq
 import tests.test_oracle_logquant as tl
+import tests.test_oracle_outliers as to
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "kvq_oracle.c")
 
@@ -52,8 +53,8 @@ MUTANTS = {
         "    memcpy(c->res_v + c->r * D, v, sizeof(float) * D);\n"
         "    c->r += 1;"),
     # keys grouped along channels of a token instead of along tokens of a channel
-    "key_groups_transposed": ("orc_quant_group(bk + (int64_t)j * G * D + ch, G, D, c->bits,",
-                              "orc_quant_group(bk + (int64_t)j * G * D + ch, G, 1, c->bits,"),
+    "key_groups_transposed": ("orc_quant_group_skip(col, G, D, c->bits,",
+                              "orc_quant_group_skip(col, G, 1, c->bits,"),
     # softmax scale dropped
     "no_softmax_scale": ("sc[j] = dot * scale;", "sc[j] = dot;"),
     # the last token of the cache is left out of the softmax denominator
@@ -94,6 +95,19 @@ MUTANTS = {
         "        memcpy(bv + (size_t)i * D, c->res_v + (size_t)i * D, sizeof(float) * D);\n"
         "        memcpy(keep_k + (size_t)i * D, c->res_k + (size_t)(W + i) * D, sizeof(float) * D);\n"
         "        memcpy(keep_v + (size_t)i * D, c->res_v + (size_t)(W + i) * D, sizeof(float) * D);"),
+    # dense-and-sparse: the outlier chosen by value instead of magnitude
+    "outlier_by_value": ("if (fabsf(x[i * stride]) > fabsf(x[best * stride])) best = i;",
+                         "if (x[i * stride] > x[best * stride]) best = i;"),
+    # dense-and-sparse: the last of equal magnitudes
+    "outlier_tie_last": ("if (fabsf(x[i * stride]) > fabsf(x[best * stride])) best = i;",
+                         "if (fabsf(x[i * stride]) >= fabsf(x[best * stride])) best = i;"),
+    # dense-and-sparse: the outlier kept in the range
+    "outlier_in_range": ("        if (i == skip) continue;\n", ""),
+    # dense-and-sparse: key outliers dequantized from their codes
+    "outlier_key_dequant_dense": (
+        "if (outliers && ko_idx[grp * D + ch] == t % G) k_out[(nS + t) * D + ch] = ko_val[grp * D + ch];", ""),
+    # dense-and-sparse: value outlier channel taken from the vector's start
+    "outlier_value_channel": ("vo_idx[t * nvg + h] == ch - h * GV", "vo_idx[t * nvg + h] == ch"),
     # residual tokens left out of the dequantized token sequence
     "drop_residual": ("memcpy(k_out + (nS + Lq) * D, res_k, sizeof(float) * r * D);",
                       "memset(k_out + (nS + Lq) * D, 0, sizeof(float) * r * D);"),
@@ -126,6 +140,12 @@ def _pins():
         pins.append(lambda w=W: tl.test_every_token_once_newest_kept_and_log_sparse_gaps(w))
     pins.append(lambda: tl.test_matches_brute(2, 0, 0, 4, 2, 8, 37))
     pins.append(tl.test_before_first_flush_is_plain_attention)
+    for case in to._cases():
+        pins.append(lambda c=case: to.test_golden_example(c))
+    for bits in (2, 4):
+        pins.append(lambda b=bits: to.test_invariants_random_groups(b, 0))
+    pins.append(lambda: to.test_slice_outliers_exact_and_matches_brute(4, 0, 0, 4, 8, 8, 37, 0))
+    pins.append(lambda: to.test_slice_outliers_exact_and_matches_brute(2, 1, 2, 8, 4, 16, 50, 0))
     return pins
 
 

@@ -60,6 +60,7 @@ class Workload:
     log_window: int = 0             # W > 0: log-sparse full-precision retention, residual = 3W
     page_groups: int = 0            # P > 0: quantized records in pages of P key groups
     prefill_chunk: int = 0          # prefill in rounds of this many tokens per sequence (0: at once)
+    outliers: int = 0               # 1: one full-precision outlier per quantization vector
 
     @property
     def gqa(self) -> int:
