@@ -50,7 +50,8 @@ DEFAULT_WORKLOAD = "llama7b_mha_int4"
 DECODE_SOURCES = ["decode_impl.h", "decode_dispatch.h", "decode.hip", "kvq_internal.h",
                   "decode_b4_d128.hip", "decode_b2_d128.hip", "decode_b4_d64.hip", "decode_b2_d64.hip",
                   "decode_mf_b4_d128.hip", "decode_mf_b2_d128.hip", "decode_mf_b4_d64.hip", "decode_mf_b2_d64.hip",
-                  "decode_mf_b8_d128.hip", "decode_mf_b8_d64.hip"]
+                  "decode_mf_b8_d128.hip", "decode_mf_b8_d64.hip",
+                  "decode_sp_b4_d128.hip", "decode_sp_b2_d128.hip", "decode_sp_b4_d64.hip", "decode_sp_b2_d64.hip"]
 
 
 def algorithmic_bytes(w: wl.Workload, n_sink: int, n_quant: int, n_resid: int) -> int:
@@ -60,6 +61,8 @@ def algorithmic_bytes(w: wl.Workload, n_sink: int, n_quant: int, n_resid: int) -
                  + (n_quant // w.k_group) * 2 * D * 4            # K scale + zero
                  + n_quant * (D // w.v_group) * 2 * 4            # V scale + zero
                  + (n_sink + n_resid) * 2 * D * e)               # full-precision tokens
+    if w.outliers:  # one per key channel group and per value group: fp32 value, place and code
+        per_slice += (n_quant // w.k_group) * D * 6 + n_quant * (D // w.v_group) * 6
     return w.batch * w.n_kv_heads * per_slice + w.batch * w.n_q_heads * D * (e + 4)
 
 
@@ -338,7 +341,7 @@ def main():
                       residual=w.residual, n_sink=w.n_sink, dtype=TORCH_DTYPES[w.dtype],
                       max_tokens=max_tokens, device=dev, codec=w.codec,
                       retention=kvq.KVQ_RETAIN_LOG if w.log_window else kvq.KVQ_RETAIN_WINDOW,
-                      page_groups=w.page_groups, pool_pages=pool_pages)
+                      page_groups=w.page_groups, pool_pages=pool_pages, outliers=w.outliers)
         if args.split_tokens:
             c.set_split_tokens(args.split_tokens)
         if len(rounds) == 1 and not ragged:
@@ -474,6 +477,7 @@ def main():
                    "residual": w.residual, "n_sink": w.n_sink, "storage": w.dtype,
                    "codec": "symmetric" if w.codec else "asymmetric",
                    **({"retention": "log-sparse", "log_window": w.log_window} if w.log_window else {}),
+                   **({"outliers": "one per quantization vector"} if w.outliers else {}),
                    **({"page_groups": w.page_groups, "pool_pages": pool_pages,
                        "prefill_chunk": w.prefill_chunk} if w.page_groups else {}),
                    "layers_rotated": L, "parallelism": "single GPU"},

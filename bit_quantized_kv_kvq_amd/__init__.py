@@ -37,7 +37,7 @@ EXPORTED = ["kvq_cache_bytes", "kvq_cache_create", "kvq_cache_destroy", "kvq_app
             "kvq_dequantize", "kvq_export",
             "kvq_cache_state", "kvq_set_split_tokens", "kvq_set_timing_events", "kvq_stream_read_probe",
             "kvq_append_ragged", "kvq_seq_lengths", "kvq_release_sequence", "kvq_pool_free_pages",
-            "kvq_last_error"]
+            "kvq_export_outliers", "kvq_last_error"]
 
 
 class KVQError(RuntimeError):
@@ -55,7 +55,8 @@ class Config(ctypes.Structure):
                 ("n_sink", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("max_tokens", ctypes.c_int64), ("sm_scale", ctypes.c_float),
                 ("codec", ctypes.c_int32), ("retention", ctypes.c_int32),
-                ("page_groups", ctypes.c_int32), ("pool_pages", ctypes.c_int64)]
+                ("page_groups", ctypes.c_int32), ("pool_pages", ctypes.c_int64),
+                ("outliers", ctypes.c_int32)]
 
 
 _lib = None
@@ -89,6 +90,7 @@ def lib() -> ctypes.CDLL:
             "kvq_seq_lengths": [P, ctypes.POINTER(i64)],
             "kvq_release_sequence": [P, ctypes.c_int32, P],
             "kvq_pool_free_pages": [P, ctypes.POINTER(i64)],
+            "kvq_export_outliers": [P, P, P, P, P, P],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -111,9 +113,9 @@ def _check(status: int):
 
 def make_config(*, batch, n_kv_heads, n_q_heads, head_dim, bits, k_group, v_group, residual,
                 n_sink=0, dtype=KVQ_BF16, max_tokens, sm_scale=0.0, codec=KVQ_CODEC_ASYMMETRIC,
-                retention=KVQ_RETAIN_WINDOW, page_groups=0, pool_pages=0) -> Config:
+                retention=KVQ_RETAIN_WINDOW, page_groups=0, pool_pages=0, outliers=0) -> Config:
     return Config(batch, n_kv_heads, n_q_heads, head_dim, bits, k_group, v_group, residual,
-                  n_sink, dtype, max_tokens, sm_scale, codec, retention, page_groups, pool_pages)
+                  n_sink, dtype, max_tokens, sm_scale, codec, retention, page_groups, pool_pages, outliers)
 
 
 def kvq_cache_bytes(cfg: Config) -> int:
@@ -195,6 +197,11 @@ def kvq_seq_lengths(handle: int, batch: int):
 
 def kvq_release_sequence(handle: int, b: int, stream: int):
     _check(lib().kvq_release_sequence(ctypes.c_void_p(handle), b, ctypes.c_void_p(stream)))
+
+
+def kvq_export_outliers(handle: int, k_idx: int, k_val: int, v_idx: int, v_val: int, stream: int):
+    _check(lib().kvq_export_outliers(ctypes.c_void_p(handle), ctypes.c_void_p(k_idx), ctypes.c_void_p(k_val),
+                                     ctypes.c_void_p(v_idx), ctypes.c_void_p(v_val), ctypes.c_void_p(stream)))
 
 
 def kvq_pool_free_pages(handle: int) -> int:

@@ -32,13 +32,15 @@ class Cache:
     (residual = 3W): a flush quantizes every other token of the oldest 2W.
     `page_groups` > 0 keeps the quantized records in pages of that many key
     groups from a pool of `pool_pages` pages (0: one per sequence at capacity).
+    `outliers` = 1 keeps one full-precision outlier per quantization vector
+    (KVQuant's dense-and-sparse groups).
     """
 
     def __init__(self, *, batch: int, n_kv_heads: int, n_q_heads: int, head_dim: int, bits: int,
                  k_group: int, v_group: int, residual: int, max_tokens: int, n_sink: int = 0,
                  dtype: torch.dtype = torch.bfloat16, sm_scale: float = 0.0,
                  device: Optional[torch.device] = None, codec: int = 0, retention: int = 0,
-                 page_groups: int = 0, pool_pages: int = 0):
+                 page_groups: int = 0, pool_pages: int = 0, outliers: int = 0):
         _k.lib()
         self.device = torch.device(device or "cuda")
         self.dtype = dtype
@@ -46,7 +48,8 @@ class Cache:
                                   head_dim=head_dim, bits=bits, k_group=k_group, v_group=v_group,
                                   residual=residual, n_sink=n_sink, dtype=torch_dtype_code(dtype),
                                   max_tokens=max_tokens, sm_scale=sm_scale, codec=codec,
-                                  retention=retention, page_groups=page_groups, pool_pages=pool_pages)
+                                  retention=retention, page_groups=page_groups, pool_pages=pool_pages,
+                                  outliers=outliers)
         self.nbytes = _k.kvq_cache_bytes(self.cfg)
         # over-allocate by 256 bytes so the handle's buffer is 256-byte aligned
         self._buf = torch.empty(self.nbytes + 256, dtype=torch.uint8, device=self.device)
@@ -189,6 +192,23 @@ class Cache:
         ptrs = [out[n].data_ptr() if out[n].numel() else 0
                 for n in ("k_codes", "k_scale", "k_zero", "v_codes", "v_scale", "v_zero")]
         _k.kvq_export(self.handle, ptrs, _stream())
+        return out
+
+    def export_outliers(self) -> Dict[str, torch.Tensor]:
+        """Outliers of dense-and-sparse records: k_idx / k_val [B, Hkv, Lq / G, D] (token
+        within the key group, exact value), v_idx / v_val [B, Hkv, Lq, D / G_V] (channel
+        within the value group, exact value)."""
+        c = self.cfg
+        Lq = self.state()[2]
+        dev = self.device
+        nk = (c.batch, c.n_kv_heads, Lq // c.k_group, c.head_dim)
+        nv = (c.batch, c.n_kv_heads, Lq, c.head_dim // c.v_group)
+        out = dict(k_idx=torch.zeros(nk, dtype=torch.uint8, device=dev),
+                   k_val=torch.zeros(nk, dtype=torch.float32, device=dev),
+                   v_idx=torch.zeros(nv, dtype=torch.uint8, device=dev),
+                   v_val=torch.zeros(nv, dtype=torch.float32, device=dev))
+        ptrs = [out[n].data_ptr() if out[n].numel() else 0 for n in ("k_idx", "k_val", "v_idx", "v_val")]
+        _k.kvq_export_outliers(self.handle, *ptrs, _stream())
         return out
 
     def set_split_tokens(self, n: int):

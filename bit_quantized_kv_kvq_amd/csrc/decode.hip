@@ -66,6 +66,19 @@ Choice choose(const Layout& L) {
             wave = rbk * (L.D / 64) * 1024 + 2 * L.nvg * rbk * 1024;  // MStream::lds_bytes
         }
     }
+    if (L.outliers) {
+        // dense-and-sparse records: the VALU stream with one query head per kv head,
+        // and its outlier terms (LdsPlan's SPB)
+        c.fn = nullptr;
+        if (L.gqa == 1 && c.tile * c.tpg == L.G) {
+            if (L.bits == 4 && L.D == 128) c.fn = dec::decode_sp_kernel_ptr<4, 128>(c.cpl, c.tile, c.tpg);
+            if (L.bits == 2 && L.D == 128) c.fn = dec::decode_sp_kernel_ptr<2, 128>(c.cpl, c.tile, c.tpg);
+            if (L.bits == 4 && L.D == 64) c.fn = dec::decode_sp_kernel_ptr<4, 64>(c.cpl, c.tile, c.tpg);
+            if (L.bits == 2 && L.D == 64) c.fn = dec::decode_sp_kernel_ptr<2, 64>(c.cpl, c.tile, c.tpg);
+        }
+        wave = ((L.gqa * dec::kLimbs * L.D + 2 * L.gqa * L.nvg * dec::kLimbs * c.tile + 15) & ~15) +
+               4 * (L.gqa * L.G + L.gqa * L.D);
+    }
     const int wg = kWaves * L.gqa * L.D + kWaves * L.gqa * 2 + 4;  // LdsPlan::wg_floats
     c.lds = kWaves * wave + 4 * wg;
     return c;
@@ -127,6 +140,10 @@ hipError_t launch_decode(const Layout& L, const DevPtrs& P, const DecodeRequest&
     a.rec_kcodes = L.rec_kcodes;
     a.rec_vcodes = L.rec_vcodes;
     a.rec_vmeta = L.rec_vmeta;
+    a.rec_kov = L.rec_kov;
+    a.rec_koi = L.rec_koi;
+    a.rec_vov = L.rec_vov;
+    a.rec_voi = L.rec_voi;
     a.Hkv = L.Hkv;
     a.S = L.S;
     a.R = L.R;

@@ -67,6 +67,7 @@ struct DecArgs {
     unsigned* counters;  // [BH]
     int64_t ng_cap;
     int rec_bytes, rec_kcodes, rec_vcodes, rec_vmeta;
+    int rec_kov, rec_koi, rec_vov, rec_voi;  // outlier fields of dense-and-sparse records
     int dtype;  // storage dtype of q, sinks and residual (DT_*)
     int Hkv, S, R, Qf, nS, nfp, G, GV, nvg, gps, ngroups, nsplit, nsplit_cap;
     // Paged records (table non-null): rec is the page pool (pool_bytes < 4 GiB),
@@ -711,15 +712,19 @@ struct MStream {
 // ---------------------------------------------------------------------------
 // LDS carve-up (dynamic shared memory)
 // ---------------------------------------------------------------------------
-template <int D, int GQ, int TILE, int MFB = 0>
+template <int D, int GQ, int TILE, int MFB = 0, int SPB = 0>
 struct LdsPlan {
     // per wave: key digits [GQ][limb][D] bytes, then two buffers of weight digits
-    // [GQ][nvg][limb][TILE] bytes (alternating by tile); with the matrix-core
+    // [GQ][nvg][limb][TILE] bytes (alternating by tile), then the outlier
+    // corrections of dense-and-sparse records (SPB bytes); with the matrix-core
     // stream, its operand rows (MFB bytes)
-    __host__ __device__ static int wave_bytes(int nvg) {
-        if (MFB > 0) return MFB;
+    __host__ __device__ static int valu_bytes(int nvg) {
         const int b = GQ * kLimbs * D + 2 * GQ * nvg * kLimbs * TILE;
         return (b + 15) & ~15;
+    }
+    __host__ __device__ static int wave_bytes(int nvg) {
+        if (MFB > 0) return MFB;
+        return valu_bytes(nvg) + SPB;
     }
     // per workgroup: wave states and the last-arrival flag
     __host__ __device__ static int wg_floats() { return kWaves * GQ * D + kWaves * GQ * 2 + 4; }
@@ -731,7 +736,10 @@ struct LdsPlan {
 // ---------------------------------------------------------------------------
 // MF: the quantized stream runs on the matrix cores (MStream; TILE 64, TPG = G / 64,
 // NVGT value groups per token); otherwise on the VALU with the CPL / TILE / TPG map.
-template <int BITS, int D, int GQ, int CPL, int TILE, int TPG, bool MF = false, int NVGT = 1>
+// SP: dense-and-sparse records (one full-precision outlier per key channel group
+// and per value group): the VALU stream adds each outlier's difference from its
+// dequantized code to the scores and outputs.
+template <int BITS, int D, int GQ, int CPL, int TILE, int TPG, bool MF = false, int NVGT = 1, bool SP = false>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
     constexpr int LPT = D / CPL;           // key lanes per token
     constexpr int TPW = 64 / LPT;          // tokens per key wave-load
@@ -758,7 +766,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
 
     extern __shared__ __align__(16) unsigned char dsm[];
     using MS = MStream<BITS, D, GQ, TPG, NVGT>;
-    using LP = LdsPlan<D, GQ, TILE, MF ? MS::lds_bytes() : 0>;
+    static_assert(!(SP && MF), "outlier corrections run on the VALU stream");
+    // outlier corrections: the key group's score terms [GQ][G], the tile's output terms [GQ][D]
+    constexpr int SPB = SP ? 4 * (GQ * TILE * TPG + GQ * D) : 0;
+    using LP = LdsPlan<D, GQ, TILE, MF ? MS::lds_bytes() : 0, SPB>;
 
     const int split = blockIdx.x;
     const int64_t bh = blockIdx.y;
@@ -778,6 +789,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
     const int nvg = a.nvg;
 
     uint8_t* kd = dsm + wave * LP::wave_bytes(nvg);            // key digits
+    float* kc = reinterpret_cast<float*>(kd + LP::valu_bytes(nvg));  // SP: key outlier terms [GQ][G]
+    float* vc = kc + GQ * TILE * TPG;                                // SP: value outlier terms [GQ][D]
+    if constexpr (SP)
+        for (int i = lane; i < GQ * D; i += 64) vc[i] = 0.0f;
     uint8_t* pd = kd + GQ * kLimbs * D;                         // weight digits (x2)
     float* wg = reinterpret_cast<float*>(dsm + kWaves * LP::wave_bytes(nvg));
     float* s_acc = wg;                                          // [kWaves][GQ][D]
@@ -906,6 +921,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
             typename UVec<VCPL>::T v[NVL];
             u32x2 vm[U];  // value scale, zero point (fp32 bits) of (token, group gz)
             typename UVec<KM>::T ks, kz;
+            // SP only: the key outliers of the KM fold channels (values; dword of
+            // (token | code << 8) u16 fields), the value outlier of (token, group gz)
+            typename UVec<KM>::T kov;
+            uint32_t koi;
+            uint32_t vov[U], voi[U];
         };
         const int last_group = n_my_groups - 1;
         // per-lane byte offsets, the same for every tile
@@ -915,6 +935,21 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
         uint32_t vm_off[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) vm_off[u] = (uint32_t)a.rec_vmeta + ((slot * U + u) * nvg + gz) * 8;
+        // SP: outlier fields of this lane's fold channels and of its (token, group gz)
+        // items; a u16 field is read with the dword that holds it
+        const uint32_t kov_off = (uint32_t)a.rec_kov + KM * lane * 4;
+        const uint32_t koi_off = (uint32_t)a.rec_koi + ((KM * lane * 2) & ~3);
+        const int koi_shift = KM == 1 ? 16 * (lane & 1) : 0;
+        const int vitem0 = slot * U * nvg + gz;  // item of token slot * U + u: vitem0 + u * nvg
+        uint32_t vov_off[U], voi_off[U];
+        int voi_shift[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int item = vitem0 + u * nvg;
+            vov_off[u] = (uint32_t)a.rec_vov + item * 4;
+            voi_off[u] = (uint32_t)a.rec_voi + ((item * 2) & ~3);
+            voi_shift[u] = 16 * (item & 1);
+        }
 
         // Loads tile `tig` of the wave's key group j; groups past the last one
         // reload the last (the loop prefetches beyond its end).  A wave with no
@@ -932,6 +967,18 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
             if (kmeta) {  // constant at every call site
                 t.ks = bload<KM>(rs, km_off, grp);
                 t.kz = bload<KM>(rs, km_off + D * 4, grp);
+                if constexpr (SP) {
+                    t.kov = bload<KM>(rs, kov_off, grp);
+                    t.koi = bload<1>(rs, koi_off, grp);
+                }
+            }
+            if constexpr (SP) {
+                // item offsets within the group: t0 * nvg items before this tile (t0 even)
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    t.vov[u] = bload<1>(rs, vov_off[u], grp + t0 * nvg * 4);
+                    t.voi[u] = bload<1>(rs, voi_off[u], grp + t0 * nvg * 2);
+                }
             }
         };
 
@@ -964,6 +1011,26 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
                 for (int j = 0; j < KM; ++j)
                     store_digits(kd + (h * kLimbs) * D + KM * lane + j, D, (int)rintf(qt[h][j] * fs.mul));
             }
+            if constexpr (SP) {
+                // key outliers: q_c (x_c - (u_c - z_c) s_c) onto the score of token t_c
+                // of the group, through a per-wave table (zeroed, then added to; LDS
+                // keeps one wave's operations in order)
+                constexpr int GT = TILE * TPG;
+                const auto kov = whole(cur.kov);
+#pragma unroll
+                for (int h = 0; h < GQ; ++h)
+#pragma unroll
+                    for (int i = 0; i < (GT + 63) / 64; ++i)
+                        if (i * 64 + lane < GT) kc[h * GT + i * 64 + lane] = 0.0f;
+#pragma unroll
+                for (int j = 0; j < KM; ++j) {
+                    const uint32_t e = (cur.koi >> (KM == 1 ? koi_shift : 16 * j)) & 0xFFFFu;
+                    const float delta = __uint_as_float(elem(kov, j)) -
+                                        ((float)(e >> 8) - __uint_as_float(elem(kz, j))) * __uint_as_float(elem(ks, j));
+#pragma unroll
+                    for (int h = 0; h < GQ; ++h) atomicAdd(&kc[h * GT + (e & 0xFFu)], qv[h][j] * delta);
+                }
+            }
             wave_lds_sync();
 #pragma unroll
             for (int h = 0; h < GQ; ++h)
@@ -983,7 +1050,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
 
         // One tile: scores, softmax update, weight digits through LDS (buffer pb of
         // two, alternating by tile), value dot products folded into fp32.
-        auto process = [&](const Tile& cur, uint8_t* pb) __attribute__((always_inline)) {
+        auto process = [&](const Tile& cur, uint8_t* pb, int tig) __attribute__((always_inline)) {
             // ---- key scores of this slot's U tokens ----
             float sc[GQ][U];
 #pragma unroll
@@ -1019,6 +1086,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
                     sc[h][u] = group_sum<LPT>(sc[h][u]) * kinv[h] - kbias[h];
+                    if constexpr (SP) sc[h][u] += kc[h * TILE * TPG + tig * TILE + slot * U + u];
                     mt = fmaxf(mt, sc[h][u]);
                 }
                 mt = slots_max<LPT>(mt);
@@ -1041,6 +1109,13 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
                     zpart[h] = fmaf(owner ? pt[u] : 0.0f, __uint_as_float(vm.y) - (float)ZB, zpart[h]);
                     lpart[h] += chunk == 0 ? p : 0.0f;
                     mx = fmaxf(mx, pt[u]);
+                    if constexpr (SP) {
+                        // value outlier of (token, group gz): p (x - (u - z) s) onto its channel
+                        const uint32_t e = (cur.voi[u] >> voi_shift[u]) & 0xFFFFu;
+                        const float dv = __uint_as_float(cur.vov[u]) -
+                                         ((float)(e >> 8) - __uint_as_float(vm.y)) * __uint_as_float(vm.x);
+                        if (owner) atomicAdd(&vc[h * D + gz * a.GV + (int)(e & 0xFFu)], p * dv);
+                    }
                 }
                 const FixScale fs = fix_scale(group_max<64>(mx));
                 vinv[h] = fs.inv;
@@ -1103,6 +1178,17 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
                 }
 #pragma unroll
                 for (int c = 0; c < VCPL; ++c) accv[h][c] = fmaf((float)acc[c], vinv[h], accv[h][c]);
+                if constexpr (SP) {
+                    // this tile's value outlier terms of the lane's channels (one lane of
+                    // the two that hold them), then cleared for the next tile
+                    if (hb == 0) {
+#pragma unroll
+                        for (int c = 0; c < VCPL; ++c) {
+                            accv[h][c] += vc[h * D + c0v + c];
+                            vc[h * D + c0v + c] = 0.0f;
+                        }
+                    }
+                }
             }
         };
 
@@ -1255,7 +1341,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
                 load(tr[NB % NR], it * GB + NB / TPG, NB % TPG, NB % TPG == 0);
                 __builtin_amdgcn_sched_barrier(0);
                 if constexpr (B % TPG == 0) fold(tr[B % NR]);
-                process(tr[B % NR], (B & 1) ? pd1 : pd0);
+                process(tr[B % NR], (B & 1) ? pd1 : pd0, B % TPG);
                 __builtin_amdgcn_sched_barrier(0);
             };
             for (; it < n_iter; ++it) StaticFor<0, BODY>::run(step);
@@ -1267,7 +1353,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
                     constexpr int I = decltype(ic)::value;
                     if (tail > I) {
                         if constexpr (I % TPG == 0) fold(tr[I]);
-                        process(tr[I], (I & 1) ? pd1 : pd0);
+                        process(tr[I], (I & 1) ? pd1 : pd0, I % TPG);
                     }
                 };
                 StaticFor<0, NR - TPG>::run(tail_step);

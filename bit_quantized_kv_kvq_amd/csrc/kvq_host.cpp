@@ -84,6 +84,7 @@ kvq_status validate(const kvq_config* c) {
     if (c->head_dim % c->v_group != 0)
         return fail(KVQ_ERR_INVALID_ARG, "head_dim (%d) is not a multiple of v_group (%d)",
                     c->head_dim, c->v_group);
+    if (c->outliers != 0 && c->outliers != 1) return fail(KVQ_ERR_INVALID_ARG, "outliers must be 0 or 1");
     if (c->page_groups < 0 || (c->page_groups & (c->page_groups - 1)) != 0)
         return fail(KVQ_ERR_INVALID_ARG, "page_groups (%d) must be 0 or a power of two", c->page_groups);
     if (c->pool_pages < 0) return fail(KVQ_ERR_INVALID_ARG, "pool_pages must be >= 0");
@@ -150,7 +151,13 @@ Layout make_layout(const kvq_config* c) {
     L.rec_kcodes = 8 * L.D;
     L.rec_vcodes = L.rec_kcodes + L.G * L.row_bytes;
     L.rec_vmeta = L.rec_vcodes + L.G * L.row_bytes;
-    L.rec_bytes = (int)align256((size_t)L.rec_vmeta + (size_t)L.G * L.nvg * 8);
+    L.outliers = c->outliers;
+    L.rec_kov = L.rec_vmeta + L.G * L.nvg * 8;
+    L.rec_koi = L.rec_kov + 4 * L.D;
+    L.rec_vov = L.rec_koi + 2 * L.D;
+    L.rec_voi = L.rec_vov + 4 * L.G * L.nvg;
+    const int rec_end = L.outliers ? L.rec_voi + 2 * L.G * L.nvg : L.rec_kov;
+    L.rec_bytes = (int)align256((size_t)rec_end);
     size_t off = 0;
     auto take = [&](size_t bytes) {
         size_t o = off;
@@ -607,6 +614,18 @@ kvq_status kvq_export(const kvq_cache* c, uint8_t* k_codes, float* k_scale, floa
                                             c->ragged ? Ragged{c->base_len, c->len_delta} : Ragged{},
                                             (hipStream_t)stream),
                               "export");
+    if (st != KVQ_OK) return st;
+    return ok();
+}
+
+kvq_status kvq_export_outliers(const kvq_cache* c, uint8_t* k_idx, float* k_val, uint8_t* v_idx, float* v_val,
+                               void* stream) {
+    if (!c) return fail(KVQ_ERR_INVALID_ARG, "cache is NULL");
+    if (!c->L.outliers) return fail(KVQ_ERR_INVALID_ARG, "the cache keeps no outliers");
+    kvq_status st = check_hip(launch_export_outliers(c->L, c->P, c->Lq, k_idx, k_val, v_idx, v_val,
+                                                     c->ragged ? Ragged{c->base_len, c->len_delta} : Ragged{},
+                                                     (hipStream_t)stream),
+                              "export_outliers");
     if (st != KVQ_OK) return st;
     return ok();
 }

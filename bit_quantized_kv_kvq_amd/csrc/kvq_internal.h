@@ -38,6 +38,10 @@ struct Layout {
     int B, Hkv, Hq, D, bits, codec, G, GV, R, S, dtype, esize, gqa, nvg, row_bytes;
     int retention;  // kvq_retention
     int Qf;         // tokens quantized per flush: R, or W = R / 3 under log-sparse retention
+    // Dense-and-sparse records (outliers = 1): after the value metadata, the key
+    // outliers' exact values fp32 [D] and (token | code << 8) u16 [D], then the
+    // value outliers' values fp32 [G][nvg] and (channel | code << 8) u16 [G][nvg].
+    int outliers, rec_kov, rec_koi, rec_vov, rec_voi;
     int64_t BH, max_tokens, Lq_cap, ng_cap;
     int rec_bytes, rec_kcodes, rec_vcodes, rec_vmeta;
     // Paged records: P = 2^lp key groups of one sequence per page, all kv heads
@@ -217,5 +221,9 @@ hipError_t launch_dequantize(const Layout& L, const DevPtrs& P, int64_t nS, int6
 hipError_t launch_export(const Layout& L, const DevPtrs& P, int64_t Lq, uint8_t* k_codes,
                          float* k_scale, float* k_zero, uint8_t* v_codes, float* v_scale,
                          float* v_zero, Ragged rg, hipStream_t stream);
+
+// Export the outliers of dense-and-sparse records (layouts as kvq_export_outliers).
+hipError_t launch_export_outliers(const Layout& L, const DevPtrs& P, int64_t Lq, uint8_t* k_idx, float* k_val,
+                                  uint8_t* v_idx, float* v_val, Ragged rg, hipStream_t stream);
 
 }  // namespace kvq

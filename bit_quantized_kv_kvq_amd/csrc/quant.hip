@@ -173,7 +173,14 @@ struct QuantArgs {
     int codec;  // kvq_codec
     int64_t bh0;  // first slice of the launch
     RecMap rm;
+    int outliers, rec_kov, rec_koi, rec_vov, rec_voi;  // dense-and-sparse records
 };
+
+// The larger of two (magnitude, index) candidates, the lower index among equal
+// magnitudes: the outlier rule of dense-and-sparse groups.
+__device__ inline void outlier_max(float& m, int& i, float m2, int i2) {
+    if (m2 > m || (m2 == m && i2 < i)) m = m2, i = i2;
+}
 
 // key rows: dword w of token row t holds channels CPD*w + j at pack_shift(j)
 // (each field biased by code_bias)
@@ -248,7 +255,10 @@ __device__ inline void load2_f32(const void* base, int64_t elem0, float& x0, flo
 // consecutive lanes share one (token, value group), each with GV/TPI channels in
 // runs of 8 (16-byte loads), and meet by lane shuffles.  Every element is read
 // twice (min/max, then codes); the second read hits the caches.  Codes go to LDS
-// and are packed from there.
+// and are packed from there.  Dense-and-sparse groups first find each vector's
+// outlier (largest magnitude, lowest index among equals; KVQuant, per-vector
+// dense-and-sparse quantization) the same way, leave it out of the min/max, and
+// store its exact value, place and code beside the record.
 template <int DT, int BITS>
 __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
     extern __shared__ __align__(16) uint8_t smem[];
@@ -272,13 +282,36 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
         const int cp = tid % CH, part = tid / CH, c = 2 * cp;
         const int64_t e0 = (src_row0 + (int64_t)part * GP * ts) * D + c;
         const int64_t sD = (int64_t)ts * D;
+        // outliers: token of largest magnitude of each of the two channels
+        int o0 = -1, o1 = -1;
+        if (a.outliers) {
+            float a0 = -1.0f, a1 = -1.0f;
+            int i0 = 0, i1 = 0;
+            for (int t = 0; t < GP; ++t) {
+                float x0, x1;
+                load2_f32<DT>(a.src_k, e0 + t * sD, x0, x1);
+                outlier_max(a0, i0, fabsf(x0), part * GP + t);
+                outlier_max(a1, i1, fabsf(x1), part * GP + t);
+            }
+            s_mm[(part * D + c) * 2] = a0, s_mm[(part * D + c) * 2 + 1] = __int_as_float(i0);
+            s_mm[(part * D + c + 1) * 2] = a1, s_mm[(part * D + c + 1) * 2 + 1] = __int_as_float(i1);
+            __syncthreads();
+            a0 = s_mm[c * 2], i0 = __float_as_int(s_mm[c * 2 + 1]);
+            a1 = s_mm[(c + 1) * 2], i1 = __float_as_int(s_mm[(c + 1) * 2 + 1]);
+            for (int q = 1; q < P; ++q) {
+                outlier_max(a0, i0, s_mm[(q * D + c) * 2], __float_as_int(s_mm[(q * D + c) * 2 + 1]));
+                outlier_max(a1, i1, s_mm[(q * D + c + 1) * 2], __float_as_int(s_mm[(q * D + c + 1) * 2 + 1]));
+            }
+            o0 = i0 - part * GP, o1 = i1 - part * GP;  // in this thread's run, or outside it
+            __syncthreads();
+        }
         float mn0 = INFINITY, mn1 = INFINITY, mx0 = -INFINITY, mx1 = -INFINITY;
 #pragma unroll 8
         for (int t = 0; t < GP; ++t) {
             float x0, x1;
             load2_f32<DT>(a.src_k, e0 + t * sD, x0, x1);
-            mn0 = fminf(mn0, x0), mx0 = fmaxf(mx0, x0);
-            mn1 = fminf(mn1, x1), mx1 = fmaxf(mx1, x1);
+            if (t != o0) mn0 = fminf(mn0, x0), mx0 = fmaxf(mx0, x0);
+            if (t != o1) mn1 = fminf(mn1, x1), mx1 = fmaxf(mx1, x1);
         }
         s_mm[(part * D + c) * 2] = mn0, s_mm[(part * D + c) * 2 + 1] = mx0;
         s_mm[(part * D + c + 1) * 2] = mn1, s_mm[(part * D + c + 1) * 2 + 1] = mx1;
@@ -301,6 +334,23 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
             kmeta[c] = p0.s, kmeta[c + 1] = p1.s;
             kmeta[D + c] = p0.z, kmeta[D + c + 1] = p1.z;
         }
+        // the outliers' exact values, token and code: by the thread whose run holds them
+        if (a.outliers) {
+            float* kov = reinterpret_cast<float*>(rec + a.rec_kov);
+            uint16_t* koi = reinterpret_cast<uint16_t*>(rec + a.rec_koi);
+            if (o0 >= 0 && o0 < GP) {
+                float x0, x1;
+                load2_f32<DT>(a.src_k, e0 + o0 * sD, x0, x1);
+                kov[c] = x0;
+                koi[c] = (uint16_t)((part * GP + o0) | (group_code(x0, p0, qmax) << 8));
+            }
+            if (o1 >= 0 && o1 < GP) {
+                float x0, x1;
+                load2_f32<DT>(a.src_k, e0 + o1 * sD, x0, x1);
+                kov[c + 1] = x1;
+                koi[c + 1] = (uint16_t)((part * GP + o1) | (group_code(x1, p1, qmax) << 8));
+            }
+        }
     }
     __syncthreads();
     pack_rows<BITS>(s_codes, G, D, a.row_bytes, rec + a.rec_kcodes);
@@ -319,12 +369,28 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
             const bool live = i < items;
             const int t = live ? i / nvg : 0, h = live ? i % nvg : 0;
             const int64_t e0 = (src_row0 + (int64_t)t * ts) * D + (int64_t)h * GV + sub * cpt;
+            // outliers: channel (within the group) of largest magnitude
+            int ov = -1;
+            if (a.outliers) {
+                float am = -1.0f;
+                int ai = 0;
+                for (int j = 0; j < cpt; j += 8) {
+                    float f[8];
+                    load8_f32<DT>(a.src_v, e0 + j, f);
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) outlier_max(am, ai, fabsf(f[k]), sub * cpt + j + k);
+                }
+                for (int m = 1; m < tpi; m <<= 1)   // lanes of one item are consecutive
+                    outlier_max(am, ai, __shfl_xor(am, m), __shfl_xor(ai, m));
+                ov = ai;
+            }
             float mn = INFINITY, mx = -INFINITY;
             for (int j = 0; j < cpt; j += 8) {
                 float f[8];
                 load8_f32<DT>(a.src_v, e0 + j, f);
 #pragma unroll
-                for (int k = 0; k < 8; ++k) mn = fminf(mn, f[k]), mx = fmaxf(mx, f[k]);
+                for (int k = 0; k < 8; ++k)
+                    if (sub * cpt + j + k != ov) mn = fminf(mn, f[k]), mx = fmaxf(mx, f[k]);
             }
             for (int o = 1; o < tpi; o <<= 1) {   // lanes of one item are consecutive
                 mn = fminf(mn, __shfl_xor(mn, o));
@@ -346,6 +412,11 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
                 if (sub == 0) {
                     vmeta[i * 2] = p.s;
                     vmeta[i * 2 + 1] = p.z;
+                }
+                if (a.outliers && ov >= sub * cpt && ov < (sub + 1) * cpt) {
+                    const float x = load_as_f32<DT>(a.src_v, e0 - sub * cpt + ov);
+                    reinterpret_cast<float*>(rec + a.rec_vov)[i] = x;
+                    reinterpret_cast<uint16_t*>(rec + a.rec_voi)[i] = (uint16_t)(ov | (group_code(x, p, qmax) << 8));
                 }
             }
         }
@@ -371,6 +442,7 @@ struct DeqArgs {
     const int* base_len;  // sequences of different lengths (see Ragged), or null
     int delta;
     int Hkv;
+    int outliers, rec_kov, rec_koi, rec_vov, rec_voi;  // dense-and-sparse records
 };
 
 // State of slice bh: the launch's (uniform) one, or the one of its sequence's length.
@@ -419,6 +491,13 @@ __global__ __launch_bounds__(256) void dequantize_kernel(DeqArgs a) {
             const float vq = (float)value_code(a, rec, tg, c);
             kx = (kq - km[a.D + c]) * km[c];
             vx = (vq - vm[1]) * vm[0];
+            if (a.outliers) {  // outliers dequantize to their exact values
+                if ((reinterpret_cast<const uint16_t*>(rec + a.rec_koi)[c] & 0xFF) == tg)
+                    kx = reinterpret_cast<const float*>(rec + a.rec_kov)[c];
+                const int item = tg * a.nvg + c / a.GV;
+                if ((reinterpret_cast<const uint16_t*>(rec + a.rec_voi)[item] & 0xFF) == c % a.GV)
+                    vx = reinterpret_cast<const float*>(rec + a.rec_vov)[item];
+            }
         } else {
             const int64_t idx = (bh * a.R + (t - nS - Lq)) * a.D + c;
             kx = load_as_f32<DT>(a.kres, idx);
@@ -468,8 +547,41 @@ __global__ __launch_bounds__(256) void export_kernel(DeqArgs a, uint8_t* k_codes
     }
 }
 
+// The outliers of dense-and-sparse records: key outliers' token within the group
+// and exact value [BH][Lq/G][D], value outliers' channel within the group and
+// exact value [BH][Lq][nvg] (rows up to the longest sequence's; a shorter
+// slice's rows past its own are not written).
+__global__ __launch_bounds__(256) void export_outliers_kernel(DeqArgs a, uint8_t* k_idx, float* k_val,
+                                                              uint8_t* v_idx, float* v_val) {
+    const int64_t bh = blockIdx.y;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    int64_t nS_b, Lq_b, r_b;
+    deq_slice(a, bh, nS_b, Lq_b, r_b);
+    const int64_t nk = (a.Lq / a.G) * a.D;
+    for (int64_t i = i0; i < (Lq_b / a.G) * a.D; i += stride) {
+        const uint8_t* rec = rec_ptr(a.rm, bh, i / a.D);
+        const int c = (int)(i % a.D);
+        if (k_idx) k_idx[bh * nk + i] = (uint8_t)(reinterpret_cast<const uint16_t*>(rec + a.rec_koi)[c] & 0xFF);
+        if (k_val) k_val[bh * nk + i] = reinterpret_cast<const float*>(rec + a.rec_kov)[c];
+    }
+    const int64_t nv = a.Lq * a.nvg;
+    for (int64_t i = i0; i < Lq_b * a.nvg; i += stride) {
+        const int64_t t = i / a.nvg;
+        const uint8_t* rec = rec_ptr(a.rm, bh, t / a.G);
+        const int item = (int)((t % a.G) * a.nvg + i % a.nvg);
+        if (v_idx) v_idx[bh * nv + i] = (uint8_t)(reinterpret_cast<const uint16_t*>(rec + a.rec_voi)[item] & 0xFF);
+        if (v_val) v_val[bh * nv + i] = reinterpret_cast<const float*>(rec + a.rec_vov)[item];
+    }
+}
+
 DeqArgs make_deq_args(const Layout& L, const DevPtrs& P, int64_t nS, int64_t Lq, int64_t r, Ragged rg) {
     DeqArgs a;
+    a.outliers = L.outliers;
+    a.rec_kov = L.rec_kov;
+    a.rec_koi = L.rec_koi;
+    a.rec_vov = L.rec_vov;
+    a.rec_voi = L.rec_voi;
     a.base_len = rg.base_len;
     a.delta = rg.delta;
     a.Hkv = L.Hkv;
@@ -585,6 +697,11 @@ hipError_t launch_quantize(const Layout& L, const DevPtrs& P, const void* src_k,
     a.codec = L.codec;
     a.bh0 = bh0;
     a.rm = rec_map(L, P);
+    a.outliers = L.outliers;
+    a.rec_kov = L.rec_kov;
+    a.rec_koi = L.rec_koi;
+    a.rec_vov = L.rec_vov;
+    a.rec_voi = L.rec_voi;
     // codes [G][D] bytes, then the keys' partial minima/maxima [P][D][2] fp32
     const size_t lds = (((size_t)L.G * L.D + 15) & ~(size_t)15) + (size_t)(256 / (L.D / 2)) * L.D * 2 * sizeof(float);
     dim3 grid((unsigned)n_groups, (unsigned)nbh);
@@ -640,6 +757,15 @@ hipError_t launch_export(const Layout& L, const DevPtrs& P, int64_t Lq, uint8_t*
     DeqArgs a = make_deq_args(L, P, 0, Lq, 0, rg);
     dim3 grid(grid_for(Lq * L.D, 256, 4096), (unsigned)L.BH);
     export_kernel<<<grid, 256, 0, stream>>>(a, k_codes, k_scale, k_zero, v_codes, v_scale, v_zero);
+    return hipGetLastError();
+}
+
+hipError_t launch_export_outliers(const Layout& L, const DevPtrs& P, int64_t Lq, uint8_t* k_idx, float* k_val,
+                                  uint8_t* v_idx, float* v_val, Ragged rg, hipStream_t stream) {
+    if (Lq == 0) return hipSuccess;
+    DeqArgs a = make_deq_args(L, P, 0, Lq, 0, rg);
+    dim3 grid(grid_for(Lq * L.nvg, 256, 4096), (unsigned)L.BH);
+    export_outliers_kernel<<<grid, 256, 0, stream>>>(a, k_idx, k_val, v_idx, v_val);
     return hipGetLastError();
 }
 

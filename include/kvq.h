@@ -127,6 +127,8 @@ typedef struct kvq_config {
                           /* two; 0 stores each sequence's records contiguously  */
     int64_t pool_pages;   /* pages in the pool (paged records); 0 = enough for    */
                           /* every sequence at max_tokens                         */
+    int32_t outliers;     /* 1: one full-precision outlier per quantization vector */
+                          /* (dense-and-sparse groups, see kvq_export_outliers)   */
 } kvq_config;
 
 typedef struct kvq_cache kvq_cache; /* opaque host-side handle */
@@ -307,6 +309,29 @@ kvq_status kvq_seq_lengths(const kvq_cache* cache, int64_t* lens);
  * Errors: INVALID_ARG (null, b outside [0, B)), DEVICE.
  */
 kvq_status kvq_release_sequence(kvq_cache* cache, int32_t b, void* stream);
+
+/*
+ * Dense-and-sparse groups (cfg.outliers = 1; "LLM系列：KVCache量化1 KIVI…" page,
+ * section 3 "KVQuant", item (4): per-vector dense-and-sparse quantization keeps
+ * a small share of numeric outliers, e.g. 1%, unquantized in a sparse matrix).
+ * Every quantization vector (a key channel over a group of G tokens, a token's
+ * G_V value channels) has one outlier: its element of largest magnitude, the
+ * lowest index among equal magnitudes.  The vector's scale and zero point come
+ * from its other elements; every element still has a code (the outlier's
+ * clamped like any other); the outlier dequantizes to its exact value, which is
+ * what attention, kvq_dequantize and this export use.  kvq_export gives the
+ * codes and metadata as without outliers.
+ *   k_idx, k_val : device, [B, Hkv, n_quant / G, D] uint8 / fp32: the outlier's
+ *                  token within each key group (per channel) and its value.
+ *   v_idx, v_val : device, [B, Hkv, n_quant, D / G_V] uint8 / fp32: the outlier's
+ *                  channel within each value group (per token) and its value.
+ * Any output may be NULL (skipped).  Rows past a shorter sequence's own are not
+ * written.  Errors: INVALID_ARG (null cache, a cache without outliers), DEVICE.
+ * Decode attention with outliers runs for caches with one query head per kv
+ * head and 2- or 4-bit codes; other configurations are UNSUPPORTED at creation.
+ */
+kvq_status kvq_export_outliers(const kvq_cache* cache, uint8_t* k_idx, float* k_val, uint8_t* v_idx,
+                               float* v_val, void* stream);
 
 /* Host-side: free pages of the pool (0 for contiguous records).  Errors: INVALID_ARG. */
 kvq_status kvq_pool_free_pages(const kvq_cache* cache, int64_t* free_pages);

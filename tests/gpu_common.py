@@ -38,7 +38,7 @@ def make_cache(w: wl.Workload, max_tokens: int | None = None, **over):
               head_dim=w.head_dim, bits=w.bits, k_group=w.k_group, v_group=w.v_group,
               residual=w.residual, n_sink=w.n_sink, dtype=TORCH_DTYPES[w.dtype],
               max_tokens=max_tokens or w.max_tokens, device=torch.device("cuda:0"), codec=w.codec,
-              retention=1 if w.log_window else 0, page_groups=w.page_groups)
+              retention=1 if w.log_window else 0, page_groups=w.page_groups, outliers=w.outliers)
     kw.update(over)
     return Cache(**kw)
 

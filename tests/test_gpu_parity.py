@@ -31,6 +31,8 @@ SMALL = {
                                                         n_q_heads=3, prefill=1000, steps=30),
     "int8_small": wl.get("llama7b_mha_int8").replace(name="int8_small", batch=2, n_kv_heads=3,
                                                      n_q_heads=6, prefill=1000, steps=30),
+    "outliers_small": wl.get("llama7b_mha_int4_outliers").replace(name="outliers_small", batch=2, n_kv_heads=3,
+                                                                  n_q_heads=3, prefill=1000, steps=30),
     "logquant_small": wl.get("logquant_gqa_int2").replace(name="logquant_small", batch=2, n_kv_heads=2,
                                                           n_q_heads=8, prefill=1000, steps=100),
 }
@@ -147,6 +149,7 @@ FULL = {
     "llama7b_mha_int4_ragged": ([(0, 0), (4, 9), (7, 31)], None),
     "logquant_gqa_int2": ([(0, 0), (6, 5)], None),
     "llama7b_mha_int4_paged": ([(0, 0), (4, 9), (7, 31)], None),
+    "llama7b_mha_int4_outliers": ([(0, 0), (5, 21)], None),
 }
 
 

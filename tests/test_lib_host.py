@@ -49,7 +49,10 @@ def _expected_bytes(c):
     else:
         Lq_cap = c.residual * (m // c.residual)
     row = D * c.bits // 8
-    rec = al(8 * D + 2 * G * row + G * (D // c.v_group) * 8)
+    nvg = D // c.v_group
+    # with outliers: key outlier values fp32 [D] and (token | code) u16 [D], value outliers
+    # fp32 and u16 per (token, value group)
+    rec = al(8 * D + 2 * G * row + G * nvg * 8 + (6 * D + 6 * G * nvg if c.outliers else 0))
     if c.page_groups:  # a pool of pages of page_groups key groups of every kv head, and a page table
         max_pages = -(-(Lq_cap // G) // c.page_groups)
         pool = c.pool_pages or c.batch * max_pages
@@ -70,7 +73,9 @@ def _expected_bytes(c):
                                 dict(retention=kvq.KVQ_RETAIN_LOG, k_group=32, residual=96, n_sink=0),
                                 dict(page_groups=4), dict(page_groups=1, max_tokens=5000),
                                 dict(page_groups=2, pool_pages=7), dict(page_groups=8, max_tokens=100),
-                                dict(page_groups=4, retention=kvq.KVQ_RETAIN_LOG, residual=192)])
+                                dict(page_groups=4, retention=kvq.KVQ_RETAIN_LOG, residual=192),
+                                dict(outliers=1, n_q_heads=4), dict(outliers=1, n_q_heads=4, bits=2, head_dim=64),
+                                dict(outliers=1, n_q_heads=4, page_groups=2, k_group=32, residual=64)])
 def test_cache_bytes_matches_layout(kw):
     c = _cfg(**kw)
     assert kvq.kvq_cache_bytes(c) == _expected_bytes(c)
@@ -101,6 +106,9 @@ def test_cache_bytes_matches_layout(kw):
     (dict(page_groups=-2), kvq.KVQ_ERR_INVALID_ARG),
     (dict(page_groups=4, pool_pages=-1), kvq.KVQ_ERR_INVALID_ARG),
     (dict(page_groups=4, pool_pages=1 << 22), kvq.KVQ_ERR_UNSUPPORTED),       # pool above 4 GiB
+    (dict(outliers=2), kvq.KVQ_ERR_INVALID_ARG),
+    (dict(outliers=1), kvq.KVQ_ERR_UNSUPPORTED),                      # two query heads per kv head
+    (dict(outliers=1, n_q_heads=4, bits=8, v_group=64), kvq.KVQ_ERR_UNSUPPORTED),
     (dict(retention=2), kvq.KVQ_ERR_INVALID_ARG),
     (dict(retention=-1), kvq.KVQ_ERR_INVALID_ARG),
     (dict(retention=kvq.KVQ_RETAIN_LOG), kvq.KVQ_ERR_INVALID_ARG),               # R = 128 is not 3W
@@ -130,6 +138,7 @@ def test_codec_field_and_null_pointers():
     assert lib.kvq_set_timing_events(None, None, None) == kvq.KVQ_ERR_INVALID_ARG
     assert lib.kvq_release_sequence(None, 0, None) == kvq.KVQ_ERR_INVALID_ARG
     assert lib.kvq_pool_free_pages(None, None) == kvq.KVQ_ERR_INVALID_ARG
+    assert lib.kvq_export_outliers(None, None, None, None, None, None) == kvq.KVQ_ERR_INVALID_ARG
     assert lib.kvq_cache_destroy(None) == kvq.KVQ_OK
     assert kvq.kvq_last_error() == ""
 
@@ -155,5 +164,6 @@ def test_workload_configs_are_supported():
                             v_group=w.v_group, residual=w.residual, n_sink=w.n_sink,
                             dtype={"f32": 0, "bf16": 1, "f16": 2}[w.dtype],
                             max_tokens=w.max_tokens, codec=w.codec,
-                            retention=kvq.KVQ_RETAIN_LOG if w.log_window else kvq.KVQ_RETAIN_WINDOW)
+                            retention=kvq.KVQ_RETAIN_LOG if w.log_window else kvq.KVQ_RETAIN_WINDOW,
+                            page_groups=w.page_groups, outliers=w.outliers)
         assert kvq.kvq_cache_bytes(c) > 0

@@ -153,6 +153,15 @@ WORKLOADS: Dict[str, Workload] = {
         prefill=4096, steps=64, attend_after_prefill=False, seed=1002,
         k_outlier_channels=4, k_outlier_scale=8.0, prefill_min_frac=0.5,
         page_groups=4, prefill_chunk=512),
+    "llama7b_mha_int4_outliers": Workload(
+        name="llama7b_mha_int4_outliers",
+        description="the Llama-7B-shaped MHA decode with dense-and-sparse groups (one full-precision "
+                    "outlier per key channel group and per value group): B8 H32 D128, context 4096, "
+                    "bf16, INT4 G128 / G_V128, R128, 64 decode steps",
+        batch=8, n_kv_heads=32, n_q_heads=32, head_dim=128, dtype="bf16",
+        bits=4, k_group=128, v_group=128, residual=128, n_sink=0,
+        prefill=4096, steps=64, attend_after_prefill=False, seed=1002,
+        k_outlier_channels=4, k_outlier_scale=8.0, outliers=1),
     "logquant_gqa_int2": Workload(
         name="logquant_gqa_int2",
         description="Llama-3.1-8B-shaped GQA decode with LogQuant's log-sparse retention: B8, "
