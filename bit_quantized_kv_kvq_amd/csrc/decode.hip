@@ -71,10 +71,10 @@ Choice choose(const Layout& L) {
         // and its outlier terms (LdsPlan's SPB)
         c.fn = nullptr;
         if (L.gqa == 1 && c.tile * c.tpg == L.G) {
-            if (L.bits == 4 && L.D == 128) c.fn = dec::decode_sp_kernel_ptr<4, 128>(c.cpl, c.tile, c.tpg);
-            if (L.bits == 2 && L.D == 128) c.fn = dec::decode_sp_kernel_ptr<2, 128>(c.cpl, c.tile, c.tpg);
-            if (L.bits == 4 && L.D == 64) c.fn = dec::decode_sp_kernel_ptr<4, 64>(c.cpl, c.tile, c.tpg);
-            if (L.bits == 2 && L.D == 64) c.fn = dec::decode_sp_kernel_ptr<2, 64>(c.cpl, c.tile, c.tpg);
+            if (L.bits == 4 && L.D == 128) c.fn = dec::decode_sp_kernel_ptr<4, 128>(c.cpl, c.tile, c.tpg, L.nvg);
+            if (L.bits == 2 && L.D == 128) c.fn = dec::decode_sp_kernel_ptr<2, 128>(c.cpl, c.tile, c.tpg, L.nvg);
+            if (L.bits == 4 && L.D == 64) c.fn = dec::decode_sp_kernel_ptr<4, 64>(c.cpl, c.tile, c.tpg, L.nvg);
+            if (L.bits == 2 && L.D == 64) c.fn = dec::decode_sp_kernel_ptr<2, 64>(c.cpl, c.tile, c.tpg, L.nvg);
         }
         wave = ((L.gqa * dec::kLimbs * L.D + 2 * L.gqa * L.nvg * dec::kLimbs * c.tile + 15) & ~15) +
                4 * (L.gqa * L.G + L.gqa * L.D);

@@ -738,8 +738,10 @@ struct LdsPlan {
 // NVGT value groups per token); otherwise on the VALU with the CPL / TILE / TPG map.
 // SP: dense-and-sparse records (one full-precision outlier per key channel group
 // and per value group): the VALU stream adds each outlier's difference from its
-// dequantized code to the scores and outputs.
-template <int BITS, int D, int GQ, int CPL, int TILE, int TPG, bool MF = false, int NVGT = 1, bool SP = false>
+// dequantized code to the scores and outputs.  SPW: caches with one value group
+// per token, on a map with four key lanes and four tokens per slot.
+template <int BITS, int D, int GQ, int CPL, int TILE, int TPG, bool MF = false, int NVGT = 1, bool SP = false,
+          bool SPW = false>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
     constexpr int LPT = D / CPL;           // key lanes per token
     constexpr int TPW = 64 / LPT;          // tokens per key wave-load
@@ -767,6 +769,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
     extern __shared__ __align__(16) unsigned char dsm[];
     using MS = MStream<BITS, D, GQ, TPG, NVGT>;
     static_assert(!(SP && MF), "outlier corrections run on the VALU stream");
+    // One value group per token (the host's choice) and as many key lanes per token
+    // as tokens per slot: lane (slot, chunk) takes the value outlier of token
+    // slot * U + chunk, the slot's four entries loading as one vector.
+    constexpr bool SP_WIDE = SP && SPW;
+    static_assert(!SPW || (SP && U == 4 && D / CPL == 4), "wide outlier map: four lanes and four tokens per slot");
     // outlier corrections: the key group's score terms [GQ][G], the tile's output terms [GQ][D]
     constexpr int SPB = SP ? 4 * (GQ * TILE * TPG + GQ * D) : 0;
     using LP = LdsPlan<D, GQ, TILE, MF ? MS::lds_bytes() : 0, SPB>;
@@ -926,6 +933,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
             typename UVec<KM>::T kov;
             uint32_t koi;
             uint32_t vov[U], voi[U];
+            // one value group per token (NVGT == 1, U == 4): the slot's four items at once
+            u32x4 vov4;
+            u32x2 voi4;
         };
         const int last_group = n_my_groups - 1;
         // per-lane byte offsets, the same for every tile
@@ -974,10 +984,15 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
             }
             if constexpr (SP) {
                 // item offsets within the group: t0 * nvg items before this tile (t0 even)
+                if constexpr (SP_WIDE) {
+                    t.vov4 = bload<4>(rs, vov_off[0], grp + t0 * 4);
+                    t.voi4 = bload<2>(rs, voi_off[0], grp + t0 * 2);
+                } else {
 #pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    t.vov[u] = bload<1>(rs, vov_off[u], grp + t0 * nvg * 4);
-                    t.voi[u] = bload<1>(rs, voi_off[u], grp + t0 * nvg * 2);
+                    for (int u = 0; u < U; ++u) {
+                        t.vov[u] = bload<1>(rs, vov_off[u], grp + t0 * nvg * 4);
+                        t.voi[u] = bload<1>(rs, voi_off[u], grp + t0 * nvg * 2);
+                    }
                 }
             }
         };
@@ -1020,8 +1035,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
 #pragma unroll
                 for (int h = 0; h < GQ; ++h)
 #pragma unroll
-                    for (int i = 0; i < (GT + 63) / 64; ++i)
-                        if (i * 64 + lane < GT) kc[h * GT + i * 64 + lane] = 0.0f;
+                    for (int i = 0; i < (GT + 63) / 64; ++i) kc[h * GT + ((i * 64 + lane) & (GT - 1))] = 0.0f;
 #pragma unroll
                 for (int j = 0; j < KM; ++j) {
                     const uint32_t e = (cur.koi >> (KM == 1 ? koi_shift : 16 * j)) & 0xFFFFu;
@@ -1100,6 +1114,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
 
                 // ---- weights p_t s_t -> fixed-point digits in LDS ----
                 float pt[U], mx = 0.0f;
+                float pw[U];  // SP_WIDE: the tokens' softmax weights
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
                     const float p = fast_exp2(sc[h][u] - mn);
@@ -1109,13 +1124,33 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
                     zpart[h] = fmaf(owner ? pt[u] : 0.0f, __uint_as_float(vm.y) - (float)ZB, zpart[h]);
                     lpart[h] += chunk == 0 ? p : 0.0f;
                     mx = fmaxf(mx, pt[u]);
-                    if constexpr (SP) {
+                    if constexpr (SP && !SP_WIDE) {
                         // value outlier of (token, group gz): p (x - (u - z) s) onto its channel
                         const uint32_t e = (cur.voi[u] >> voi_shift[u]) & 0xFFFFu;
                         const float dv = __uint_as_float(cur.vov[u]) -
                                          ((float)(e >> 8) - __uint_as_float(vm.y)) * __uint_as_float(vm.x);
-                        if (owner) atomicAdd(&vc[h * D + gz * a.GV + (int)(e & 0xFFu)], p * dv);
+                        atomicAdd(&vc[h * D + gz * a.GV + (int)(e & 0xFFu)], owner ? p * dv : 0.0f);
                     }
+                    if constexpr (SP_WIDE) pw[u] = p;
+                }
+                if constexpr (SP_WIDE) {
+                    // this lane's token of the slot (u = chunk): its value outlier's term
+                    // (element-wise selects, no branches)
+                    float pc = pw[0];
+                    u32x2 vmc = whole(cur.vm[0]);
+                    uint32_t xv = cur.vov4.x;
+#pragma unroll
+                    for (int u = 1; u < 4; ++u) {
+                        const bool sel = chunk == u;
+                        const u32x2 vmu = whole(cur.vm[u]);
+                        pc = sel ? pw[u] : pc;
+                        vmc.x = sel ? vmu.x : vmc.x;
+                        vmc.y = sel ? vmu.y : vmc.y;
+                        xv = sel ? elem(cur.vov4, u) : xv;
+                    }
+                    const uint32_t e = ((chunk < 2 ? cur.voi4.x : cur.voi4.y) >> (16 * (chunk & 1))) & 0xFFFFu;
+                    const float dv = __uint_as_float(xv) - ((float)(e >> 8) - __uint_as_float(vmc.y)) * __uint_as_float(vmc.x);
+                    atomicAdd(&vc[h * D + (int)(e & 0xFFu)], pc * dv);
                 }
                 const FixScale fs = fix_scale(group_max<64>(mx));
                 vinv[h] = fs.inv;
@@ -1179,14 +1214,13 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
 #pragma unroll
                 for (int c = 0; c < VCPL; ++c) accv[h][c] = fmaf((float)acc[c], vinv[h], accv[h][c]);
                 if constexpr (SP) {
-                    // this tile's value outlier terms of the lane's channels (one lane of
-                    // the two that hold them), then cleared for the next tile
-                    if (hb == 0) {
+                    // this tile's value outlier terms of the lane's channels (taken by one
+                    // lane of the two that hold them), then cleared for the next tile
 #pragma unroll
-                        for (int c = 0; c < VCPL; ++c) {
-                            accv[h][c] += vc[h * D + c0v + c];
-                            vc[h * D + c0v + c] = 0.0f;
-                        }
+                    for (int c = 0; c < VCPL; ++c) {
+                        const float x = vc[h * D + c0v + c];
+                        accv[h][c] += hb == 0 ? x : 0.0f;
+                        vc[h * D + c0v + c] = 0.0f;
                     }
                 }
             }
