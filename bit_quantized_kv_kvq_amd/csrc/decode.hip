@@ -67,14 +67,16 @@ Choice choose(const Layout& L) {
         }
     }
     if (L.outliers) {
-        // dense-and-sparse records: the VALU stream with one query head per kv head,
-        // and its outlier terms (LdsPlan's SPB)
+        // dense-and-sparse records: the VALU stream (32-token tiles for several query
+        // heads per kv head, as without outliers) and its outlier terms (LdsPlan's SPB)
         c.fn = nullptr;
-        if (L.gqa == 1 && c.tile * c.tpg == L.G) {
-            if (L.bits == 4 && L.D == 128) c.fn = dec::decode_sp_kernel_ptr<4, 128>(c.cpl, c.tile, c.tpg, L.nvg);
-            if (L.bits == 2 && L.D == 128) c.fn = dec::decode_sp_kernel_ptr<2, 128>(c.cpl, c.tile, c.tpg, L.nvg);
-            if (L.bits == 4 && L.D == 64) c.fn = dec::decode_sp_kernel_ptr<4, 64>(c.cpl, c.tile, c.tpg, L.nvg);
-            if (L.bits == 2 && L.D == 64) c.fn = dec::decode_sp_kernel_ptr<2, 64>(c.cpl, c.tile, c.tpg, L.nvg);
+        c.tile = (L.gqa == 1 && L.G >= 64) ? 64 : 32;  // the VALU map (the matrix-core choice may have set 64)
+        c.tpg = L.G / c.tile;
+        if (c.tile * c.tpg == L.G) {
+            if (L.bits == 4 && L.D == 128) c.fn = dec::decode_sp_kernel_ptr<4, 128>(L.gqa, c.cpl, c.tile, c.tpg, L.nvg);
+            if (L.bits == 2 && L.D == 128) c.fn = dec::decode_sp_kernel_ptr<2, 128>(L.gqa, c.cpl, c.tile, c.tpg, L.nvg);
+            if (L.bits == 4 && L.D == 64) c.fn = dec::decode_sp_kernel_ptr<4, 64>(L.gqa, c.cpl, c.tile, c.tpg, L.nvg);
+            if (L.bits == 2 && L.D == 64) c.fn = dec::decode_sp_kernel_ptr<2, 64>(L.gqa, c.cpl, c.tile, c.tpg, L.nvg);
         }
         wave = ((L.gqa * dec::kLimbs * L.D + 2 * L.gqa * L.nvg * dec::kLimbs * c.tile + 15) & ~15) +
                4 * (L.gqa * L.G + L.gqa * L.D);

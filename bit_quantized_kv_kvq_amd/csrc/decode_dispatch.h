@@ -18,20 +18,21 @@ const void* decode_kernel_ptr(int gqa, int cpl, int tile, int tpg);
 template <int BITS, int D>
 const void* decode_mf_kernel_ptr(int gqa, int tpg, int nvg);
 
-// Dense-and-sparse records (one outlier per quantization vector), one query head
-// per kv head: kernel entry for (key channels per lane, tile, tiles per key
-// group), or nullptr.  Defined in decode_sp_b<bits>_d<head_dim>.hip.
+// Dense-and-sparse records (one outlier per quantization vector), on the VALU
+// stream: kernel entry for (query heads per kv head, key channels per lane, tile,
+// tiles per key group, value groups per token), or nullptr.  Defined in
+// decode_sp_b<bits>_d<head_dim>.hip.
 template <int BITS, int D>
-const void* decode_sp_kernel_ptr(int cpl, int tile, int tpg, int nvg);
+const void* decode_sp_kernel_ptr(int gqa, int cpl, int tile, int tpg, int nvg);
 
 template <>
-const void* decode_sp_kernel_ptr<4, 128>(int, int, int, int);
+const void* decode_sp_kernel_ptr<4, 128>(int, int, int, int, int);
 template <>
-const void* decode_sp_kernel_ptr<2, 128>(int, int, int, int);
+const void* decode_sp_kernel_ptr<2, 128>(int, int, int, int, int);
 template <>
-const void* decode_sp_kernel_ptr<4, 64>(int, int, int, int);
+const void* decode_sp_kernel_ptr<4, 64>(int, int, int, int, int);
 template <>
-const void* decode_sp_kernel_ptr<2, 64>(int, int, int, int);
+const void* decode_sp_kernel_ptr<2, 64>(int, int, int, int, int);
 
 template <>
 const void* decode_kernel_ptr<4, 128>(int, int, int, int);
@@ -125,29 +126,40 @@ const void* decode_mf_kernel_ptr<8, 64>(int, int, int);
         return nullptr;                                                              \
     }
 
-#define KVQ_DECODE_SP_CASE(BITS, D_, CPL_, TILE_, TPG_)                  \
-    if (cpl == CPL_ && tile == TILE_ && tpg == TPG_)                     \
-        return reinterpret_cast<const void*>(&decode_kernel<BITS, D_, 1, CPL_, TILE_, TPG_, false, 1, true>);
+#define KVQ_DECODE_SP_CASE(BITS, D_, GQ_, CPL_, TILE_, TPG_)                   \
+    if (gqa == GQ_ && cpl == CPL_ && tile == TILE_ && tpg == TPG_)              \
+        return reinterpret_cast<const void*>(&decode_kernel<BITS, D_, GQ_, CPL_, TILE_, TPG_, false, 1, true>);
 
 // one value group per token on the four-lane, four-token map (D 128, 32 channels per lane, 64-token tiles)
 #define KVQ_DECODE_SPW_CASE(BITS, TPG_)                                           \
-    if (nvg == 1 && cpl == 32 && tile == 64 && tpg == TPG_)                       \
+    if (gqa == 1 && nvg == 1 && cpl == 32 && tile == 64 && tpg == TPG_)           \
         return reinterpret_cast<const void*>(&decode_kernel<BITS, 128, 1, 32, 64, TPG_, false, 1, true, true>);
 
-#define KVQ_DECODE_SP_MHA(BITS, D_, CPL_)     \
-    KVQ_DECODE_SP_CASE(BITS, D_, CPL_, 32, 1) \
-    KVQ_DECODE_SP_CASE(BITS, D_, CPL_, 64, 1) \
-    KVQ_DECODE_SP_CASE(BITS, D_, CPL_, 64, 2) \
-    KVQ_DECODE_SP_CASE(BITS, D_, CPL_, 64, 4)
+#define KVQ_DECODE_SP_MHA(BITS, D_, CPL_)        \
+    KVQ_DECODE_SP_CASE(BITS, D_, 1, CPL_, 32, 1) \
+    KVQ_DECODE_SP_CASE(BITS, D_, 1, CPL_, 64, 1) \
+    KVQ_DECODE_SP_CASE(BITS, D_, 1, CPL_, 64, 2) \
+    KVQ_DECODE_SP_CASE(BITS, D_, 1, CPL_, 64, 4)
+
+// several query heads per kv head: 32-token tiles, groups of 32 to 256 tokens
+#define KVQ_DECODE_SP_GQA(BITS, D_, GQ_, CPL_)      \
+    KVQ_DECODE_SP_CASE(BITS, D_, GQ_, CPL_, 32, 1)  \
+    KVQ_DECODE_SP_CASE(BITS, D_, GQ_, CPL_, 32, 2)  \
+    KVQ_DECODE_SP_CASE(BITS, D_, GQ_, CPL_, 32, 4)  \
+    KVQ_DECODE_SP_CASE(BITS, D_, GQ_, CPL_, 32, 8)
 
 #define KVQ_DECODE_SP_TABLE_D128(BITS)                                                          \
     KVQ_DECODE_SPW_CASE(BITS, 1) KVQ_DECODE_SPW_CASE(BITS, 2) KVQ_DECODE_SPW_CASE(BITS, 4)      \
-    KVQ_DECODE_SP_MHA(BITS, 128, 32) KVQ_DECODE_SP_MHA(BITS, 128, 16)
-#define KVQ_DECODE_SP_TABLE_D64(BITS) KVQ_DECODE_SP_MHA(BITS, 64, 16)
+    KVQ_DECODE_SP_MHA(BITS, 128, 32) KVQ_DECODE_SP_MHA(BITS, 128, 16)                           \
+    KVQ_DECODE_SP_GQA(BITS, 128, 2, 16) KVQ_DECODE_SP_GQA(BITS, 128, 4, 16)                     \
+    KVQ_DECODE_SP_GQA(BITS, 128, 8, (BITS == 4 ? 8 : 16))
+#define KVQ_DECODE_SP_TABLE_D64(BITS)                                                           \
+    KVQ_DECODE_SP_MHA(BITS, 64, 16) KVQ_DECODE_SP_GQA(BITS, 64, 2, 16) KVQ_DECODE_SP_GQA(BITS, 64, 4, 16) \
+    KVQ_DECODE_SP_GQA(BITS, 64, 8, (BITS == 4 ? 8 : 16))
 
 #define KVQ_DEFINE_SP_KERNEL_PTR(BITS, D_)                                      \
     template <>                                                                 \
-    const void* decode_sp_kernel_ptr<BITS, D_>(int cpl, int tile, int tpg, int nvg) { \
+    const void* decode_sp_kernel_ptr<BITS, D_>(int gqa, int cpl, int tile, int tpg, int nvg) { \
         KVQ_DECODE_SP_TABLE_D##D_(BITS)                                         \
         return nullptr;                                                         \
     }

@@ -327,8 +327,8 @@ kvq_status kvq_release_sequence(kvq_cache* cache, int32_t b, void* stream);
  *                  channel within each value group (per token) and its value.
  * Any output may be NULL (skipped).  Rows past a shorter sequence's own are not
  * written.  Errors: INVALID_ARG (null cache, a cache without outliers), DEVICE.
- * Decode attention with outliers runs for caches with one query head per kv
- * head and 2- or 4-bit codes; other configurations are UNSUPPORTED at creation.
+ * Decode attention with outliers runs for 2- and 4-bit codes (any number of
+ * query heads per kv head); 8-bit codes with outliers are UNSUPPORTED at creation.
  */
 kvq_status kvq_export_outliers(const kvq_cache* cache, uint8_t* k_idx, float* k_val, uint8_t* v_idx,
                                float* v_val, void* stream);

@@ -87,6 +87,9 @@ VARIANTS = [
     dict(dtype="f32", head_dim=64, v_group=32, bits=2),
     dict(codec=1),
     dict(residual=96, log_window=32),                             # with log-sparse retention
+    dict(n_q_heads=4),                                            # 2 query heads per kv head
+    dict(n_q_heads=8, k_group=64, v_group=64, residual=128),      # 4, groups of two 32-token tiles
+    dict(n_q_heads=16, bits=2, k_group=128, residual=128),        # 8
 ]
 
 

@@ -75,6 +75,7 @@ def _expected_bytes(c):
                                 dict(page_groups=2, pool_pages=7), dict(page_groups=8, max_tokens=100),
                                 dict(page_groups=4, retention=kvq.KVQ_RETAIN_LOG, residual=192),
                                 dict(outliers=1, n_q_heads=4), dict(outliers=1, n_q_heads=4, bits=2, head_dim=64),
+                                dict(outliers=1), dict(outliers=1, n_q_heads=32),
                                 dict(outliers=1, n_q_heads=4, page_groups=2, k_group=32, residual=64)])
 def test_cache_bytes_matches_layout(kw):
     c = _cfg(**kw)
@@ -107,8 +108,7 @@ def test_cache_bytes_matches_layout(kw):
     (dict(page_groups=4, pool_pages=-1), kvq.KVQ_ERR_INVALID_ARG),
     (dict(page_groups=4, pool_pages=1 << 22), kvq.KVQ_ERR_UNSUPPORTED),       # pool above 4 GiB
     (dict(outliers=2), kvq.KVQ_ERR_INVALID_ARG),
-    (dict(outliers=1), kvq.KVQ_ERR_UNSUPPORTED),                      # two query heads per kv head
-    (dict(outliers=1, n_q_heads=4, bits=8, v_group=64), kvq.KVQ_ERR_UNSUPPORTED),
+    (dict(outliers=1, n_q_heads=4, bits=8, v_group=64), kvq.KVQ_ERR_UNSUPPORTED),   # 8-bit codes
     (dict(retention=2), kvq.KVQ_ERR_INVALID_ARG),
     (dict(retention=-1), kvq.KVQ_ERR_INVALID_ARG),
     (dict(retention=kvq.KVQ_RETAIN_LOG), kvq.KVQ_ERR_INVALID_ARG),               # R = 128 is not 3W
