@@ -1,5 +1,5 @@
 /*
- * kvq.h -- decode attention over a low-bit (INT4 / INT2) KV cache on MI355X.
+ * kvq.h -- decode attention over a low-bit (INT2 / INT4 / INT8) KV cache on MI355X.
  *
  * The cache follows the KIVI scheme ("LLM系列：KVCache量化1 KIVI: A Tuning-Free
  * Asymmetric 2bit Quantiz", section 1 "KIVI"):
