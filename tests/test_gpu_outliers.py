@@ -177,6 +177,24 @@ def test_adversarial_groups():
     _check(w, cache, Ks, Vs, q, out, lse)
 
 
+@pytest.mark.parametrize("kw", [VARIANTS[0], VARIANTS[2], VARIANTS[9]])
+def test_repeat_calls_are_bitwise_deterministic(kw):
+    """The outlier terms meet through LDS atomic adds; repeated calls must still agree bit for bit."""
+    require_gpu()
+    w = _w(**kw)
+    cache = make_cache(w, max_tokens=400)
+    K, V = _tokens(w, 333, 61, 2.0), _tokens(w, 333, 62)
+    cache.append(to_torch(K, w.dtype, DEV), to_torch(V, w.dtype, DEV))
+    q = to_torch(wl.random_tokens(63, (w.batch, w.n_q_heads, w.head_dim), w.dtype), w.dtype, DEV)
+    o0, l0 = cache.decode(q)
+    torch.cuda.synchronize()
+    o0, l0 = o0.clone(), l0.clone()
+    for _ in range(20):
+        o, l = cache.decode(q)
+        torch.cuda.synchronize()
+        assert torch.equal(o, o0) and torch.equal(l, l0)
+
+
 def test_outlier_export_needs_outliers():
     require_gpu()
     cache = make_cache(_w(outliers=0), max_tokens=64)
