@@ -390,12 +390,14 @@ def main():
         i = (s // L) % w.steps
         # cache state before and after this step's append: the schedule fixes it
         n = w.prefill + s // L + 1
-        _, _, r0 = slice_counts(w, n - 1)
-        # The step is one kvq_append_decode call when the token joins the residual
-        # without filling it; otherwise (a sink, a flush, or sequences of different
-        # lengths) the library appends and decodes in two launches, and the bench
-        # makes the same two calls itself so that the events bracket the decode alone.
-        fused = n > w.n_sink and r0 + 1 < w.residual and not ragged
+        # The step is one kvq_append_decode call when every sequence's token joins
+        # its residual without filling it; otherwise (a sink or a flush somewhere)
+        # the library appends and decodes in two launches, and the bench makes the
+        # same two calls itself so that the events bracket the decode alone.
+        fused = True
+        for n0 in lens0:
+            nb = n0 + s // L          # this sequence's tokens before the append
+            fused &= nb >= w.n_sink and slice_counts(w, nb)[2] + 1 < w.residual
         plan.append((fused, ctypes.c_void_p(c.handle), ctypes.c_void_p(Ks[i].data_ptr()),
                      ctypes.c_void_p(Vs[i].data_ptr()), ctypes.c_void_p(Q[i % Q.shape[0]].data_ptr()),
                      ctypes.c_void_p(c._ws_ptr), c.ws_bytes))

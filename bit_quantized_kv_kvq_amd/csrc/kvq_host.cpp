@@ -560,10 +560,19 @@ kvq_status kvq_append_decode(kvq_cache* c, const void* k, const void* v, const v
     if (!c || !k || !v || !q || !out || !ws)
         return fail(KVQ_ERR_INVALID_ARG, "cache, k, v, q, out or ws is NULL");
     const Layout& L = c->L;
-    // A token that lands in a sink slot or fills the residual (flush), or a cache
-    // whose sequences differ in length, takes the two-call path; every other token
-    // is appended inside the decode launch.
-    if (c->ragged || c->nS < L.S || c->r + 1 >= L.R) {
+    // A token that lands in a sink slot or fills the residual (flush), in any
+    // sequence, takes the two-call path; every other token is appended inside the
+    // decode launch (for sequences of different lengths, each at its own row).
+    bool fused = true;
+    if (c->ragged) {
+        for (int b = 0; b < L.B && fused; ++b) {
+            const SliceState ss = slice_state(c->len[b], L.S, L.R, L.Qf);
+            fused = c->len[b] >= L.S && ss.r + 1 < L.R;
+        }
+    } else {
+        fused = c->nS >= L.S && c->r + 1 < L.R;
+    }
+    if (!fused) {
         kvq_status st = kvq_append(c, k, v, 1, stream);
         if (st != KVQ_OK) return st;
         return kvq_decode_attention(c, q, out, lse, ws, ws_bytes, stream);
@@ -580,7 +589,8 @@ kvq_status kvq_append_decode(kvq_cache* c, const void* k, const void* v, const v
     DecodeRequest rq;
     rq.Lq = c->Lq;
     rq.nS = c->nS;
-    rq.r = c->r + 1;
+    rq.r = c->r + 1;  // the state after the append (no sequence flushes)
+    if (c->ragged) rq.rg = Ragged{c->base_len, c->len_delta + 1};
     rq.split_tokens = c->split_tokens;
     rq.num_cu = c->num_cu;
     rq.nsplit_cap = c->nsplit_cap;
@@ -591,8 +601,12 @@ kvq_status kvq_append_decode(kvq_cache* c, const void* k, const void* v, const v
     kvq_status st = check_hip(launch_decode(L, c->P, rq, q, out, lse, ws, c->sm_scale, (hipStream_t)stream),
                               "append_decode");
     if (st != KVQ_OK) return st;
-    c->r += 1;
     for (auto& n : c->len) n += 1;
+    if (c->ragged) {
+        c->len_delta += 1;
+        return (st = settle(c, false, (hipStream_t)stream)) != KVQ_OK ? st : ok();
+    }
+    c->r += 1;
     return ok();
 }
 

@@ -214,10 +214,11 @@ kvq_status kvq_decode_attention(kvq_cache* cache, const void* q, float* out, flo
  * those of kvq_append(cache, k, v, 1, stream) followed by
  * kvq_decode_attention(cache, q, out, lse, ws, ws_bytes, stream) (KIVI notes,
  * section 1: the step's key and value join the residual before the logits of
- * the grouped part and the residual are concatenated).  When the token goes to
- * the residual without filling it, the append happens inside the decode launch
- * (the kernel reads the new token from k and v and stores it into the
- * residual); a token that becomes a sink or fills the residual (a flush) takes
+ * the grouped part and the residual are concatenated).  When every sequence's
+ * token goes to its residual without filling it, the append happens inside the
+ * decode launch (the kernel reads the new tokens from k and v and stores each
+ * into its sequence's residual row, sequences of different lengths included);
+ * when some token becomes a sink or fills its residual (a flush), the step takes
  * the two-call path.
  *   k, v : device, [B, Hkv, 1, D] contiguous, in cfg.dtype, 16-byte aligned;
  *          they must stay unmodified until the enqueued work completes.

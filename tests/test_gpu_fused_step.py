@@ -97,3 +97,39 @@ def test_fused_step_validates_before_enqueueing():
     with pytest.raises(kvq.KVQError) as ei:   # capacity
         c.append_decode(K[:, :, 64:65].contiguous(), K[:, :, 64:65].contiguous(), q)
     assert ei.value.status == kvq.KVQ_ERR_CAPACITY
+
+
+@pytest.mark.parametrize("kw", [dict(n_sink=3), dict(bits=2, n_q_heads=8, k_group=64, residual=128, v_group=64),
+                                dict(residual=96, log_window=32), dict(outliers=1)])
+def test_fused_step_on_sequences_of_different_lengths(kw):
+    """Sequences of different lengths: the one-launch step (each token at its own
+    sequence's residual row) equals the two calls bit for bit, and steps in which
+    some sequence takes a sink or flushes fall back to them."""
+    require_gpu()
+    w = _w(**kw).replace(batch=4)
+    lens = [150, 2, 64, 97]
+    steps = 140
+    n = max(lens) + steps
+    log("case %s lens %s" % (kw, lens))
+    K = wl.random_tokens(41, (w.batch, w.n_kv_heads, max(lens), w.head_dim), w.dtype, 2.0)
+    V = wl.random_tokens(42, (w.batch, w.n_kv_heads, max(lens), w.head_dim), w.dtype)
+    Kd, Vd = to_torch(K, w.dtype, DEV), to_torch(V, w.dtype, DEV)
+    a, b = make_cache(w, max_tokens=n, page_groups=2), make_cache(w, max_tokens=n)
+    a.append_ragged(Kd, Vd, lens)
+    b.append_ragged(Kd, Vd, lens)
+    for s in range(steps):
+        k1 = to_torch(wl.random_tokens(1000 + s, (w.batch, w.n_kv_heads, 1, w.head_dim), w.dtype), w.dtype, DEV)
+        v1 = to_torch(wl.random_tokens(2000 + s, (w.batch, w.n_kv_heads, 1, w.head_dim), w.dtype), w.dtype, DEV)
+        q = to_torch(wl.random_tokens(3000 + s, (w.batch, w.n_q_heads, w.head_dim), w.dtype), w.dtype, DEV)
+        oa, la = a.append_decode(k1, v1, q)
+        b.append(k1, v1)
+        ob, lb = b.decode(q)
+        torch.cuda.synchronize()
+        assert a.seq_lengths() == b.seq_lengths() and a.state() == b.state()
+        assert torch.equal(oa, ob) and torch.equal(la, lb), s
+    ea, eb = export_cpu(a), export_cpu(b)
+    for name in ea:
+        np.testing.assert_array_equal(ea[name], eb[name], err_msg=name)
+    ka, va = a.dequantize()
+    kb, vb = b.dequantize()
+    assert torch.equal(ka, kb) and torch.equal(va, vb)
