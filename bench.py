@@ -51,7 +51,8 @@ DECODE_SOURCES = ["decode_impl.h", "decode_dispatch.h", "decode.hip", "kvq_inter
                   "decode_b4_d128.hip", "decode_b2_d128.hip", "decode_b4_d64.hip", "decode_b2_d64.hip",
                   "decode_mf_b4_d128.hip", "decode_mf_b2_d128.hip", "decode_mf_b4_d64.hip", "decode_mf_b2_d64.hip",
                   "decode_mf_b8_d128.hip", "decode_mf_b8_d64.hip",
-                  "decode_sp_b4_d128.hip", "decode_sp_b2_d128.hip", "decode_sp_b4_d64.hip", "decode_sp_b2_d64.hip"]
+                  "decode_sp_b4_d128.hip", "decode_sp_b2_d128.hip", "decode_sp_b4_d64.hip", "decode_sp_b2_d64.hip",
+                  "decode_mfsp_b4_d128.hip", "decode_mfsp_b2_d128.hip"]
 
 
 def algorithmic_bytes(w: wl.Workload, n_sink: int, n_quant: int, n_resid: int) -> int:

@@ -22,6 +22,7 @@ SOURCES = ["decode_mf_b4_d128.hip", "decode_mf_b2_d128.hip", "decode_mf_b4_d64.h
            "decode_mf_b8_d128.hip", "decode_mf_b8_d64.hip",
            "decode_b4_d128.hip", "decode_b2_d128.hip", "decode_b4_d64.hip", "decode_b2_d64.hip",
            "decode_sp_b4_d128.hip", "decode_sp_b2_d128.hip", "decode_sp_b4_d64.hip", "decode_sp_b2_d64.hip",
+           "decode_mfsp_b4_d128.hip", "decode_mfsp_b2_d128.hip",
            "kvq_host.cpp", "quant.hip", "decode.hip", "probe.hip"]
 
 # -packed-fp32-ops: no packed fp32 VALU instructions anywhere.

@@ -67,19 +67,29 @@ Choice choose(const Layout& L) {
         }
     }
     if (L.outliers) {
-        // dense-and-sparse records: the VALU stream (32-token tiles for several query
-        // heads per kv head, as without outliers) and its outlier terms (LdsPlan's SPB)
+        // dense-and-sparse records, with their outlier terms (LdsPlan's SPB): on the
+        // matrix cores where the plain cache would be (head_dim 128), else the VALU
+        // stream (32-token tiles for several query heads per kv head)
         c.fn = nullptr;
-        c.tile = (L.gqa == 1 && L.G >= 64) ? 64 : 32;  // the VALU map (the matrix-core choice may have set 64)
-        c.tpg = L.G / c.tile;
-        if (c.tile * c.tpg == L.G) {
-            if (L.bits == 4 && L.D == 128) c.fn = dec::decode_sp_kernel_ptr<4, 128>(L.gqa, c.cpl, c.tile, c.tpg, L.nvg);
-            if (L.bits == 2 && L.D == 128) c.fn = dec::decode_sp_kernel_ptr<2, 128>(L.gqa, c.cpl, c.tile, c.tpg, L.nvg);
-            if (L.bits == 4 && L.D == 64) c.fn = dec::decode_sp_kernel_ptr<4, 64>(L.gqa, c.cpl, c.tile, c.tpg, L.nvg);
-            if (L.bits == 2 && L.D == 64) c.fn = dec::decode_sp_kernel_ptr<2, 64>(L.gqa, c.cpl, c.tile, c.tpg, L.nvg);
+        const int spb = 4 * (L.gqa * L.G + L.gqa * L.D);
+        if (L.gqa >= 2 && L.G >= 64 && L.G <= 256 && L.GV >= 64 && L.D == 128 && L.bits != 8) {
+            c.tile = 64;
+            c.tpg = L.G / 64;
+            if (L.bits == 4) c.fn = dec::decode_mfsp_kernel_ptr<4>(L.gqa, c.tpg, L.nvg);
+            if (L.bits == 2) c.fn = dec::decode_mfsp_kernel_ptr<2>(L.gqa, c.tpg, L.nvg);
+            const int rbk = (L.gqa + 3) / 4;
+            wave = rbk * (L.D / 64) * 1024 + 2 * L.nvg * rbk * 1024 + spb;  // MStream::lds_bytes + SPB
+        } else {
+            c.tile = (L.gqa == 1 && L.G >= 64) ? 64 : 32;  // the VALU map (the matrix-core choice may have set 64)
+            c.tpg = L.G / c.tile;
+            if (c.tile * c.tpg == L.G) {
+                if (L.bits == 4 && L.D == 128) c.fn = dec::decode_sp_kernel_ptr<4, 128>(L.gqa, c.cpl, c.tile, c.tpg, L.nvg);
+                if (L.bits == 2 && L.D == 128) c.fn = dec::decode_sp_kernel_ptr<2, 128>(L.gqa, c.cpl, c.tile, c.tpg, L.nvg);
+                if (L.bits == 4 && L.D == 64) c.fn = dec::decode_sp_kernel_ptr<4, 64>(L.gqa, c.cpl, c.tile, c.tpg, L.nvg);
+                if (L.bits == 2 && L.D == 64) c.fn = dec::decode_sp_kernel_ptr<2, 64>(L.gqa, c.cpl, c.tile, c.tpg, L.nvg);
+            }
+            wave = ((L.gqa * dec::kLimbs * L.D + 2 * L.gqa * L.nvg * dec::kLimbs * c.tile + 15) & ~15) + spb;
         }
-        wave = ((L.gqa * dec::kLimbs * L.D + 2 * L.gqa * L.nvg * dec::kLimbs * c.tile + 15) & ~15) +
-               4 * (L.gqa * L.G + L.gqa * L.D);
     }
     const int wg = kWaves * L.gqa * L.D + kWaves * L.gqa * 2 + 4;  // LdsPlan::wg_floats
     c.lds = kWaves * wave + 4 * wg;

@@ -25,6 +25,16 @@ const void* decode_mf_kernel_ptr(int gqa, int tpg, int nvg);
 template <int BITS, int D>
 const void* decode_sp_kernel_ptr(int gqa, int cpl, int tile, int tpg, int nvg);
 
+// Dense-and-sparse records on the matrix cores (several query heads per kv head,
+// head_dim 128): entry for (query heads per kv head, 64-token tiles per key group,
+// value groups per token), or nullptr.  Defined in decode_mfsp_b<bits>_d128.hip.
+template <int BITS>
+const void* decode_mfsp_kernel_ptr(int gqa, int tpg, int nvg);
+template <>
+const void* decode_mfsp_kernel_ptr<4>(int, int, int);
+template <>
+const void* decode_mfsp_kernel_ptr<2>(int, int, int);
+
 template <>
 const void* decode_sp_kernel_ptr<4, 128>(int, int, int, int, int);
 template <>
@@ -156,6 +166,19 @@ const void* decode_mf_kernel_ptr<8, 64>(int, int, int);
 #define KVQ_DECODE_SP_TABLE_D64(BITS)                                                           \
     KVQ_DECODE_SP_MHA(BITS, 64, 16) KVQ_DECODE_SP_GQA(BITS, 64, 2, 16) KVQ_DECODE_SP_GQA(BITS, 64, 4, 16) \
     KVQ_DECODE_SP_GQA(BITS, 64, 8, (BITS == 4 ? 8 : 16))
+
+#define KVQ_DECODE_MFSP_CASE(BITS, GQ_, TPG_, NVG_)                      \
+    if (gqa == GQ_ && tpg == TPG_ && nvg == NVG_)                        \
+        return reinterpret_cast<const void*>(&decode_kernel<BITS, 128, GQ_, 16, 64, TPG_, true, NVG_, true>);
+#define KVQ_DECODE_MFSP_TPG(BITS, GQ_, NVG_) \
+    KVQ_DECODE_MFSP_CASE(BITS, GQ_, 1, NVG_) KVQ_DECODE_MFSP_CASE(BITS, GQ_, 2, NVG_) KVQ_DECODE_MFSP_CASE(BITS, GQ_, 4, NVG_)
+#define KVQ_DEFINE_MFSP_KERNEL_PTR(BITS)                                                      \
+    template <>                                                                               \
+    const void* decode_mfsp_kernel_ptr<BITS>(int gqa, int tpg, int nvg) {                     \
+        KVQ_DECODE_MFSP_TPG(BITS, 2, 1) KVQ_DECODE_MFSP_TPG(BITS, 4, 1) KVQ_DECODE_MFSP_TPG(BITS, 8, 1) \
+        KVQ_DECODE_MFSP_TPG(BITS, 2, 2) KVQ_DECODE_MFSP_TPG(BITS, 4, 2) KVQ_DECODE_MFSP_TPG(BITS, 8, 2) \
+        return nullptr;                                                                       \
+    }
 
 #define KVQ_DEFINE_SP_KERNEL_PTR(BITS, D_)                                      \
     template <>                                                                 \

@@ -371,7 +371,12 @@ __device__ __forceinline__ uint32_t digits256(int n) { return ((uint32_t)(n + 32
 // exact recombination of digit rows 0..2 of a product (row 3 is zero)
 __device__ __forceinline__ int horner256(const i32x4& r) { return (r[2] * 256 + r[1]) * 256 + r[0]; }
 
-template <int BITS, int D, int GQ, int TPG, int NVG>
+// SP: dense-and-sparse records.  The outliers' differences from their codes'
+// values go through per-wave LDS tables as on the VALU stream: key terms onto the
+// scores of the group's tokens (once per group), value terms onto the channels of
+// the tile's outputs.  A lane owns one (head, token) pair of each score product
+// and one (head, channel) pair of each output accumulator.
+template <int BITS, int D, int GQ, int TPG, int NVG, bool SP = false>
 struct MStream {
     static constexpr int TM = 64;               // tokens per tile
     static constexpr int NSB = TM / 16;         // key products per tile and row block
@@ -404,7 +409,18 @@ struct MStream {
         u32x4 v[NVB][VBB];
         typename UVec<2 * NVG>::T vm[NSB];  // (scale, zero) of each value group of token 16 sb + l % 16
         typename UVec<KM>::T ks, kz;
+        // SP only: key outliers of the KM fold channels (values; dword of u16 fields),
+        // value outliers of token 16 sb + l % 16 (values; dword of its groups' u16 fields)
+        typename UVec<KM>::T kov;
+        uint32_t koi;
+        typename UVec<NVG>::T vov[NSB];
+        uint32_t voi[NSB];
     };
+    static constexpr int GT = TM * TPG;  // tokens per key group
+    float* kc;  // SP: key outlier terms [GQ][GT]
+    float* vc;  // SP: value outlier terms [GQ][D]
+    uint32_t kov_off, koi_off, vov_off, voi_off;
+    int koi_shift, voi_shift;
 
     __amdgpu_buffer_rsrc_t rs;
     GroupAddr ga;
@@ -430,6 +446,14 @@ struct MStream {
         km_off = KM * lane * 4;
         ak_lds = lds;
         av_lds = lds + AK_BYTES;
+        kc = reinterpret_cast<float*>(lds + lds_bytes());
+        vc = kc + GQ * GT;
+        kov_off = (uint32_t)a.rec_kov + KM * lane * 4;
+        koi_off = (uint32_t)a.rec_koi + ((KM * lane * 2) & ~3);
+        koi_shift = KM == 1 ? 16 * (lane & 1) : 0;
+        vov_off = (uint32_t)a.rec_vov + j * NVG * 4;
+        voi_off = (uint32_t)a.rec_voi + ((j * NVG * 2) & ~3);
+        voi_shift = NVG == 1 ? 16 * (j & 1) : 0;
         // padding rows (digit row 3 of every head, absent heads) stay zero
         for (int i = lane * 16; i < lds_bytes(); i += 64 * 16) *reinterpret_cast<u32x4*>(lds + i) = u32x4{0u, 0u, 0u, 0u};
         wave_lds_sync();
@@ -462,6 +486,17 @@ struct MStream {
         if (kmeta) {  // constant at every call site
             tt.ks = bload<KM>(rs, km_off, grp);
             tt.kz = bload<KM>(rs, km_off + D * 4, grp);
+            if constexpr (SP) {
+                tt.kov = bload<KM>(rs, kov_off, grp);
+                tt.koi = bload<1>(rs, koi_off, grp);
+            }
+        }
+        if constexpr (SP) {
+#pragma unroll
+            for (int sb = 0; sb < NSB; ++sb) {
+                tt.vov[sb] = bload<NVG>(rs, vov_off, grp + (t0 + 16 * sb) * NVG * 4);
+                tt.voi[sb] = bload<1>(rs, voi_off, grp + (t0 + 16 * sb) * NVG * 2);
+            }
         }
     }
 
@@ -507,6 +542,22 @@ struct MStream {
                 dst[128] = (uint8_t)(d >> 16);
             }
         }
+        if constexpr (SP) {
+            // key outliers: q_c (x_c - (u_c - z_c) s_c) onto the score of token t_c
+            const auto kov = whole(cur.kov);
+#pragma unroll
+            for (int h = 0; h < GQ; ++h)
+#pragma unroll
+                for (int i = 0; i < (GT + 63) / 64; ++i) kc[h * GT + ((i * 64 + lane) & (GT - 1))] = 0.0f;
+#pragma unroll
+            for (int j = 0; j < KM; ++j) {
+                const uint32_t e = (cur.koi >> (KM == 1 ? koi_shift : 16 * j)) & 0xFFFFu;
+                const float delta = __uint_as_float(elem(kov, j)) -
+                                    ((float)(e >> 8) - __uint_as_float(elem(kz, j))) * __uint_as_float(elem(ks, j));
+#pragma unroll
+                for (int h = 0; h < GQ; ++h) atomicAdd(&kc[h * GT + (int)(e & 0xFFu)], qv[h][j] * delta);
+            }
+        }
         wave_lds_sync();
         const int hs = lane >> 4;
 #pragma unroll
@@ -550,7 +601,7 @@ struct MStream {
 
     // One tile: scores on the matrix cores, softmax update, weight digits through
     // LDS (buffer `buf` of two), value products folded into fp32.
-    __device__ __forceinline__ void process(const Tile& cur, int buf) {
+    __device__ __forceinline__ void process(const Tile& cur, int buf, int tig) {
         const i32x4 zero = {0, 0, 0, 0};
         float sc[RBK][NSB];
 #pragma unroll
@@ -573,6 +624,10 @@ struct MStream {
 #pragma unroll
                 for (int kk = 1; kk < NKK; ++kk) r = mfma_i8(ak[rb][kk], bk[kk], r);
                 sc[rb][sb] = combine(r) * kinv_l[rb] - kbias_l[rb];
+                if constexpr (SP) {  // rows of absent heads read a valid head's term, unused
+                    const int head = min(4 * rb + (lane >> 4), GQ - 1);
+                    sc[rb][sb] += kc[head * GT + tig * TM + 16 * sb + (lane & 15)];
+                }
             }
         }
         uint8_t* avb = av_lds + buf * AV_BYTES;
@@ -607,6 +662,17 @@ struct MStream {
                     w[sb] = p[sb] * __uint_as_float(elem(vmw, 2 * g));
                     z2[rb][g] = fmaf(w[sb], __uint_as_float(elem(vmw, 2 * g + 1)) - ZOFF, z2[rb][g]);
                     wmax = fmaxf(wmax, w[sb]);
+                    if constexpr (SP) {
+                        // value outlier of (token 16 sb + l % 16, group g): p (x - (u - z) s) onto
+                        // its channel; rows of absent heads add nothing
+                        const int head = 4 * rb + (lane >> 4);
+                        const uint32_t e = (cur.voi[sb] >> (NVG == 1 ? voi_shift : 16 * g)) & 0xFFFFu;
+                        const float dv = __uint_as_float(elem(whole(cur.vov[sb]), g)) -
+                                         ((float)(e >> 8) - __uint_as_float(elem(vmw, 2 * g + 1))) *
+                                             __uint_as_float(elem(vmw, 2 * g));
+                        atomicAdd(&vc[min(head, GQ - 1) * D + g * (D / NVG) + (int)(e & 0xFFu)],
+                                  head < GQ ? p[sb] * dv : 0.0f);
+                    }
                 }
                 const FixScale fs = fix_scale(group_max<16>(wmax));
                 vinv[rb][g] = fs.inv;
@@ -645,6 +711,20 @@ struct MStream {
                 }
             }
         }
+        if constexpr (SP) {
+            // this tile's value outlier terms of the lane's (head, channel) accumulators,
+            // then cleared for the next tile (rows of absent heads read a valid head's)
+#pragma unroll
+            for (int rb = 0; rb < RBK; ++rb) {
+                const int head = min(4 * rb + (lane >> 4), GQ - 1);
+#pragma unroll
+                for (int n = 0; n < NVM; ++n) {
+                    float* q = &vc[head * D + 64 * (n / 4) + 4 * (lane & 15) + (n % 4)];
+                    acc2[rb][n] += *q;
+                    *q = 0.0f;
+                }
+            }
+        }
     }
 
     // The wave's key groups, through the tile ring (as in the VALU stream).
@@ -657,7 +737,7 @@ struct MStream {
             load(t[NB % NRM], it * GB + NB / TPG, NB % TPG, NB % TPG == 0);
             __builtin_amdgcn_sched_barrier(0);
             if constexpr (B % TPG == 0) fold(t[B % NRM], qv);
-            process(t[B % NRM], B & 1);
+            process(t[B % NRM], B & 1, B % TPG);
             __builtin_amdgcn_sched_barrier(0);
         };
         for (; it < n_iter; ++it) StaticFor<0, BODY>::run(step);
@@ -667,7 +747,7 @@ struct MStream {
                 constexpr int I = decltype(ic)::value;
                 if (tail > I) {
                     if constexpr (I % TPG == 0) fold(t[I], qv);
-                    process(t[I], I & 1);
+                    process(t[I], I & 1, I % TPG);
                 }
             };
             StaticFor<0, NRM - TPG>::run(tail_step);
@@ -723,7 +803,7 @@ struct LdsPlan {
         return (b + 15) & ~15;
     }
     __host__ __device__ static int wave_bytes(int nvg) {
-        if (MFB > 0) return MFB;
+        if (MFB > 0) return MFB + SPB;
         return valu_bytes(nvg) + SPB;
     }
     // per workgroup: wave states and the last-arrival flag
@@ -767,8 +847,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
     static_assert(TILE % 32 == 0 && (U == 2 || U == 4 || U == 8), "digit runs of 2, 4 or 8 bytes");
 
     extern __shared__ __align__(16) unsigned char dsm[];
-    using MS = MStream<BITS, D, GQ, TPG, NVGT>;
-    static_assert(!(SP && MF), "outlier corrections run on the VALU stream");
+    using MS = MStream<BITS, D, GQ, TPG, NVGT, SP>;
     // One value group per token (the host's choice) and as many key lanes per token
     // as tokens per slot: lane (slot, chunk) takes the value outlier of token
     // slot * U + chunk, the slot's four entries loading as one vector.
@@ -796,7 +875,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
     const int nvg = a.nvg;
 
     uint8_t* kd = dsm + wave * LP::wave_bytes(nvg);            // key digits
-    float* kc = reinterpret_cast<float*>(kd + LP::valu_bytes(nvg));  // SP: key outlier terms [GQ][G]
+    // SP: key outlier terms [GQ][G] (the matrix-core stream's own copy of this pointer is the same)
+    float* kc = reinterpret_cast<float*>(kd + (MF ? MS::lds_bytes() : LP::valu_bytes(nvg)));
     float* vc = kc + GQ * TILE * TPG;                                // SP: value outlier terms [GQ][D]
     if constexpr (SP)
         for (int i = lane; i < GQ * D; i += 64) vc[i] = 0.0f;

@@ -90,6 +90,11 @@ VARIANTS = [
     dict(n_q_heads=4),                                            # 2 query heads per kv head
     dict(n_q_heads=8, k_group=64, v_group=64, residual=128),      # 4, groups of two 32-token tiles
     dict(n_q_heads=16, bits=2, k_group=128, residual=128),        # 8
+    # several query heads per kv head with G, G_V >= 64: the matrix cores
+    dict(n_q_heads=4, k_group=64, v_group=64, residual=128),              # g = 2
+    dict(n_q_heads=8, k_group=128, v_group=128, residual=128),            # g = 4, two tiles per group
+    dict(n_q_heads=8, bits=2, k_group=256, v_group=64, residual=256),     # two value groups, four tiles
+    dict(n_q_heads=16, bits=2, k_group=64, v_group=64, residual=64, n_sink=2),  # g = 8
 ]
 
 
@@ -107,7 +112,7 @@ def test_bulk_append_against_oracle(kw, n):
     _check(w, cache, K, V, q, out, lse)
 
 
-@pytest.mark.parametrize("kw", [VARIANTS[0], VARIANTS[2]])
+@pytest.mark.parametrize("kw", [VARIANTS[0], VARIANTS[2], VARIANTS[13]])
 def test_steps_and_ragged_paged(kw):
     require_gpu()
     w = _w(**kw).replace(batch=3)
@@ -177,7 +182,7 @@ def test_adversarial_groups():
     _check(w, cache, Ks, Vs, q, out, lse)
 
 
-@pytest.mark.parametrize("kw", [VARIANTS[0], VARIANTS[2], VARIANTS[9]])
+@pytest.mark.parametrize("kw", [VARIANTS[0], VARIANTS[2], VARIANTS[9], VARIANTS[12]])
 def test_repeat_calls_are_bitwise_deterministic(kw):
     """The outlier terms meet through LDS atomic adds; repeated calls must still agree bit for bit."""
     require_gpu()

@@ -150,6 +150,7 @@ FULL = {
     "logquant_gqa_int2": ([(0, 0), (6, 5)], None),
     "llama7b_mha_int4_paged": ([(0, 0), (4, 9), (7, 31)], None),
     "llama7b_mha_int4_outliers": ([(0, 0), (5, 21)], None),
+    "gqa_32k_int4_outliers": ([(0, 0), (15, 7)], None),
 }
 
 

@@ -162,6 +162,15 @@ WORKLOADS: Dict[str, Workload] = {
         bits=4, k_group=128, v_group=128, residual=128, n_sink=0,
         prefill=4096, steps=64, attend_after_prefill=False, seed=1002,
         k_outlier_channels=4, k_outlier_scale=8.0, outliers=1),
+    "gqa_32k_int4_outliers": Workload(
+        name="gqa_32k_int4_outliers",
+        description="the GQA decode with dense-and-sparse groups (one full-precision outlier per key "
+                    "channel group and per value group): B16, 32 query heads on 8 KV heads, D128, "
+                    "context 32768, bf16, INT4 G128 / G_V128, R128, 16 decode steps",
+        batch=16, n_kv_heads=8, n_q_heads=32, head_dim=128, dtype="bf16",
+        bits=4, k_group=128, v_group=128, residual=128, n_sink=0,
+        prefill=32768, steps=16, attend_after_prefill=False, seed=1004,
+        k_offset_range=3.0, outliers=1),
     "logquant_gqa_int2": Workload(
         name="logquant_gqa_int2",
         description="Llama-3.1-8B-shaped GQA decode with LogQuant's log-sparse retention: B8, "
