@@ -632,6 +632,8 @@ struct MStream {
         }
         uint8_t* avb = av_lds + buf * AV_BYTES;
         float vinv[RBK][NVG];
+        float sp_val[SP ? RBK : 1][SP ? NVG : 1][SP ? NSB : 1];  // SP: value outlier terms and places
+        int sp_idx[SP ? RBK : 1][SP ? NVG : 1][SP ? NSB : 1];
         const int tok = lane & 15, row = 4 * (lane >> 4);
 #pragma unroll
         for (int rb = 0; rb < RBK; ++rb) {
@@ -664,14 +666,15 @@ struct MStream {
                     wmax = fmaxf(wmax, w[sb]);
                     if constexpr (SP) {
                         // value outlier of (token 16 sb + l % 16, group g): p (x - (u - z) s) onto
-                        // its channel; rows of absent heads add nothing
+                        // its channel, added after the weights are read back; rows of absent heads
+                        // add nothing
                         const int head = 4 * rb + (lane >> 4);
                         const uint32_t e = (cur.voi[sb] >> (NVG == 1 ? voi_shift : 16 * g)) & 0xFFFFu;
                         const float dv = __uint_as_float(elem(whole(cur.vov[sb]), g)) -
                                          ((float)(e >> 8) - __uint_as_float(elem(vmw, 2 * g + 1))) *
                                              __uint_as_float(elem(vmw, 2 * g));
-                        atomicAdd(&vc[min(head, GQ - 1) * D + g * (D / NVG) + (int)(e & 0xFFu)],
-                                  head < GQ ? p[sb] * dv : 0.0f);
+                        sp_val[rb][g][sb] = head < GQ ? p[sb] * dv : 0.0f;
+                        sp_idx[rb][g][sb] = min(head, GQ - 1) * D + g * (D / NVG) + (int)(e & 0xFFu);
                     }
                 }
                 const FixScale fs = fix_scale(group_max<16>(wmax));
@@ -693,6 +696,16 @@ struct MStream {
 #pragma unroll
             for (int rb = 0; rb < RBK; ++rb)
                 av[g][rb] = *reinterpret_cast<const i32x4*>(avb + ((g * RBK + rb) * 16 + (lane & 15)) * 64 + (lane >> 4) * 16);
+        if constexpr (SP) {
+            // after the weights' reads (LDS keeps a wave's operations in order): the atomics'
+            // latency overlaps the value products, and the read-back below comes after them
+#pragma unroll
+            for (int rb = 0; rb < RBK; ++rb)
+#pragma unroll
+                for (int g = 0; g < NVG; ++g)
+#pragma unroll
+                    for (int sb = 0; sb < NSB; ++sb) atomicAdd(&vc[sp_idx[rb][g][sb]], sp_val[rb][g][sb]);
+        }
 #pragma unroll
         for (int m = 0; m < NVB; ++m) {
             u32x4 w[VBB];
