@@ -25,6 +25,7 @@ WsLayout ws_layout(const Layout& L, int cap) {
 struct Choice {
     const void* fn;
     int cpl, tile, tpg, lds;
+    int occ;  // workgroups per CU the kernel is planned for
 };
 
 Choice choose(const Layout& L) {
@@ -38,6 +39,7 @@ Choice choose(const Layout& L) {
     else
         c.cpl = 16;
     c.fn = nullptr;
+    c.occ = 1;
     if (c.tile * c.tpg == L.G) {
         if (L.bits == 4 && L.D == 128) c.fn = dec::decode_kernel_ptr<4, 128>(L.gqa, c.cpl, c.tile, c.tpg);
         if (L.bits == 2 && L.D == 128) c.fn = dec::decode_kernel_ptr<2, 128>(L.gqa, c.cpl, c.tile, c.tpg);
@@ -60,6 +62,7 @@ Choice choose(const Layout& L) {
         if (L.bits == 8 && L.D == 64) mf = dec::decode_mf_kernel_ptr<8, 64>(L.gqa, tpg, L.nvg);
         if (mf != nullptr) {
             c.fn = mf;
+            c.occ = dec::mf_two_waves(L.bits, L.gqa, false) ? 2 : 1;
             c.tile = 64;
             c.tpg = tpg;
             const int rbk = (L.gqa + 3) / 4;
@@ -71,6 +74,7 @@ Choice choose(const Layout& L) {
         // matrix cores where the plain cache would be (head_dim 128), else the VALU
         // stream (32-token tiles for several query heads per kv head)
         c.fn = nullptr;
+        c.occ = 1;
         const int spb = 4 * (L.gqa * L.G + L.gqa * L.D);
         if (L.gqa >= 2 && L.G >= 64 && L.G <= 256 && L.GV >= 64 && L.D == 128 && L.bits != 8) {
             c.tile = 64;
@@ -108,11 +112,11 @@ hipError_t launch_decode(const Layout& L, const DevPtrs& P, const DecodeRequest&
     if (!ch.fn) return hipErrorInvalidValue;
     const WsLayout w = ws_layout(L, rq.nsplit_cap);
 
-    // Split plan: about one workgroup per CU, whole key groups per split, a
-    // multiple of the wave count when splits are long.  Long per-wave streams
-    // beat more workgroups per CU: every stream pays a start-up latency and the
-    // split combine, while the prefetch ring already covers the memory latency
-    // at one workgroup per CU.
+    // Split plan: about one workgroup per CU (two for the streams that run two
+    // waves per SIMD), whole key groups per split, a multiple of the wave count
+    // when splits are long.  Long per-wave streams beat more workgroups per CU:
+    // every stream pays a start-up latency and the split combine, while the
+    // prefetch ring already covers the memory latency at one workgroup per CU.
     const int64_t ng = rq.Lq / L.G;
     const int cap_q = rq.nsplit_cap;
     int64_t gps = 1;
@@ -121,7 +125,7 @@ hipError_t launch_decode(const Layout& L, const DevPtrs& P, const DecodeRequest&
     } else if (ng > 0) {
         // Sequences of different lengths: planned for the longest (splitting by
         // the total over all slices measured slower: more workgroups and combines).
-        const int64_t slots = rq.num_cu;
+        const int64_t slots = (int64_t)rq.num_cu * ch.occ;
         gps = (L.BH * ng + slots - 1) / slots;
         if (gps > kWaves) gps = (gps + kWaves - 1) / kWaves * kWaves;
     }
