@@ -62,7 +62,7 @@ Choice choose(const Layout& L) {
         if (L.bits == 8 && L.D == 64) mf = dec::decode_mf_kernel_ptr<8, 64>(L.gqa, tpg, L.nvg);
         if (mf != nullptr) {
             c.fn = mf;
-            c.occ = dec::mf_two_waves(L.bits, L.gqa, false) ? 2 : 1;
+            c.occ = dec::two_waves(true, L.bits, L.gqa, false) ? 2 : 1;
             c.tile = 64;
             c.tpg = tpg;
             const int rbk = (L.gqa + 3) / 4;
@@ -79,6 +79,7 @@ Choice choose(const Layout& L) {
         if (L.gqa >= 2 && L.G >= 64 && L.G <= 256 && L.GV >= 64 && L.D == 128 && L.bits != 8) {
             c.tile = 64;
             c.tpg = L.G / 64;
+            c.occ = dec::two_waves(true, L.bits, L.gqa, true) ? 2 : 1;
             if (L.bits == 4) c.fn = dec::decode_mfsp_kernel_ptr<4>(L.gqa, c.tpg, L.nvg);
             if (L.bits == 2) c.fn = dec::decode_mfsp_kernel_ptr<2>(L.gqa, c.tpg, L.nvg);
             const int rbk = (L.gqa + 3) / 4;
@@ -87,6 +88,7 @@ Choice choose(const Layout& L) {
             c.tile = (L.gqa == 1 && L.G >= 64) ? 64 : 32;  // the VALU map (the matrix-core choice may have set 64)
             c.tpg = L.G / c.tile;
             if (c.tile * c.tpg == L.G) {
+                c.occ = dec::two_waves(false, L.bits, L.gqa, true) ? 2 : 1;
                 if (L.bits == 4 && L.D == 128) c.fn = dec::decode_sp_kernel_ptr<4, 128>(L.gqa, c.cpl, c.tile, c.tpg, L.nvg);
                 if (L.bits == 2 && L.D == 128) c.fn = dec::decode_sp_kernel_ptr<2, 128>(L.gqa, c.cpl, c.tile, c.tpg, L.nvg);
                 if (L.bits == 4 && L.D == 64) c.fn = dec::decode_sp_kernel_ptr<4, 64>(L.gqa, c.cpl, c.tile, c.tpg, L.nvg);

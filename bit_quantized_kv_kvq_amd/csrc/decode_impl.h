@@ -376,13 +376,17 @@ __device__ __forceinline__ int horner256(const i32x4& r) { return (r[2] * 256 + 
 // scores of the group's tokens (once per group), value terms onto the channels of
 // the tile's outputs.  A lane owns one (head, token) pair of each score product
 // and one (head, channel) pair of each output accumulator.
-// Matrix-core streams of 2-bit codes with at most four query heads per kv head
-// fit in 256 registers with a ring of two tiles, and then run two waves per SIMD
-// (two workgroups per CU): the second wave hides the per-tile latency of the
-// first (reductions, LDS round trips), which bounds these streams rather than
-// HBM.  Wider codes are HBM-bound and keep one wave per SIMD with a ring of four
-// tiles; eight query heads per kv head would spill at 256 registers.
-__host__ __device__ constexpr bool mf_two_waves(int bits, int gq, bool sp) { return bits == 2 && gq <= 4 && !sp; }
+// Streams that run two waves per SIMD (two workgroups per CU) with a ring of two
+// tiles: dense-and-sparse ones on either unit, and 2-bit matrix-core ones, with at
+// most four query heads per kv head.  They fit in 256 registers (a few spill
+// outside the loop), and the second wave hides the per-tile latency of the first
+// (reductions, LDS round trips, the outlier tables' atomics), which bounds these
+// streams rather than HBM.  Plain 4- and 8-bit streams and the plain VALU stream
+// are HBM-bound and keep one wave per SIMD with a ring of four tiles, which keeps
+// more bytes in flight; eight query heads per kv head would spill at 256 registers.
+__host__ __device__ constexpr bool two_waves(bool mf, int bits, int gq, bool sp) {
+    return gq <= 4 && (sp || (mf && bits == 2));
+}
 
 template <int BITS, int D, int GQ, int TPG, int NVG, bool SP = false>
 struct MStream {
@@ -407,7 +411,7 @@ struct MStream {
     static constexpr int AV_BYTES = NVG * RBK * 1024;
     // Ring of NRM tile buffers, NRM - 1 in flight while one is processed.  (Six
     // buffers measured slower: more register traffic per tile.)
-    static constexpr int NRM = mf_two_waves(BITS, GQ, SP) ? 2 : 4;
+    static constexpr int NRM = two_waves(true, BITS, GQ, SP) ? 2 : 4;
     static constexpr int BODY = TPG > NRM ? TPG : NRM;  // tiles per loop iteration
     static constexpr int GB = BODY / TPG;               // key groups per loop iteration
     static __host__ __device__ constexpr int lds_bytes() { return AK_BYTES + 2 * AV_BYTES; }
@@ -843,7 +847,7 @@ struct LdsPlan {
 // per token, on a map with four key lanes and four tokens per slot.
 template <int BITS, int D, int GQ, int CPL, int TILE, int TPG, bool MF = false, int NVGT = 1, bool SP = false,
           bool SPW = false>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MF && mf_two_waves(BITS, GQ, SP) ? 2 : 1)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(two_waves(MF, BITS, GQ, SP) ? 2 : 1)))
 void decode_kernel(DecArgs a) {
     constexpr int LPT = D / CPL;           // key lanes per token
     constexpr int TPW = 64 / LPT;          // tokens per key wave-load
@@ -984,8 +988,8 @@ void decode_kernel(DecArgs a) {
     // compiler copy the tile buffers at the back edge, which waits for the loads in
     // flight and serialises the memory stream.)
     // Ring of NR tile buffers: NR - 1 tiles in flight while one is processed.
-    constexpr int NR = 4;
-    constexpr int BODY = TPG > NR ? TPG : NR;  // tiles per loop iteration (4 or 8)
+    constexpr int NR = two_waves(false, BITS, GQ, SP) ? 2 : 4;
+    constexpr int BODY = TPG > NR ? TPG : NR;  // tiles per loop iteration (2, 4 or 8)
     constexpr int GB = BODY / TPG;             // key groups per loop iteration
     const int g_begin = split * a.gps;
     const int g_end = min(g_begin + a.gps, ng_s);
