@@ -107,6 +107,35 @@ def test_long_groups_against_oracle(kw, n):
         assert_export_slice_matches(ex, st, b, h)
 
 
+# 2-bit matrix-core streams with at most four query heads per kv head run two waves
+# per SIMD with a ring of two tiles; eight heads keep one wave and a ring of four.
+# Each instantiation shape, with the default split plan and with nine key groups per
+# split (waves of three and two groups: the ring's tail after the last whole
+# iteration).
+@pytest.mark.parametrize("kw", [
+    dict(n_q_heads=4, bits=2, k_group=64, residual=128, v_group=64),     # g = 2, two value groups
+    dict(n_q_heads=8, bits=2, k_group=128, residual=128, v_group=128),   # g = 4, two tiles per group
+    dict(n_q_heads=8, bits=2, k_group=256, residual=256, v_group=64),    # g = 4, four tiles per group
+    dict(n_q_heads=4, bits=2, head_dim=64, k_group=64, residual=64, v_group=64, dtype="f32"),  # D64
+    dict(n_q_heads=16, bits=2, k_group=64, residual=128, v_group=64),    # g = 8, one wave
+])
+@pytest.mark.parametrize("split_groups", [0, 9])
+def test_two_wave_streams_against_oracle(kw, split_groups):
+    require_gpu()
+    w = _w(**kw)
+    n = 40 * w.k_group + w.residual // 2 + 3
+    log("case %s split_groups=%d n=%d" % (kw, split_groups, n))
+    cache = make_cache(w, max_tokens=n)
+    if split_groups:
+        cache.set_split_tokens(split_groups * w.k_group)
+    K, V = _tokens(w, n, 51, 2.0), _tokens(w, n, 52)
+    cache.append(to_torch(K, w.dtype, DEV), to_torch(V, w.dtype, DEV))
+    sts, err = _attend_and_check(w, cache, K, V)
+    ex = export_cpu(cache)
+    for (b, h), st in sts.items():
+        assert_export_slice_matches(ex, st, b, h)
+
+
 def test_bulk_append_equals_one_token_appends():
     require_gpu()
     w = _w(n_sink=2, bits=2)
