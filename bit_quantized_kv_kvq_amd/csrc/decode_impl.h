@@ -251,6 +251,12 @@ __device__ __forceinline__ void publish(float* p, float v) {
 __device__ __forceinline__ float fetch(const float* p) {
     return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// Two adjacent floats (8-byte aligned) with one device-scope load.
+__device__ __forceinline__ float2 fetch2(const float* p) {
+    const unsigned long long v = __hip_atomic_load(reinterpret_cast<unsigned long long*>(const_cast<float*>(p)),
+                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return float2{__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32))};
+}
 
 __device__ __forceinline__ int dot8(uint32_t a, uint32_t b, int c) {
     return __builtin_amdgcn_sdot8((int)a, (int)b, c, false);
@@ -1572,42 +1578,113 @@ void decode_kernel(DecArgs a) {
     __syncthreads();
     if (!*s_last) return;
 
-    // Each thread merges the splits of its (head, channel) elements on its own:
-    // the maxima, sums and accumulators of a batch of kBatch splits are all
-    // loaded before the first is used (one L2 round trip per batch), and merged
-    // in split order with an online rescale between batches.
     const int ns = a.nsplit;
     const float* pml = a.part_ml + bh * a.nsplit_cap * GQ * 2;
     const float* pacc = a.part_acc + bh * a.nsplit_cap * GQ * D;
-    constexpr int kBatch = 16;
-    for (int e = tid; e < GQ * D; e += kThreads) {
-        const int h = e / D, c = e % D;
-        float M = -INFINITY, L = 0.0f, A = 0.0f;
-        for (int i0 = 0; i0 < ns; i0 += kBatch) {
-            float mi[kBatch], li[kBatch], ai[kBatch];
+    // Every load here is a round trip to the coherence point (about a microsecond),
+    // so the merge is arranged around few round trips.  With at most kStage
+    // (split, head) pairs: the maxima and sums of all pairs go to LDS in one round
+    // trip, together with the accumulators of the first batch of splits; each
+    // thread then takes its elements' maxima and sums from LDS and loads the
+    // remaining accumulators in batches of 64 (element, split) values.  The splits
+    // are merged in split order, with each split's weight exp2(m_i - M) under the
+    // overall maximum M.
+    constexpr int kStage = 512;
+    constexpr int NE = (GQ * D + kThreads - 1) / kThreads;  // (head, channel) elements per thread
+    constexpr int SB = 64 / NE;                             // splits per batch of accumulators
+    __shared__ float2 s_pml[kStage];
+    if (ns * GQ <= kStage) {
+        const int npair = ns * GQ;
+        int hk[NE], ck[NE];
 #pragma unroll
-            for (int k = 0; k < kBatch; ++k) {
-                const int i = min(i0 + k, ns - 1);
-                mi[k] = fetch(&pml[(i * GQ + h) * 2]);
-                li[k] = fetch(&pml[(i * GQ + h) * 2 + 1]);
-                ai[k] = fetch(&pacc[(i * GQ + h) * D + c]);
-            }
-            float Mb = M;
-#pragma unroll
-            for (int k = 0; k < kBatch; ++k) Mb = i0 + k < ns ? fmaxf(Mb, mi[k]) : Mb;
-            const float f = M == -INFINITY ? 0.0f : fast_exp2(M - Mb);
-            L *= f;
-            A *= f;
-#pragma unroll
-            for (int k = 0; k < kBatch; ++k) {
-                const float w = (i0 + k < ns && mi[k] != -INFINITY) ? fast_exp2(mi[k] - Mb) : 0.0f;
-                L = fmaf(li[k], w, L);
-                A = fmaf(ai[k], w, A);
-            }
-            M = Mb;
+        for (int k = 0; k < NE; ++k) {
+            const int e = min(tid + k * kThreads, GQ * D - 1);
+            hk[k] = e / D;
+            ck[k] = e % D;
         }
-        a.out[(qrow0 + h) * D + c] = A / L;
-        if (c == 0 && a.lse) a.lse[qrow0 + h] = (M + __log2f(L)) * 0.69314718055994530942f;
+        float2 mlr[kStage / kThreads];
+#pragma unroll
+        for (int r = 0; r < kStage / kThreads; ++r) mlr[r] = fetch2(&pml[2 * min(tid + r * kThreads, npair - 1)]);
+        float ai[NE][SB];
+        auto load_batch = [&](int i0) __attribute__((always_inline)) {
+#pragma unroll
+            for (int kk = 0; kk < SB; ++kk)
+#pragma unroll
+                for (int k = 0; k < NE; ++k) ai[k][kk] = fetch(&pacc[(min(i0 + kk, ns - 1) * GQ + hk[k]) * D + ck[k]]);
+        };
+        load_batch(0);
+#pragma unroll
+        for (int r = 0; r < kStage / kThreads; ++r)
+            if (tid + r * kThreads < npair) s_pml[tid + r * kThreads] = mlr[r];
+        __syncthreads();
+        float M[NE], L[NE], A[NE];
+#pragma unroll
+        for (int k = 0; k < NE; ++k) {
+            M[k] = -INFINITY;
+            for (int i = 0; i < ns; ++i) M[k] = fmaxf(M[k], s_pml[i * GQ + hk[k]].x);
+            L[k] = 0.0f;
+            A[k] = 0.0f;
+        }
+        auto weight = [&](int i, int k) __attribute__((always_inline)) {
+            const float mi = s_pml[i * GQ + hk[k]].x;
+            return mi == -INFINITY ? 0.0f : fast_exp2(mi - M[k]);
+        };
+        for (int i0 = 0; i0 < ns; i0 += SB) {
+            if (i0 > 0) load_batch(i0);
+#pragma unroll
+            for (int kk = 0; kk < SB; ++kk) {
+                if (i0 + kk < ns) {
+#pragma unroll
+                    for (int k = 0; k < NE; ++k) {
+                        const float w = weight(i0 + kk, k);
+                        L[k] = fmaf(s_pml[(i0 + kk) * GQ + hk[k]].y, w, L[k]);
+                        A[k] = fmaf(ai[k][kk], w, A[k]);
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < NE; ++k) {
+            if (tid + k * kThreads < GQ * D) {
+                a.out[(qrow0 + hk[k]) * D + ck[k]] = A[k] / L[k];
+                if (ck[k] == 0 && a.lse) a.lse[qrow0 + hk[k]] = (M[k] + __log2f(L[k])) * 0.69314718055994530942f;
+            }
+        }
+    } else {
+        // More pairs than LDS stages: each thread merges the splits of its elements
+        // on its own, loading the maxima, sums and accumulators of kBatch splits
+        // before using any, in split order with an online rescale between batches.
+        constexpr int kBatch = 16;
+        for (int e = tid; e < GQ * D; e += kThreads) {
+            const int h = e / D, c = e % D;
+            float M = -INFINITY, L = 0.0f, A = 0.0f;
+            for (int i0 = 0; i0 < ns; i0 += kBatch) {
+                float mi[kBatch], li[kBatch], ai[kBatch];
+#pragma unroll
+                for (int k = 0; k < kBatch; ++k) {
+                    const int i = min(i0 + k, ns - 1);
+                    const float2 ml = fetch2(&pml[(i * GQ + h) * 2]);
+                    mi[k] = ml.x;
+                    li[k] = ml.y;
+                    ai[k] = fetch(&pacc[(i * GQ + h) * D + c]);
+                }
+                float Mb = M;
+#pragma unroll
+                for (int k = 0; k < kBatch; ++k) Mb = i0 + k < ns ? fmaxf(Mb, mi[k]) : Mb;
+                const float f = M == -INFINITY ? 0.0f : fast_exp2(M - Mb);
+                L *= f;
+                A *= f;
+#pragma unroll
+                for (int k = 0; k < kBatch; ++k) {
+                    const float w = (i0 + k < ns && mi[k] != -INFINITY) ? fast_exp2(mi[k] - Mb) : 0.0f;
+                    L = fmaf(li[k], w, L);
+                    A = fmaf(ai[k], w, A);
+                }
+                M = Mb;
+            }
+            a.out[(qrow0 + h) * D + c] = A / L;
+            if (c == 0 && a.lse) a.lse[qrow0 + h] = (M + __log2f(L)) * 0.69314718055994530942f;
+        }
     }
     if (tid == 0) __hip_atomic_store(&a.counters[bh], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
