@@ -52,16 +52,18 @@ def load(path: str):
     L.orc_outlier_index.restype = i64
     L.orc_dequant.argtypes = [ctypes.c_uint8, ctypes.c_float, ctypes.c_float]
     L.orc_dequant.restype = ctypes.c_float
-    L.orc_build_slice.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, i32, P, P, i64] + [P] * 14 + [P]
+    L.orc_build_slice.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, i32, i32, P, P, i64] + [P] * 14 + [P]
     L.orc_build_slice.restype = i32
-    L.orc_dequant_slice.argtypes = [i32, i32, i32, i64, i64, i64] + [P] * 10 + [i32] + [P] * 6
+    L.orc_dequant_slice.argtypes = [i32, i32, i32, i32, i64, i64, i64] + [P] * 10 + [i32] + [P] * 6
     L.orc_dequant_slice.restype = None
     L.orc_attention.argtypes = [P, P, P, i64, i32, dbl, P, P]
     L.orc_attention.restype = None
-    L.orc_decode_slices.argtypes = [i64, i32, i32, i32, i32, i64, i64, i64, dbl] + [P] * 10 + [i32] + [P] * 7
+    L.orc_decode_slices.argtypes = [i64, i32, i32, i32, i32, i32, i64, i64, i64, dbl] + [P] * 10 + [i32] + [P] * 7
     L.orc_decode_slices.restype = None
     L.orc_num_threads.argtypes = []
     L.orc_num_threads.restype = i32
+    L.orc_set_num_threads.argtypes = [i32]
+    L.orc_set_num_threads.restype = None
     return L
 
 
@@ -145,7 +147,7 @@ def quantized_count(m: int, residual: int, log_window: int = 0) -> int:
 
 def build_slice(k_tok, v_tok, *, head_dim: int, bits: int, k_group: int, v_group: int,
                 residual: int, n_sink: int, codec: int = 0, log_window: int = 0,
-                outliers: int = 0) -> Dict[str, np.ndarray]:
+                outliers: int = 0, key_axis: int = 0) -> Dict[str, np.ndarray]:
     """Append the tokens of one (sequence, kv-head) one at a time; return the state.
 
     k_tok, v_tok: fp32 [n, D] (already rounded to the storage dtype).  codec: 0
@@ -164,17 +166,18 @@ def build_slice(k_tok, v_tok, *, head_dim: int, bits: int, k_group: int, v_group
     nS = min(n, S)
     Lq = quantized_count(n - nS, R, log_window)
     nvg = D // GV
+    kmeta = (Lq, 1) if key_axis else (Lq // G, D)
     st = dict(
         sink_k=np.zeros((S, D), np.float32), sink_v=np.zeros((S, D), np.float32),
-        k_codes=np.zeros((Lq, D), np.uint8), k_scale=np.zeros((Lq // G, D), np.float32),
-        k_zero=np.zeros((Lq // G, D), np.float32),
+        k_codes=np.zeros((Lq, D), np.uint8), k_scale=np.zeros(kmeta, np.float32),
+        k_zero=np.zeros(kmeta, np.float32),
         v_codes=np.zeros((Lq, D), np.uint8), v_scale=np.zeros((Lq, nvg), np.float32),
         v_zero=np.zeros((Lq, nvg), np.float32),
         res_k=np.zeros((R, D), np.float32), res_v=np.zeros((R, D), np.float32),
         ko_idx=np.full((Lq // G, D), -1, np.int32), ko_val=np.zeros((Lq // G, D), np.float32),
         vo_idx=np.full((Lq, nvg), -1, np.int32), vo_val=np.zeros((Lq, nvg), np.float32))
     counts = np.zeros(4, np.int64)
-    rc = lib().orc_build_slice(D, bits, codec, G, GV, R, S, log_window, outliers, _p(k_tok), _p(v_tok), n,
+    rc = lib().orc_build_slice(D, bits, codec, G, GV, R, S, log_window, outliers, key_axis, _p(k_tok), _p(v_tok), n,
                                _p(st["sink_k"]), _p(st["sink_v"]),
                                _p(st["k_codes"]), _p(st["k_scale"]), _p(st["k_zero"]),
                                _p(st["v_codes"]), _p(st["v_scale"]), _p(st["v_zero"]),
@@ -191,7 +194,7 @@ def build_slice(k_tok, v_tok, *, head_dim: int, bits: int, k_group: int, v_group
     st["res_v"] = st["res_v"][:r_]
     st.update(n_sink=nS_, n_quant=Lq_, n_resid=r_, flushes=fl, head_dim=D, bits=bits,
               k_group=G, v_group=GV, residual=R, S=S, codec=codec, log_window=log_window,
-              outliers=outliers)
+              outliers=outliers, key_axis=key_axis)
     return st
 
 
@@ -206,7 +209,8 @@ def dequant_slice(st) -> tuple:
             ("sink_k", "sink_v", "k_codes", "k_scale", "k_zero", "v_codes", "v_scale",
              "v_zero", "res_k", "res_v")]
     sparse = [np.ascontiguousarray(st[k]) for k in ("ko_idx", "ko_val", "vo_idx", "vo_val")]
-    lib().orc_dequant_slice(D, G, GV, nS, Lq, r, *[_p(a) for a in arrs], int(st.get("outliers", 0)),
+    lib().orc_dequant_slice(D, G, GV, int(st.get("key_axis", 0)), nS, Lq, r, *[_p(a) for a in arrs],
+                            int(st.get("outliers", 0)),
                             *[_p(a) for a in sparse], _p(ko), _p(vo))
     return ko, vo
 
@@ -248,7 +252,8 @@ def decode_slices(states, q, scale: float):
     sparse = [stack(k) for k in ("ko_idx", "ko_val", "vo_idx", "vo_val")]
     out = np.zeros((n, g, D), np.float64)
     lse = np.zeros((n, g), np.float64)
-    lib().orc_decode_slices(n, g, D, G, GV, nS, Lq, r, float(scale), *[_p(a) for a in arrs],
+    lib().orc_decode_slices(n, g, D, G, GV, int(st0.get("key_axis", 0)), nS, Lq, r, float(scale),
+                            *[_p(a) for a in arrs],
                             int(st0.get("outliers", 0)), *[_p(a) for a in sparse],
                             _p(q), _p(out), _p(lse))
     return out, lse
@@ -256,6 +261,11 @@ def decode_slices(states, q, scale: float):
 
 def num_threads() -> int:
     return int(lib().orc_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads of the oracle's parallel regions (for timing it on fewer cores)."""
+    lib().orc_set_num_threads(int(n))
 
 
 # ---------------------------------------------------------------------------
@@ -282,7 +292,7 @@ def slice_state(w, b: int, kvh: int, n_steps: int):
     k, v = slice_tokens_f32(w, b, kvh, n_steps)
     return build_slice(k, v, head_dim=w.head_dim, bits=w.bits, k_group=w.k_group,
                        v_group=w.v_group, residual=w.residual, n_sink=w.n_sink, codec=w.codec,
-                       log_window=w.log_window, outliers=w.outliers)
+                       log_window=w.log_window, outliers=w.outliers, key_axis=w.key_axis)
 
 
 def expected_outputs(w, b: int, kvh: int, n_steps: int, qi: int, scale: float | None = None):

@@ -92,7 +92,7 @@ def attention(q, K, V, scale: float):
 
 
 def build_slice(k_tok, v_tok, *, bits, k_group, v_group, residual, n_sink, codec=0, log_window=0,
-                outliers=0):
+                outliers=0, key_axis=0):
     """Token-by-token cache construction, written independently of the C oracle.
 
     log_window W > 0: LogQuant's log-sparse retention ("Resumo Técnico: LogQuant",
@@ -102,6 +102,10 @@ def build_slice(k_tok, v_tok, *, bits, k_group, v_group, residual, n_sink, codec
 
     outliers = 1: dense-and-sparse groups (quant_group_sparse); an outlier
     dequantizes to its own value.
+
+    key_axis = 1: head-granular keys ("Atom…" review, section 三, model-components
+    table, KV-cache row): every token's key row is one group, as a value row is
+    with v_group equal to the row length; k_meta then holds one [(s, z)] per token.
 
     Returns dict with lists: sinks, quantized (dequantized K', V' rows in the
     order they were quantized), residual rows, codes and metadata, outliers
@@ -132,8 +136,15 @@ def build_slice(k_tok, v_tok, *, bits, k_group, v_group, residual, n_sink, codec
         else:
             out_k, out_v = res_k, res_v
             res_k, res_v = [], []
+        # head-granular keys: each quantized token's key row is one group
+        if key_axis:
+            for row in out_k:
+                s, z, q = quant_group(row, bits, codec)
+                qk_rows.append([dequant(code, s, z) for code in q])
+                k_codes.append(list(q))
+                k_meta.append([(s, z)])
         # keys: per channel over each run of k_group tokens
-        for j0 in range(0, len(out_k), k_group):
+        for j0 in range(0, len(out_k) if not key_axis else 0, k_group):
             block = out_k[j0:j0 + k_group]
             rows = [[None] * D for _ in block]
             crow = [[0] * D for _ in block]

@@ -29,6 +29,10 @@
  *     and appended once it holds R tokens, then emptied
  *       ("LLM系列：KVCache量化1 KIVI: A Tuning-Free Asymmetric 2bit Quantiz",
  *        section 1 "KIVI", key-cache split into grouped part and residual)
+ *   - head-granular keys (key_axis 1): each token's key, the D channels of one
+ *     attention head, is one asymmetric group, like a value group of G_V = D
+ *       (Atom review, section 三, model-components table, KV-cache row: low-bit
+ *        asymmetric quantization at attention-head granularity)
  *   - LogQuant's log-sparse retention (W > 0): the full-precision part holds
  *     at most 3W tokens; when full, its oldest 2W tokens are thinned to every
  *     other one, the thinned-out W are quantized, and the newest W stay
@@ -177,12 +181,16 @@ float orc_dequant(uint8_t q, float s, float z)
 /* cache state of one (sequence, kv-head) slice                            */
 /* ---------------------------------------------------------------------- */
 
+#define ORC_KEY_PER_CHANNEL 0
+#define ORC_KEY_PER_TOKEN 1
+
 typedef struct {
     int D, bits, codec, G, GV, R, S;
+    int key_axis;                               /* ORC_KEY_PER_CHANNEL or ORC_KEY_PER_TOKEN */
     int W;                                      /* log window; 0: whole-residual flush */
     /* buffers owned by the caller */
     float* sink_k; float* sink_v;               /* [S, D]            */
-    uint8_t* k_codes; float* k_scale; float* k_zero;   /* [Lq,D] [Lq/G,D] */
+    uint8_t* k_codes; float* k_scale; float* k_zero;   /* [Lq,D] [Lq/G,D], per token [Lq] */
     uint8_t* v_codes; float* v_scale; float* v_zero;   /* [Lq,D] [Lq,D/GV] */
     float* res_k; float* res_v;                 /* [R, D]            */
     int outliers;                               /* one per vector, or none */
@@ -199,8 +207,16 @@ static void quantize_block(orc_slice* c, const float* bk, const float* bv, int m
 {
     const int D = c->D, G = c->G, GV = c->GV;
     const int nvg = D / GV;
+    /* head-granular keys: one group per token over its D channels */
+    if (c->key_axis == ORC_KEY_PER_TOKEN) {
+        for (int t = 0; t < m; ++t) {
+            const int64_t tok = c->Lq + t;
+            orc_quant_group(bk + (int64_t)t * D, D, 1, c->bits, c->codec,
+                            &c->k_scale[tok], &c->k_zero[tok], c->k_codes + tok * D, 1);
+        }
+    }
     /* keys: one group per channel over each run of G tokens */
-    for (int j = 0; j < m / G; ++j) {
+    for (int j = 0; c->key_axis == ORC_KEY_PER_CHANNEL && j < m / G; ++j) {
         int64_t grp = c->Lq / G + j;
         for (int ch = 0; ch < D; ++ch) {
             const float* col = bk + (int64_t)j * G * D + ch;
@@ -298,10 +314,12 @@ static void append_token(orc_slice* c, const float* k, const float* v)
  * outliers = 1 keeps one outlier per quantization vector: ko_idx, ko_val
  * [Lq/G, D] (token within the group, exact value), vo_idx, vo_val [Lq, D/GV]
  * (channel within the group, exact value); with outliers = 0 they are unused.
+ * key_axis = ORC_KEY_PER_TOKEN quantizes each token's key as one group (k_scale,
+ * k_zero [Lq]) instead of each channel over G tokens; it takes no outliers.
  * Returns 0, or -1 on an invalid configuration.
  */
 int orc_build_slice(int D, int bits, int codec, int G, int GV, int R, int S, int W, int outliers,
-                    const float* k_tok, const float* v_tok, int64_t n,
+                    int key_axis, const float* k_tok, const float* v_tok, int64_t n,
                     float* sink_k, float* sink_v,
                     uint8_t* k_codes, float* k_scale, float* k_zero,
                     uint8_t* v_codes, float* v_scale, float* v_zero,
@@ -314,7 +332,9 @@ int orc_build_slice(int D, int bits, int codec, int G, int GV, int R, int S, int
     if (R % G != 0 || D % GV != 0) return -1;
     if (W < 0 || (W > 0 && (R != 3 * W || W % G != 0))) return -1;
     if (outliers != 0 && (outliers != 1 || G < 2 || GV < 2)) return -1;
-    orc_slice c = {D, bits, codec, G, GV, R, S, W, sink_k, sink_v, k_codes, k_scale, k_zero,
+    if (key_axis != ORC_KEY_PER_CHANNEL && key_axis != ORC_KEY_PER_TOKEN) return -1;
+    if (key_axis == ORC_KEY_PER_TOKEN && outliers) return -1;
+    orc_slice c = {D, bits, codec, G, GV, R, S, key_axis, W, sink_k, sink_v, k_codes, k_scale, k_zero,
                    v_codes, v_scale, v_zero, res_k, res_v, outliers, ko_idx, ko_val, vo_idx, vo_val,
                    0, 0, 0, 0};
     for (int64_t t = 0; t < n; ++t)
@@ -327,8 +347,9 @@ int orc_build_slice(int D, int bits, int codec, int G, int GV, int R, int S, int
  * Dequantize one slice in storage order: sinks, then the quantized tokens in
  * the order they were quantized, then the full-precision part (chronological
  * order when whole residuals are flushed).  k_out, v_out: fp32 [nS+Lq+r, D].
+ * key_axis selects the key scale / zero layout ([Lq/G, D], or [Lq] per token).
  */
-void orc_dequant_slice(int D, int G, int GV, int64_t nS, int64_t Lq, int64_t r,
+void orc_dequant_slice(int D, int G, int GV, int key_axis, int64_t nS, int64_t Lq, int64_t r,
                        const float* sink_k, const float* sink_v,
                        const uint8_t* k_codes, const float* k_scale, const float* k_zero,
                        const uint8_t* v_codes, const float* v_scale, const float* v_zero,
@@ -343,8 +364,8 @@ void orc_dequant_slice(int D, int G, int GV, int64_t nS, int64_t Lq, int64_t r,
     for (int64_t t = 0; t < Lq; ++t) {
         int64_t grp = t / G;
         for (int ch = 0; ch < D; ++ch) {
-            k_out[(nS + t) * D + ch] = orc_dequant(k_codes[t * D + ch],
-                                                   k_scale[grp * D + ch], k_zero[grp * D + ch]);
+            const int64_t km = key_axis == ORC_KEY_PER_TOKEN ? t : grp * D + ch;
+            k_out[(nS + t) * D + ch] = orc_dequant(k_codes[t * D + ch], k_scale[km], k_zero[km]);
             int h = ch / GV;
             v_out[(nS + t) * D + ch] = orc_dequant(v_codes[t * D + ch],
                                                    v_scale[t * nvg + h], v_zero[t * nvg + h]);
@@ -395,7 +416,7 @@ void orc_attention(const float* q, const float* K, const float* V, int64_t T, in
  * q is fp32 [n, g, D]; out [n, g, D] and lse [n, g] are binary64.
  * Slices are independent, so they are spread over OpenMP threads.
  */
-void orc_decode_slices(int64_t n, int g, int D, int G, int GV,
+void orc_decode_slices(int64_t n, int g, int D, int G, int GV, int key_axis,
                        int64_t nS, int64_t Lq, int64_t r, double scale,
                        const float* sink_k, const float* sink_v,
                        const uint8_t* k_codes, const float* k_scale, const float* k_zero,
@@ -407,14 +428,14 @@ void orc_decode_slices(int64_t n, int g, int D, int G, int GV,
 {
     const int64_t T = nS + Lq + r;
     const int64_t nvg = D / GV;
+    const int64_t nkm = key_axis == ORC_KEY_PER_TOKEN ? Lq : (Lq / G) * D;  /* key scales per slice */
     #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t i = 0; i < n; ++i) {
         float* kf = (float*)malloc(sizeof(float) * (T > 0 ? T : 1) * D);
         float* vf = (float*)malloc(sizeof(float) * (T > 0 ? T : 1) * D);
-        orc_dequant_slice(D, G, GV, nS, Lq, r,
+        orc_dequant_slice(D, G, GV, key_axis, nS, Lq, r,
                           sink_k + i * nS * D, sink_v + i * nS * D,
-                          k_codes + i * Lq * D, k_scale + i * (Lq / G) * D,
-                          k_zero + i * (Lq / G) * D,
+                          k_codes + i * Lq * D, k_scale + i * nkm, k_zero + i * nkm,
                           v_codes + i * Lq * D, v_scale + i * Lq * nvg, v_zero + i * Lq * nvg,
                           res_k + i * r * D, res_v + i * r * D, outliers,
                           ko_idx + (outliers ? i * (Lq / G) * D : 0), ko_val + (outliers ? i * (Lq / G) * D : 0),
@@ -433,5 +454,15 @@ int orc_num_threads(void)
     return omp_get_max_threads();
 #else
     return 1;
+#endif
+}
+
+/* Threads of the parallel regions above (timing of the oracle only; n >= 1). */
+void orc_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    omp_set_num_threads(n > 0 ? n : 1);
+#else
+    (void)n;
 #endif
 }

@@ -11,6 +11,7 @@ import pytest
 import oracle
 import tests.test_oracle_cache as tc
 import tests.test_oracle_codec as tq
+import tests.test_oracle_keys as tk
 import tests.test_oracle_logquant as tl
 import tests.test_oracle_outliers as to
 
@@ -108,6 +109,12 @@ MUTANTS = {
         "if (outliers && ko_idx[grp * D + ch] == t % G) k_out[(nS + t) * D + ch] = ko_val[grp * D + ch];", ""),
     # dense-and-sparse: value outlier channel taken from the vector's start
     "outlier_value_channel": ("vo_idx[t * nvg + h] == ch - h * GV", "vo_idx[t * nvg + h] == ch"),
+    # head-granular keys: the token block read column by column (a transposed row)
+    "key_token_transposed": ("orc_quant_group(bk + (int64_t)t * D, D, 1, c->bits, c->codec,",
+                             "orc_quant_group(bk + (int64_t)t, D, m, c->bits, c->codec,"),
+    # head-granular keys: every token dequantized with the first token of its key group's scale
+    "key_token_scale_of_group": ("key_axis == ORC_KEY_PER_TOKEN ? t : grp * D + ch",
+                                 "key_axis == ORC_KEY_PER_TOKEN ? grp * G : grp * D + ch"),
     # residual tokens left out of the dequantized token sequence
     "drop_residual": ("memcpy(k_out + (nS + Lq) * D, res_k, sizeof(float) * r * D);",
                       "memset(k_out + (nS + Lq) * D, 0, sizeof(float) * r * D);"),
@@ -146,6 +153,10 @@ def _pins():
         pins.append(lambda b=bits: to.test_invariants_random_groups(b, 0))
     pins.append(lambda: to.test_slice_outliers_exact_and_matches_brute(4, 0, 0, 4, 8, 8, 37, 0))
     pins.append(lambda: to.test_slice_outliers_exact_and_matches_brute(2, 1, 2, 8, 4, 16, 50, 0))
+    for case in tk._cases():
+        pins.append(lambda c=case: tk.test_golden_cache(c))
+    pins.append(lambda: tk.test_invariants_random_slices(4, 0))
+    pins.append(lambda: tk.test_matches_brute(2, 0, 2, 0, 8, 4, 45, 1))
     return pins
 
 

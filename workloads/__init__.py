@@ -18,6 +18,8 @@ tokens) stand in for the real activations those pages measure.
 from __future__ import annotations
 
 import dataclasses
+import os
+from concurrent.futures import ThreadPoolExecutor
 from typing import Dict, Iterator, Tuple
 
 import numpy as np
@@ -61,6 +63,7 @@ class Workload:
     page_groups: int = 0            # P > 0: quantized records in pages of P key groups
     prefill_chunk: int = 0          # prefill in rounds of this many tokens per sequence (0: at once)
     outliers: int = 0               # 1: one full-precision outlier per quantization vector
+    key_axis: int = 0               # 0: keys per channel over G tokens; 1: per token over D channels
 
     @property
     def gqa(self) -> int:
@@ -347,15 +350,25 @@ def query_slice(w: Workload, b: int, hq: int):
     return to_storage(query_f32(w, b, hq), w.dtype)
 
 
+def _each_slice(fn, pairs) -> None:
+    """fn(pair) for every pair, on a pool of threads (numpy's generators release the
+    GIL); every slice has its own generator, so the values do not depend on the
+    order.  At most 16 threads."""
+    with ThreadPoolExecutor(max(1, min(16, os.cpu_count() or 1))) as ex:
+        list(ex.map(fn, pairs))
+
+
 def prefill_batch(w: Workload, n: int | None = None):
-    """Storage arrays K, V [B, Hkv, n, D] of the whole prefill (row by row)."""
+    """Storage arrays K, V [B, Hkv, n, D] of the whole prefill (slice by slice)."""
     n = w.prefill if n is None else n
     dt = storage_np_dtype(w.dtype)
     K = np.empty((w.batch, w.n_kv_heads, n, w.head_dim), dtype=dt)
     V = np.empty_like(K)
-    for b in range(w.batch):
-        for h in range(w.n_kv_heads):
-            K[b, h], V[b, h] = prefill_slice(w, b, h, n)
+
+    def fill(p):
+        K[p[0], p[1]], V[p[0], p[1]] = prefill_slice(w, p[0], p[1], n)
+
+    _each_slice(fill, [(b, h) for b in range(w.batch) for h in range(w.n_kv_heads)])
     return K, V
 
 
@@ -364,10 +377,11 @@ def steps_batch(w: Workload):
     dt = storage_np_dtype(w.dtype)
     K = np.empty((w.steps, w.batch, w.n_kv_heads, w.head_dim), dtype=dt)
     V = np.empty_like(K)
-    for b in range(w.batch):
-        for h in range(w.n_kv_heads):
-            k, v = step_slice(w, b, h)
-            K[:, b, h], V[:, b, h] = k, v
+
+    def fill(p):
+        K[:, p[0], p[1]], V[:, p[0], p[1]] = step_slice(w, p[0], p[1])
+
+    _each_slice(fill, [(b, h) for b in range(w.batch) for h in range(w.n_kv_heads)])
     return K, V
 
 
@@ -375,9 +389,11 @@ def queries_batch(w: Workload):
     """Storage array Q [n_queries, B, Hq, D]."""
     dt = storage_np_dtype(w.dtype)
     Q = np.empty((n_queries(w), w.batch, w.n_q_heads, w.head_dim), dtype=dt)
-    for b in range(w.batch):
-        for h in range(w.n_q_heads):
-            Q[:, b, h] = query_slice(w, b, h)
+
+    def fill(p):
+        Q[:, p[0], p[1]] = query_slice(w, p[0], p[1])
+
+    _each_slice(fill, [(b, h) for b in range(w.batch) for h in range(w.n_q_heads)])
     return Q
 
 
