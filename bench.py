@@ -45,8 +45,10 @@ import workloads as wl  # noqa: E402
 METRIC = "effective KV GB/s (and % HBM peak) of quantized decode attention; tokens/s"
 HBM_PEAK_GBS = 8000.0
 MALL_BYTES = 256 * 2 ** 20
-EVENT_STRIDE = 8
-DEFAULT_WORKLOAD = "llama7b_mha_int4"
+MAX_EVENT_STRIDE = 8
+MIN_TIMED_LAUNCHES = 16
+# the largest single-GPU workload (B32 H32 D128, context 8192, INT2: about 1.1 GB per call)
+DEFAULT_WORKLOAD = "kivi2_long_batch"
 DECODE_SOURCES = ["decode_impl.h", "decode_dispatch.h", "decode.hip", "kvq_internal.h",
                   "decode_b4_d128.hip", "decode_b2_d128.hip", "decode_b4_d64.hip", "decode_b2_d64.hip",
                   "decode_mf_b4_d128.hip", "decode_mf_b2_d128.hip", "decode_mf_b4_d64.hip", "decode_mf_b2_d64.hip",
@@ -91,38 +93,93 @@ def decode_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_from_profile(w: wl.Workload):
-    """HBM bytes per decode launch from the committed counter summary, if it was
-    taken on the current decode kernel source for this workload; else None."""
-    path = os.path.join(ROOT, "profiles", "decode_traffic_%s.json" % w.name)
+def n_layers(w: wl.Workload, layers: int = 0) -> int:
+    """Caches rotated per step: enough that their combined decode traffic is three
+    times the 256 MB MALL (layers = 0), or the given count."""
+    if layers:
+        return layers
+    b0 = algorithmic_bytes_seqs(w, wl.prefill_lengths(w))
+    return min(64, max(2, math.ceil(3 * MALL_BYTES / b0)))
+
+
+def default_steps(w: wl.Workload, L: int) -> int:
+    """Timed steps by default: every layer appends as many tokens as separate two
+    flushes (R, or W under log-sparse retention), so the region holds each layer's
+    residual flush once (its amortised share of the steps)."""
+    return L * (w.log_window or w.residual)
+
+
+def event_stride(steps: int) -> int:
+    """Kernel events on every stride-th timed step: at most every 8th (timing every
+    step lengthens the steps a little), and at least MIN_TIMED_LAUNCHES launches,
+    or every launch when the region has fewer steps."""
+    return max(1, min(MAX_EVENT_STRIDE, steps // MIN_TIMED_LAUNCHES))
+
+
+def step_plan(w: wl.Workload, L: int, total_steps: int):
+    """For each step s (warm-up steps first): whether the step is one fused launch
+    (every sequence's token joins its residual without filling it) and the
+    algorithmic bytes of its decode call (the cache state after the append)."""
+    lens0 = wl.prefill_lengths(w)
+    plan = []
+    for s in range(total_steps):
+        fused = True
+        for n0 in lens0:
+            nb = n0 + s // L          # this sequence's tokens before the append
+            fused &= nb >= w.n_sink and slice_counts(w, nb)[2] + 1 < w.residual
+        plan.append((fused, algorithmic_bytes_seqs(w, [n0 + s // L + 1 for n0 in lens0])))
+    return plan
+
+
+def traffic_path(w: wl.Workload) -> str:
+    return os.path.join(ROOT, "profiles", "decode_traffic_%s.json" % w.name)
+
+
+def traffic_from_profile(w: wl.Workload, steps: int, warmup: int, layers: int):
+    """HBM bytes per timed decode launch, from the committed counter summary of a
+    run of this exact schedule (workload, steps, warm-up, layers) on the current
+    decode kernel source; else None."""
+    path = traffic_path(w)
     if not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
     if t.get("decode_source_hash") != decode_source_hash():
         return None
-    return t.get("hbm_bytes_per_launch")
+    for r in t.get("runs", []):
+        if (r["steps"], r["warmup"], r["layers"]) == (steps, warmup, layers):
+            return r["hbm_bytes_per_launch"]
+    return None
 
 
 COPY_PROBE_BYTES = 1 << 30
+READ_PROBE_BYTES = 1 << 31
 
 
-def copy_probe(torch, dev):
-    """A plain device copy of known size (1 GiB read, 1 GiB written), ten times, so
-    that rocprofv3's FETCH_SIZE / WRITE_SIZE per dispatch can be scaled to bytes."""
+def copy_probe(torch, dev, kvq):
+    """Kernels of known traffic, ten dispatches each, so that rocprofv3's FETCH_SIZE /
+    WRITE_SIZE per dispatch can be scaled to bytes: a plain device copy (1 GiB read,
+    1 GiB written) and the library's streaming read (2 GiB read once, nothing
+    written but one word)."""
     src = torch.ones(COPY_PROBE_BYTES // 4, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
     for _ in range(10):
         torch.mul(src, 1.0, out=dst)
+    del src, dst
+    x = torch.ones(READ_PROBE_BYTES // 4, dtype=torch.int32, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    sp = torch.cuda.current_stream().cuda_stream
+    for _ in range(10):
+        kvq.kvq_stream_read_probe(x.data_ptr(), READ_PROBE_BYTES, 4, sink.data_ptr(), sp)
     torch.cuda.synchronize()
     print(json.dumps({"copy_probe_bytes_read": COPY_PROBE_BYTES, "copy_probe_bytes_written": COPY_PROBE_BYTES,
-                      "dispatches": 10}))
+                      "read_probe_bytes_read": READ_PROBE_BYTES, "dispatches": 10}))
 
 
 def stream_read_ceiling(torch, dev, kvq) -> dict:
     """Bandwidth of a plain streaming read of 2 GiB (kvq_stream_read_probe): the best,
     over 1 to 16 workgroups per CU, of the median of 7 timed reads."""
-    nbytes = 2 ** 31
+    nbytes = READ_PROBE_BYTES
     x = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
     sink = torch.zeros(1, dtype=torch.int32, device=dev)
     sp = torch.cuda.current_stream().cuda_stream
@@ -147,34 +204,56 @@ def stream_read_ceiling(torch, dev, kvq) -> dict:
             "ms": round(best[0], 4)}
 
 
-def _counter_means(path: str, name_part: str) -> dict:
-    """Mean value per dispatch of each counter of the kernels whose name contains name_part."""
+def _counter_rows(path: str, name_part: str, counter: str) -> list:
+    """Values of one counter for the dispatches of kernels whose name contains
+    name_part, in dispatch order."""
     import csv
-    sums, counts = {}, {}
+    rows = []
     with open(path) as f:
         for r in csv.DictReader(f):
-            if name_part in r["Kernel_Name"]:
-                k = r["Counter_Name"]
-                sums[k] = sums.get(k, 0.0) + float(r["Counter_Value"])
-                counts[k] = counts.get(k, 0) + 1
-    return {k: sums[k] / counts[k] for k in sums}
+            if name_part in r["Kernel_Name"] and r["Counter_Name"] == counter:
+                rows.append((int(r["Dispatch_Id"]), float(r["Counter_Value"])))
+    rows.sort()
+    return [v for _, v in rows]
 
 
-def write_traffic(w: wl.Workload, dec_fetch: str, dec_write: str, copy_fetch: str, copy_write: str):
-    """HBM bytes per decode launch: the decode kernel's FETCH_SIZE and WRITE_SIZE (KiB per
-    dispatch) scaled by what the same counters read for the 1 GiB copy probe."""
-    f_dec = _counter_means(dec_fetch, "decode_kernel")["FETCH_SIZE"]
-    w_dec = _counter_means(dec_write, "decode_kernel")["WRITE_SIZE"]
-    f_cp = _counter_means(copy_fetch, "elementwise")["FETCH_SIZE"]
-    w_cp = _counter_means(copy_write, "elementwise")["WRITE_SIZE"]
-    k_fetch = COPY_PROBE_BYTES / (f_cp * 1024.0)
-    k_write = COPY_PROBE_BYTES / (w_cp * 1024.0)
+def write_traffic(w: wl.Workload, steps: int, warmup: int, layers: int, dec_fetch: str, dec_write: str,
+                  probe_fetch: str, copy_write: str):
+    """Adds one schedule's HBM bytes per timed decode launch to the workload's
+    traffic summary: the decode kernel's FETCH_SIZE and WRITE_SIZE (KiB per
+    dispatch; the mean over the last `steps` decode dispatches, i.e. the timed
+    ones) scaled by what the same counters read for kernels of known traffic
+    (FETCH_SIZE: the library's 2 GiB streaming read; WRITE_SIZE: the 1 GiB copy)."""
+    L = n_layers(w, layers)
+    f_dec = _counter_rows(dec_fetch, "decode_kernel", "FETCH_SIZE")[-steps:]
+    w_dec = _counter_rows(dec_write, "decode_kernel", "WRITE_SIZE")[-steps:]
+    assert len(f_dec) == steps and len(w_dec) == steps, (len(f_dec), len(w_dec), steps)
+    f_rd = _counter_rows(probe_fetch, "stream_read_kernel", "FETCH_SIZE")
+    f_cp = _counter_rows(probe_fetch, "elementwise", "FETCH_SIZE")
+    w_cp = _counter_rows(copy_write, "elementwise", "WRITE_SIZE")
+    mean = lambda v: sum(v) / len(v)
+    k_fetch = READ_PROBE_BYTES / (mean(f_rd) * 1024.0)
+    k_fetch_copy = COPY_PROBE_BYTES / (mean(f_cp) * 1024.0)
+    k_write = COPY_PROBE_BYTES / (mean(w_cp) * 1024.0)
+    plan = step_plan(w, L, warmup + steps)[warmup:]
+    alg = sum(b for _, b in plan) / len(plan)
+    run = {"steps": steps, "warmup": warmup, "layers": L,
+           "fetch_kib_per_dispatch": mean(f_dec), "write_kib_per_dispatch": mean(w_dec),
+           "hbm_bytes_per_launch": int(mean(f_dec) * 1024.0 * k_fetch + mean(w_dec) * 1024.0 * k_write),
+           "algorithmic_bytes_per_launch": int(alg)}
+    run["traffic_over_algorithmic"] = round(run["hbm_bytes_per_launch"] / alg, 4)
+    path = traffic_path(w)
+    old = {}
+    if os.path.exists(path):
+        with open(path) as f:
+            old = json.load(f)
+    runs = [r for r in old.get("runs", []) if old.get("decode_source_hash") == decode_source_hash()
+            and (r["steps"], r["warmup"], r["layers"]) != (steps, warmup, L)]
     out = {"workload": w.name, "decode_source_hash": decode_source_hash(),
-           "fetch_kib_per_dispatch": f_dec, "write_kib_per_dispatch": w_dec,
-           "copy_probe_fetch_kib": f_cp, "copy_probe_write_kib": w_cp,
-           "fetch_scale": k_fetch, "write_scale": k_write,
-           "hbm_bytes_per_launch": int(f_dec * 1024.0 * k_fetch + w_dec * 1024.0 * k_write)}
-    path = os.path.join(ROOT, "profiles", "decode_traffic_%s.json" % w.name)
+           "read_probe_fetch_kib": mean(f_rd), "read_probe_fetch_scale": k_fetch,
+           "copy_probe_fetch_kib": mean(f_cp), "copy_probe_fetch_scale": k_fetch_copy,
+           "copy_probe_write_kib": mean(w_cp), "write_scale": k_write,
+           "runs": runs + [run]}
     os.makedirs(os.path.dirname(path), exist_ok=True)
     with open(path, "w") as f:
         json.dump(out, f, indent=1)
@@ -218,26 +297,60 @@ class HipEvents:
             self.lib.hipEventDestroy(e)
 
 
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _timed(fn, budget_s: float):
+    """Runs fn() repeatedly for about budget_s seconds (at least once); returns
+    (seconds per run, runs)."""
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        fn()
+        reps += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    return (time.perf_counter() - t0) / reps, reps
+
+
 def cpu_baseline(w: wl.Workload, budget_s: float):
-    """The oracle, as it is, on host cores: the decode step (dequantize + binary64
-    attention) of a bounded sample of (sequence, kv-head) slices of the workload."""
+    """The oracle, as it is, on the host's cores, over a bounded sample of the
+    workload's (sequence, kv-head) slices.  Three phases:
+      - decode step: dequantize + binary64 attention of the sampled slices after
+        the prefill (OpenMP across slices); `value` is its effective GB/s over the
+        same algorithmic bytes as the GPU line;
+      - prefill quantization: the oracle's cache build (one-token appends and the
+        residual flushes) over the sampled slices' prefill tokens;
+      - append and flush: the build of one residual's worth of tokens (R appends
+        and one flush; the sinks first when the workload keeps them).
+    The small workloads (tiny, Llama-7B-shaped) also time the decode step on one
+    thread.  Slices run on a thread pool of the oracle's thread count (the C
+    oracle releases the GIL); each phase gets a share of budget_s."""
     import oracle
+    from concurrent.futures import ThreadPoolExecutor
+    threads = oracle.num_threads()
     n_slices_total = w.batch * w.n_kv_heads
-    # sample: as many slices as fit about budget_s of CPU work, measured on a probe
     slices = [(b, h) for b in range(w.batch) for h in range(w.n_kv_heads)]
+    g = w.gqa
+    scale = oracle.default_scale(w.head_dim)
+    # sample: as many slices as fit the decode share of the budget, measured on a probe
     probe = slices[:1]
     states = [oracle.slice_state(w, b, h, 0) for b, h in probe]
-    g = w.gqa
     qs = np.stack([np.stack([wl.storage_to_f32(wl.query_slice(w, b, h * g + j)[0], w.dtype)
                              for j in range(g)]) for b, h in probe])
-    scale = oracle.default_scale(w.head_dim)
     t0 = time.perf_counter()
     oracle.decode_slices(states, qs, scale)
     t_probe = max(time.perf_counter() - t0, 1e-4)
-    threads = oracle.num_threads()
-    n = int(min(n_slices_total, max(threads, budget_s / t_probe * threads)))
-    n = max(1, n)
-    sample = slices[:n]
+    n = int(min(n_slices_total, max(threads, 0.5 * budget_s / t_probe * threads)))
+    sample = slices[:max(1, n)]
+    lens = wl.prefill_lengths(w)
     # one batched oracle call per sequence (its slices share one length)
     groups = []
     for b in sorted({b for b, _ in sample}):
@@ -245,25 +358,55 @@ def cpu_baseline(w: wl.Workload, budget_s: float):
         groups.append(([oracle.slice_state(w, b, h, 0) for h in hs],
                        np.stack([np.stack([wl.storage_to_f32(wl.query_slice(w, b, h * g + j)[0], w.dtype)
                                            for j in range(g)]) for h in hs])))
-    reps, t0 = 0, time.perf_counter()
-    while True:   # repeat the sampled step until the budget is spent
-        for states, qs in groups:
-            oracle.decode_slices(states, qs, scale)
-        reps += 1
-        if time.perf_counter() - t0 >= budget_s:
-            break
-    dt = (time.perf_counter() - t0) / reps
+
+    def decode_step():
+        for st_, q_ in groups:
+            oracle.decode_slices(st_, q_, scale)
+
+    dt, reps = _timed(decode_step, 0.5 * budget_s)
     # algorithmic bytes of the sampled slices (a sequence's bytes split evenly over its kv heads)
-    lens = wl.prefill_lengths(w)
     full = algorithmic_bytes_seqs(w, lens)
     sampled = sum(algorithmic_bytes_seqs(w, [lens[b]]) / w.n_kv_heads for b, _ in sample)
     frac = sampled / full
-    gbs = sampled / dt / 1e9
-    return {"value": round(gbs, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": "decode step (dequantize + binary64 attention) of %d of %d (sequence, "
-                      "kv-head) slices after the %d-token prefill, repeated %d times in %.1f s; "
-                      "%.4f s per sampled step" % (n, n_slices_total, w.prefill, reps, dt * reps, dt),
-            "seconds_per_step_estimate": round(dt / frac, 4)}
+    res = {"value": round(sampled / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+           "cpu_model": _cpu_model(),
+           "sample": "decode step (dequantize + binary64 attention) of %d of %d (sequence, kv-head) "
+                     "slices after the %d-token prefill, repeated %d times in %.1f s; %.4f s per "
+                     "sampled step" % (len(sample), n_slices_total, w.prefill, reps, dt * reps, dt),
+           "seconds_per_step_estimate": round(dt / frac, 4)}
+
+    # prefill quantization and append/flush: the oracle's slice build from fp32 tokens
+    def build(args):
+        k, v = args
+        return oracle.build_slice(k, v, head_dim=w.head_dim, bits=w.bits, k_group=w.k_group,
+                                  v_group=w.v_group, residual=w.residual, n_sink=w.n_sink, codec=w.codec,
+                                  log_window=w.log_window, outliers=w.outliers)
+
+    toks = [oracle.slice_tokens_f32(w, b, h, 0) for b, h in sample[:threads]]
+    with ThreadPoolExecutor(threads) as ex:
+        dtp, rp = _timed(lambda: list(ex.map(build, toks)), 0.25 * budget_s)
+        n_in = sum(k.shape[0] for k, _ in toks)
+        e = wl.elem_bytes(w.dtype)
+        res["prefill_quantize"] = {
+            "slice_tokens_per_s": round(n_in / dtp, 1),
+            "input_gb_per_s": round(n_in * 2 * w.head_dim * e / dtp / 1e9, 4),
+            "sample": "%d slices x %d tokens, %d runs" % (len(toks), toks[0][0].shape[0], rp)}
+        m = w.n_sink + w.residual
+        short = [(k[:m], v[:m]) for k, v in toks]
+        dta, ra = _timed(lambda: list(ex.map(build, short)), 0.1 * budget_s)
+        res["append_flush"] = {
+            "us_per_token": round(dta / (len(short) * m) * threads * 1e6, 3),
+            "sample": "%d slices x (%d appends incl. one flush of %d tokens), %d runs, %d threads; "
+                      "per token per thread" % (len(short), m, w.residual, ra, threads)}
+    if w.name in ("tiny", "llama7b_mha_int4"):
+        oracle.set_num_threads(1)
+        try:
+            dt1, r1 = _timed(decode_step, 0.15 * budget_s)
+        finally:
+            oracle.set_num_threads(threads)
+        res["decode_step_1_thread"] = {"value": round(sampled / dt1 / 1e9, 4), "unit": "GB/s",
+                                       "seconds_per_sampled_step": round(dt1, 5), "runs": r1}
+    return res
 
 
 def main():
@@ -276,18 +419,26 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--layers", type=int, default=0, help="caches rotated per step (0 = auto)")
     ap.add_argument("--split-tokens", type=int, default=0)
-    ap.add_argument("--cpu-budget", type=float, default=12.0,
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="untimed decode calls before the warm-up steps, to bring the GPU to its "
+                         "steady clock (they leave every cache unchanged)")
+    ap.add_argument("--cpu-budget", type=float, default=16.0,
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
     ap.add_argument("--copy-probe", action="store_true",
-                    help="run only a plain 1 GiB device copy (calibrates the HBM byte counters)")
-    ap.add_argument("--write-traffic", nargs=4, metavar=("DECODE_FETCH", "DECODE_WRITE", "COPY_FETCH",
+                    help="run only kernels of known traffic (calibrates the HBM byte counters)")
+    ap.add_argument("--write-traffic", nargs=4, metavar=("DECODE_FETCH", "DECODE_WRITE", "PROBE_FETCH",
                                                          "COPY_WRITE"),
-                    help="write profiles/decode_traffic_<workload>.json from rocprofv3 --pmc "
+                    help="add this schedule (--workload, --steps, --warmup, --layers) to "
+                         "profiles/decode_traffic_<workload>.json from rocprofv3 --pmc "
                          "counter_collection.csv files of the bench and of --copy-probe (no GPU)")
     args = ap.parse_args()
+    w = wl.get(args.workload)
+    L = n_layers(w, args.layers)
+    if args.steps is None:
+        args.steps = default_steps(w, L)
 
     if args.write_traffic:
-        write_traffic(wl.get(args.workload), *args.write_traffic)
+        write_traffic(w, args.steps, args.warmup, args.layers, *args.write_traffic)
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -306,20 +457,11 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     if args.copy_probe:
-        copy_probe(torch, dev)
+        copy_probe(torch, dev, kvq)
         return
-    w = wl.get(args.workload)
 
-    # size of one cache's decode traffic; enough layers to overflow the MALL 3x
     lens0 = wl.prefill_lengths(w)
     ragged = len(set(lens0)) > 1
-    b0 = algorithmic_bytes_seqs(w, lens0)
-    L = args.layers or min(64, max(2, math.ceil(3 * MALL_BYTES / b0)))
-    # by default every layer appends as many tokens as separate two flushes (R, or
-    # W under log-sparse retention) in the timed region, so the region holds each
-    # layer's residual flush once (its amortised share of the steps)
-    if args.steps is None:
-        args.steps = L * (w.log_window or w.residual)
     total_steps = args.warmup + args.steps
     per_layer_steps = (total_steps + L - 1) // L
     max_tokens = w.prefill + per_layer_steps
@@ -364,14 +506,14 @@ def main():
 
     stream = torch.cuda.current_stream()
     hip = HipEvents()
-    # Every EVENT_STRIDE-th timed step, the library records two events at the
-    # start and end of the decode kernel itself (kvq_set_timing_events); these
-    # give the kernel duration of the roofline.  Half a stride later, two events
-    # recorded on the stream around the call give the call's duration, dispatch
-    # gaps included (reported beside it).  Timing every step would lengthen the
-    # steps being measured.
-    timed_steps = [k for k in range(args.steps) if k % EVENT_STRIDE == 0]
-    call_steps = [k for k in range(args.steps) if k % EVENT_STRIDE == EVENT_STRIDE // 2]
+    # Every stride-th timed step, the library records two events at the start and
+    # end of the decode kernel itself (kvq_set_timing_events); these give the
+    # kernel duration of the roofline.  Half a stride later, two events recorded on
+    # the stream around the call give the call's duration, dispatch gaps included
+    # (reported beside it).
+    stride = event_stride(args.steps)
+    timed_steps = [k for k in range(args.steps) if k % stride == 0]
+    call_steps = [k for k in range(args.steps) if k % stride == stride // 2]
     ev = {k: (hip.create(), hip.create()) for k in timed_steps}
     ev_call = {k: (hip.create(), hip.create()) for k in call_steps}
 
@@ -385,24 +527,19 @@ def main():
     set_events = lib.kvq_set_timing_events
     sp = ctypes.c_void_p(stream.cuda_stream)
     out_p, lse_p = ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(lse.data_ptr())
+    # The step is one kvq_append_decode call when every sequence's token joins its
+    # residual without filling it; otherwise (a sink or a flush somewhere) the
+    # library appends and decodes in two launches, and the bench makes the same two
+    # calls itself so that the events bracket the decode alone.
+    schedule = step_plan(w, L, total_steps)
     plan, step_bytes = [], []
-    for s in range(total_steps):
-        c = caches[s % L]
-        i = (s // L) % w.steps
-        # cache state before and after this step's append: the schedule fixes it
-        n = w.prefill + s // L + 1
-        # The step is one kvq_append_decode call when every sequence's token joins
-        # its residual without filling it; otherwise (a sink or a flush somewhere)
-        # the library appends and decodes in two launches, and the bench makes the
-        # same two calls itself so that the events bracket the decode alone.
-        fused = True
-        for n0 in lens0:
-            nb = n0 + s // L          # this sequence's tokens before the append
-            fused &= nb >= w.n_sink and slice_counts(w, nb)[2] + 1 < w.residual
+    for s_, (fused, nbytes) in enumerate(schedule):
+        c = caches[s_ % L]
+        i = (s_ // L) % w.steps
         plan.append((fused, ctypes.c_void_p(c.handle), ctypes.c_void_p(Ks[i].data_ptr()),
                      ctypes.c_void_p(Vs[i].data_ptr()), ctypes.c_void_p(Q[i % Q.shape[0]].data_ptr()),
                      ctypes.c_void_p(c._ws_ptr), c.ws_bytes))
-        step_bytes.append(algorithmic_bytes_seqs(w, [n0 + s // L + 1 for n0 in lens0]))
+        step_bytes.append(nbytes)
 
     def step(s: int, k):
         fused, h, kp, vp, qp, wsp, wsb = plan[s]
@@ -425,6 +562,16 @@ def main():
         if k in ev_call:
             hip.record(ev_call[k][1], sp)
 
+    # Clock settling: decode calls of every layer with the first query, which read
+    # the caches and change nothing, until settle_ms have passed.
+    t_set = time.perf_counter()
+    while (time.perf_counter() - t_set) * 1e3 < args.settle_ms:
+        for c in caches:
+            st = decode_fn(ctypes.c_void_p(c.handle), ctypes.c_void_p(Q[0].data_ptr()), out_p, lse_p,
+                           ctypes.c_void_p(c._ws_ptr), c.ws_bytes, sp)
+            if st:
+                raise kvq.KVQError(st, kvq.kvq_last_error())
+        torch.cuda.synchronize()
     for s in range(args.warmup):
         step(s, None)
     torch.cuda.synchronize()
@@ -451,7 +598,7 @@ def main():
     timed_bytes = [step_bytes[k] for k in timed_steps]
     launch_bytes = sum(timed_bytes) / len(timed_bytes)
     achieved = sum(timed_bytes) / (sum(dec_ms) * 1e-3) / 1e9
-    traffic = traffic_from_profile(w)
+    traffic = traffic_from_profile(w, args.steps, args.warmup, L)
 
     ceiling = stream_read_ceiling(torch, dev, kvq)
 
@@ -460,6 +607,7 @@ def main():
         print("bench: CPU baseline (oracle)", file=sys.stderr, flush=True)
         cpu = cpu_baseline(w, args.cpu_budget)
 
+    mf = (w.gqa >= 2 or w.bits == 8) and w.k_group >= 64 and w.v_group >= 64
     res = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -471,7 +619,11 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        # what the path computes in: packed integer codes times a fixed-point image
+        # (2^-19 relative) of the folded query and of the softmax weights, summed in
+        # int32; scales, softmax and accumulation in fp32
+        "dtype": "int%d codes x fixed-point, int32 %s; f32 softmax" % (
+            w.bits, "MFMA" if mf else "dot products"),
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "n_kv_heads": w.n_kv_heads,
                    "n_q_heads": w.n_q_heads, "head_dim": w.head_dim, "context": w.prefill,

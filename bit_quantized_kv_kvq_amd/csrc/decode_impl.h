@@ -1355,7 +1355,9 @@ void decode_kernel(DecArgs a) {
         // key and value rows, then the tile prefetch; everything up to the first
         // iteration's arithmetic is straight-line code for one storage dtype, so
         // each wait is for its own loads only, not for the prefetch behind them.
-        // Rows past the split's end reload its first row and get weight 0.
+        // Rows past the split's end reload its first row (row 0 when the slice has no
+        // full-precision token, which may never have been written); their scores are
+        // -inf and their value terms are skipped by selects.
         const int f0 = (int)((int64_t)split * nfp_s / a.nsplit);
         const int f1 = (int)((int64_t)(split + 1) * nfp_s / a.nsplit);
         constexpr int CPLF = 16;          // key channels per lane
@@ -1453,12 +1455,18 @@ void decode_kernel(DecArgs a) {
 #pragma unroll
                     for (int k = 0; k < TPWF / 2; ++k) {
                         const int sl = 2 * k + hb;
+                        // a row past the split's end holds a reloaded row that may never have
+                        // been written (no full-precision token at all): it is skipped by a
+                        // select, since a zero weight times non-finite bits is not zero
+                        const bool vsl = j0 + sl < f1;
 #pragma unroll
                         for (int h = 0; h < GQ; ++h) {
-                            const float psl = __shfl(pv[h], sl * LPTF);  // 0 past the end
+                            const float psl = __shfl(pv[h], sl * LPTF);
 #pragma unroll
-                            for (int c = 0; c < VCPL; ++c)
-                                accv[h][c] = fmaf(psl, packed_f32<DT>(vw[st][k], c), accv[h][c]);
+                            for (int c = 0; c < VCPL; ++c) {
+                                const float nv = fmaf(psl, packed_f32<DT>(vw[st][k], c), accv[h][c]);
+                                accv[h][c] = vsl ? nv : accv[h][c];
+                            }
                         }
                     }
                 }

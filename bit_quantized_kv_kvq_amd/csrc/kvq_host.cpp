@@ -560,6 +560,18 @@ kvq_status kvq_append_decode(kvq_cache* c, const void* k, const void* v, const v
     if (!c || !k || !v || !q || !out || !ws)
         return fail(KVQ_ERR_INVALID_ARG, "cache, k, v, q, out or ws is NULL");
     const Layout& L = c->L;
+    // Everything either path checks is checked here, before anything is enqueued:
+    // the two-call path below must not append the token and then fail its decode.
+    if (!aligned(k, 16) || !aligned(v, 16)) return fail(KVQ_ERR_INVALID_ARG, "k and v must be 16-byte aligned");
+    if (!aligned(q, 4) || !aligned(out, 4) || (lse && !aligned(lse, 4)) || !aligned(ws, 256))
+        return fail(KVQ_ERR_INVALID_ARG, "misaligned q, out, lse or ws");
+    if (1 > L.max_tokens - max_len(c))
+        return fail(KVQ_ERR_CAPACITY, "append of 1 token exceeds max_tokens %lld", (long long)L.max_tokens);
+    {
+        const size_t need = decode_workspace_bytes(L, c->nsplit_cap);
+        if (ws_bytes < need)
+            return fail(KVQ_ERR_BUFFER_TOO_SMALL, "workspace holds %zu bytes, needs %zu", ws_bytes, need);
+    }
     // A token that lands in a sink slot or fills the residual (flush), in any
     // sequence, takes the two-call path; every other token is appended inside the
     // decode launch (for sequences of different lengths, each at its own row).
@@ -573,19 +585,11 @@ kvq_status kvq_append_decode(kvq_cache* c, const void* k, const void* v, const v
         fused = c->nS >= L.S && c->r + 1 < L.R;
     }
     if (!fused) {
+        // The decode needs every sequence non-empty after the append: it is (one more token each).
         kvq_status st = kvq_append(c, k, v, 1, stream);
         if (st != KVQ_OK) return st;
         return kvq_decode_attention(c, q, out, lse, ws, ws_bytes, stream);
     }
-    if (!aligned(k, 16) || !aligned(v, 16)) return fail(KVQ_ERR_INVALID_ARG, "k and v must be 16-byte aligned");
-    if (!aligned(q, 4) || !aligned(out, 4) || (lse && !aligned(lse, 4)) || !aligned(ws, 256))
-        return fail(KVQ_ERR_INVALID_ARG, "misaligned q, out, lse or ws");
-    const int64_t total = c->nS + c->Lq + c->r;
-    if (1 > L.max_tokens - total)
-        return fail(KVQ_ERR_CAPACITY, "append of 1 token exceeds max_tokens %lld", (long long)L.max_tokens);
-    const size_t need = decode_workspace_bytes(L, c->nsplit_cap);
-    if (ws_bytes < need)
-        return fail(KVQ_ERR_BUFFER_TOO_SMALL, "workspace holds %zu bytes, needs %zu", ws_bytes, need);
     DecodeRequest rq;
     rq.Lq = c->Lq;
     rq.nS = c->nS;

@@ -7,7 +7,9 @@ every attention call checked.
 """
 from __future__ import annotations
 
+import os
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import pytest
@@ -79,14 +81,32 @@ class WorkloadRun:
         out, lse = self.cache.decode(self.Q[qi].contiguous())
         return out, lse
 
-    def run(self, on_attend):
-        """on_attend(n_steps, qi, out, lse) after every attention call of the schedule."""
-        for op, idx in wl.schedule(self.w):
+    def run(self, on_attend, fused: bool = False):
+        """on_attend(n_steps, qi, out, lse) after every attention call of the schedule.
+
+        fused: every append that an attention call follows is made with it in one
+        kvq_append_decode call, as the benchmark steps (the library itself takes
+        the two-call path on steps where a token becomes a sink or fills a residual).
+        """
+        sched = list(wl.schedule(self.w))
+        i = 0
+        while i < len(sched):
+            op, idx = sched[i]
+            if op == "append" and fused and i + 1 < len(sched) and sched[i + 1][0] == "attend":
+                qi = sched[i + 1][1]
+                out, lse = self.cache.append_decode(self.Ks[idx][:, :, None].contiguous(),
+                                                    self.Vs[idx][:, :, None].contiguous(),
+                                                    self.Q[qi].contiguous())
+                self.n_steps = idx + 1
+                on_attend(self.n_steps, qi, out, lse)
+                i += 2
+                continue
             if op == "append":
                 self.append_step(idx)
             else:
                 out, lse = self.attend(idx)
                 on_attend(self.n_steps, idx, out, lse)
+            i += 1
 
 
 def export_cpu(cache):
@@ -108,6 +128,50 @@ def assert_export_slice_matches(ex, st, b: int, kvh: int):
         got = np.ascontiguousarray(ex[name][b, kvh, :rows]).view(np.uint32)
         want = np.ascontiguousarray(st[name]).view(np.uint32)
         np.testing.assert_array_equal(got, want, err_msg=name)
+
+
+def _pool_size() -> int:
+    # at most 16 workers: the GPU machine's CPU share, whatever os.cpu_count() reports
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def oracle_states_iter(w, pairs, n_steps: int):
+    """(pair, oracle state) for each (b, kvh) pair, built on a thread pool (the
+    draws and the oracle's C code release the GIL), in the order of pairs."""
+    with ThreadPoolExecutor(_pool_size()) as ex:
+        yield from zip(pairs, ex.map(lambda p: oracle.slice_state(w, p[0], p[1], n_steps), pairs))
+
+
+def expected_outputs_many(w, pairs, n_steps: int, qi: int):
+    """{(b, kvh): (out [g, D], lse [g])} of the binary64 oracle, on a thread pool."""
+    with ThreadPoolExecutor(_pool_size()) as ex:
+        res = ex.map(lambda p: oracle.expected_outputs(w, p[0], p[1], n_steps, qi), pairs)
+        return dict(zip(pairs, res))
+
+
+def sample_pairs(w, n_random: int = 8, seed: int = 0):
+    """The four corner (sequence, kv head) slices and n_random seeded others."""
+    B, H = w.batch, w.n_kv_heads
+    pairs = sorted({(0, 0), (0, H - 1), (B - 1, 0), (B - 1, H - 1)})
+    rest = [(b, h) for b in range(B) for h in range(H) if (b, h) not in pairs]
+    rng = np.random.default_rng([w.seed, 77, seed])
+    pick = rng.choice(len(rest), size=min(n_random, len(rest)), replace=False) if rest else []
+    return pairs + sorted(rest[int(i)] for i in pick)
+
+
+def check_outputs_many(w, out_cpu, lse_cpu, pairs, n_steps: int, qi: int):
+    """check_outputs for several slices, with the oracle run on a thread pool."""
+    exp = expected_outputs_many(w, pairs, n_steps, qi)
+    g = w.gqa
+    worst = 0.0
+    for (b, kvh), (eo, el) in exp.items():
+        got = out_cpu[b, kvh * g:(kvh + 1) * g].astype(np.float64)
+        err = float(np.abs(got - eo).max())
+        lerr = float(np.abs(lse_cpu[b, kvh * g:(kvh + 1) * g].astype(np.float64) - el).max())
+        assert err <= ATOL, (w.name, b, kvh, n_steps, qi, err)
+        assert lerr <= ATOL, (w.name, b, kvh, n_steps, qi, lerr)
+        worst = max(worst, err, lerr)
+    return worst
 
 
 def check_outputs(w, out_cpu, lse_cpu, b: int, kvh: int, n_steps: int, qi: int):

@@ -51,3 +51,62 @@ def test_prefill_rounds_cover_each_prefill_once():
             assert n == 0 or t0 == got[b]          # each round continues where the last stopped
             got[b] += n
     assert got == lens
+
+
+@pytest.mark.parametrize("steps", [1, 5, 15, 16, 20, 31, 64, 127, 256, 1000])
+def test_event_stride_times_enough_launches(steps):
+    """At least 16 timed launches whatever --steps is (every launch below that), and
+    never more than one in eight of a long region."""
+    stride = bench.event_stride(steps)
+    timed = len(range(0, steps, stride))
+    assert timed >= min(16, steps)
+    assert 1 <= stride <= 8
+
+
+def test_step_plan_fuses_only_steps_without_sinks_or_flushes():
+    w = wl.get("long_128k_sink_int2").replace(prefill=300)   # S4, R256: 44 residual tokens
+    L = 2
+    plan = bench.step_plan(w, L, 2 * 300)
+    for s, (fused, nbytes) in enumerate(plan):
+        n_before = w.prefill + s // L
+        nS, Lq, r = bench.slice_counts(w, n_before)
+        assert fused == (nS >= w.n_sink and r + 1 < w.residual)
+        assert nbytes == bench.algorithmic_bytes_seqs(w, [n_before + 1])
+    assert not all(f for f, _ in plan) and any(f for f, _ in plan)
+
+
+def test_write_traffic_averages_the_timed_dispatches(tmp_path, monkeypatch):
+    """The traffic summary scales the decode kernel's counters by the probes' and
+    averages the last `steps` decode dispatches only (the timed ones)."""
+    import csv
+    import json
+    w = wl.get("llama7b_mha_int4")
+    steps, warmup = 4, 3
+    monkeypatch.setattr(bench, "traffic_path", lambda w_: str(tmp_path / "t.json"))
+
+    def write(path, rows):
+        with open(path, "w", newline="") as f:
+            wr = csv.DictWriter(f, ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+            wr.writeheader()
+            for r in rows:
+                wr.writerow(dict(zip(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"], r)))
+
+    dec = [(i, "kvq::dec::decode_kernel<4>", "FETCH_SIZE", 1000.0 if i < warmup else 100.0 * i)
+           for i in range(warmup + steps)]
+    decw = [(i, "kvq::dec::decode_kernel<4>", "WRITE_SIZE", 7.0) for i in range(warmup + steps)]
+    probe = [(100 + i, "kvq::stream_read_kernel", "FETCH_SIZE", 2 ** 21 / 2.0) for i in range(3)] + \
+            [(200 + i, "elementwise_kernel", "FETCH_SIZE", 2 ** 20 / 2.2) for i in range(3)]
+    copyw = [(300 + i, "elementwise_kernel", "WRITE_SIZE", 2 ** 20) for i in range(3)]
+    for name, rows in (("f", dec), ("w", decw), ("p", probe), ("c", copyw)):
+        write(tmp_path / name, rows)
+    bench.write_traffic(w, steps, warmup, 2, *(str(tmp_path / n) for n in "fwpc"))
+    t = json.load(open(tmp_path / "t.json"))
+    run = t["runs"][0]
+    timed = [100.0 * i for i in range(warmup, warmup + steps)]
+    assert run["fetch_kib_per_dispatch"] == sum(timed) / steps
+    assert abs(t["read_probe_fetch_scale"] - 2.0) < 1e-12 and abs(t["copy_probe_fetch_scale"] - 2.2) < 1e-12
+    assert run["hbm_bytes_per_launch"] == int(sum(timed) / steps * 1024 * 2.0 + 7.0 * 1024)
+    plan = bench.step_plan(w, 2, warmup + steps)[warmup:]
+    assert run["algorithmic_bytes_per_launch"] == int(sum(b for _, b in plan) / steps)
+    assert bench.traffic_from_profile(w, steps, warmup, 2) == run["hbm_bytes_per_launch"]
+    assert bench.traffic_from_profile(w, steps + 1, warmup, 2) is None

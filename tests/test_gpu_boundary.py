@@ -32,7 +32,8 @@ def _oracle_states(w, K, V):
     vf = wl.storage_to_f32(V, w.dtype)
     return {(b, h): oracle.build_slice(kf[b, h], vf[b, h], head_dim=w.head_dim, bits=w.bits,
                                        k_group=w.k_group, v_group=w.v_group,
-                                       residual=w.residual, n_sink=w.n_sink, codec=w.codec)
+                                       residual=w.residual, n_sink=w.n_sink, codec=w.codec,
+                                       outliers=w.outliers)
             for b in range(w.batch) for h in range(w.n_kv_heads)}
 
 
@@ -352,3 +353,66 @@ def test_stream_read_probe():
             kvq.kvq_stream_read_probe(*args, sink.data_ptr(), sp)
         assert ei.value.status == kvq.KVQ_ERR_INVALID_ARG, why
     assert torch.equal(x, torch.arange(1 << 20, dtype=torch.int32, device=DEV))  # read only
+
+
+# The cache buffer needs no initialisation and the workspace only zeroed counters.
+# Both are filled with 0xFF bytes (NaN as fp32, NaN or -NaN as bf16 / f16) before
+# the first append, and attention runs right after a prefill that leaves no
+# full-precision token in the slice (a whole number of residuals, no sinks): no
+# unwritten byte may reach an output, not even multiplied by a zero weight.
+@pytest.mark.parametrize("kw", [
+    dict(),                                                      # VALU stream, bf16
+    dict(dtype="f32", head_dim=64, v_group=16, bits=2),          # VALU stream, f32
+    dict(n_q_heads=8, k_group=64, residual=128, v_group=64),     # matrix cores, g = 4
+    dict(bits=8, k_group=64, residual=128, v_group=64),          # 8-bit, matrix cores
+    dict(outliers=1),                                            # dense-and-sparse
+])
+def test_uninitialised_buffers_do_not_reach_outputs(kw):
+    require_gpu()
+    w = _w(**kw)
+    log("case %s" % kw)
+    cache = make_cache(w, max_tokens=4 * w.residual)
+    cache._buf.fill_(0xFF)
+    ws_off = (w.batch * w.n_kv_heads * 4 + 255) // 256 * 256   # past the counters
+    base = cache._ws_ptr - cache._ws.data_ptr()
+    cache._ws[base + ws_off:].fill_(0xFF)
+    torch.cuda.synchronize()
+    n = 2 * w.residual
+    K, V = _tokens(w, n, 71, 2.0), _tokens(w, n, 72)
+    cache.append(to_torch(K, w.dtype, DEV), to_torch(V, w.dtype, DEV))
+    assert cache.state() == (n, 0, n, 0)
+    _attend_and_check(w, cache, K, V, seed=73)
+    # one fused step then has a single full-precision token
+    K1, V1 = _tokens(w, 1, 74), _tokens(w, 1, 75)
+    q = wl.random_tokens(76, (w.batch, w.n_q_heads, w.head_dim), w.dtype)
+    out, lse = cache.append_decode(to_torch(K1, w.dtype, DEV), to_torch(V1, w.dtype, DEV), to_torch(q, w.dtype, DEV))
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all() and torch.isfinite(lse).all()
+    _attend_and_check(w, cache, np.concatenate([K, K1], 2), np.concatenate([V, V1], 2), seed=77)
+
+
+# Split combines of more (split, head) pairs than the combine stages in LDS (512):
+# one sequence, one kv head, a split per key group.
+@pytest.mark.parametrize("kw,groups", [
+    (dict(n_q_heads=8, n_kv_heads=1, batch=1, k_group=64, residual=128, v_group=64), 100),   # 800 pairs
+    (dict(n_q_heads=4, n_kv_heads=1, batch=1, k_group=64, residual=128, v_group=64), 150),   # 600 pairs
+    (dict(n_q_heads=8, n_kv_heads=1, batch=1, bits=2, k_group=32, residual=64, v_group=32), 120),  # VALU
+])
+def test_combine_of_many_splits(kw, groups):
+    require_gpu()
+    w = _w(**kw)
+    n = groups * w.k_group + 5
+    log("case %s n=%d" % (kw, n))
+    cache = make_cache(w, max_tokens=n)
+    K, V = _tokens(w, n, 81, 2.0), _tokens(w, n, 82)
+    cache.append(to_torch(K, w.dtype, DEV), to_torch(V, w.dtype, DEV))
+    q = to_torch(wl.random_tokens(83, (w.batch, w.n_q_heads, w.head_dim), w.dtype), w.dtype, DEV)
+    ref, ref_lse = cache.decode(q)
+    ref, ref_lse = ref.clone(), ref_lse.clone()
+    cache.set_split_tokens(w.k_group)   # one split per key group
+    _attend_and_check(w, cache, K, V, seed=83)
+    out, lse = cache.decode(q)
+    torch.cuda.synchronize()
+    scale = max(1.0, ref.abs().max().item())
+    assert (out - ref).abs().max().item() <= 5e-5 * scale
+    assert (lse - ref_lse).abs().max().item() <= 5e-5 * max(1.0, ref_lse.abs().max().item())

@@ -99,6 +99,38 @@ def test_fused_step_validates_before_enqueueing():
     assert ei.value.status == kvq.KVQ_ERR_CAPACITY
 
 
+def test_fused_step_validates_before_a_flush_step():
+    """A step whose token fills the residual takes the two-call path (append, flush,
+    decode); a workspace or alignment error must still leave the cache unchanged, so
+    that a caller who fixes the arguments and retries appends the token once."""
+    require_gpu()
+    import bit_quantized_kv_kvq_amd as kvq
+    w = _w()
+    R = w.residual
+    c = make_cache(w, max_tokens=3 * R)
+    K = to_torch(wl.random_tokens(43, (w.batch, w.n_kv_heads, 2 * R, w.head_dim), w.dtype), w.dtype, DEV)
+    q = to_torch(wl.random_tokens(44, (w.batch, w.n_q_heads, w.head_dim), w.dtype), w.dtype, DEV)
+    c.append(K[:, :, :2 * R - 1].contiguous(), K[:, :, :2 * R - 1].contiguous())
+    before = c.state()
+    assert before[3] == R - 1   # the next token fills the residual
+    kt = K[:, :, 2 * R - 1:2 * R].contiguous()
+    out = torch.empty((w.batch, w.n_q_heads, w.head_dim), device=DEV)
+    s = torch.cuda.current_stream().cuda_stream
+    with pytest.raises(kvq.KVQError) as ei:   # workspace too small
+        kvq.kvq_append_decode(c.handle, kt.data_ptr(), kt.data_ptr(), q.data_ptr(), out.data_ptr(), 0,
+                              c._ws_ptr, 16, s)
+    assert ei.value.status == kvq.KVQ_ERR_BUFFER_TOO_SMALL
+    assert c.state() == before
+    with pytest.raises(kvq.KVQError) as ei:   # misaligned output
+        kvq.kvq_append_decode(c.handle, kt.data_ptr(), kt.data_ptr(), q.data_ptr(), out.data_ptr() + 2, 0,
+                              c._ws_ptr, c.ws_bytes, s)
+    assert ei.value.status == kvq.KVQ_ERR_INVALID_ARG
+    assert c.state() == before
+    o1, _ = c.append_decode(kt, kt, q)   # the retry flushes once
+    torch.cuda.synchronize()
+    assert c.state() == (before[0] + 1, 0, before[2] + R, 0)
+
+
 @pytest.mark.parametrize("kw", [dict(n_sink=3), dict(bits=2, n_q_heads=8, k_group=64, residual=128, v_group=64),
                                 dict(residual=96, log_window=32), dict(outliers=1)])
 def test_fused_step_on_sequences_of_different_lengths(kw):

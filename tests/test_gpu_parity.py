@@ -13,7 +13,8 @@ import torch
 import oracle
 import workloads as wl
 from tests.gpu_common import (ATOL, WorkloadRun, assert_export_slice_matches, check_outputs,
-                              export_cpu, gpu, log, make_cache, require_gpu)
+                              check_outputs_many, export_cpu, gpu, log, make_cache, oracle_states_iter,
+                              require_gpu, sample_pairs)
 
 pytestmark = gpu
 
@@ -136,50 +137,56 @@ def test_repeat_calls_are_bitwise_deterministic():
 
 
 # ---------------------------------------------------------------------------
-# full-size workloads, sampled slices
+# full-size workloads in the launch configuration the benchmark times
 # ---------------------------------------------------------------------------
 
-FULL = {
-    "llama7b_mha_int4": ([(0, 0), (3, 17), (7, 31)], None),
-    "kivi2_long_batch": ([(0, 0), (31, 31)], None),
-    "gqa_32k_int4": ([(0, 0), (15, 7)], None),
-    "long_128k_sink_int2": ([(0, 0), (0, 7)], {0, 3, 4, 7}),
-    "llama7b_mha_int4_sym": ([(0, 0), (5, 9)], None),
-    "llama7b_mha_int8": ([(0, 0), (7, 30)], None),
-    "llama7b_mha_int4_ragged": ([(0, 0), (4, 9), (7, 31)], None),
-    "logquant_gqa_int2": ([(0, 0), (6, 5)], None),
-    "llama7b_mha_int4_paged": ([(0, 0), (4, 9), (7, 31)], None),
-    "llama7b_mha_int4_outliers": ([(0, 0), (5, 21)], None),
-    "gqa_32k_int4_outliers": ([(0, 0), (15, 7)], None),
-}
+# Every workload at its full size, prefilled and then stepped exactly as bench.py
+# steps it: one kvq_append_decode call per decode step (the one-launch step with
+# the automatic split plan: one split per slice on the Llama-7B-shaped and KIVI
+# workloads, the single-split branch of the kernel; the library falls back to
+# append + decode on sink and flush steps).  After the prefill, every slice's
+# export of the Llama-7B-shaped, KIVI 2-bit, GQA and long-context workloads is
+# compared bit for bit (a sample of slices for the others); at the first and last decode steps and at every step
+# that flushed, the four corner slices and eight seeded others are compared with
+# the oracle element by element.
+FULL = ["tiny", "llama7b_mha_int4", "kivi2_long_batch", "gqa_32k_int4", "long_128k_sink_int2",
+        "llama7b_mha_int4_sym", "llama7b_mha_int8", "llama7b_mha_int4_ragged", "logquant_gqa_int2",
+        "llama7b_mha_int4_paged", "llama7b_mha_int4_outliers", "gqa_32k_int4_outliers"]
+EXPORT_ALL = {"llama7b_mha_int4", "kivi2_long_batch", "gqa_32k_int4", "long_128k_sink_int2"}
 
 
-@pytest.mark.parametrize("name", list(FULL))
-def test_full_size_sampled(name):
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_bench_path(name):
     require_gpu()
     w = wl.get(name)
-    samples, steps_to_check = FULL[name]
-    log("full-size case %s: %s" % (name, w.description))
+    pairs = sample_pairs(w)
+    log("full-size case %s: %s; sampled slices %s" % (name, w.description, pairs))
     run = WorkloadRun(w)
     log("  prefill uploaded and quantized")
     ex = export_cpu(run.cache)
-    for b, h in samples:
-        assert_export_slice_matches(ex, oracle.slice_state(w, b, h, 0), b, h)
+    every = [(b, h) for b in range(w.batch) for h in range(w.n_kv_heads)]
+    n_exp = 0
+    for (b, h), st in oracle_states_iter(w, every if name in EXPORT_ALL else pairs, 0):
+        assert_export_slice_matches(ex, st, b, h)
+        n_exp += 1
     del ex
+    log("  exports after the prefill bit-exact on %d slices" % n_exp)
     last_q = wl.n_queries(w) - 1
-    checked = []
+    checked, worst = [], [0.0]
+    last_Lq = [run.cache.state()[2]]
 
     def on_attend(n_steps, qi, out, lse):
-        want = qi in (0, last_q) or (steps_to_check is not None and qi in steps_to_check)
-        if not want:
+        Lq = run.cache.state()[2]
+        flushed, last_Lq[0] = Lq != last_Lq[0], Lq
+        if not (qi in (0, last_q) or flushed):
             return
         torch.cuda.synchronize()
         o, l = out.cpu().numpy(), lse.cpu().numpy()
-        for b, h in samples:
-            checked.append(check_outputs(w, o, l, b, h, n_steps, qi))
+        worst[0] = max(worst[0], check_outputs_many(w, o, l, pairs, n_steps, qi))
+        checked.append(qi)
 
-    run.run(on_attend)
+    run.run(on_attend, fused=True)
     ex = export_cpu(run.cache)
-    for b, h in samples:
-        assert_export_slice_matches(ex, oracle.slice_state(w, b, h, w.steps), b, h)
-    log("  %s: %d sampled outputs, max err %.3g" % (name, len(checked), max(checked)))
+    for (b, h), st in oracle_states_iter(w, pairs, w.steps):
+        assert_export_slice_matches(ex, st, b, h)
+    log("  %s: queries %s checked on %d slices, max err %.3g" % (name, checked, len(pairs), worst[0]))
