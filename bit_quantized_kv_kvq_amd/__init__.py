@@ -29,11 +29,13 @@ STATUS_NAMES = {0: "KVQ_OK", -1: "KVQ_ERR_INVALID_ARG", -2: "KVQ_ERR_UNSUPPORTED
                 -3: "KVQ_ERR_CAPACITY", -4: "KVQ_ERR_BUFFER_TOO_SMALL", -5: "KVQ_ERR_DEVICE"}
 
 KVQ_F32, KVQ_BF16, KVQ_F16 = 0, 1, 2
+KVQ_STATIC_SCRATCH_BYTES = 16 << 20
 KVQ_CODEC_ASYMMETRIC, KVQ_CODEC_SYMMETRIC = 0, 1
 KVQ_RETAIN_WINDOW, KVQ_RETAIN_LOG = 0, 1
 
 EXPORTED = ["kvq_cache_bytes", "kvq_cache_create", "kvq_cache_destroy", "kvq_append",
-            "kvq_decode_workspace_bytes", "kvq_decode_attention", "kvq_append_decode",
+            "kvq_decode_workspace_bytes", "kvq_decode_attention", "kvq_decode_attention_static",
+            "kvq_append_decode",
             "kvq_dequantize", "kvq_export",
             "kvq_cache_state", "kvq_set_split_tokens", "kvq_set_timing_events", "kvq_stream_read_probe",
             "kvq_append_ragged", "kvq_seq_lengths", "kvq_release_sequence", "kvq_pool_free_pages",
@@ -79,6 +81,7 @@ def lib() -> ctypes.CDLL:
             "kvq_append": [P, P, P, i64, P],
             "kvq_decode_workspace_bytes": [P, ctypes.POINTER(ctypes.c_size_t)],
             "kvq_decode_attention": [P, P, P, P, P, ctypes.c_size_t, P],
+            "kvq_decode_attention_static": [P, P, P, P, P],
             "kvq_append_decode": [P, P, P, P, P, P, P, ctypes.c_size_t, P],
             "kvq_dequantize": [P, P, P, P],
             "kvq_export": [P, P, P, P, P, P, P, P],
@@ -151,6 +154,12 @@ def kvq_decode_attention(handle: int, q_ptr: int, out_ptr: int, lse_ptr: int, ws
     _check(lib().kvq_decode_attention(ctypes.c_void_p(handle), ctypes.c_void_p(q_ptr),
                                       ctypes.c_void_p(out_ptr), ctypes.c_void_p(lse_ptr or None),
                                       ctypes.c_void_p(ws_ptr), ws_bytes, ctypes.c_void_p(stream)))
+
+
+def kvq_decode_attention_static(handle: int, q_ptr: int, out_ptr: int, lse_ptr: int, stream: int):
+    _check(lib().kvq_decode_attention_static(ctypes.c_void_p(handle), ctypes.c_void_p(q_ptr),
+                                             ctypes.c_void_p(out_ptr), ctypes.c_void_p(lse_ptr or None),
+                                             ctypes.c_void_p(stream)))
 
 
 def kvq_append_decode(handle: int, k_ptr: int, v_ptr: int, q_ptr: int, out_ptr: int, lse_ptr: int,

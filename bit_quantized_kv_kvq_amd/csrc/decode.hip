@@ -3,6 +3,8 @@
 // (counters, then split maxima/sums, then split accumulators).
 #include <hip/hip_ext.h>
 
+#include <mutex>
+
 #include "decode_dispatch.h"
 
 namespace kvq {
@@ -105,6 +107,42 @@ Choice choose(const Layout& L) {
 }  // namespace
 
 size_t decode_workspace_bytes(const Layout& L, int max_splits) { return ws_layout(L, max_splits).total; }
+
+namespace {
+// The decode workspace of callers that cannot allocate.  In host code `scratch`
+// names a host-side stand-in, not device memory: the device address comes from
+// hipGetSymbolAddress, per device.
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+__global__ __launch_bounds__(256) void clear_words_kernel(uint4* p, size_t n16) {
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += (size_t)gridDim.x * blockDim.x)
+        p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+}  // namespace
+
+hipError_t static_scratch(hipStream_t stream, void** ptr) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (p == nullptr) return hipErrorInvalidSymbol;
+        clear_words_kernel<<<1024, 256, 0, stream>>>(static_cast<uint4*>(p), kStaticScratchBytes / 16);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
+}
 
 bool decode_supported(const Layout& L) { return choose(L).fn != nullptr; }
 

@@ -17,6 +17,8 @@
 
 using namespace kvq;
 
+static_assert(KVQ_STATIC_SCRATCH_BYTES == kStaticScratchBytes, "the header states the static scratch's size");
+
 namespace kvq {
 // probe.hip: one streaming read of n16 16-byte words at buf with `blocks` workgroups of 256
 hipError_t launch_stream_read(const void* buf, int64_t n16, int blocks, unsigned* sink, hipStream_t stream);
@@ -529,13 +531,30 @@ kvq_status kvq_decode_workspace_bytes(const kvq_cache* c, size_t* bytes) {
     return ok();
 }
 
-kvq_status kvq_decode_attention(kvq_cache* c, const void* q, float* out, float* lse, void* ws,
-                                size_t ws_bytes, void* stream) {
-    if (!c || !q || !out || !ws) return fail(KVQ_ERR_INVALID_ARG, "cache, q, out or ws is NULL");
-    if (!aligned(q, 4) || !aligned(out, 4) || (lse && !aligned(lse, 4)) || !aligned(ws, 256))
-        return fail(KVQ_ERR_INVALID_ARG, "misaligned q, out, lse or ws");
+}  // extern "C"
+
+namespace {
+
+// The checks of a decode call that do not involve the workspace.
+kvq_status decode_checks(const kvq_cache* c, const void* q, const float* out, const float* lse) {
+    if (!c || !q || !out) return fail(KVQ_ERR_INVALID_ARG, "cache, q or out is NULL");
+    if (!aligned(q, 4) || !aligned(out, 4) || (lse && !aligned(lse, 4)))
+        return fail(KVQ_ERR_INVALID_ARG, "misaligned q, out or lse");
     if (*std::min_element(c->len.begin(), c->len.end()) == 0)
         return fail(KVQ_ERR_INVALID_ARG, c->ragged ? "attention on an empty sequence" : "attention on an empty cache");
+    return KVQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kvq_status kvq_decode_attention(kvq_cache* c, const void* q, float* out, float* lse, void* ws,
+                                size_t ws_bytes, void* stream) {
+    kvq_status st = decode_checks(c, q, out, lse);
+    if (st != KVQ_OK) return st;
+    if (!ws) return fail(KVQ_ERR_INVALID_ARG, "ws is NULL");
+    if (!aligned(ws, 256)) return fail(KVQ_ERR_INVALID_ARG, "misaligned ws");
     const size_t need = decode_workspace_bytes(c->L, c->nsplit_cap);
     if (ws_bytes < need)
         return fail(KVQ_ERR_BUFFER_TOO_SMALL, "workspace holds %zu bytes, needs %zu", ws_bytes, need);
@@ -549,10 +568,21 @@ kvq_status kvq_decode_attention(kvq_cache* c, const void* q, float* out, float* 
     rq.nsplit_cap = c->nsplit_cap;
     rq.ev_start = c->ev_start;
     rq.ev_stop = c->ev_stop;
-    kvq_status st = check_hip(launch_decode(c->L, c->P, rq, q, out, lse, ws, c->sm_scale, (hipStream_t)stream),
-                              "decode");
+    st = check_hip(launch_decode(c->L, c->P, rq, q, out, lse, ws, c->sm_scale, (hipStream_t)stream), "decode");
     if (st != KVQ_OK) return st;
     return ok();
+}
+
+kvq_status kvq_decode_attention_static(kvq_cache* c, const void* q, float* out, float* lse, void* stream) {
+    kvq_status st = decode_checks(c, q, out, lse);
+    if (st != KVQ_OK) return st;
+    const size_t need = decode_workspace_bytes(c->L, c->nsplit_cap);
+    if (need > kStaticScratchBytes)
+        return fail(KVQ_ERR_BUFFER_TOO_SMALL, "this cache's decode needs %zu bytes of scratch; the static "
+                    "scratch holds %zu (use kvq_decode_attention with a workspace)", need, kStaticScratchBytes);
+    void* ws = nullptr;
+    if ((st = check_hip(static_scratch((hipStream_t)stream, &ws), "static scratch")) != KVQ_OK) return st;
+    return kvq_decode_attention(c, q, out, lse, ws, need, stream);
 }
 
 kvq_status kvq_append_decode(kvq_cache* c, const void* k, const void* v, const void* q, float* out,

@@ -211,6 +211,15 @@ bool decode_supported(const Layout& L);
 
 size_t decode_workspace_bytes(const Layout& L, int max_splits);
 
+// Static scratch for callers that cannot allocate: one file-scope device array of
+// kStaticScratchBytes per device, laid out as a decode workspace.  Its device
+// address (hipGetSymbolAddress, taken once per device with that device current)
+// is returned in *ptr; the first call on a device also enqueues, on `stream`, a
+// clear of the array (the completion counters must start at zero; every decode
+// leaves them at zero).
+constexpr size_t kStaticScratchBytes = (size_t)16 << 20;
+hipError_t static_scratch(hipStream_t stream, void** ptr);
+
 // Dequantize to [BH][T_out][D] fp32 (T_out = nS + Lq + r, the longest sequence's
 // length with rg); with rg, rows past a slice's own length are not written.
 hipError_t launch_dequantize(const Layout& L, const DevPtrs& P, int64_t nS, int64_t Lq, int64_t r,

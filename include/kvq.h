@@ -209,6 +209,28 @@ kvq_status kvq_decode_attention(kvq_cache* cache, const void* q, float* out, flo
                                 void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * kvq_decode_attention for callers that cannot allocate device memory or pass a
+ * workspace (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation): the same computation and result, bit for bit, with the
+ * workspace taken from a static array inside the library instead of `ws`.
+ *   - The array holds 16 MiB per device (KVQ_STATIC_SCRATCH_BYTES) and is
+ *     allocated when the library is loaded; each device the library runs on
+ *     keeps its own copy until the process ends.  The call itself allocates
+ *     nothing.
+ *   - Every call on one device shares that device's array: calls that overlap
+ *     on one device (on different streams or threads) race and give undefined
+ *     results.  Calls ordered on one stream are safe.
+ *   - The first call on a device clears the array on `stream` before its decode;
+ *     every call leaves the array's completion counters at zero for the next.
+ *   q, out, lse, stream : as for kvq_decode_attention.
+ * Errors: those of kvq_decode_attention, and BUFFER_TOO_SMALL when this cache's
+ * decode needs more than KVQ_STATIC_SCRATCH_BYTES of workspace
+ * (kvq_decode_workspace_bytes), checked before anything is enqueued.
+ */
+#define KVQ_STATIC_SCRATCH_BYTES ((size_t)16 << 20)
+kvq_status kvq_decode_attention_static(kvq_cache* cache, const void* q, float* out, float* lse, void* stream);
+
+/*
  * One decode step in one call: append one token per sequence, then decode
  * attention with the given query; the result and the cache state are exactly
  * those of kvq_append(cache, k, v, 1, stream) followed by
