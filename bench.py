@@ -54,14 +54,17 @@ DECODE_SOURCES = ["decode_impl.h", "decode_dispatch.h", "decode.hip", "kvq_inter
                   "decode_mf_b4_d128.hip", "decode_mf_b2_d128.hip", "decode_mf_b4_d64.hip", "decode_mf_b2_d64.hip",
                   "decode_mf_b8_d128.hip", "decode_mf_b8_d64.hip",
                   "decode_sp_b4_d128.hip", "decode_sp_b2_d128.hip", "decode_sp_b4_d64.hip", "decode_sp_b2_d64.hip",
-                  "decode_mfsp_b4_d128.hip", "decode_mfsp_b2_d128.hip"]
+                  "decode_mfsp_b4_d128.hip", "decode_mfsp_b2_d128.hip",
+                  "decode_kt_b4_d128.hip", "decode_kt_b2_d128.hip", "decode_kt_b8_d128.hip",
+                  "decode_kt_b4_d64.hip", "decode_kt_b2_d64.hip", "decode_kt_b8_d64.hip"]
 
 
 def algorithmic_bytes(w: wl.Workload, n_sink: int, n_quant: int, n_resid: int) -> int:
     """Bytes the method itself must move for one decode-attention call."""
     D, e = w.head_dim, wl.elem_bytes(w.dtype)
+    kmeta = n_quant * 2 * 4 if w.key_axis else (n_quant // w.k_group) * 2 * D * 4  # per token, or per channel
     per_slice = (n_quant * 2 * D * w.bits // 8                 # K and V codes
-                 + (n_quant // w.k_group) * 2 * D * 4            # K scale + zero
+                 + kmeta                                         # K scale + zero
                  + n_quant * (D // w.v_group) * 2 * 4            # V scale + zero
                  + (n_sink + n_resid) * 2 * D * e)               # full-precision tokens
     if w.outliers:  # one per key channel group and per value group: fp32 value, place and code
@@ -380,7 +383,7 @@ def cpu_baseline(w: wl.Workload, budget_s: float):
         k, v = args
         return oracle.build_slice(k, v, head_dim=w.head_dim, bits=w.bits, k_group=w.k_group,
                                   v_group=w.v_group, residual=w.residual, n_sink=w.n_sink, codec=w.codec,
-                                  log_window=w.log_window, outliers=w.outliers)
+                                  log_window=w.log_window, outliers=w.outliers, key_axis=w.key_axis)
 
     toks = [oracle.slice_tokens_f32(w, b, h, 0) for b, h in sample[:threads]]
     with ThreadPoolExecutor(threads) as ex:
@@ -484,7 +487,8 @@ def main():
                       residual=w.residual, n_sink=w.n_sink, dtype=TORCH_DTYPES[w.dtype],
                       max_tokens=max_tokens, device=dev, codec=w.codec,
                       retention=kvq.KVQ_RETAIN_LOG if w.log_window else kvq.KVQ_RETAIN_WINDOW,
-                      page_groups=w.page_groups, pool_pages=pool_pages, outliers=w.outliers)
+                      page_groups=w.page_groups, pool_pages=pool_pages, outliers=w.outliers,
+                      key_axis=w.key_axis)
         if args.split_tokens:
             c.set_split_tokens(args.split_tokens)
         if len(rounds) == 1 and not ragged:
@@ -633,6 +637,7 @@ def main():
                    "codec": "symmetric" if w.codec else "asymmetric",
                    **({"retention": "log-sparse", "log_window": w.log_window} if w.log_window else {}),
                    **({"outliers": "one per quantization vector"} if w.outliers else {}),
+                   **({"keys": "per token over head_dim (head-granular)"} if w.key_axis else {}),
                    **({"page_groups": w.page_groups, "pool_pages": pool_pages,
                        "prefill_chunk": w.prefill_chunk} if w.page_groups else {}),
                    "layers_rotated": L, "parallelism": "single GPU"},

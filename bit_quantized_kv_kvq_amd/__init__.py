@@ -32,6 +32,7 @@ KVQ_F32, KVQ_BF16, KVQ_F16 = 0, 1, 2
 KVQ_STATIC_SCRATCH_BYTES = 16 << 20
 KVQ_CODEC_ASYMMETRIC, KVQ_CODEC_SYMMETRIC = 0, 1
 KVQ_RETAIN_WINDOW, KVQ_RETAIN_LOG = 0, 1
+KVQ_KEY_PER_CHANNEL, KVQ_KEY_PER_TOKEN = 0, 1
 
 EXPORTED = ["kvq_cache_bytes", "kvq_cache_create", "kvq_cache_destroy", "kvq_append",
             "kvq_decode_workspace_bytes", "kvq_decode_attention", "kvq_decode_attention_static",
@@ -58,7 +59,7 @@ class Config(ctypes.Structure):
                 ("max_tokens", ctypes.c_int64), ("sm_scale", ctypes.c_float),
                 ("codec", ctypes.c_int32), ("retention", ctypes.c_int32),
                 ("page_groups", ctypes.c_int32), ("pool_pages", ctypes.c_int64),
-                ("outliers", ctypes.c_int32)]
+                ("outliers", ctypes.c_int32), ("key_axis", ctypes.c_int32)]
 
 
 _lib = None
@@ -116,9 +117,11 @@ def _check(status: int):
 
 def make_config(*, batch, n_kv_heads, n_q_heads, head_dim, bits, k_group, v_group, residual,
                 n_sink=0, dtype=KVQ_BF16, max_tokens, sm_scale=0.0, codec=KVQ_CODEC_ASYMMETRIC,
-                retention=KVQ_RETAIN_WINDOW, page_groups=0, pool_pages=0, outliers=0) -> Config:
+                retention=KVQ_RETAIN_WINDOW, page_groups=0, pool_pages=0, outliers=0,
+                key_axis=KVQ_KEY_PER_CHANNEL) -> Config:
     return Config(batch, n_kv_heads, n_q_heads, head_dim, bits, k_group, v_group, residual,
-                  n_sink, dtype, max_tokens, sm_scale, codec, retention, page_groups, pool_pages, outliers)
+                  n_sink, dtype, max_tokens, sm_scale, codec, retention, page_groups, pool_pages, outliers,
+                  key_axis)
 
 
 def kvq_cache_bytes(cfg: Config) -> int:

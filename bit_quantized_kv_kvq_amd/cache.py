@@ -33,14 +33,15 @@ class Cache:
     `page_groups` > 0 keeps the quantized records in pages of that many key
     groups from a pool of `pool_pages` pages (0: one per sequence at capacity).
     `outliers` = 1 keeps one full-precision outlier per quantization vector
-    (KVQuant's dense-and-sparse groups).
+    (KVQuant's dense-and-sparse groups).  `key_axis` = KVQ_KEY_PER_TOKEN groups
+    each token's key over its head_dim channels (Atom's head granularity).
     """
 
     def __init__(self, *, batch: int, n_kv_heads: int, n_q_heads: int, head_dim: int, bits: int,
                  k_group: int, v_group: int, residual: int, max_tokens: int, n_sink: int = 0,
                  dtype: torch.dtype = torch.bfloat16, sm_scale: float = 0.0,
                  device: Optional[torch.device] = None, codec: int = 0, retention: int = 0,
-                 page_groups: int = 0, pool_pages: int = 0, outliers: int = 0):
+                 page_groups: int = 0, pool_pages: int = 0, outliers: int = 0, key_axis: int = 0):
         _k.lib()
         self.device = torch.device(device or "cuda")
         self.dtype = dtype
@@ -49,7 +50,7 @@ class Cache:
                                   residual=residual, n_sink=n_sink, dtype=torch_dtype_code(dtype),
                                   max_tokens=max_tokens, sm_scale=sm_scale, codec=codec,
                                   retention=retention, page_groups=page_groups, pool_pages=pool_pages,
-                                  outliers=outliers)
+                                  outliers=outliers, key_axis=key_axis)
         self.nbytes = _k.kvq_cache_bytes(self.cfg)
         # over-allocate by 256 bytes so the handle's buffer is 256-byte aligned
         self._buf = torch.empty(self.nbytes + 256, dtype=torch.uint8, device=self.device)
@@ -182,7 +183,8 @@ class Cache:
         dev = self.device
         out = dict(
             k_codes=torch.zeros((c.batch, c.n_kv_heads, Lq, c.head_dim), dtype=torch.uint8, device=dev),
-            k_scale=torch.zeros((c.batch, c.n_kv_heads, Lq // c.k_group, c.head_dim),
+            k_scale=torch.zeros((c.batch, c.n_kv_heads, Lq, 1) if c.key_axis else
+                                (c.batch, c.n_kv_heads, Lq // c.k_group, c.head_dim),
                                 dtype=torch.float32, device=dev),
             v_codes=torch.zeros((c.batch, c.n_kv_heads, Lq, c.head_dim), dtype=torch.uint8, device=dev),
             v_scale=torch.zeros((c.batch, c.n_kv_heads, Lq, c.head_dim // c.v_group),

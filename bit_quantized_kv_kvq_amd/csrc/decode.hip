@@ -99,6 +99,35 @@ Choice choose(const Layout& L) {
             wave = ((L.gqa * dec::kLimbs * L.D + 2 * L.gqa * L.nvg * dec::kLimbs * c.tile + 15) & ~15) + spb;
         }
     }
+    if (L.key_axis) {
+        // per-token keys (64-token tiles, one or two per record): on the matrix cores
+        // where the per-channel cache would be, else the VALU stream for one query head
+        // per kv head; other shapes have no kernel
+        c.fn = nullptr;
+        c.occ = 1;
+        c.tile = 64;
+        c.tpg = L.G / 64;
+        const bool mf = (L.gqa >= 2 || L.bits == 8) && L.GV >= 64 && (L.D == 128 || L.nvg == 1);
+        const void* kt = nullptr;
+        if (mf || (L.gqa == 1 && L.bits != 8)) {
+            if (L.bits == 2 && L.D == 128) kt = dec::decode_kt_kernel_ptr<2, 128>(L.gqa, c.cpl, c.tpg, L.nvg, mf);
+            if (L.bits == 4 && L.D == 128) kt = dec::decode_kt_kernel_ptr<4, 128>(L.gqa, c.cpl, c.tpg, L.nvg, mf);
+            if (L.bits == 8 && L.D == 128) kt = dec::decode_kt_kernel_ptr<8, 128>(L.gqa, c.cpl, c.tpg, L.nvg, mf);
+            if (L.bits == 2 && L.D == 64) kt = dec::decode_kt_kernel_ptr<2, 64>(L.gqa, c.cpl, c.tpg, L.nvg, mf);
+            if (L.bits == 4 && L.D == 64) kt = dec::decode_kt_kernel_ptr<4, 64>(L.gqa, c.cpl, c.tpg, L.nvg, mf);
+            if (L.bits == 8 && L.D == 64) kt = dec::decode_kt_kernel_ptr<8, 64>(L.gqa, c.cpl, c.tpg, L.nvg, mf);
+        }
+        if (kt != nullptr) {
+            c.fn = kt;
+            c.occ = dec::two_waves(mf, L.bits, L.gqa, false) ? 2 : 1;
+            if (mf) {
+                const int rbk = (L.gqa + 3) / 4;
+                wave = rbk * (L.D / 64) * 1024 + 2 * L.nvg * rbk * 1024;  // MStream::lds_bytes
+            } else {
+                wave = (L.gqa * dec::kLimbs * L.D + 2 * L.gqa * L.nvg * dec::kLimbs * c.tile + 15) & ~15;
+            }
+        }
+    }
     const int wg = kWaves * L.gqa * L.D + kWaves * L.gqa * 2 + 4;  // LdsPlan::wg_floats
     c.lds = kWaves * wave + 4 * wg;
     return c;

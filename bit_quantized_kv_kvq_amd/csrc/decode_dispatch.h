@@ -30,6 +30,25 @@ const void* decode_sp_kernel_ptr(int gqa, int cpl, int tile, int tpg, int nvg);
 // value groups per token), or nullptr.  Defined in decode_mfsp_b<bits>_d128.hip.
 template <int BITS>
 const void* decode_mfsp_kernel_ptr(int gqa, int tpg, int nvg);
+// Per-token keys: the VALU stream (one query head per kv head, 2- and 4-bit codes,
+// 64-token tiles) when mf is false, the matrix-core stream otherwise; entry for
+// (query heads per kv head, key channels per lane, 64-token tiles per key group,
+// value groups per token), or nullptr.  Defined in decode_kt_b<bits>_d<head_dim>.hip.
+template <int BITS, int D>
+const void* decode_kt_kernel_ptr(int gqa, int cpl, int tpg, int nvg, bool mf);
+template <>
+const void* decode_kt_kernel_ptr<2, 128>(int, int, int, int, bool);
+template <>
+const void* decode_kt_kernel_ptr<4, 128>(int, int, int, int, bool);
+template <>
+const void* decode_kt_kernel_ptr<8, 128>(int, int, int, int, bool);
+template <>
+const void* decode_kt_kernel_ptr<2, 64>(int, int, int, int, bool);
+template <>
+const void* decode_kt_kernel_ptr<4, 64>(int, int, int, int, bool);
+template <>
+const void* decode_kt_kernel_ptr<8, 64>(int, int, int, int, bool);
+
 template <>
 const void* decode_mfsp_kernel_ptr<4>(int, int, int);
 template <>
@@ -185,6 +204,40 @@ const void* decode_mf_kernel_ptr<8, 64>(int, int, int);
     const void* decode_sp_kernel_ptr<BITS, D_>(int gqa, int cpl, int tile, int tpg, int nvg) { \
         KVQ_DECODE_SP_TABLE_D##D_(BITS)                                         \
         return nullptr;                                                         \
+    }
+
+// per-token keys: key groups of 64 or 128 tokens (one or two 64-token tiles)
+#define KVQ_DECODE_KT_VALU(BITS, D_, CPL_, TPG_)                                         \
+    if (!mf && gqa == 1 && cpl == CPL_ && tpg == TPG_)                                  \
+        return reinterpret_cast<const void*>(                                          \
+            &decode_kernel<BITS, D_, 1, CPL_, 64, TPG_, false, 1, false, false, true>);
+#define KVQ_DECODE_KT_MF(BITS, D_, GQ_, TPG_, NVG_)                                      \
+    if (mf && gqa == GQ_ && tpg == TPG_ && nvg == NVG_)                                 \
+        return reinterpret_cast<const void*>(                                          \
+            &decode_kernel<BITS, D_, GQ_, 16, 64, TPG_, true, NVG_, false, false, true>);
+#define KVQ_DECODE_KT_MF_TPG(BITS, D_, GQ_, NVG_) \
+    KVQ_DECODE_KT_MF(BITS, D_, GQ_, 1, NVG_) KVQ_DECODE_KT_MF(BITS, D_, GQ_, 2, NVG_)
+#define KVQ_DECODE_KT_MF_GQ(BITS, D_, NVG_)                                             \
+    KVQ_DECODE_KT_MF_TPG(BITS, D_, 2, NVG_) KVQ_DECODE_KT_MF_TPG(BITS, D_, 4, NVG_)     \
+    KVQ_DECODE_KT_MF_TPG(BITS, D_, 8, NVG_)
+#define KVQ_DECODE_KT_TABLE_D128(BITS)                                                  \
+    KVQ_DECODE_KT_VALU(BITS, 128, 32, 1) KVQ_DECODE_KT_VALU(BITS, 128, 32, 2)           \
+    KVQ_DECODE_KT_VALU(BITS, 128, 16, 1) KVQ_DECODE_KT_VALU(BITS, 128, 16, 2)           \
+    KVQ_DECODE_KT_MF_GQ(BITS, 128, 1) KVQ_DECODE_KT_MF_GQ(BITS, 128, 2)
+#define KVQ_DECODE_KT_TABLE_D64(BITS)                                                   \
+    KVQ_DECODE_KT_VALU(BITS, 64, 16, 1) KVQ_DECODE_KT_VALU(BITS, 64, 16, 2) KVQ_DECODE_KT_MF_GQ(BITS, 64, 1)
+// 8-bit codes: the matrix cores only, one query head per kv head as well
+#define KVQ_DECODE_KT8_TABLE_D128                                                       \
+    KVQ_DECODE_KT_MF_TPG(8, 128, 1, 1) KVQ_DECODE_KT_MF_TPG(8, 128, 1, 2)               \
+    KVQ_DECODE_KT_MF_GQ(8, 128, 1) KVQ_DECODE_KT_MF_GQ(8, 128, 2)
+#define KVQ_DECODE_KT8_TABLE_D64 KVQ_DECODE_KT_MF_TPG(8, 64, 1, 1) KVQ_DECODE_KT_MF_GQ(8, 64, 1)
+
+#define KVQ_DEFINE_KT_KERNEL_PTR(BITS, D_, TABLE)                                       \
+    template <>                                                                         \
+    const void* decode_kt_kernel_ptr<BITS, D_>(int gqa, int cpl, int tpg, int nvg, bool mf) { \
+        (void)cpl;                                                                      \
+        TABLE                                                                           \
+        return nullptr;                                                                 \
     }
 
 #define KVQ_DEFINE_KERNEL_PTR(BITS, D_)                                               \

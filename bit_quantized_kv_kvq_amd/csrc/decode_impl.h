@@ -394,7 +394,12 @@ __host__ __device__ constexpr bool two_waves(bool mf, int bits, int gq, bool sp)
     return gq <= 4 && (sp || (mf && bits == 2));
 }
 
-template <int BITS, int D, int GQ, int TPG, int NVG, bool SP = false>
+// KT: per-token keys (one scale and zero point per token over its D channels):
+// the query's digit rows are folded once per wave, not per key group, and each
+// score takes its token's scale s_t and zero z_t after the product:
+//   q . k'_t = s_t (sum_c q_c u_tc - (z_t - o) sum_c q_c)
+// with sum_c q_c taken over the query's fixed-point image.
+template <int BITS, int D, int GQ, int TPG, int NVG, bool SP = false, bool KT = false>
 struct MStream {
     static constexpr int TM = 64;               // tokens per tile
     static constexpr int NSB = TM / 16;         // key products per tile and row block
@@ -427,6 +432,7 @@ struct MStream {
         u32x4 v[NVB][VBB];
         typename UVec<2 * NVG>::T vm[NSB];  // (scale, zero) of each value group of token 16 sb + l % 16
         typename UVec<KM>::T ks, kz;
+        typename UVec<2>::T km[NSB];  // KT: (scale, zero) of token 16 sb + l % 16
         // SP only: key outliers of the KM fold channels (values; dword of u16 fields),
         // value outliers of token 16 sb + l % 16 (values; dword of its groups' u16 fields)
         typename UVec<KM>::T kov;
@@ -443,12 +449,13 @@ struct MStream {
     __amdgpu_buffer_rsrc_t rs;
     GroupAddr ga;
     int last_group, lane;
-    uint32_t k_off, v_off, vm_off, km_off;
+    uint32_t k_off, v_off, vm_off, km_off, kt_off;
     uint8_t* ak_lds;  // [RBK][NKK][16 rows][64 bytes]
     uint8_t* av_lds;  // [2][NVG][RBK][16 rows][64 bytes]
     Tile t[NRM];
     i32x4 ak[RBK][NKK];
     float kinv_l[RBK], kbias_l[RBK];
+    float kqs_l[RBK];  // KT: sum over channels of the lane's head's folded query (fixed-point image)
     float m_l[RBK], l2[RBK], z2[RBK][NVG], acc2[RBK][NVM];
 
     __device__ __forceinline__ void init(const DecArgs& a, __amdgpu_buffer_rsrc_t rsrc, const GroupAddr& addr,
@@ -462,6 +469,7 @@ struct MStream {
         v_off = (uint32_t)a.rec_vcodes + (kb * VBB * D + 4 * j) * 4;
         vm_off = (uint32_t)a.rec_vmeta + j * NVG * 8;
         km_off = KM * lane * 4;
+        kt_off = j * 8;
         ak_lds = lds;
         av_lds = lds + AK_BYTES;
         kc = reinterpret_cast<float*>(lds + lds_bytes());
@@ -501,7 +509,11 @@ struct MStream {
                 tt.v[m][bb] = bload<4>(rs, v_off, grp + ((t0 / TB + bb) * D + 64 * m) * 4);
 #pragma unroll
         for (int sb = 0; sb < NSB; ++sb) tt.vm[sb] = bload<2 * NVG>(rs, vm_off, grp + (t0 + 16 * sb) * NVG * 8);
-        if (kmeta) {  // constant at every call site
+        if constexpr (KT) {
+#pragma unroll
+            for (int sb = 0; sb < NSB; ++sb) tt.km[sb] = bload<2>(rs, kt_off, grp + (t0 + 16 * sb) * 8);
+        }
+        if (!KT && kmeta) {  // constant at every call site
             tt.ks = bload<KM>(rs, km_off, grp);
             tt.kz = bload<KM>(rs, km_off + D * 4, grp);
             if constexpr (SP) {
@@ -595,6 +607,52 @@ struct MStream {
         }
     }
 
+    // Per-token keys: the query's digit rows (no key scale folded in), once per
+    // wave; per lane 2^-k and the image's channel sum of its head.
+    __device__ __forceinline__ void fold_kt(const float (&qv)[GQ][KM]) {
+        float kinv[GQ], kqs[GQ];
+#pragma unroll
+        for (int h = 0; h < GQ; ++h) {
+            float mx = 0.0f;
+#pragma unroll
+            for (int j = 0; j < KM; ++j) mx = fmaxf(mx, fabsf(qv[h][j]));
+            const FixScale fs = fix_scale(group_max<64>(mx));
+            kinv[h] = fs.inv;
+            float nsum = 0.0f;
+#pragma unroll
+            for (int j = 0; j < KM; ++j) {
+                const int c = KM * lane + j;
+                const int kb = c / (D / 4), kk = (c % (D / 4)) / 16, e = c % 16;
+                uint8_t* dst = ak_lds + ((h / 4 * NKK + kk) * 16 + 4 * (h % 4)) * 64 + kb * 16 + e;
+                const int n = (int)rintf(qv[h][j] * fs.mul);
+                const uint32_t d = digits256(n);
+                dst[0] = (uint8_t)d;
+                dst[64] = (uint8_t)(d >> 8);
+                dst[128] = (uint8_t)(d >> 16);
+                nsum += (float)n;
+            }
+            kqs[h] = group_sum<64>(nsum) * fs.inv;
+        }
+        wave_lds_sync();
+        const int hs = lane >> 4;
+#pragma unroll
+        for (int rb = 0; rb < RBK; ++rb) {
+#pragma unroll
+            for (int kk = 0; kk < NKK; ++kk)
+                ak[rb][kk] = *reinterpret_cast<const i32x4*>(ak_lds + ((rb * NKK + kk) * 16 + (lane & 15)) * 64 + hs * 16);
+            float ki = 0.0f, kq = 0.0f;
+#pragma unroll
+            for (int hh = 0; hh < 4; ++hh)
+                if (4 * rb + hh < GQ) {
+                    ki = hs == hh ? kinv[4 * rb + hh] : ki;
+                    kq = hs == hh ? kqs[4 * rb + hh] : kq;
+                }
+            kinv_l[rb] = ki;
+            kqs_l[rb] = kq;
+            kbias_l[rb] = 0.0f;
+        }
+    }
+
     // Digit rows of one product back to the integer sum: in int32 (Horner) for
     // 4- and 2-bit codes, whose totals stay below 2^31; in fp32 for 8-bit codes
     // (each row sum is exact in fp32, the total may exceed 2^31).
@@ -641,7 +699,13 @@ struct MStream {
                 i32x4 r = mfma_i8(ak[rb][0], bk[0], zero);
 #pragma unroll
                 for (int kk = 1; kk < NKK; ++kk) r = mfma_i8(ak[rb][kk], bk[kk], r);
-                sc[rb][sb] = combine(r) * kinv_l[rb] - kbias_l[rb];
+                if constexpr (KT) {
+                    const auto kmw = whole(cur.km[sb]);
+                    sc[rb][sb] = __uint_as_float(elem(kmw, 0)) *
+                                 (combine(r) * kinv_l[rb] - (__uint_as_float(elem(kmw, 1)) - ZOFF) * kqs_l[rb]);
+                } else {
+                    sc[rb][sb] = combine(r) * kinv_l[rb] - kbias_l[rb];
+                }
                 if constexpr (SP) {  // rows of absent heads read a valid head's term, unused
                     const int head = min(4 * rb + (lane >> 4), GQ - 1);
                     sc[rb][sb] += kc[head * GT + tig * TM + 16 * sb + (lane & 15)];
@@ -762,12 +826,13 @@ struct MStream {
     __device__ __forceinline__ void run(int n_my_groups, const float (&qv)[GQ][KM]) {
         const int n_iter = n_my_groups / GB;
         int it = 0;
+        if constexpr (KT) fold_kt(qv);
         auto step = [&](auto bc) __attribute__((always_inline)) {
             constexpr int B = decltype(bc)::value;
             constexpr int NB = B + NRM - 1;
             load(t[NB % NRM], it * GB + NB / TPG, NB % TPG, NB % TPG == 0);
             __builtin_amdgcn_sched_barrier(0);
-            if constexpr (B % TPG == 0) fold(t[B % NRM], qv);
+            if constexpr (!KT && B % TPG == 0) fold(t[B % NRM], qv);
             process(t[B % NRM], B & 1, B % TPG);
             __builtin_amdgcn_sched_barrier(0);
         };
@@ -777,7 +842,7 @@ struct MStream {
             auto tail_step = [&](auto ic) __attribute__((always_inline)) {
                 constexpr int I = decltype(ic)::value;
                 if (tail > I) {
-                    if constexpr (I % TPG == 0) fold(t[I], qv);
+                    if constexpr (!KT && I % TPG == 0) fold(t[I], qv);
                     process(t[I], I & 1, I % TPG);
                 }
             };
@@ -850,9 +915,12 @@ struct LdsPlan {
 // SP: dense-and-sparse records (one full-precision outlier per key channel group
 // and per value group): the VALU stream adds each outlier's difference from its
 // dequantized code to the scores and outputs.  SPW: caches with one value group
-// per token, on a map with four key lanes and four tokens per slot.
+// per token, on a map with four key lanes and four tokens per slot.  KT: per-token
+// keys (one scale and zero point per token over its D channels): the query is
+// folded once per wave and every score takes its token's scale and zero point,
+//   q . k'_t = s_t (sum_c q_c (u_tc - bias) - (z_t - bias) sum_c q_c).
 template <int BITS, int D, int GQ, int CPL, int TILE, int TPG, bool MF = false, int NVGT = 1, bool SP = false,
-          bool SPW = false>
+          bool SPW = false, bool KT = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(two_waves(MF, BITS, GQ, SP) ? 2 : 1)))
 void decode_kernel(DecArgs a) {
     constexpr int LPT = D / CPL;           // key lanes per token
@@ -879,7 +947,8 @@ void decode_kernel(DecArgs a) {
     static_assert(TILE % 32 == 0 && (U == 2 || U == 4 || U == 8), "digit runs of 2, 4 or 8 bytes");
 
     extern __shared__ __align__(16) unsigned char dsm[];
-    using MS = MStream<BITS, D, GQ, TPG, NVGT, SP>;
+    using MS = MStream<BITS, D, GQ, TPG, NVGT, SP, KT>;
+    static_assert(!(KT && SP), "per-token keys take no outliers");
     // One value group per token (the host's choice) and as many key lanes per token
     // as tokens per slot: lane (slot, chunk) takes the value outlier of token
     // slot * U + chunk, the slot's four entries loading as one vector.
@@ -1039,6 +1108,7 @@ void decode_kernel(DecArgs a) {
             typename UVec<LW>::T k[U];
             typename UVec<VCPL>::T v[NVL];
             u32x2 vm[U];  // value scale, zero point (fp32 bits) of (token, group gz)
+            u32x2 km[U];  // KT: key scale, zero point (fp32 bits) of each token
             typename UVec<KM>::T ks, kz;
             // SP only: the key outliers of the KM fold channels (values; dword of
             // (token | code << 8) u16 fields), the value outlier of (token, group gz)
@@ -1054,9 +1124,12 @@ void decode_kernel(DecArgs a) {
         const uint32_t k_off = (uint32_t)a.rec_kcodes + slot * U * RB + chunk * (LW * 4);
         const uint32_t v_off = (uint32_t)a.rec_vcodes + (hb * NVL * D + c0v) * 4;
         const uint32_t km_off = KM * lane * 4;
-        uint32_t vm_off[U];
+        uint32_t vm_off[U], kt_off[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) vm_off[u] = (uint32_t)a.rec_vmeta + ((slot * U + u) * nvg + gz) * 8;
+        for (int u = 0; u < U; ++u) {
+            vm_off[u] = (uint32_t)a.rec_vmeta + ((slot * U + u) * nvg + gz) * 8;
+            kt_off[u] = (slot * U + u) * 8;  // KT: the token's (scale, zero) at the record's start
+        }
         // SP: outlier fields of this lane's fold channels and of its (token, group gz)
         // items; a u16 field is read with the dword that holds it
         const uint32_t kov_off = (uint32_t)a.rec_kov + KM * lane * 4;
@@ -1086,7 +1159,11 @@ void decode_kernel(DecArgs a) {
             for (int vl = 0; vl < NVL; ++vl) t.v[vl] = bload<VCPL>(rs, v_off + vl * D * 4, grp + (t0 / TB) * D * 4);
 #pragma unroll
             for (int u = 0; u < U; ++u) t.vm[u] = bload<2>(rs, vm_off[u], grp + t0 * nvg * 8);
-            if (kmeta) {  // constant at every call site
+            if constexpr (KT) {
+#pragma unroll
+                for (int u = 0; u < U; ++u) t.km[u] = bload<2>(rs, kt_off[u], grp + t0 * 8);
+            }
+            if (!KT && kmeta) {  // constant at every call site
                 t.ks = bload<KM>(rs, km_off, grp);
                 t.kz = bload<KM>(rs, km_off + D * 4, grp);
                 if constexpr (SP) {
@@ -1111,6 +1188,24 @@ void decode_kernel(DecArgs a) {
 
         uint32_t kl[GQ][kLimbs][KND];  // key digit dwords of this lane's channels
         float kinv[GQ], kbias[GQ];
+
+        // This lane's key digit dwords, read back from the wave's digit bytes.
+        auto load_kl = [&]() __attribute__((always_inline)) {
+#pragma unroll
+            for (int h = 0; h < GQ; ++h)
+#pragma unroll
+                for (int li = 0; li < kLimbs; ++li) {
+                    const uint8_t* base = kd + (h * kLimbs + li) * D + chunk * CPL;
+#pragma unroll
+                    for (int nd = 0; nd < KND; ++nd) {
+                        if constexpr (VB == 4)
+                            kl[h][li][nd] = digit_dword(base + 8 * nd, base + 8 * nd + 4);
+                        else
+                            kl[h][li][nd] = digit_dword(base + 16 * (nd >> 1) + 4 * (nd & 1),
+                                                        base + 16 * (nd >> 1) + 8 + 4 * (nd & 1));
+                    }
+                }
+        };
 
         // Folds the key scales of a group into the query, in fixed point: digit
         // dwords of rint(q_c s_c 2^k) for this lane's key channels, and the
@@ -1158,20 +1253,32 @@ void decode_kernel(DecArgs a) {
                 }
             }
             wave_lds_sync();
+            load_kl();
+        };
+
+        // Per-token keys: the query's digits (no key scale folded in), once per wave,
+        // with 2^-k and the image's channel sum kqs = sum_c n_c 2^-k.
+        float kqs[GQ];
+        auto fold_kt = [&]() __attribute__((always_inline)) {
 #pragma unroll
-            for (int h = 0; h < GQ; ++h)
+            for (int h = 0; h < GQ; ++h) {
+                float mx = 0.0f;
 #pragma unroll
-                for (int li = 0; li < kLimbs; ++li) {
-                    const uint8_t* base = kd + (h * kLimbs + li) * D + chunk * CPL;
+                for (int j = 0; j < KM; ++j) mx = fmaxf(mx, fabsf(qv[h][j]));
+                const FixScale fs = fix_scale(group_max<64>(mx));
+                kinv[h] = fs.inv;
+                kbias[h] = 0.0f;
+                float nsum = 0.0f;
 #pragma unroll
-                    for (int nd = 0; nd < KND; ++nd) {
-                        if constexpr (VB == 4)
-                            kl[h][li][nd] = digit_dword(base + 8 * nd, base + 8 * nd + 4);
-                        else
-                            kl[h][li][nd] = digit_dword(base + 16 * (nd >> 1) + 4 * (nd & 1),
-                                                        base + 16 * (nd >> 1) + 8 + 4 * (nd & 1));
-                    }
+                for (int j = 0; j < KM; ++j) {
+                    const int n = (int)rintf(qv[h][j] * fs.mul);
+                    store_digits(kd + (h * kLimbs) * D + KM * lane + j, D, n);
+                    nsum += (float)n;
                 }
+                kqs[h] = group_sum<64>(nsum) * fs.inv;
+            }
+            wave_lds_sync();
+            load_kl();
         };
 
         // One tile: scores, softmax update, weight digits through LDS (buffer pb of
@@ -1211,7 +1318,13 @@ void decode_kernel(DecArgs a) {
                 float mt = -INFINITY;
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
-                    sc[h][u] = group_sum<LPT>(sc[h][u]) * kinv[h] - kbias[h];
+                    if constexpr (KT) {
+                        const u32x2 km = whole(cur.km[u]);
+                        sc[h][u] = __uint_as_float(km.x) *
+                                   (group_sum<LPT>(sc[h][u]) * kinv[h] - (__uint_as_float(km.y) - (float)ZB) * kqs[h]);
+                    } else {
+                        sc[h][u] = group_sum<LPT>(sc[h][u]) * kinv[h] - kbias[h];
+                    }
                     if constexpr (SP) sc[h][u] += kc[h * TILE * TPG + tig * TILE + slot * U + u];
                     mt = fmaxf(mt, sc[h][u]);
                 }
@@ -1489,12 +1602,13 @@ void decode_kernel(DecArgs a) {
         } else if (n_my_groups > 0) {
             const int n_iter = n_my_groups / GB;
             int it = 0;
+            if constexpr (KT) fold_kt();
             auto step = [&](auto bc) __attribute__((always_inline)) {
                 constexpr int B = decltype(bc)::value;
                 constexpr int NB = B + NR - 1;  // body tile to prefetch (may be in the next iteration)
                 load(tr[NB % NR], it * GB + NB / TPG, NB % TPG, NB % TPG == 0);
                 __builtin_amdgcn_sched_barrier(0);
-                if constexpr (B % TPG == 0) fold(tr[B % NR]);
+                if constexpr (!KT && B % TPG == 0) fold(tr[B % NR]);
                 process(tr[B % NR], (B & 1) ? pd1 : pd0, B % TPG);
                 __builtin_amdgcn_sched_barrier(0);
             };
@@ -1506,7 +1620,7 @@ void decode_kernel(DecArgs a) {
                 auto tail_step = [&](auto ic) __attribute__((always_inline)) {
                     constexpr int I = decltype(ic)::value;
                     if (tail > I) {
-                        if constexpr (I % TPG == 0) fold(tr[I]);
+                        if constexpr (!KT && I % TPG == 0) fold(tr[I]);
                         process(tr[I], (I & 1) ? pd1 : pd0, I % TPG);
                     }
                 };

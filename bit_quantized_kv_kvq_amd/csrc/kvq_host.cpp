@@ -87,6 +87,8 @@ kvq_status validate(const kvq_config* c) {
         return fail(KVQ_ERR_INVALID_ARG, "head_dim (%d) is not a multiple of v_group (%d)",
                     c->head_dim, c->v_group);
     if (c->outliers != 0 && c->outliers != 1) return fail(KVQ_ERR_INVALID_ARG, "outliers must be 0 or 1");
+    if (c->key_axis != KVQ_KEY_PER_CHANNEL && c->key_axis != KVQ_KEY_PER_TOKEN)
+        return fail(KVQ_ERR_INVALID_ARG, "key_axis must be KVQ_KEY_PER_CHANNEL or KVQ_KEY_PER_TOKEN");
     if (c->page_groups < 0 || (c->page_groups & (c->page_groups - 1)) != 0)
         return fail(KVQ_ERR_INVALID_ARG, "page_groups (%d) must be 0 or a power of two", c->page_groups);
     if (c->pool_pages < 0) return fail(KVQ_ERR_INVALID_ARG, "pool_pages must be >= 0");
@@ -111,6 +113,11 @@ kvq_status validate(const kvq_config* c) {
         return fail(KVQ_ERR_UNSUPPORTED, "v_group must be a multiple of 16");
     if ((int64_t)c->batch * c->n_kv_heads > 65535)
         return fail(KVQ_ERR_UNSUPPORTED, "batch * n_kv_heads must be at most 65535");
+    if (c->key_axis == KVQ_KEY_PER_TOKEN) {
+        if (c->k_group != 64 && c->k_group != 128)
+            return fail(KVQ_ERR_UNSUPPORTED, "per-token keys need k_group 64 or 128");
+        if (c->outliers) return fail(KVQ_ERR_UNSUPPORTED, "per-token keys do not take outliers");
+    }
     {   // the decode kernel addresses one slice's records, or the page pool, with
         // 32-bit offsets
         const Layout L = make_layout(c);
@@ -150,7 +157,8 @@ Layout make_layout(const kvq_config* c) {
         L.Lq_cap = m < L.R ? 0 : ((m - L.R) / L.Qf + 1) * L.Qf;
     }
     L.ng_cap = L.Lq_cap / L.G;
-    L.rec_kcodes = 8 * L.D;
+    L.key_axis = c->key_axis;
+    L.rec_kcodes = 8 * (L.key_axis == KVQ_KEY_PER_TOKEN ? L.G : L.D);  // key (scale, zero): [2][D] or [G][2]
     L.rec_vcodes = L.rec_kcodes + L.G * L.row_bytes;
     L.rec_vmeta = L.rec_vcodes + L.G * L.row_bytes;
     L.outliers = c->outliers;

@@ -22,7 +22,9 @@ constexpr int kMaxCombine = 1024;      // max (splits x query heads per kv head)
 // Lq_cap = R * floor((max_tokens - S) / R): the largest quantized length a
 // sequence of max_tokens tokens can reach.  A key group's record holds, in the
 // order decode attention streams them:
-//   kmeta  : fp32 [2][D]              key scales, then key zero points
+//   kmeta  : fp32 [2][D]              key scales, then key zero points; with
+//                                     per-token keys fp32 [G][2], (scale, zero)
+//                                     of each token
 //   kcodes : [G][D*bits/8]            key codes, one packed row per token
 //   vcodes : [G/TB][D] uint32         value codes: for each block of TB = 32/bits
 //                                     tokens, one dword per channel holding the
@@ -37,6 +39,7 @@ constexpr int kMaxCombine = 1024;      // max (splits x query heads per kv head)
 struct Layout {
     int B, Hkv, Hq, D, bits, codec, G, GV, R, S, dtype, esize, gqa, nvg, row_bytes;
     int retention;  // kvq_retention
+    int key_axis;   // kvq_key_axis: 0 keys per channel over G tokens, 1 per token over D channels
     int Qf;         // tokens quantized per flush: R, or W = R / 3 under log-sparse retention
     // Dense-and-sparse records (outliers = 1): after the value metadata, the key
     // outliers' exact values fp32 [D] and (token | code << 8) u16 [D], then the

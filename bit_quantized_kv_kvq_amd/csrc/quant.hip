@@ -170,8 +170,9 @@ struct QuantArgs {
     int D, G, GV, nvg, row_bytes;
     int64_t ng_cap;
     int rec_bytes, rec_kcodes, rec_vcodes, rec_vmeta;
-    int codec;  // kvq_codec
-    int64_t bh0;  // first slice of the launch
+    int codec;     // kvq_codec
+    int key_axis;  // kvq_key_axis
+    int64_t bh0;   // first slice of the launch
     RecMap rm;
     int outliers, rec_kov, rec_koi, rec_vov, rec_voi;  // dense-and-sparse records
 };
@@ -249,13 +250,89 @@ __device__ inline void load2_f32(const void* base, int64_t elem0, float& x0, flo
     }
 }
 
+// Per-token groups: for each of the G tokens of a key group, one group per run of
+// GV channels (nvg = D / GV groups per token), quantized into s_codes ([G][D]
+// bytes) with (scale, zero) in meta [G][nvg][2].  TPI consecutive lanes share one
+// (token, group), each with GV/TPI channels in runs of 8 (16-byte loads), and
+// meet by lane shuffles.  Values always; keys too under per-token keys (GV = D).
+// sp_rec: the record whose value-outlier fields take dense-and-sparse outliers
+// (null: no outliers).
+template <int DT, int BITS>
+__device__ inline void token_groups(const QuantArgs& a, const void* src, int64_t src_row0, int GV, int nvg,
+                                    float* meta, uint8_t* s_codes, uint8_t* sp_rec) {
+    constexpr float qmax = (float)((1 << BITS) - 1);
+    const int D = a.D, G = a.G, tid = threadIdx.x, ts = a.tok_stride;
+    const bool sparse = sp_rec != nullptr;
+    const int items = G * nvg;
+    int tpi = 256 / items;                    // lanes per (token, group)
+    tpi = tpi < 1 ? 1 : tpi > GV / 8 ? GV / 8 : tpi;
+    const int cpt = GV / tpi;                 // channels per lane, a multiple of 8
+    for (int i0 = 0; i0 < items * tpi; i0 += 256) {
+        const int i = (i0 + tid) / tpi, sub = (i0 + tid) % tpi;
+        const bool live = i < items;
+        const int t = live ? i / nvg : 0, h = live ? i % nvg : 0;
+        const int64_t e0 = (src_row0 + (int64_t)t * ts) * D + (int64_t)h * GV + sub * cpt;
+        // outliers: channel (within the group) of largest magnitude
+        int ov = -1;
+        if (sparse) {
+            float am = -1.0f;
+            int ai = 0;
+            for (int j = 0; j < cpt; j += 8) {
+                float f[8];
+                load8_f32<DT>(src, e0 + j, f);
+#pragma unroll
+                for (int k = 0; k < 8; ++k) outlier_max(am, ai, fabsf(f[k]), sub * cpt + j + k);
+            }
+            for (int m = 1; m < tpi; m <<= 1)   // lanes of one item are consecutive
+                outlier_max(am, ai, __shfl_xor(am, m), __shfl_xor(ai, m));
+            ov = ai;
+        }
+        float mn = INFINITY, mx = -INFINITY;
+        for (int j = 0; j < cpt; j += 8) {
+            float f[8];
+            load8_f32<DT>(src, e0 + j, f);
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                if (sub * cpt + j + k != ov) mn = fminf(mn, f[k]), mx = fmaxf(mx, f[k]);
+        }
+        for (int o = 1; o < tpi; o <<= 1) {   // lanes of one item are consecutive
+            mn = fminf(mn, __shfl_xor(mn, o));
+            mx = fmaxf(mx, __shfl_xor(mx, o));
+        }
+        const QParams p = a.codec ? group_params_sym(mn, mx, qmax) : group_params(mn, mx, qmax);
+        if (live) {
+            for (int j = 0; j < cpt; j += 8) {
+                float f[8];
+                load8_f32<DT>(src, e0 + j, f);
+                uint32_t lo = 0, hi = 0;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    lo |= group_code(f[k], p, qmax) << (8 * k);
+                    hi |= group_code(f[k + 4], p, qmax) << (8 * k);
+                }
+                *reinterpret_cast<uint2*>(s_codes + t * D + h * GV + sub * cpt + j) = make_uint2(lo, hi);
+            }
+            if (sub == 0) {
+                meta[i * 2] = p.s;
+                meta[i * 2 + 1] = p.z;
+            }
+            if (sparse && ov >= sub * cpt && ov < (sub + 1) * cpt) {
+                const float x = load_as_f32<DT>(src, e0 - sub * cpt + ov);
+                reinterpret_cast<float*>(sp_rec + a.rec_vov)[i] = x;
+                reinterpret_cast<uint16_t*>(sp_rec + a.rec_voi)[i] = (uint16_t)(ov | (group_code(x, p, qmax) << 8));
+            }
+        }
+    }
+}
+
 // One workgroup per key group.  Keys: thread (channel pair cp, part p) covers
 // tokens [p G/P, (p+1) G/P) of channels 2cp, 2cp+1 (coalesced across the
 // workgroup); the P partial minima/maxima of a channel meet in LDS.  Values: TPI
 // consecutive lanes share one (token, value group), each with GV/TPI channels in
 // runs of 8 (16-byte loads), and meet by lane shuffles.  Every element is read
 // twice (min/max, then codes); the second read hits the caches.  Codes go to LDS
-// and are packed from there.  Dense-and-sparse groups first find each vector's
+// and are packed from there.  Per-token keys take the values' path with one group
+// per token over D channels.  Dense-and-sparse groups first find each vector's
 // outlier (largest magnitude, lowest index among equals; KVQuant, per-vector
 // dense-and-sparse quantization) the same way, leave it out of the min/max, and
 // store its exact value, place and code beside the record.
@@ -275,7 +352,11 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
     float* kmeta = reinterpret_cast<float*>(rec);
 
     // ---- keys ----
-    {
+    if (a.key_axis == 1) {
+        // per token: one group over the token's D channels ("Atom…" review, section
+        // 三, model-components table, KV-cache row: attention-head granularity)
+        token_groups<DT, BITS>(a, a.src_k, src_row0, D, 1, kmeta, s_codes, nullptr);
+    } else {
         const int CH = D / 2;            // channel pairs
         const int P = 256 / CH;          // token parts (4 for D = 128, 8 for D = 64)
         const int GP = G / P;            // tokens per thread
@@ -357,70 +438,8 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
     __syncthreads();
 
     // ---- values ----
-    {
-        const int GV = a.GV, nvg = a.nvg;
-        float* vmeta = reinterpret_cast<float*>(rec + a.rec_vmeta);
-        const int items = G * nvg;
-        int tpi = 256 / items;                    // lanes per (token, group)
-        tpi = tpi < 1 ? 1 : tpi > GV / 8 ? GV / 8 : tpi;
-        const int cpt = GV / tpi;                 // channels per lane, a multiple of 8
-        for (int i0 = 0; i0 < items * tpi; i0 += 256) {
-            const int i = (i0 + tid) / tpi, sub = (i0 + tid) % tpi;
-            const bool live = i < items;
-            const int t = live ? i / nvg : 0, h = live ? i % nvg : 0;
-            const int64_t e0 = (src_row0 + (int64_t)t * ts) * D + (int64_t)h * GV + sub * cpt;
-            // outliers: channel (within the group) of largest magnitude
-            int ov = -1;
-            if (a.outliers) {
-                float am = -1.0f;
-                int ai = 0;
-                for (int j = 0; j < cpt; j += 8) {
-                    float f[8];
-                    load8_f32<DT>(a.src_v, e0 + j, f);
-#pragma unroll
-                    for (int k = 0; k < 8; ++k) outlier_max(am, ai, fabsf(f[k]), sub * cpt + j + k);
-                }
-                for (int m = 1; m < tpi; m <<= 1)   // lanes of one item are consecutive
-                    outlier_max(am, ai, __shfl_xor(am, m), __shfl_xor(ai, m));
-                ov = ai;
-            }
-            float mn = INFINITY, mx = -INFINITY;
-            for (int j = 0; j < cpt; j += 8) {
-                float f[8];
-                load8_f32<DT>(a.src_v, e0 + j, f);
-#pragma unroll
-                for (int k = 0; k < 8; ++k)
-                    if (sub * cpt + j + k != ov) mn = fminf(mn, f[k]), mx = fmaxf(mx, f[k]);
-            }
-            for (int o = 1; o < tpi; o <<= 1) {   // lanes of one item are consecutive
-                mn = fminf(mn, __shfl_xor(mn, o));
-                mx = fmaxf(mx, __shfl_xor(mx, o));
-            }
-            const QParams p = a.codec ? group_params_sym(mn, mx, qmax) : group_params(mn, mx, qmax);
-            if (live) {
-                for (int j = 0; j < cpt; j += 8) {
-                    float f[8];
-                    load8_f32<DT>(a.src_v, e0 + j, f);
-                    uint32_t lo = 0, hi = 0;
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        lo |= group_code(f[k], p, qmax) << (8 * k);
-                        hi |= group_code(f[k + 4], p, qmax) << (8 * k);
-                    }
-                    *reinterpret_cast<uint2*>(s_codes + t * D + h * GV + sub * cpt + j) = make_uint2(lo, hi);
-                }
-                if (sub == 0) {
-                    vmeta[i * 2] = p.s;
-                    vmeta[i * 2 + 1] = p.z;
-                }
-                if (a.outliers && ov >= sub * cpt && ov < (sub + 1) * cpt) {
-                    const float x = load_as_f32<DT>(a.src_v, e0 - sub * cpt + ov);
-                    reinterpret_cast<float*>(rec + a.rec_vov)[i] = x;
-                    reinterpret_cast<uint16_t*>(rec + a.rec_voi)[i] = (uint16_t)(ov | (group_code(x, p, qmax) << 8));
-                }
-            }
-        }
-    }
+    token_groups<DT, BITS>(a, a.src_v, src_row0, a.GV, a.nvg, reinterpret_cast<float*>(rec + a.rec_vmeta), s_codes,
+                           a.outliers ? rec : nullptr);
     __syncthreads();
     pack_blocks<BITS>(s_codes, G, D, reinterpret_cast<uint32_t*>(rec + a.rec_vcodes));
 }
@@ -443,6 +462,7 @@ struct DeqArgs {
     int delta;
     int Hkv;
     int outliers, rec_kov, rec_koi, rec_vov, rec_voi;  // dense-and-sparse records
+    int key_axis;  // kvq_key_axis: key (scale, zero) [2][D], or [G][2] per token
 };
 
 // State of slice bh: the launch's (uniform) one, or the one of its sequence's length.
@@ -489,7 +509,9 @@ __global__ __launch_bounds__(256) void dequantize_kernel(DeqArgs a) {
             const float* vm = reinterpret_cast<const float*>(rec + a.rec_vmeta) + ((int64_t)tg * a.nvg + c / a.GV) * 2;
             const float kq = (float)key_code(a, rec, tg, c);
             const float vq = (float)value_code(a, rec, tg, c);
-            kx = (kq - km[a.D + c]) * km[c];
+            const float ks = a.key_axis ? km[2 * tg] : km[c];
+            const float kz = a.key_axis ? km[2 * tg + 1] : km[a.D + c];
+            kx = (kq - kz) * ks;
             vx = (vq - vm[1]) * vm[0];
             if (a.outliers) {  // outliers dequantize to their exact values
                 if ((reinterpret_cast<const uint16_t*>(rec + a.rec_koi)[c] & 0xFF) == tg)
@@ -528,13 +550,21 @@ __global__ __launch_bounds__(256) void export_kernel(DeqArgs a, uint8_t* k_codes
         if (k_codes) k_codes[bh * ncode + i] = (uint8_t)key_code(a, rec, tg, c);
         if (v_codes) v_codes[bh * ncode + i] = (uint8_t)value_code(a, rec, tg, c);
     }
-    const int64_t nk = (a.Lq / a.G) * a.D;
-    for (int64_t i = i0; i < (Lq_b / a.G) * a.D; i += stride) {
-        const int64_t g = i / a.D;
-        const int c = (int)(i % a.D);
-        const float* km = reinterpret_cast<const float*>(rec_ptr(a.rm, bh, g));
-        if (k_scale) k_scale[bh * nk + i] = km[c];
-        if (k_zero) k_zero[bh * nk + i] = km[a.D + c];
+    if (a.key_axis) {   // per token: [Lq][1]
+        for (int64_t t = i0; t < Lq_b; t += stride) {
+            const float* km = reinterpret_cast<const float*>(rec_ptr(a.rm, bh, t / a.G)) + 2 * (t % a.G);
+            if (k_scale) k_scale[bh * a.Lq + t] = km[0];
+            if (k_zero) k_zero[bh * a.Lq + t] = km[1];
+        }
+    } else {
+        const int64_t nk = (a.Lq / a.G) * a.D;
+        for (int64_t i = i0; i < (Lq_b / a.G) * a.D; i += stride) {
+            const int64_t g = i / a.D;
+            const int c = (int)(i % a.D);
+            const float* km = reinterpret_cast<const float*>(rec_ptr(a.rm, bh, g));
+            if (k_scale) k_scale[bh * nk + i] = km[c];
+            if (k_zero) k_zero[bh * nk + i] = km[a.D + c];
+        }
     }
     const int64_t nv = a.Lq * a.nvg;
     for (int64_t i = i0; i < Lq_b * a.nvg; i += stride) {
@@ -577,6 +607,7 @@ __global__ __launch_bounds__(256) void export_outliers_kernel(DeqArgs a, uint8_t
 
 DeqArgs make_deq_args(const Layout& L, const DevPtrs& P, int64_t nS, int64_t Lq, int64_t r, Ragged rg) {
     DeqArgs a;
+    a.key_axis = L.key_axis;
     a.outliers = L.outliers;
     a.rec_kov = L.rec_kov;
     a.rec_koi = L.rec_koi;
@@ -695,6 +726,7 @@ hipError_t launch_quantize(const Layout& L, const DevPtrs& P, const void* src_k,
     a.rec_vcodes = L.rec_vcodes;
     a.rec_vmeta = L.rec_vmeta;
     a.codec = L.codec;
+    a.key_axis = L.key_axis;
     a.bh0 = bh0;
     a.rm = rec_map(L, P);
     a.outliers = L.outliers;

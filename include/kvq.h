@@ -105,6 +105,24 @@ typedef enum kvq_retention {
     KVQ_RETAIN_LOG = 1
 } kvq_retention;
 
+/*
+ * Grouping of the keys:
+ *   PER_CHANNEL: one group per channel over each run of G tokens (KIVI notes,
+ *                "LLM系列：KVCache量化1 KIVI…", section 1: keys per channel).
+ *   PER_TOKEN:   one group per token over its head_dim channels, i.e. one
+ *                scale and zero point per token and kv head ("Atom: Low-bit
+ *                Quantization for Efficient and Accurate LLM Serving", section
+ *                三, model-components table, KV-cache row: asymmetric low-bit
+ *                quantization at attention-head granularity).  G then only sets
+ *                how many tokens a record holds: 64 or 128.  Not combined with
+ *                outliers; with several query heads per kv head, or 8-bit codes,
+ *                it needs G_V >= 64.
+ */
+typedef enum kvq_key_axis {
+    KVQ_KEY_PER_CHANNEL = 0,
+    KVQ_KEY_PER_TOKEN = 1
+} kvq_key_axis;
+
 typedef struct kvq_config {
     int32_t batch;        /* B  >= 1                                              */
     int32_t n_kv_heads;   /* Hkv >= 1                                             */
@@ -129,6 +147,7 @@ typedef struct kvq_config {
                           /* every sequence at max_tokens                         */
     int32_t outliers;     /* 1: one full-precision outlier per quantization vector */
                           /* (dense-and-sparse groups, see kvq_export_outliers)   */
+    int32_t key_axis;     /* kvq_key_axis of the key groups (0: per channel)      */
 } kvq_config;
 
 typedef struct kvq_cache kvq_cache; /* opaque host-side handle */
@@ -146,11 +165,14 @@ kvq_status kvq_cache_bytes(const kvq_config* cfg, size_t* bytes);
  * initialisation.  *out receives the handle, to be freed with
  * kvq_cache_destroy.  Errors: INVALID_ARG (null pointer, non-positive sizes,
  * Hq % Hkv != 0, R % G != 0, D % G_V != 0, codec not a kvq_codec, retention not a
- * kvq_retention, log-sparse retention with R not a multiple of 3G, page_groups not 0
- * or a power of two, pool_pages < 0, misaligned buffer),
+ * kvq_retention, key_axis not a kvq_key_axis, log-sparse retention with R not a
+ * multiple of 3G, page_groups not 0 or a power of two, pool_pages < 0, misaligned
+ * buffer),
  * UNSUPPORTED (bits not 2/4/8, D not 64/128, Hq/Hkv not 1/2/4/8, G not in
  * {32, 64, 128, 256}, G_V not a multiple of 16, 8-bit codes with G or G_V
- * below 64, B * Hkv > 65535, more than
+ * below 64, per-token keys with G not 64 or 128, with outliers, or with G_V
+ * below 64 where several query heads share a kv head or codes are 8-bit,
+ * B * Hkv > 65535, more than
  * 2 GiB of quantized records per (sequence, kv head), a page pool above 4 GiB,
  * pages so small that a decode split would span more than 63 of them), BUFFER_TOO_SMALL,
  * DEVICE (no current HIP device).
@@ -267,7 +289,8 @@ kvq_status kvq_dequantize(const kvq_cache* cache, float* k_out, float* v_out, vo
  * Export the quantized part in a canonical, unpacked layout (for bit-exact
  * comparison; independent of the internal packing):
  *   k_codes, v_codes : device uint8 [B, Hkv, n_quant, D]
- *   k_scale, k_zero  : device fp32  [B, Hkv, n_quant / G, D]
+ *   k_scale, k_zero  : device fp32  [B, Hkv, n_quant / G, D]; with
+ *                      KVQ_KEY_PER_TOKEN keys [B, Hkv, n_quant, 1]
  *   v_scale, v_zero  : device fp32  [B, Hkv, n_quant, D / G_V]
  * (n_quant of kvq_cache_state; rows past a shorter sequence's own quantized
  * tokens are not written).  Any pointer may be NULL to skip that array.

@@ -40,7 +40,8 @@ def make_cache(w: wl.Workload, max_tokens: int | None = None, **over):
               head_dim=w.head_dim, bits=w.bits, k_group=w.k_group, v_group=w.v_group,
               residual=w.residual, n_sink=w.n_sink, dtype=TORCH_DTYPES[w.dtype],
               max_tokens=max_tokens or w.max_tokens, device=torch.device("cuda:0"), codec=w.codec,
-              retention=1 if w.log_window else 0, page_groups=w.page_groups, outliers=w.outliers)
+              retention=1 if w.log_window else 0, page_groups=w.page_groups, outliers=w.outliers,
+              key_axis=w.key_axis)
     kw.update(over)
     return Cache(**kw)
 
@@ -124,7 +125,8 @@ def assert_export_slice_matches(ex, st, b: int, kvh: int):
     assert ex["k_codes"].shape[2] >= Lq
     np.testing.assert_array_equal(ex["k_codes"][b, kvh, :Lq], st["k_codes"])
     np.testing.assert_array_equal(ex["v_codes"][b, kvh, :Lq], st["v_codes"])
-    for name, rows in (("k_scale", Lq // G), ("k_zero", Lq // G), ("v_scale", Lq), ("v_zero", Lq)):
+    krows = Lq if st.get("key_axis", 0) else Lq // G   # per-token keys: one (scale, zero) per token
+    for name, rows in (("k_scale", krows), ("k_zero", krows), ("v_scale", Lq), ("v_zero", Lq)):
         got = np.ascontiguousarray(ex[name][b, kvh, :rows]).view(np.uint32)
         want = np.ascontiguousarray(st[name]).view(np.uint32)
         np.testing.assert_array_equal(got, want, err_msg=name)

@@ -35,6 +35,9 @@ def test_algorithmic_bytes_count_every_field():
     wo = w.replace(outliers=1)
     extra = (Lq // G) * D * 6 + Lq * 6            # one (value, place, code) per key and value vector
     assert bench.algorithmic_bytes(wo, 0, Lq, r) == w.batch * w.n_kv_heads * (per_slice + extra) + q_out
+    wk = w.replace(key_axis=1)                    # head-granular keys: one (scale, zero) per token
+    per_tok = Lq * 2 * D * 4 // 8 + Lq * 2 * 4 + Lq * 2 * 4 + r * 2 * D * e
+    assert bench.algorithmic_bytes(wk, 0, Lq, r) == w.batch * w.n_kv_heads * per_tok + q_out
     # ragged: a sequence's share of the bytes is that of a batch of one
     lens = [4096, 2048]
     wr = w.replace(batch=2)

@@ -33,7 +33,7 @@ def _oracle_states(w, K, V):
     return {(b, h): oracle.build_slice(kf[b, h], vf[b, h], head_dim=w.head_dim, bits=w.bits,
                                        k_group=w.k_group, v_group=w.v_group,
                                        residual=w.residual, n_sink=w.n_sink, codec=w.codec,
-                                       outliers=w.outliers)
+                                       outliers=w.outliers, key_axis=w.key_axis)
             for b in range(w.batch) for h in range(w.n_kv_heads)}
 
 

@@ -36,6 +36,8 @@ SMALL = {
                                                                   n_q_heads=3, prefill=1000, steps=30),
     "logquant_small": wl.get("logquant_gqa_int2").replace(name="logquant_small", batch=2, n_kv_heads=2,
                                                           n_q_heads=8, prefill=1000, steps=100),
+    "headgran_small": wl.get("llama7b_mha_int4_headgran").replace(name="headgran_small", batch=2, n_kv_heads=3,
+                                                                  n_q_heads=3, prefill=1000, steps=30),
 }
 
 
@@ -151,7 +153,8 @@ def test_repeat_calls_are_bitwise_deterministic():
 # the oracle element by element.
 FULL = ["tiny", "llama7b_mha_int4", "kivi2_long_batch", "gqa_32k_int4", "long_128k_sink_int2",
         "llama7b_mha_int4_sym", "llama7b_mha_int8", "llama7b_mha_int4_ragged", "logquant_gqa_int2",
-        "llama7b_mha_int4_paged", "llama7b_mha_int4_outliers", "gqa_32k_int4_outliers"]
+        "llama7b_mha_int4_paged", "llama7b_mha_int4_outliers", "gqa_32k_int4_outliers",
+        "llama7b_mha_int4_headgran"]
 EXPORT_ALL = {"llama7b_mha_int4", "kivi2_long_batch", "gqa_32k_int4", "long_128k_sink_int2"}
 
 

@@ -52,7 +52,9 @@ def _expected_bytes(c):
     nvg = D // c.v_group
     # with outliers: key outlier values fp32 [D] and (token | code) u16 [D], value outliers
     # fp32 and u16 per (token, value group)
-    rec = al(8 * D + 2 * G * row + G * nvg * 8 + (6 * D + 6 * G * nvg if c.outliers else 0))
+    # key (scale, zero): fp32 [2][D] per channel, or [G][2] per token
+    kmeta = 8 * G if c.key_axis else 8 * D
+    rec = al(kmeta + 2 * G * row + G * nvg * 8 + (6 * D + 6 * G * nvg if c.outliers else 0))
     if c.page_groups:  # a pool of pages of page_groups key groups of every kv head, and a page table
         max_pages = -(-(Lq_cap // G) // c.page_groups)
         pool = c.pool_pages or c.batch * max_pages
@@ -76,7 +78,11 @@ def _expected_bytes(c):
                                 dict(page_groups=4, retention=kvq.KVQ_RETAIN_LOG, residual=192),
                                 dict(outliers=1, n_q_heads=4), dict(outliers=1, n_q_heads=4, bits=2, head_dim=64),
                                 dict(outliers=1), dict(outliers=1, n_q_heads=32),
-                                dict(outliers=1, n_q_heads=4, page_groups=2, k_group=32, residual=64)])
+                                dict(outliers=1, n_q_heads=4, page_groups=2, k_group=32, residual=64),
+                                dict(key_axis=1, n_q_heads=4, v_group=64), dict(key_axis=1, n_q_heads=4, k_group=128,
+                                                                                v_group=128),
+                                dict(key_axis=1, n_q_heads=4, v_group=64, page_groups=2),
+                                dict(key_axis=1, n_q_heads=4, v_group=32, bits=2)])
 def test_cache_bytes_matches_layout(kw):
     c = _cfg(**kw)
     assert kvq.kvq_cache_bytes(c) == _expected_bytes(c)
@@ -113,6 +119,10 @@ def test_cache_bytes_matches_layout(kw):
     (dict(retention=-1), kvq.KVQ_ERR_INVALID_ARG),
     (dict(retention=kvq.KVQ_RETAIN_LOG), kvq.KVQ_ERR_INVALID_ARG),               # R = 128 is not 3W
     (dict(retention=kvq.KVQ_RETAIN_LOG, residual=256, k_group=128), kvq.KVQ_ERR_INVALID_ARG),  # 3G does not divide R
+    (dict(key_axis=2), kvq.KVQ_ERR_INVALID_ARG),
+    (dict(key_axis=1, k_group=32), kvq.KVQ_ERR_UNSUPPORTED),        # per-token keys: records of 64 or 128 tokens
+    (dict(key_axis=1, k_group=128, residual=256, n_q_heads=4, outliers=1), kvq.KVQ_ERR_UNSUPPORTED),
+    (dict(key_axis=1), kvq.KVQ_ERR_UNSUPPORTED),                    # several query heads with G_V = 32
 ])
 def test_invalid_configs_are_rejected(kw, status):
     with pytest.raises(kvq.KVQError) as ei:
@@ -165,5 +175,5 @@ def test_workload_configs_are_supported():
                             dtype={"f32": 0, "bf16": 1, "f16": 2}[w.dtype],
                             max_tokens=w.max_tokens, codec=w.codec,
                             retention=kvq.KVQ_RETAIN_LOG if w.log_window else kvq.KVQ_RETAIN_WINDOW,
-                            page_groups=w.page_groups, outliers=w.outliers)
+                            page_groups=w.page_groups, outliers=w.outliers, key_axis=w.key_axis)
         assert kvq.kvq_cache_bytes(c) > 0

@@ -174,6 +174,16 @@ WORKLOADS: Dict[str, Workload] = {
         bits=4, k_group=128, v_group=128, residual=128, n_sink=0,
         prefill=32768, steps=16, attend_after_prefill=False, seed=1004,
         k_offset_range=3.0, outliers=1),
+    "llama7b_mha_int4_headgran": Workload(
+        name="llama7b_mha_int4_headgran",
+        description="the Llama-7B-shaped MHA decode with head-granular groups (Atom's KV-cache "
+                    "quantization: each token's key and value one asymmetric group over the head's "
+                    "128 channels): B8 H32 D128, context 4096, bf16, INT4, records of 128 tokens, "
+                    "R128, 64 decode steps",
+        batch=8, n_kv_heads=32, n_q_heads=32, head_dim=128, dtype="bf16",
+        bits=4, k_group=128, v_group=128, residual=128, n_sink=0,
+        prefill=4096, steps=64, attend_after_prefill=False, seed=1002,
+        k_outlier_channels=4, k_outlier_scale=8.0, key_axis=1),
     "logquant_gqa_int2": Workload(
         name="logquant_gqa_int2",
         description="Llama-3.1-8B-shaped GQA decode with LogQuant's log-sparse retention: B8, "
