@@ -1,6 +1,7 @@
 // decode.hip -- decode attention launch: instantiation choice, split planning
-// (about one workgroup per CU) and workspace layout
-// (counters, then split maxima/sums, then split accumulators).
+// (about one workgroup per CU), the split combine's grouping and the workspace
+// layout (counters, then split maxima/sums and accumulators, then those of the
+// combine's groups).
 #include <hip/hip_ext.h>
 
 #include <mutex>
@@ -10,17 +11,37 @@
 namespace kvq {
 
 namespace {
+// Splits per slice up to which the slice's last arrival merges them all; above
+// it, groups of about sqrt(nsplit) splits merge first (two-level combine).  Both
+// keep every merge within kMaxMerge partials for nsplit <= kMaxSplits.
+constexpr int kOneLevelSplits = kMaxMerge;
+static_assert(kOneLevelSplits <= kMaxMerge, "one-level combine within a merge");
+
+int ceil_sqrt(int n) {
+    int s = 0;
+    while (s * s < n) ++s;
+    return s;
+}
+// splits per first-level group for nsplit splits (>= nsplit: one level)
+int combine_group(int nsplit) { return nsplit > kOneLevelSplits ? ceil_sqrt(nsplit) : nsplit; }
+// groups of any split count up to cap: ceil(n / ceil(sqrt n)) <= ceil(sqrt n)
+int combine_groups_cap(int cap) { return cap > kOneLevelSplits ? ceil_sqrt(cap) : 1; }
+
 struct WsLayout {
-    size_t off_counters, off_ml, off_acc, total;
+    size_t off_counters, off_ml, off_acc, off_gml, off_gacc, total;
+    int gcap;
 };
 
 WsLayout ws_layout(const Layout& L, int cap) {
     WsLayout w;
     auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    w.gcap = combine_groups_cap(cap);
     w.off_counters = 0;
-    w.off_ml = al((size_t)L.BH * sizeof(unsigned));
+    w.off_ml = al((size_t)L.BH * (1 + w.gcap) * sizeof(unsigned));
     w.off_acc = al(w.off_ml + (size_t)L.BH * cap * L.gqa * 2 * sizeof(float));
-    w.total = al(w.off_acc + (size_t)L.BH * cap * L.gqa * L.D * sizeof(float));
+    w.off_gml = al(w.off_acc + (size_t)L.BH * cap * L.gqa * L.D * sizeof(float));
+    w.off_gacc = al(w.off_gml + (size_t)L.BH * w.gcap * L.gqa * 2 * sizeof(float));
+    w.total = al(w.off_gacc + (size_t)L.BH * w.gcap * L.gqa * L.D * sizeof(float));
     return w;
 }
 
@@ -205,6 +226,9 @@ hipError_t launch_decode(const Layout& L, const DevPtrs& P, const DecodeRequest&
     if (L.lp >= 0 && gps > 63 * ((int64_t)1 << L.lp)) gps = 63 * ((int64_t)1 << L.lp);
     const int nsplit_q = ng > 0 ? (int)((ng + gps - 1) / gps) : 0;
     const int nsplit = nsplit_q > 0 ? nsplit_q : 1;
+    // nsplit <= nsplit_cap <= kMaxSplits: every merge of the combine takes at most
+    // kMaxMerge partials
+    if (nsplit > kMaxSplits) return hipErrorInvalidValue;
 
     dec::DecArgs a;
     a.rec = P.rec;
@@ -220,6 +244,9 @@ hipError_t launch_decode(const Layout& L, const DevPtrs& P, const DecodeRequest&
     a.counters = reinterpret_cast<unsigned*>((char*)ws + w.off_counters);
     a.part_ml = reinterpret_cast<float*>((char*)ws + w.off_ml);
     a.part_acc = reinterpret_cast<float*>((char*)ws + w.off_acc);
+    a.grp_ml = reinterpret_cast<float*>((char*)ws + w.off_gml);
+    a.grp_acc = reinterpret_cast<float*>((char*)ws + w.off_gacc);
+    a.cgroups_cap = w.gcap;
     a.ng_cap = L.ng_cap;
     a.rec_bytes = L.rec_bytes;
     a.rec_kcodes = L.rec_kcodes;
@@ -243,6 +270,7 @@ hipError_t launch_decode(const Layout& L, const DevPtrs& P, const DecodeRequest&
     a.ngroups = (int)ng;
     a.nsplit = nsplit;
     a.nsplit_cap = rq.nsplit_cap;
+    a.cgs = combine_group(nsplit);
     a.qscale = sm_scale * 1.4426950408889634f;
     a.base_len = rq.rg.base_len;
     a.len_delta = rq.rg.delta;

@@ -64,7 +64,7 @@ struct DecArgs {
     float* lse;
     float* part_acc;     // [BH][nsplit_cap][GQ][D]
     float* part_ml;      // [BH][nsplit_cap][GQ][2]
-    unsigned* counters;  // [BH]
+    unsigned* counters;  // [BH] slice counters, then the group counters
     int64_t ng_cap;
     int rec_bytes, rec_kcodes, rec_vcodes, rec_vmeta;
     int rec_kov, rec_koi, rec_vov, rec_voi;  // outlier fields of dense-and-sparse records
@@ -80,6 +80,12 @@ struct DecArgs {
     // tokens, and nS, nfp, ngroups above are replaced by its own; null otherwise.
     const int* base_len;
     int len_delta;
+    // Two-level split combine: splits in groups of cgs (cgs >= nsplit: one level);
+    // group partials [BH][cgroups_cap][GQ][D] and [BH][cgroups_cap][GQ][2], group
+    // counters [BH][cgroups_cap] after the slice counters.
+    float* grp_acc;
+    float* grp_ml;
+    int cgs, cgroups_cap;
 };
 
 constexpr int kLimbs = 5;
@@ -1682,133 +1688,111 @@ void decode_kernel(DecArgs a) {
     }
     if (single) return;
 
-    // Last workgroup of this slice merges all splits (log-sum-exp combine).
-    // The partials were written with device-scope stores, which write through the
-    // XCD's L2; every wave waits until its stores are acknowledged, then one
-    // thread counts the arrival.  The last arrival reads the partials back with
-    // device-scope loads.  No L2 write-back or invalidate is needed because all
-    // data exchanged between workgroups moves through device-scope accesses.
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_waitcnt(0);
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __syncthreads();
-    if (tid == 0) {
-        const unsigned prev =
-            __hip_atomic_fetch_add(&a.counters[bh], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        *s_last = prev == (unsigned)(a.nsplit - 1);
-    }
-    __syncthreads();
-    if (!*s_last) return;
-
-    const int ns = a.nsplit;
-    const float* pml = a.part_ml + bh * a.nsplit_cap * GQ * 2;
-    const float* pacc = a.part_acc + bh * a.nsplit_cap * GQ * D;
+    // Split combine by last arrival, in one level or two.  With a.cgs < nsplit the
+    // splits form groups of a.cgs consecutive splits: the last arrival of a group
+    // merges the group's partials into a group partial, and the last group merger
+    // of the slice merges the group partials into the output.  The merges of the
+    // early groups overlap the streams still running, and no workgroup reads more
+    // than max(a.cgs, groups) partials (one workgroup reading all of a long slice's
+    // partials through device-scope loads would otherwise set the kernel's end).
+    // With a.cgs >= nsplit the slice's last arrival merges every split.
+    //
+    // Ordering.  Every value exchanged between workgroups (partials, counters) is
+    // written and read with device-scope accesses, which the hardware performs at
+    // the device's coherence point rather than in one XCD's L2, so no L2
+    // write-back or invalidate is needed.  A publishing workgroup's stores must be
+    // complete before its arrival is counted: every wave waits until all its
+    // memory operations are acknowledged (s_waitcnt 0; the signal fences around it
+    // keep the compiler from moving memory accesses across the wait), and the
+    // workgroup barrier puts every wave's wait before the one thread's atomic add
+    // on the counter.  The merger issues its loads only after that add has returned
+    // the count that makes it last: the branch on the count (through LDS and a
+    // barrier) precedes every load of the merge.
+    const int ng1 = (a.nsplit + a.cgs - 1) / a.cgs;  // groups of the first level
+    const int grp = split / a.cgs;
+    const float* pml = a.part_ml + (bh * a.nsplit_cap + (int64_t)grp * a.cgs) * GQ * 2;
+    const float* pacc = a.part_acc + (bh * a.nsplit_cap + (int64_t)grp * a.cgs) * GQ * D;
+    int ns = min(a.cgs, a.nsplit - grp * a.cgs);  // partials the next merge takes
+    // slice counter at [bh]; with two levels, group counters at [BH + bh * cgroups_cap + grp]
+    unsigned* ctr = ng1 > 1 ? a.counters + gridDim.y + bh * a.cgroups_cap + grp : a.counters + bh;
+    bool final = ng1 == 1;
     // Every load here is a round trip to the coherence point (about a microsecond),
-    // so the merge is arranged around few round trips.  With at most kStage
-    // (split, head) pairs: the maxima and sums of all pairs go to LDS in one round
-    // trip, together with the accumulators of the first batch of splits; each
-    // thread then takes its elements' maxima and sums from LDS and loads the
-    // remaining accumulators in batches of 64 (element, split) values.  The splits
-    // are merged in split order, with each split's weight exp2(m_i - M) under the
-    // overall maximum M.
-    constexpr int kStage = 512;
+    // so a merge takes one: a merge takes at most kMaxMerge partials (the host's
+    // grouping), whose maxima and sums go to LDS while each thread loads its
+    // elements' accumulators of every partial.  The partials are merged in split
+    // (or group) order, each weighted by exp2(m_i - M) under the overall maximum M.
     constexpr int NE = (GQ * D + kThreads - 1) / kThreads;  // (head, channel) elements per thread
-    constexpr int SB = 64 / NE;                             // splits per batch of accumulators
-    __shared__ float2 s_pml[kStage];
-    if (ns * GQ <= kStage) {
-        const int npair = ns * GQ;
-        int hk[NE], ck[NE];
+    constexpr int NP = (kMaxMerge * GQ + kThreads - 1) / kThreads;  // (partial, head) pairs per thread
+    __shared__ float2 s_pml[kMaxMerge * GQ];
+    int hk[NE], ck[NE];
 #pragma unroll
-        for (int k = 0; k < NE; ++k) {
-            const int e = min(tid + k * kThreads, GQ * D - 1);
-            hk[k] = e / D;
-            ck[k] = e % D;
+    for (int k = 0; k < NE; ++k) {
+        const int e = min(tid + k * kThreads, GQ * D - 1);
+        hk[k] = e / D;
+        ck[k] = e % D;
+    }
+    for (;;) {
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_waitcnt(0);
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __syncthreads();
+        if (tid == 0) {
+            const unsigned prev = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            *s_last = prev == (unsigned)(ns - 1);
         }
-        float2 mlr[kStage / kThreads];
+        __syncthreads();
+        if (!*s_last) return;
+        const int npair = ns * GQ;
+        float2 mlr[NP];
 #pragma unroll
-        for (int r = 0; r < kStage / kThreads; ++r) mlr[r] = fetch2(&pml[2 * min(tid + r * kThreads, npair - 1)]);
-        float ai[NE][SB];
-        auto load_batch = [&](int i0) __attribute__((always_inline)) {
+        for (int r = 0; r < NP; ++r) mlr[r] = fetch2(&pml[2 * min(tid + r * kThreads, npair - 1)]);
+        float ai[NE][kMaxMerge];
 #pragma unroll
-            for (int kk = 0; kk < SB; ++kk)
+        for (int i = 0; i < kMaxMerge; ++i)
 #pragma unroll
-                for (int k = 0; k < NE; ++k) ai[k][kk] = fetch(&pacc[(min(i0 + kk, ns - 1) * GQ + hk[k]) * D + ck[k]]);
-        };
-        load_batch(0);
+            for (int k = 0; k < NE; ++k) ai[k][i] = fetch(&pacc[(min(i, ns - 1) * GQ + hk[k]) * D + ck[k]]);
 #pragma unroll
-        for (int r = 0; r < kStage / kThreads; ++r)
+        for (int r = 0; r < NP; ++r)
             if (tid + r * kThreads < npair) s_pml[tid + r * kThreads] = mlr[r];
         __syncthreads();
-        float M[NE], L[NE], A[NE];
 #pragma unroll
         for (int k = 0; k < NE; ++k) {
-            M[k] = -INFINITY;
-            for (int i = 0; i < ns; ++i) M[k] = fmaxf(M[k], s_pml[i * GQ + hk[k]].x);
-            L[k] = 0.0f;
-            A[k] = 0.0f;
-        }
-        auto weight = [&](int i, int k) __attribute__((always_inline)) {
-            const float mi = s_pml[i * GQ + hk[k]].x;
-            return mi == -INFINITY ? 0.0f : fast_exp2(mi - M[k]);
-        };
-        for (int i0 = 0; i0 < ns; i0 += SB) {
-            if (i0 > 0) load_batch(i0);
-#pragma unroll
-            for (int kk = 0; kk < SB; ++kk) {
-                if (i0 + kk < ns) {
-#pragma unroll
-                    for (int k = 0; k < NE; ++k) {
-                        const float w = weight(i0 + kk, k);
-                        L[k] = fmaf(s_pml[(i0 + kk) * GQ + hk[k]].y, w, L[k]);
-                        A[k] = fmaf(ai[k][kk], w, A[k]);
-                    }
-                }
-            }
-        }
-#pragma unroll
-        for (int k = 0; k < NE; ++k) {
-            if (tid + k * kThreads < GQ * D) {
-                a.out[(qrow0 + hk[k]) * D + ck[k]] = A[k] / L[k];
-                if (ck[k] == 0 && a.lse) a.lse[qrow0 + hk[k]] = (M[k] + __log2f(L[k])) * 0.69314718055994530942f;
-            }
-        }
-    } else {
-        // More pairs than LDS stages: each thread merges the splits of its elements
-        // on its own, loading the maxima, sums and accumulators of kBatch splits
-        // before using any, in split order with an online rescale between batches.
-        constexpr int kBatch = 16;
-        for (int e = tid; e < GQ * D; e += kThreads) {
-            const int h = e / D, c = e % D;
             float M = -INFINITY, L = 0.0f, A = 0.0f;
-            for (int i0 = 0; i0 < ns; i0 += kBatch) {
-                float mi[kBatch], li[kBatch], ai[kBatch];
+            for (int i = 0; i < ns; ++i) M = fmaxf(M, s_pml[i * GQ + hk[k]].x);
 #pragma unroll
-                for (int k = 0; k < kBatch; ++k) {
-                    const int i = min(i0 + k, ns - 1);
-                    const float2 ml = fetch2(&pml[(i * GQ + h) * 2]);
-                    mi[k] = ml.x;
-                    li[k] = ml.y;
-                    ai[k] = fetch(&pacc[(i * GQ + h) * D + c]);
+            for (int i = 0; i < kMaxMerge; ++i) {
+                if (i < ns) {
+                    const float2 ml = s_pml[i * GQ + hk[k]];
+                    const float w = ml.x == -INFINITY ? 0.0f : fast_exp2(ml.x - M);
+                    L = fmaf(ml.y, w, L);
+                    A = fmaf(ai[k][i], w, A);
                 }
-                float Mb = M;
-#pragma unroll
-                for (int k = 0; k < kBatch; ++k) Mb = i0 + k < ns ? fmaxf(Mb, mi[k]) : Mb;
-                const float f = M == -INFINITY ? 0.0f : fast_exp2(M - Mb);
-                L *= f;
-                A *= f;
-#pragma unroll
-                for (int k = 0; k < kBatch; ++k) {
-                    const float w = (i0 + k < ns && mi[k] != -INFINITY) ? fast_exp2(mi[k] - Mb) : 0.0f;
-                    L = fmaf(li[k], w, L);
-                    A = fmaf(ai[k], w, A);
-                }
-                M = Mb;
             }
-            a.out[(qrow0 + h) * D + c] = A / L;
-            if (c == 0 && a.lse) a.lse[qrow0 + h] = (M + __log2f(L)) * 0.69314718055994530942f;
+            if (tid + k * kThreads >= GQ * D) continue;
+            const int h = hk[k], c = ck[k];
+            if (final) {
+                a.out[(qrow0 + h) * D + c] = A / L;
+                if (c == 0 && a.lse) a.lse[qrow0 + h] = (M + __log2f(L)) * 0.69314718055994530942f;
+            } else {
+                // this group's partial
+                const int64_t gidx = (bh * a.cgroups_cap + grp) * GQ + h;
+                publish(&a.grp_acc[gidx * D + c], A);
+                if (c == 0) {
+                    publish(&a.grp_ml[gidx * 2], M);
+                    publish(&a.grp_ml[gidx * 2 + 1], L);
+                }
+            }
         }
+        // this counter's arrivals are all counted: clear it for the next call
+        if (tid == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (final) return;
+        // second level: this group's partial is published; count it at the slice
+        pml = a.grp_ml + bh * a.cgroups_cap * GQ * 2;
+        pacc = a.grp_acc + bh * a.cgroups_cap * GQ * D;
+        ns = ng1;
+        ctr = a.counters + bh;
+        final = true;
     }
-    if (tid == 0) __hip_atomic_store(&a.counters[bh], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace dec

@@ -253,7 +253,7 @@ kvq_status kvq_cache_create(const kvq_config* cfg, void* dev_buf, size_t bytes, 
     c->split_tokens = 0;
     c->num_cu = ncu > 0 ? ncu : 256;
     const int64_t want = std::max<int64_t>(8, (16LL * c->num_cu + L.BH - 1) / L.BH);
-    const int64_t cap_q = std::min<int64_t>(std::min<int64_t>(want, 256), kMaxCombine / L.gqa - 1);
+    const int64_t cap_q = std::min<int64_t>(std::min<int64_t>(want, kMaxSplits - 1), kMaxCombine / L.gqa - 1);
     c->nsplit_cap = (int)cap_q + 1;
     if (L.lp >= 0) {
         // a decode split spans at most 63 pages' worth of key groups

@@ -13,6 +13,11 @@ enum DType : int { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2 };
 constexpr int kWaves = 4;              // waves per decode / quantize workgroup
 constexpr int kThreads = 64 * kWaves;  // 256 threads
 constexpr int kMaxCombine = 1024;      // max (splits x query heads per kv head)
+// Partials one workgroup merges in the split combine.  Up to kMaxMerge splits per
+// slice merge in one level; more form groups of ceil(sqrt(nsplit)) splits, whose
+// group partials merge in a second level, so a slice holds at most kMaxMerge^2.
+constexpr int kMaxMerge = 16;
+constexpr int kMaxSplits = kMaxMerge * kMaxMerge;
 
 // ---------------------------------------------------------------------------
 // Device buffer layout of one cache.  Slices bh = b * Hkv + kvh come first:

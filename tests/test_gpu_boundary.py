@@ -373,7 +373,9 @@ def test_uninitialised_buffers_do_not_reach_outputs(kw):
     log("case %s" % kw)
     cache = make_cache(w, max_tokens=4 * w.residual)
     cache._buf.fill_(0xFF)
-    ws_off = (w.batch * w.n_kv_heads * 4 + 255) // 256 * 256   # past the counters
+    # past the counters: at most 1 + 16 per slice (a slice counter and, for the
+    # two-level split combine, up to 16 group counters)
+    ws_off = (w.batch * w.n_kv_heads * 17 * 4 + 255) // 256 * 256
     base = cache._ws_ptr - cache._ws.data_ptr()
     cache._ws[base + ws_off:].fill_(0xFF)
     torch.cuda.synchronize()
@@ -391,12 +393,18 @@ def test_uninitialised_buffers_do_not_reach_outputs(kw):
     _attend_and_check(w, cache, np.concatenate([K, K1], 2), np.concatenate([V, V1], 2), seed=77)
 
 
-# Split combines of more (split, head) pairs than the combine stages in LDS (512):
-# one sequence, one kv head, a split per key group.
+# Split combines over many splits: one sequence, one kv head, a split per key
+# group.  Up to 16 splits merge in one level; more merge in groups of
+# ceil(sqrt(nsplit)) splits, then over the groups (17 splits: groups of 5, 5, 5, 2;
+# 256, the most a slice holds: 16 groups of 16).
 @pytest.mark.parametrize("kw,groups", [
-    (dict(n_q_heads=8, n_kv_heads=1, batch=1, k_group=64, residual=128, v_group=64), 100),   # 800 pairs
-    (dict(n_q_heads=4, n_kv_heads=1, batch=1, k_group=64, residual=128, v_group=64), 150),   # 600 pairs
+    (dict(n_q_heads=8, n_kv_heads=1, batch=1, k_group=64, residual=128, v_group=64), 100),   # groups of 10
+    (dict(n_q_heads=4, n_kv_heads=1, batch=1, k_group=64, residual=128, v_group=64), 150),   # groups of 13
     (dict(n_q_heads=8, n_kv_heads=1, batch=1, bits=2, k_group=32, residual=64, v_group=32), 120),  # VALU
+    (dict(n_q_heads=4, n_kv_heads=1, batch=1, k_group=64, residual=128, v_group=64), 16),    # one level
+    (dict(n_q_heads=4, n_kv_heads=1, batch=1, k_group=64, residual=64, v_group=64), 17),     # ragged groups
+    (dict(n_q_heads=2, n_kv_heads=1, batch=1, bits=2, k_group=32, residual=64, v_group=32), 256),  # 16 x 16
+    (dict(n_q_heads=1, n_kv_heads=1, batch=1, bits=4, k_group=64, residual=64, v_group=64), 256),  # MHA, 16 x 16
 ])
 def test_combine_of_many_splits(kw, groups):
     require_gpu()
@@ -406,6 +414,7 @@ def test_combine_of_many_splits(kw, groups):
     cache = make_cache(w, max_tokens=n)
     K, V = _tokens(w, n, 81, 2.0), _tokens(w, n, 82)
     cache.append(to_torch(K, w.dtype, DEV), to_torch(V, w.dtype, DEV))
+    assert cache.state()[2] == groups * w.k_group
     q = to_torch(wl.random_tokens(83, (w.batch, w.n_q_heads, w.head_dim), w.dtype), w.dtype, DEV)
     ref, ref_lse = cache.decode(q)
     ref, ref_lse = ref.clone(), ref_lse.clone()
