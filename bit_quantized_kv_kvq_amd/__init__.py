@@ -17,7 +17,9 @@ import ctypes
 import os
 from typing import Optional, Tuple
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvq.so")
+# KVQ_LIB names another build of the library (the host-sanitized one of
+# `python -m bit_quantized_kv_kvq_amd.build --sanitize`)
+LIB_PATH = os.environ.get("KVQ_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvq.so")
 
 KVQ_OK = 0
 KVQ_ERR_INVALID_ARG = -1

@@ -1,6 +1,17 @@
 """Build libkvq.so for gfx950 with hipcc (in-tree; the .so ships with the sources).
 
     python -m bit_quantized_kv_kvq_amd.build [--jobs N]
+    python -m bit_quantized_kv_kvq_amd.build --sanitize
+
+--sanitize builds _build/san/libkvq_san.so instead: the host code of the
+sources with host code in them (the C ABI, launch planning, validation) under
+AddressSanitizer and UndefinedBehaviorSanitizer (-Xarch_host: the gfx950 code is
+built as usual), linked with the kernels of a normal build.  A process loads it
+with the clang ASan runtime preloaded (sanitizer_runtime() names it), e.g.
+
+    LD_PRELOAD=$(python -c "import bit_quantized_kv_kvq_amd.build as b; print(b.sanitizer_runtime())") \
+    ASAN_OPTIONS=detect_leaks=0 KVQ_LIB=bit_quantized_kv_kvq_amd/_build/san/libkvq_san.so \
+    python -m pytest tests/test_lib_host.py
 """
 from __future__ import annotations
 
@@ -72,7 +83,55 @@ def build(jobs: int | None = None, verbose: bool = True) -> str:
     return LIB
 
 
+# sources whose host code does more than register kernels
+HOST_SOURCES = ["kvq_host.cpp", "quant.hip", "decode.hip", "probe.hip"]
+SAN_FLAGS = ["-O1", "-g", "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=undefined"]
+
+
+def sanitizer_runtime() -> str:
+    """Path of the clang AddressSanitizer runtime to preload for libkvq_san.so."""
+    out = subprocess.run([HIPCC, "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True,
+                         text=True).stdout.strip()
+    if not os.path.isabs(out):
+        raise RuntimeError("no clang ASan runtime found")
+    return out
+
+
+def build_sanitized(jobs: int | None = None) -> str:
+    """_build/san/libkvq_san.so: HOST_SOURCES with host-side ASan + UBSan, the other
+    objects from a normal build (built first if missing)."""
+    san = os.path.join(BUILD, "san")
+    os.makedirs(san, exist_ok=True)
+    if not all(os.path.exists(os.path.join(BUILD, os.path.splitext(s)[0] + ".o")) for s in SOURCES):
+        build(jobs, verbose=False)
+
+    def one(src):
+        obj = os.path.join(san, os.path.splitext(src)[0] + ".o")
+        flags = [f for f in FLAGS if f != "-O3"]
+        cmd = [HIPCC, *flags, *SAN_FLAGS, *(DECODE_FLAGS if src.startswith("decode") else []),
+               *(["-x", "hip"] if src.endswith(".cpp") else []), "-c", os.path.join(CSRC, src), "-o", obj]
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError("hipcc failed for %s:\n%s" % (src, res.stderr))
+        return obj
+
+    with cf.ThreadPoolExecutor(jobs or len(HOST_SOURCES)) as ex:
+        objs = list(ex.map(one, HOST_SOURCES))
+    objs += [os.path.join(BUILD, os.path.splitext(s)[0] + ".o") for s in SOURCES if s not in HOST_SOURCES]
+    out = os.path.join(san, "libkvq_san.so")
+    subprocess.check_call([HIPCC, "--offload-arch=" + ARCH, "-shared", "-shared-libsan", "-Xarch_host",
+                           "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined", "-o", out, *objs])
+    print("built", out)
+    return out
+
+
 if __name__ == "__main__":
     ap = argparse.ArgumentParser()
     ap.add_argument("--jobs", type=int, default=None)
-    build(ap.parse_args().jobs)
+    ap.add_argument("--sanitize", action="store_true")
+    args = ap.parse_args()
+    if args.sanitize:
+        build_sanitized(args.jobs)
+    else:
+        build(args.jobs)

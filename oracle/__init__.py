@@ -67,10 +67,26 @@ def load(path: str):
     return L
 
 
+def build_sanitized() -> str:
+    """The oracle under gcc's AddressSanitizer and UndefinedBehaviorSanitizer
+    (libkvq_oracle_san.so beside the source).  A process loads it through
+    KVQ_ORACLE_LIB with gcc's libasan and libubsan preloaded, e.g.
+
+        LD_PRELOAD=$(gcc -print-file-name=libasan.so):$(gcc -print-file-name=libubsan.so) \
+        ASAN_OPTIONS=detect_leaks=0 KVQ_ORACLE_LIB=oracle/libkvq_oracle_san.so \
+        python -m pytest tests/test_oracle_*.py
+    """
+    out = os.path.join(_HERE, "libkvq_oracle_san.so")
+    flags = [f for f in CFLAGS if f != "-O2"] + ["-O1", "-g", "-fno-omit-frame-pointer",
+                                                 "-fsanitize=address,undefined", "-fno-sanitize-recover=all"]
+    subprocess.check_call(["gcc", *flags, _SRC, "-o", out, "-lm"])
+    return out
+
+
 def lib():
     global _lib
     if _lib is None:
-        _lib = load(build())
+        _lib = load(os.environ.get("KVQ_ORACLE_LIB") or build())
     return _lib
 
 
