@@ -447,8 +447,9 @@ struct MStream {
         uint32_t voi[NSB];
     };
     static constexpr int GT = TM * TPG;  // tokens per key group
-    float* kc;  // SP: key outlier terms [GQ][GT]
-    float* vc;  // SP: value outlier terms [GQ][D]
+    int* kc;       // SP: key outlier terms [GQ][GT], fixed point of 2^-k
+    int* vc;       // SP: value outlier terms [GQ][D], fixed point
+    float kc_inv;  // SP: 2^-k of the key group's terms
     uint32_t kov_off, koi_off, vov_off, voi_off;
     int koi_shift, voi_shift;
 
@@ -478,7 +479,7 @@ struct MStream {
         kt_off = j * 8;
         ak_lds = lds;
         av_lds = lds + AK_BYTES;
-        kc = reinterpret_cast<float*>(lds + lds_bytes());
+        kc = reinterpret_cast<int*>(lds + lds_bytes());
         vc = kc + GQ * GT;
         kov_off = (uint32_t)a.rec_kov + KM * lane * 4;
         koi_off = (uint32_t)a.rec_koi + ((KM * lane * 2) & ~3);
@@ -579,20 +580,36 @@ struct MStream {
             }
         }
         if constexpr (SP) {
-            // key outliers: q_c (x_c - (u_c - z_c) s_c) onto the score of token t_c
+            // key outliers: q_c (x_c - (u_c - z_c) s_c) onto the score of token t_c, added
+            // in fixed point (LDS integer atomics; float ones run far slower): each term
+            // below 2^23 units of the group's largest, so the at most D terms of one
+            // token stay within int32
             const auto kov = whole(cur.kov);
-#pragma unroll
-            for (int h = 0; h < GQ; ++h)
-#pragma unroll
-                for (int i = 0; i < (GT + 63) / 64; ++i) kc[h * GT + ((i * 64 + lane) & (GT - 1))] = 0.0f;
+            float kt[KM][GQ], kmx = 0.0f;
+            int tk[KM];
 #pragma unroll
             for (int j = 0; j < KM; ++j) {
                 const uint32_t e = (cur.koi >> (KM == 1 ? koi_shift : 16 * j)) & 0xFFFFu;
                 const float delta = __uint_as_float(elem(kov, j)) -
                                     ((float)(e >> 8) - __uint_as_float(elem(kz, j))) * __uint_as_float(elem(ks, j));
+                tk[j] = (int)(e & 0xFFu);
 #pragma unroll
-                for (int h = 0; h < GQ; ++h) atomicAdd(&kc[h * GT + (int)(e & 0xFFu)], qv[h][j] * delta);
+                for (int h = 0; h < GQ; ++h) {
+                    kt[j][h] = qv[h][j] * delta;
+                    kmx = fmaxf(kmx, fabsf(kt[j][h]));
+                }
             }
+            const FixScale fs = fix_scale(group_max<64>(kmx));
+            const float kmul = fs.mul * 32.0f;
+            kc_inv = fs.inv * (1.0f / 32.0f);
+#pragma unroll
+            for (int h = 0; h < GQ; ++h)
+#pragma unroll
+                for (int i = 0; i < (GT + 63) / 64; ++i) kc[h * GT + ((i * 64 + lane) & (GT - 1))] = 0;
+#pragma unroll
+            for (int j = 0; j < KM; ++j)
+#pragma unroll
+                for (int h = 0; h < GQ; ++h) atomicAdd(&kc[h * GT + tk[j]], (int)rintf(kt[j][h] * kmul));
         }
         wave_lds_sync();
         const int hs = lane >> 4;
@@ -714,7 +731,7 @@ struct MStream {
                 }
                 if constexpr (SP) {  // rows of absent heads read a valid head's term, unused
                     const int head = min(4 * rb + (lane >> 4), GQ - 1);
-                    sc[rb][sb] += kc[head * GT + tig * TM + 16 * sb + (lane & 15)];
+                    sc[rb][sb] += (float)kc[head * GT + tig * TM + 16 * sb + (lane & 15)] * kc_inv;
                 }
             }
         }
@@ -784,15 +801,29 @@ struct MStream {
 #pragma unroll
             for (int rb = 0; rb < RBK; ++rb)
                 av[g][rb] = *reinterpret_cast<const i32x4*>(avb + ((g * RBK + rb) * 16 + (lane & 15)) * 64 + (lane >> 4) * 16);
+        float vc_inv = 0.0f;
         if constexpr (SP) {
             // after the weights' reads (LDS keeps a wave's operations in order): the atomics'
-            // latency overlaps the value products, and the read-back below comes after them
+            // latency overlaps the value products, and the read-back below comes after them.
+            // Fixed point as for the keys: each term below 2^24 units of the tile's
+            // largest, at most TM terms per (head, channel).
+            float vmx = 0.0f;
 #pragma unroll
             for (int rb = 0; rb < RBK; ++rb)
 #pragma unroll
                 for (int g = 0; g < NVG; ++g)
 #pragma unroll
-                    for (int sb = 0; sb < NSB; ++sb) atomicAdd(&vc[sp_idx[rb][g][sb]], sp_val[rb][g][sb]);
+                    for (int sb = 0; sb < NSB; ++sb) vmx = fmaxf(vmx, fabsf(sp_val[rb][g][sb]));
+            const FixScale fs = fix_scale(group_max<64>(vmx));
+            const float vmul = fs.mul * 64.0f;
+            vc_inv = fs.inv * (1.0f / 64.0f);
+#pragma unroll
+            for (int rb = 0; rb < RBK; ++rb)
+#pragma unroll
+                for (int g = 0; g < NVG; ++g)
+#pragma unroll
+                    for (int sb = 0; sb < NSB; ++sb)
+                        atomicAdd(&vc[sp_idx[rb][g][sb]], (int)rintf(sp_val[rb][g][sb] * vmul));
         }
 #pragma unroll
         for (int m = 0; m < NVB; ++m) {
@@ -820,9 +851,9 @@ struct MStream {
                 const int head = min(4 * rb + (lane >> 4), GQ - 1);
 #pragma unroll
                 for (int n = 0; n < NVM; ++n) {
-                    float* q = &vc[head * D + 64 * (n / 4) + 4 * (lane & 15) + (n % 4)];
-                    acc2[rb][n] += *q;
-                    *q = 0.0f;
+                    int* q = &vc[head * D + 64 * (n / 4) + 4 * (lane & 15) + (n % 4)];
+                    acc2[rb][n] = fmaf((float)*q, vc_inv, acc2[rb][n]);
+                    *q = 0;
                 }
             }
         }
@@ -983,10 +1014,12 @@ void decode_kernel(DecArgs a) {
 
     uint8_t* kd = dsm + wave * LP::wave_bytes(nvg);            // key digits
     // SP: key outlier terms [GQ][G] (the matrix-core stream's own copy of this pointer is the same)
-    float* kc = reinterpret_cast<float*>(kd + (MF ? MS::lds_bytes() : LP::valu_bytes(nvg)));
-    float* vc = kc + GQ * TILE * TPG;                                // SP: value outlier terms [GQ][D]
+    // (both in fixed point: LDS integer atomics run far faster than float ones)
+    int* kc = reinterpret_cast<int*>(kd + (MF ? MS::lds_bytes() : LP::valu_bytes(nvg)));
+    int* vc = kc + GQ * TILE * TPG;                                  // SP: value outlier terms [GQ][D]
+    float kc_inv = 0.0f;                                             // SP: 2^-k of the key group's terms
     if constexpr (SP)
-        for (int i = lane; i < GQ * D; i += 64) vc[i] = 0.0f;
+        for (int i = lane; i < GQ * D; i += 64) vc[i] = 0;
     uint8_t* pd = kd + GQ * kLimbs * D;                         // weight digits (x2)
     float* wg = reinterpret_cast<float*>(dsm + kWaves * LP::wave_bytes(nvg));
     float* s_acc = wg;                                          // [kWaves][GQ][D]
@@ -1242,21 +1275,35 @@ void decode_kernel(DecArgs a) {
             if constexpr (SP) {
                 // key outliers: q_c (x_c - (u_c - z_c) s_c) onto the score of token t_c
                 // of the group, through a per-wave table (zeroed, then added to; LDS
-                // keeps one wave's operations in order)
+                // keeps one wave's operations in order), in fixed point: each term below
+                // 2^23 units of the group's largest, at most D terms per token
                 constexpr int GT = TILE * TPG;
                 const auto kov = whole(cur.kov);
-#pragma unroll
-                for (int h = 0; h < GQ; ++h)
-#pragma unroll
-                    for (int i = 0; i < (GT + 63) / 64; ++i) kc[h * GT + ((i * 64 + lane) & (GT - 1))] = 0.0f;
+                float kt[KM][GQ], kmx = 0.0f;
+                int tk[KM];
 #pragma unroll
                 for (int j = 0; j < KM; ++j) {
                     const uint32_t e = (cur.koi >> (KM == 1 ? koi_shift : 16 * j)) & 0xFFFFu;
                     const float delta = __uint_as_float(elem(kov, j)) -
                                         ((float)(e >> 8) - __uint_as_float(elem(kz, j))) * __uint_as_float(elem(ks, j));
+                    tk[j] = (int)(e & 0xFFu);
 #pragma unroll
-                    for (int h = 0; h < GQ; ++h) atomicAdd(&kc[h * GT + (e & 0xFFu)], qv[h][j] * delta);
+                    for (int h = 0; h < GQ; ++h) {
+                        kt[j][h] = qv[h][j] * delta;
+                        kmx = fmaxf(kmx, fabsf(kt[j][h]));
+                    }
                 }
+                const FixScale fs = fix_scale(group_max<64>(kmx));
+                const float kmul = fs.mul * 32.0f;
+                kc_inv = fs.inv * (1.0f / 32.0f);
+#pragma unroll
+                for (int h = 0; h < GQ; ++h)
+#pragma unroll
+                    for (int i = 0; i < (GT + 63) / 64; ++i) kc[h * GT + ((i * 64 + lane) & (GT - 1))] = 0;
+#pragma unroll
+                for (int j = 0; j < KM; ++j)
+#pragma unroll
+                    for (int h = 0; h < GQ; ++h) atomicAdd(&kc[h * GT + tk[j]], (int)rintf(kt[j][h] * kmul));
             }
             wave_lds_sync();
             load_kl();
@@ -1319,6 +1366,7 @@ void decode_kernel(DecArgs a) {
             }
             // ---- online softmax: wave-uniform running max, rescaled every tile ----
             float vinv[GQ];
+            float vcinv[SP ? GQ : 1];  // SP: 2^-k of the value outlier terms of head h
 #pragma unroll
             for (int h = 0; h < GQ; ++h) {
                 float mt = -INFINITY;
@@ -1331,7 +1379,7 @@ void decode_kernel(DecArgs a) {
                     } else {
                         sc[h][u] = group_sum<LPT>(sc[h][u]) * kinv[h] - kbias[h];
                     }
-                    if constexpr (SP) sc[h][u] += kc[h * TILE * TPG + tig * TILE + slot * U + u];
+                    if constexpr (SP) sc[h][u] += (float)kc[h * TILE * TPG + tig * TILE + slot * U + u] * kc_inv;
                     mt = fmaxf(mt, sc[h][u]);
                 }
                 mt = slots_max<LPT>(mt);
@@ -1346,6 +1394,8 @@ void decode_kernel(DecArgs a) {
                 // ---- weights p_t s_t -> fixed-point digits in LDS ----
                 float pt[U], mx = 0.0f;
                 float pw[U];  // SP_WIDE: the tokens' softmax weights
+                float vt[SP ? U : 1];  // SP: value outlier terms p (x - (u - z) s) and their channels
+                int vi[SP ? U : 1];
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
                     const float p = fast_exp2(sc[h][u] - mn);
@@ -1360,7 +1410,8 @@ void decode_kernel(DecArgs a) {
                         const uint32_t e = (cur.voi[u] >> voi_shift[u]) & 0xFFFFu;
                         const float dv = __uint_as_float(cur.vov[u]) -
                                          ((float)(e >> 8) - __uint_as_float(vm.y)) * __uint_as_float(vm.x);
-                        atomicAdd(&vc[h * D + gz * a.GV + (int)(e & 0xFFu)], owner ? p * dv : 0.0f);
+                        vt[u] = owner ? p * dv : 0.0f;
+                        vi[u] = h * D + gz * a.GV + (int)(e & 0xFFu);
                     }
                     if constexpr (SP_WIDE) pw[u] = p;
                 }
@@ -1381,7 +1432,21 @@ void decode_kernel(DecArgs a) {
                     }
                     const uint32_t e = ((chunk < 2 ? cur.voi4.x : cur.voi4.y) >> (16 * (chunk & 1))) & 0xFFFFu;
                     const float dv = __uint_as_float(xv) - ((float)(e >> 8) - __uint_as_float(vmc.y)) * __uint_as_float(vmc.x);
-                    atomicAdd(&vc[h * D + (int)(e & 0xFFu)], pc * dv);
+                    vt[0] = pc * dv;
+                    vi[0] = h * D + (int)(e & 0xFFu);
+                }
+                if constexpr (SP) {
+                    // the tile's value outlier terms of head h into the table in fixed point:
+                    // each below 2^24 units of the largest, at most TILE terms per channel
+                    constexpr int NT = SP_WIDE ? 1 : U;
+                    float vmx = 0.0f;
+#pragma unroll
+                    for (int u = 0; u < NT; ++u) vmx = fmaxf(vmx, fabsf(vt[u]));
+                    const FixScale vfs = fix_scale(group_max<64>(vmx));
+                    const float vmul = vfs.mul * 64.0f;
+                    vcinv[h] = vfs.inv * (1.0f / 64.0f);
+#pragma unroll
+                    for (int u = 0; u < NT; ++u) atomicAdd(&vc[vi[u]], (int)rintf(vt[u] * vmul));
                 }
                 const FixScale fs = fix_scale(group_max<64>(mx));
                 vinv[h] = fs.inv;
@@ -1449,9 +1514,9 @@ void decode_kernel(DecArgs a) {
                     // lane of the two that hold them), then cleared for the next tile
 #pragma unroll
                     for (int c = 0; c < VCPL; ++c) {
-                        const float x = vc[h * D + c0v + c];
+                        const float x = (float)vc[h * D + c0v + c] * vcinv[h];
                         accv[h][c] += hb == 0 ? x : 0.0f;
-                        vc[h * D + c0v + c] = 0.0f;
+                        vc[h * D + c0v + c] = 0;
                     }
                 }
             }
