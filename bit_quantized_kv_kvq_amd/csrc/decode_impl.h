@@ -389,15 +389,17 @@ __device__ __forceinline__ int horner256(const i32x4& r) { return (r[2] * 256 + 
 // the tile's outputs.  A lane owns one (head, token) pair of each score product
 // and one (head, channel) pair of each output accumulator.
 // Streams that run two waves per SIMD (two workgroups per CU) with a ring of two
-// tiles: dense-and-sparse ones on either unit, and 2-bit matrix-core ones, with at
+// tiles: dense-and-sparse ones on the VALU and 2-bit matrix-core ones, with at
 // most four query heads per kv head.  They fit in 256 registers (a few spill
 // outside the loop), and the second wave hides the per-tile latency of the first
 // (reductions, LDS round trips, the outlier tables' atomics), which bounds these
-// streams rather than HBM.  Plain 4- and 8-bit streams and the plain VALU stream
-// are HBM-bound and keep one wave per SIMD with a ring of four tiles, which keeps
-// more bytes in flight; eight query heads per kv head would spill at 256 registers.
+// streams rather than HBM.  Plain 4- and 8-bit streams, the plain VALU stream and
+// the 4-bit dense-and-sparse matrix-core stream are HBM-bound and keep one wave
+// per SIMD with a ring of four tiles, which keeps more bytes in flight (measured
+// on the GQA outlier workload: 126 against 129 us with two waves); eight query
+// heads per kv head would spill at 256 registers.
 __host__ __device__ constexpr bool two_waves(bool mf, int bits, int gq, bool sp) {
-    return gq <= 4 && (sp || (mf && bits == 2));
+    return gq <= 4 && ((mf && bits == 2) || (sp && !mf));
 }
 
 // KT: per-token keys (one scale and zero point per token over its D channels):
