@@ -104,14 +104,26 @@ __device__ __forceinline__ float dpp(float v) {
 __device__ __forceinline__ float lane_value(float v, int l) {
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
 }
+// DPP move that only the rows in ROWS (a 4-bit row mask) take; the other rows get `old`.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_rows(float old, float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, old), __builtin_bit_cast(int, v),
+                                                                 CTRL, ROWS, 0xF, false));
+}
 // Whole-wave sum and max when every lane of each 16-lane row holds its row's
-// result: the four row results are read as scalars (no cross-row shuffle through
-// LDS), and every lane gets the same bits.  Full exec mask required.
+// result r0..r3: row_bcast:15 combines row 0's result into row 1 and row 2's into
+// row 3, row_bcast:31 then combines lane 31 (rows 0 and 1) into row 3, and lane
+// 63's total, (r3 + r2) + (r1 + r0), is read as a scalar, so every lane gets the
+// same bits (the same as any order of the two pairs).  Full exec mask required.
 __device__ __forceinline__ float rows_sum(float v) {
-    return (lane_value(v, 0) + lane_value(v, 16)) + (lane_value(v, 32) + lane_value(v, 48));
+    v += dpp_rows<0x142, 0xA>(0.0f, v);  // row_bcast:15 into rows 1, 3
+    v += dpp_rows<0x143, 0x8>(0.0f, v);  // row_bcast:31 into row 3
+    return lane_value(v, 63);
 }
 __device__ __forceinline__ float rows_max(float v) {
-    return fmaxf(fmaxf(lane_value(v, 0), lane_value(v, 16)), fmaxf(lane_value(v, 32), lane_value(v, 48)));
+    v = fmaxf(v, dpp_rows<0x142, 0xA>(v, v));
+    v = fmaxf(v, dpp_rows<0x143, 0x8>(v, v));
+    return lane_value(v, 63);
 }
 
 // Sum over aligned groups of N consecutive lanes; every lane of a group gets the
