@@ -425,3 +425,42 @@ def test_combine_of_many_splits(kw, groups):
     scale = max(1.0, ref.abs().max().item())
     assert (out - ref).abs().max().item() <= 5e-5 * scale
     assert (lse - ref_lse).abs().max().item() <= 5e-5 * max(1.0, ref_lse.abs().max().item())
+
+
+# Sequences of very different lengths under a split plan made for the longest:
+# most splits of the short sequences hold no key group (and the shortest no
+# quantized token at all), so their partials are empty; with more than 16 splits
+# the combine runs in two levels, and a group of empty partials merges to an empty
+# group partial.
+@pytest.mark.parametrize("kw", [
+    dict(batch=3, n_kv_heads=2, n_q_heads=8, bits=2, k_group=64, residual=128, v_group=64),  # matrix cores
+    dict(batch=3, n_kv_heads=2, n_q_heads=2, k_group=32, residual=64, v_group=32),          # VALU stream
+])
+def test_ragged_lengths_under_many_splits(kw):
+    require_gpu()
+    w = _w(**kw)
+    lens = [3000, 130, 1]
+    n_max = max(lens)
+    log("case %s lens %s" % (kw, lens))
+    cache = make_cache(w, max_tokens=n_max)
+    K, V = _tokens(w, n_max, 111, 2.0), _tokens(w, n_max, 112)
+    cache.append_ragged(to_torch(K, w.dtype, DEV), to_torch(V, w.dtype, DEV), lens)
+    cache.set_split_tokens(w.k_group)   # one split per key group of the longest: more than 16
+    q = wl.random_tokens(113, (w.batch, w.n_q_heads, w.head_dim), w.dtype)
+    out, lse = cache.decode(to_torch(q, w.dtype, DEV))
+    torch.cuda.synchronize()
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    kf, vf, qf = (wl.storage_to_f32(x, w.dtype) for x in (K, V, q))
+    scale = oracle.default_scale(w.head_dim)
+    err = 0.0
+    for b in range(w.batch):
+        for h in range(w.n_kv_heads):
+            st = oracle.build_slice(kf[b, h, :lens[b]], vf[b, h, :lens[b]], head_dim=w.head_dim, bits=w.bits,
+                                    k_group=w.k_group, v_group=w.v_group, residual=w.residual,
+                                    n_sink=w.n_sink, codec=w.codec)
+            Kd, Vd = oracle.dequant_slice(st)
+            for j in range(w.gqa):
+                eo, el = oracle.attention(qf[b, h * w.gqa + j], Kd, Vd, scale)
+                err = max(err, float(np.abs(out[b, h * w.gqa + j] - eo).max()),
+                          abs(float(lse[b, h * w.gqa + j]) - el))
+    assert err <= ATOL, err
