@@ -49,6 +49,7 @@ struct Choice {
     const void* fn;
     int cpl, tile, tpg, lds;
     int occ;  // workgroups per CU the kernel is planned for
+    bool mf;  // the quantized stream runs on the matrix cores
 };
 
 Choice choose(const Layout& L) {
@@ -63,6 +64,7 @@ Choice choose(const Layout& L) {
         c.cpl = 16;
     c.fn = nullptr;
     c.occ = 1;
+    c.mf = false;
     if (c.tile * c.tpg == L.G) {
         if (L.bits == 4 && L.D == 128) c.fn = dec::decode_kernel_ptr<4, 128>(L.gqa, c.cpl, c.tile, c.tpg);
         if (L.bits == 2 && L.D == 128) c.fn = dec::decode_kernel_ptr<2, 128>(L.gqa, c.cpl, c.tile, c.tpg);
@@ -85,6 +87,7 @@ Choice choose(const Layout& L) {
         if (L.bits == 8 && L.D == 64) mf = dec::decode_mf_kernel_ptr<8, 64>(L.gqa, tpg, L.nvg);
         if (mf != nullptr) {
             c.fn = mf;
+            c.mf = true;
             c.occ = dec::two_waves(true, L.bits, L.gqa, false) ? 2 : 1;
             c.tile = 64;
             c.tpg = tpg;
@@ -98,8 +101,10 @@ Choice choose(const Layout& L) {
         // stream (32-token tiles for several query heads per kv head)
         c.fn = nullptr;
         c.occ = 1;
+        c.mf = false;
         const int spb = 4 * (L.gqa * L.G + L.gqa * L.D);
         if (L.gqa >= 2 && L.G >= 64 && L.G <= 256 && L.GV >= 64 && L.D == 128 && L.bits != 8) {
+            c.mf = true;
             c.tile = 64;
             c.tpg = L.G / 64;
             c.occ = dec::two_waves(true, L.bits, L.gqa, true) ? 2 : 1;
@@ -126,6 +131,7 @@ Choice choose(const Layout& L) {
         // per kv head; other shapes have no kernel
         c.fn = nullptr;
         c.occ = 1;
+        c.mf = false;
         c.tile = 64;
         c.tpg = L.G / 64;
         const bool mf = (L.gqa >= 2 || L.bits == 8) && L.GV >= 64 && (L.D == 128 || L.nvg == 1);
@@ -140,6 +146,7 @@ Choice choose(const Layout& L) {
         }
         if (kt != nullptr) {
             c.fn = kt;
+            c.mf = mf;
             c.occ = dec::two_waves(mf, L.bits, L.gqa, false) ? 2 : 1;
             if (mf) {
                 const int rbk = (L.gqa + 3) / 4;
@@ -230,6 +237,34 @@ hipError_t launch_decode(const Layout& L, const DevPtrs& P, const DecodeRequest&
     // kMaxMerge partials
     if (nsplit > kMaxSplits) return hipErrorInvalidValue;
 
+    // Split weights.  With two workgroups per CU and a grid that fills every slot
+    // exactly once, the workgroup dispatched first on a CU runs ahead of the one
+    // dispatched second: its waves are older and win the SIMDs' issue arbitration
+    // (per-workgroup timestamps: 33 against 42.5 us of stream on the LogQuant
+    // decode, 20 against 26 us on the long-context one, on every CU).  Workgroups
+    // take one slot on every CU, in dispatch order, before any CU takes a second,
+    // and the grid is split-major, so splits below num_cu / BH run first on their
+    // CUs; they take 11/8 of the others' key groups, so that both end together.
+    // This is done for the matrix-core stream (on the VALU stream's outlier kernel,
+    // the one other stream run two per CU, it measured 1% slower).  Otherwise (and
+    // for paged records, whose splits are bounded in pages, or a fixed split size)
+    // every split takes gps groups and the grid is slice-major.  The kernels compile
+    // the weighted plan exactly where ch.mf && ch.occ == 2 (their WSPLIT).
+    int s1 = nsplit;
+    int64_t gps2 = gps;
+    if (ch.mf && ch.occ == 2 && L.lp < 0 && rq.split_tokens == 0 && nsplit > 1 && ng > 0 &&
+        (int64_t)nsplit * L.BH == 2 * (int64_t)rq.num_cu && rq.num_cu % L.BH == 0) {
+        s1 = nsplit / 2;  // = num_cu / BH
+        const int64_t pair = (ng + s1 - 1) / s1;  // groups of a first and a second split
+        const int64_t g1 = (pair * 11 + 9) / 19;
+        if (g1 >= 1 && pair - g1 >= 1) {
+            gps = g1;
+            gps2 = pair - g1;
+        } else {
+            s1 = nsplit;
+        }
+    }
+
     dec::DecArgs a;
     a.rec = P.rec;
     a.ksink = P.ksink;
@@ -267,6 +302,9 @@ hipError_t launch_decode(const Layout& L, const DevPtrs& P, const DecodeRequest&
     a.GV = L.GV;
     a.nvg = L.nvg;
     a.gps = (int)gps;
+    a.s1 = s1;
+    a.gps2 = (int)gps2;
+    a.split_major = s1 < nsplit ? 1 : 0;
     a.ngroups = (int)ng;
     a.nsplit = nsplit;
     a.nsplit_cap = rq.nsplit_cap;
@@ -281,7 +319,7 @@ hipError_t launch_decode(const Layout& L, const DevPtrs& P, const DecodeRequest&
     a.page_bytes = (uint32_t)L.page_bytes;
     a.pool_bytes = (uint32_t)(L.pool_pages * L.page_bytes);
     void* args[] = {&a};
-    const dim3 grid((unsigned)nsplit, (unsigned)L.BH);
+    const dim3 grid = a.split_major ? dim3((unsigned)L.BH, (unsigned)nsplit) : dim3((unsigned)nsplit, (unsigned)L.BH);
     if (rq.ev_start != nullptr)
         return hipExtLaunchKernel(ch.fn, grid, dim3(kThreads), args, (size_t)ch.lds, stream, rq.ev_start,
                                   rq.ev_stop, 0);

@@ -86,6 +86,9 @@ struct DecArgs {
     float* grp_acc;
     float* grp_ml;
     int cgs, cgroups_cap;
+    // Split weights: splits below s1 take gps key groups, the others gps2; the grid
+    // is then split-major (split_major = 1).
+    int s1, gps2, split_major;
 };
 
 constexpr int kLimbs = 5;
@@ -1009,8 +1012,14 @@ void decode_kernel(DecArgs a) {
     constexpr int SPB = SP ? 4 * (GQ * TILE * TPG + GQ * D) : 0;
     using LP = LdsPlan<D, GQ, TILE, MF ? MS::lds_bytes() : 0, SPB>;
 
-    const int split = blockIdx.x;
-    const int64_t bh = blockIdx.y;
+    // grid = (nsplit, BH), or (BH, nsplit) with weighted splits (split_major: consecutive
+    // workgroups are the same split of consecutive slices).  The host weights the splits
+    // of the matrix-core stream run two workgroups per CU only; other instantiations
+    // compile without the weighted plan.
+    constexpr bool WSPLIT = MF && two_waves(MF, BITS, GQ, SP);
+    const bool split_major = WSPLIT && a.split_major;
+    const int split = split_major ? blockIdx.y : blockIdx.x;
+    const int64_t bh = split_major ? blockIdx.x : blockIdx.y;
     const int b = (int)(bh / a.Hkv), kvh = (int)(bh % a.Hkv);
     // this slice's sinks, full-precision tokens and key groups
     int nS_s = a.nS, nfp_s = a.nfp, ng_s = a.ngroups;
@@ -1119,8 +1128,11 @@ void decode_kernel(DecArgs a) {
     constexpr int NR = two_waves(false, BITS, GQ, SP) ? 2 : 4;
     constexpr int BODY = TPG > NR ? TPG : NR;  // tiles per loop iteration (2, 4 or 8)
     constexpr int GB = BODY / TPG;             // key groups per loop iteration
-    const int g_begin = split * a.gps;
-    const int g_end = min(g_begin + a.gps, ng_s);
+    // splits 0 .. s1 - 1 take gps key groups each, the others gps2 (fewer where the
+    // host weights the splits, see the split plan)
+    const bool first = !WSPLIT || split < a.s1;
+    const int g_begin = first ? split * a.gps : a.s1 * a.gps + (split - a.s1) * a.gps2;
+    const int g_end = min(g_begin + (first ? a.gps : a.gps2), ng_s);
     const int n_my_groups = g_begin + wave < g_end ? (g_end - g_begin - wave + kWaves - 1) / kWaves : 0;
 
     {
@@ -1793,7 +1805,8 @@ void decode_kernel(DecArgs a) {
     const float* pacc = a.part_acc + (bh * a.nsplit_cap + (int64_t)grp * a.cgs) * GQ * D;
     int ns = min(a.cgs, a.nsplit - grp * a.cgs);  // partials the next merge takes
     // slice counter at [bh]; with two levels, group counters at [BH + bh * cgroups_cap + grp]
-    unsigned* ctr = ng1 > 1 ? a.counters + gridDim.y + bh * a.cgroups_cap + grp : a.counters + bh;
+    const int64_t n_slices = split_major ? gridDim.x : gridDim.y;
+    unsigned* ctr = ng1 > 1 ? a.counters + n_slices + bh * a.cgroups_cap + grp : a.counters + bh;
     bool final = ng1 == 1;
     // Every load here is a round trip to the coherence point (about a microsecond),
     // so a merge takes one: a merge takes at most kMaxMerge partials (the host's

@@ -464,3 +464,64 @@ def test_ragged_lengths_under_many_splits(kw):
                 err = max(err, float(np.abs(out[b, h * w.gqa + j] - eo).max()),
                           abs(float(lse[b, h * w.gqa + j]) - el))
     assert err <= ATOL, err
+
+
+# Weighted split plan.  The 2-bit matrix-core streams run two workgroups per CU;
+# where the default plan fills every slot once (splits x slices = 2 x CUs, the
+# slices dividing the CUs), the splits dispatched first on their CUs take 11/8 of
+# the key groups of the others, on a split-major grid.  With T = 2 CUs / slices,
+# 4T - 3 key groups (4T - 2 where the residual flushes two groups at a time) plan
+# T splits, the first half of 5 groups and the second of 3, the last one empty (or
+# of one group); the shorter sequence of the ragged case leaves more splits empty.
+# The result must match the oracle and the plain plan of the same split count
+# (four groups a split, a fixed split size, which the weighting skips).
+@pytest.mark.parametrize("kw", [
+    dict(n_q_heads=8, bits=2, k_group=64, residual=128, v_group=64),                       # g = 4
+    dict(n_q_heads=4, bits=2, head_dim=64, k_group=64, residual=64, v_group=64, dtype="f32"),  # g = 2, D64
+    dict(n_q_heads=8, bits=2, k_group=64, residual=128, v_group=64, key_axis=1),           # per-token keys
+    dict(n_q_heads=8, bits=2, k_group=64, residual=128, v_group=64, outliers=1),           # dense-and-sparse
+])
+@pytest.mark.parametrize("ragged", [False, True])
+def test_weighted_split_plan(kw, ragged):
+    require_gpu()
+    w = _w(**kw)
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    bh = w.batch * w.n_kv_heads
+    if n_cu % bh:
+        pytest.skip("weighted plan needs the slices to divide the %d CUs" % n_cu)
+    T = 2 * n_cu // bh
+    ng = 4 * T - 3
+    n = ng * w.k_group + w.residual // 2 + 7
+    lens = [n, n - 37 * w.k_group - 5] if ragged else [n, n]
+    log("case %s ragged=%s n=%d lens=%s CUs=%d" % (kw, ragged, n, lens, n_cu))
+    cache = make_cache(w, max_tokens=n)
+    K, V = _tokens(w, n, 121, 2.0), _tokens(w, n, 122)
+    if ragged:
+        cache.append_ragged(to_torch(K, w.dtype, DEV), to_torch(V, w.dtype, DEV), lens)
+    else:
+        cache.append(to_torch(K, w.dtype, DEV), to_torch(V, w.dtype, DEV))
+    q = wl.random_tokens(123, (w.batch, w.n_q_heads, w.head_dim), w.dtype)
+    qd = to_torch(q, w.dtype, DEV)
+    out, lse = cache.decode(qd)
+    out, lse = out.clone(), lse.clone()
+    cache.set_split_tokens(4 * w.k_group)   # same split count, equal splits
+    ref, ref_lse = cache.decode(qd)
+    torch.cuda.synchronize()
+    scale = max(1.0, ref.abs().max().item())
+    assert (out - ref).abs().max().item() <= 5e-5 * scale
+    assert (lse - ref_lse).abs().max().item() <= 5e-5 * max(1.0, ref_lse.abs().max().item())
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    kf, vf, qf = (wl.storage_to_f32(x, w.dtype) for x in (K, V, q))
+    sc = oracle.default_scale(w.head_dim)
+    err = 0.0
+    for b in range(w.batch):
+        for h in range(w.n_kv_heads):
+            st = oracle.build_slice(kf[b, h, :lens[b]], vf[b, h, :lens[b]], head_dim=w.head_dim, bits=w.bits,
+                                    k_group=w.k_group, v_group=w.v_group, residual=w.residual,
+                                    n_sink=w.n_sink, codec=w.codec, outliers=w.outliers, key_axis=w.key_axis)
+            Kd, Vd = oracle.dequant_slice(st)
+            for j in range(w.gqa):
+                eo, el = oracle.attention(qf[b, h * w.gqa + j], Kd, Vd, sc)
+                err = max(err, float(np.abs(out[b, h * w.gqa + j] - eo).max()),
+                          abs(float(lse[b, h * w.gqa + j]) - el))
+    assert err <= ATOL, err
