@@ -35,6 +35,9 @@
 //   - values: dword (block, channel) of the value codes holds one channel of TB
 //     consecutive tokens; a lane owns D/32 channels of one block, so its value
 //     dot products run along tokens;
+//   - the folded query's digits go through LDS as bytes that already pair the
+//     channels of a code nibble dword (the writer takes the partner channel's
+//     digits from a neighbouring lane), so a lane reads its digit dwords whole;
 //   - softmax weights and digits move between the two mappings through LDS as
 //     bytes, and are packed into digit dwords with one shift-or;
 //   - the running max is wave-uniform and updated once per tile;
@@ -297,15 +300,6 @@ __device__ __forceinline__ FixScale fix_scale(float maxabs) {
     return f;
 }
 
-// balanced base-16 digits of n (|n| <= 2^18): digit i as a two's-complement nibble
-__device__ __forceinline__ void store_digits(uint8_t* dst, int stride, int n) {
-#pragma unroll
-    for (int i = 0; i < kLimbs; ++i) {
-        dst[i * stride] = (uint8_t)(n & 15);
-        n = (n + 8) >> 4;
-    }
-}
-
 // Digit `li` (a two's-complement nibble, in the low half of a byte) of the
 // balanced base-16 expansion of each of U integers, stored as U consecutive bytes.
 // Adding C_li = 8 (16^li - 1) / 15 turns the digits below li into their offset
@@ -326,11 +320,45 @@ __device__ __forceinline__ void store_digit_run(uint8_t* dst, const int (&n)[U],
 
 __device__ __forceinline__ uint32_t lds32(const uint8_t* p) { return *reinterpret_cast<const uint32_t*>(p); }
 
-// A nibble dword of codes pairs a "lo" run of 4 items (byte k, low nibble) with a
-// "hi" run of 4 items (byte k, high nibble); the matching digit dword is built
-// from the two runs of digit bytes.
-__device__ __forceinline__ uint32_t digit_dword(const uint8_t* lo, const uint8_t* hi) {
-    return lds32(lo) | (lds32(hi) << 4);
+// Key digit bytes of the VALU stream, paired.  A nibble dword of codes holds the
+// codes of channel pairs (c, c + P), c a "lo" channel (c mod 2P < P): P = 4 for
+// 4-bit codes, 8 for 2-bit codes.  Limb li of a head's folded query is stored as
+// D/2 bytes, one per pair: the digit of c in the low nibble, that of c + P in the
+// high one, at byte (c / 2P) P + c mod 2P.  A lane's digit dwords of one limb (its
+// CPL channels, a multiple of 2P) are then consecutive, read without combining.
+// The writer lane of KM channels c.. (c lo) takes the digits of c + P.. from lane
+// + P / KM (a DPP row shift within the row of 16 lanes); the lanes of hi channels
+// write the same pattern into a second, unread area of the same size.
+template <int KM, int P>
+__device__ __forceinline__ void store_key_digits(uint8_t* lo_base, uint8_t* hi_base, int stride, int lane,
+                                                 const int (&n)[KM]) {
+    static_assert(KM == 1 || KM == 2, "one or two fold channels per lane");
+    constexpr int LPD = 4 / KM;                  // limbs per packed dword
+    constexpr int NW = (kLimbs + LPD - 1) / LPD;
+    constexpr int KPL = P / KM;                  // lanes from the owner of c to that of c + P
+    static_assert(KPL >= 1 && 2 * KPL <= 16, "pair partner within the lane's row");
+    uint32_t w[NW];
+#pragma unroll
+    for (int k = 0; k < NW; ++k) w[k] = 0u;
+#pragma unroll
+    for (int li = 0; li < kLimbs; ++li) {
+        const int C = (int)((8u * ((1u << (4 * li)) - 1u)) / 15u);
+#pragma unroll
+        for (int j = 0; j < KM; ++j)
+            w[li / LPD] |= (((uint32_t)(n[j] + C) >> (4 * li)) & 15u) << (8 * (KM * (li % LPD) + j));
+    }
+#pragma unroll
+    for (int k = 0; k < NW; ++k) w[k] |= (uint32_t)__builtin_amdgcn_mov_dpp((int)w[k], 0x100 + KPL, 0xF, 0xF, true) << 4;
+    const int c = KM * lane;
+    const bool lo = c % (2 * P) < P;
+    const int cl = lo ? c : c - P;
+    uint8_t* dst = (lo ? lo_base : hi_base) + (cl / (2 * P)) * P + cl % (2 * P);
+#pragma unroll
+    for (int li = 0; li < kLimbs; ++li) {
+        const uint32_t v = w[li / LPD] >> (8 * KM * (li % LPD));
+        if constexpr (KM == 2) *reinterpret_cast<uint16_t*>(dst + li * stride) = (uint16_t)v;
+        else dst[li * stride] = (uint8_t)v;
+    }
 }
 
 // nw dwords from p (aligned to the largest load used): 16-byte loads where they
@@ -944,7 +972,8 @@ struct MStream {
 // ---------------------------------------------------------------------------
 template <int D, int GQ, int TILE, int MFB = 0, int SPB = 0>
 struct LdsPlan {
-    // per wave: key digits [GQ][limb][D] bytes, then two buffers of weight digits
+    // per wave: key digits [GQ][limb][D/2] paired bytes and an unread area of the
+    // same size (written by the lanes of the pairs' upper channels), then two buffers of weight digits
     // [GQ][nvg][limb][TILE] bytes (alternating by tile), then the outlier
     // corrections of dense-and-sparse records (SPB bytes); with the matrix-core
     // stream, its operand rows (MFB bytes)
@@ -1254,22 +1283,32 @@ void decode_kernel(DecArgs a) {
         uint32_t kl[GQ][kLimbs][KND];  // key digit dwords of this lane's channels
         float kinv[GQ], kbias[GQ];
 
-        // This lane's key digit dwords, read back from the wave's digit bytes.
+        // This lane's key digit dwords, read back from the wave's paired digit bytes
+        // (store_key_digits: limb li of head h at kd + (h * kLimbs + li) * D / 2, the
+        // pairs of this lane's channels at chunk * CPL / 2).
+        constexpr int KP = VB == 4 ? 4 : 8;  // channel distance of a code nibble pair
+        static_assert(CPL % (2 * KP) == 0, "a lane's channels are whole pair blocks");
         auto load_kl = [&]() __attribute__((always_inline)) {
 #pragma unroll
             for (int h = 0; h < GQ; ++h)
 #pragma unroll
                 for (int li = 0; li < kLimbs; ++li) {
-                    const uint8_t* base = kd + (h * kLimbs + li) * D + chunk * CPL;
-#pragma unroll
-                    for (int nd = 0; nd < KND; ++nd) {
-                        if constexpr (VB == 4)
-                            kl[h][li][nd] = digit_dword(base + 8 * nd, base + 8 * nd + 4);
-                        else
-                            kl[h][li][nd] = digit_dword(base + 16 * (nd >> 1) + 4 * (nd & 1),
-                                                        base + 16 * (nd >> 1) + 8 + 4 * (nd & 1));
+                    const uint8_t* base = kd + (h * kLimbs + li) * (D / 2) + chunk * (CPL / 2);
+                    if constexpr (KND == 4) {
+                        const u32x4 x = *reinterpret_cast<const u32x4*>(base);
+                        kl[h][li][0] = x.x, kl[h][li][1] = x.y, kl[h][li][2] = x.z, kl[h][li][3] = x.w;
+                    } else if constexpr (KND == 2) {
+                        const u32x2 x = *reinterpret_cast<const u32x2*>(base);
+                        kl[h][li][0] = x.x, kl[h][li][1] = x.y;
+                    } else {
+                        static_assert(KND == 1, "1, 2 or 4 digit dwords per limb");
+                        kl[h][li][0] = lds32(base);
                     }
                 }
+        };
+        // the folded query's digits of head h: n[j] of channel KM * lane + j
+        auto store_kd = [&](int h, const int (&n)[KM]) __attribute__((always_inline)) {
+            store_key_digits<KM, KP>(kd + h * kLimbs * (D / 2), kd + (GQ + h) * kLimbs * (D / 2), D / 2, lane, n);
         };
 
         // Folds the key scales of a group into the query, in fixed point: digit
@@ -1294,9 +1333,10 @@ void decode_kernel(DecArgs a) {
                 const FixScale fs = fix_scale(group_max<64>(mx[h]));
                 kinv[h] = fs.inv;
                 kbias[h] = group_sum<64>(bp[h]);
+                int n[KM];
 #pragma unroll
-                for (int j = 0; j < KM; ++j)
-                    store_digits(kd + (h * kLimbs) * D + KM * lane + j, D, (int)rintf(qt[h][j] * fs.mul));
+                for (int j = 0; j < KM; ++j) n[j] = (int)rintf(qt[h][j] * fs.mul);
+                store_kd(h, n);
             }
             if constexpr (SP) {
                 // key outliers: q_c (x_c - (u_c - z_c) s_c) onto the score of token t_c
@@ -1348,12 +1388,13 @@ void decode_kernel(DecArgs a) {
                 kinv[h] = fs.inv;
                 kbias[h] = 0.0f;
                 float nsum = 0.0f;
+                int n[KM];
 #pragma unroll
                 for (int j = 0; j < KM; ++j) {
-                    const int n = (int)rintf(qv[h][j] * fs.mul);
-                    store_digits(kd + (h * kLimbs) * D + KM * lane + j, D, n);
-                    nsum += (float)n;
+                    n[j] = (int)rintf(qv[h][j] * fs.mul);
+                    nsum += (float)n[j];
                 }
+                store_kd(h, n);
                 kqs[h] = group_sum<64>(nsum) * fs.inv;
             }
             wave_lds_sync();
