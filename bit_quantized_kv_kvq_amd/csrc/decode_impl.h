@@ -110,25 +110,32 @@ __device__ __forceinline__ float dpp(float v) {
 __device__ __forceinline__ float lane_value(float v, int l) {
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
 }
-// DPP move that only the rows in ROWS (a 4-bit row mask) take; the other rows get `old`.
-template <int CTRL, int ROWS>
-__device__ __forceinline__ float dpp_rows(float old, float v) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, old), __builtin_bit_cast(int, v),
-                                                                 CTRL, ROWS, 0xF, false));
-}
 // Whole-wave sum and max when every lane of each 16-lane row holds its row's
 // result r0..r3: row_bcast:15 combines row 0's result into row 1 and row 2's into
 // row 3, row_bcast:31 then combines lane 31 (rows 0 and 1) into row 3, and lane
 // 63's total, (r3 + r2) + (r1 + r0), is read as a scalar, so every lane gets the
 // same bits (the same as any order of the two pairs).  Full exec mask required.
+// Each step is one DPP add or max whose row mask leaves the other rows' values in
+// place (built from an update_dpp and an add, the compiler emits a copy, a DPP move
+// and the add).  The compiler does not see DPP inside the asm, so the asm keeps
+// the wait states itself: two before each DPP read of a VGPR just written by a
+// VALU instruction, and one before a v_readlane of it.
 __device__ __forceinline__ float rows_sum(float v) {
-    v += dpp_rows<0x142, 0xA>(0.0f, v);  // row_bcast:15 into rows 1, 3
-    v += dpp_rows<0x143, 0x8>(0.0f, v);  // row_bcast:31 into row 3
+    asm("s_nop 1\n\t"
+        "v_add_f32_dpp %0, %0, %0 row_bcast:15 row_mask:0xa bank_mask:0xf\n\t"
+        "s_nop 1\n\t"
+        "v_add_f32_dpp %0, %0, %0 row_bcast:31 row_mask:0x8 bank_mask:0xf\n\t"
+        "s_nop 0"
+        : "+v"(v));
     return lane_value(v, 63);
 }
 __device__ __forceinline__ float rows_max(float v) {
-    v = fmaxf(v, dpp_rows<0x142, 0xA>(v, v));
-    v = fmaxf(v, dpp_rows<0x143, 0x8>(v, v));
+    asm("s_nop 1\n\t"
+        "v_max_f32_dpp %0, %0, %0 row_bcast:15 row_mask:0xa bank_mask:0xf\n\t"
+        "s_nop 1\n\t"
+        "v_max_f32_dpp %0, %0, %0 row_bcast:31 row_mask:0x8 bank_mask:0xf\n\t"
+        "s_nop 0"
+        : "+v"(v));
     return lane_value(v, 63);
 }
 
@@ -285,6 +292,13 @@ __device__ __forceinline__ float2 fetch2(const float* p) {
 __device__ __forceinline__ int dot8(uint32_t a, uint32_t b, int c) {
     return __builtin_amdgcn_sdot8((int)a, (int)b, c, false);
 }
+// The same with a zero accumulator, as the three-operand form with an inline 0
+// (the builtin with c = 0 becomes a register cleared to 0 and the accumulating form).
+__device__ __forceinline__ int dot8_0(uint32_t a, uint32_t b) {
+    int r;
+    asm("v_dot8_i32_i4 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
 
 // Fixed-point scale for values of magnitude <= maxabs: mul = 2^(18-E), inv = 2^(E-18)
 // with maxabs < 2^E, so |rint(x * mul)| <= 2^18 fits five balanced hex digits.
@@ -300,22 +314,68 @@ __device__ __forceinline__ FixScale fix_scale(float maxabs) {
     return f;
 }
 
-// Digit `li` (a two's-complement nibble, in the low half of a byte) of the
-// balanced base-16 expansion of each of U integers, stored as U consecutive bytes.
-// Adding C_li = 8 (16^li - 1) / 15 turns the digits below li into their offset
-// (non-negative) form, so the shifted sum holds digit li in its low nibble.
+// (a & m) | (b & ~m) in one instruction (the compiler emits an and and an and-or)
+__device__ __forceinline__ uint32_t bfi(uint32_t m, uint32_t a, uint32_t b) {
+    uint32_t r;
+    asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "s"(m), "v"(a), "v"(b));
+    return r;
+}
+
+// Pair bytes of two digit words x (low nibbles) and y (high nibbles), all five
+// limbs as two's-complement nibbles: limbs 0, 2, 4 in bytes 0, 1, 2 of ev, limbs
+// 1, 3 in bytes 0, 1 of od.
+__device__ __forceinline__ void pair_bytes(uint32_t x, uint32_t y, uint32_t& ev, uint32_t& od) {
+    ev = bfi(0x0F0F0Fu, x, y << 4);
+    od = bfi(0x0F0F0Fu, x >> 4, y);
+}
+
+// Stores limb li's pair byte of each of N pair words (pair_bytes) as N consecutive
+// bytes at dst + li * stride.
+template <int N>
+__device__ __forceinline__ void store_limb_bytes(uint8_t* dst, int stride, const uint32_t (&ev)[N],
+                                                 const uint32_t (&od)[N]) {
+    if constexpr (N == 1) {
+        dst[0] = (uint8_t)ev[0];
+        dst[2 * stride] = (uint8_t)(ev[0] >> 8);
+        dst[4 * stride] = (uint8_t)(ev[0] >> 16);
+        dst[stride] = (uint8_t)od[0];
+        dst[3 * stride] = (uint8_t)(od[0] >> 8);
+    } else if constexpr (N == 2) {
+        // bytes (k of word 0, k of word 1) for k = 0, 1 (limbs 0 and 2, or 1 and 3), and k = 2
+        const uint32_t e02 = __builtin_amdgcn_perm(ev[1], ev[0], 0x05010400u);
+        const uint32_t e4 = __builtin_amdgcn_perm(ev[1], ev[0], 0x0C0C0602u);
+        const uint32_t o13 = __builtin_amdgcn_perm(od[1], od[0], 0x05010400u);
+        *reinterpret_cast<uint16_t*>(dst) = (uint16_t)e02;
+        *reinterpret_cast<uint16_t*>(dst + 2 * stride) = (uint16_t)(e02 >> 16);
+        *reinterpret_cast<uint16_t*>(dst + 4 * stride) = (uint16_t)e4;
+        *reinterpret_cast<uint16_t*>(dst + stride) = (uint16_t)o13;
+        *reinterpret_cast<uint16_t*>(dst + 3 * stride) = (uint16_t)(o13 >> 16);
+    } else {
+        static_assert(N == 4, "1, 2 or 4 bytes per limb");
+#pragma unroll
+        for (int li = 0; li < kLimbs; ++li) {
+            uint32_t w = 0;
+#pragma unroll
+            for (int i = 0; i < N; ++i) w |= ((((li & 1) ? od[i] : ev[i]) >> (8 * (li >> 1))) & 0xFFu) << (8 * i);
+            *reinterpret_cast<uint32_t*>(dst + li * stride) = w;
+        }
+    }
+}
+
+// The five balanced base-16 digits of U integers (|n| <= 2^18), paired: byte i of
+// limb li's run (runs `stride` bytes apart) holds digit li of n[i] in its low
+// nibble and that of n[i + U / 2] in its high nibble, as two's-complement nibbles.
+// n + 0x88888 holds digit + 8 in every nibble (the balanced digits of |n| <= 2^18
+// are the offset digits of n + 0x88888), and the exclusive or with 0x88888 turns
+// each nibble into its digit's 4-bit form, so one add and one xor give all five.
 template <int U>
-__device__ __forceinline__ void store_digit_run(uint8_t* dst, const int (&n)[U], int li) {
-    const int C = (int)((8u * ((1u << (4 * li)) - 1u)) / 15u);
-    uint32_t w[(U + 3) / 4];
+__device__ __forceinline__ void store_pair_digits(uint8_t* dst, int stride, const int (&n)[U]) {
+    constexpr int UH = U / 2;
+    uint32_t ev[UH], od[UH];
 #pragma unroll
-    for (int k = 0; k < (U + 3) / 4; ++k) w[k] = 0;
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-        w[u / 4] |= (((uint32_t)(n[u] + C) >> (4 * li)) & 15u) << (8 * (u % 4));
-    if constexpr (U == 2) *reinterpret_cast<uint16_t*>(dst) = (uint16_t)w[0];
-    else if constexpr (U == 4) *reinterpret_cast<uint32_t*>(dst) = w[0];
-    else *reinterpret_cast<u32x2*>(dst) = u32x2{w[0], w[1]};
+    for (int i = 0; i < UH; ++i)
+        pair_bytes((uint32_t)(n[i] + 0x88888) ^ 0x88888u, (uint32_t)(n[i + UH] + 0x88888) ^ 0x88888u, ev[i], od[i]);
+    store_limb_bytes<UH>(dst, stride, ev, od);
 }
 
 __device__ __forceinline__ uint32_t lds32(const uint8_t* p) { return *reinterpret_cast<const uint32_t*>(p); }
@@ -333,32 +393,21 @@ template <int KM, int P>
 __device__ __forceinline__ void store_key_digits(uint8_t* lo_base, uint8_t* hi_base, int stride, int lane,
                                                  const int (&n)[KM]) {
     static_assert(KM == 1 || KM == 2, "one or two fold channels per lane");
-    constexpr int LPD = 4 / KM;                  // limbs per packed dword
-    constexpr int NW = (kLimbs + LPD - 1) / LPD;
     constexpr int KPL = P / KM;                  // lanes from the owner of c to that of c + P
     static_assert(KPL >= 1 && 2 * KPL <= 16, "pair partner within the lane's row");
-    uint32_t w[NW];
+    // All five digits of channel c + j as two's-complement nibbles (the add and
+    // xor of store_pair_digits), those of c + P + j from the partner lane, and
+    // their pair bytes: limbs 0, 2, 4 in bytes 0, 1, 2 of ev, limbs 1, 3 of od.
+    uint32_t ev[KM], od[KM];
 #pragma unroll
-    for (int k = 0; k < NW; ++k) w[k] = 0u;
-#pragma unroll
-    for (int li = 0; li < kLimbs; ++li) {
-        const int C = (int)((8u * ((1u << (4 * li)) - 1u)) / 15u);
-#pragma unroll
-        for (int j = 0; j < KM; ++j)
-            w[li / LPD] |= (((uint32_t)(n[j] + C) >> (4 * li)) & 15u) << (8 * (KM * (li % LPD) + j));
+    for (int j = 0; j < KM; ++j) {
+        const uint32_t x = (uint32_t)(n[j] + 0x88888) ^ 0x88888u;
+        pair_bytes(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x100 + KPL, 0xF, 0xF, true), ev[j], od[j]);
     }
-#pragma unroll
-    for (int k = 0; k < NW; ++k) w[k] |= (uint32_t)__builtin_amdgcn_mov_dpp((int)w[k], 0x100 + KPL, 0xF, 0xF, true) << 4;
     const int c = KM * lane;
     const bool lo = c % (2 * P) < P;
     const int cl = lo ? c : c - P;
-    uint8_t* dst = (lo ? lo_base : hi_base) + (cl / (2 * P)) * P + cl % (2 * P);
-#pragma unroll
-    for (int li = 0; li < kLimbs; ++li) {
-        const uint32_t v = w[li / LPD] >> (8 * KM * (li % LPD));
-        if constexpr (KM == 2) *reinterpret_cast<uint16_t*>(dst + li * stride) = (uint16_t)v;
-        else dst[li * stride] = (uint8_t)v;
-    }
+    store_limb_bytes<KM>((lo ? lo_base : hi_base) + (cl / (2 * P)) * P + cl % (2 * P), stride, ev, od);
 }
 
 // nw dwords from p (aligned to the largest load used): 16-byte loads where they
@@ -1028,6 +1077,15 @@ void decode_kernel(DecArgs a) {
     static_assert(NVL >= 1 && NVL * 2 * TB == TILE, "tile must be whole value wave-loads");
     static_assert(TPG == 1 || TPG == 2 || TPG == 4 || TPG == 8, "tiles per key group");
     static_assert(TILE % 32 == 0 && (U == 2 || U == 4 || U == 8), "digit runs of 2, 4 or 8 bytes");
+    // A nibble dword of value codes pairs tokens t and t + PT in each byte (PT = 4
+    // for 4-bit codes, 8 for 2-bit ones; pairs of a block of 2 PT tokens in order).
+    // The U tokens of a key slot are UH such pairs, tokens tok0 + tok_off(u): the
+    // slot's weight digits then go to LDS as bytes that already pair them, and
+    // the value lanes read their digit dwords whole.
+    constexpr int PT = VB == 4 ? 4 : 8;
+    constexpr int UH = U / 2;
+    static_assert(PT % UH == 0, "a slot's pairs lie in one block of 2 PT tokens");
+    constexpr auto tok_off = [](int u) constexpr { return u % UH + PT * (u / UH); };
 
     extern __shared__ __align__(16) unsigned char dsm[];
     using MS = MStream<BITS, D, GQ, TPG, NVGT, SP, KT>;
@@ -1079,6 +1137,8 @@ void decode_kernel(DecArgs a) {
     int* s_last = reinterpret_cast<int*>(s_ml + kWaves * GQ * 2);
 
     const int slot = lane / LPT, chunk = lane % LPT;
+    const int sp0 = slot * UH;                                // the slot's first token pair
+    const int tok0 = 2 * PT * (sp0 / PT) + sp0 % PT;         // its first token
     const int hb = lane >> 5;                  // value half: block parity
     const int c0v = (lane & 31) * VCPL;        // value channels of this lane
     const int gv = c0v / a.GV;                 // their value group
@@ -1194,7 +1254,7 @@ void decode_kernel(DecArgs a) {
         MS ms;             // the matrix-core stream (MF only)
         if constexpr (MF) ms.init(a, rs, ga, n_my_groups, lane, kd);
 
-        // One tile of the wave's stream.  Key token slot * U + u of the tile is
+        // One tile of the wave's stream.  Key token tok0 + tok_off(u) of the tile is
         // scored by the LPT lanes of `slot`; value block hb * NVL + vl (TB tokens)
         // of channels c0v.. is handled by this lane.  ks/kz (key scales and zero
         // points of this lane's KM fold channels) are loaded with a group's first tile.
@@ -1215,26 +1275,25 @@ void decode_kernel(DecArgs a) {
         };
         const int last_group = n_my_groups - 1;
         // per-lane byte offsets, the same for every tile
-        const uint32_t k_off = (uint32_t)a.rec_kcodes + slot * U * RB + chunk * (LW * 4);
+        const uint32_t k_off = (uint32_t)a.rec_kcodes + tok0 * RB + chunk * (LW * 4);
         const uint32_t v_off = (uint32_t)a.rec_vcodes + (hb * NVL * D + c0v) * 4;
         const uint32_t km_off = KM * lane * 4;
         uint32_t vm_off[U], kt_off[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            vm_off[u] = (uint32_t)a.rec_vmeta + ((slot * U + u) * nvg + gz) * 8;
-            kt_off[u] = (slot * U + u) * 8;  // KT: the token's (scale, zero) at the record's start
+            vm_off[u] = (uint32_t)a.rec_vmeta + ((tok0 + tok_off(u)) * nvg + gz) * 8;
+            kt_off[u] = (tok0 + tok_off(u)) * 8;  // KT: the token's (scale, zero) at the record's start
         }
         // SP: outlier fields of this lane's fold channels and of its (token, group gz)
         // items; a u16 field is read with the dword that holds it
         const uint32_t kov_off = (uint32_t)a.rec_kov + KM * lane * 4;
         const uint32_t koi_off = (uint32_t)a.rec_koi + ((KM * lane * 2) & ~3);
         const int koi_shift = KM == 1 ? 16 * (lane & 1) : 0;
-        const int vitem0 = slot * U * nvg + gz;  // item of token slot * U + u: vitem0 + u * nvg
         uint32_t vov_off[U], voi_off[U];
         int voi_shift[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int item = vitem0 + u * nvg;
+            const int item = (tok0 + tok_off(u)) * nvg + gz;
             vov_off[u] = (uint32_t)a.rec_vov + item * 4;
             voi_off[u] = (uint32_t)a.rec_voi + ((item * 2) & ~3);
             voi_shift[u] = 16 * (item & 1);
@@ -1248,7 +1307,7 @@ void decode_kernel(DecArgs a) {
             const uint32_t grp = ga.at(min(j, max(last_group, 0)));
             const int t0 = tig * TILE;
 #pragma unroll
-            for (int u = 0; u < U; ++u) t.k[u] = bload<LW>(rs, k_off + u * RB, grp + t0 * RB);
+            for (int u = 0; u < U; ++u) t.k[u] = bload<LW>(rs, k_off + tok_off(u) * RB, grp + t0 * RB);
 #pragma unroll
             for (int vl = 0; vl < NVL; ++vl) t.v[vl] = bload<VCPL>(rs, v_off + vl * D * 4, grp + (t0 / TB) * D * 4);
 #pragma unroll
@@ -1268,8 +1327,11 @@ void decode_kernel(DecArgs a) {
             if constexpr (SP) {
                 // item offsets within the group: t0 * nvg items before this tile (t0 even)
                 if constexpr (SP_WIDE) {
-                    t.vov4 = bload<4>(rs, vov_off[0], grp + t0 * 4);
-                    t.voi4 = bload<2>(rs, voi_off[0], grp + t0 * 2);
+                    // tokens tok0, tok0 + 1 and their partners tok0 + PT, tok0 + PT + 1 (tok0 even)
+                    const u32x2 x0 = bload<2>(rs, vov_off[0], grp + t0 * 4);
+                    const u32x2 x1 = bload<2>(rs, vov_off[UH], grp + t0 * 4);
+                    t.vov4 = u32x4{x0.x, x0.y, x1.x, x1.y};
+                    t.voi4 = u32x2{bload<1>(rs, voi_off[0], grp + t0 * 2), bload<1>(rs, voi_off[UH], grp + t0 * 2)};
                 } else {
 #pragma unroll
                     for (int u = 0; u < U; ++u) {
@@ -1421,9 +1483,11 @@ void decode_kernel(DecArgs a) {
                 }
 #pragma unroll
                 for (int h = 0; h < GQ; ++h) {
-                    int acc = 0;
+                    int acc = dot8_0(kl[h][kLimbs - 1][0], cw[0]);
 #pragma unroll
-                    for (int li = kLimbs - 1; li >= 0; --li) {
+                    for (int nd = 1; nd < KND; ++nd) acc = dot8(kl[h][kLimbs - 1][nd], cw[nd], acc);
+#pragma unroll
+                    for (int li = kLimbs - 2; li >= 0; --li) {
                         acc <<= 4;
 #pragma unroll
                         for (int nd = 0; nd < KND; ++nd) acc = dot8(kl[h][li][nd], cw[nd], acc);
@@ -1446,7 +1510,7 @@ void decode_kernel(DecArgs a) {
                     } else {
                         sc[h][u] = group_sum<LPT>(sc[h][u]) * kinv[h] - kbias[h];
                     }
-                    if constexpr (SP) sc[h][u] += (float)kc[h * TILE * TPG + tig * TILE + slot * U + u] * kc_inv;
+                    if constexpr (SP) sc[h][u] += (float)kc[h * TILE * TPG + tig * TILE + tok0 + tok_off(u)] * kc_inv;
                     mt = fmaxf(mt, sc[h][u]);
                 }
                 mt = slots_max<LPT>(mt);
@@ -1520,10 +1584,8 @@ void decode_kernel(DecArgs a) {
                 int n[U];
 #pragma unroll
                 for (int u = 0; u < U; ++u) n[u] = (int)rintf(pt[u] * fs.mul);
-                // every lane of a (slot, value group) writes the same bytes
-                uint8_t* dst = pb + ((h * nvg + gz) * kLimbs) * TILE + slot * U;
-#pragma unroll
-                for (int li = 0; li < kLimbs; ++li) store_digit_run<U>(dst + li * TILE, n, li);
+                // the slot's pair bytes (every lane of a (slot, value group) writes the same bytes)
+                store_pair_digits<U>(pb + ((h * nvg + gz) * kLimbs) * TILE + sp0, TILE, n);
             }
             wave_lds_sync();
 
@@ -1544,34 +1606,38 @@ void decode_kernel(DecArgs a) {
             }
 #pragma unroll
             for (int h = 0; h < GQ; ++h) {
-                const uint8_t* pbase = pb + ((h * nvg + gv) * kLimbs) * TILE + hb * (TILE / 2);
+                const uint8_t* pbase = pb + ((h * nvg + gv) * kLimbs) * TILE + hb * (TILE / 4);
                 int acc[VCPL];
 #pragma unroll
                 for (int c = 0; c < VCPL; ++c) acc[c] = 0;
 #pragma unroll
                 for (int li = kLimbs - 1; li >= 0; --li) {
-                    // digit bytes of this half's TILE / 2 tokens
-                    uint32_t w[TILE / 8];
-#pragma unroll
-                    for (int q4 = 0; q4 < TILE / 32; ++q4) {
-                        const u32x4 x = *reinterpret_cast<const u32x4*>(pbase + li * TILE + 16 * q4);
-                        w[4 * q4] = x.x, w[4 * q4 + 1] = x.y, w[4 * q4 + 2] = x.z, w[4 * q4 + 3] = x.w;
+                    // pair bytes of this half's TILE / 2 tokens: digit dwords that line up
+                    // with its value code nibble dwords
+                    uint32_t w[TILE / 16];
+                    if constexpr (TILE / 16 == 4) {
+                        const u32x4 x = *reinterpret_cast<const u32x4*>(pbase + li * TILE);
+                        w[0] = x.x, w[1] = x.y, w[2] = x.z, w[3] = x.w;
+                    } else {
+                        static_assert(TILE / 16 == 2, "32- or 64-token tiles");
+                        const u32x2 x = *reinterpret_cast<const u32x2*>(pbase + li * TILE);
+                        w[0] = x.x, w[1] = x.y;
                     }
 #pragma unroll
                     for (int c = 0; c < VCPL; ++c) acc[c] <<= 4;
 #pragma unroll
                     for (int vl = 0; vl < NVL; ++vl) {
                         uint32_t dl[VNE];
-                        if constexpr (VB == 4) {
-                            dl[0] = w[2 * vl] | (w[2 * vl + 1] << 4);
-                        } else {
-                            dl[0] = w[4 * vl] | (w[4 * vl + 2] << 4);
-                            dl[VNE - 1] = w[4 * vl + 1] | (w[4 * vl + 3] << 4);
-                        }
+#pragma unroll
+                        for (int e = 0; e < VNE; ++e) dl[e] = w[vl * VNE + e];
 #pragma unroll
                         for (int c = 0; c < VCPL; ++c)
 #pragma unroll
-                            for (int e = 0; e < VNE; ++e) acc[c] = dot8(dl[e], vw[vl][c][e], acc[c]);
+                            for (int e = 0; e < VNE; ++e) {
+                                // the first product of a channel starts its sum
+                                if (li == kLimbs - 1 && vl == 0 && e == 0) acc[c] = dot8_0(dl[e], vw[vl][c][e]);
+                                else acc[c] = dot8(dl[e], vw[vl][c][e], acc[c]);
+                            }
                     }
                 }
 #pragma unroll
