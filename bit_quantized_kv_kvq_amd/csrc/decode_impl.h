@@ -1921,7 +1921,6 @@ void decode_kernel(DecArgs a) {
     // elements' accumulators of every partial.  The partials are merged in split
     // (or group) order, each weighted by exp2(m_i - M) under the overall maximum M.
     constexpr int NE = (GQ * D + kThreads - 1) / kThreads;  // (head, channel) elements per thread
-    constexpr int NP = (kMaxMerge * GQ + kThreads - 1) / kThreads;  // (partial, head) pairs per thread
     __shared__ float2 s_pml[kMaxMerge * GQ];
     int hk[NE], ck[NE];
 #pragma unroll
@@ -1941,47 +1940,60 @@ void decode_kernel(DecArgs a) {
         }
         __syncthreads();
         if (!*s_last) return;
-        const int npair = ns * GQ;
-        float2 mlr[NP];
+        // The merge, with NB >= ns partials' loads per element (the power of two
+        // above ns): loads beyond ns repeat the last partial's addresses, and each is
+        // a round trip of its own to the coherence point, so they are not padded to
+        // kMaxMerge.
+        auto merge = [&](auto nbc) __attribute__((always_inline)) {
+            constexpr int NB = decltype(nbc)::value;
+            constexpr int NPB = (NB * GQ + kThreads - 1) / kThreads;  // (partial, head) pairs per thread
+            const int npair = ns * GQ;
+            float2 mlr[NPB];
 #pragma unroll
-        for (int r = 0; r < NP; ++r) mlr[r] = fetch2(&pml[2 * min(tid + r * kThreads, npair - 1)]);
-        float ai[NE][kMaxMerge];
+            for (int r = 0; r < NPB; ++r) mlr[r] = fetch2(&pml[2 * min(tid + r * kThreads, npair - 1)]);
+            float ai[NE][NB];
 #pragma unroll
-        for (int i = 0; i < kMaxMerge; ++i)
+            for (int i = 0; i < NB; ++i)
 #pragma unroll
-            for (int k = 0; k < NE; ++k) ai[k][i] = fetch(&pacc[(min(i, ns - 1) * GQ + hk[k]) * D + ck[k]]);
+                for (int k = 0; k < NE; ++k) ai[k][i] = fetch(&pacc[(min(i, ns - 1) * GQ + hk[k]) * D + ck[k]]);
 #pragma unroll
-        for (int r = 0; r < NP; ++r)
-            if (tid + r * kThreads < npair) s_pml[tid + r * kThreads] = mlr[r];
-        __syncthreads();
+            for (int r = 0; r < NPB; ++r)
+                if (tid + r * kThreads < npair) s_pml[tid + r * kThreads] = mlr[r];
+            __syncthreads();
 #pragma unroll
-        for (int k = 0; k < NE; ++k) {
-            float M = -INFINITY, L = 0.0f, A = 0.0f;
-            for (int i = 0; i < ns; ++i) M = fmaxf(M, s_pml[i * GQ + hk[k]].x);
+            for (int k = 0; k < NE; ++k) {
+                float M = -INFINITY, L = 0.0f, A = 0.0f;
+                for (int i = 0; i < ns; ++i) M = fmaxf(M, s_pml[i * GQ + hk[k]].x);
 #pragma unroll
-            for (int i = 0; i < kMaxMerge; ++i) {
-                if (i < ns) {
-                    const float2 ml = s_pml[i * GQ + hk[k]];
-                    const float w = ml.x == -INFINITY ? 0.0f : fast_exp2(ml.x - M);
-                    L = fmaf(ml.y, w, L);
-                    A = fmaf(ai[k][i], w, A);
+                for (int i = 0; i < NB; ++i) {
+                    if (i < ns) {
+                        const float2 ml = s_pml[i * GQ + hk[k]];
+                        const float w = ml.x == -INFINITY ? 0.0f : fast_exp2(ml.x - M);
+                        L = fmaf(ml.y, w, L);
+                        A = fmaf(ai[k][i], w, A);
+                    }
+                }
+                if (tid + k * kThreads >= GQ * D) continue;
+                const int h = hk[k], c = ck[k];
+                if (final) {
+                    a.out[(qrow0 + h) * D + c] = A / L;
+                    if (c == 0 && a.lse) a.lse[qrow0 + h] = (M + __log2f(L)) * 0.69314718055994530942f;
+                } else {
+                    // this group's partial
+                    const int64_t gidx = (bh * a.cgroups_cap + grp) * GQ + h;
+                    publish(&a.grp_acc[gidx * D + c], A);
+                    if (c == 0) {
+                        publish(&a.grp_ml[gidx * 2], M);
+                        publish(&a.grp_ml[gidx * 2 + 1], L);
+                    }
                 }
             }
-            if (tid + k * kThreads >= GQ * D) continue;
-            const int h = hk[k], c = ck[k];
-            if (final) {
-                a.out[(qrow0 + h) * D + c] = A / L;
-                if (c == 0 && a.lse) a.lse[qrow0 + h] = (M + __log2f(L)) * 0.69314718055994530942f;
-            } else {
-                // this group's partial
-                const int64_t gidx = (bh * a.cgroups_cap + grp) * GQ + h;
-                publish(&a.grp_acc[gidx * D + c], A);
-                if (c == 0) {
-                    publish(&a.grp_ml[gidx * 2], M);
-                    publish(&a.grp_ml[gidx * 2 + 1], L);
-                }
-            }
-        }
+        };
+        static_assert(kMaxMerge == 16, "merge sizes 2, 4, 8, 16");
+        if (ns <= 2) merge(std::integral_constant<int, 2>());
+        else if (ns <= 4) merge(std::integral_constant<int, 4>());
+        else if (ns <= 8) merge(std::integral_constant<int, 8>());
+        else merge(std::integral_constant<int, 16>());
         // this counter's arrivals are all counted: clear it for the next call
         if (tid == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (final) return;
