@@ -64,6 +64,9 @@ def _attend_and_check(w, cache, K, V, seed=5):
     dict(n_q_heads=4),                                  # GQA 2
     dict(n_q_heads=16, bits=2),                         # GQA 8
     dict(n_q_heads=16, bits=4, head_dim=64),            # GQA 8, D64
+    dict(n_q_heads=16, bits=4),                         # GQA 8, D128: 8 channels per lane, 8 tokens per slot
+    dict(v_group=16, k_group=64, residual=128),         # 16-channel value groups: 8 tokens per slot
+    dict(v_group=16, k_group=64, residual=128, bits=2),
     dict(n_sink=3),
     dict(k_group=64, residual=128, v_group=128),        # 64-token tiles, one per group
     dict(k_group=128, residual=128, v_group=64),        # two tiles per group
