@@ -657,9 +657,14 @@ struct MStream {
                 bp[h] = fmaf(qt[h][j], __uint_as_float(elem(kz, j)) - ZOFF, bp[h]);
             }
         }
+        // One fixed-point scale for the group's query heads, from their largest
+        // |q_c s_c|: one whole-wave reduction instead of one per head.
+        float mxa = mx[0];
+#pragma unroll
+        for (int h = 1; h < GQ; ++h) mxa = fmaxf(mxa, mx[h]);
+        const FixScale fs = fix_scale(group_max<64>(mxa));
 #pragma unroll
         for (int h = 0; h < GQ; ++h) {
-            const FixScale fs = fix_scale(group_max<64>(mx[h]));
             kinv[h] = fs.inv;
             kbias[h] = group_sum<64>(bp[h]);
 #pragma unroll
