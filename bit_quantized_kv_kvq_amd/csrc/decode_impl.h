@@ -1821,6 +1821,18 @@ void decode_kernel(DecArgs a) {
                 process(tr[B % NR], (B & 1) ? pd1 : pd0, B % TPG);
                 __builtin_amdgcn_sched_barrier(0);
             };
+            // Issue priority by progress: the wave's iterations run in quarters at
+            // priority 3, 2, 1 and 0.  Of two workgroups on a CU, the SIMDs otherwise
+            // favour the older one's waves throughout, so the younger falls behind and
+            // its slot ends last; now the one with less of its stream done wins, and
+            // the two run closer to level.
+            __builtin_amdgcn_s_setprio(3);
+            for (; it < n_iter / 4; ++it) StaticFor<0, BODY>::run(step);
+            __builtin_amdgcn_s_setprio(2);
+            for (; it < n_iter / 2; ++it) StaticFor<0, BODY>::run(step);
+            __builtin_amdgcn_s_setprio(1);
+            for (; it < 3 * n_iter / 4; ++it) StaticFor<0, BODY>::run(step);
+            __builtin_amdgcn_s_setprio(0);
             for (; it < n_iter; ++it) StaticFor<0, BODY>::run(step);
             // Groups after the last whole iteration: fewer than GB, so at most
             // NR - TPG tiles, already in the first NR - 1 buffers.
