@@ -1826,14 +1826,16 @@ void decode_kernel(DecArgs a) {
             // favour the older one's waves throughout, so the younger falls behind and
             // its slot ends last; now the one with less of its stream done wins, and
             // the two run closer to level.
+            // (One loop: the priority changes by scalar branches at the quarter
+            // boundaries, outside the unrolled body.)
+            const int q1 = n_iter / 4, q2 = n_iter / 2, q3 = 3 * n_iter / 4;
             __builtin_amdgcn_s_setprio(3);
-            for (; it < n_iter / 4; ++it) StaticFor<0, BODY>::run(step);
-            __builtin_amdgcn_s_setprio(2);
-            for (; it < n_iter / 2; ++it) StaticFor<0, BODY>::run(step);
-            __builtin_amdgcn_s_setprio(1);
-            for (; it < 3 * n_iter / 4; ++it) StaticFor<0, BODY>::run(step);
-            __builtin_amdgcn_s_setprio(0);
-            for (; it < n_iter; ++it) StaticFor<0, BODY>::run(step);
+            for (; it < n_iter; ++it) {
+                if (it == q1) __builtin_amdgcn_s_setprio(2);
+                if (it == q2) __builtin_amdgcn_s_setprio(1);
+                if (it == q3) __builtin_amdgcn_s_setprio(0);
+                StaticFor<0, BODY>::run(step);
+            }
             // Groups after the last whole iteration: fewer than GB, so at most
             // NR - TPG tiles, already in the first NR - 1 buffers.
             if constexpr (GB > 1) {
