@@ -28,7 +28,8 @@
 // Mapping on CDNA4 (wave64), one workgroup = 4 waves = one split:
 //   - a slice's quantized part is a stream of key-group records (key scales and
 //     zeros, key code rows, value code blocks, value scales and zeros); wave w of
-//     the split streams groups w, w+4, ... tile by tile, one tile ahead;
+//     the split streams groups w, w+4, ... tile by tile through a ring of
+//     tiles, the next ones in flight while one is processed;
 //   - keys: a token row is spread over LPT = D / CPL lanes (CPL codes each), so a
 //     wave scores TPW = 64 / LPT tokens per load; the per-lane integer partials
 //     are summed over the LPT lanes with DPP;
@@ -38,8 +39,13 @@
 //   - the folded query's digits go through LDS as bytes that already pair the
 //     channels of a code nibble dword (the writer takes the partner channel's
 //     digits from a neighbouring lane), so a lane reads its digit dwords whole;
-//   - softmax weights and digits move between the two mappings through LDS as
-//     bytes, and are packed into digit dwords with one shift-or;
+//   - the softmax weights' digits move between the two mappings through LDS as
+//     bytes that pair the tokens of a value code nibble dword (a key slot scores
+//     whole token pairs), so a value lane reads its digit dwords whole;
+//   - all five digits of an integer come from one add and one xor (n + 0x88888
+//     holds each digit + 8 in its nibble);
+//   - issue priority falls as a wave's stream advances, so of two workgroups
+//     sharing a CU the one with less done is served first;
 //   - the running max is wave-uniform and updated once per tile;
 //   - sinks and residual tokens (full precision) are spread over the splits and
 //     scored with fp32 FMAs through the same state;
